@@ -1,0 +1,160 @@
+"""Byte layout of the packed KV store, written from its format description.
+
+TEST INFRASTRUCTURE ONLY.  Used to turn the oracle's encoded streams into the
+store's bytes (for bit-exact comparison with what the device encoder wrote)
+and to read a device store back.  Shares no code with the device library.
+
+Layout (all little-endian; every sub-array starts on a 256-byte boundary):
+
+header (align_up(256 + 32*B, 4096) bytes)
+  u32 magic 0x52564B31, u32 version 1, i32 W, i32 d, i32 H, i32 G,
+  i32 group_tokens, i32 B, i32 kv_dtype (0 bf16, 1 f32), u32 flags,
+  i64 capacity, i64 total_bytes;  at 256 + 32*b: i64 len, i64 cap,
+  i64 offset, i64 reserved  for request b.
+request region b (cap = cap_b, a multiple of 32; ng = cap/32):
+  Kplanes u32 [G][d][W][ng]   bit i of word (g,c,p,gamma) = plane p (bit
+                              W-1-p of the code) of token 32*gamma+i, chan c
+  Vplanes u32 [G][cap][W][d/32]  bit (c%32) of word (g,j,p,c/32) = plane p
+                              of token j, channel c
+  Kmeta   u32 [G][ng][d]      lo bf16 bits | rng bf16 bits << 16
+  Vmeta   u32 [G][ng][d]
+  EK      f64 [G][d]          sum over closed groups (in order) of rng_K^2
+  EV      f64 [G][ng]         sum over channels (in order) of rng_V^2
+  Ktail   elem [G][32][d]     open-group keys (slot i = token 32*floor(len/32)+i)
+  Vtail   elem [G][32][d]
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MAGIC = 0x52564B31
+
+
+def _al(x: int, a: int) -> int:
+    return (x + a - 1) // a * a
+
+
+def header_bytes(B: int) -> int:
+    return _al(256 + 32 * B, 4096)
+
+
+def region_layout(G: int, d: int, W: int, cap: int, esize: int) -> dict:
+    """Byte offsets (relative to the region start) and sizes of each
+    sub-array of one request region."""
+    ng = cap // 32
+    parts = [
+        ("Kplanes", G * d * W * ng * 4),
+        ("Vplanes", G * cap * W * (d // 32) * 4),
+        ("Kmeta", G * ng * d * 4),
+        ("Vmeta", G * ng * d * 4),
+        ("EK", G * d * 8),
+        ("EV", G * ng * 8),
+        ("Ktail", G * 32 * d * esize),
+        ("Vtail", G * 32 * d * esize),
+    ]
+    off = 0
+    lay = {}
+    for name, size in parts:
+        off = _al(off, 256)
+        lay[name] = (off, size)
+        off += size
+    lay["_size"] = _al(off, 4096)
+    return lay
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint32)
+
+
+def pack_unit(enc_k, enc_v, cap: int, dtype: str) -> dict:
+    """Arrays one (request, KV head) unit occupies in a request region of
+    capacity ``cap`` tokens, for the oracle's encoded key/value streams."""
+    W = enc_k.W
+    tp, d = enc_k.codes.shape
+    ng = cap // 32
+    ngc = enc_k.n_groups
+    kpl = np.zeros((d, W, ng), dtype=np.uint32)
+    ck = enc_k.codes.reshape(ngc, 32, d)
+    for p in range(W):
+        bits = ((ck >> (W - 1 - p)) & 1).astype(np.uint64)       # [ngc][32][d]
+        word = (bits << np.arange(32, dtype=np.uint64)[None, :, None]).sum(axis=1)
+        kpl[:, p, :ngc] = word.T.astype(np.uint32)
+    vpl = np.zeros((cap, W, d // 32), dtype=np.uint32)
+    for p in range(W):
+        bits = ((enc_v.codes >> (W - 1 - p)) & 1).astype(np.uint64)  # [tp][d]
+        bits = bits.reshape(tp, d // 32, 32)
+        word = (bits << np.arange(32, dtype=np.uint64)[None, None, :]).sum(axis=2)
+        vpl[:tp, p, :] = word.astype(np.uint32)
+
+    def meta(enc):
+        m = np.zeros((ng, d), dtype=np.uint32)
+        m[:ngc] = _bf16_bits(enc.lo) | (_bf16_bits(enc.rng) << 16)
+        return m
+
+    ek = np.zeros(d)
+    for gam in range(ngc):
+        ek = ek + enc_k.rng[gam] * enc_k.rng[gam]
+    ev = np.zeros(ng)
+    for c in range(d):
+        ev[:ngc] = ev[:ngc] + enc_v.rng[:, c] * enc_v.rng[:, c]
+
+    def tail(enc):
+        r = enc.tail.shape[0]
+        if dtype == "bf16":
+            t = np.zeros((32, d), dtype=np.uint16)
+            t[:r] = _bf16_bits(enc.tail).astype(np.uint16)
+        else:
+            t = np.zeros((32, d), dtype=np.float32)
+            t[:r] = enc.tail.astype(np.float32)
+        return t
+
+    return dict(Kplanes=kpl, Vplanes=vpl, Kmeta=meta(enc_k), Vmeta=meta(enc_v),
+                EK=ek, EV=ev, Ktail=tail(enc_k), Vtail=tail(enc_v))
+
+
+def read_header(buf: np.ndarray) -> dict:
+    """Parse the store header from raw bytes (uint8 array)."""
+    b = np.asarray(buf, dtype=np.uint8)
+    u32 = b[:48].view(np.uint32)
+    i32 = b[:48].view(np.int32)
+    i64 = b[:48].view(np.int64)
+    hdr = dict(magic=int(u32[0]), version=int(u32[1]), W=int(i32[2]), d=int(i32[3]),
+               H=int(i32[4]), G=int(i32[5]), group_tokens=int(i32[6]),
+               B=int(i32[7]), kv_dtype=int(i32[8]), flags=int(u32[9]),
+               capacity=int(i64[5]))
+    reqs = []
+    for r in range(hdr["B"]):
+        rec = b[256 + 32 * r: 256 + 32 * r + 32].view(np.int64)
+        reqs.append(dict(len=int(rec[0]), cap=int(rec[1]), offset=int(rec[2])))
+    hdr["requests"] = reqs
+    return hdr
+
+
+def unpack_unit(buf: np.ndarray, hdr: dict, b: int, g: int) -> dict:
+    """The arrays of unit (b, g) from raw store bytes."""
+    G, d, W = hdr["G"], hdr["d"], hdr["W"]
+    req = hdr["requests"][b]
+    cap = req["cap"]
+    ng = cap // 32
+    esize = 2 if hdr["kv_dtype"] == 0 else 4
+    lay = region_layout(G, d, W, cap, esize)
+    base = req["offset"]
+
+    def sub(name, dt, shape):
+        off, size = lay[name]
+        per = size // G
+        raw = np.asarray(buf[base + off + g * per: base + off + (g + 1) * per], dtype=np.uint8)
+        return raw.view(dt).reshape(shape)
+
+    edt = np.uint16 if esize == 2 else np.float32
+    return dict(
+        Kplanes=sub("Kplanes", np.uint32, (d, W, ng)),
+        Vplanes=sub("Vplanes", np.uint32, (cap, W, d // 32)),
+        Kmeta=sub("Kmeta", np.uint32, (ng, d)),
+        Vmeta=sub("Vmeta", np.uint32, (ng, d)),
+        EK=sub("EK", np.float64, (d,)),
+        EV=sub("EV", np.float64, (ng,)),
+        Ktail=sub("Ktail", edt, (32, d)),
+        Vtail=sub("Vtail", edt, (32, d)),
+    )
