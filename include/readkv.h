@@ -1,0 +1,167 @@
+/*
+ * readkv.h -- C ABI of the ReadKV decode-attention library for AMD MI355X
+ * (gfx950).
+ *
+ * The method ("Read What Matters: Query-Adaptive Quantization for KV
+ * Caches", arXiv 2610.11245): every cached key and value scalar is stored
+ * once as a W-bit progressive code whose every prefix is decodable (Sec. 3.1).
+ * At each decode step the query chooses how many prefix bits of every key
+ * channel to read under a read budget, attention is computed from the
+ * reconstructed keys, and that attention chooses how many prefix bits of
+ * every value token to read (Sec. 3.2-3.3, Algorithm 1; a staged(2) reader
+ * in the sense of Sec. 2).  Stored records are never rewritten.
+ *
+ * Code used here: per (request, KV head, channel, 32-token group) uniform
+ * min/max quantiser; lo = bf16 group minimum rounded down, rng = bf16 range
+ * rounded up; code = min(floor((x - lo) * 2^W / rng), 2^W - 1); stored as W
+ * MSB-first bit-planes.  A depth-t prefix P reconstructs to
+ * lo + rng * (2P + 1) / 2^(t+1).  Refinement gains follow D(t) ~ 4^-t.
+ *
+ * Ownership: the caller allocates every buffer (store, workspace, inputs,
+ * outputs) in device memory and keeps it alive until the enqueued work
+ * completes.  The library allocates nothing, never synchronises the stream
+ * (except readkv_store_init and readkv_store_status, which say so), and
+ * keeps no global state beyond its loaded kernels.  Calls on different
+ * streams are independent if they use different stores and workspaces.
+ *
+ * Errors: every entry point returns 0 on success or a negative READKV_E*
+ * code.  All argument checks happen on the host before anything is
+ * enqueued; on error nothing is enqueued.  READKV_ELAUNCH reports a failed
+ * kernel launch.  Device-side conditions (non-finite input, append beyond
+ * capacity) set sticky flags in the store header, read with
+ * readkv_store_status.
+ *
+ * `stream` arguments are hipStream_t values passed as void* (NULL = the
+ * default stream).
+ */
+#ifndef READKV_H
+#define READKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define READKV_OK 0
+#define READKV_EINVAL (-1)       /* bad argument or config                  */
+#define READKV_ENOSPC (-2)       /* append larger than the store capacity   */
+#define READKV_EWORKSPACE (-3)   /* store or workspace buffer too small     */
+#define READKV_EDTYPE (-4)       /* unknown element type                    */
+#define READKV_EUNSUPPORTED (-5) /* valid but not built (d_h != 128, ...)   */
+#define READKV_ELAUNCH (-6)      /* a HIP launch or copy failed             */
+
+#define READKV_BF16 0
+#define READKV_F32 1
+
+/* Value-item scale s in the value weight (Sec. 3.2, Eq. (3); App. D.2):
+ * PHYSICAL = sum over channels of the token group's squared range,
+ * UNIT = 1 (standardised units). */
+#define READKV_VSCALE_PHYSICAL 0
+#define READKV_VSCALE_UNIT 1
+
+/* Store flags (readkv_store_status) */
+#define READKV_FLAG_NONFINITE 1u /* a group held a non-finite value; it was
+                                    stored with lo = rng = 0 and codes 0     */
+#define READKV_FLAG_OVERFLOW 2u  /* an append ran past a request's capacity;
+                                    the tokens beyond it were dropped        */
+
+typedef struct readkv_config {
+  int32_t W;               /* stored bits per scalar, 1..8 (Sec. 2: W)     */
+  int32_t head_dim;        /* d_h; this build supports 128                 */
+  int32_t num_q_heads;     /* H query heads                                */
+  int32_t num_kv_heads;    /* G KV heads; H % G == 0, H/G <= 8 (GQA map
+                              g(h) = h / (H/G), Sec. 3.1)                  */
+  int32_t group_tokens;    /* quantiser group along tokens; must be 32     */
+  int32_t batch;           /* B requests                                   */
+  int64_t capacity_tokens; /* largest per-request capacity, tokens (also
+                              the default capacity of every request)       */
+  int32_t kv_dtype;        /* READKV_BF16 or READKV_F32: element type of
+                              appended K/V, of the open-group buffer and of
+                              queries                                      */
+  int32_t reserved;        /* must be 0                                    */
+} readkv_config;
+
+/* Check a config.  Returns 0, EINVAL, EDTYPE or EUNSUPPORTED. */
+int readkv_validate_config(const readkv_config* cfg);
+
+/* Bytes of device memory a store needs.  req_capacity: host array [batch]
+ * of per-request capacities in tokens, each in 1..capacity_tokens (ragged
+ * batches get per-request regions), or NULL to give every request
+ * cfg->capacity_tokens.  Capacities round up to a multiple of 32.  Host only. */
+int readkv_store_bytes(const readkv_config* cfg, const int64_t* req_capacity,
+                       size_t* bytes);
+
+/* Bytes of device workspace one readkv_decode_attn call needs (scores,
+ * probabilities, weights, depth schedules, partial outputs; sized for
+ * capacity_tokens per request).  Host only. */
+int readkv_workspace_bytes(const readkv_config* cfg, size_t* bytes);
+
+/* Format a store: writes the header (per-request lengths 0) and zeroes every
+ * record.  store_bytes must be >= readkv_store_bytes.  Synchronises
+ * `stream` before returning (the header is staged from host memory). */
+int readkv_store_init(const readkv_config* cfg, void* store,
+                      size_t store_bytes, const int64_t* req_capacity,
+                      void* stream);
+
+/* Append new tokens (the encoder of Sec. 3.1 / Algorithm 1).
+ * k_new, v_new: device [batch][num_kv_heads][n_max][head_dim] in kv_dtype;
+ *   request b contributes its first n_new[b] rows (ragged prefill).
+ * n_new: device int32 [batch], or NULL for n_max rows in every request.
+ * When a request's open group reaches 32 tokens the group is quantised and
+ * its bit-planes, metadata and energy sums are written once; tokens of a
+ * still-open group are kept exactly.  Returns ENOSPC if n_max exceeds the
+ * store's default capacity. */
+int readkv_encode_append(const readkv_config* cfg, void* store,
+                         const void* k_new, const void* v_new,
+                         const int32_t* n_new, int32_t n_max, void* stream);
+
+/* One decode step of ReadKV attention for every request and query head.
+ * q: device [batch][num_q_heads][head_dim] in kv_dtype.
+ * R_K, R_V: read bits per scalar for the key and value stages (finite,
+ *   >= 0; the nominal rate is R = (R_K + R_V)/2, Sec. 3.3).  Budgets are
+ *   per (request, KV head): B_K = floor(R_K * d_h) key refinements over the
+ *   d_h channels, B_V = floor(R_V * T_packed) value refinements over the
+ *   tokens of closed groups (R as float32, product in double).
+ * vscale: READKV_VSCALE_PHYSICAL or READKV_VSCALE_UNIT.
+ * out: device fp32 [batch][num_q_heads][head_dim].
+ * workspace: device, >= readkv_workspace_bytes.
+ * key_depths_out: device u8 [batch][num_kv_heads][head_dim] or NULL.
+ * value_depths_out: device u8 [batch][num_kv_heads][capacity_max] or NULL
+ *   (entries beyond a request's packed length are unspecified).
+ * Allocation is ChooseDepths (Sec. 3.3) with gains a_i * 4^-t, exact under
+ * diminishing gains (App. E.2.1, Prop. 8); ties go to the lowest channel /
+ * token index; only positive gains are taken. */
+int readkv_decode_attn(const readkv_config* cfg, const void* store,
+                       const void* q, float R_K, float R_V, int32_t vscale,
+                       float* out, void* workspace, size_t workspace_bytes,
+                       uint8_t* key_depths_out, uint8_t* value_depths_out,
+                       void* stream);
+
+/* readkv_decode_attn with timing hooks: `events` points to 6 hipEvent_t
+ * handles created by the caller (as void*); events[0] is recorded on
+ * `stream` before the first kernel and events[i] after kernel i of the
+ * step, in the order key allocation, score, value allocation, value
+ * gather, output reduction.  Arguments and results are otherwise those of
+ * readkv_decode_attn (EINVAL if events is NULL). */
+int readkv_decode_attn_timed(const readkv_config* cfg, const void* store,
+                             const void* q, float R_K, float R_V,
+                             int32_t vscale, float* out, void* workspace,
+                             size_t workspace_bytes, uint8_t* key_depths_out,
+                             uint8_t* value_depths_out, void* const* events,
+                             void* stream);
+
+/* Read the store's sticky flags and per-request lengths (host arrays;
+ * lengths_out [batch] may be NULL).  Synchronous device-to-host copy. */
+int readkv_store_status(const readkv_config* cfg, const void* store,
+                        uint32_t* flags_out, int64_t* lengths_out);
+
+/* Static description of an error code. */
+const char* readkv_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* READKV_H */

@@ -149,6 +149,7 @@ def encode_stream(X: np.ndarray, W: int = 8, group_tokens: int = 32) -> EncodedS
     bad = bad | ~(np.isfinite(lo) & np.isfinite(rng)).all(axis=1)
     lo = np.where(bad[:, None], 0.0, lo)
     rng = np.where(bad[:, None], 0.0, rng)
+    lo = np.where(lo == 0.0, 0.0, lo)   # a zero minimum is stored as +0
     diff = Gs - lo[:, None, :]                             # fl64(x - lo) >= 0
     num = np.ldexp(diff, W)
     den = np.broadcast_to(rng[:, None, :], num.shape)

@@ -1,0 +1,233 @@
+// Encoder: append tokens, and quantise + bit-plane pack every group that
+// closes ("Read What Matters", Sec. 3.1 / Algorithm 1 encoder; uniform
+// quantiser of "KV Cache Compression Through the Lens of Transform Coding",
+// Sec. III-C, Definition 2, in cell form).
+//
+// Per closed group (32 tokens) and channel c:
+//   lo   = largest bf16 <= min x                      (directed rounding)
+//   rng  = smallest bf16 >= fl64(max x - lo)
+//   code = min(floor(fl64(x - lo) * 2^W / rng), 2^W - 1), exact; 0 if rng = 0
+// The floor is exact: the fp64 quotient is corrected by comparing q*rng
+// with the numerator, both of which are exact in fp64 (q <= 2^W has at
+// most 9 bits and rng 8 significant bits).
+#include "kernels_common.h"
+#include "readkv_internal.h"
+
+namespace readkv {
+
+__device__ __forceinline__ int64_t clamp_n(const ReqRecord& r, const int32_t* n_new, int b,
+                                           int n_max) {
+  int64_t n = n_new ? (int64_t)n_new[b] : (int64_t)n_max;
+  if (n < 0) n = 0;
+  if (n > n_max) n = n_max;
+  if (r.len + n > r.cap) n = r.cap - r.len;
+  return n;
+}
+
+// grid (max groups closing, G, B), 256 threads: threads 0..127 encode the
+// key channels, 128..255 the value channels of one closing group.
+template <int DT>
+__global__ __launch_bounds__(256) void k_encode_groups(uint8_t* store, const void* knew,
+                                                       const void* vnew, const int32_t* n_new,
+                                                       int n_max, int G, int W) {
+  constexpr int esize = DT == 0 ? 2 : 4;
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const ReqRecord r = req_of(store, b);
+  const int64_t len0 = r.len;
+  const int64_t n = clamp_n(r, n_new, b, n_max);
+  const int64_t first = len0 / kGroup;
+  const int64_t count = (len0 + n) / kGroup - first;
+  if (i >= count) return;
+  const int64_t gam = first + i;
+  const Unit u = unit_of(store, r, g, G, kDim, W, esize);
+
+  const int tid = threadIdx.x;
+  const bool isv = tid >= 128;
+  const int c = tid & 127;
+  const void* src = isv ? vnew : knew;
+  const uint8_t* tail = isv ? u.vtail : u.ktail;
+  const int64_t row0 = ((int64_t)b * G + g) * n_max;
+
+  __shared__ int bad_s[2];
+  __shared__ double rv2[128];
+  if (tid < 2) bad_s[tid] = 0;
+  __syncthreads();
+
+  double x[kGroup];
+  bool finite = true;
+  double mn = 0.0, mx = 0.0;
+#pragma unroll
+  for (int s = 0; s < kGroup; ++s) {
+    const int64_t j = gam * kGroup + s;
+    x[s] = (j < len0) ? load_elem<DT>(tail, (int64_t)s * kDim + c)
+                      : load_elem<DT>(src, (row0 + (j - len0)) * kDim + c);
+    finite = finite && isfinite(x[s]);
+  }
+  if (!finite) atomicOr(&bad_s[isv], 1);
+  if (finite) {
+    mn = x[0];
+    mx = x[0];
+#pragma unroll
+    for (int s = 1; s < kGroup; ++s) {
+      mn = fmin(mn, x[s]);
+      mx = fmax(mx, x[s]);
+    }
+  }
+  const uint32_t lo_b = bf16_round_dir(mn, false);
+  const double lo = (double)bf16_to_float(lo_b);
+  const uint32_t rng_b = bf16_round_dir(mx - lo, true);
+  const double rng = (double)bf16_to_float(rng_b);
+  if (!(isfinite(lo) && isfinite(rng))) atomicOr(&bad_s[isv], 1);
+  __syncthreads();
+  const bool bad = bad_s[isv] != 0;
+
+  uint32_t code[kGroup];
+  const double scale = (double)(1u << W);
+  const double cmax = (double)((1u << W) - 1u);
+#pragma unroll
+  for (int s = 0; s < kGroup; ++s) {
+    double q = 0.0;
+    if (!bad && rng > 0.0) {
+      const double num = (x[s] - lo) * scale;  // fl64(x - lo) * 2^W, exact scaling
+      q = floor(num / rng);
+      if (q * rng > num) q -= 1.0;             // q*rng exact: <= 9 x 8 significant bits
+      else if ((q + 1.0) * rng <= num) q += 1.0;
+      q = fmin(q, cmax);
+    }
+    code[s] = (uint32_t)q;
+  }
+  const uint32_t meta = bad ? 0u : (lo_b | (rng_b << 16));
+  const double r2 = bad ? 0.0 : rng * rng;
+  if (bad && c == 0) atomicOr(&header_of(store)->flags, 1u);
+
+  if (!isv) {
+    u.kmeta[gam * kDim + c] = meta;
+    for (int p = 0; p < W; ++p) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int s = 0; s < kGroup; ++s) word |= ((code[s] >> (W - 1 - p)) & 1u) << s;
+      u.kplanes[((int64_t)c * W + p) * u.ng + gam] = word;
+    }
+  } else {
+    u.vmeta[gam * kDim + c] = meta;
+    rv2[c] = r2;
+    const int half = c >> 6;  // which 64-channel half this wave holds
+    for (int s = 0; s < kGroup; ++s) {
+      const int64_t j = gam * kGroup + s;
+      for (int p = 0; p < W; ++p) {
+        const uint64_t m = __ballot((code[s] >> (W - 1 - p)) & 1u);
+        if ((c & 63) == 0) {
+          uint32_t* dst = u.vplanes + ((j * W + p) * (kDim / 32)) + 2 * half;
+          dst[0] = (uint32_t)m;
+          dst[1] = (uint32_t)(m >> 32);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 128) {
+    double e = 0.0;
+    for (int cc = 0; cc < kDim; ++cc) e = e + rv2[cc];
+    u.ev[gam] = e;
+  }
+}
+
+// grid (G, B), 128 threads: E^K[c] += rng^2 of every newly closed group,
+// in group order.
+template <int DT>
+__global__ __launch_bounds__(128) void k_ek_update(uint8_t* store, const int32_t* n_new, int n_max,
+                                                   int G, int W) {
+  constexpr int esize = DT == 0 ? 2 : 4;
+  const int g = blockIdx.x, b = blockIdx.y;
+  const ReqRecord r = req_of(store, b);
+  const int64_t n = clamp_n(r, n_new, b, n_max);
+  const int64_t first = r.len / kGroup;
+  const int64_t last = (r.len + n) / kGroup;
+  if (last == first) return;
+  const Unit u = unit_of(store, r, g, G, kDim, W, esize);
+  const int c = threadIdx.x;
+  double e = u.ek[c];
+  for (int64_t gam = first; gam < last; ++gam) {
+    const double rng = (double)bf16_to_float(u.kmeta[gam * kDim + c] >> 16);
+    e = e + rng * rng;
+  }
+  u.ek[c] = e;
+}
+
+// grid (B), 256 threads: move the still-open tokens into the tail buffer and
+// publish the new length.
+template <int DT>
+__global__ __launch_bounds__(256) void k_tail_update(uint8_t* store, const void* knew,
+                                                     const void* vnew, const int32_t* n_new,
+                                                     int n_max, int G, int W) {
+  constexpr int esize = DT == 0 ? 2 : 4;
+  const int b = blockIdx.x;
+  ReqRecord* rp = reinterpret_cast<ReqRecord*>(store + 256 + 32 * (int64_t)b);
+  const ReqRecord r = *rp;
+  const int64_t want = n_new ? (int64_t)n_new[b] : (int64_t)n_max;
+  const int64_t n = clamp_n(r, n_new, b, n_max);
+  const int64_t len1 = r.len + n;
+  const int64_t base = (len1 / kGroup) * kGroup;
+  const int64_t from = base > r.len ? base : r.len;  // older tail tokens stay in place
+  const int64_t cnt = len1 - from;
+  const int64_t per_g = cnt * kDim;
+  for (int64_t e = threadIdx.x; e < (int64_t)G * per_g; e += blockDim.x) {
+    const int g = (int)(e / per_g);
+    const int64_t rem = e - (int64_t)g * per_g;
+    const int64_t j = from + rem / kDim;
+    const int c = (int)(rem % kDim);
+    const Unit u = unit_of(store, r, g, G, kDim, W, esize);
+    const int64_t src = (((int64_t)b * G + g) * n_max + (j - r.len)) * kDim + c;
+    const int64_t dst = (j - base) * kDim + c;
+    if constexpr (DT == 0) {
+      ((uint16_t*)u.ktail)[dst] = ((const uint16_t*)knew)[src];
+      ((uint16_t*)u.vtail)[dst] = ((const uint16_t*)vnew)[src];
+    } else {
+      ((float*)u.ktail)[dst] = ((const float*)knew)[src];
+      ((float*)u.vtail)[dst] = ((const float*)vnew)[src];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    rp->len = len1;
+    if (n < want) atomicOr(&header_of(store)->flags, 2u);
+  }
+}
+
+__global__ void k_fill_zero(uint32_t* p, int64_t nwords) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nwords;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+int launch_store_zero(void* store, size_t bytes, hipStream_t st) {
+  const int64_t nw = (int64_t)(bytes / 4);
+  int blocks = (int)((nw + 255) / 256);
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_fill_zero, dim3(blocks), dim3(256), 0, st, (uint32_t*)store, nw);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+int launch_encode(const EncodeArgs& a, hipStream_t st) {
+  const int max_groups = (int)((a.n_max + kGroup - 1) / kGroup);
+  if (a.n_max <= 0) return 0;
+  if (a.dtype == 0) {
+    hipLaunchKernelGGL((k_encode_groups<0>), dim3(max_groups, a.G, a.B), dim3(256), 0, st,
+                       (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
+    hipLaunchKernelGGL((k_ek_update<0>), dim3(a.G, a.B), dim3(128), 0, st, (uint8_t*)a.store,
+                       a.n_new, a.n_max, a.G, a.W);
+    hipLaunchKernelGGL((k_tail_update<0>), dim3(a.B), dim3(256), 0, st, (uint8_t*)a.store,
+                       a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
+  } else {
+    hipLaunchKernelGGL((k_encode_groups<1>), dim3(max_groups, a.G, a.B), dim3(256), 0, st,
+                       (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
+    hipLaunchKernelGGL((k_ek_update<1>), dim3(a.G, a.B), dim3(128), 0, st, (uint8_t*)a.store,
+                       a.n_new, a.n_max, a.G, a.W);
+    hipLaunchKernelGGL((k_tail_update<1>), dim3(a.B), dim3(256), 0, st, (uint8_t*)a.store,
+                       a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // namespace readkv

@@ -1,0 +1,130 @@
+// Store and workspace layout shared by the host entry points and the kernels.
+//
+// Store = header + one region per request.  Header: 256 bytes of fields,
+// then one 32-byte record {len, cap, offset, reserved} per request,
+// rounded up to 4096 bytes.  A request region with capacity `cap` tokens
+// (multiple of 32, ng = cap/32 groups) holds, each sub-array 256-byte
+// aligned:
+//   Kplanes u32 [G][d][W][ng]      token-packed: bit i of word (g,c,p,gamma)
+//                                  is plane p of token 32*gamma+i, channel c
+//   Vplanes u32 [G][cap][W][d/32]  channel-packed: a token's t-plane prefix
+//                                  is t*d/8 contiguous bytes
+//   Kmeta   u32 [G][ng][d]         lo bf16 | rng bf16 << 16
+//   Vmeta   u32 [G][ng][d]
+//   EK      f64 [G][d]             sum over closed groups of rng_K^2
+//   EV      f64 [G][ng]            per group: sum over channels of rng_V^2
+//   Ktail   elem [G][32][d]        open group, exact input values
+//   Vtail   elem [G][32][d]
+// Plane p holds bit (W-1-p) of the code (most significant first), so a
+// depth-t read of a key channel is t whole lines and a depth-t read of a
+// value token is one contiguous run.
+#pragma once
+#include <stdint.h>
+
+#ifdef __HIPCC__
+#define RKV_HD __host__ __device__ __forceinline__
+#else
+#define RKV_HD inline
+#endif
+
+namespace readkv {
+
+constexpr uint32_t kMagic = 0x52564B31u;
+constexpr uint32_t kVersion = 1u;
+constexpr int kGroup = 32;      // tokens per quantiser group
+constexpr int kDim = 128;       // head_dim supported by the kernels
+constexpr int kKeyTile = 1024;  // tokens per score workgroup (32 groups)
+constexpr int kValChunk = 256;  // tokens per value-gather workgroup
+
+struct StoreHeader {          // first 256 bytes of a store
+  uint32_t magic, version;
+  int32_t W, d, H, G, group_tokens, B, kv_dtype;
+  uint32_t flags;
+  int64_t capacity, total_bytes;
+  int64_t reserved[25];
+};
+static_assert(sizeof(StoreHeader) == 256, "header size");
+
+struct ReqRecord {            // at byte 256 + 32*b
+  int64_t len, cap, offset, reserved;
+};
+
+RKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+RKV_HD int64_t header_bytes(int B) { return align_up(256 + 32 * (int64_t)B, 4096); }
+
+struct RegionLayout {
+  int64_t kplanes, vplanes, kmeta, vmeta, ek, ev, ktail, vtail, size;
+};
+
+RKV_HD RegionLayout region_layout(int G, int d, int W, int64_t cap, int esize) {
+  const int64_t ng = cap / kGroup;
+  RegionLayout L;
+  int64_t off = 0;
+  L.kplanes = off; off += (int64_t)G * d * W * ng * 4; off = align_up(off, 256);
+  L.vplanes = off; off += (int64_t)G * cap * W * (d / 32) * 4; off = align_up(off, 256);
+  L.kmeta = off; off += (int64_t)G * ng * d * 4; off = align_up(off, 256);
+  L.vmeta = off; off += (int64_t)G * ng * d * 4; off = align_up(off, 256);
+  L.ek = off; off += (int64_t)G * d * 8; off = align_up(off, 256);
+  L.ev = off; off += (int64_t)G * ng * 8; off = align_up(off, 256);
+  L.ktail = off; off += (int64_t)G * kGroup * d * esize; off = align_up(off, 256);
+  L.vtail = off; off += (int64_t)G * kGroup * d * esize;
+  L.size = align_up(off, 4096);
+  return L;
+}
+
+// Pointers to one (request, KV head) unit's arrays.
+struct Unit {
+  uint32_t* kplanes;   // [d][W][ng]
+  uint32_t* vplanes;   // [cap][W][d/32]
+  uint32_t* kmeta;     // [ng][d]
+  uint32_t* vmeta;     // [ng][d]
+  double* ek;          // [d]
+  double* ev;          // [ng]
+  uint8_t* ktail;      // [32][d] elements
+  uint8_t* vtail;
+  int64_t cap, ng;
+};
+
+RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int W,
+                    int esize) {
+  const RegionLayout L = region_layout(G, d, W, r.cap, esize);
+  uint8_t* base = store + r.offset;
+  const int64_t ng = r.cap / kGroup;
+  Unit u;
+  u.cap = r.cap;
+  u.ng = ng;
+  u.kplanes = (uint32_t*)(base + L.kplanes) + (int64_t)g * d * W * ng;
+  u.vplanes = (uint32_t*)(base + L.vplanes) + (int64_t)g * r.cap * W * (d / 32);
+  u.kmeta = (uint32_t*)(base + L.kmeta) + (int64_t)g * ng * d;
+  u.vmeta = (uint32_t*)(base + L.vmeta) + (int64_t)g * ng * d;
+  u.ek = (double*)(base + L.ek) + (int64_t)g * d;
+  u.ev = (double*)(base + L.ev) + (int64_t)g * ng;
+  u.ktail = base + L.ktail + (int64_t)g * kGroup * d * esize;
+  u.vtail = base + L.vtail + (int64_t)g * kGroup * d * esize;
+  return u;
+}
+
+// Decode workspace (one call).  capmax = largest request capacity.
+struct WsLayout {
+  int64_t tk, tv, logits, tilepart, ftile, aval, opart, size;
+  int ntile, nchunk;
+};
+
+RKV_HD WsLayout ws_layout(int B, int H, int G, int d, int64_t capmax) {
+  WsLayout L;
+  L.ntile = (int)((capmax + kKeyTile - 1) / kKeyTile);
+  L.nchunk = (int)((capmax + kValChunk - 1) / kValChunk);
+  int64_t off = 0;
+  L.tk = off; off = align_up(off + (int64_t)B * G * d, 256);                 // u8
+  L.tv = off; off = align_up(off + (int64_t)B * G * capmax, 256);            // u8
+  L.logits = off; off = align_up(off + (int64_t)B * H * capmax * 8, 256);    // f64
+  L.tilepart = off; off = align_up(off + (int64_t)B * H * L.ntile * 16, 256);// f64x2
+  L.ftile = off; off = align_up(off + (int64_t)B * H * L.ntile * 8, 256);   // f64
+  L.aval = off; off = align_up(off + (int64_t)B * G * capmax * 8, 256);      // f64
+  L.opart = off; off = align_up(off + (int64_t)B * H * L.nchunk * d * 4, 256); // f32
+  L.size = off;
+  return L;
+}
+
+}  // namespace readkv

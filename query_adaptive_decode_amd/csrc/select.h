@@ -1,0 +1,101 @@
+// Block-level top-k threshold search over 64-bit keys (the bit patterns of
+// non-negative doubles, which order like the doubles themselves).
+//
+// ChooseDepths ("Read What Matters", Sec. 3.3) takes the B largest positive
+// refinement gains, ties to the lowest item index.  Because every item's
+// gains strictly decrease with depth, the chosen set is exactly "every gain
+// above a threshold tau, plus the lowest-index items whose gain equals tau"
+// (App. E.2.1, Prop. 8).  tau is found by an MSB-first radix descent:
+// each pass histograms one digit of the keys that still match the chosen
+// prefix and keeps the digit where the running count from the top crosses
+// the number still to be chosen.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace readkv {
+
+// Outcome of a threshold search: a key is chosen iff it is positive and
+// (key & mask) > prefix, or (key & mask) == prefix and it is among the
+// `take_eq` lowest-index keys with that masked value (`n_eq` of them exist).
+// all_pos: every positive key is chosen.
+struct Threshold {
+  uint64_t prefix, mask;
+  uint32_t take_eq, n_eq;
+  int all_pos;
+};
+
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  const int l = __lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t t = __shfl_up(v, o, 64);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Wave 0 of the block scans NB bins (LDS) from the highest digit down and
+// finds the digit where the cumulative count reaches `rem`.  Requires the
+// total count >= rem >= 1.  Writes digit and count strictly above it.
+template <int NB>
+__device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t rem, uint32_t* out_digit,
+                                                uint32_t* out_above) {
+  constexpr int PER = NB / 64;
+  const int l = __lane_id();
+  uint32_t h[PER];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    h[i] = hist[NB - 1 - (l * PER + i)];
+    tot += h[i];
+  }
+  const uint32_t incl = wave_incl_scan_u32(tot);
+  const uint32_t excl = incl - tot;
+  const uint64_t bal = __ballot(incl >= rem);
+  const int L = __ffsll((unsigned long long)bal) - 1;
+  if (l == L) {
+    uint32_t c = excl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (c + h[i] >= rem) {
+        *out_digit = (uint32_t)(NB - 1 - (l * PER + i));
+        *out_above = c;
+        break;
+      }
+      c += h[i];
+    }
+  }
+}
+
+// Exclusive prefix sum over the threads of a block, in thread order.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum /*LDS NT/64+1*/) {
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const uint32_t incl = wave_incl_scan_u32(v);
+  if ((tid & 63) == 63) wsum[w] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0;
+    for (int i = 0; i < NT / 64; ++i) {
+      const uint32_t t = wsum[i];
+      wsum[i] = acc;
+      acc += t;
+    }
+    wsum[NT / 64] = acc;
+  }
+  __syncthreads();
+  const uint32_t r = wsum[w] + incl - v;
+  __syncthreads();
+  return r;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* wsum) {
+  const uint32_t e = block_excl_scan<NT>(v, wsum);
+  (void)e;
+  return wsum[NT / 64];  // total is left in wsum[NT/64] until the next scan
+}
+
+}  // namespace readkv

@@ -1,0 +1,112 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every declared
+symbol, and its host-only entry points validate arguments and size buffers
+as the header documents.  No GPU work is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "readkv.h")
+
+
+def _lib_or_skip():
+    from query_adaptive_decode_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libreadkv.so not built (run __graft_entry__.build())")
+    return binding
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(readkv_\w+)\(", txt, re.M)))
+
+
+def test_header_compiles_as_c():
+    src = '#include "readkv.h"\nint main(void){readkv_config c; (void)c; return 0;}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                        "-x", "c", "-", "-fsyntax-only"], input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_library_exports_every_declared_symbol():
+    b = _lib_or_skip()
+    decl = declared_functions()
+    assert set(decl) == set(b.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    syms = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in decl:
+        assert name in syms, name
+        getattr(b.lib(), name)
+
+
+def test_config_validation_codes():
+    b = _lib_or_skip()
+    ok = b.make_config(num_q_heads=32, num_kv_heads=8, batch=4, capacity_tokens=8192)
+    assert b.validate_config(ok) == 0
+    cases = {
+        -1: [dict(W=0), dict(W=9), dict(num_q_heads=30, num_kv_heads=8), dict(batch=0),
+             dict(capacity_tokens=0), dict(num_kv_heads=0)],
+        -4: [dict(kv_dtype=7)],
+        -5: [dict(head_dim=64), dict(group_tokens=16), dict(num_q_heads=80, num_kv_heads=8)],
+    }
+    for code, variants in cases.items():
+        for v in variants:
+            kw = dict(num_q_heads=32, num_kv_heads=8, batch=4, capacity_tokens=8192)
+            kw.update(v)
+            assert b.validate_config(b.make_config(**kw)) == code, v
+    assert b.lib().readkv_validate_config(None) == -1
+    assert b.lib().readkv_strerror(-2).decode() == "append larger than the store capacity"
+
+
+def test_store_size_matches_format_description():
+    b = _lib_or_skip()
+    from oracle import store_format as F
+    for (B, H, G, cap, dt) in [(1, 1, 1, 1024, 1), (16, 32, 8, 8320, 0), (3, 28, 4, 100, 0)]:
+        cfg = b.make_config(num_q_heads=H, num_kv_heads=G, batch=B, capacity_tokens=cap, kv_dtype=dt)
+        caps = [cap - 7 * i for i in range(B)]
+        for rc in (None, caps):
+            want = F.header_bytes(B)
+            for i in range(B):
+                c = cap if rc is None else rc[i]
+                c = (c + 31) // 32 * 32
+                want += F.region_layout(G, 128, 8, c, 2 if dt == 0 else 4)["_size"]
+            assert b.store_bytes(cfg, rc) == want
+    cfg = b.make_config(batch=2, capacity_tokens=64)
+    with pytest.raises(b.ReadKVError):
+        b.store_bytes(cfg, [64, 65])           # above capacity_tokens
+    assert b.workspace_bytes(cfg) > 0
+
+
+def test_entry_points_reject_bad_arguments_before_launch():
+    b = _lib_or_skip()
+    L = b.lib()
+    cfg = b.make_config(batch=2, capacity_tokens=256)
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every call below fails its host checks
+    by = ctypes.byref(cfg)
+    assert L.readkv_encode_append(by, None, fake, fake, None, 4, None) == -1
+    assert L.readkv_encode_append(by, fake, fake, fake, None, -1, None) == -1
+    assert L.readkv_encode_append(by, fake, fake, fake, None, 257, None) == -2
+    assert L.readkv_encode_append(by, fake, None, fake, None, 4, None) == -1
+    ws = b.workspace_bytes(cfg)
+    for rk, rv in [(float("nan"), 1.0), (1.0, float("inf")), (-0.5, 1.0), (1.0, -1.0)]:
+        assert L.readkv_decode_attn(by, fake, fake, rk, rv, 0, fake, fake, ws, None, None, None) == -1
+    assert L.readkv_decode_attn(by, fake, fake, 1.0, 1.0, 5, fake, fake, ws, None, None, None) == -1
+    assert L.readkv_decode_attn(by, fake, fake, 1.0, 1.0, 0, fake, fake, ws - 1, None, None, None) == -3
+    assert L.readkv_decode_attn(by, None, fake, 1.0, 1.0, 0, fake, fake, ws, None, None, None) == -1
+    assert L.readkv_store_init(by, fake, 16, None, None) == -3
+    bad = b.make_config(batch=2, capacity_tokens=256, head_dim=64)
+    assert L.readkv_decode_attn(ctypes.byref(bad), fake, fake, 1.0, 1.0, 0, fake, fake, ws, None, None,
+                                None) == -5
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from query_adaptive_decode_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

@@ -1,0 +1,215 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64
+oracle on the same seeded inputs.
+
+* store bytes written by the device encoder == the oracle's encoding packed
+  by the format description (bit-exact; energies exact because both sides
+  sum in the documented order);
+* key depths equal to the oracle's (weights are bit-identical);
+* value depths equal up to logged near ties (see parity_util);
+* outputs within 2e-3 relative L2 per (request, query head).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import store_format as F
+from query_adaptive_decode_amd import synth, workload
+from query_adaptive_decode_amd.binding import ReadKVCache, VSCALE_PHYSICAL, VSCALE_UNIT
+from tests.parity_util import OUT_REL_L2, alloc_mismatch, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    from query_adaptive_decode_amd import binding
+    binding.lib()   # raises if the library was not built
+
+
+class Run:
+    """Prefill + `steps` (append, decode) rounds on the GPU, keeping every
+    decode's outputs and depth schedules on the host."""
+
+    def __init__(self, cfg, steps, rates, vscale=VSCALE_PHYSICAL, repeat=False):
+        self.cfg, self.steps, self.rates, self.vscale = cfg, steps, rates, vscale
+        B, H, G = cfg["B"], cfg["H"], cfg["G"]
+        say(f"[case] {cfg['name']} B={B} H={H} G={G} T0={synth.context_lengths(cfg).tolist()[:4]}"
+            f" steps={steps} rates={rates} vscale={vscale}")
+        h = workload.host_inputs(cfg, steps)
+        dv = workload.to_device(h)
+        self.lcfg = workload.config_for(cfg, steps)
+        cap = self.lcfg.capacity_tokens
+        cache = ReadKVCache(self.lcfg)
+        cache.append(dv["kpre"], dv["vpre"], n_new=dv["npre"].to(torch.int32),
+                     n_max=dv["kpre"].shape[2])
+        self.rec = []
+        for s in range(steps):
+            cache.append(dv["kstep"][s], dv["vstep"][s])
+            for (rk, rv) in rates:
+                tk = torch.zeros(B * G * 128, dtype=torch.uint8, device="cuda")
+                tv = torch.zeros(B * G * ((cap + 31) // 32 * 32), dtype=torch.uint8, device="cuda")
+                out = cache.decode(dv["q"][s], rk, rv, vscale=vscale, key_depths=tk, value_depths=tv)
+                item = dict(step=s, rk=rk, rv=rv, out=out.cpu().numpy(),
+                            tk=tk.cpu().numpy().reshape(B, G, 128),
+                            tv=tv.cpu().numpy().reshape(B, G, -1))
+                if repeat:
+                    out2 = cache.decode(dv["q"][s], rk, rv, vscale=vscale, key_depths=tk, value_depths=tv)
+                    item["out2"] = out2.cpu().numpy()
+                    item["tv2"] = tv.cpu().numpy().reshape(B, G, -1)
+                self.rec.append(item)
+        torch.cuda.synchronize()
+        self.flags, self.lens = cache.status()
+        self.store = cache.store.cpu().numpy()
+        say(f"[gpu done] flags={self.flags} lens={self.lens[:4]}")
+        self._units = {}
+
+    def unit(self, b, g):
+        if (b, g) not in self._units:
+            T0 = int(synth.context_lengths(self.cfg)[b])
+            self._units[(b, g)] = synth.kv_unit(self.cfg, b, g, T0 + self.steps)
+        return self._units[(b, g)]
+
+    def check(self, units=None, steps=None):
+        cfg = self.cfg
+        G, H = cfg["G"], cfg["H"]
+        gqa = H // G
+        units = units or [(b, g) for b in range(cfg["B"]) for g in range(G)]
+        near_total = 0
+        worst = 0.0
+        for it in self.rec:
+            if steps is not None and it["step"] not in steps:
+                continue
+            for (b, g) in units:
+                T0 = int(synth.context_lengths(cfg)[b])
+                n = T0 + it["step"] + 1
+                K, V = self.unit(b, g)
+                q = synth.q_step(cfg, b, it["step"])[g * gqa:(g + 1) * gqa]
+                res = O.decode_unit(q, K[:n], V[:n], W=cfg["W"], R_K=it["rk"], R_V=it["rv"],
+                                    vscale="unit" if self.vscale == VSCALE_UNIT else "physical")
+                tag = f"step={it['step']} R=({it['rk']},{it['rv']}) unit=({b},{g}) n={n}"
+                assert np.array_equal(it["tk"][b, g], res["tK"]), f"key depths differ {tag}"
+                tp = res["tp"]
+                near, bad, det = alloc_mismatch(it["tv"][b, g, :tp], res["tV"], res["wv"], cfg["W"])
+                assert bad == 0, f"value depths differ {tag}: {det}"
+                near_total += near
+                err = rel_l2(it["out"][b, g * gqa:(g + 1) * gqa], res["out"])
+                worst = max(worst, float(err.max()))
+                assert np.all(err <= OUT_REL_L2), f"output rel L2 {err.max():.3e} {tag}"
+                if "out2" in it:
+                    assert np.array_equal(it["out"], it["out2"]) and np.array_equal(it["tv"], it["tv2"])
+        say(f"[parity] {cfg['name']}: near ties {near_total}, worst rel L2 {worst:.3e}")
+        return worst
+
+    def check_store(self, units=None):
+        cfg = self.cfg
+        hdr = F.read_header(self.store)
+        assert hdr["magic"] == F.MAGIC and hdr["flags"] == 0
+        units = units or [(b, g) for b in range(cfg["B"]) for g in range(cfg["G"])]
+        for (b, g) in units:
+            T0 = int(synth.context_lengths(cfg)[b])
+            n = T0 + self.steps
+            assert hdr["requests"][b]["len"] == n
+            K, V = self.unit(b, g)
+            ek, ev = O.encode_stream(K[:n]), O.encode_stream(V[:n])
+            cap = hdr["requests"][b]["cap"]
+            want = F.pack_unit(ek, ev, cap, cfg["dtype"])
+            got = F.unpack_unit(self.store, hdr, b, g)
+            ngc, tp, r = ek.n_groups, ek.t_packed, n - ek.t_packed
+            tag = f"unit=({b},{g}) n={n}"
+            assert np.array_equal(got["Kplanes"][:, :, :ngc], want["Kplanes"][:, :, :ngc]), tag
+            assert np.array_equal(got["Vplanes"][:tp], want["Vplanes"][:tp]), tag
+            assert np.array_equal(got["Kmeta"][:ngc], want["Kmeta"][:ngc]), tag
+            assert np.array_equal(got["Vmeta"][:ngc], want["Vmeta"][:ngc]), tag
+            assert np.array_equal(got["EK"], want["EK"]), tag
+            assert np.array_equal(got["EV"][:ngc], want["EV"][:ngc]), tag
+            assert np.array_equal(got["Ktail"][:r], want["Ktail"][:r]), tag
+            assert np.array_equal(got["Vtail"][:r], want["Vtail"][:r]), tag
+        say(f"[store] {cfg['name']}: {len(units)} units bit-exact")
+
+
+def test_tiny_fp32_full_workload():
+    cfg = synth.workload(1)
+    run = Run(cfg, steps=16, rates=[(4.0, 4.0), (2.0, 2.0)], repeat=True)
+    run.check_store()
+    run.check()
+
+
+def test_llama_shape_small_context():
+    cfg = synth.workload(2, B=2, T0=2000)
+    run = Run(cfg, steps=3, rates=[(4.0, 4.0), (2.0, 2.0), (3.3, 2.7)])
+    run.check_store()
+    run.check()
+
+
+def test_gqa7_ragged_batch():
+    cfg = synth.workload(4, B=3, T0=(40, 1500))
+    run = Run(cfg, steps=2, rates=[(6.0, 6.0), (2.0, 2.0), (3.5, 2.5)])
+    run.check_store()
+    run.check()
+
+
+def test_peaky_needles_unit_scale():
+    cfg = synth.workload(3, B=1, T0=3000)
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 2.0)], vscale=VSCALE_UNIT)
+    run.check()
+
+
+@pytest.mark.parametrize("T0", [5, 31, 32, 33, 1023, 1025, 2047])
+def test_ragged_tails_and_tiles(T0):
+    cfg = synth.workload(2, B=1, H=8, G=2, T0=T0)
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (0.0, 0.0), (8.0, 8.0), (100.0, 0.5), (0.25, 100.0)])
+    run.check_store()
+    run.check()
+
+
+def test_full_size_llama_layer_sampled_units():
+    # the benchmark's configuration (B=16, 32/8 heads, T0=8192) with the
+    # oracle run on a sample of (request, KV head) units
+    cfg = synth.workload(2)
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 2.0)])
+    units = [(0, 0), (5, 3), (11, 6), (15, 7)]
+    run.check_store(units)
+    run.check(units)
+
+
+def test_nonfinite_input_sets_flag():
+    cfg = synth.workload(2, B=1, H=4, G=1, T0=64)
+    lcfg = workload.config_for(cfg, 0)
+    h = workload.host_inputs(cfg, 0)
+    k = h["kpre"].copy()
+    k[0, 0, 40, 3] = 0x7FC0          # bf16 NaN in group 1
+    say("[case] nonfinite flag")
+    dv = workload.to_device(dict(k=k, v=h["vpre"]))
+    cache = ReadKVCache(lcfg)
+    cache.append(dv["k"], dv["v"])
+    torch.cuda.synchronize()
+    flags, lens = cache.status()
+    assert flags & 1 and lens == [64]
+    hdr = F.read_header(cache.store.cpu().numpy())
+    got = F.unpack_unit(cache.store.cpu().numpy(), hdr, 0, 0)
+    assert np.all(got["Kmeta"][1] == 0) and np.all(got["Kmeta"][0] != 0)
+
+
+def test_append_past_capacity_sets_flag_and_clamps():
+    cfg = synth.workload(2, B=1, H=4, G=1, T0=60)
+    lcfg = workload.config_for(cfg, 0)   # capacity 64 (60 rounded up)
+    h = workload.host_inputs(cfg, 0)
+    say("[case] capacity overflow")
+    dv = workload.to_device(h)
+    cache = ReadKVCache(lcfg)
+    cache.append(dv["kpre"], dv["vpre"])
+    cache.append(dv["kpre"][:, :, :8].contiguous(), dv["vpre"][:, :, :8].contiguous())
+    torch.cuda.synchronize()
+    flags, lens = cache.status()
+    assert flags & 2 and lens == [64]
