@@ -161,6 +161,18 @@ def cpu_baseline(cfg, budget_s=12.0):
                        f"T={ctx}, (W,R)=(8,4), float64 numpy single thread, {t_all:.1f} s")
 
 
+def copy_probe(torch, mib=512, reps=3):
+    """A plain device-to-device copy of a known size: its FETCH_SIZE /
+    WRITE_SIZE counter readings give the scale from counter units to bytes."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"# copy probe: {reps} copies of {mib} MiB", file=sys.stderr, flush=True)
+    del src, dst
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +181,8 @@ def main():
     ap.add_argument("--rates", default="4,2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only: the decode path has no "
@@ -179,6 +193,8 @@ def main():
 
     cfg = synth.workload(2)
     rates = [float(r) for r in args.rates.split(",")]
+    if args.copy_probe:
+        copy_probe(torch)
     total_steps = args.warmup + 2 * args.steps
     t = time.perf_counter()
     hin = workload.host_inputs(cfg, total_steps)
