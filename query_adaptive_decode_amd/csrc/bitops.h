@@ -76,6 +76,43 @@ RKV_HDI uint64_t transpose8(uint64_t x) {
   return x;
 }
 
+// transpose8 on the two 32-bit halves of x (lo = bits 0..31, hi = 32..63),
+// the form the kernels use: the first two exchange stages stay inside each
+// half, the last one crosses them through a 64-bit funnel shift.
+RKV_HDI void transpose8_halves(uint32_t& lo, uint32_t& hi) {
+  uint32_t t;
+  t = (lo ^ (lo >> 7)) & 0x00AA00AAu;
+  lo ^= t ^ (t << 7);
+  t = (hi ^ (hi >> 7)) & 0x00AA00AAu;
+  hi ^= t ^ (t << 7);
+  t = (lo ^ (lo >> 14)) & 0x0000CCCCu;
+  lo ^= t ^ (t << 14);
+  t = (hi ^ (hi >> 14)) & 0x0000CCCCu;
+  hi ^= t ^ (t << 14);
+  const uint32_t fun = (uint32_t)(((((uint64_t)hi) << 32) | lo) >> 28);
+  t = (lo ^ fun) & 0xF0F0F0F0u;
+  lo ^= t;
+  hi ^= t >> 4;
+}
+
+// Byte permute with the semantics of the gfx950 v_perm_b32 instruction:
+// byte i of the result is byte sel_i of the 8-byte value {a (bytes 4..7),
+// b (bytes 0..3)}; selector 0x0C gives 0x00.  (Host model for tests; the
+// kernels call the instruction.)
+RKV_HDI uint32_t perm_bytes(uint32_t a, uint32_t b, uint32_t sel) {
+  const uint64_t v = ((uint64_t)a << 32) | b;
+  uint32_t r = 0;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t s = (sel >> (8 * i)) & 0xFFu;
+    uint32_t byte = 0;
+    if (s < 8) byte = (uint32_t)(v >> (8 * s)) & 0xFFu;
+    else if (s == 0x0C) byte = 0;
+    else if (s >= 0x0D) byte = 0xFF;
+    r |= byte << (8 * i);
+  }
+  return r;
+}
+
 // Un-plane: `planes` holds plane p (bit i = element i) in byte 7-p.  The
 // result's byte i is element i's code prefix with plane p at bit 7-p
 // (missing planes are zero), i.e. X = P * 2^(8-t) for a depth-t prefix P.

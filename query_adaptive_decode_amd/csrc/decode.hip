@@ -1,25 +1,27 @@
 // One ReadKV decode step ("Read What Matters: Query-Adaptive Quantization
 // for KV Caches", Sec. 3.2-3.3, Algorithm 1) as five launches on one stream:
 //
-//   k_key_alloc   (B*G blocks)        key weights (Eq. (2)) and ChooseDepths
+//   k_key_alloc   (B*G waves)         key weights (Eq. (2)) and ChooseDepths
 //                                     over the d_h channels -> t^K
-//   k_score       (tiles x G x B)     prefix-gather of the chosen key planes,
-//                                     reconstructed logits, per-tile max and
-//                                     sum of exp (split-context softmax)
+//   k_score       (B*G x tiles)       prefix-gather of the chosen key planes
+//                                     through LDS, reconstructed logits in
+//                                     fp64, per-tile max and sum of exp
+//                                     (split-context softmax)
 //   k_value_alloc (B*G blocks)        softmax statistics, value weights
 //                                     (Eq. (3)) and ChooseDepths over the
 //                                     packed tokens -> t^V
-//   k_gather      (chunks x G x B)    prefix-gather of the chosen value planes
-//                                     and attention-weighted sum per chunk
-//   k_out_reduce  (B*H blocks)        fixed-order sum of the chunk partials
+//   k_gather      (B*G x chunks)      prefix-gather of the chosen value
+//                                     planes, attention-weighted sums per
+//                                     chunk
+//   k_out_reduce  (B*H*d threads)     chunk partials summed in chunk order
 //
 // The k_value_alloc -> k_gather boundary is the staged(2) reader's second
 // batch: value reads depend on attention computed from the first batch.
 //
 // Reconstruction of a depth-t prefix P (t MSB-first planes) of a group with
-// metadata (lo, rng): x_hat = lo + rng * (2P + 1) / 2^(t+1).  The kernels
-// un-plane an 8-element byte column into X = P * 2^(8-t) (missing planes
-// read as zero) and use x_hat = lo + rng * (2X + 2^(8-t)) / 512.
+// metadata (lo, rng): x_hat = lo + rng (2P + 1) / 2^(t+1).  The kernels
+// un-plane an 8-element bit column into X = P 2^(8-t) (missing planes read
+// as zero) and use x_hat = lo + rng 2^-(t+1) + rng X / 256.
 #include <math.h>
 
 #include "kernels_common.h"
@@ -28,204 +30,404 @@
 
 namespace readkv {
 
-// ---------------------------------------------------------------------------
-// Key allocation: one block of 256 threads per (request, KV head).  Thread
-// 2c+h holds the gains of channel c at levels 4h+1 .. 4h+4.
-// ---------------------------------------------------------------------------
-template <int DT>
-__global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
-                                                   int W, float RK, uint8_t* tk) {
-  constexpr int NT = 256;
-  constexpr int esize = DT == 0 ? 2 : 4;
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const int gqa = H / G;
-  const ReqRecord r = req_of(store, b);
-  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const int tid = threadIdx.x;
-  const int c = tid >> 1, half = tid & 1;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t wsum[NT / 64 + 1];
-  __shared__ uint32_t sh[2];
+constexpr double kInvSqrtD = 0.088388347648318440550;  // 1/sqrt(128)
 
-  // key weight, Eq. (2): (sum_h q_hc^2) * (sum over groups of rng_c^2)
-  double qsq = 0.0;
-  for (int hh = 0; hh < gqa; ++hh) {
-    const double qv = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * gqa + hh) * kDim + c);
-    qsq = qsq + qv * qv;
-  }
-  const double w = qsq * u.ek[c];
-  uint64_t key[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int t = half * 4 + m + 1;
-    key[m] = (t <= W) ? dbits(w * ldexp_pow2(-2 * t)) : 0ull;
-  }
-  const uint32_t k = (uint32_t)floor((double)RK * (double)kDim);
+// byte `ob` of each of 8 plane words (plane p -> byte 7-p of hi:lo), then
+// the 8x8 bit transpose: byte i of hi:lo becomes element 8*ob+i's code
+// prefix, MSB-first (missing planes must be passed as zero words)
+__device__ __forceinline__ void unplane8(const uint32_t (&w)[8], uint32_t sel, uint32_t& lo,
+                                         uint32_t& hi) {
+  const uint32_t r01 = __builtin_amdgcn_perm(w[0], w[1], sel);
+  const uint32_t r23 = __builtin_amdgcn_perm(w[2], w[3], sel);
+  const uint32_t r45 = __builtin_amdgcn_perm(w[4], w[5], sel);
+  const uint32_t r67 = __builtin_amdgcn_perm(w[6], w[7], sel);
+  hi = __builtin_amdgcn_perm(r01, r23, 0x05040100u);
+  lo = __builtin_amdgcn_perm(r45, r67, 0x05040100u);
+  transpose8_halves(lo, hi);
+}
 
-  // ---- threshold search (8 passes of 8 bits) ----
-  uint32_t npos_l = 0;
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) npos_l += key[m] > 0;
-  block_excl_scan<NT>(npos_l, wsum);
-  const uint32_t npos = wsum[NT / 64];
-  __syncthreads();
-  uint64_t prefix = 0, mask = 0;
-  uint32_t rem = k, n_eq = 0;
-  const bool all_pos = npos <= k;
-  if (!all_pos && k > 0) {
-    for (int pass = 0; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
-      hist[tid] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        if (key[m] > 0 && (key[m] & mask) == prefix)
-          atomicAdd(&hist[(uint32_t)(key[m] >> shift) & 255u], 1u);
-      __syncthreads();
-      if (tid < 64) wave_find_digit<256>(hist, rem, &sh[0], &sh[1]);
-      __syncthreads();
-      const uint32_t d = sh[0];
-      const uint32_t cnt = hist[d];
-      rem -= sh[1];
-      prefix |= (uint64_t)d << shift;
-      mask |= 0xFFull << shift;
-      n_eq = cnt;
-      __syncthreads();
-      if (cnt == rem) break;
-    }
-  }
-  // ---- count chosen levels ----
-  uint32_t sel = 0, tie = 0;
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    if (key[m] == 0) continue;
-    if (all_pos) { ++sel; continue; }
-    if (k == 0) continue;
-    const uint64_t km = key[m] & mask;
-    if (km > prefix) ++sel;
-    else if (km == prefix) ++tie;
-  }
-  if (!all_pos && k > 0 && rem < n_eq) {
-    // ties resolved toward the lowest channel (thread order = channel order)
-    const uint32_t before = block_excl_scan<NT>(tie, wsum);
-    if (tie && before < rem) ++sel;
-  } else {
-    sel += tie;
-  }
-  sel += __shfl_xor(sel, 1, 64);
-  if (half == 0) tk[((int64_t)b * G + g) * kDim + c] = (uint8_t)sel;
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 // ---------------------------------------------------------------------------
-// Score: block of 128 threads per 1024-token tile of one (request, KV head).
-// Thread (gs, k) = (tid/4, tid%4) owns tokens 8k..8k+7 of group gs of the
-// tile and loops over the channels with t^K_c > 0.  Logits are fp64:
-//   s_hj = [ sum_c q_hc (lo + rng 2^-(t_c+1)) + sum_c (q_hc rng / 256) X_jc ] / sqrt(d)
-// The block writes e_hj = exp(s_hj - m_tile) and (m_tile, sum_j e_hj).
+// Key allocation: one wave per (request, KV head).  Lane l holds channels l
+// and l+64 and their W candidate gains w_c 4^-t (t = 1..W).  The B_K largest
+// positive gains are chosen, ties to the lowest channel (App. E.2.1: with
+// strictly decreasing per-item gains this is ChooseDepths' result).  The
+// threshold is found in two steps on the 64-bit patterns of the fp64 gains:
+// bisection on the 12-bit sign+exponent field, then an exact rank among the
+// candidates in the threshold's exponent class.
 // ---------------------------------------------------------------------------
-template <int GQA, int DT>
-__global__ __launch_bounds__(128) void k_score(const uint8_t* store, const void* q, const uint8_t* tk,
-                                               int H, int G, int W, int64_t capmax, int ntile_ws,
-                                               double* ebuf, double* tilepart) {
+template <int DT>
+__global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
+                                                  int W, float RK, uint8_t* tk) {
   constexpr int esize = DT == 0 ? 2 : 4;
-  const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int unit = blockIdx.x;
+  const int b = unit / G, g = unit - b * G;
+  const int gqa = H / G;
+  const ReqRecord r = req_of(store, b);
+  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
+  const int lane = threadIdx.x;
+  __shared__ uint64_t ck[2 * 64 * 8];
+  __shared__ uint32_t cc[2 * 64 * 8];
+
+  uint64_t key[2][8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    double qsq = 0.0;
+    for (int hh = 0; hh < gqa; ++hh) {
+      const double qv = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * gqa + hh) * kDim + c);
+      qsq = __dadd_rn(qsq, __dmul_rn(qv, qv));
+    }
+    const double w = __dmul_rn(qsq, u.ek[c]);
+#pragma unroll
+    for (int t = 1; t <= 8; ++t) {
+      const double gt = __dmul_rn(w, ldexp_pow2(-2 * t));
+      key[k][t - 1] = (t <= W && gt > 0.0) ? dbits(gt) : 0ull;
+    }
+  }
+  const uint32_t Bk = (uint32_t)floor((double)RK * (double)kDim);
+  uint32_t np = 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) np += key[k][t] != 0ull;
+  const uint32_t npos = wave_sum_u32(np);
+
+  uint32_t sel[2] = {0u, 0u};
+  if (npos <= Bk) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sel[k] += key[k][t] != 0ull;
+  } else if (Bk > 0) {
+    // largest exponent class E with count(key >> 52 >= E) >= Bk
+    int lo = 0, hi = 2047;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      uint32_t c_ = 0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) c_ += key[k][t] != 0ull && (int)(key[k][t] >> 52) >= mid;
+      if (wave_sum_u32(c_) >= Bk) lo = mid;
+      else hi = mid - 1;
+    }
+    const int Es = lo;
+    uint32_t ab = 0, at = 0;
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const int e = (int)(key[k][t] >> 52);
+        ab += key[k][t] != 0ull && e > Es;
+        at += key[k][t] != 0ull && e == Es;
+      }
+    const uint32_t above = wave_sum_u32(ab);
+    const uint32_t rem = Bk - above;  // >= 1 by the choice of Es
+    // candidates in class Es: with normal gains at most one level per
+    // channel; lane slot k holds channel lane + 64 k
+    uint32_t atc[2] = {0u, 0u};
+    uint64_t atm[2] = {0ull, 0ull};
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        if (key[k][t] != 0ull && (int)(key[k][t] >> 52) == Es) {
+          ++atc[k];
+          atm[k] = key[k][t] & 0x000FFFFFFFFFFFFFull;
+        }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) sel[k] += key[k][t] != 0ull && (int)(key[k][t] >> 52) > Es;
+    if (!__any(atc[0] > 1u || atc[1] > 1u)) {
+      // MSB-first search for the rem-th largest mantissa in the class
+      uint64_t pre = 0ull;
+      uint32_t rm = rem;
+      for (int bit = 51; bit >= 0; --bit) {
+        const uint64_t hi_mask = ~((2ull << bit) - 1ull);  // bits above `bit`
+        const bool f0 = atc[0] && ((atm[0] ^ pre) & hi_mask) == 0ull && ((atm[0] >> bit) & 1ull);
+        const bool f1 = atc[1] && ((atm[1] ^ pre) & hi_mask) == 0ull && ((atm[1] >> bit) & 1ull);
+        const uint32_t c1 = (uint32_t)(__popcll(__ballot(f0)) + __popcll(__ballot(f1)));
+        if (c1 >= rm) pre |= 1ull << bit;
+        else rm -= c1;
+      }
+      // above the threshold mantissa: taken; equal: the first rm in channel order
+      const bool e0 = atc[0] && atm[0] == pre, e1 = atc[1] && atm[1] == pre;
+      const uint64_t b0 = __ballot(e0), b1 = __ballot(e1);
+      const uint64_t below = (1ull << lane) - 1ull;
+      if (atc[0] && atm[0] > pre) ++sel[0];
+      if (atc[1] && atm[1] > pre) ++sel[1];
+      if (e0 && (uint32_t)__popcll(b0 & below) < rm) ++sel[0];
+      if (e1 && (uint32_t)(__popcll(b0) + __popcll(b1 & below)) < rm) ++sel[1];
+    } else {
+      // several levels of one channel in the class (subnormal gains): rank
+      // every class member against the compacted list
+      const uint32_t incl = wave_incl_scan_u32(at);
+      const uint32_t nat = __shfl(incl, 63, 64);
+      uint32_t pos = incl - at;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+          if (key[k][t] != 0ull && (int)(key[k][t] >> 52) == Es) {
+            ck[pos] = key[k][t];
+            cc[pos] = (uint32_t)(lane + 64 * k);
+            ++pos;
+          }
+      __syncthreads();
+      for (int k = 0; k < 2; ++k) {
+        const uint32_t c = (uint32_t)(lane + 64 * k);
+        for (int t = 0; t < 8; ++t) {
+          const uint64_t kk = key[k][t];
+          if (kk == 0ull || (int)(kk >> 52) != Es) continue;
+          uint32_t beats = 0;
+          for (uint32_t m = 0; m < nat; ++m) {
+            const uint64_t k2 = ck[m];
+            beats += (k2 > kk) || (k2 == kk && cc[m] < c);
+          }
+          if (beats < rem) ++sel[k];
+        }
+      }
+    }
+  }
+  tk[(int64_t)unit * kDim + lane] = (uint8_t)sel[0];
+  tk[(int64_t)unit * kDim + lane + 64] = (uint8_t)sel[1];
+}
+
+// ---------------------------------------------------------------------------
+// Score: one block of 256 threads per 512-token tile (16 groups) of one
+// (request, KV head).
+//  1. Stage in LDS the tile's segment of every chosen key line (channel c,
+//     plane p < t^K_c): 16 words = 64 B per line, loaded as 16 B pieces, and
+//     the tile's key metadata.  LDS layout planes[group][slot], slot =
+//     (sum over channels below c of t^K) + p.
+//  2. Per-group constants
+//       C_h = sum_c q_hc (lo_c + rng_c 2^-(t_c+1)) - 4096 sum_{t_c>0} beta_hc
+//     with beta_hc = q_hc rng_c / 256 (exact products of bf16 values).
+//  3. Wave w takes channels w, w+4, ... (so a channel's depth t is uniform
+//     in the wave), lane o its 8 tokens 8o..8o+7 of the tile.  Per channel
+//     the lane gathers byte o%4 of its group's t plane words, transposes the
+//     8x8 bit block into the tokens' prefix codes X and accumulates
+//     beta_hc (4096 + X) in fp64; 4096 + X is assembled as a double straight
+//     from the code byte (one byte permute), the 4096 part cancels against C.
+//  4. The four waves' sums are added in wave order through LDS; logits
+//     s = (C + sum) / sqrt(d); open-group tokens use exact keys.  Each thread
+//     finishes two tokens: e = exp(s - m_tile) (fp64, and rounded to fp16 for
+//     the value gather) and the block writes (m_tile, sum e) per head.
+// Grid (unit, tile): consecutive blocks are different units, so all tiles
+// of a unit run on one XCD and share its L2 (a 128 B line holds two tiles'
+// 64 B segments of a key line).
+// Dynamic LDS: max(16 * (max slots | 1) words, the 64 x 8 x GQA fp64 wave
+// reduction buffer).
+// ---------------------------------------------------------------------------
+// transpose8_halves for lo == 0 (at most 4 planes present)
+__device__ __forceinline__ void transpose8_hi4(uint32_t& lo, uint32_t& hi) {
+  uint32_t t;
+  t = (hi ^ (hi >> 7)) & 0x00AA00AAu;
+  hi ^= t ^ (t << 7);
+  t = (hi ^ (hi >> 14)) & 0x0000CCCCu;
+  hi ^= t ^ (t << 14);
+  t = (hi << 4) & 0xF0F0F0F0u;
+  lo = t;
+  hi ^= t >> 4;
+}
+
+// the double 4096 + (byte i of y), built from its bit pattern
+__device__ __forceinline__ double code_plus_4096(uint32_t y, int i) {
+  const uint32_t hi = __builtin_amdgcn_perm(0x40B00000u, y, 0x0706000Cu | ((uint32_t)i << 8));
+  return __hiloint2double((int)hi, 0);
+}
+
+template <int GQA, int DT>
+__global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void* q, const uint8_t* tk,
+                                               int H, int G, int W, int64_t capmax, int ntile_ws,
+                                               double* ebuf, _Float16* e16, double* tilepart) {
+  constexpr int esize = DT == 0 ? 2 : 4;
+  constexpr int NG = kTile / kGroup;  // 16
+  extern __shared__ uint32_t planes[];
+  __shared__ double qs[GQA][kDim];
+  __shared__ uint32_t meta[NG][kDim];
+  __shared__ double Cs[NG][GQA];
+  __shared__ double tails[kGroup][GQA];
+  __shared__ double red[4][GQA];
+  __shared__ uint16_t offs[kDim + 1];
+  __shared__ uint8_t tks[kDim];
+  __shared__ uint8_t s2c[kDim * 8];
+  __shared__ uint32_t wtot[2];
+
+  const int tile = blockIdx.y, b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
-  const int64_t t0 = (int64_t)tile * kKeyTile;
+  const int64_t t0 = (int64_t)tile * kTile;
   if (t0 >= len) return;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t gam0 = t0 / kGroup;
+  int64_t ngp64 = Tp / kGroup - gam0;
+  const int ngp = (int)(ngp64 < 0 ? 0 : (ngp64 > NG ? NG : ngp64));  // packed groups in tile
 
-  __shared__ double qs[GQA][kDim];
-  __shared__ uint8_t ts[kDim];
-  __shared__ uint8_t act[kDim];
-  __shared__ int nact_s[2];
-  __shared__ double red[2][GQA];
-
-  for (int hh = 0; hh < GQA; ++hh)
-    qs[hh][tid] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + tid);
-  const uint8_t tc = tk[((int64_t)b * G + g) * kDim + tid];
-  ts[tid] = tc;
-  {
-    const uint64_t bal = __ballot(tc > 0);
-    const int lane = tid & 63, w = tid >> 6;
-    const uint32_t rank = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) nact_s[w] = __popcll(bal);
-    __syncthreads();
-    if (tc > 0) act[rank + (w ? nact_s[0] : 0)] = (uint8_t)tid;
+  for (int i = tid; i < GQA * kDim; i += 256)
+    qs[i / kDim][i % kDim] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA) * kDim + i);
+  if (tid < kDim) tks[tid] = tk[((int64_t)b * G + g) * kDim + tid];
+  for (int i = tid; i < NG * kDim; i += 256) {
+    const int gl = i / kDim, c = i % kDim;
+    meta[gl][c] = (gl < ngp) ? u.kmeta[(gam0 + gl) * kDim + c] : 0u;
   }
   __syncthreads();
-  const int nact = nact_s[0] + nact_s[1];
-  const double inv_sqrt_d = 0.088388347648318440550;  // 1/sqrt(128)
+  uint32_t tv_ = 0, inc = 0;
+  if (tid < kDim) {
+    tv_ = tks[tid];
+    inc = wave_incl_scan_u32(tv_);
+    if (lane == 63) wtot[wv] = inc;
+  }
+  __syncthreads();
+  if (tid < kDim) {
+    if (wv == 1) inc += wtot[0];
+    offs[tid + 1] = (uint16_t)inc;
+    if (tid == 0) offs[0] = 0;
+    const uint32_t o = inc - tv_;
+    for (uint32_t p = 0; p < tv_; ++p) s2c[o + p] = (uint8_t)tid;
+  }
+  __syncthreads();
+  const int ns = offs[kDim];
+  const int nsp = ns | 1;
 
-  const int gs = tid >> 2, k = tid & 3;
-  const int64_t gam = (int64_t)tile * (kKeyTile / kGroup) + gs;
-  const bool packed = (gam + 1) * kGroup <= Tp;
-  double sv[8][GQA];
-
-  if (packed) {
-    double C[GQA];
+  // ---- 1. stage key plane segments: (slot, quad) -> 16 B global loads ----
+  {
+    const int nq = ns * 4;
+    const uint32_t* kpl = u.kplanes;
+    for (int base = 0; base < nq; base += 256 * 8) {
+      uint4 v[8];
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) C[hh] = 0.0;
-    for (int c = k; c < kDim; c += 4) {
-      const uint32_t m = u.kmeta[gam * kDim + c];
-      const double lo = (double)bf16_to_float(m & 0xFFFFu);
-      const double rng = (double)bf16_to_float(m >> 16);
-      const double base = lo + rng * ldexp_pow2(-(int)ts[c] - 1);
+      for (int k = 0; k < 8; ++k) {
+        const int idx = base + k * 256 + tid;
+        v[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (idx < nq) {
+          const int s = idx >> 2, q4 = idx & 3;
+          const int c = s2c[s];
+          const int p = s - offs[c];
+          if (4 * q4 < ngp)
+            v[k] = *reinterpret_cast<const uint4*>(kpl + ((int64_t)c * W + p) * u.ngk + gam0 + 4 * q4);
+        }
+      }
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) C[hh] = fma(qs[hh][c], base, C[hh]);
+      for (int k = 0; k < 8; ++k) {
+        const int idx = base + k * 256 + tid;
+        if (idx < nq) {
+          const int s = idx >> 2, q4 = idx & 3;
+          planes[(4 * q4 + 0) * nsp + s] = v[k].x;
+          planes[(4 * q4 + 1) * nsp + s] = v[k].y;
+          planes[(4 * q4 + 2) * nsp + s] = v[k].z;
+          planes[(4 * q4 + 3) * nsp + s] = v[k].w;
+        }
+      }
+    }
+  }
+  // ---- 2. per-group constants ----
+  {
+    const int gl = tid >> 4, cs = tid & 15;
+    double ca[GQA];
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) ca[hh] = 0.0;
+    if (gl < ngp) {
+      for (int k = 0; k < kDim / 16; ++k) {
+        const int c = cs + 16 * k;
+        const uint32_t m = meta[gl][c];
+        const int t = tks[c];
+        const double lo = (double)bf16_to_float(m & 0xFFFFu);
+        const double rng = (double)bf16_to_float(m >> 16);
+        const double base = lo + rng * ldexp_pow2(-t - 1) - (t > 0 ? 16.0 * rng : 0.0);
+#pragma unroll
+        for (int hh = 0; hh < GQA; ++hh) ca[hh] = fma(qs[hh][c], base, ca[hh]);
+      }
     }
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
-      C[hh] += __shfl_xor(C[hh], 1, 64);
-      C[hh] += __shfl_xor(C[hh], 2, 64);
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) ca[hh] += __shfl_xor(ca[hh], o, 64);
     }
-    double acc[8][GQA];
+    if (cs == 0)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int hh = 0; hh < GQA; ++hh) Cs[gl][hh] = ca[hh];
+  }
+  __syncthreads();
+
+  // ---- 3. un-plane and accumulate: wave wv, channels wv, wv+4, ... ----
+  double acc[8][GQA];
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) acc[i][hh] = 0.0;
-    for (int ai = 0; ai < nact; ++ai) {
-      const int c = act[ai];
-      const int t = ts[c];
-      const double rng = (double)bf16_to_float(u.kmeta[gam * kDim + c] >> 16);
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) acc[i][hh] = 0.0;
+  {
+    const int gl = lane >> 2, ob = lane & 3;
+    const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)ob) << 8) | (uint32_t)ob;
+    const uint32_t* pl = planes + gl * nsp;
+    for (int c = wv; c < kDim; c += 4) {
+      const int t = tks[c];
+      if (t == 0) continue;
+      const int s0 = offs[c];
+      const double rs = (double)bf16_to_float(meta[gl][c] >> 16) * (1.0 / 256.0);
       double beta[GQA];
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) beta[hh] = qs[hh][c] * rng * (1.0 / 256.0);
-      const uint32_t* line = u.kplanes + (int64_t)c * W * u.ng + gam;
-      uint64_t x = 0;
-      for (int p = 0; p < t; ++p) {
-        const uint32_t wd = line[(int64_t)p * u.ng];
-        x |= (uint64_t)((wd >> (8 * k)) & 0xFFu) << (8 * (7 - p));
+      for (int hh = 0; hh < GQA; ++hh) beta[hh] = qs[hh][c] * rs;
+      uint32_t lo, hi;
+      if (t <= 4) {
+        const uint32_t w0 = pl[s0];
+        const uint32_t w1 = t > 1 ? pl[s0 + 1] : 0u;
+        const uint32_t w2 = t > 2 ? pl[s0 + 2] : 0u;
+        const uint32_t w3 = t > 3 ? pl[s0 + 3] : 0u;
+        hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w0, w1, sel), __builtin_amdgcn_perm(w2, w3, sel),
+                                   0x05040100u);
+        transpose8_hi4(lo, hi);
+      } else {
+        uint32_t w[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) w[p] = (p < t) ? pl[s0 + p] : 0u;
+        unplane8(w, sel, lo, hi);
       }
-      const uint64_t y = transpose8(x);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double xv = (double)(uint32_t)((y >> (8 * i)) & 0xFFu);
+      for (int e = 0; e < 8; ++e) {
+        const double X = code_plus_4096(e < 4 ? lo : hi, e & 3);
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) acc[i][hh] = fma(beta[hh], xv, acc[i][hh]);
+        for (int hh = 0; hh < GQA; ++hh) acc[e][hh] = fma(beta[hh], X, acc[e][hh]);
       }
     }
+  }
+  // ---- the four waves' partial sums, added in wave order ----
+  double* wred = reinterpret_cast<double*>(planes);  // [8 * GQA][64]
+  __syncthreads();
+  for (int w = 0; w < 4; ++w) {
+    if (wv == w) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+      for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) sv[i][hh] = (C[hh] + acc[i][hh]) * inv_sqrt_d;
+        for (int hh = 0; hh < GQA; ++hh) {
+          double* p = wred + (e * GQA + hh) * 64 + lane;
+          *p = (w == 0) ? acc[e][hh] : (*p + acc[e][hh]);
+        }
+    }
+    __syncthreads();
   }
 
-  // open-group tokens: exact keys.  The open group is group Tp/32, which
-  // lies in tile Tp/1024; thread (rr, k) takes slot rr, channels 32k..32k+31.
+  // ---- 4. open group (exact keys) ----
   const int64_t ntail = len - Tp;
-  const bool tail_tile = ntail > 0 && Tp / kKeyTile == tile;
-  const int rr = tid >> 2;
-  const bool has_tail = tail_tile && rr < ntail && k == 0;
-  double st[GQA];
+  const bool tail_here = ntail > 0 && Tp >= t0 && Tp < t0 + kTile;
+  if (tail_here) {
+    const int rr = tid >> 3, part = tid & 7;
+    double st[GQA];
 #pragma unroll
-  for (int hh = 0; hh < GQA; ++hh) st[hh] = 0.0;
-  if (tail_tile) {
+    for (int hh = 0; hh < GQA; ++hh) st[hh] = 0.0;
     if (rr < ntail) {
-      for (int c = k * 32; c < k * 32 + 32; ++c) {
+      for (int c = part * 16; c < part * 16 + 16; ++c) {
         const double kv = load_elem<DT>(u.ktail, (int64_t)rr * kDim + c);
 #pragma unroll
         for (int hh = 0; hh < GQA; ++hh) st[hh] = fma(qs[hh][c], kv, st[hh]);
@@ -235,140 +437,188 @@ __global__ __launch_bounds__(128) void k_score(const uint8_t* store, const void*
     for (int hh = 0; hh < GQA; ++hh) {
       st[hh] += __shfl_xor(st[hh], 1, 64);
       st[hh] += __shfl_xor(st[hh], 2, 64);
-      st[hh] *= inv_sqrt_d;
+      st[hh] += __shfl_xor(st[hh], 4, 64);
     }
+    if (part == 0 && rr < ntail)
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) tails[rr][hh] = st[hh] * kInvSqrtD;
   }
+  __syncthreads();
 
-  // ---- split-context softmax partials for this tile ----
-  double mloc[GQA];
+  // ---- softmax partials: thread -> tokens 2 tid, 2 tid + 1 of the tile ----
+  const int oc = tid >> 2, e0 = 2 * (tid & 3);
+  const int glt = oc >> 2;
+  const bool pk = glt < ngp;
+  const bool has_tail = tail_here && tid < ntail;
+  double sv[2][GQA];
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh)
+      sv[k][hh] = pk ? (Cs[glt][hh] + wred[((e0 + k) * GQA + hh) * 64 + oc]) * kInvSqrtD : 0.0;
+  double mt[GQA];
 #pragma unroll
   for (int hh = 0; hh < GQA; ++hh) {
-    double m = has_tail ? st[hh] : -INFINITY;
-    if (packed)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = fmax(m, sv[i][hh]);
+    double m = has_tail ? tails[tid][hh] : -INFINITY;
+    if (pk) m = fmax(m, fmax(sv[0][hh], sv[1][hh]));
     m = wave_max(m);
-    if ((tid & 63) == 0) red[tid >> 6][hh] = m;
+    if (lane == 0) red[wv][hh] = m;
   }
   __syncthreads();
 #pragma unroll
-  for (int hh = 0; hh < GQA; ++hh) mloc[hh] = fmax(red[0][hh], red[1][hh]);
+  for (int hh = 0; hh < GQA; ++hh) mt[hh] = fmax(fmax(red[0][hh], red[1][hh]), fmax(red[2][hh], red[3][hh]));
   __syncthreads();
 #pragma unroll
   for (int hh = 0; hh < GQA; ++hh) {
+    const int64_t row = ((int64_t)b * H + (int64_t)g * GQA + hh) * capmax;
     double z = 0.0;
-    double* ep = ebuf + ((int64_t)b * H + (int64_t)g * GQA + hh) * capmax;
-    if (packed) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const double e = exp(sv[i][hh] - mloc[hh]);
-        ep[gam * kGroup + 8 * k + i] = e;
-        z += e;
-      }
+    if (pk) {
+      const int64_t j = t0 + 2 * tid;
+      const double ea = exp(sv[0][hh] - mt[hh]), eb = exp(sv[1][hh] - mt[hh]);
+      ebuf[row + j] = ea;
+      ebuf[row + j + 1] = eb;
+      e16[row + j] = (_Float16)ea;
+      e16[row + j + 1] = (_Float16)eb;
+      z = ea + eb;
     }
     if (has_tail) {
-      const double e = exp(st[hh] - mloc[hh]);
-      ep[Tp + rr] = e;
-      z += e;
+      const double ev = exp(tails[tid][hh] - mt[hh]);
+      ebuf[row + Tp + tid] = ev;
+      e16[row + Tp + tid] = (_Float16)ev;
+      z += ev;
     }
     z = wave_sum(z);
-    if ((tid & 63) == 0) red[tid >> 6][hh] = z;
+    if (lane == 0) red[wv][hh] = z;
   }
   __syncthreads();
   if (tid < GQA) {
     double* tp = tilepart + (((int64_t)b * H + (int64_t)g * GQA + tid) * ntile_ws + tile) * 2;
-    tp[0] = mloc[tid];
-    tp[1] = red[0][tid] + red[1][tid];
+    tp[0] = mt[tid];
+    tp[1] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Value allocation: one block of 1024 threads per (request, KV head).
+// Value allocation: one block of 1024 threads per (request, KV head); token
+// j is owned by thread j mod 1024 (coalesced reads).
 //   m_h = max_tile m_tile, Z_h = sum_tile z_tile exp(m_tile - m_h)
-//   f_{h,tile} = exp(m_tile - m_h) / Z_h       (alpha_hat = e * f)
-//   a_j = (sum_h alpha_hat_hj^2) * s_gamma(j)  (Eq. (3))
-// then ChooseDepths with B_V = floor(R_V * T_packed) over (token, level)
-// gains a_j 4^-t.  Threshold search: first pass on the 11-bit exponent of
-// the gains (a token's W gains land in bins e_j - 2, ..., e_j - 2W), then
-// 9,9,9,9,8,8-bit mantissa passes.
+//   f_{h,tile} = exp(m_tile - m_h) / Z_h         (alpha_hat = e * f)
+//   a_j = (sum_h alpha_hat_hj^2) * s_gamma(j)     (Eq. (3))
+// then ChooseDepths with B_V = floor(R_V * T_packed) over the (token, level)
+// gains a_j 4^-t, ties to the lowest token.  A token with a normal a_j
+// whose exponent field E exceeds 2W has its W gains at exponents E-2t with
+// a_j's mantissa; smaller ("tiny") ones are multiplied out.  Threshold
+// search: the exponent class E* of the B_V-th largest gain from an exponent
+// histogram (E* and the count above it), then 11/11/10/10/10-bit radix
+// passes over the mantissas of the candidates in class E*.
 // ---------------------------------------------------------------------------
 constexpr int kVNT = 1024;
+constexpr int kVPMAX = 16;  // tokens per thread held in registers
 
-template <bool REG>
+// hist[bin] += 1 for every active lane, one LDS atomic per distinct bin of
+// the wave: a lane's peers with the same 11-bit bin are found by matching
+// the ballots of each bin bit; the lowest peer adds the peer count.
+__device__ __forceinline__ void agg_add(uint32_t* hist, uint32_t bin, bool act) {
+  uint64_t same = __ballot(act);
+#pragma unroll
+  for (int bit = 0; bit < 11; ++bit) {
+    const uint64_t ones = __ballot(act && ((bin >> bit) & 1u));
+    same &= ((bin >> bit) & 1u) ? ones : ~ones;
+  }
+  if (act && (same & ((1ull << __lane_id()) - 1ull)) == 0ull)
+    atomicAdd(&hist[bin & 2047u], (uint32_t)__popcll(same));
+}
+
+template <int GQA, bool REG>
 __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int H, int G, int W,
                                                       int esize, float RV, int vscale,
                                                       int64_t capmax, int ntile_ws,
                                                       const double* ebuf, const double* tilepart,
                                                       double* ftile, double* aval, uint8_t* tv) {
   constexpr int NT = kVNT;
-  constexpr int PMAX = 16;
   const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const int gqa = H / G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
-  const int ntile_b = (int)((len + kKeyTile - 1) / kKeyTile);
+  const int ntile_b = (int)((len + kTile - 1) / kTile);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   __shared__ uint32_t hA[2048];
   __shared__ uint32_t hB[2048];
   __shared__ uint32_t wsum[NT / 64 + 1];
   __shared__ uint32_t sh[2];
 
-  // ---- softmax statistics -> per-tile factors ----
-  if (tid < gqa) {
-    const int h = g * gqa + tid;
+  // ---- softmax statistics -> per-tile factors (wave h handles head h) ----
+  if (wv < GQA) {
+    const int h = g * GQA + wv;
     const double* tp = tilepart + ((int64_t)b * H + h) * ntile_ws * 2;
     double m = -INFINITY;
-    for (int t = 0; t < ntile_b; ++t) m = fmax(m, tp[2 * t]);
+    for (int t = lane; t < ntile_b; t += 64) m = fmax(m, tp[2 * t]);
+    m = wave_max(m);
     double Z = 0.0;
-    for (int t = 0; t < ntile_b; ++t) Z += tp[2 * t + 1] * exp(tp[2 * t] - m);
+    for (int t = lane; t < ntile_b; t += 64) Z += tp[2 * t + 1] * exp(tp[2 * t] - m);
+    Z = wave_sum(Z);
     double* f = ftile + ((int64_t)b * H + h) * ntile_ws;
-    for (int t = 0; t < ntile_b; ++t) f[t] = exp(tp[2 * t] - m) / Z;
+    for (int t = lane; t < ntile_b; t += 64) f[t] = exp(tp[2 * t] - m) / Z;
   }
+  for (int i = tid; i < 2048; i += NT) { hA[i] = 0u; hB[i] = 0u; }
+  __threadfence_block();
   __syncthreads();
 
-  // ---- value weights for owned tokens (blocked ownership) ----
-  const int64_t per = (Tp + NT - 1) / NT;
-  const int64_t j0 = (int64_t)tid * per;
-  const int64_t j1 = (j0 + per < Tp) ? j0 + per : Tp;
-  const double* fb = ftile + ((int64_t)b * H + (int64_t)g * gqa) * ntile_ws;
-  const double* eb = ebuf + ((int64_t)b * H + (int64_t)g * gqa) * capmax;
+  // ---- value weights ----
+  const int per = (int)((Tp + NT - 1) / NT);
+  // loop bound over owned-token rounds: a compile-time constant when the
+  // weights live in registers (so that the loops unroll and index them
+  // statically), the actual count otherwise
+  const int kmax = REG ? kVPMAX : per;
+  const double* fb = ftile + ((int64_t)b * H + (int64_t)g * GQA) * ntile_ws;
+  const double* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
   double* ab = aval + ((int64_t)b * G + g) * capmax;
   uint8_t* tvb = tv + ((int64_t)b * G + g) * capmax;
-  double areg[REG ? PMAX : 1];
-  for (int64_t j = j0; j < j1; ++j) {
-    double asq = 0.0;
-    const int tl = (int)(j / kKeyTile);
-    for (int hh = 0; hh < gqa; ++hh) {
-      const double al = eb[(int64_t)hh * capmax + j] * fb[(int64_t)hh * ntile_ws + tl];
-      asq = asq + al * al;
+  double areg[REG ? kVPMAX : 1];
+#pragma unroll
+  for (int k = 0; k < kmax; ++k) {
+    if (k >= per) break;
+    const int64_t j = tid + (int64_t)NT * k;
+    double a = 0.0;
+    if (j < Tp) {
+      const int tl = (int)(j / kTile);
+      double asq = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) {
+        const double al = __dmul_rn(eb[(int64_t)hh * capmax + j], fb[(int64_t)hh * ntile_ws + tl]);
+        asq = __dadd_rn(asq, __dmul_rn(al, al));
+      }
+      a = (vscale == 0) ? __dmul_rn(asq, u.ev[j / kGroup]) : asq;
     }
-    const double a = (vscale == 0) ? asq * u.ev[j / kGroup] : asq;
-    if constexpr (REG) areg[j - j0] = a; else ab[j] = a;
+    if constexpr (REG) areg[k] = a;
+    else if (j < Tp) ab[j] = a;
   }
-  auto aof = [&](int64_t j) -> double {
-    if constexpr (REG) return areg[j - j0]; else return ab[j];
+  auto aof = [&](int k) -> double {
+    const int64_t j = tid + (int64_t)NT * k;
+    if (j >= Tp) return 0.0;
+    if constexpr (REG) return areg[k];
+    else return ab[j];
   };
 
-  const uint32_t k = (uint32_t)floor((double)RV * (double)Tp);
-  const uint32_t twoW = 2u * (uint32_t)W;
+  const uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
+  const int twoW = 2 * W;
 
-  // ---- pass 1: exponent histogram of all candidate gains ----
-  for (int i = tid; i < 2048; i += NT) { hA[i] = 0; hB[i] = 0; }
-  __syncthreads();
+  // ---- exponent histogram: hA[E] regular tokens, hB[E] tiny tokens' gains ----
   uint32_t npos_l = 0;
-  for (int64_t j = j0; j < j1; ++j) {
-    const double a = aof(j);
-    if (!(a > 0.0)) continue;
-    const uint32_t e = (uint32_t)(dbits(a) >> 52);
-    if (e > twoW) {
-      atomicAdd(&hA[e], 1u);
-      npos_l += W;
-    } else {
+#pragma unroll
+  for (int k = 0; k < kmax; ++k) {
+    if (k >= per) break;
+    const double a = aof(k);
+    const bool posv = a > 0.0;
+    const int E = (int)(dbits(a) >> 52);
+    const bool reg = posv && E > twoW;
+    agg_add(hA, (uint32_t)E, reg);
+    if (reg) npos_l += W;
+    if (posv && !reg) {
       for (int t = 1; t <= W; ++t) {
-        const uint64_t kk = dbits(a * ldexp_pow2(-2 * t));
+        const uint64_t kk = dbits(__dmul_rn(a, ldexp_pow2(-2 * t)));
         if (kk) { atomicAdd(&hB[(uint32_t)(kk >> 52)], 1u); ++npos_l; }
       }
     }
@@ -376,304 +626,428 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   block_excl_scan<NT>(npos_l, wsum);
   const uint32_t npos = wsum[NT / 64];
   __syncthreads();
-  // combine: hB[E] += sum_t hA[E + 2t]
+  // hB[E] += sum_t hA[E + 2t]: the gain-exponent histogram of all candidates
   for (int E = tid; E < 2048; E += NT) {
     uint32_t s = hB[E];
     for (int t = 1; t <= W; ++t)
       if (E + 2 * t < 2048) s += hA[E + 2 * t];
-    hB[E] = s;  // each thread only touches its own E; hA is read-only here
+    hB[E] = s;
   }
   __syncthreads();
 
-  uint64_t prefix = 0, mask = 0;
-  uint32_t rem = k, n_eq = 0;
-  const bool all_pos = npos <= k;
-  if (!all_pos && k > 0) {
-    if (tid < 64) wave_find_digit<2048>(hB, rem, &sh[0], &sh[1]);
+  const bool all_pos = npos <= Bv;
+  int Es = -1;
+  uint64_t prefix = 0, mask = 0;  // over the 52 mantissa bits
+  uint32_t rem = 0, n_eq = 0;
+  if (!all_pos && Bv > 0) {
+    if (tid < 64) wave_find_digit<2048>(hB, Bv, &sh[0], &sh[1]);
     __syncthreads();
-    {
-      const uint32_t d = sh[0];
-      n_eq = hB[d];
-      rem -= sh[1];
-      prefix = (uint64_t)d << 52;
-      mask = 0xFFFull << 52;
-    }
+    Es = (int)sh[0];
+    rem = Bv - sh[1];
+    n_eq = hB[Es];
     __syncthreads();
-    const int shifts[6] = {43, 34, 25, 16, 8, 0};
-    const int widths[6] = {9, 9, 9, 9, 8, 8};
-    for (int pass = 0; pass < 6 && n_eq != rem; ++pass) {
-      const int shift = shifts[pass];
-      const uint32_t dmask = (1u << widths[pass]) - 1u;
-      for (int i = tid; i < 512; i += NT) hA[i] = 0;
+    // digits of the 52 mantissa bits: 11, 11, 10, 10, 10 (MSB first)
+    for (int pass = 0; pass < 5 && n_eq != rem; ++pass) {
+      const int width = pass < 2 ? 11 : 10;
+      const int shift = pass < 2 ? 41 - 11 * pass : 40 - 10 * pass;
+      const uint32_t dmask = (1u << width) - 1u;
+      for (int i = tid; i < 2048; i += NT) hA[i] = 0u;
       __syncthreads();
-      const uint32_t Estar = (uint32_t)(prefix >> 52);
-      for (int64_t j = j0; j < j1; ++j) {
-        const double a = aof(j);
+#pragma unroll
+      for (int k = 0; k < kmax; ++k) {
+        if (k >= per) break;
+        const double a = aof(k);
         if (!(a > 0.0)) continue;
         const uint64_t ab_ = dbits(a);
-        const uint32_t e = (uint32_t)(ab_ >> 52);
-        if (e > twoW) {
-          const int dd = (int)e - (int)Estar;
-          if (dd < 2 || dd > (int)twoW || (dd & 1)) continue;
-          const uint64_t kk = ab_ - ((uint64_t)dd << 52);
-          if ((kk & mask) == prefix) atomicAdd(&hA[(uint32_t)(kk >> shift) & dmask], 1u);
+        const int E = (int)(ab_ >> 52);
+        if (E > twoW) {
+          const int d = E - Es;
+          if (d >= 2 && d <= twoW && !(d & 1)) {
+            const uint64_t mnt = ab_ & 0x000FFFFFFFFFFFFFull;
+            if ((mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
+          }
         } else {
           for (int t = 1; t <= W; ++t) {
-            const uint64_t kk = dbits(a * ldexp_pow2(-2 * t));
-            if (kk && (kk & mask) == prefix) atomicAdd(&hA[(uint32_t)(kk >> shift) & dmask], 1u);
+            const uint64_t kk = dbits(__dmul_rn(a, ldexp_pow2(-2 * t)));
+            if (kk && (int)(kk >> 52) == Es) {
+              const uint64_t mnt = kk & 0x000FFFFFFFFFFFFFull;
+              if ((mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
+            }
           }
         }
       }
       __syncthreads();
       if (tid < 64) {
-        if (widths[pass] == 9) wave_find_digit<512>(hA, rem, &sh[0], &sh[1]);
-        else wave_find_digit<256>(hA, rem, &sh[0], &sh[1]);
+        if (width == 11) wave_find_digit<2048>(hA, rem, &sh[0], &sh[1]);
+        else wave_find_digit<1024>(hA, rem, &sh[0], &sh[1]);
       }
       __syncthreads();
-      const uint32_t d = sh[0];
-      n_eq = hA[d];
+      const uint32_t dg = sh[0];
+      n_eq = hA[dg];
       rem -= sh[1];
-      prefix |= (uint64_t)d << shift;
+      prefix |= (uint64_t)dg << shift;
       mask |= (uint64_t)dmask << shift;
       __syncthreads();
     }
   }
 
-  // ---- depths ----
-  auto count_levels = [&](double a, uint32_t& sel, uint32_t& tie) {
-    sel = 0;
-    tie = 0;
-    if (!(a > 0.0)) return;
-    for (int t = 1; t <= W; ++t) {
-      const uint64_t kk = dbits(a * ldexp_pow2(-2 * t));
-      if (!kk) continue;
-      if (all_pos) { ++sel; continue; }
-      if (k == 0) continue;
-      const uint64_t km = kk & mask;
-      if (km > prefix) ++sel;
-      else if (km == prefix) ++tie;
+  // ---- depths: levels above the threshold, plus ties in token order ----
+  // returns (levels above the threshold) | (levels equal to it) << 16
+  auto count_levels = [&](double a) -> uint32_t {
+    uint32_t above = 0, tie = 0;
+    if (!(a > 0.0)) return 0u;
+    const uint64_t ab_ = dbits(a);
+    const int E = (int)(ab_ >> 52);
+    if (all_pos) {
+      if (E > twoW) above = (uint32_t)W;
+      else
+        for (int t = 1; t <= W; ++t) above += dbits(__dmul_rn(a, ldexp_pow2(-2 * t))) != 0ull;
+      return above;
     }
+    if (Bv == 0) return 0u;
+    if (E > twoW) {
+      const int d = E - Es;
+      if (d > 0) {
+        int n = (d - 1) >> 1;
+        above = (uint32_t)(n > W ? W : n);
+      }
+      if (d >= 2 && d <= twoW && !(d & 1)) {
+        const uint64_t mnt = (ab_ & 0x000FFFFFFFFFFFFFull) & mask;
+        if (mnt > prefix) ++above;
+        else if (mnt == prefix) ++tie;
+      }
+    } else {
+      for (int t = 1; t <= W; ++t) {
+        const uint64_t kk = dbits(__dmul_rn(a, ldexp_pow2(-2 * t)));
+        if (!kk) continue;
+        const int e = (int)(kk >> 52);
+        if (e > Es) ++above;
+        else if (e == Es) {
+          const uint64_t mnt = (kk & 0x000FFFFFFFFFFFFFull) & mask;
+          if (mnt > prefix) ++above;
+          else if (mnt == prefix) ++tie;
+        }
+      }
+    }
+    return above | (tie << 16);
   };
-  uint32_t before = 0;
-  const bool rank_ties = !all_pos && k > 0 && rem < n_eq;
-  if (rank_ties) {
-    uint32_t mytie = 0;
-    for (int64_t j = j0; j < j1; ++j) {
-      uint32_t s_, t_;
-      count_levels(aof(j), s_, t_);
-      mytie += t_;
+  const bool rank_ties = !all_pos && Bv > 0 && rem < n_eq;
+  uint32_t running = 0;  // ties in earlier rounds (token order = round, thread)
+#pragma unroll
+  for (int k = 0; k < kmax; ++k) {
+    if (k >= per) break;
+    const int64_t j = tid + (int64_t)NT * k;
+    const uint32_t lv = count_levels(aof(k));
+    uint32_t above = lv & 0xFFFFu;
+    const uint32_t tie = lv >> 16;
+    if (rank_ties) {
+      const uint32_t before = block_excl_scan<NT>(tie, wsum) + running;
+      running += wsum[NT / 64];
+      __syncthreads();
+      if (tie && before < rem) ++above;
+    } else {
+      above += tie;
     }
-    before = block_excl_scan<NT>(mytie, wsum);
-  }
-  for (int64_t j = j0; j < j1; ++j) {
-    uint32_t s_, t_;
-    count_levels(aof(j), s_, t_);
-    if (t_) {
-      if (!rank_ties) s_ += t_;
-      else if (before < rem) ++s_;
-      before += t_;
-    }
-    tvb[j] = (uint8_t)s_;
+    if (j < Tp) tvb[j] = (uint8_t)above;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Gather: block of 256 threads per 256-token chunk of one (request, KV head).
-// Thread (s, k) = (tid/16, tid%16) handles tokens s, s+16, ... of the chunk
-// and channels 8k..8k+7: it reads byte k of each of the token's t^V_j plane
-// rows, un-planes them and accumulates alpha_hat * v_hat in fp32.
+// Gather: one block of 256 threads per 256-token chunk (8 groups) of one
+// (request, KV head).  The chosen value plane rows (16 B per token and
+// plane) are staged in LDS.  Lane (group gl, token parity ts, channel octet
+// bo) walks its 16 tokens of group gl in pairs and accumulates, per head,
+//   A = sum e,  Bh = sum e 2^-(t+1),  U_c = sum e X_c
+// with e = exp(s - m_tile) rounded to fp16 and X_c the un-planed 8-bit
+// prefix codes, via fp16 dot products (X enters as the fp16 value 1024 + X;
+// the 1024 A part is removed afterwards).  Per group,
+//   sum_j e_j v_hat_jc = lo_c A + rng_c (Bh + U_c / 256).
+// The chunk partial is f_{h,tile} times the sum over the chunk's groups.
+// Grid (unit, chunk): consecutive blocks are different units, so all chunks
+// of a unit are dispatched to the same XCD.
 // ---------------------------------------------------------------------------
 template <int GQA, int DT>
 __global__ __launch_bounds__(256) void k_gather(const uint8_t* store, const uint8_t* tv, int H, int G,
                                                 int W, int64_t capmax, int ntile_ws, int nchunk_ws,
-                                                const double* ebuf, const double* ftile,
+                                                const _Float16* e16, const double* ftile,
                                                 float* opart) {
   constexpr int esize = DT == 0 ? 2 : 4;
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  constexpr int NG = kChunk / kGroup;  // 8
+  __shared__ uint4 vrows[kChunk * 8];
+  __shared__ uint32_t vmeta_s[NG][kDim];
+  __shared__ _Float16 es[GQA][kChunk];
+  __shared__ uint16_t offs[kChunk];
+  __shared__ uint8_t tvs[kChunk];
+  __shared__ uint8_t s2t[kChunk * 8];
+  __shared__ float fs[GQA];
+  __shared__ uint32_t wsum[256 / 64 + 1];
+
+  const int chunk = blockIdx.y, b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
-  const int64_t c0 = (int64_t)chunk * kValChunk;
+  const int64_t c0 = (int64_t)chunk * kChunk;
   if (c0 >= len) return;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const int tid = threadIdx.x;
-
-  __shared__ float al_s[GQA][kValChunk];
-  __shared__ float lo_s[kValChunk / kGroup][kDim];
-  __shared__ float rs_s[kValChunk / kGroup][kDim];
-  __shared__ uint8_t tv_s[kValChunk];
-  __shared__ float red[4][GQA][kDim];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tile = (int)(c0 / kTile);
+  const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
 
   {
     const int64_t j = c0 + tid;
-    if (j < len) {
-      tv_s[tid] = (j < Tp) ? tv[((int64_t)b * G + g) * capmax + j] : 0;
-      const int tl = (int)(j / kKeyTile);
+    tvs[tid] = (j < Tp) ? tv[((int64_t)b * G + g) * capmax + j] : (uint8_t)0;
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) {
-        const int64_t hrow = (int64_t)b * H + (int64_t)g * GQA + hh;
-        al_s[hh][tid] = (float)(ebuf[hrow * capmax + j] * ftile[hrow * ntile_ws + tl]);
-      }
-    }
-    for (int i = tid; i < (kValChunk / kGroup) * kDim; i += 256) {
+    for (int hh = 0; hh < GQA; ++hh)
+      es[hh][tid] = (j < len) ? e16[(hrow0 + hh) * capmax + j] : (_Float16)0.0f;
+    for (int i = tid; i < NG * kDim; i += 256) {
       const int gl = i / kDim, c = i % kDim;
       const int64_t gam = c0 / kGroup + gl;
-      if ((gam + 1) * kGroup <= Tp) {
-        const uint32_t m = u.vmeta[gam * kDim + c];
-        lo_s[gl][c] = bf16_to_float(m & 0xFFFFu);
-        rs_s[gl][c] = bf16_to_float(m >> 16) * (1.0f / 512.0f);
+      vmeta_s[gl][c] = ((gam + 1) * kGroup <= Tp) ? u.vmeta[gam * kDim + c] : 0u;
+    }
+    if (tid < GQA) fs[tid] = (float)ftile[(hrow0 + tid) * ntile_ws + tile];
+  }
+  __syncthreads();
+  const uint32_t tj = tvs[tid];
+  const uint32_t ex = block_excl_scan<256>(tj, wsum);
+  const int nslots = (int)wsum[256 / 64];
+  offs[tid] = (uint16_t)ex;
+  for (uint32_t p = 0; p < tj; ++p) s2t[ex + p] = (uint8_t)tid;
+  __syncthreads();
+  {
+    const uint4* vp = reinterpret_cast<const uint4*>(u.vplanes);
+    for (int base = 0; base < nslots; base += 256 * 8) {
+      uint4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s = base + k * 256 + tid;
+        v[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (s < nslots) {
+          const int jl = s2t[s];
+          const int p = s - offs[jl];
+          v[k] = vp[(c0 + jl) * W + p];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int s = base + k * 256 + tid;
+        if (s < nslots) vrows[s] = v[k];
       }
     }
   }
   __syncthreads();
 
-  const int s = tid >> 4, k = tid & 15;
-  float acc[8][GQA];
+  const int gsl = lane >> 5, ts = (lane >> 4) & 1, bo = lane & 15;
+  const int gl = 2 * wv + gsl;
+  const int64_t gam = c0 / kGroup + gl;
+  const bool gpacked = (gam + 1) * kGroup <= Tp;
+  const int wb = bo >> 2, ob = bo & 3;
+  const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)ob) << 8) | (uint32_t)ob;
+  const uint32_t* rows = reinterpret_cast<const uint32_t*>(vrows);
+  float O[GQA][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int hh = 0; hh < GQA; ++hh)
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) acc[i][hh] = 0.f;
-  const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(u.vplanes);
-  for (int it = 0; it < kValChunk / 16; ++it) {
-    const int jl = s + 16 * it;
-    const int64_t j = c0 + jl;
-    if (j >= len) break;
-    float v[8];
-    if (j < Tp) {
-      const int t = tv_s[jl];
-      const int gl = jl >> 5;
-      uint64_t x = 0;
-      const uint8_t* row = vbytes + (j * W) * (kDim / 8) + k;
-      for (int p = 0; p < t; ++p) x |= (uint64_t)row[p * (kDim / 8)] << (8 * (7 - p));
-      const uint64_t y = transpose8(x);
-      const float half = (float)(256 >> t);
+    for (int i = 0; i < 8; ++i) O[hh][i] = 0.f;
+
+  if (gpacked) {
+    float A[GQA], Bh[GQA], U[GQA][8];
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      A[hh] = 0.f;
+      Bh[hh] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) U[hh][i] = 0.f;
+    }
+    for (int k = 0; k < 8; ++k) {
+      const int jA = 32 * gl + ts + 4 * k, jB = jA + 2;
+      uint32_t ya[2], yb[2];
+      const int tA = tvs[jA], tB = tvs[jB];
+      {
+        uint32_t w[8];
+        const int s0 = offs[jA];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) w[p] = (p < tA) ? rows[(s0 + p) * 4 + wb] : 0u;
+        unplane8(w, sel, ya[0], ya[1]);
+      }
+      {
+        uint32_t w[8];
+        const int s0 = offs[jB];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) w[p] = (p < tB) ? rows[(s0 + p) * 4 + wb] : 0u;
+        unplane8(w, sel, yb[0], yb[1]);
+      }
+      uint32_t P[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const float X = (float)(uint32_t)((y >> (8 * i)) & 0xFFu);
-        v[i] = fmaf(rs_s[gl][8 * k + i], fmaf(2.0f, X, half), lo_s[gl][8 * k + i]);
+        const uint32_t sl = 0x0C000C00u | ((uint32_t)(4 + (i & 3)) << 16) | (uint32_t)(i & 3);
+        P[i] = __builtin_amdgcn_perm(yb[i >> 2], ya[i >> 2], sl) | 0x64006400u;
       }
-    } else {
+      const float hA_ = ldexp_pow2f(-tA - 1), hB_ = ldexp_pow2f(-tB - 1);
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) {
+        f16x2 ep;
+        ep.x = es[hh][jA];
+        ep.y = es[hh][jB];
+        const float ea = (float)ep.x, eb2 = (float)ep.y;
+        A[hh] += ea + eb2;
+        Bh[hh] = fmaf(ea, hA_, fmaf(eb2, hB_, Bh[hh]));
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          U[hh][i] = __builtin_amdgcn_fdot2(ep, __builtin_bit_cast(f16x2, P[i]), U[hh][i], false);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t m = vmeta_s[gl][8 * bo + i];
+      const float lo = bf16_to_float(m & 0xFFFFu), rng = bf16_to_float(m >> 16);
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh)
+        O[hh][i] = fmaf(lo, A[hh], rng * (Bh[hh] + (U[hh][i] - 1024.f * A[hh]) * (1.f / 256.f)));
+    }
+  } else {
+    // open group: exact values
+    for (int k = 0; k < kGroup / 2; ++k) {
+      const int jl = 32 * gl + ts + 2 * k;
+      const int64_t j = c0 + jl;
+      if (j < Tp || j >= len) continue;
       const int64_t slot = j - Tp;
+      float v[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = load_elem_f<DT>(u.vtail, slot * kDim + 8 * k + i);
-    }
+      for (int i = 0; i < 8; ++i) v[i] = load_elem_f<DT>(u.vtail, slot * kDim + 8 * bo + i);
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) {
-      const float a = al_s[hh][jl];
+      for (int hh = 0; hh < GQA; ++hh) {
+        const float e = (float)es[hh][jl];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i][hh] = fmaf(a, v[i], acc[i][hh]);
+        for (int i = 0; i < 8; ++i) O[hh][i] = fmaf(e, v[i], O[hh][i]);
+      }
     }
   }
-  // reduce the 4 token slots of each wave, then the 4 waves
+  // reduce over (group slot, token parity) within the wave, then over waves
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int hh = 0; hh < GQA; ++hh)
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) {
-      float vv = acc[i][hh];
-      vv += __shfl_xor(vv, 16, 64);
-      vv += __shfl_xor(vv, 32, 64);
-      acc[i][hh] = vv;
+    for (int i = 0; i < 8; ++i) {
+      float v = O[hh][i] * fs[hh];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      O[hh][i] = v;
     }
-  if ((tid & 63) < 16) {
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(vrows);  // [4][GQA][128]
+  if (lane < 16)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int hh = 0; hh < GQA; ++hh)
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) red[tid >> 6][hh][8 * k + i] = acc[i][hh];
-  }
+      for (int i = 0; i < 8; ++i) red[(wv * GQA + hh) * kDim + 8 * bo + i] = O[hh][i];
   __syncthreads();
   for (int o = tid; o < GQA * kDim; o += 256) {
     const int hh = o / kDim, c = o % kDim;
-    const float sum = (red[0][hh][c] + red[1][hh][c]) + (red[2][hh][c] + red[3][hh][c]);
-    opart[(((int64_t)b * H + (int64_t)g * GQA + hh) * nchunk_ws + chunk) * kDim + c] = sum;
+    const float s = (red[(0 * GQA + hh) * kDim + c] + red[(1 * GQA + hh) * kDim + c]) +
+                    (red[(2 * GQA + hh) * kDim + c] + red[(3 * GQA + hh) * kDim + c]);
+    opart[((hrow0 + hh) * nchunk_ws + chunk) * kDim + c] = s;
   }
 }
 
-// out[b][h][c] = sum over the request's chunks, in chunk order.
-__global__ __launch_bounds__(128) void k_out_reduce(const uint8_t* store, int H, int nchunk_ws,
-                                                    const float* opart, float* out) {
-  const int bh = blockIdx.x;
-  const int b = bh / H;
+// out[b][h][c] = sum over the request's chunks, in chunk order.  One thread
+// per output element; the chunk loads are independent.
+__global__ __launch_bounds__(256) void k_out_reduce(const uint8_t* store, int H, int nchunk_ws,
+                                                    int64_t nout, const float* opart, float* out) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o >= nout) return;
+  const int64_t bh = o / kDim;
+  const int c = (int)(o - bh * kDim);
+  const int b = (int)(bh / H);
   const ReqRecord r = req_of(store, b);
-  const int nch = (int)((r.len + kValChunk - 1) / kValChunk);
-  const float* p = opart + (int64_t)bh * nchunk_ws * kDim + threadIdx.x;
+  const int nch = (int)((r.len + kChunk - 1) / kChunk);
+  const float* p = opart + bh * nchunk_ws * kDim + c;
   float s = 0.f;
-  for (int ch = 0; ch < nch; ++ch) s += p[(int64_t)ch * kDim];
-  out[(int64_t)bh * kDim + threadIdx.x] = s;
+  int ch = 0;
+  for (; ch + 4 <= nch; ch += 4) {
+    const float v0 = p[(int64_t)ch * kDim], v1 = p[(int64_t)(ch + 1) * kDim];
+    const float v2 = p[(int64_t)(ch + 2) * kDim], v3 = p[(int64_t)(ch + 3) * kDim];
+    s += v0;
+    s += v1;
+    s += v2;
+    s += v3;
+  }
+  for (; ch < nch; ++ch) s += p[(int64_t)ch * kDim];
+  out[o] = s;
 }
 
 // ---------------------------------------------------------------------------
-template <int GQA, int DT>
-static void launch_score_gather(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk,
-                                const uint8_t* tv, hipStream_t st, int phase) {
-  uint8_t* ws = a.ws;
-  if (phase == 0) {
-    hipLaunchKernelGGL((k_score<GQA, DT>), dim3(L.ntile, a.G, a.B), dim3(128), 0, st,
-                       (const uint8_t*)a.store, a.q, tk, a.H, a.G, a.W, a.capmax, L.ntile,
-                       (double*)(ws + L.logits), (double*)(ws + L.tilepart));
-  } else {
-    hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(L.nchunk, a.G, a.B), dim3(256), 0, st,
-                       (const uint8_t*)a.store, tv, a.H, a.G, a.W, a.capmax, L.ntile, L.nchunk,
-                       (const double*)(ws + L.logits), (const double*)(ws + L.ftile),
-                       (float*)(ws + L.opart));
-  }
-}
-
-template <int DT>
-static bool dispatch_gqa(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk,
-                         const uint8_t* tv, hipStream_t st, int phase) {
-  switch (a.H / a.G) {
-    case 1: launch_score_gather<1, DT>(a, L, tk, tv, st, phase); return true;
-    case 2: launch_score_gather<2, DT>(a, L, tk, tv, st, phase); return true;
-    case 3: launch_score_gather<3, DT>(a, L, tk, tv, st, phase); return true;
-    case 4: launch_score_gather<4, DT>(a, L, tk, tv, st, phase); return true;
-    case 5: launch_score_gather<5, DT>(a, L, tk, tv, st, phase); return true;
-    case 6: launch_score_gather<6, DT>(a, L, tk, tv, st, phase); return true;
-    case 7: launch_score_gather<7, DT>(a, L, tk, tv, st, phase); return true;
-    case 8: launch_score_gather<8, DT>(a, L, tk, tv, st, phase); return true;
-    default: return false;
-  }
-}
-
 static inline void mark(const DecodeArgs& a, int i, hipStream_t st) {
   if (a.events) hipEventRecord((hipEvent_t)a.events[i], st);
 }
 
-int launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const WsLayout L = ws_layout(a.B, a.H, a.G, kDim, a.capmax);
-  mark(a, 0, st);
+template <int GQA, int DT>
+static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   uint8_t* ws = a.ws;
   uint8_t* tk = a.key_depths_out ? a.key_depths_out : ws + L.tk;
   uint8_t* tv = a.value_depths_out ? a.value_depths_out : ws + L.tv;
-  const int esize = a.dtype == 0 ? 2 : 4;
-  if (a.dtype == 0)
-    hipLaunchKernelGGL((k_key_alloc<0>), dim3(a.B * a.G), dim3(256), 0, st,
-                       (const uint8_t*)a.store, a.q, a.H, a.G, a.W, a.RK, tk);
-  else
-    hipLaunchKernelGGL((k_key_alloc<1>), dim3(a.B * a.G), dim3(256), 0, st,
-                       (const uint8_t*)a.store, a.q, a.H, a.G, a.W, a.RK, tk);
+  const int esize = DT == 0 ? 2 : 4;
+
+  mark(a, 0, st);
+  hipLaunchKernelGGL((k_key_alloc<DT>), dim3(a.B * a.G), dim3(64), 0, st, (const uint8_t*)a.store,
+                     a.q, a.H, a.G, a.W, a.RK, tk);
   mark(a, 1, st);
-  bool ok = a.dtype == 0 ? dispatch_gqa<0>(a, L, tk, tv, st, 0) : dispatch_gqa<1>(a, L, tk, tv, st, 0);
-  if (!ok) return -5;
+  // slots staged per score tile: at most min(B_K, 128 W) chosen key lines
+  double bk = floor((double)a.RK * (double)kDim);
+  if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
+  size_t dyn = (size_t)(kTile / kGroup) * (size_t)(((int)bk) | 1) * 4;
+  const size_t dyn_red = (size_t)64 * 8 * GQA * 8;  // wave reduction buffer
+  if (dyn < dyn_red) dyn = dyn_red;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GQA, DT>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, 16 * 1025 * 4 + 64);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, L.ntile), dim3(256), dyn, st,
+                     (const uint8_t*)a.store, a.q, (const uint8_t*)tk, a.H, a.G, a.W, a.capmax,
+                     L.ntile, (double*)(ws + L.ebuf), (_Float16*)(ws + L.e16),
+                     (double*)(ws + L.tilepart));
   mark(a, 2, st);
-  const bool reg = a.capmax <= (int64_t)kVNT * 16;
-  if (reg)
-    hipLaunchKernelGGL((k_value_alloc<true>), dim3(a.B * a.G), dim3(kVNT), 0, st,
+  if (a.capmax <= (int64_t)kVNT * kVPMAX)
+    hipLaunchKernelGGL((k_value_alloc<GQA, true>), dim3(a.B * a.G), dim3(kVNT), 0, st,
                        (const uint8_t*)a.store, a.H, a.G, a.W, esize, a.RV, a.vscale, a.capmax,
-                       L.ntile, (const double*)(ws + L.logits), (const double*)(ws + L.tilepart),
+                       L.ntile, (const double*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
                        (double*)(ws + L.ftile), (double*)(ws + L.aval), tv);
   else
-    hipLaunchKernelGGL((k_value_alloc<false>), dim3(a.B * a.G), dim3(kVNT), 0, st,
+    hipLaunchKernelGGL((k_value_alloc<GQA, false>), dim3(a.B * a.G), dim3(kVNT), 0, st,
                        (const uint8_t*)a.store, a.H, a.G, a.W, esize, a.RV, a.vscale, a.capmax,
-                       L.ntile, (const double*)(ws + L.logits), (const double*)(ws + L.tilepart),
+                       L.ntile, (const double*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
                        (double*)(ws + L.ftile), (double*)(ws + L.aval), tv);
   mark(a, 3, st);
-  ok = a.dtype == 0 ? dispatch_gqa<0>(a, L, tk, tv, st, 1) : dispatch_gqa<1>(a, L, tk, tv, st, 1);
-  if (!ok) return -5;
+  hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(a.B * a.G, L.nchunk), dim3(256), 0, st,
+                     (const uint8_t*)a.store, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax, L.ntile,
+                     L.nchunk, (const _Float16*)(ws + L.e16), (const double*)(ws + L.ftile),
+                     (float*)(ws + L.opart));
+  const int64_t nout = (int64_t)a.B * a.H * kDim;
+  hipLaunchKernelGGL(k_out_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st,
+                     (const uint8_t*)a.store, a.H, L.nchunk, nout, (const float*)(ws + L.opart),
+                     a.out);
   mark(a, 4, st);
-  hipLaunchKernelGGL(k_out_reduce, dim3(a.B * a.H), dim3(128), 0, st, (const uint8_t*)a.store, a.H,
-                     L.nchunk, (const float*)(ws + L.opart), a.out);
-  mark(a, 5, st);
   return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+template <int DT>
+static int dispatch_gqa(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
+  switch (a.H / a.G) {
+    case 1: return launch_all<1, DT>(a, L, st);
+    case 2: return launch_all<2, DT>(a, L, st);
+    case 3: return launch_all<3, DT>(a, L, st);
+    case 4: return launch_all<4, DT>(a, L, st);
+    case 5: return launch_all<5, DT>(a, L, st);
+    case 6: return launch_all<6, DT>(a, L, st);
+    case 7: return launch_all<7, DT>(a, L, st);
+    case 8: return launch_all<8, DT>(a, L, st);
+    default: return -5;
+  }
+}
+
+int launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const WsLayout L = ws_layout(a.B, a.H, a.G, kDim, a.capmax);
+  return a.dtype == 0 ? dispatch_gqa<0>(a, L, st) : dispatch_gqa<1>(a, L, st);
 }
 
 }  // namespace readkv

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void k_encode_groups(uint8_t* store, const voi
       uint32_t word = 0;
 #pragma unroll
       for (int s = 0; s < kGroup; ++s) word |= ((code[s] >> (W - 1 - p)) & 1u) << s;
-      u.kplanes[((int64_t)c * W + p) * u.ng + gam] = word;
+      u.kplanes[((int64_t)c * W + p) * u.ngk + gam] = word;
     }
   } else {
     u.vmeta[gam * kDim + c] = meta;

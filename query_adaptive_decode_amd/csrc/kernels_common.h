@@ -39,6 +39,11 @@ __device__ __forceinline__ double ldexp_pow2(int e) {
   return bitsd((uint64_t)(e + 1023) << 52);
 }
 
+__device__ __forceinline__ float ldexp_pow2f(int e) {
+  // 2^e for -126 <= e <= 127
+  return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
 // wave64 helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 

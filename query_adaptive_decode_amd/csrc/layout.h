@@ -5,8 +5,10 @@
 // rounded up to 4096 bytes.  A request region with capacity `cap` tokens
 // (multiple of 32, ng = cap/32 groups) holds, each sub-array 256-byte
 // aligned:
-//   Kplanes u32 [G][d][W][ng]      token-packed: bit i of word (g,c,p,gamma)
-//                                  is plane p of token 32*gamma+i, channel c
+//   Kplanes u32 [G][d][W][ngk]     token-packed: bit i of word (g,c,p,gamma)
+//                                  is plane p of token 32*gamma+i, channel c;
+//                                  ngk = ng rounded up to a multiple of 4, so
+//                                  every 4-group run is one aligned 16 B load
 //   Vplanes u32 [G][cap][W][d/32]  channel-packed: a token's t-plane prefix
 //                                  is t*d/8 contiguous bytes
 //   Kmeta   u32 [G][ng][d]         lo bf16 | rng bf16 << 16
@@ -33,8 +35,9 @@ constexpr uint32_t kMagic = 0x52564B31u;
 constexpr uint32_t kVersion = 1u;
 constexpr int kGroup = 32;      // tokens per quantiser group
 constexpr int kDim = 128;       // head_dim supported by the kernels
-constexpr int kKeyTile = 1024;  // tokens per score workgroup (32 groups)
-constexpr int kValChunk = 256;  // tokens per value-gather workgroup
+constexpr int kTile = 512;      // tokens per score workgroup (16 groups);
+                                // also the softmax split-context unit
+constexpr int kChunk = 256;     // tokens per value-gather workgroup (8 groups)
 
 struct StoreHeader {          // first 256 bytes of a store
   uint32_t magic, version;
@@ -53,6 +56,9 @@ RKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 RKV_HD int64_t header_bytes(int B) { return align_up(256 + 32 * (int64_t)B, 4096); }
 
+// words per key-plane line (one (channel, plane) over all groups)
+RKV_HD int64_t key_line_words(int64_t cap) { return align_up(cap / kGroup, 4); }
+
 struct RegionLayout {
   int64_t kplanes, vplanes, kmeta, vmeta, ek, ev, ktail, vtail, size;
 };
@@ -61,7 +67,7 @@ RKV_HD RegionLayout region_layout(int G, int d, int W, int64_t cap, int esize) {
   const int64_t ng = cap / kGroup;
   RegionLayout L;
   int64_t off = 0;
-  L.kplanes = off; off += (int64_t)G * d * W * ng * 4; off = align_up(off, 256);
+  L.kplanes = off; off += (int64_t)G * d * W * key_line_words(cap) * 4; off = align_up(off, 256);
   L.vplanes = off; off += (int64_t)G * cap * W * (d / 32) * 4; off = align_up(off, 256);
   L.kmeta = off; off += (int64_t)G * ng * d * 4; off = align_up(off, 256);
   L.vmeta = off; off += (int64_t)G * ng * d * 4; off = align_up(off, 256);
@@ -75,7 +81,7 @@ RKV_HD RegionLayout region_layout(int G, int d, int W, int64_t cap, int esize) {
 
 // Pointers to one (request, KV head) unit's arrays.
 struct Unit {
-  uint32_t* kplanes;   // [d][W][ng]
+  uint32_t* kplanes;   // [d][W][ngk]
   uint32_t* vplanes;   // [cap][W][d/32]
   uint32_t* kmeta;     // [ng][d]
   uint32_t* vmeta;     // [ng][d]
@@ -83,7 +89,7 @@ struct Unit {
   double* ev;          // [ng]
   uint8_t* ktail;      // [32][d] elements
   uint8_t* vtail;
-  int64_t cap, ng;
+  int64_t cap, ng, ngk;
 };
 
 RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int W,
@@ -94,7 +100,8 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
   Unit u;
   u.cap = r.cap;
   u.ng = ng;
-  u.kplanes = (uint32_t*)(base + L.kplanes) + (int64_t)g * d * W * ng;
+  u.ngk = key_line_words(r.cap);
+  u.kplanes = (uint32_t*)(base + L.kplanes) + (int64_t)g * d * W * u.ngk;
   u.vplanes = (uint32_t*)(base + L.vplanes) + (int64_t)g * r.cap * W * (d / 32);
   u.kmeta = (uint32_t*)(base + L.kmeta) + (int64_t)g * ng * d;
   u.vmeta = (uint32_t*)(base + L.vmeta) + (int64_t)g * ng * d;
@@ -106,23 +113,33 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 }
 
 // Decode workspace (one call).  capmax = largest request capacity.
+//   tk     u8  [B][G][d]          key depths
+//   tv     u8  [B][G][capmax]     value depths
+//   ebuf   f64 [B][H][capmax]     exp(s - m_tile) per token (tile = kTile)
+//   e16    f16 [B][H][capmax]     the same rounded to fp16 (value gather)
+//   tilepart f64 [B][H][ntile][2] (m_tile, sum of exp) per tile
+//   ftile  f64 [B][H][ntile]      exp(m_tile - m) / Z
+//   aval   f64 [B][G][capmax]     value weights (only when they do not fit
+//                                 in the allocator's registers)
+//   opart  f32 [B][H][nchunk][d]  per-chunk partial outputs
 struct WsLayout {
-  int64_t tk, tv, logits, tilepart, ftile, aval, opart, size;
+  int64_t tk, tv, ebuf, e16, tilepart, ftile, aval, opart, size;
   int ntile, nchunk;
 };
 
 RKV_HD WsLayout ws_layout(int B, int H, int G, int d, int64_t capmax) {
   WsLayout L;
-  L.ntile = (int)((capmax + kKeyTile - 1) / kKeyTile);
-  L.nchunk = (int)((capmax + kValChunk - 1) / kValChunk);
+  L.ntile = (int)((capmax + kTile - 1) / kTile);
+  L.nchunk = (int)((capmax + kChunk - 1) / kChunk);
   int64_t off = 0;
-  L.tk = off; off = align_up(off + (int64_t)B * G * d, 256);                 // u8
-  L.tv = off; off = align_up(off + (int64_t)B * G * capmax, 256);            // u8
-  L.logits = off; off = align_up(off + (int64_t)B * H * capmax * 8, 256);    // f64
-  L.tilepart = off; off = align_up(off + (int64_t)B * H * L.ntile * 16, 256);// f64x2
-  L.ftile = off; off = align_up(off + (int64_t)B * H * L.ntile * 8, 256);   // f64
-  L.aval = off; off = align_up(off + (int64_t)B * G * capmax * 8, 256);      // f64
-  L.opart = off; off = align_up(off + (int64_t)B * H * L.nchunk * d * 4, 256); // f32
+  L.tk = off; off = align_up(off + (int64_t)B * G * d, 256);
+  L.tv = off; off = align_up(off + (int64_t)B * G * capmax, 256);
+  L.ebuf = off; off = align_up(off + (int64_t)B * H * capmax * 8, 256);
+  L.e16 = off; off = align_up(off + (int64_t)B * H * capmax * 2, 256);
+  L.tilepart = off; off = align_up(off + (int64_t)B * H * L.ntile * 16, 256);
+  L.ftile = off; off = align_up(off + (int64_t)B * H * L.ntile * 8, 256);
+  L.aval = off; off = align_up(off + (int64_t)B * G * capmax * 8, 256);
+  L.opart = off; off = align_up(off + (int64_t)B * H * L.nchunk * d * 4, 256);
   L.size = off;
   return L;
 }

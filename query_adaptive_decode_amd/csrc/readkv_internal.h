@@ -25,7 +25,7 @@ struct DecodeArgs {
   uint8_t* value_depths_out;
   int B, H, G, W, dtype;
   int64_t capmax;
-  void* const* events;  // NULL, or 6 hipEvent_t recorded around the 5 kernels
+  void* const* events;  // NULL, or 5 hipEvent_t recorded around the 4 kernels
 };
 
 int launch_store_zero(void* store, size_t bytes, hipStream_t st);

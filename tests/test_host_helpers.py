@@ -67,3 +67,54 @@ def test_transpose8_is_bit_transpose(probe):
                 if (x >> (8 * r + c)) & 1:
                     want |= 1 << (8 * c + r)
         assert y == want
+
+
+def test_transpose8_halves_matches_64bit_form(probe):
+    rng = np.random.default_rng(2)
+    xs = [int(x) for x in rng.integers(0, 2 ** 63, 300, dtype=np.int64)] + [0, 2 ** 64 - 1, 1 << 63, 0xFF]
+    want = [int(s, 16) for s in _run(probe, [f"t {x:x}" for x in xs])]
+    got = [int(s, 16) for s in _run(probe, [f"h {x:x}" for x in xs])]
+    assert got == want
+
+
+def _perm_ref(a, b, sel):
+    v = (a << 32) | b
+    r = 0
+    for i in range(4):
+        s = (sel >> (8 * i)) & 0xFF
+        byte = (v >> (8 * s)) & 0xFF if s < 8 else (0 if s == 0x0C else 0xFF)
+        r |= byte << (8 * i)
+    return r
+
+
+def test_byte_gather_and_unplane_give_prefix_codes(probe):
+    """The kernels' un-plane: gather byte `ob` of plane words w0..w7 with two
+    levels of byte permutes, transpose, and read token i's code from byte i.
+    Checked against direct bit extraction, with the permute model itself
+    checked against a direct byte-select reference."""
+    rng = np.random.default_rng(3)
+    lines = []
+    cases = []
+    for _ in range(60):
+        w = [int(x) for x in rng.integers(0, 2 ** 32, 8, dtype=np.uint64)]
+        t = int(rng.integers(1, 9))
+        w = [w[p] if p < t else 0 for p in range(8)]
+        ob = int(rng.integers(0, 4))
+        sel = 0x0C0C0000 | ((4 + ob) << 8) | ob
+        cases.append((w, t, ob, sel))
+        lines += [f"p {w[0]:x} {w[1]:x} {sel:x}", f"p {w[2]:x} {w[3]:x} {sel:x}",
+                  f"p {w[4]:x} {w[5]:x} {sel:x}", f"p {w[6]:x} {w[7]:x} {sel:x}"]
+    out = [int(s, 16) for s in _run(probe, lines)]
+    lines2 = []
+    for k, (w, t, ob, sel) in enumerate(cases):
+        r01, r23, r45, r67 = out[4 * k:4 * k + 4]
+        assert r01 == _perm_ref(w[0], w[1], sel) and r67 == _perm_ref(w[6], w[7], sel)
+        lines2 += [f"p {r01:x} {r23:x} 5040100", f"p {r45:x} {r67:x} 5040100"]
+    out2 = [int(s, 16) for s in _run(probe, lines2)]
+    lines3 = [f"h {(out2[2 * k] << 32) | out2[2 * k + 1]:x}" for k in range(len(cases))]
+    ys = [int(s, 16) for s in _run(probe, lines3)]
+    for (w, t, ob, sel), y in zip(cases, ys):
+        for i in range(8):
+            tok = 8 * ob + i
+            want = sum(((w[p] >> tok) & 1) << (7 - p) for p in range(8))
+            assert (y >> (8 * i)) & 0xFF == want
