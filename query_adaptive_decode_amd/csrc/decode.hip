@@ -48,12 +48,6 @@ __device__ __forceinline__ void unplane8(const uint32_t (&w)[8], uint32_t sel, u
   transpose8_halves(lo, hi);
 }
 
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // ---------------------------------------------------------------------------
 // Key allocation: one wave per (request, KV head).  Lane l holds channels l
 // and l+64 and their W candidate gains w_c 4^-t (t = 1..W).  The B_K largest
@@ -93,12 +87,12 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
     }
   }
   const uint32_t Bk = (uint32_t)floor((double)RK * (double)kDim);
-  uint32_t np = 0;
+  // wave-wide counts are sums of ballot popcounts over the 16 candidate slots
+  uint32_t npos = 0;
 #pragma unroll
   for (int k = 0; k < 2; ++k)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) np += key[k][t] != 0ull;
-  const uint32_t npos = wave_sum_u32(np);
+    for (int t = 0; t < 8; ++t) npos += (uint32_t)__popcll(__ballot(key[k][t] != 0ull));
 
   uint32_t sel[2] = {0u, 0u};
   if (npos <= Bk) {
@@ -115,21 +109,21 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
 #pragma unroll
       for (int k = 0; k < 2; ++k)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) c_ += key[k][t] != 0ull && (int)(key[k][t] >> 52) >= mid;
-      if (wave_sum_u32(c_) >= Bk) lo = mid;
+        for (int t = 0; t < 8; ++t)
+          c_ += (uint32_t)__popcll(__ballot(key[k][t] != 0ull && (int)(key[k][t] >> 52) >= mid));
+      if (c_ >= Bk) lo = mid;
       else hi = mid - 1;
     }
     const int Es = lo;
-    uint32_t ab = 0, at = 0;
+    uint32_t above = 0, at = 0;
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         const int e = (int)(key[k][t] >> 52);
-        ab += key[k][t] != 0ull && e > Es;
+        above += (uint32_t)__popcll(__ballot(key[k][t] != 0ull && e > Es));
         at += key[k][t] != 0ull && e == Es;
       }
-    const uint32_t above = wave_sum_u32(ab);
     const uint32_t rem = Bk - above;  // >= 1 by the choice of Es
     // candidates in class Es: with normal gains at most one level per
     // channel; lane slot k holds channel lane + 64 k
@@ -254,7 +248,7 @@ __global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void*
   constexpr int NG = kTile / kGroup;  // 16
   extern __shared__ uint32_t planes[];
   __shared__ double qs[GQA][kDim];
-  __shared__ uint32_t meta[NG][kDim];
+  __shared__ uint32_t meta[NG][kDim + 1];  // padded: the 16 groups fall in distinct banks
   __shared__ double Cs[NG][GQA];
   __shared__ double tails[kGroup][GQA];
   __shared__ double red[4][GQA];
@@ -351,10 +345,7 @@ __global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void*
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) {
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ca[hh] += __shfl_xor(ca[hh], o, 64);
-    }
+    for (int hh = 0; hh < GQA; ++hh) ca[hh] = group_sum<16>(ca[hh]);
     if (cs == 0)
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) Cs[gl][hh] = ca[hh];
@@ -402,21 +393,27 @@ __global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void*
       }
     }
   }
-  // ---- the four waves' partial sums, added in wave order ----
-  double* wred = reinterpret_cast<double*>(planes);  // [8 * GQA][64]
+  // ---- the four waves' partial sums: waves 0,1 store, waves 2,3 add; the
+  // epilogue adds the two buffers (fixed order (w0 + w2) + (w1 + w3)) ----
+  double* wred = reinterpret_cast<double*>(planes);  // [2][8 * GQA][64]
   __syncthreads();
-  for (int w = 0; w < 4; ++w) {
-    if (wv == w) {
+  if (wv < 2) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 8; ++e)
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) {
-          double* p = wred + (e * GQA + hh) * 64 + lane;
-          *p = (w == 0) ? acc[e][hh] : (*p + acc[e][hh]);
-        }
-    }
-    __syncthreads();
+      for (int hh = 0; hh < GQA; ++hh) wred[(wv * 8 * GQA + e * GQA + hh) * 64 + lane] = acc[e][hh];
   }
+  __syncthreads();
+  if (wv >= 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) {
+        double* p = wred + ((wv - 2) * 8 * GQA + e * GQA + hh) * 64 + lane;
+        *p = *p + acc[e][hh];
+      }
+  }
+  __syncthreads();
 
   // ---- 4. open group (exact keys) ----
   const int64_t ntail = len - Tp;
@@ -434,19 +431,16 @@ __global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void*
       }
     }
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) {
-      st[hh] += __shfl_xor(st[hh], 1, 64);
-      st[hh] += __shfl_xor(st[hh], 2, 64);
-      st[hh] += __shfl_xor(st[hh], 4, 64);
-    }
+    for (int hh = 0; hh < GQA; ++hh) st[hh] = group_sum<8>(st[hh]);
     if (part == 0 && rr < ntail)
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) tails[rr][hh] = st[hh] * kInvSqrtD;
   }
   __syncthreads();
 
-  // ---- softmax partials: thread -> tokens 2 tid, 2 tid + 1 of the tile ----
-  const int oc = tid >> 2, e0 = 2 * (tid & 3);
+  // ---- softmax partials: thread (oc = tid % 64, pair = tid / 64) finishes
+  // tokens 8 oc + 2 pair and 8 oc + 2 pair + 1 of the tile ----
+  const int oc = lane, e0 = 2 * wv;
   const int glt = oc >> 2;
   const bool pk = glt < ngp;
   const bool has_tail = tail_here && tid < ntail;
@@ -455,7 +449,9 @@ __global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void*
   for (int k = 0; k < 2; ++k)
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh)
-      sv[k][hh] = pk ? (Cs[glt][hh] + wred[((e0 + k) * GQA + hh) * 64 + oc]) * kInvSqrtD : 0.0;
+      sv[k][hh] = pk ? (Cs[glt][hh] + (wred[((e0 + k) * GQA + hh) * 64 + oc] +
+                                        wred[(8 * GQA + (e0 + k) * GQA + hh) * 64 + oc])) * kInvSqrtD
+                     : 0.0;
   double mt[GQA];
 #pragma unroll
   for (int hh = 0; hh < GQA; ++hh) {
@@ -473,18 +469,19 @@ __global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void*
     const int64_t row = ((int64_t)b * H + (int64_t)g * GQA + hh) * capmax;
     double z = 0.0;
     if (pk) {
-      const int64_t j = t0 + 2 * tid;
+      const int64_t j = t0 + 8 * oc + e0;  // even: the pair is 16 B / 4 B aligned
       const double ea = exp(sv[0][hh] - mt[hh]), eb = exp(sv[1][hh] - mt[hh]);
-      ebuf[row + j] = ea;
-      ebuf[row + j + 1] = eb;
-      e16[row + j] = (_Float16)ea;
-      e16[row + j + 1] = (_Float16)eb;
+      *reinterpret_cast<double2*>(ebuf + row + j) = make_double2(ea, eb);
+      f16x2 hp;
+      hp.x = (_Float16)(float)ea;
+      hp.y = (_Float16)(float)eb;
+      *reinterpret_cast<f16x2*>(e16 + row + j) = hp;
       z = ea + eb;
     }
     if (has_tail) {
       const double ev = exp(tails[tid][hh] - mt[hh]);
       ebuf[row + Tp + tid] = ev;
-      e16[row + Tp + tid] = (_Float16)ev;
+      e16[row + Tp + tid] = (_Float16)(float)ev;
       z += ev;
     }
     z = wave_sum(z);
@@ -754,31 +751,51 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
 
 // ---------------------------------------------------------------------------
 // Gather: one block of 256 threads per 256-token chunk (8 groups) of one
-// (request, KV head).  The chosen value plane rows (16 B per token and
-// plane) are staged in LDS.  Lane (group gl, token parity ts, channel octet
-// bo) walks its 16 tokens of group gl in pairs and accumulates, per head,
-//   A = sum e,  Bh = sum e 2^-(t+1),  U_c = sum e X_c
-// with e = exp(s - m_tile) rounded to fp16 and X_c the un-planed 8-bit
-// prefix codes, via fp16 dot products (X enters as the fp16 value 1024 + X;
-// the 1024 A part is removed afterwards).  Per group,
-//   sum_j e_j v_hat_jc = lo_c A + rng_c (Bh + U_c / 256).
-// The chunk partial is f_{h,tile} times the sum over the chunk's groups.
-// Grid (unit, chunk): consecutive blocks are different units, so all chunks
-// of a unit are dispatched to the same XCD.
+// (request, KV head).
+//  1. The chosen value plane rows (16 B per token and plane) are staged in
+//     LDS.
+//  2. Every refined token (t > 0) is un-planed: 16 lanes per token, one per
+//     8-channel octet, byte gather + 8x8 bit transpose, and its prefix codes
+//     X (= P 2^(8-t)) are written token-major to an LDS code tile (tokens
+//     with t = 0 keep X = 0).  Deep (t > 4) and shallow tokens are processed
+//     from two separate lists so that the code path is uniform per wave.
+//  3. Per group gamma and head h, with e = exp(s - m_tile) rounded to fp16,
+//       sum_j e_j v_hat_jc = lo_c A + rng_c (Bh + U_c / 256),
+//     A = sum e, Bh = sum e 2^-(t+1), U_c = sum e X_c.  U comes from
+//     v_mfma_f32_16x16x32_f16: A operand = codes of 16 channels x 32 tokens
+//     (one group), read channel-major from the code tile with the LDS
+//     transpose read and turned into the fp16 values 1024 + X by one byte
+//     permute per pair; B operand = e for 16 columns (head, group) with
+//     zeros off the column's own group, so one column set covers 16/GQA
+//     groups; the 1024 A part is removed when the group is folded in.
+//  4. Column partials are added per head in group order, open-group tokens
+//     (exact values) are added, and the chunk partial f_{h,tile} O is
+//     written.  Grid (unit, chunk): all chunks of a unit on one XCD.
 // ---------------------------------------------------------------------------
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
 template <int GQA, int DT>
 __global__ __launch_bounds__(256) void k_gather(const uint8_t* store, const uint8_t* tv, int H, int G,
                                                 int W, int64_t capmax, int ntile_ws, int nchunk_ws,
                                                 const _Float16* e16, const double* ftile,
                                                 float* opart) {
   constexpr int esize = DT == 0 ? 2 : 4;
-  constexpr int NG = kChunk / kGroup;  // 8
-  __shared__ uint4 vrows[kChunk * 8];
+  constexpr int NG = kChunk / kGroup;                       // 8 groups per chunk
+  constexpr int GS = (16 / GQA < NG) ? 16 / GQA : NG;       // groups per MFMA column set
+  constexpr int NSET = (NG + GS - 1) / GS;
+  constexpr int XS = kDim + 8;  // code-tile row stride: rows 2 apart fall in different banks
+  __shared__ uint4 vrows[kChunk * 8];                       // staged rows; reused below
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kChunk * XS];    // codes [token][channel]
+  __shared__ __attribute__((aligned(16))) _Float16 es[GQA][kChunk];
   __shared__ uint32_t vmeta_s[NG][kDim];
-  __shared__ _Float16 es[GQA][kChunk];
+  __shared__ float Ag[NG][GQA], Bg[NG][GQA];
   __shared__ uint16_t offs[kChunk];
   __shared__ uint8_t tvs[kChunk];
   __shared__ uint8_t s2t[kChunk * 8];
+  __shared__ uint8_t lst[kChunk];
   __shared__ float fs[GQA];
   __shared__ uint32_t wsum[256 / 64 + 1];
 
@@ -792,6 +809,7 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t* store, const uint
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int tile = (int)(c0 / kTile);
   const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
+  const int64_t gam0 = c0 / kGroup;
 
   {
     const int64_t j = c0 + tid;
@@ -801,18 +819,31 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t* store, const uint
       es[hh][tid] = (j < len) ? e16[(hrow0 + hh) * capmax + j] : (_Float16)0.0f;
     for (int i = tid; i < NG * kDim; i += 256) {
       const int gl = i / kDim, c = i % kDim;
-      const int64_t gam = c0 / kGroup + gl;
+      const int64_t gam = gam0 + gl;
       vmeta_s[gl][c] = ((gam + 1) * kGroup <= Tp) ? u.vmeta[gam * kDim + c] : 0u;
     }
     if (tid < GQA) fs[tid] = (float)ftile[(hrow0 + tid) * ntile_ws + tile];
+    uint2* xz = reinterpret_cast<uint2*>(xl);
+    for (int i = tid; i < kChunk * XS / 8; i += 256) xz[i] = make_uint2(0u, 0u);
   }
   __syncthreads();
+  // one scan for three prefix sums: slots (12 bits), deep tokens (9 bits)
+  // and shallow tokens (9 bits), packed in one word
   const uint32_t tj = tvs[tid];
-  const uint32_t ex = block_excl_scan<256>(tj, wsum);
-  const int nslots = (int)wsum[256 / 64];
+  const uint32_t deep = tj > 4u ? 1u : 0u, shallow = (tj >= 1u && tj <= 4u) ? 1u : 0u;
+  const uint32_t pk3 = block_excl_scan<256>(tj | (deep << 12) | (shallow << 21), wsum);
+  const uint32_t tot3 = wsum[256 / 64];
+  const uint32_t ex = pk3 & 0xFFFu, pd = (pk3 >> 12) & 0x1FFu, ps = pk3 >> 21;
+  const int nslots = (int)(tot3 & 0xFFFu);
+  const int ndeep = (int)((tot3 >> 12) & 0x1FFu);
+  const int nref = ndeep + (int)(tot3 >> 21);
   offs[tid] = (uint16_t)ex;
   for (uint32_t p = 0; p < tj; ++p) s2t[ex + p] = (uint8_t)tid;
+  if (deep) lst[pd] = (uint8_t)tid;
+  if (shallow) lst[ndeep + ps] = (uint8_t)tid;
   __syncthreads();
+
+  // ---- 1. stage the chosen rows ----
   {
     const uint4* vp = reinterpret_cast<const uint4*>(u.vplanes);
     for (int base = 0; base < nslots; base += 256 * 8) {
@@ -834,117 +865,125 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t* store, const uint
       }
     }
   }
+  // per-group sums of e (A) and of e 2^-(t+1) (Bh): TPP threads per
+  // (group, head), each over 32/TPP tokens, then a shuffle reduction
+  {
+    constexpr int NP = NG * GQA;
+    constexpr int TPP = NP <= 8 ? 32 : (NP <= 16 ? 16 : (NP <= 32 ? 8 : 4));
+    constexpr int TK = kGroup / TPP;
+    const int pr = tid / TPP, part = tid % TPP;
+    float a = 0.f, bh = 0.f;
+    if (pr < NP) {
+      const int gl = pr / GQA, hh = pr % GQA;
+#pragma unroll
+      for (int k = 0; k < TK; ++k) {
+        const int jl = kGroup * gl + part * TK + k;
+        const float e = (float)es[hh][jl];
+        a += e;
+        bh = fmaf(e, ldexp_pow2f(-(int)tvs[jl] - 1), bh);
+      }
+    }
+    a = group_sum<TPP>(a);
+    bh = group_sum<TPP>(bh);
+    if (pr < NP && part == 0) {
+      Ag[pr / GQA][pr % GQA] = a;
+      Bg[pr / GQA][pr % GQA] = bh;
+    }
+  }
   __syncthreads();
 
-  const int gsl = lane >> 5, ts = (lane >> 4) & 1, bo = lane & 15;
-  const int gl = 2 * wv + gsl;
-  const int64_t gam = c0 / kGroup + gl;
-  const bool gpacked = (gam + 1) * kGroup <= Tp;
-  const int wb = bo >> 2, ob = bo & 3;
-  const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)ob) << 8) | (uint32_t)ob;
-  const uint32_t* rows = reinterpret_cast<const uint32_t*>(vrows);
-  float O[GQA][8];
+  // ---- 2. un-plane refined tokens into the code tile ----
+  {
+    const int bo = lane & 15, wb = bo >> 2, ob = bo & 3;
+    const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)ob) << 8) | (uint32_t)ob;
+    const uint32_t* rows = reinterpret_cast<const uint32_t*>(vrows);
+    for (int i = 4 * wv + (lane >> 4); i < ndeep; i += 16) {
+      const int jl = lst[i];
+      const int t = tvs[jl], s0 = offs[jl];
+      uint32_t w[8];
 #pragma unroll
-  for (int hh = 0; hh < GQA; ++hh)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) O[hh][i] = 0.f;
+      for (int p = 0; p < 8; ++p) w[p] = (p < t) ? rows[(s0 + p) * 4 + wb] : 0u;
+      uint32_t lo, hi;
+      unplane8(w, sel, lo, hi);
+      *reinterpret_cast<uint2*>(xl + jl * XS + 8 * bo) = make_uint2(lo, hi);
+    }
+    for (int i = ndeep + 4 * wv + (lane >> 4); i < nref; i += 16) {
+      const int jl = lst[i];
+      const int t = tvs[jl], s0 = offs[jl];
+      const uint32_t w0 = rows[s0 * 4 + wb];
+      const uint32_t w1 = t > 1 ? rows[(s0 + 1) * 4 + wb] : 0u;
+      const uint32_t w2 = t > 2 ? rows[(s0 + 2) * 4 + wb] : 0u;
+      const uint32_t w3 = t > 3 ? rows[(s0 + 3) * 4 + wb] : 0u;
+      uint32_t lo, hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w0, w1, sel),
+                                              __builtin_amdgcn_perm(w2, w3, sel), 0x05040100u);
+      transpose8_hi4(lo, hi);
+      *reinterpret_cast<uint2*>(xl + jl * XS + 8 * bo) = make_uint2(lo, hi);
+    }
+  }
+  __syncthreads();
 
-  if (gpacked) {
-    float A[GQA], Bh[GQA], U[GQA][8];
+  // ---- 3. MFMA per (16-channel block, column set); wave wv: blocks 2wv, 2wv+1 ----
+  const int m = lane & 15, kb = lane >> 4;
+  const int gp = m / GQA, hn = m % GQA;
+  const bool colv = m < GS * GQA;
+  float Oacc[2][4];
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) {
-      A[hh] = 0.f;
-      Bh[hh] = 0.f;
+  for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) U[hh][i] = 0.f;
-    }
-    for (int k = 0; k < 8; ++k) {
-      const int jA = 32 * gl + ts + 4 * k, jB = jA + 2;
-      uint32_t ya[2], yb[2];
-      const int tA = tvs[jA], tB = tvs[jB];
-      {
-        uint32_t w[8];
-        const int s0 = offs[jA];
+    for (int rr = 0; rr < 4; ++rr) Oacc[bl][rr] = 0.f;
+  for (int set = 0; set < NSET; ++set) {
+    const int gbase = set * GS;
 #pragma unroll
-        for (int p = 0; p < 8; ++p) w[p] = (p < tA) ? rows[(s0 + p) * 4 + wb] : 0u;
-        unplane8(w, sel, ya[0], ya[1]);
+    for (int bl = 0; bl < 2; ++bl) {
+      const int cb = 16 * (2 * wv + bl);
+      f32x4 D = {0.f, 0.f, 0.f, 0.f};
+      for (int gi = 0; gi < GS; ++gi) {
+        const int gl = gbase + gi;
+        if (gl >= NG || (gam0 + gl + 1) * kGroup > Tp) continue;
+        const int t0 = kGroup * gl + 8 * kb;
+        const uint8_t* src = xl + (t0 + (m >> 1)) * XS + cb + 8 * (m & 1);
+        const i32x2 xv = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)src);
+        uint32_t ap[4];
+        ap[0] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.x, 0x04010400u);
+        ap[1] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.x, 0x04030402u);
+        ap[2] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.y, 0x04010400u);
+        ap[3] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.y, 0x04030402u);
+        const f16x8 av = __builtin_bit_cast(f16x8, ap);
+        f16x8 bv = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (colv && gp == gi) bv = *reinterpret_cast<const f16x8*>(&es[hn][t0]);
+        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, D, 0, 0, 0);
       }
-      {
-        uint32_t w[8];
-        const int s0 = offs[jB];
+      // fold: D row = channel cb + 4 kb + rr, column m = (gp, hn)
+      const int gl = gbase + gp;
+      if (colv && gl < NG && (gam0 + gl + 1) * kGroup <= Tp) {
+        const float A = Ag[gl][hn], Bh = Bg[gl][hn];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) w[p] = (p < tB) ? rows[(s0 + p) * 4 + wb] : 0u;
-        unplane8(w, sel, yb[0], yb[1]);
-      }
-      uint32_t P[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sl = 0x0C000C00u | ((uint32_t)(4 + (i & 3)) << 16) | (uint32_t)(i & 3);
-        P[i] = __builtin_amdgcn_perm(yb[i >> 2], ya[i >> 2], sl) | 0x64006400u;
-      }
-      const float hA_ = ldexp_pow2f(-tA - 1), hB_ = ldexp_pow2f(-tB - 1);
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) {
-        f16x2 ep;
-        ep.x = es[hh][jA];
-        ep.y = es[hh][jB];
-        const float ea = (float)ep.x, eb2 = (float)ep.y;
-        A[hh] += ea + eb2;
-        Bh[hh] = fmaf(ea, hA_, fmaf(eb2, hB_, Bh[hh]));
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          U[hh][i] = __builtin_amdgcn_fdot2(ep, __builtin_bit_cast(f16x2, P[i]), U[hh][i], false);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t m = vmeta_s[gl][8 * bo + i];
-      const float lo = bf16_to_float(m & 0xFFFFu), rng = bf16_to_float(m >> 16);
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh)
-        O[hh][i] = fmaf(lo, A[hh], rng * (Bh[hh] + (U[hh][i] - 1024.f * A[hh]) * (1.f / 256.f)));
-    }
-  } else {
-    // open group: exact values
-    for (int k = 0; k < kGroup / 2; ++k) {
-      const int jl = 32 * gl + ts + 2 * k;
-      const int64_t j = c0 + jl;
-      if (j < Tp || j >= len) continue;
-      const int64_t slot = j - Tp;
-      float v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = load_elem_f<DT>(u.vtail, slot * kDim + 8 * bo + i);
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) {
-        const float e = (float)es[hh][jl];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) O[hh][i] = fmaf(e, v[i], O[hh][i]);
+        for (int rr = 0; rr < 4; ++rr) {
+          const uint32_t mt = vmeta_s[gl][cb + 4 * kb + rr];
+          const float lo = bf16_to_float(mt & 0xFFFFu), rng = bf16_to_float(mt >> 16);
+          Oacc[bl][rr] += fmaf(lo, A, rng * (Bh + (D[rr] - 1024.f * A) * (1.f / 256.f)));
+        }
       }
     }
   }
-  // reduce over (group slot, token parity) within the wave, then over waves
-#pragma unroll
-  for (int hh = 0; hh < GQA; ++hh)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float v = O[hh][i] * fs[hh];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      O[hh][i] = v;
-    }
   __syncthreads();
-  float* red = reinterpret_cast<float*>(vrows);  // [4][GQA][128]
-  if (lane < 16)
+  float* red2 = reinterpret_cast<float*>(vrows);  // [16 columns][128 channels]
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh)
+  for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) red[(wv * GQA + hh) * kDim + 8 * bo + i] = O[hh][i];
+    for (int rr = 0; rr < 4; ++rr) red2[m * kDim + 16 * (2 * wv + bl) + 4 * kb + rr] = Oacc[bl][rr];
   __syncthreads();
+
+  // ---- 4. per-head sums over the column groups, open group, chunk partial ----
+  const int64_t jt0 = Tp > c0 ? Tp : c0;
+  const int64_t jt1 = len < c0 + kChunk ? len : c0 + kChunk;
   for (int o = tid; o < GQA * kDim; o += 256) {
     const int hh = o / kDim, c = o % kDim;
-    const float s = (red[(0 * GQA + hh) * kDim + c] + red[(1 * GQA + hh) * kDim + c]) +
-                    (red[(2 * GQA + hh) * kDim + c] + red[(3 * GQA + hh) * kDim + c]);
-    opart[((hrow0 + hh) * nchunk_ws + chunk) * kDim + c] = s;
+    float s = 0.f;
+    for (int q = 0; q < GS; ++q) s += red2[(q * GQA + hh) * kDim + c];
+    for (int64_t j = jt0; j < jt1; ++j)
+      s = fmaf((float)es[hh][j - c0], load_elem_f<DT>(u.vtail, (j - Tp) * kDim + c), s);
+    opart[((hrow0 + hh) * nchunk_ws + chunk) * kDim + c] = s * fs[hh];
   }
 }
 
@@ -994,7 +1033,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   double bk = floor((double)a.RK * (double)kDim);
   if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
   size_t dyn = (size_t)(kTile / kGroup) * (size_t)(((int)bk) | 1) * 4;
-  const size_t dyn_red = (size_t)64 * 8 * GQA * 8;  // wave reduction buffer
+  const size_t dyn_red = (size_t)2 * 64 * 8 * GQA * 8;  // wave reduction buffers
   if (dyn < dyn_red) dyn = dyn_red;
   static bool attr_set = false;
   if (!attr_set) {

@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "bitops.h"
 #include "layout.h"
 
@@ -44,19 +46,85 @@ __device__ __forceinline__ float ldexp_pow2f(int e) {
   return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
-// wave64 helpers
+// wave64 helpers built on DPP lane moves (no LDS round trips).
+// DPP control codes of the GFX9 family.
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = dbits(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return bitsd(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = dbits(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return bitsd(((uint64_t)hi << 32) | lo);
+}
+
+// op-reduction over each 16-lane row; every lane of the row gets the result
+template <typename T, typename Op>
+__device__ __forceinline__ T row_reduce(T v, Op op) {
+  if constexpr (sizeof(T) == 8) {
+    v = op(v, dpp_f64<kDppQuadXor1>(v));
+    v = op(v, dpp_f64<kDppQuadXor2>(v));
+    v = op(v, dpp_f64<kDppRowHalfMirror>(v));
+    v = op(v, dpp_f64<kDppRowMirror>(v));
+  } else {
+    v = op(v, dpp_f32<kDppQuadXor1>(v));
+    v = op(v, dpp_f32<kDppQuadXor2>(v));
+    v = op(v, dpp_f32<kDppRowHalfMirror>(v));
+    v = op(v, dpp_f32<kDppRowMirror>(v));
+  }
   return v;
 }
-__device__ __forceinline__ double wave_max(double v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
+
+// sum over groups of P consecutive lanes (P = 2, 4, 8, 16, 32, 64); every
+// lane of a group gets its group's sum
+template <int P, typename T>
+__device__ __forceinline__ T group_sum(T v) {
+  auto dpp = [](T x, auto ctrl) {
+    if constexpr (sizeof(T) == 8) return dpp_f64<decltype(ctrl)::value>(x);
+    else return dpp_f32<decltype(ctrl)::value>(x);
+  };
+  if constexpr (P >= 2) v += dpp(v, std::integral_constant<int, kDppQuadXor1>{});
+  if constexpr (P >= 4) v += dpp(v, std::integral_constant<int, kDppQuadXor2>{});
+  if constexpr (P >= 8) v += dpp(v, std::integral_constant<int, kDppRowHalfMirror>{});
+  if constexpr (P >= 16) v += dpp(v, std::integral_constant<int, kDppRowMirror>{});
+  if constexpr (P >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (P >= 64) v += __shfl_xor(v, 32, 64);
   return v;
+}
+
+// sum / max over the wave (rows combined in fixed order 0,1,2,3)
+__device__ __forceinline__ double wave_sum(double v) {
+  v = row_reduce(v, [](double a, double b) { return a + b; });
+  return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
+}
+__device__ __forceinline__ double wave_max(double v) {
+  v = row_reduce(v, [](double a, double b) { return fmax(a, b); });
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_reduce(v, [](float a, float b) { return a + b; });
+  auto rl = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+  return (rl(v, 0) + rl(v, 16)) + (rl(v, 32) + rl(v, 48));
 }
 
 }  // namespace readkv

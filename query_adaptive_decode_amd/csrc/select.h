@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels_common.h"
+
 namespace readkv {
 
 // Outcome of a threshold search: a key is chosen iff it is positive and
@@ -25,13 +27,15 @@ struct Threshold {
   int all_pos;
 };
 
+// inclusive prefix sum over the wave: DPP row shifts inside each 16-lane
+// row, then the row totals broadcast to the following rows
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
-  const int l = __lane_id();
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (l >= o) v += t;
-  }
+  v += dpp_u32<kDppRowShr1>(v);
+  v += dpp_u32<kDppRowShr2>(v);
+  v += dpp_u32<kDppRowShr4>(v);
+  v += dpp_u32<kDppRowShr8>(v);
+  v += dpp_u32<kDppRowBcast15, 0xA>(v);
+  v += dpp_u32<kDppRowBcast31, 0xC>(v);
   return v;
 }
 
