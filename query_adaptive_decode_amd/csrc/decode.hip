@@ -197,30 +197,54 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
 }
 
 // ---------------------------------------------------------------------------
-// Score: one block of 256 threads per 512-token tile (16 groups) of one
-// (request, KV head).
-//  1. Stage in LDS the tile's segment of every chosen key line (channel c,
-//     plane p < t^K_c): 16 words = 64 B per line, loaded as 16 B pieces, and
-//     the tile's key metadata.  LDS layout planes[group][slot], slot =
-//     (sum over channels below c of t^K) + p.
-//  2. Per-group constants
-//       C_h = sum_c q_hc (lo_c + rng_c 2^-(t_c+1)) - 4096 sum_{t_c>0} beta_hc
-//     with beta_hc = q_hc rng_c / 256 (exact products of bf16 values).
-//  3. Wave w takes channels w, w+4, ... (so a channel's depth t is uniform
-//     in the wave), lane o its 8 tokens 8o..8o+7 of the tile.  Per channel
-//     the lane gathers byte o%4 of its group's t plane words, transposes the
-//     8x8 bit block into the tokens' prefix codes X and accumulates
-//     beta_hc (4096 + X) in fp64; 4096 + X is assembled as a double straight
-//     from the code byte (one byte permute), the 4096 part cancels against C.
-//  4. The four waves' sums are added in wave order through LDS; logits
-//     s = (C + sum) / sqrt(d); open-group tokens use exact keys.  Each thread
-//     finishes two tokens: e = exp(s - m_tile) (fp64, and rounded to fp16 for
-//     the value gather) and the block writes (m_tile, sum e) per head.
-// Grid (unit, tile): consecutive blocks are different units, so all tiles
-// of a unit run on one XCD and share its L2 (a 128 B line holds two tiles'
-// 64 B segments of a key line).
-// Dynamic LDS: max(16 * (max slots | 1) words, the 64 x 8 x GQA fp64 wave
-// reduction buffer).
+// Score: a block of 256 threads takes a run of consecutive 512-token tiles
+// (16 groups each) of one (request, KV head).  The logit of token j and
+// query head h is
+//   s_hj = (C_gh + sum_c beta_hc X'_jc) / sqrt(d),
+//   beta_hc = q_hc rng_gc / 256,  X' = X - 128 (X = P 2^(8-t), the prefix
+//   code in the top bits of a byte),
+//   C_gh = sum_c q_hc (lo_gc + rng_gc 2^-(t_c+1) + [t_c > 0] rng_gc / 2)
+// (the reconstruction x_hat = lo + rng 2^-(t+1) + rng X / 256 with the -128
+// offset folded into C; channels with t_c = 0 contribute only to C).
+// The sum over channels is an exact integer matrix product on the int8
+// matrix cores: with a per-head power of two 2^sig_h (so that every
+// |q_hc rng_gc| 2^sig_h < 2^46), the integer N_hc = rint(q_hc rng_gc 2^sig_h)
+// is split into six signed 8-bit digits, and
+//   sum_c beta_hc X'_jc = 2^(-sig_h - 8) sum_k 2^(8k) sum_c digit_k(N_hc) X'_jc
+// with every inner sum exact in int32.  One fp64 FMA produces the digits:
+// q 2^sig * rng + (2^52 + 0x808080808080) rounds q rng 2^sig to an integer
+// N and leaves N + 0x808080808080 in the low 48 mantissa bits, whose byte k
+// is digit_k + 128 (flipping bit 7 gives the two's-complement digit).
+// The rounding error of N is below 2^-46 of the per-head bound, far below
+// the float64 rounding of the reconstructed logits it replaces.
+//
+// Once per block: depths, query, per-head scales, the slot table.  Per tile:
+//  1. The tile's segment of every chosen key line (channel c, plane p < t_c;
+//     16 words = 64 B) sits in LDS as planes[slot][group], slot = (sum of t
+//     over channels below c) + p.  The next tile's segments and metadata are
+//     in flight to registers while this tile is computed; they are written
+//     to LDS after its last un-plane, and the loads for the tile after are
+//     issued at once.  Barriers inside the tile loop wait for LDS traffic
+//     only, never for those loads.
+//  2. Per-group constants C_gh in fp64 (16 lanes per group, DPP sums).
+//  3. Four slabs of 32 channels.  Un-plane: wave w takes the slab's channels
+//     w, w+4, ... (uniform depth in the wave, taken from a scalar table),
+//     lane o the tile's tokens 8o..8o+7: byte o%4 of its group's t plane
+//     words, an 8x8 bit transpose gives the 8 codes (the top plane inverted
+//     first, which makes them X'), stored as a code tile [channel][token].
+//     MFMA: wave w takes groups 4w..4w+3; per group it writes the digit
+//     words of its 32 channels x GQA heads, then v_mfma_i32_16x16x32_i8 with
+//     A = digits and B = codes (16 tokens x 32 channels), both read with the
+//     transposing ds_read_b64_tr_b8, accumulating over the slabs.  An A chunk
+//     holds digits 4m..4m+3 of two heads, so the 16 rows of one MFMA are
+//     (4 heads) x (4 digits) and lane l of the result holds all its digits of
+//     head l/16 for token l%16: the digit sums are combined in-lane.
+//  4. Digit sums -> logits (fp64) in registers; open-group tokens use exact
+//     keys; per head the tile max m, e = exp(s - m) (fp64, and rounded to
+//     fp16 for the value gather) and sum e (split-context softmax).
+// Grid (unit, run): consecutive blocks are different units, so all runs of
+// a unit are on one XCD and share its L2.
+// Dynamic LDS: 64 B per staged slot (at most min(B_K, 128 W) slots).
 // ---------------------------------------------------------------------------
 // transpose8_halves for lo == 0 (at most 4 planes present)
 __device__ __forceinline__ void transpose8_hi4(uint32_t& lo, uint32_t& hi) {
@@ -234,52 +258,135 @@ __device__ __forceinline__ void transpose8_hi4(uint32_t& lo, uint32_t& hi) {
   hi ^= t >> 4;
 }
 
-// the double 4096 + (byte i of y), built from its bit pattern
-__device__ __forceinline__ double code_plus_4096(uint32_t y, int i) {
-  const uint32_t hi = __builtin_amdgcn_perm(0x40B00000u, y, 0x0706000Cu | ((uint32_t)i << 8));
-  return __hiloint2double((int)hi, 0);
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2v __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2v lds_i32x2v;
+
+// 2^52 + sum_{k<6} 128 * 2^(8k)
+constexpr double kDigitBias = 4503599627370496.0 + 141289400074368.0;
+constexpr int kSigTop = 46;  // |q rng 2^sig| < 2^46
+constexpr int kStagePre = 8;  // 16 B pieces per thread loaded ahead of the tile
+
+__device__ __forceinline__ long tr8_read(const uint8_t* p) {
+  const i32x2v v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2v*)p);
+  return __builtin_bit_cast(long, v);
+}
+
+__device__ __forceinline__ double swizzle_xor16(double v) {
+  const uint64_t u = dbits(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)u, 0x401F);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(u >> 32), 0x401F);
+  return bitsd(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int ilogb_bits(double v) {  // exponent of |v| (subnormals: -1023)
+  return (int)((dbits(v) >> 52) & 0x7FFu) - 1023;
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads (a full __syncthreads()
+// would also drain the prefetch of the next tile).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// e^x for x <= 0 (or -inf), relative error below 1e-13: Cody-Waite range
+// reduction x = k ln2 + r with
+// |r| <= ln2 / 2 (k = rint(x / ln2), r by a two-part ln2), e^r by its
+// degree-11 Taylor polynomial, then the exact scaling 2^k.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  if (!(x > -745.0)) return 0.0;
+  const double k = rint(x * 1.4426950408889634074);
+  const double r = fma(k, -1.9082149292705877000e-10, fma(k, -6.9314718036912381649e-01, x));
+  double p = 2.5052108385441718775e-08;            // 1/11!
+  p = fma(p, r, 2.7557319223985890653e-07);        // 1/10!
+  p = fma(p, r, 2.7557319223985892510e-06);        // 1/9!
+  p = fma(p, r, 2.4801587301587301566e-05);        // 1/8!
+  p = fma(p, r, 1.9841269841269841253e-04);        // 1/7!
+  p = fma(p, r, 1.3888888888888889419e-03);        // 1/6!
+  p = fma(p, r, 8.3333333333333332177e-03);        // 1/5!
+  p = fma(p, r, 4.1666666666666664354e-02);        // 1/4!
+  p = fma(p, r, 1.6666666666666665741e-01);        // 1/3!
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)k);
+}
+
+// max over the 32-lane half of the wave (lanes 0..31 / 32..63), in every lane
+__device__ __forceinline__ double half_max(double v) {
+  v = row_reduce(v, [](double a, double b) { return fmax(a, b); });
+  return fmax(v, swizzle_xor16(v));
+}
+__device__ __forceinline__ double half_sum(double v) {
+  v = row_reduce(v, [](double a, double b) { return a + b; });
+  const double o = swizzle_xor16(v);
+  return (threadIdx.x & 16) ? o + v : v + o;  // rows in order 0 + 1, 2 + 3
 }
 
 template <int GQA, int DT>
-__global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void* q, const uint8_t* tk,
-                                               int H, int G, int W, int64_t capmax, int ntile_ws,
-                                               double* ebuf, _Float16* e16, double* tilepart) {
+__global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const void* q, const uint8_t* tk,
+                                                  int H, int G, int W, int64_t capmax, int ntile_ws,
+                                                  double* ebuf, _Float16* e16, double* tilepart) {
   constexpr int esize = DT == 0 ? 2 : 4;
-  constexpr int NG = kTile / kGroup;  // 16
-  extern __shared__ uint32_t planes[];
-  __shared__ double qs[GQA][kDim];
-  __shared__ uint32_t meta[NG][kDim + 1];  // padded: the 16 groups fall in distinct banks
+  constexpr int NG = kTile / kGroup;  // 16 groups; wave w owns groups 4w .. 4w + 3
+  constexpr int NHQ = (GQA + 3) / 4;  // head quads: two MFMA row blocks each
+  constexpr int CXS = kTile + 16;     // code-tile row stride (bytes)
+  constexpr int AOS = 2 * 8 * 2 * 8 + 16;  // digit chunks of a channel octet: [j][set] x 8 B, padded
+  constexpr int AMS = 4 * AOS;        // one (head quad, digit half) block of 32 channels
+  constexpr int AGS = NHQ * 2 * AMS;  // one group's digit chunks
+  constexpr int PRE = kStagePre;
+  constexpr int MPT = NG * kDim / 256;
+  extern __shared__ __attribute__((aligned(16))) uint32_t planes[];  // [slot][16]
+  __shared__ double qd[GQA][kDim];
+  __shared__ uint32_t meta[NG][kDim + 1];
+  __shared__ __attribute__((aligned(16))) uint8_t cx[32 * CXS];
+  __shared__ __attribute__((aligned(16))) uint8_t at[4][AGS];
   __shared__ double Cs[NG][GQA];
   __shared__ double tails[kGroup][GQA];
-  __shared__ double red[4][GQA];
+  __shared__ double redm[4][GQA], redz[4][GQA], mfin[GQA];
+  __shared__ int emx[2][GQA];
   __shared__ uint16_t offs[kDim + 1];
-  __shared__ uint8_t tks[kDim];
+  __shared__ __attribute__((aligned(4))) uint8_t tks[kDim];
+  __shared__ uint8_t cperm[kDim];
   __shared__ uint8_t s2c[kDim * 8];
   __shared__ uint32_t wtot[2];
 
-  const int tile = blockIdx.y, b = blockIdx.x / G, g = blockIdx.x % G;
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
-  const int64_t t0 = (int64_t)tile * kTile;
-  if (t0 >= len) return;
+  const int ntl = (int)((len + kTile - 1) / kTile);
+  // this block's share of the unit's tiles: an even split over gridDim.y
+  const int tile_begin = (int)(((int64_t)blockIdx.y * ntl) / gridDim.y);
+  const int tile_end = (int)(((int64_t)(blockIdx.y + 1) * ntl) / gridDim.y);
+  if (tile_begin >= tile_end) return;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t gam0 = t0 / kGroup;
-  int64_t ngp64 = Tp / kGroup - gam0;
-  const int ngp = (int)(ngp64 < 0 ? 0 : (ngp64 > NG ? NG : ngp64));  // packed groups in tile
 
-  for (int i = tid; i < GQA * kDim; i += 256)
-    qs[i / kDim][i % kDim] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA) * kDim + i);
-  if (tid < kDim) tks[tid] = tk[((int64_t)b * G + g) * kDim + tid];
-  for (int i = tid; i < NG * kDim; i += 256) {
-    const int gl = i / kDim, c = i % kDim;
-    meta[gl][c] = (gl < ngp) ? u.kmeta[(gam0 + gl) * kDim + c] : 0u;
-  }
-  __syncthreads();
+  // ---- once per block: depths, query, per-head digit scale, slot table ----
   uint32_t tv_ = 0, inc = 0;
   if (tid < kDim) {
-    tv_ = tks[tid];
+    const int c = tid;
+    tv_ = tk[((int64_t)b * G + g) * kDim + c];
+    tks[c] = (uint8_t)tv_;
+    const double ek = u.ek[c];
+    // 2^er >= sqrt(E_c) >= every closed group's rng_c
+    const int er = ek > 0.0 ? ((ilogb_bits(ek) + 2) >> 1) : 0;
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      const double qv = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + c);
+      qd[hh][c] = qv;
+      int e = (qv != 0.0 && ek > 0.0 && tv_ > 0u) ? ilogb_bits(qv) + 1 + er : -100000;
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) e = max(e, __shfl_xor(e, sh, 64));
+      if (lane == 0) emx[wv][hh] = e;
+    }
     inc = wave_incl_scan_u32(tv_);
     if (lane == 63) wtot[wv] = inc;
   }
@@ -290,208 +397,319 @@ __global__ __launch_bounds__(256) void k_score(const uint8_t* store, const void*
     if (tid == 0) offs[0] = 0;
     const uint32_t o = inc - tv_;
     for (uint32_t p = 0; p < tv_; ++p) s2c[o + p] = (uint8_t)tid;
+    // channel order by depth, deepest first (stable): the slabs then hold
+    // channels of similar depth, and trailing depth-0 slabs are skipped
+    uint32_t rank = 0;
+    const uint32_t* t4 = reinterpret_cast<const uint32_t*>(tks);
+#pragma unroll 1
+    for (int k = 0; k < kDim / 4; ++k) {
+      const uint32_t w = t4[k];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t te = (w >> (8 * e)) & 0xFFu;
+        rank += (te > tv_) || (te == tv_ && 4 * k + e < tid);
+      }
+    }
+    cperm[rank] = (uint8_t)tid;
   }
   __syncthreads();
   const int ns = offs[kDim];
-  const int nsp = ns | 1;
+  const int nq = ns * 4;  // 16 B pieces per tile
+  // scalar table: lane 8 s + i of wave w describes the channel at sorted
+  // position 32 s + w + 4 i (depth | first slot << 8; slot 0 when depth 0)
+  uint32_t cinf = 0;
+  if (lane < 32) {
+    const int c = cperm[32 * (lane >> 3) + wv + 4 * (lane & 7)];
+    const uint32_t t = tks[c];
+    cinf = t | ((t ? (uint32_t)offs[c] : 0u) << 8);
+  }
+  // digit scale 2^sig of head h: lane quad q of head quad hq is head 4 hq + q
+  auto head_sig = [&](int hh) -> int {
+    const int e = max(emx[0][hh], emx[1][hh]);
+    return e > -100000 ? kSigTop - e : 0;
+  };
 
-  // ---- 1. stage key plane segments: (slot, quad) -> 16 B global loads ----
-  {
-    const int nq = ns * 4;
-    const uint32_t* kpl = u.kplanes;
-    for (int base = 0; base < nq; base += 256 * 8) {
-      uint4 v[8];
+  // staging: piece idx = (slot s, quad q4) -> planes[s][4 q4 .. 4 q4 + 3]
+  auto piece = [&](int idx, int64_t gam0, int ngp) -> uint4 {
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    const int s = idx >> 2, q4 = idx & 3;
+    const int c = s2c[s];
+    const int p = s - offs[c];
+    if (4 * q4 < ngp)
+      v = *reinterpret_cast<const uint4*>(u.kplanes + ((int64_t)c * W + p) * u.ngk + gam0 + 4 * q4);
+    return v;
+  };
+  auto tile_ngp = [&](int tile) -> int {
+    const int64_t n = Tp / kGroup - (int64_t)tile * NG;
+    return (int)(n < 0 ? 0 : (n > NG ? NG : n));
+  };
+  uint4 pre[PRE];
+  uint32_t pmeta[MPT];
+  auto load_ahead = [&](int tile) {
+    const int64_t gam0 = (int64_t)tile * NG;
+    const int ngp = tile_ngp(tile);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int idx = base + k * 256 + tid;
-        v[k] = make_uint4(0u, 0u, 0u, 0u);
-        if (idx < nq) {
-          const int s = idx >> 2, q4 = idx & 3;
-          const int c = s2c[s];
-          const int p = s - offs[c];
-          if (4 * q4 < ngp)
-            v[k] = *reinterpret_cast<const uint4*>(kpl + ((int64_t)c * W + p) * u.ngk + gam0 + 4 * q4);
+    for (int k = 0; k < PRE; ++k) {
+      const int idx = k * 256 + tid;
+      pre[k] = idx < nq ? piece(idx, gam0, ngp) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < MPT; ++k) {
+      const int i = k * 256 + tid, gl = i / kDim, c = i % kDim;
+      pmeta[k] = gl < ngp ? u.kmeta[(gam0 + gl) * kDim + c] : 0u;
+    }
+  };
+  auto store_ahead = [&](int tile) {
+#pragma unroll
+    for (int k = 0; k < PRE; ++k) {
+      const int idx = k * 256 + tid;
+      if (idx < nq) *reinterpret_cast<uint4*>(planes + idx * 4) = pre[k];
+    }
+#pragma unroll
+    for (int k = 0; k < MPT; ++k) {
+      const int i = k * 256 + tid;
+      meta[i / kDim][i % kDim] = pmeta[k];
+    }
+    // pieces past the prefetched ones (deep reads only)
+    const int64_t gam0 = (int64_t)tile * NG;
+    const int ngp = tile_ngp(tile);
+    for (int idx = PRE * 256 + tid; idx < nq; idx += 256)
+      *reinterpret_cast<uint4*>(planes + idx * 4) = piece(idx, gam0, ngp);
+  };
+  load_ahead(tile_begin);
+  store_ahead(tile_begin);
+  __syncthreads();
+  // the register prefetch runs one tile ahead; it is issued right after the
+  // previous staging write, before the epilogue's global stores, so that no
+  // wait on those stores delays it
+  if (tile_begin + 1 < tile_end) load_ahead(tile_begin + 1);
+
+  const int kq = lane >> 4, jj = (lane & 15) >> 1, ss = lane & 1;
+  // transposing plane read: lane 2j + s of quarter q addresses plane 7 - j,
+  // groups 4q + 2s and 4q + 2s + 1 (8 bytes); lane o then holds the plane
+  // bytes of octet o
+  const int troff = (7 - jj) * 64 + (4 * kq + 2 * ss) * 4;
+  // digit chunk (channel octet co, channel j, set s) of block (hq, half m)
+  auto achunk = [&](int hq, int m, int co, int j, int s) -> int {
+    return (2 * hq + m) * AMS + co * AOS + (2 * j + s) * 8;
+  };
+  const int c32 = lane & 31, sA = lane >> 5;  // A-build: channel, head pair of the quad
+
+  for (int tile = tile_begin; tile < tile_end; ++tile) {
+    const int64_t t0 = (int64_t)tile * kTile;
+    const int ngp = tile_ngp(tile);
+    const bool more = tile + 1 < tile_end;
+
+    // ---- per-group constants (16 lanes per group); open group, exact keys ----
+    {
+      const int gq = tid >> 4, cs = tid & 15;
+      double ca[GQA];
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) ca[hh] = 0.0;
+      if (gq < ngp) {
+#pragma unroll 2
+        for (int k = 0; k < kDim / 16; ++k) {
+          const int c = cs + 16 * k;
+          const uint32_t m = meta[gq][c];
+          const int t = tks[c];
+          const double lo = (double)bf16_to_float(m & 0xFFFFu);
+          const double rng = (double)bf16_to_float(m >> 16);
+          const double base = lo + rng * ldexp_pow2(-t - 1) + (t > 0 ? 0.5 * rng : 0.0);
+#pragma unroll
+          for (int hh = 0; hh < GQA; ++hh) ca[hh] = fma(qd[hh][c], base, ca[hh]);
         }
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int idx = base + k * 256 + tid;
-        if (idx < nq) {
-          const int s = idx >> 2, q4 = idx & 3;
-          planes[(4 * q4 + 0) * nsp + s] = v[k].x;
-          planes[(4 * q4 + 1) * nsp + s] = v[k].y;
-          planes[(4 * q4 + 2) * nsp + s] = v[k].z;
-          planes[(4 * q4 + 3) * nsp + s] = v[k].w;
+      for (int hh = 0; hh < GQA; ++hh) ca[hh] = group_sum<16>(ca[hh]);
+      if (cs == 0)
+#pragma unroll
+        for (int hh = 0; hh < GQA; ++hh) Cs[gq][hh] = ca[hh];
+    }
+    const int64_t ntail = len - Tp;
+    const bool tail_here = ntail > 0 && Tp >= t0 && Tp < t0 + kTile;
+    if (tail_here) {
+      const int rr = tid >> 3, part = tid & 7;
+      double st[GQA];
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) st[hh] = 0.0;
+      if (rr < ntail) {
+        for (int c = part * 16; c < part * 16 + 16; ++c) {
+          const double kv = load_elem<DT>(u.ktail, (int64_t)rr * kDim + c);
+#pragma unroll
+          for (int hh = 0; hh < GQA; ++hh) st[hh] = fma(qd[hh][c], kv, st[hh]);
         }
       }
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) st[hh] = group_sum<8>(st[hh]);
+      if (part == 0 && rr < ntail)
+#pragma unroll
+        for (int hh = 0; hh < GQA; ++hh) tails[rr][hh] = st[hh] * kInvSqrtD;
     }
-  }
-  // ---- 2. per-group constants ----
-  {
-    const int gl = tid >> 4, cs = tid & 15;
-    double ca[GQA];
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) ca[hh] = 0.0;
-    if (gl < ngp) {
-      for (int k = 0; k < kDim / 16; ++k) {
-        const int c = cs + 16 * k;
-        const uint32_t m = meta[gl][c];
-        const int t = tks[c];
-        const double lo = (double)bf16_to_float(m & 0xFFFFu);
-        const double rng = (double)bf16_to_float(m >> 16);
-        const double base = lo + rng * ldexp_pow2(-t - 1) - (t > 0 ? 16.0 * rng : 0.0);
-#pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) ca[hh] = fma(qs[hh][c], base, ca[hh]);
-      }
-    }
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) ca[hh] = group_sum<16>(ca[hh]);
-    if (cs == 0)
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) Cs[gl][hh] = ca[hh];
-  }
-  __syncthreads();
+    lds_barrier();  // constants and open-group logits (the slab loop may not run)
 
-  // ---- 3. un-plane and accumulate: wave wv, channels wv, wv+4, ... ----
-  double acc[8][GQA];
+    // ---- un-plane + int8 MFMA, one 32-channel slab at a time ----
+    i32x4 acc[8][NHQ][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) acc[i][hh] = 0.0;
-  {
-    const int gl = lane >> 2, ob = lane & 3;
-    const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)ob) << 8) | (uint32_t)ob;
-    const uint32_t* pl = planes + gl * nsp;
-    for (int c = wv; c < kDim; c += 4) {
-      const int t = tks[c];
-      if (t == 0) continue;
-      const int s0 = offs[c];
-      const double rs = (double)bf16_to_float(meta[gl][c] >> 16) * (1.0 / 256.0);
-      double beta[GQA];
+      for (int hq = 0; hq < NHQ; ++hq) acc[i][hq][0] = acc[i][hq][1] = i32x4{0, 0, 0, 0};
+#pragma unroll 1
+    for (int slab = 0; slab < 4; ++slab) {
+      if (tks[cperm[32 * slab]] == 0) break;  // deepest first: the rest is depth 0
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) beta[hh] = qs[hh][c] * rs;
-      uint32_t lo, hi;
-      if (t <= 4) {
-        const uint32_t w0 = pl[s0];
-        const uint32_t w1 = t > 1 ? pl[s0 + 1] : 0u;
-        const uint32_t w2 = t > 2 ? pl[s0 + 2] : 0u;
-        const uint32_t w3 = t > 3 ? pl[s0 + 3] : 0u;
-        hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w0, w1, sel), __builtin_amdgcn_perm(w2, w3, sel),
-                                   0x05040100u);
-        transpose8_hi4(lo, hi);
-      } else {
-        uint32_t w[8];
+      for (int bt = 0; bt < 2; ++bt) {
+        // 4 channels of nearly equal depth (sorted positions w + 4 (4 bt + k)).
+        // One transposing LDS read per channel gives lane o the 8 plane
+        // bytes of its octet o (plane p in byte 7 - p; planes past the depth
+        // are read from the padding and masked).
+        int tk4[4], tmax = 0;
+        uint2 pb[4];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) w[p] = (p < t) ? pl[s0 + p] : 0u;
-        unplane8(w, sel, lo, hi);
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t inf = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 4 * bt + k);
+          tk4[k] = (int)(inf & 0xFFu);
+          tmax = max(tmax, tk4[k]);
+          const long v = tr8_read(reinterpret_cast<const uint8_t*>(planes) + (inf >> 8) * 64 + troff);
+          pb[k] = __builtin_bit_cast(uint2, v);
+        }
+        if (tmax == 0) continue;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int t = tk4[k];
+          // keep bytes 7 .. 8 - t (planes 0 .. t - 1)
+          const uint64_t keep = t >= 8 ? ~0ull : (t <= 0 ? 0ull : ~0ull << (64 - 8 * t));
+          uint32_t lo = pb[k].x & (uint32_t)keep;
+          uint32_t hi = (pb[k].y & (uint32_t)(keep >> 32)) ^ 0xFF000000u;
+          if (tmax <= 4) transpose8_hi4(lo, hi);
+          else transpose8_halves(lo, hi);
+          const int cl = wv + 4 * (4 * bt + k);
+          *reinterpret_cast<uint2*>(cx + cl * CXS + 8 * lane) = make_uint2(lo, hi);
+        }
       }
+      lds_barrier();
+      // digit words of this lane's channel (sorted position c32), heads
+      // 4 hq + 2 sA and 4 hq + 2 sA + 1: the chunk of digit half m holds
+      // digits 4m .. 4m + 3 of both heads
+      const int cA = cperm[32 * slab + c32];
+      const bool liveA = tks[cA] > 0;
+      double qa[NHQ][2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double X = code_plus_4096(e < 4 ? lo : hi, e & 3);
+      for (int hq = 0; hq < NHQ; ++hq)
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) acc[e][hh] = fma(beta[hh], X, acc[e][hh]);
+        for (int e = 0; e < 2; ++e) {
+          const int hh = 4 * hq + 2 * sA + e;
+          qa[hq][e] = (hh < GQA && liveA) ? qd[min(hh, GQA - 1)][cA] * ldexp_pow2(head_sig(min(hh, GQA - 1))) : 0.0;
+        }
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int gw = 4 * wv + gi;
+        if (gw >= ngp) break;
+        {
+          const double rng = (double)bf16_to_float(meta[gw][cA] >> 16);
+#pragma unroll
+          for (int hq = 0; hq < NHQ; ++hq) {
+            const uint64_t d0 = dbits(fma(qa[hq][0], rng, kDigitBias)) ^ 0x8080808080808080ull;
+            const uint64_t d1 = dbits(fma(qa[hq][1], rng, kDigitBias)) ^ 0x8080808080808080ull;
+            *reinterpret_cast<uint2*>(&at[wv][achunk(hq, 0, c32 >> 3, c32 & 7, sA)]) =
+                make_uint2((uint32_t)d0, (uint32_t)d1);
+            *reinterpret_cast<uint2*>(&at[wv][achunk(hq, 1, c32 >> 3, c32 & 7, sA)]) =
+                make_uint2((uint32_t)(d0 >> 32), (uint32_t)(d1 >> 32));
+          }
+        }
+        wave_lds_fence();
+        long A[NHQ][2];
+#pragma unroll
+        for (int hq = 0; hq < NHQ; ++hq)
+#pragma unroll
+          for (int m = 0; m < 2; ++m) A[hq][m] = tr8_read(&at[wv][achunk(hq, m, kq, jj, ss)]);
+#pragma unroll
+        for (int tl = 0; tl < 2; ++tl) {
+          const int tb = 2 * gi + tl;         // the wave's token block
+          const int oct = 2 * (8 * wv + tb);  // first octet of the block
+          const long Bv = tr8_read(cx + (8 * kq + jj) * CXS + 8 * (oct + ss));
+#pragma unroll
+          for (int hq = 0; hq < NHQ; ++hq)
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+              acc[tb][hq][m] = __builtin_amdgcn_mfma_i32_16x16x32_i8(A[hq][m], Bv, acc[tb][hq][m], 0, 0, 0);
+        }
+        wave_lds_fence();
       }
+      lds_barrier();
     }
-  }
-  // ---- the four waves' partial sums: waves 0,1 store, waves 2,3 add; the
-  // epilogue adds the two buffers (fixed order (w0 + w2) + (w1 + w3)) ----
-  double* wred = reinterpret_cast<double*>(planes);  // [2][8 * GQA][64]
-  __syncthreads();
-  if (wv < 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) wred[(wv * 8 * GQA + e * GQA + hh) * 64 + lane] = acc[e][hh];
-  }
-  __syncthreads();
-  if (wv >= 2) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) {
-        double* p = wred + ((wv - 2) * 8 * GQA + e * GQA + hh) * 64 + lane;
-        *p = *p + acc[e][hh];
-      }
-  }
-  __syncthreads();
+    // the staged planes and metadata of this tile are dead: next tile in
+    if (more) store_ahead(tile + 1);
+    if (tile + 2 < tile_end) load_ahead(tile + 2);
 
-  // ---- 4. open group (exact keys) ----
-  const int64_t ntail = len - Tp;
-  const bool tail_here = ntail > 0 && Tp >= t0 && Tp < t0 + kTile;
-  if (tail_here) {
-    const int rr = tid >> 3, part = tid & 7;
-    double st[GQA];
+    // ---- logits in registers: lane -> (token 16 (8 w + tb) + lane % 16,
+    // head 4 hq + lane / 16); its digits sit in its own accumulators ----
+    const int toff = (int)(Tp - t0);  // tile-local first open-group token (if here)
+    const int hl = lane >> 4;
+    double sv[8][NHQ];
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) st[hh] = 0.0;
-    if (rr < ntail) {
-      for (int c = part * 16; c < part * 16 + 16; ++c) {
-        const double kv = load_elem<DT>(u.ktail, (int64_t)rr * kDim + c);
+    for (int hq = 0; hq < NHQ; ++hq) {
+      const int hh = 4 * hq + hl;
+      const int hc = min(hh, GQA - 1);
+      const int sg = head_sig(hc);
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) st[hh] = fma(qs[hh][c], kv, st[hh]);
+      for (int tb = 0; tb < 8; ++tb) {
+        const int gw = 4 * wv + (tb >> 1);
+        const int tok = 16 * (8 * wv + tb) + (lane & 15);
+        double s = -INFINITY;
+        if (hh < GQA) {
+          if (gw < ngp) {
+            const i32x4 d0 = acc[tb][hq][0], d1 = acc[tb][hq][1];
+            const double P = fma((double)d1[1], 0x1p40, fma((double)d1[0], 0x1p32,
+                             fma((double)d0[3], 0x1p24, fma((double)d0[2], 0x1p16,
+                             fma((double)d0[1], 0x1p8, (double)d0[0])))));
+            s = (Cs[gw][hc] + ldexp(P, -sg - 8)) * kInvSqrtD;
+          } else if (tail_here && tok >= toff && tok < toff + ntail) {
+            s = tails[tok - toff][hc];
+          }
+        }
+        sv[tb][hq] = s;
       }
     }
+    // tile max per head: lanes of a quad share the head
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) st[hh] = group_sum<8>(st[hh]);
-    if (part == 0 && rr < ntail)
+    for (int hq = 0; hq < NHQ; ++hq) {
+      double m = sv[0][hq];
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) tails[rr][hh] = st[hh] * kInvSqrtD;
-  }
-  __syncthreads();
-
-  // ---- softmax partials: thread (oc = tid % 64, pair = tid / 64) finishes
-  // tokens 8 oc + 2 pair and 8 oc + 2 pair + 1 of the tile ----
-  const int oc = lane, e0 = 2 * wv;
-  const int glt = oc >> 2;
-  const bool pk = glt < ngp;
-  const bool has_tail = tail_here && tid < ntail;
-  double sv[2][GQA];
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh)
-      sv[k][hh] = pk ? (Cs[glt][hh] + (wred[((e0 + k) * GQA + hh) * 64 + oc] +
-                                        wred[(8 * GQA + (e0 + k) * GQA + hh) * 64 + oc])) * kInvSqrtD
-                     : 0.0;
-  double mt[GQA];
-#pragma unroll
-  for (int hh = 0; hh < GQA; ++hh) {
-    double m = has_tail ? tails[tid][hh] : -INFINITY;
-    if (pk) m = fmax(m, fmax(sv[0][hh], sv[1][hh]));
-    m = wave_max(m);
-    if (lane == 0) red[wv][hh] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < GQA; ++hh) mt[hh] = fmax(fmax(red[0][hh], red[1][hh]), fmax(red[2][hh], red[3][hh]));
-  __syncthreads();
-#pragma unroll
-  for (int hh = 0; hh < GQA; ++hh) {
-    const int64_t row = ((int64_t)b * H + (int64_t)g * GQA + hh) * capmax;
-    double z = 0.0;
-    if (pk) {
-      const int64_t j = t0 + 8 * oc + e0;  // even: the pair is 16 B / 4 B aligned
-      const double ea = exp(sv[0][hh] - mt[hh]), eb = exp(sv[1][hh] - mt[hh]);
-      *reinterpret_cast<double2*>(ebuf + row + j) = make_double2(ea, eb);
-      f16x2 hp;
-      hp.x = (_Float16)(float)ea;
-      hp.y = (_Float16)(float)eb;
-      *reinterpret_cast<f16x2*>(e16 + row + j) = hp;
-      z = ea + eb;
+      for (int tb = 1; tb < 8; ++tb) m = fmax(m, sv[tb][hq]);
+      m = row_reduce(m, [](double a, double c) { return fmax(a, c); });
+      const int hh = 4 * hq + hl;
+      if ((lane & 15) == 0 && hh < GQA) redm[wv][hh] = m;
     }
-    if (has_tail) {
-      const double ev = exp(tails[tid][hh] - mt[hh]);
-      ebuf[row + Tp + tid] = ev;
-      e16[row + Tp + tid] = (_Float16)(float)ev;
-      z += ev;
+    lds_barrier();
+#pragma unroll
+    for (int hq = 0; hq < NHQ; ++hq) {
+      const int hh = 4 * hq + hl;
+      const int hc = min(hh, GQA - 1);
+      const double mt = fmax(fmax(redm[0][hc], redm[1][hc]), fmax(redm[2][hc], redm[3][hc]));
+      const int64_t row = ((int64_t)b * H + (int64_t)g * GQA + hc) * capmax + t0;
+      double z = 0.0;
+#pragma unroll
+      for (int tb = 0; tb < 8; ++tb) {
+        const int tok = 16 * (8 * wv + tb) + (lane & 15);
+        if (sv[tb][hq] > -INFINITY) {
+          const double e = exp_nonpos(sv[tb][hq] - mt);
+          ebuf[row + tok] = e;
+          e16[row + tok] = (_Float16)(float)e;
+          z += e;
+        }
+      }
+      z = row_reduce(z, [](double a, double c) { return a + c; });
+      if ((lane & 15) == 0 && hh < GQA) {
+        redz[wv][hh] = z;
+        if (wv == 0) mfin[hh] = mt;
+      }
     }
-    z = wave_sum(z);
-    if (lane == 0) red[wv][hh] = z;
-  }
-  __syncthreads();
-  if (tid < GQA) {
-    double* tp = tilepart + (((int64_t)b * H + (int64_t)g * GQA + tid) * ntile_ws + tile) * 2;
-    tp[0] = mt[tid];
-    tp[1] = (red[0][tid] + red[1][tid]) + (red[2][tid] + red[3][tid]);
+    lds_barrier();
+    if (tid < GQA) {
+      double* tp = tilepart + (((int64_t)b * H + (int64_t)g * GQA + tid) * ntile_ws + tile) * 2;
+      tp[0] = mfin[tid];
+      tp[1] = (redz[0][tid] + redz[1][tid]) + (redz[2][tid] + redz[3][tid]);
+    }
   }
 }
 
@@ -1014,6 +1232,19 @@ __global__ __launch_bounds__(256) void k_out_reduce(const uint8_t* store, int H,
 }
 
 // ---------------------------------------------------------------------------
+static int device_cu_count() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      n = v;
+    else
+      n = 256;
+  }
+  return n;
+}
+
 static inline void mark(const DecodeArgs& a, int i, hipStream_t st) {
   if (a.events) hipEventRecord((hipEvent_t)a.events[i], st);
 }
@@ -1029,19 +1260,28 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   hipLaunchKernelGGL((k_key_alloc<DT>), dim3(a.B * a.G), dim3(64), 0, st, (const uint8_t*)a.store,
                      a.q, a.H, a.G, a.W, a.RK, tk);
   mark(a, 1, st);
-  // slots staged per score tile: at most min(B_K, 128 W) chosen key lines
+  // slots staged per score tile: at most min(B_K, 128 W) chosen key lines,
+  // 64 B each
   double bk = floor((double)a.RK * (double)kDim);
   if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
-  size_t dyn = (size_t)(kTile / kGroup) * (size_t)(((int)bk) | 1) * 4;
-  const size_t dyn_red = (size_t)2 * 64 * 8 * GQA * 8;  // wave reduction buffers
-  if (dyn < dyn_red) dyn = dyn_red;
+  if (bk < 0.0) bk = 0.0;
+  // (+8 slots: un-plane reads of a batch may run past a shallower channel's
+  // last slot; those words are masked)
+  size_t dyn = ((size_t)bk + 8) * 64;
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GQA, DT>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, 16 * 1025 * 4 + 64);
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (kDim * 8 + 8) * 64);
     attr_set = true;
   }
-  hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, L.ntile), dim3(256), dyn, st,
+  // each unit's tiles split evenly over nrun blocks: about two blocks per
+  // compute unit in all
+  const int64_t total_tiles = (int64_t)a.B * a.G * L.ntile;
+  const int64_t slots = 2 * (int64_t)device_cu_count();
+  int run = (int)((total_tiles + slots - 1) / slots);
+  if (run < 1) run = 1;
+  const int nrun = (L.ntile + run - 1) / run;
+  hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), dyn, st,
                      (const uint8_t*)a.store, a.q, (const uint8_t*)tk, a.H, a.G, a.W, a.capmax,
                      L.ntile, (double*)(ws + L.ebuf), (_Float16*)(ws + L.e16),
                      (double*)(ws + L.tilepart));
