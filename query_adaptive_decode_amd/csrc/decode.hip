@@ -226,7 +226,8 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
 //     to LDS after its last un-plane, and the loads for the tile after are
 //     issued at once.  Barriers inside the tile loop wait for LDS traffic
 //     only, never for those loads.
-//  2. Per-group constants C_gh in fp64 (16 lanes per group, DPP sums).
+//  2. Per-group constants C_gh: a 16 x 128 x GQA fp64 contraction on the
+//     matrix cores (v_mfma_f64_16x16x4_f64).
 //  3. Four slabs of 32 channels.  Un-plane: wave w takes the slab's channels
 //     w, w+4, ... (uniform depth in the wave, taken from a scalar table),
 //     lane o the tile's tokens 8o..8o+7: byte o%4 of its group's t plane
@@ -259,6 +260,7 @@ __device__ __forceinline__ void transpose8_hi4(uint32_t& lo, uint32_t& hi) {
 }
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2v __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2v lds_i32x2v;
 
@@ -295,27 +297,37 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// e^x for x <= 0 (or -inf), relative error below 1e-13: Cody-Waite range
-// reduction x = k ln2 + r with
-// |r| <= ln2 / 2 (k = rint(x / ln2), r by a two-part ln2), e^r by its
-// degree-11 Taylor polynomial, then the exact scaling 2^k.
+// e^x for x <= 0 (or -inf), relative error below 1e-9.  Cody-Waite range
+// reduction x = k ln2 + r (k = rint(x / ln2), ln2 in two parts, so r is
+// exact to ~1e-17 and |r| <= ln2 / 2), then
+//   e^r = 1 + r + r^2 (1/2 + r P(r)),  P(r) = sum_{i>=0} r^i / (i + 3)!
+// with P's Taylor polynomial (degree 7: truncation below 1e-12) evaluated
+// in fp32: its rounding error, weighted by |r|^3 <= 0.042, stays below
+// 1e-9 of the result.  Then the exact scaling 2^k.
 __device__ __forceinline__ double exp_nonpos(double x) {
-  if (!(x > -745.0)) return 0.0;
-  const double k = rint(x * 1.4426950408889634074);
-  const double r = fma(k, -1.9082149292705877000e-10, fma(k, -6.9314718036912381649e-01, x));
-  double p = 2.5052108385441718775e-08;            // 1/11!
-  p = fma(p, r, 2.7557319223985890653e-07);        // 1/10!
-  p = fma(p, r, 2.7557319223985892510e-06);        // 1/9!
-  p = fma(p, r, 2.4801587301587301566e-05);        // 1/8!
-  p = fma(p, r, 1.9841269841269841253e-04);        // 1/7!
-  p = fma(p, r, 1.3888888888888889419e-03);        // 1/6!
-  p = fma(p, r, 8.3333333333333332177e-03);        // 1/5!
-  p = fma(p, r, 4.1666666666666664354e-02);        // 1/4!
-  p = fma(p, r, 1.6666666666666665741e-01);        // 1/3!
-  p = fma(p, r, 0.5);
-  p = fma(p, r, 1.0);
-  p = fma(p, r, 1.0);
-  return ldexp(p, (int)k);
+  const double xc = fmax(x, -745.0);
+  const double k = rint(xc * 1.4426950408889634074);
+  const double r = fma(k, -1.9082149292705877000e-10, fma(k, -6.9314718036912381649e-01, xc));
+  const float rf = (float)r;
+  float pp = 2.7557319e-07f;                 // 1/10!
+  pp = fmaf(pp, rf, 2.7557319e-06f);         // 1/9!
+  pp = fmaf(pp, rf, 2.4801587e-05f);         // 1/8!
+  pp = fmaf(pp, rf, 1.9841270e-04f);         // 1/7!
+  pp = fmaf(pp, rf, 1.3888889e-03f);         // 1/6!
+  pp = fmaf(pp, rf, 8.3333333e-03f);         // 1/5!
+  pp = fmaf(pp, rf, 4.1666668e-02f);         // 1/4!
+  pp = fmaf(pp, rf, 1.6666667e-01f);         // 1/3!
+  const double e = fma(r * r, fma(r, (double)pp, 0.5), 1.0 + r);
+  const double v = ldexp(e, (int)k);
+  return x > -745.0 ? v : 0.0;
+}
+
+// fp64 -> fp16 through an fp32 value the optimiser cannot fold away (a
+// direct f64 -> f16 truncation is a long software sequence on this target)
+__device__ __forceinline__ _Float16 to_half(double v) {
+  float f = (float)v;
+  asm volatile("" : "+v"(f));
+  return (_Float16)f;
 }
 
 // max over the 32-lane half of the wave (lanes 0..31 / 32..63), in every lane
@@ -347,7 +359,8 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   __shared__ uint32_t meta[NG][kDim + 1];
   __shared__ __attribute__((aligned(16))) uint8_t cx[32 * CXS];
   __shared__ __attribute__((aligned(16))) uint8_t at[4][AGS];
-  __shared__ double Cs[NG][GQA];
+  __shared__ double Cpart[4][NG][GQA];  // per-wave partial constants
+  __shared__ double kap[kDim];         // 2^-(t_c+1) + [t_c > 0] / 2
   __shared__ double tails[kGroup][GQA];
   __shared__ double redm[4][GQA], redz[4][GQA], mfin[GQA];
   __shared__ int emx[2][GQA];
@@ -411,6 +424,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       }
     }
     cperm[rank] = (uint8_t)tid;
+    kap[tid] = ldexp_pow2(-(int)tv_ - 1) + (tv_ > 0u ? 0.5 : 0.0);
   }
   __syncthreads();
   const int ns = offs[kDim];
@@ -500,30 +514,26 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     const int ngp = tile_ngp(tile);
     const bool more = tile + 1 < tile_end;
 
-    // ---- per-group constants (16 lanes per group); open group, exact keys ----
+    // ---- per-group constants C[g][h] = sum_c base[g][c] q[h][c] on the fp64
+    // matrix cores: wave w contracts its 32 channels in 8 steps of 4 (A:
+    // lane l = (group l % 16, channel l / 16), B: (channel l / 16, head
+    // l % 16)); result lane l, register i = (group 4 i + l / 16, head l % 16) ----
     {
-      const int gq = tid >> 4, cs = tid & 15;
-      double ca[GQA];
+      const int gA = lane & 15, kk = lane >> 4;
+      f64x4 cd = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) ca[hh] = 0.0;
-      if (gq < ngp) {
-#pragma unroll 2
-        for (int k = 0; k < kDim / 16; ++k) {
-          const int c = cs + 16 * k;
-          const uint32_t m = meta[gq][c];
-          const int t = tks[c];
-          const double lo = (double)bf16_to_float(m & 0xFFFFu);
-          const double rng = (double)bf16_to_float(m >> 16);
-          const double base = lo + rng * ldexp_pow2(-t - 1) + (t > 0 ? 0.5 * rng : 0.0);
-#pragma unroll
-          for (int hh = 0; hh < GQA; ++hh) ca[hh] = fma(qd[hh][c], base, ca[hh]);
-        }
+      for (int st = 0; st < 8; ++st) {
+        const int c = 32 * wv + 4 * st + kk;
+        const uint32_t m = meta[gA][c];
+        const double lo = (double)bf16_to_float(m & 0xFFFFu);
+        const double rng = (double)bf16_to_float(m >> 16);
+        const double base = fma(rng, kap[c], lo);
+        const double qb = gA < GQA ? qd[min(gA, GQA - 1)][c] : 0.0;
+        cd = __builtin_amdgcn_mfma_f64_16x16x4f64(base, qb, cd, 0, 0, 0);
       }
+      if (gA < GQA)
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) ca[hh] = group_sum<16>(ca[hh]);
-      if (cs == 0)
-#pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) Cs[gq][hh] = ca[hh];
+        for (int i = 0; i < 4; ++i) Cpart[wv][4 * i + kk][gA] = cd[i];
     }
     const int64_t ntail = len - Tp;
     const bool tail_here = ntail > 0 && Tp >= t0 && Tp < t0 + kTile;
@@ -662,7 +672,8 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
             const double P = fma((double)d1[1], 0x1p40, fma((double)d1[0], 0x1p32,
                              fma((double)d0[3], 0x1p24, fma((double)d0[2], 0x1p16,
                              fma((double)d0[1], 0x1p8, (double)d0[0])))));
-            s = (Cs[gw][hc] + ldexp(P, -sg - 8)) * kInvSqrtD;
+            const double C = (Cpart[0][gw][hc] + Cpart[1][gw][hc]) + (Cpart[2][gw][hc] + Cpart[3][gw][hc]);
+            s = (C + ldexp(P, -sg - 8)) * kInvSqrtD;
           } else if (tail_here && tok >= toff && tok < toff + ntail) {
             s = tails[tok - toff][hc];
           }
@@ -686,15 +697,16 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       const int hh = 4 * hq + hl;
       const int hc = min(hh, GQA - 1);
       const double mt = fmax(fmax(redm[0][hc], redm[1][hc]), fmax(redm[2][hc], redm[3][hc]));
-      const int64_t row = ((int64_t)b * H + (int64_t)g * GQA + hc) * capmax + t0;
+      const int64_t lane0 = ((int64_t)b * H + (int64_t)g * GQA + hc) * capmax + t0 + 128 * wv + (lane & 15);
+      double* const ep = ebuf + lane0;
+      _Float16* const hp = e16 + lane0;
       double z = 0.0;
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb) {
-        const int tok = 16 * (8 * wv + tb) + (lane & 15);
+        const double e = exp_nonpos(sv[tb][hq] - mt);
         if (sv[tb][hq] > -INFINITY) {
-          const double e = exp_nonpos(sv[tb][hq] - mt);
-          ebuf[row + tok] = e;
-          e16[row + tok] = (_Float16)(float)e;
+          ep[16 * tb] = e;
+          hp[16 * tb] = to_half(e);
           z += e;
         }
       }
@@ -968,179 +980,134 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
 }
 
 // ---------------------------------------------------------------------------
-// Gather: one block of 256 threads per 256-token chunk (8 groups) of one
-// (request, KV head).
-//  1. The chosen value plane rows (16 B per token and plane) are staged in
-//     LDS.
-//  2. Every refined token (t > 0) is un-planed: 16 lanes per token, one per
-//     8-channel octet, byte gather + 8x8 bit transpose, and its prefix codes
-//     X (= P 2^(8-t)) are written token-major to an LDS code tile (tokens
-//     with t = 0 keep X = 0).  Deep (t > 4) and shallow tokens are processed
-//     from two separate lists so that the code path is uniform per wave.
-//  3. Per group gamma and head h, with e = exp(s - m_tile) rounded to fp16,
+// Gather: a block of 256 threads takes a run of consecutive 128-token chunks
+// (4 groups each) of one (request, KV head) and accumulates its share of
+//   O_h = sum_j alpha_hj v_hat_j,  alpha_hj = e_hj f_{h,tile(j)}
+// (e = exp(s - m_tile) rounded to fp16, f_{h,tile} = exp(m_tile - m) / Z).
+// Per chunk:
+//  1. The chosen value plane rows (16 B per token and plane) sit in LDS as
+//     rows[plane][token]; depths, weights and metadata of the chunk too.  All
+//     of it was loaded into registers while the previous chunk was computed
+//     (the depths one chunk further ahead, as the row loads need them).
+//  2. Un-plane: a 16-lane quarter takes one token; one transposing LDS read
+//     (ds_read_b64_tr_b8) gives lane o the 8 plane bytes of channel octet o,
+//     planes past the token's depth are masked, an 8x8 bit transpose gives
+//     the 8 prefix codes X = P 2^(8-t) (depth-0 tokens give zeros), written
+//     token-major to a code tile.
+//  3. Per group gamma and head h,
 //       sum_j e_j v_hat_jc = lo_c A + rng_c (Bh + U_c / 256),
 //     A = sum e, Bh = sum e 2^-(t+1), U_c = sum e X_c.  U comes from
 //     v_mfma_f32_16x16x32_f16: A operand = codes of 16 channels x 32 tokens
-//     (one group), read channel-major from the code tile with the LDS
-//     transpose read and turned into the fp16 values 1024 + X by one byte
-//     permute per pair; B operand = e for 16 columns (head, group) with
-//     zeros off the column's own group, so one column set covers 16/GQA
-//     groups; the 1024 A part is removed when the group is folded in.
-//  4. Column partials are added per head in group order, open-group tokens
-//     (exact values) are added, and the chunk partial f_{h,tile} O is
-//     written.  Grid (unit, chunk): all chunks of a unit on one XCD.
+//     (one group), read channel-major from the code tile with the transposing
+//     LDS read and turned into the fp16 values 1024 + X by one byte permute
+//     per pair; B operand = e for 16 columns (head, group) with zeros off the
+//     column's own group; the 1024 A part is removed when the group is
+//     folded into the block's running sums (scaled by f of the chunk's tile).
+// At the end of the run: column sums per head, the open group's tokens
+// (exact values), one partial output per run.  Barriers inside the chunk
+// loop wait for LDS traffic only, never for the loads in flight.
+// Grid (unit, run): all runs of a unit on one XCD.
 // ---------------------------------------------------------------------------
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 template <int GQA, int DT>
-__global__ __launch_bounds__(256) void k_gather(const uint8_t* store, const uint8_t* tv, int H, int G,
-                                                int W, int64_t capmax, int ntile_ws, int nchunk_ws,
-                                                const _Float16* e16, const double* ftile,
-                                                float* opart) {
+__global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const uint8_t* tv, int H,
+                                                   int G, int W, int64_t capmax, int ntile_ws,
+                                                   int nrun_ws, const _Float16* e16,
+                                                   const double* ftile, float* opart) {
   constexpr int esize = DT == 0 ? 2 : 4;
-  constexpr int NG = kChunk / kGroup;                       // 8 groups per chunk
-  constexpr int GS = (16 / GQA < NG) ? 16 / GQA : NG;       // groups per MFMA column set
+  constexpr int NG = kChunk / kGroup;                  // 4 groups per chunk
+  constexpr int GS = (16 / GQA < NG) ? 16 / GQA : NG;  // groups per MFMA column set
   constexpr int NSET = (NG + GS - 1) / GS;
   constexpr int XS = kDim + 8;  // code-tile row stride: rows 2 apart fall in different banks
-  __shared__ uint4 vrows[kChunk * 8];                       // staged rows; reused below
-  __shared__ __attribute__((aligned(16))) uint8_t xl[kChunk * XS];    // codes [token][channel]
+  constexpr int MPT = NG * kDim / 256;  // metadata words per thread
+  __shared__ __attribute__((aligned(16))) uint4 rows[8][kChunk];     // [plane][token]; reused at the end
+  __shared__ __attribute__((aligned(16))) uint8_t xl[kChunk * XS];   // codes [token][channel]
   __shared__ __attribute__((aligned(16))) _Float16 es[GQA][kChunk];
   __shared__ uint32_t vmeta_s[NG][kDim];
   __shared__ float Ag[NG][GQA], Bg[NG][GQA];
-  __shared__ uint16_t offs[kChunk];
-  __shared__ uint8_t tvs[kChunk];
-  __shared__ uint8_t s2t[kChunk * 8];
-  __shared__ uint8_t lst[kChunk];
+  __shared__ __attribute__((aligned(4))) uint8_t tvs[kChunk];
   __shared__ float fs[GQA];
-  __shared__ uint32_t wsum[256 / 64 + 1];
 
-  const int chunk = blockIdx.y, b = blockIdx.x / G, g = blockIdx.x % G;
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
-  const int64_t c0 = (int64_t)chunk * kChunk;
-  if (c0 >= len) return;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
-  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int tile = (int)(c0 / kTile);
   const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
-  const int64_t gam0 = c0 / kGroup;
-
-  {
-    const int64_t j = c0 + tid;
-    tvs[tid] = (j < Tp) ? tv[((int64_t)b * G + g) * capmax + j] : (uint8_t)0;
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh)
-      es[hh][tid] = (j < len) ? e16[(hrow0 + hh) * capmax + j] : (_Float16)0.0f;
-    for (int i = tid; i < NG * kDim; i += 256) {
-      const int gl = i / kDim, c = i % kDim;
-      const int64_t gam = gam0 + gl;
-      vmeta_s[gl][c] = ((gam + 1) * kGroup <= Tp) ? u.vmeta[gam * kDim + c] : 0u;
-    }
-    if (tid < GQA) fs[tid] = (float)ftile[(hrow0 + tid) * ntile_ws + tile];
-    uint2* xz = reinterpret_cast<uint2*>(xl);
-    for (int i = tid; i < kChunk * XS / 8; i += 256) xz[i] = make_uint2(0u, 0u);
+  const int nch = (int)((len + kChunk - 1) / kChunk);
+  const int cb = (int)(((int64_t)blockIdx.y * nch) / gridDim.y);
+  const int ce = (int)(((int64_t)(blockIdx.y + 1) * nch) / gridDim.y);
+  if (cb >= ce) {  // empty run: its partial output is zero
+    for (int o = tid; o < GQA * kDim; o += 256)
+      opart[((hrow0 + o / kDim) * nrun_ws + blockIdx.y) * kDim + o % kDim] = 0.f;
+    return;
   }
-  __syncthreads();
-  // one scan for three prefix sums: slots (12 bits), deep tokens (9 bits)
-  // and shallow tokens (9 bits), packed in one word
-  const uint32_t tj = tvs[tid];
-  const uint32_t deep = tj > 4u ? 1u : 0u, shallow = (tj >= 1u && tj <= 4u) ? 1u : 0u;
-  const uint32_t pk3 = block_excl_scan<256>(tj | (deep << 12) | (shallow << 21), wsum);
-  const uint32_t tot3 = wsum[256 / 64];
-  const uint32_t ex = pk3 & 0xFFFu, pd = (pk3 >> 12) & 0x1FFu, ps = pk3 >> 21;
-  const int nslots = (int)(tot3 & 0xFFFu);
-  const int ndeep = (int)((tot3 >> 12) & 0x1FFu);
-  const int nref = ndeep + (int)(tot3 >> 21);
-  offs[tid] = (uint16_t)ex;
-  for (uint32_t p = 0; p < tj; ++p) s2t[ex + p] = (uint8_t)tid;
-  if (deep) lst[pd] = (uint8_t)tid;
-  if (shallow) lst[ndeep + ps] = (uint8_t)tid;
-  __syncthreads();
+  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
+  const uint8_t* tvu = tv + ((int64_t)b * G + g) * capmax;
+  const int jl = tid & (kChunk - 1), rh = tid >> 7;  // row loads: token jl, planes rh, rh + 2, ...
 
-  // ---- 1. stage the chosen rows ----
-  {
-    const uint4* vp = reinterpret_cast<const uint4*>(u.vplanes);
-    for (int base = 0; base < nslots; base += 256 * 8) {
-      uint4 v[8];
+  // ---- register prefetch of one chunk ----
+  uint32_t ptv = 0;                 // depth of token jl (for the row loads)
+  _Float16 pes[GQA];
+  uint32_t pmeta[MPT];
+  float pfs = 0.f;
+  uint4 prow0, prow1, prow2, prow3;  // planes rh, rh + 2, rh + 4, rh + 6 of token jl
+  auto tv_of = [&](int chunk) __attribute__((always_inline)) -> uint32_t {
+    const int64_t j = (int64_t)chunk * kChunk + jl;
+    return j < Tp ? (uint32_t)tvu[j] : 0u;
+  };
+  auto load_small = [&](int chunk) __attribute__((always_inline)) {
+    const int64_t c0 = (int64_t)chunk * kChunk;
+    if (tid < kChunk) {
+      const int64_t j = c0 + tid;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int s = base + k * 256 + tid;
-        v[k] = make_uint4(0u, 0u, 0u, 0u);
-        if (s < nslots) {
-          const int jl = s2t[s];
-          const int p = s - offs[jl];
-          v[k] = vp[(c0 + jl) * W + p];
-        }
-      }
+      for (int hh = 0; hh < GQA; ++hh)
+        pes[hh] = (j < len) ? e16[(hrow0 + hh) * capmax + j] : (_Float16)0.0f;
+    }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int s = base + k * 256 + tid;
-        if (s < nslots) vrows[s] = v[k];
-      }
+    for (int k = 0; k < MPT; ++k) {
+      const int i = k * 256 + tid, gl = i / kDim, c = i % kDim;
+      const int64_t gam = c0 / kGroup + gl;
+      pmeta[k] = ((gam + 1) * kGroup <= Tp) ? u.vmeta[gam * kDim + c] : 0u;
     }
-  }
-  // per-group sums of e (A) and of e 2^-(t+1) (Bh): TPP threads per
-  // (group, head), each over 32/TPP tokens, then a shuffle reduction
-  {
-    constexpr int NP = NG * GQA;
-    constexpr int TPP = NP <= 8 ? 32 : (NP <= 16 ? 16 : (NP <= 32 ? 8 : 4));
-    constexpr int TK = kGroup / TPP;
-    const int pr = tid / TPP, part = tid % TPP;
-    float a = 0.f, bh = 0.f;
-    if (pr < NP) {
-      const int gl = pr / GQA, hh = pr % GQA;
+    if (tid < GQA) pfs = (float)ftile[(hrow0 + tid) * ntile_ws + (int)(c0 / kTile)];
+  };
+  auto load_rows = [&](int chunk, uint32_t t) __attribute__((always_inline)) {
+    const uint4* vp = reinterpret_cast<const uint4*>(u.vplanes) + ((int64_t)chunk * kChunk + jl) * W;
+    // planes past the depth re-read plane 0 of the same row (same line, no
+    // extra traffic); they are masked in the un-plane
+    const uint32_t p0 = (uint32_t)rh;
+    prow0 = vp[p0 < t ? p0 : 0u];
+    prow1 = vp[p0 + 2 < t ? p0 + 2 : 0u];
+    prow2 = vp[p0 + 4 < t ? p0 + 4 : 0u];
+    prow3 = vp[p0 + 6 < t ? p0 + 6 : 0u];
+  };
+  auto store_chunk = [&](uint32_t t) __attribute__((always_inline)) {
+    if (tid < kChunk) {
+      tvs[tid] = (uint8_t)t;
 #pragma unroll
-      for (int k = 0; k < TK; ++k) {
-        const int jl = kGroup * gl + part * TK + k;
-        const float e = (float)es[hh][jl];
-        a += e;
-        bh = fmaf(e, ldexp_pow2f(-(int)tvs[jl] - 1), bh);
-      }
+      for (int hh = 0; hh < GQA; ++hh) es[hh][tid] = pes[hh];
     }
-    a = group_sum<TPP>(a);
-    bh = group_sum<TPP>(bh);
-    if (pr < NP && part == 0) {
-      Ag[pr / GQA][pr % GQA] = a;
-      Bg[pr / GQA][pr % GQA] = bh;
+#pragma unroll
+    for (int k = 0; k < MPT; ++k) {
+      const int i = k * 256 + tid;
+      vmeta_s[i / kDim][i % kDim] = pmeta[k];
     }
-  }
-  __syncthreads();
+    if (tid < GQA) fs[tid] = pfs;
+    (void)t;  // rows past the depth hold plane 0 again: masked in the un-plane
+    rows[rh][jl] = prow0;
+    rows[rh + 2][jl] = prow1;
+    rows[rh + 4][jl] = prow2;
+    rows[rh + 6][jl] = prow3;
+  };
 
-  // ---- 2. un-plane refined tokens into the code tile ----
-  {
-    const int bo = lane & 15, wb = bo >> 2, ob = bo & 3;
-    const uint32_t sel = 0x0C0C0000u | ((4u + (uint32_t)ob) << 8) | (uint32_t)ob;
-    const uint32_t* rows = reinterpret_cast<const uint32_t*>(vrows);
-    for (int i = 4 * wv + (lane >> 4); i < ndeep; i += 16) {
-      const int jl = lst[i];
-      const int t = tvs[jl], s0 = offs[jl];
-      uint32_t w[8];
-#pragma unroll
-      for (int p = 0; p < 8; ++p) w[p] = (p < t) ? rows[(s0 + p) * 4 + wb] : 0u;
-      uint32_t lo, hi;
-      unplane8(w, sel, lo, hi);
-      *reinterpret_cast<uint2*>(xl + jl * XS + 8 * bo) = make_uint2(lo, hi);
-    }
-    for (int i = ndeep + 4 * wv + (lane >> 4); i < nref; i += 16) {
-      const int jl = lst[i];
-      const int t = tvs[jl], s0 = offs[jl];
-      const uint32_t w0 = rows[s0 * 4 + wb];
-      const uint32_t w1 = t > 1 ? rows[(s0 + 1) * 4 + wb] : 0u;
-      const uint32_t w2 = t > 2 ? rows[(s0 + 2) * 4 + wb] : 0u;
-      const uint32_t w3 = t > 3 ? rows[(s0 + 3) * 4 + wb] : 0u;
-      uint32_t lo, hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(w0, w1, sel),
-                                              __builtin_amdgcn_perm(w2, w3, sel), 0x05040100u);
-      transpose8_hi4(lo, hi);
-      *reinterpret_cast<uint2*>(xl + jl * XS + 8 * bo) = make_uint2(lo, hi);
-    }
-  }
-  __syncthreads();
+  uint32_t t_rows = tv_of(cb);  // depth of token jl in the chunk whose rows are in flight
+  load_small(cb);
+  load_rows(cb, t_rows);
+  uint32_t t_next = cb + 1 < ce ? tv_of(cb + 1) : 0u;
 
-  // ---- 3. MFMA per (16-channel block, column set); wave wv: blocks 2wv, 2wv+1 ----
   const int m = lane & 15, kb = lane >> 4;
   const int gp = m / GQA, hn = m % GQA;
   const bool colv = m < GS * GQA;
@@ -1149,85 +1116,138 @@ __global__ __launch_bounds__(256) void k_gather(const uint8_t* store, const uint
   for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) Oacc[bl][rr] = 0.f;
-  for (int set = 0; set < NSET; ++set) {
-    const int gbase = set * GS;
+  const int q4 = lane >> 4, L = lane & 15;
+  // transposing plane read: lane 2e + s of a quarter addresses plane 7 - e,
+  // bytes 8s .. 8s + 7 of the quarter's token row; lane L then holds the
+  // plane bytes of channel octet L
+  const int troff = (7 - (L >> 1)) * (kChunk * 16) + 8 * (L & 1);
+
+  for (int chunk = cb; chunk < ce; ++chunk) {
+    const int64_t c0 = (int64_t)chunk * kChunk;
+    const int64_t gam0 = c0 / kGroup;
+    store_chunk(t_rows);
+    lds_barrier();
+    // next chunk's loads go out now and land while this one is computed
+    if (chunk + 1 < ce) {
+      t_rows = t_next;
+      load_small(chunk + 1);
+      load_rows(chunk + 1, t_rows);
+      t_next = chunk + 2 < ce ? tv_of(chunk + 2) : 0u;
+    }
+    // per-group sums of e (A) and of e 2^-(t+1) (Bh): TPP threads per
+    // (group, head), each over 32/TPP tokens, then a shuffle reduction
+    {
+      constexpr int NP = NG * GQA;
+      constexpr int TPP = NP <= 8 ? 32 : (NP <= 16 ? 16 : (NP <= 32 ? 8 : 4));
+      constexpr int TK = kGroup / TPP;
+      const int pr = tid / TPP, part = tid % TPP;
+      float a = 0.f, bh = 0.f;
+      if (pr < NP) {
+        const int gl = pr / GQA, hh = pr % GQA;
 #pragma unroll
-    for (int bl = 0; bl < 2; ++bl) {
-      const int cb = 16 * (2 * wv + bl);
-      f32x4 D = {0.f, 0.f, 0.f, 0.f};
-      for (int gi = 0; gi < GS; ++gi) {
-        const int gl = gbase + gi;
-        if (gl >= NG || (gam0 + gl + 1) * kGroup > Tp) continue;
-        const int t0 = kGroup * gl + 8 * kb;
-        const uint8_t* src = xl + (t0 + (m >> 1)) * XS + cb + 8 * (m & 1);
-        const i32x2 xv = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)src);
-        uint32_t ap[4];
-        ap[0] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.x, 0x04010400u);
-        ap[1] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.x, 0x04030402u);
-        ap[2] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.y, 0x04010400u);
-        ap[3] = __builtin_amdgcn_perm(0x64646464u, (uint32_t)xv.y, 0x04030402u);
-        const f16x8 av = __builtin_bit_cast(f16x8, ap);
-        f16x8 bv = {0, 0, 0, 0, 0, 0, 0, 0};
-        if (colv && gp == gi) bv = *reinterpret_cast<const f16x8*>(&es[hn][t0]);
-        D = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, D, 0, 0, 0);
+        for (int k = 0; k < TK; ++k) {
+          const int j = kGroup * gl + part * TK + k;
+          const float e = (float)es[hh][j];
+          a += e;
+          bh = fmaf(e, ldexp_pow2f(-(int)tvs[j] - 1), bh);
+        }
       }
-      // fold: D row = channel cb + 4 kb + rr, column m = (gp, hn)
-      const int gl = gbase + gp;
-      if (colv && gl < NG && (gam0 + gl + 1) * kGroup <= Tp) {
-        const float A = Ag[gl][hn], Bh = Bg[gl][hn];
+      a = group_sum<TPP>(a);
+      bh = group_sum<TPP>(bh);
+      if (pr < NP && part == 0) {
+        Ag[pr / GQA][pr % GQA] = a;
+        Bg[pr / GQA][pr % GQA] = bh;
+      }
+    }
+    // ---- un-plane: wave w, step i -> tokens 32 w + 4 i + quarter ----
+#pragma unroll 2
+    for (int it = 0; it < 8; ++it) {
+      const int j0 = 32 * wv + 4 * it;
+      const uint32_t t4 = *reinterpret_cast<const uint32_t*>(&tvs[j0]);  // the 4 tokens' depths
+      const uint32_t tmax = max(max(t4 & 0xFFu, (t4 >> 8) & 0xFFu), max((t4 >> 16) & 0xFFu, t4 >> 24));
+      const int j = j0 + q4;
+      const uint32_t t = (t4 >> (8 * q4)) & 0xFFu;
+      const long v = tr8_read(reinterpret_cast<const uint8_t*>(rows) + j * 16 + troff);
+      const uint2 pb = __builtin_bit_cast(uint2, v);
+      const uint64_t keep = t >= 8u ? ~0ull : (t == 0u ? 0ull : ~0ull << (64 - 8 * t));
+      uint32_t lo = pb.x & (uint32_t)keep, hi = pb.y & (uint32_t)(keep >> 32);
+      if (tmax <= 4u) transpose8_hi4(lo, hi);
+      else transpose8_halves(lo, hi);
+      *reinterpret_cast<uint2*>(xl + j * XS + 8 * L) = make_uint2(lo, hi);
+    }
+    lds_barrier();
+
+    // ---- MFMA per (16-channel block, column set); wave w: blocks 2w, 2w+1 ----
+    for (int set = 0; set < NSET; ++set) {
+      const int gbase = set * GS;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const uint32_t mt = vmeta_s[gl][cb + 4 * kb + rr];
-          const float lo = bf16_to_float(mt & 0xFFFFu), rng = bf16_to_float(mt >> 16);
-          Oacc[bl][rr] += fmaf(lo, A, rng * (Bh + (D[rr] - 1024.f * A) * (1.f / 256.f)));
+      for (int bl = 0; bl < 2; ++bl) {
+        const int cbk = 16 * (2 * wv + bl);
+        f32x4 D = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gi = 0; gi < GS; ++gi) {
+          const int gl = gbase + gi;
+          if (gl >= NG || (gam0 + gl + 1) * kGroup > Tp) continue;
+          const int t0 = kGroup * gl + 8 * kb;
+          const uint2 xv = __builtin_bit_cast(uint2, tr8_read(xl + (t0 + (m >> 1)) * XS + cbk + 8 * (m & 1)));
+          uint32_t ap[4];
+          ap[0] = __builtin_amdgcn_perm(0x64646464u, xv.x, 0x04010400u);
+          ap[1] = __builtin_amdgcn_perm(0x64646464u, xv.x, 0x04030402u);
+          ap[2] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04010400u);
+          ap[3] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04030402u);
+          const f16x8 av = __builtin_bit_cast(f16x8, ap);
+          f16x8 bv = {0, 0, 0, 0, 0, 0, 0, 0};
+          if (colv && gp == gi) bv = *reinterpret_cast<const f16x8*>(&es[hn][t0]);
+          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, D, 0, 0, 0);
+        }
+        // fold: D row = channel cbk + 4 kb + rr, column m = (gp, hn)
+        const int gl = gbase + gp;
+        if (colv && gl < NG && (gam0 + gl + 1) * kGroup <= Tp) {
+          const float A = Ag[gl][hn], Bh = Bg[gl][hn], f = fs[hn];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const uint32_t mt = vmeta_s[gl][cbk + 4 * kb + rr];
+            const float lo = bf16_to_float(mt & 0xFFFFu), rng = bf16_to_float(mt >> 16);
+            Oacc[bl][rr] = fmaf(f, fmaf(lo, A, rng * (Bh + (D[rr] - 1024.f * A) * (1.f / 256.f))), Oacc[bl][rr]);
+          }
         }
       }
     }
+    lds_barrier();
   }
-  __syncthreads();
-  float* red2 = reinterpret_cast<float*>(vrows);  // [16 columns][128 channels]
+
+  // ---- column sums per head, open group, partial output of the run ----
+  float* red2 = reinterpret_cast<float*>(rows);  // [16 columns][128 channels]
 #pragma unroll
   for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) red2[m * kDim + 16 * (2 * wv + bl) + 4 * kb + rr] = Oacc[bl][rr];
   __syncthreads();
-
-  // ---- 4. per-head sums over the column groups, open group, chunk partial ----
-  const int64_t jt0 = Tp > c0 ? Tp : c0;
-  const int64_t jt1 = len < c0 + kChunk ? len : c0 + kChunk;
+  const int64_t cl0 = (int64_t)(ce - 1) * kChunk;  // the last chunk (es, fs still in LDS)
+  const int64_t jt0 = Tp > cl0 ? Tp : cl0;
+  const int64_t jt1 = len < cl0 + kChunk ? len : cl0 + kChunk;
   for (int o = tid; o < GQA * kDim; o += 256) {
     const int hh = o / kDim, c = o % kDim;
     float s = 0.f;
-    for (int q = 0; q < GS; ++q) s += red2[(q * GQA + hh) * kDim + c];
+    for (int qq = 0; qq < GS; ++qq) s += red2[(qq * GQA + hh) * kDim + c];
+    float st = 0.f;
     for (int64_t j = jt0; j < jt1; ++j)
-      s = fmaf((float)es[hh][j - c0], load_elem_f<DT>(u.vtail, (j - Tp) * kDim + c), s);
-    opart[((hrow0 + hh) * nchunk_ws + chunk) * kDim + c] = s * fs[hh];
+      st = fmaf((float)es[hh][j - cl0], load_elem_f<DT>(u.vtail, (j - Tp) * kDim + c), st);
+    opart[((hrow0 + hh) * nrun_ws + blockIdx.y) * kDim + c] = fmaf(st, fs[hh], s);
   }
 }
 
-// out[b][h][c] = sum over the request's chunks, in chunk order.  One thread
-// per output element; the chunk loads are independent.
-__global__ __launch_bounds__(256) void k_out_reduce(const uint8_t* store, int H, int nchunk_ws,
-                                                    int64_t nout, const float* opart, float* out) {
+// out[b][h][c] = sum over the unit's runs, in run order.  One thread per
+// output element.
+__global__ __launch_bounds__(256) void k_out_reduce(int nrun, int nrun_ws, int64_t nout,
+                                                    const float* opart, float* out) {
   const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (o >= nout) return;
   const int64_t bh = o / kDim;
   const int c = (int)(o - bh * kDim);
-  const int b = (int)(bh / H);
-  const ReqRecord r = req_of(store, b);
-  const int nch = (int)((r.len + kChunk - 1) / kChunk);
-  const float* p = opart + bh * nchunk_ws * kDim + c;
+  const float* p = opart + bh * nrun_ws * kDim + c;
   float s = 0.f;
-  int ch = 0;
-  for (; ch + 4 <= nch; ch += 4) {
-    const float v0 = p[(int64_t)ch * kDim], v1 = p[(int64_t)(ch + 1) * kDim];
-    const float v2 = p[(int64_t)(ch + 2) * kDim], v3 = p[(int64_t)(ch + 3) * kDim];
-    s += v0;
-    s += v1;
-    s += v2;
-    s += v3;
-  }
-  for (; ch < nch; ++ch) s += p[(int64_t)ch * kDim];
+  for (int k = 0; k < nrun; ++k) s += p[(int64_t)k * kDim];
   out[o] = s;
 }
 
@@ -1297,14 +1317,22 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
                        L.ntile, (const double*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
                        (double*)(ws + L.ftile), (double*)(ws + L.aval), tv);
   mark(a, 3, st);
-  hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(a.B * a.G, L.nchunk), dim3(256), 0, st,
-                     (const uint8_t*)a.store, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax, L.ntile,
-                     L.nchunk, (const _Float16*)(ws + L.e16), (const double*)(ws + L.ftile),
-                     (float*)(ws + L.opart));
-  const int64_t nout = (int64_t)a.B * a.H * kDim;
-  hipLaunchKernelGGL(k_out_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st,
-                     (const uint8_t*)a.store, a.H, L.nchunk, nout, (const float*)(ws + L.opart),
-                     a.out);
+  {
+    // runs of consecutive chunks per block: about four blocks per compute
+    // unit (37 KB of LDS each)
+    const int64_t total = (int64_t)a.B * a.G * L.nchunk;
+    const int64_t slots = 4 * (int64_t)device_cu_count();
+    int run = (int)((total + slots - 1) / slots);
+    if (run < 1) run = 1;
+    const int nrun = (L.nchunk + run - 1) / run;
+    hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), 0, st,
+                       (const uint8_t*)a.store, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax,
+                       L.ntile, L.nchunk, (const _Float16*)(ws + L.e16),
+                       (const double*)(ws + L.ftile), (float*)(ws + L.opart));
+    const int64_t nout = (int64_t)a.B * a.H * kDim;
+    hipLaunchKernelGGL(k_out_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st, nrun,
+                       L.nchunk, nout, (const float*)(ws + L.opart), a.out);
+  }
   mark(a, 4, st);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }

@@ -37,7 +37,7 @@ constexpr int kGroup = 32;      // tokens per quantiser group
 constexpr int kDim = 128;       // head_dim supported by the kernels
 constexpr int kTile = 512;      // tokens per score workgroup (16 groups);
                                 // also the softmax split-context unit
-constexpr int kChunk = 256;     // tokens per value-gather workgroup (8 groups)
+constexpr int kChunk = 128;     // tokens per value-gather step (4 groups)
 
 struct StoreHeader {          // first 256 bytes of a store
   uint32_t magic, version;
@@ -121,7 +121,8 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 //   ftile  f64 [B][H][ntile]      exp(m_tile - m) / Z
 //   aval   f64 [B][G][capmax]     value weights (only when they do not fit
 //                                 in the allocator's registers)
-//   opart  f32 [B][H][nchunk][d]  per-chunk partial outputs
+//   opart  f32 [B][H][nchunk][d]  partial outputs, one per run of chunks
+//                                 (at most nchunk runs)
 struct WsLayout {
   int64_t tk, tv, ebuf, e16, tilepart, ftile, aval, opart, size;
   int ntile, nchunk;
