@@ -15,6 +15,8 @@
 
 namespace readkv {
 
+constexpr int kSmallAppend = 64;  // tokens per request up to which one launch appends
+
 __device__ __forceinline__ int64_t clamp_n(const ReqRecord& r, const int32_t* n_new, int b,
                                            int n_max) {
   int64_t n = n_new ? (int64_t)n_new[b] : (int64_t)n_max;
@@ -24,32 +26,21 @@ __device__ __forceinline__ int64_t clamp_n(const ReqRecord& r, const int32_t* n_
   return n;
 }
 
-// grid (max groups closing, G, B), 256 threads: threads 0..127 encode the
-// key channels, 128..255 the value channels of one closing group.
+// Encode closed group gam of unit (b, g) with one block of 256 threads:
+// threads 0..127 take the key channels, 128..255 the value channels.  Rows
+// j < len0 of the group come from the tail buffer, the others from the new
+// tokens (row0 = the unit's first new-token row).  Returns rng^2 of the
+// thread's channel (0 for a non-finite group).  Contains block barriers:
+// every thread of the block must call it.
 template <int DT>
-__global__ __launch_bounds__(256) void k_encode_groups(uint8_t* store, const void* knew,
-                                                       const void* vnew, const int32_t* n_new,
-                                                       int n_max, int G, int W) {
-  constexpr int esize = DT == 0 ? 2 : 4;
-  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const ReqRecord r = req_of(store, b);
-  const int64_t len0 = r.len;
-  const int64_t n = clamp_n(r, n_new, b, n_max);
-  const int64_t first = len0 / kGroup;
-  const int64_t count = (len0 + n) / kGroup - first;
-  if (i >= count) return;
-  const int64_t gam = first + i;
-  const Unit u = unit_of(store, r, g, G, kDim, W, esize);
-
+__device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, const void* knew,
+                                               const void* vnew, int64_t row0, int64_t len0,
+                                               int64_t gam, int W, int* bad_s, double* rv2) {
   const int tid = threadIdx.x;
   const bool isv = tid >= 128;
   const int c = tid & 127;
   const void* src = isv ? vnew : knew;
   const uint8_t* tail = isv ? u.vtail : u.ktail;
-  const int64_t row0 = ((int64_t)b * G + g) * n_max;
-
-  __shared__ int bad_s[2];
-  __shared__ double rv2[128];
   if (tid < 2) bad_s[tid] = 0;
   __syncthreads();
 
@@ -130,6 +121,27 @@ __global__ __launch_bounds__(256) void k_encode_groups(uint8_t* store, const voi
     for (int cc = 0; cc < kDim; ++cc) e = e + rv2[cc];
     u.ev[gam] = e;
   }
+  return r2;
+}
+
+// grid (max groups closing, G, B), 256 threads: one closing group per block.
+template <int DT>
+__global__ __launch_bounds__(256) void k_encode_groups(uint8_t* store, const void* knew,
+                                                       const void* vnew, const int32_t* n_new,
+                                                       int n_max, int G, int W) {
+  constexpr int esize = DT == 0 ? 2 : 4;
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const ReqRecord r = req_of(store, b);
+  const int64_t len0 = r.len;
+  const int64_t n = clamp_n(r, n_new, b, n_max);
+  const int64_t first = len0 / kGroup;
+  const int64_t count = (len0 + n) / kGroup - first;
+  if (i >= count) return;
+  __shared__ int bad_s[2];
+  __shared__ double rv2[128];
+  const Unit u = unit_of(store, r, g, G, kDim, W, esize);
+  encode_group<DT>(store, u, knew, vnew, ((int64_t)b * G + g) * n_max, len0, first + i, W, bad_s,
+                   rv2);
 }
 
 // grid (G, B), 128 threads: E^K[c] += rng^2 of every newly closed group,
@@ -194,6 +206,63 @@ __global__ __launch_bounds__(256) void k_tail_update(uint8_t* store, const void*
   }
 }
 
+// Small appends (n_max <= kSmallAppend tokens per request), one launch: grid
+// (G, B), 256 threads per (request, KV head): encode the closing groups in
+// group order, add their rng_K^2 to E^K in that order, move the still-open
+// tokens into the tail.  The request's last block to finish (a ticket
+// counter in the request record's spare field, reset by that block)
+// publishes the new length, after every block has read the old one.
+template <int DT>
+__global__ __launch_bounds__(256) void k_append_small(uint8_t* store, const void* knew,
+                                                      const void* vnew, const int32_t* n_new,
+                                                      int n_max, int G, int W) {
+  constexpr int esize = DT == 0 ? 2 : 4;
+  const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  __shared__ int bad_s[2];
+  __shared__ double rv2[128];
+  __shared__ int last_s;
+  ReqRecord* rp = reinterpret_cast<ReqRecord*>(store + 256 + 32 * (int64_t)b);
+  const ReqRecord r = *rp;
+  const int64_t want = n_new ? (int64_t)n_new[b] : (int64_t)n_max;
+  const int64_t n = clamp_n(r, n_new, b, n_max);
+  const int64_t len0 = r.len, len1 = len0 + n;
+  const int64_t first = len0 / kGroup, last = len1 / kGroup;
+  const int64_t base = last * kGroup;
+  const int64_t from = base > len0 ? base : len0;  // older tail tokens stay in place
+  const Unit u = unit_of(store, r, g, G, kDim, W, esize);
+  const int64_t row0 = ((int64_t)b * G + g) * n_max;
+  for (int64_t gam = first; gam < last; ++gam) {
+    const double r2 = encode_group<DT>(store, u, knew, vnew, row0, len0, gam, W, bad_s, rv2);
+    if (tid < kDim) u.ek[tid] = u.ek[tid] + r2;
+    __syncthreads();  // the group's tail rows are read before they are replaced
+  }
+  const int64_t per = (len1 - from) * kDim;
+  for (int64_t e = tid; e < per; e += 256) {
+    const int64_t j = from + e / kDim;
+    const int c = (int)(e % kDim);
+    const int64_t srow = (row0 + (j - len0)) * kDim + c, drow = (j - base) * kDim + c;
+    if constexpr (DT == 0) {
+      ((uint16_t*)u.ktail)[drow] = ((const uint16_t*)knew)[srow];
+      ((uint16_t*)u.vtail)[drow] = ((const uint16_t*)vnew)[srow];
+    } else {
+      ((float*)u.ktail)[drow] = ((const float*)knew)[srow];
+      ((float*)u.vtail)[drow] = ((const float*)vnew)[srow];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    unsigned long long* ticket = reinterpret_cast<unsigned long long*>(&rp->reserved);
+    __threadfence();
+    last_s = atomicAdd(ticket, 1ull) == (unsigned long long)(G - 1);
+  }
+  __syncthreads();
+  if (tid == 0 && last_s) {
+    *reinterpret_cast<unsigned long long*>(&rp->reserved) = 0ull;
+    rp->len = len1;
+    if (n < want) atomicOr(&header_of(store)->flags, 2u);
+  }
+}
+
 __global__ void k_fill_zero(uint32_t* p, int64_t nwords) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < nwords;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -210,8 +279,17 @@ int launch_store_zero(void* store, size_t bytes, hipStream_t st) {
 }
 
 int launch_encode(const EncodeArgs& a, hipStream_t st) {
-  const int max_groups = (int)((a.n_max + kGroup - 1) / kGroup);
   if (a.n_max <= 0) return 0;
+  if (a.n_max <= kSmallAppend) {
+    if (a.dtype == 0)
+      hipLaunchKernelGGL((k_append_small<0>), dim3(a.G, a.B), dim3(256), 0, st, (uint8_t*)a.store, a.knew,
+                         a.vnew, a.n_new, a.n_max, a.G, a.W);
+    else
+      hipLaunchKernelGGL((k_append_small<1>), dim3(a.G, a.B), dim3(256), 0, st, (uint8_t*)a.store, a.knew,
+                         a.vnew, a.n_new, a.n_max, a.G, a.W);
+    return hipGetLastError() == hipSuccess ? 0 : -6;
+  }
+  const int max_groups = (int)((a.n_max + kGroup - 1) / kGroup);
   if (a.dtype == 0) {
     hipLaunchKernelGGL((k_encode_groups<0>), dim3(max_groups, a.G, a.B), dim3(256), 0, st,
                        (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);

@@ -1,7 +1,8 @@
 // Store and workspace layout shared by the host entry points and the kernels.
 //
 // Store = header + one region per request.  Header: 256 bytes of fields,
-// then one 32-byte record {len, cap, offset, reserved} per request,
+// then one 32-byte record {len, cap, offset, ticket} per request (ticket:
+// the append's completion counter, zero between calls),
 // rounded up to 4096 bytes.  A request region with capacity `cap` tokens
 // (multiple of 32, ng = cap/32 groups) holds, each sub-array 256-byte
 // aligned:
