@@ -26,6 +26,36 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 KERNELS = ["key_alloc", "score", "value_alloc", "value_gather"]
+METRIC = "decode attn query-heads\u00b7ctx-tokens/s + achieved HBM GB/s vs peak, (W,R)=(8,4),(8,2)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_step_llama3-8b-B16-T8192.txt")
+
+
+def source_hash():
+    """sha256 over the HIP sources and headers the library is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "query_adaptive_decode_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary,
+    or None when it was taken on other sources (or is missing)."""
+    try:
+        rows = [l.strip() for l in open(TRAFFIC_FILE) if "=" in l and not l.startswith("#")]
+    except OSError:
+        return None
+    kv = dict(l.split("=", 1) for l in rows)
+    if kv.get("source_sha256") != source_hash():
+        return None
+    try:
+        return float(kv[f"{kernel}.fetch_bytes"]) + float(kv[f"{kernel}.write_bytes"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _hip():
@@ -52,7 +82,7 @@ def _elapsed(h, a, b):
     return ms.value
 
 
-def run_rate(cfg, dev, lcfg, R, warmup, steps, torch):
+def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, evict=True):
     from query_adaptive_decode_amd import binding as Bd
     B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
     T0 = int(cfg["T0"])
@@ -105,6 +135,24 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch):
         vsum += tv[:, :, :tp].sum(dtype=torch.int64)
         s += 1
     torch.cuda.synchronize()
+    # ---- cache-evicted steps: a 512 MiB write before each step pushes the
+    # store out of L2 and the Infinity Cache; the step is timed with events ----
+    evict_ms = None
+    if evict:
+        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tot = 0.0
+        for i in range(steps):
+            scratch.fill_(i & 0xFF)
+            ev0.record()
+            cache.append(dev["kstep"][s], dev["vstep"][s])
+            cache.decode(dev["q"][s], R, R, out=out)
+            ev1.record()
+            ev1.synchronize()
+            tot += ev0.elapsed_time(ev1)
+            s += 1
+        evict_ms = tot / steps
+        del scratch
     kern_ms = {k: 0.0 for k in KERNELS}
     enc_ms = 0.0
     for i in range(steps):
@@ -122,6 +170,7 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch):
            "key_alloc": B * G * d * 8 + B * H * d * 2, "value_alloc": B * G * ng * 8}
     step_bytes = kpay + vpay + 2 * meta
     return dict(R=R, ms_per_step=wall / steps * 1e3, qh_tok_per_s=qh_tok / wall,
+                evicted_ms_per_step=evict_ms,
                 kernel_ms=kern_ms, encode_ms=enc_ms, alg_bytes=alg, step_alg_bytes=step_bytes,
                 logical_GBps_step=step_bytes / (wall / steps) / 1e9,
                 mean_key_bits_per_scalar=float(ksum.item()) / steps / (B * G * d),
@@ -180,11 +229,13 @@ def copy_probe(torch, mib=512, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rates", default="4,2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-evict", action="store_true",
+                    help="skip the cache-evicted per-step timing")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -199,7 +250,11 @@ def main():
     rates = [float(r) for r in args.rates.split(",")]
     if args.copy_probe:
         copy_probe(torch)
-    total_steps = args.warmup + 2 * args.steps
+    total_steps = args.warmup + (3 if not args.no_evict else 2) * args.steps
+    if total_steps > int(cfg["steps"]):
+        print(json.dumps({"error": f"warmup + {'3' if not args.no_evict else '2'} x steps = {total_steps} "
+                                   f"exceeds the workload's {cfg['steps']} decode steps"}))
+        sys.exit(2)
     t = time.perf_counter()
     hin = workload.host_inputs(cfg, total_steps)
     dev = workload.to_device(hin)
@@ -208,16 +263,17 @@ def main():
     print(f"# inputs ready in {time.perf_counter() - t:.1f} s", file=sys.stderr, flush=True)
     res = {}
     for R in rates:
-        res[R] = run_rate(cfg, dev, lcfg, R, args.warmup, args.steps, torch)
+        res[R] = run_rate(cfg, dev, lcfg, R, args.warmup, args.steps, torch, evict=not args.no_evict)
         r = res[R]
         print(f"# R={R}: {r['ms_per_step']:.3f} ms/step, {r['qh_tok_per_s'] / 1e9:.2f} G qh*tok/s, "
               f"kernels {json.dumps({k: round(v * 1e3, 1) for k, v in r['kernel_ms'].items()})} us, "
-              f"encode {r['encode_ms'] * 1e3:.1f} us", file=sys.stderr, flush=True)
+              f"encode {r['encode_ms'] * 1e3:.1f} us, evicted "
+              f"{(r['evicted_ms_per_step'] or 0.0):.3f} ms/step", file=sys.stderr, flush=True)
     head = res[rates[0]]
     dom = max(["score", "value_gather"], key=lambda k: head["kernel_ms"][k])
     ach = head["alg_bytes"][dom] / (head["kernel_ms"][dom] * 1e-3) / 1e9
     line = {
-        "metric": "decode attn query-heads*ctx-tokens/s, (W,R)=(8,%g)" % rates[0],
+        "metric": METRIC,
         "value": head["qh_tok_per_s"],
         "unit": "query-heads*ctx-tokens/s",
         "n_gpus": 1,
@@ -227,15 +283,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f64/f32",
+        "dtype": "u8 codes; i8 MFMA + f64 logits; f16 MFMA + f32 values",
         "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": cfg["B"], "q_heads": cfg["H"],
                    "kv_heads": cfg["G"], "head_dim": cfg["d"], "prompt_tokens": cfg["T0"],
                    "W": cfg["W"], "R": rates, "step": "append 1 token/request + decode"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None},
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(dom),
+                     "alg_bytes_per_launch": head["alg_bytes"][dom],
+                     "kernel_us": head["kernel_ms"][dom] * 1e3},
         "rates": {f"8,{R:g}": {
             "qh_tok_per_s": r["qh_tok_per_s"], "ms_per_step": r["ms_per_step"],
+            "evicted_ms_per_step": r["evicted_ms_per_step"],
             "kernel_us": {k: v * 1e3 for k, v in r["kernel_ms"].items()},
             "encode_us": r["encode_ms"] * 1e3,
             "logical_bytes_per_step": r["step_alg_bytes"],

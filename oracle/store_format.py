@@ -14,7 +14,7 @@ header (align_up(256 + 32*B, 4096) bytes)
 request region b (cap = cap_b, a multiple of 32; ng = cap/32):
   Kplanes u32 [G][d][W][ngk]  bit i of word (g,c,p,gamma) = plane p (bit
                               W-1-p of the code) of token 32*gamma+i, chan c;
-                              ngk = ng rounded up to a multiple of 4
+                              ngk = ng rounded up to a multiple of 32
   Vplanes u32 [G][cap][W][d/32]  bit (c%32) of word (g,j,p,c/32) = plane p
                               of token j, channel c
   Kmeta   u32 [G][ng][d]      lo bf16 bits | rng bf16 bits << 16
@@ -43,7 +43,7 @@ def region_layout(G: int, d: int, W: int, cap: int, esize: int) -> dict:
     """Byte offsets (relative to the region start) and sizes of each
     sub-array of one request region."""
     ng = cap // 32
-    ngk = _al(ng, 4)
+    ngk = _al(ng, 32)
     parts = [
         ("Kplanes", G * d * W * ngk * 4),
         ("Vplanes", G * cap * W * (d // 32) * 4),
@@ -76,7 +76,7 @@ def pack_unit(enc_k, enc_v, cap: int, dtype: str) -> dict:
     tp, d = enc_k.codes.shape
     ng = cap // 32
     ngc = enc_k.n_groups
-    kpl = np.zeros((d, W, _al(ng, 4)), dtype=np.uint32)
+    kpl = np.zeros((d, W, _al(ng, 32)), dtype=np.uint32)
     ck = enc_k.codes.reshape(ngc, 32, d)
     for p in range(W):
         bits = ((ck >> (W - 1 - p)) & 1).astype(np.uint64)       # [ngc][32][d]
@@ -151,7 +151,7 @@ def unpack_unit(buf: np.ndarray, hdr: dict, b: int, g: int) -> dict:
 
     edt = np.uint16 if esize == 2 else np.float32
     return dict(
-        Kplanes=sub("Kplanes", np.uint32, (d, W, _al(ng, 4))),
+        Kplanes=sub("Kplanes", np.uint32, (d, W, _al(ng, 32))),
         Vplanes=sub("Vplanes", np.uint32, (cap, W, d // 32)),
         Kmeta=sub("Kmeta", np.uint32, (ng, d)),
         Vmeta=sub("Vmeta", np.uint32, (ng, d)),

@@ -57,13 +57,13 @@ __device__ __forceinline__ void unplane8(const uint32_t (&w)[8], uint32_t sel, u
 // bisection on the 12-bit sign+exponent field, then an exact rank among the
 // candidates in the threshold's exponent class.
 // ---------------------------------------------------------------------------
-template <int DT>
+template <int GQA, int DT>
 __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
                                                   int W, float RK, uint8_t* tk) {
   constexpr int esize = DT == 0 ? 2 : 4;
   const int unit = blockIdx.x;
   const int b = unit / G, g = unit - b * G;
-  const int gqa = H / G;
+  constexpr int gqa = GQA;
   const ReqRecord r = req_of(store, b);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const int lane = threadIdx.x;
@@ -71,15 +71,20 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
   __shared__ uint32_t cc[2 * 64 * 8];
 
   uint64_t key[2][8];
+  double wv[2];
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int c = lane + 64 * k;
+    double qv[GQA];
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh)
+      qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * gqa + hh) * kDim + c);
+    const double ekc = u.ek[c];
     double qsq = 0.0;
-    for (int hh = 0; hh < gqa; ++hh) {
-      const double qv = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * gqa + hh) * kDim + c);
-      qsq = __dadd_rn(qsq, __dmul_rn(qv, qv));
-    }
-    const double w = __dmul_rn(qsq, u.ek[c]);
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
+    const double w = __dmul_rn(qsq, ekc);
+    wv[k] = w;
 #pragma unroll
     for (int t = 1; t <= 8; ++t) {
       const double gt = __dmul_rn(w, ldexp_pow2(-2 * t));
@@ -95,7 +100,75 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
     for (int t = 0; t < 8; ++t) npos += (uint32_t)__popcll(__ballot(key[k][t] != 0ull));
 
   uint32_t sel[2] = {0u, 0u};
-  if (npos <= Bk) {
+  // Fast path: every positive weight w_c has a normal exponent field E_c in
+  // [2W + 1, 2046], so each gain w_c 4^-(t+1) is exact with field
+  // E_c - 2t - 2 and mantissa M_c.  Gains then order by that field first;
+  // the B_K-th largest lies in the highest field level L with
+  //   count(L) = sum_c #{t < W : E_c - 2t - 2 >= L} >= B_K
+  // (bisection on L), and at that level each channel has at most one
+  // candidate, ranked by (M_c descending, c ascending).
+  int ec[2];
+  uint64_t mc[2];
+  uint32_t rk[2] = {0u, 0u};
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint64_t wb = dbits(wv[k]);
+    ec[k] = wv[k] > 0.0 ? (int)(wb >> 52) : -1;  // no candidate unless w_c > 0
+    mc[k] = wb & 0x000FFFFFFFFFFFFFull;
+  }
+  const bool fast = !__any((ec[0] >= 0 && (ec[0] < 2 * W + 1 || ec[0] > 2046)) ||
+                           (ec[1] >= 0 && (ec[1] < 2 * W + 1 || ec[1] > 2046)));
+  auto cnt_ge = [&](int k, int lvl) -> int {  // #{t < W : E - 2t - 2 >= lvl} for slot k
+    if (ec[k] < 0) return 0;
+    const int d = ec[k] - 2 - lvl;
+    return d < 0 ? 0 : min(d / 2 + 1, W);
+  };
+  auto wave_isum = [](int v) -> int {  // DPP row sums, then the four rows
+    v += (int)dpp_u32<kDppQuadXor1>((uint32_t)v);
+    v += (int)dpp_u32<kDppQuadXor2>((uint32_t)v);
+    v += (int)dpp_u32<kDppRowHalfMirror>((uint32_t)v);
+    v += (int)dpp_u32<kDppRowMirror>((uint32_t)v);
+    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+  };
+  if (fast && npos > Bk && Bk > 0) {
+    int lo_l = 1, hi_l = 2046;  // count(lo_l) >= Bk holds (all candidates are >= 1)
+    while (lo_l < hi_l) {
+      const int mid = (lo_l + hi_l + 1) >> 1;
+      if ((uint32_t)wave_isum(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
+      else hi_l = mid - 1;
+    }
+    const int Ls = lo_l;
+    const uint32_t above = (uint32_t)wave_isum(cnt_ge(0, Ls + 1) + cnt_ge(1, Ls + 1));
+    const uint32_t rem = Bk - above;  // >= 1
+    bool at[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      sel[k] = (uint32_t)cnt_ge(k, Ls + 1);
+      const int d = ec[k] - 2 - Ls;
+      at[k] = ec[k] >= 0 && d >= 0 && (d & 1) == 0 && d / 2 < W;
+    }
+    // rank within the level: walk the lanes holding a candidate there
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      uint64_t lanes = __ballot(at[k2]);
+      while (lanes) {
+        const int src = __builtin_ctzll(lanes);
+        lanes &= lanes - 1;
+        const uint64_t m2 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mc[k2] >> 32), src) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mc[k2], src);
+        const int c2 = src + 64 * k2;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int c = lane + 64 * k;
+          if (at[k] && (m2 > mc[k] || (m2 == mc[k] && c2 < c))) ++rk[k];
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (at[k] && rk[k] < rem) ++sel[k];
+  } else if (npos <= Bk) {
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
@@ -1277,7 +1350,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   const int esize = DT == 0 ? 2 : 4;
 
   mark(a, 0, st);
-  hipLaunchKernelGGL((k_key_alloc<DT>), dim3(a.B * a.G), dim3(64), 0, st, (const uint8_t*)a.store,
+  hipLaunchKernelGGL((k_key_alloc<GQA, DT>), dim3(a.B * a.G), dim3(64), 0, st, (const uint8_t*)a.store,
                      a.q, a.H, a.G, a.W, a.RK, tk);
   mark(a, 1, st);
   // slots staged per score tile: at most min(B_K, 128 W) chosen key lines,

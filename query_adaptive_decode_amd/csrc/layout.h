@@ -8,8 +8,10 @@
 // aligned:
 //   Kplanes u32 [G][d][W][ngk]     token-packed: bit i of word (g,c,p,gamma)
 //                                  is plane p of token 32*gamma+i, channel c;
-//                                  ngk = ng rounded up to a multiple of 4, so
-//                                  every 4-group run is one aligned 16 B load
+//                                  ngk = ng rounded up to a multiple of 32:
+//                                  every line is whole 128 B cache lines, so
+//                                  a 16-group (512-token) segment is one
+//                                  aligned 64 B half line
 //   Vplanes u32 [G][cap][W][d/32]  channel-packed: a token's t-plane prefix
 //                                  is t*d/8 contiguous bytes
 //   Kmeta   u32 [G][ng][d]         lo bf16 | rng bf16 << 16
@@ -58,7 +60,7 @@ RKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 RKV_HD int64_t header_bytes(int B) { return align_up(256 + 32 * (int64_t)B, 4096); }
 
 // words per key-plane line (one (channel, plane) over all groups)
-RKV_HD int64_t key_line_words(int64_t cap) { return align_up(cap / kGroup, 4); }
+RKV_HD int64_t key_line_words(int64_t cap) { return align_up(cap / kGroup, 32); }
 
 struct RegionLayout {
   int64_t kplanes, vplanes, kmeta, vmeta, ek, ev, ktail, vtail, size;
