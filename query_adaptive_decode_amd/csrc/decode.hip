@@ -442,6 +442,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   __shared__ uint8_t cperm[kDim];
   __shared__ uint8_t s2c[kDim * 8];
   __shared__ uint32_t wtot[2];
+  __shared__ uint32_t dcnt[2][9];  // channels per depth value, per wave
 
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
@@ -455,26 +456,54 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
+  auto tile_ngp = [&](int tile) -> int {
+    const int64_t n = Tp / kGroup - (int64_t)tile * NG;
+    return (int)(n < 0 ? 0 : (n > NG ? NG : n));
+  };
+  uint32_t pmeta[MPT];
+  auto load_meta = [&](int tile) {
+    const int64_t gam0 = (int64_t)tile * NG;
+    const int ngp = tile_ngp(tile);
+#pragma unroll
+    for (int k = 0; k < MPT; ++k) {
+      const int i = k * 256 + tid, gl = i / kDim, c = i % kDim;
+      pmeta[k] = gl < ngp ? u.kmeta[(gam0 + gl) * kDim + c] : 0u;
+    }
+  };
+  load_meta(tile_begin);  // independent of the depths: in flight during the setup
+
   // ---- once per block: depths, query, per-head digit scale, slot table ----
-  uint32_t tv_ = 0, inc = 0;
+  uint32_t tv_ = 0, inc = 0, below = 0;
   if (tid < kDim) {
     const int c = tid;
     tv_ = tk[((int64_t)b * G + g) * kDim + c];
-    tks[c] = (uint8_t)tv_;
+    double qv[GQA];
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh)
+      qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + c);
     const double ek = u.ek[c];
+    tks[c] = (uint8_t)tv_;
     // 2^er >= sqrt(E_c) >= every closed group's rng_c
     const int er = ek > 0.0 ? ((ilogb_bits(ek) + 2) >> 1) : 0;
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
-      const double qv = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + c);
-      qd[hh][c] = qv;
-      int e = (qv != 0.0 && ek > 0.0 && tv_ > 0u) ? ilogb_bits(qv) + 1 + er : -100000;
-#pragma unroll
-      for (int sh = 32; sh >= 1; sh >>= 1) e = max(e, __shfl_xor(e, sh, 64));
-      if (lane == 0) emx[wv][hh] = e;
+      qd[hh][c] = qv[hh];
+      const int e = (qv[hh] != 0.0 && ek > 0.0 && tv_ > 0u) ? ilogb_bits(qv[hh]) + 1 + er : -100000;
+      const int em = wave_max_i32(e);
+      if (lane == 0) emx[wv][hh] = em;
     }
     inc = wave_incl_scan_u32(tv_);
     if (lane == 63) wtot[wv] = inc;
+    // depth histogram of the wave, and this channel's rank among equal
+    // depths below it in the wave
+    uint64_t mine = 0ull;
+#pragma unroll
+    for (int v = 0; v <= 8; ++v) {
+      const uint64_t bv = __ballot(tv_ == (uint32_t)v);
+      if (tv_ == (uint32_t)v) mine = bv;
+      if (lane == v) dcnt[wv][v] = (uint32_t)__popcll(bv);
+    }
+    below = (uint32_t)__popcll(mine & ((1ull << lane) - 1ull));
   }
   __syncthreads();
   if (tid < kDim) {
@@ -485,17 +514,10 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     for (uint32_t p = 0; p < tv_; ++p) s2c[o + p] = (uint8_t)tid;
     // channel order by depth, deepest first (stable): the slabs then hold
     // channels of similar depth, and trailing depth-0 slabs are skipped
-    uint32_t rank = 0;
-    const uint32_t* t4 = reinterpret_cast<const uint32_t*>(tks);
-#pragma unroll 1
-    for (int k = 0; k < kDim / 4; ++k) {
-      const uint32_t w = t4[k];
+    uint32_t rank = below + (wv == 1 ? dcnt[0][tv_] : 0u);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t te = (w >> (8 * e)) & 0xFFu;
-        rank += (te > tv_) || (te == tv_ && 4 * k + e < tid);
-      }
-    }
+    for (int v = 1; v <= 8; ++v)
+      if ((uint32_t)v > tv_) rank += dcnt[0][v] + dcnt[1][v];
     cperm[rank] = (uint8_t)tid;
     kap[tid] = ldexp_pow2(-(int)tv_ - 1) + (tv_ > 0u ? 0.5 : 0.0);
   }
@@ -526,13 +548,8 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       v = *reinterpret_cast<const uint4*>(u.kplanes + ((int64_t)c * W + p) * u.ngk + gam0 + 4 * q4);
     return v;
   };
-  auto tile_ngp = [&](int tile) -> int {
-    const int64_t n = Tp / kGroup - (int64_t)tile * NG;
-    return (int)(n < 0 ? 0 : (n > NG ? NG : n));
-  };
   uint4 pre[PRE];
-  uint32_t pmeta[MPT];
-  auto load_ahead = [&](int tile) {
+  auto load_pieces = [&](int tile) {
     const int64_t gam0 = (int64_t)tile * NG;
     const int ngp = tile_ngp(tile);
 #pragma unroll
@@ -540,11 +557,10 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       const int idx = k * 256 + tid;
       pre[k] = idx < nq ? piece(idx, gam0, ngp) : make_uint4(0u, 0u, 0u, 0u);
     }
-#pragma unroll
-    for (int k = 0; k < MPT; ++k) {
-      const int i = k * 256 + tid, gl = i / kDim, c = i % kDim;
-      pmeta[k] = gl < ngp ? u.kmeta[(gam0 + gl) * kDim + c] : 0u;
-    }
+  };
+  auto load_ahead = [&](int tile) {
+    load_pieces(tile);
+    load_meta(tile);
   };
   auto store_ahead = [&](int tile) {
 #pragma unroll
@@ -563,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     for (int idx = PRE * 256 + tid; idx < nq; idx += 256)
       *reinterpret_cast<uint4*>(planes + idx * 4) = piece(idx, gam0, ngp);
   };
-  load_ahead(tile_begin);
+  load_pieces(tile_begin);  // the first tile's metadata is already in flight
   store_ahead(tile_begin);
   __syncthreads();
   // the register prefetch runs one tile ahead; it is issued right after the
