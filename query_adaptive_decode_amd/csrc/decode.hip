@@ -57,56 +57,26 @@ __device__ __forceinline__ void unplane8(const uint32_t (&w)[8], uint32_t sel, u
 // bisection on the 12-bit sign+exponent field, then an exact rank among the
 // candidates in the threshold's exponent class.
 // ---------------------------------------------------------------------------
-template <int GQA, int DT>
-__global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
-                                                  int W, float RK, uint8_t* tk) {
-  constexpr int esize = DT == 0 ? 2 : 4;
-  const int unit = blockIdx.x;
-  const int b = unit / G, g = unit - b * G;
-  constexpr int gqa = GQA;
-  const ReqRecord r = req_of(store, b);
-  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const int lane = threadIdx.x;
-  __shared__ uint64_t ck[2 * 64 * 8];
-  __shared__ uint32_t cc[2 * 64 * 8];
-
-  uint64_t key[2][8];
-  double wv[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = lane + 64 * k;
-    double qv[GQA];
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh)
-      qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * gqa + hh) * kDim + c);
-    const double ekc = u.ek[c];
-    double qsq = 0.0;
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
-    const double w = __dmul_rn(qsq, ekc);
-    wv[k] = w;
-#pragma unroll
-    for (int t = 1; t <= 8; ++t) {
-      const double gt = __dmul_rn(w, ldexp_pow2(-2 * t));
-      key[k][t - 1] = (t <= W && gt > 0.0) ? dbits(gt) : 0ull;
-    }
-  }
-  const uint32_t Bk = (uint32_t)floor((double)RK * (double)kDim);
-  // wave-wide counts are sums of ballot popcounts over the 16 candidate slots
-  uint32_t npos = 0;
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) npos += (uint32_t)__popcll(__ballot(key[k][t] != 0ull));
-
-  uint32_t sel[2] = {0u, 0u};
+// ChooseDepths for one unit's d_h = 128 key channels by one wave: lane l
+// holds channels l and l + 64 with weights wv[0], wv[1]; the W candidate
+// gains of a channel are w_c 4^-t, t = 1..W, and the B_K largest positive
+// ones are chosen, ties to the lowest channel (with strictly decreasing
+// per-item gains this is ChooseDepths' result, [ReadKV] App. E.2.1).
+// Returns the depths of the lane's two channels.  ck / cc: 1024-entry LDS
+// scratch for the rare exact-rank path.  Wave-level only (no block barrier).
+__device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, uint32_t Bk,
+                                                uint64_t* ck, uint32_t* cc, uint32_t (&sel)[2]) {
+  const int lane = __lane_id();
+  sel[0] = 0u;
+  sel[1] = 0u;
   // Fast path: every positive weight w_c has a normal exponent field E_c in
   // [2W + 1, 2046], so each gain w_c 4^-(t+1) is exact with field
   // E_c - 2t - 2 and mantissa M_c.  Gains then order by that field first;
   // the B_K-th largest lies in the highest field level L with
   //   count(L) = sum_c #{t < W : E_c - 2t - 2 >= L} >= B_K
-  // (bisection on L), and at that level each channel has at most one
-  // candidate, ranked by (M_c descending, c ascending).
+  // (bisection on L between the lowest and the highest candidate level),
+  // and at that level each channel has at most one candidate, ranked by
+  // (M_c descending, c ascending).
   int ec[2];
   uint64_t mc[2];
   uint32_t rk[2] = {0u, 0u};
@@ -131,8 +101,20 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
     return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
            (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
   };
-  if (fast && npos > Bk && Bk > 0) {
-    int lo_l = 1, hi_l = 2046;  // count(lo_l) >= Bk holds (all candidates are >= 1)
+  if (fast) {
+    const uint32_t nposf = (uint32_t)W * (uint32_t)(__popcll(__ballot(ec[0] >= 0)) +
+                                                    __popcll(__ballot(ec[1] >= 0)));
+    if (nposf <= Bk) {
+      sel[0] = ec[0] >= 0 ? (uint32_t)W : 0u;
+      sel[1] = ec[1] >= 0 ? (uint32_t)W : 0u;
+      return;
+    }
+    if (Bk == 0) return;
+    // candidate levels span [min E - 2W, max E - 2]
+    const int emax = wave_max_i32(max(ec[0], ec[1]));
+    const int lo0 = min(ec[0] >= 0 ? ec[0] : 4096, ec[1] >= 0 ? ec[1] : 4096);
+    const int emin = -wave_max_i32(-lo0);  // some channel is positive here
+    int lo_l = max(1, emin - 2 * W), hi_l = emax - 2;
     while (lo_l < hi_l) {
       const int mid = (lo_l + hi_l + 1) >> 1;
       if ((uint32_t)wave_isum(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
@@ -168,7 +150,26 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
 #pragma unroll
     for (int k = 0; k < 2; ++k)
       if (at[k] && rk[k] < rem) ++sel[k];
-  } else if (npos <= Bk) {
+    return;
+  }
+  // Exact path (some gain is subnormal or not finite): the 64-bit patterns
+  // of the fp64 gains themselves
+  uint64_t key[2][8];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+#pragma unroll
+    for (int t = 1; t <= 8; ++t) {
+      const double gt = __dmul_rn(wv[k], ldexp_pow2(-2 * t));
+      key[k][t - 1] = (t <= W && gt > 0.0) ? dbits(gt) : 0ull;
+    }
+  }
+  // wave-wide counts are sums of ballot popcounts over the 16 candidate slots
+  uint32_t npos = 0;
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+#pragma unroll
+    for (int t = 0; t < 8; ++t) npos += (uint32_t)__popcll(__ballot(key[k][t] != 0ull));
+  if (npos <= Bk) {
 #pragma unroll
     for (int k = 0; k < 2; ++k)
 #pragma unroll
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
             cc[pos] = (uint32_t)(lane + 64 * k);
             ++pos;
           }
-      __syncthreads();
+      wave_lds_fence();
       for (int k = 0; k < 2; ++k) {
         const uint32_t c = (uint32_t)(lane + 64 * k);
         for (int t = 0; t < 8; ++t) {
@@ -265,6 +266,35 @@ __global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const vo
       }
     }
   }
+}
+
+template <int GQA, int DT>
+__global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
+                                                  int W, float RK, uint8_t* tk) {
+  constexpr int esize = DT == 0 ? 2 : 4;
+  const int unit = blockIdx.x;
+  const int b = unit / G, g = unit - b * G;
+  const ReqRecord r = req_of(store, b);
+  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
+  const int lane = threadIdx.x;
+  __shared__ uint64_t ck[2 * 64 * 8];
+  __shared__ uint32_t cc[2 * 64 * 8];
+  double wv[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    double qv[GQA];
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh)
+      qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + c);
+    const double ekc = u.ek[c];
+    double qsq = 0.0;
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
+    wv[k] = __dmul_rn(qsq, ekc);
+  }
+  uint32_t sel[2];
+  key_depths_wave(wv, W, (uint32_t)floor((double)RK * (double)kDim), ck, cc, sel);
   tk[(int64_t)unit * kDim + lane] = (uint8_t)sel[0];
   tk[(int64_t)unit * kDim + lane + 64] = (uint8_t)sel[1];
 }
@@ -358,11 +388,6 @@ __device__ __forceinline__ int ilogb_bits(double v) {  // exponent of |v| (subno
   return (int)((dbits(v) >> 52) & 0x7FFu) - 1023;
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, not for its outstanding global loads (a full __syncthreads()
 // would also drain the prefetch of the next tile).
@@ -415,9 +440,10 @@ __device__ __forceinline__ double half_sum(double v) {
 }
 
 template <int GQA, int DT>
-__global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const void* q, const uint8_t* tk,
-                                                  int H, int G, int W, int64_t capmax, int ntile_ws,
-                                                  double* ebuf, _Float16* e16, double* tilepart) {
+__global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const void* q, uint8_t* tk,
+                                                  int H, int G, int W, float RK, int64_t capmax,
+                                                  int ntile_ws, double* ebuf, _Float16* e16,
+                                                  double* tilepart) {
   constexpr int esize = DT == 0 ? 2 : 4;
   constexpr int NG = kTile / kGroup;  // 16 groups; wave w owns groups 4w .. 4w + 3
   constexpr int NHQ = (GQA + 3) / 4;  // head quads: two MFMA row blocks each
@@ -451,7 +477,11 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   // this block's share of the unit's tiles: an even split over gridDim.y
   const int tile_begin = (int)(((int64_t)blockIdx.y * ntl) / gridDim.y);
   const int tile_end = (int)(((int64_t)(blockIdx.y + 1) * ntl) / gridDim.y);
-  if (tile_begin >= tile_end) return;
+  if (tile_begin >= tile_end) {
+    // an empty request has no closed group (E^K = 0): all key depths are 0
+    if (ntl == 0 && blockIdx.y == 0 && threadIdx.x < kDim) tk[((int64_t)b * G + g) * kDim + threadIdx.x] = 0;
+    return;
+  }
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -473,22 +503,50 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   load_meta(tile_begin);  // independent of the depths: in flight during the setup
 
   // ---- once per block: depths, query, per-head digit scale, slot table ----
-  uint32_t tv_ = 0, inc = 0, below = 0;
+  // key allocation of the unit (every block of the unit computes it; the
+  // first writes it out): w_c = (sum_h q_hc^2) E^K_c in head order, then
+  // ChooseDepths over the channels by wave 0
+  double ek = 0.0;
   if (tid < kDim) {
     const int c = tid;
-    tv_ = tk[((int64_t)b * G + g) * kDim + c];
     double qv[GQA];
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh)
       qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + c);
-    const double ek = u.ek[c];
-    tks[c] = (uint8_t)tv_;
+    ek = u.ek[c];
+    double qsq = 0.0;
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      qd[hh][c] = qv[hh];
+      qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
+    }
+    kap[c] = __dmul_rn(qsq, ek);  // the key weight, until kap is set below
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const double w2[2] = {kap[lane], kap[lane + 64]};
+    uint32_t sel[2];
+    key_depths_wave(w2, W, (uint32_t)floor((double)RK * (double)kDim),
+                    reinterpret_cast<uint64_t*>(planes),
+                    reinterpret_cast<uint32_t*>(planes) + 2 * 2 * 64 * 8, sel);
+    tks[lane] = (uint8_t)sel[0];
+    tks[lane + 64] = (uint8_t)sel[1];
+    if (tile_begin == 0) {  // the unit's first non-empty run writes the depths out
+      tk[((int64_t)b * G + g) * kDim + lane] = (uint8_t)sel[0];
+      tk[((int64_t)b * G + g) * kDim + lane + 64] = (uint8_t)sel[1];
+    }
+  }
+  __syncthreads();
+  uint32_t tv_ = 0, inc = 0, below = 0;
+  if (tid < kDim) {
+    const int c = tid;
+    tv_ = tks[c];
     // 2^er >= sqrt(E_c) >= every closed group's rng_c
     const int er = ek > 0.0 ? ((ilogb_bits(ek) + 2) >> 1) : 0;
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
-      qd[hh][c] = qv[hh];
-      const int e = (qv[hh] != 0.0 && ek > 0.0 && tv_ > 0u) ? ilogb_bits(qv[hh]) + 1 + er : -100000;
+      const double qv = qd[hh][c];
+      const int e = (qv != 0.0 && ek > 0.0 && tv_ > 0u) ? ilogb_bits(qv) + 1 + er : -100000;
       const int em = wave_max_i32(e);
       if (lane == 0) emx[wv][hh] = em;
     }
@@ -1366,8 +1424,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   const int esize = DT == 0 ? 2 : 4;
 
   mark(a, 0, st);
-  hipLaunchKernelGGL((k_key_alloc<GQA, DT>), dim3(a.B * a.G), dim3(64), 0, st, (const uint8_t*)a.store,
-                     a.q, a.H, a.G, a.W, a.RK, tk);
+  // (the key allocation runs inside the score kernel)
   mark(a, 1, st);
   // slots staged per score tile: at most min(B_K, 128 W) chosen key lines,
   // 64 B each
@@ -1377,6 +1434,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   // (+8 slots: un-plane reads of a batch may run past a shallower channel's
   // last slot; those words are masked)
   size_t dyn = ((size_t)bk + 8) * 64;
+  if (dyn < (size_t)(2 * 64 * 8) * 12) dyn = (size_t)(2 * 64 * 8) * 12;  // key-allocation scratch
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GQA, DT>),
@@ -1391,7 +1449,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   if (run < 1) run = 1;
   const int nrun = (L.ntile + run - 1) / run;
   hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), dyn, st,
-                     (const uint8_t*)a.store, a.q, (const uint8_t*)tk, a.H, a.G, a.W, a.capmax,
+                     (const uint8_t*)a.store, a.q, tk, a.H, a.G, a.W, a.RK, a.capmax,
                      L.ntile, (double*)(ws + L.ebuf), (_Float16*)(ws + L.e16),
                      (double*)(ws + L.tilepart));
   mark(a, 2, st);

@@ -112,6 +112,12 @@ __device__ __forceinline__ T group_sum(T v) {
   return v;
 }
 
+// orders this wave's LDS accesses before and after it (no block barrier)
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // integer max over the wave, every lane gets it
 __device__ __forceinline__ int wave_max_i32(int v) {
   v = max(v, (int)dpp_u32<kDppQuadXor1>((uint32_t)v));
