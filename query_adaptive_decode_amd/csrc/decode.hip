@@ -93,14 +93,6 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
     const int d = ec[k] - 2 - lvl;
     return d < 0 ? 0 : min(d / 2 + 1, W);
   };
-  auto wave_isum = [](int v) -> int {  // DPP row sums, then the four rows
-    v += (int)dpp_u32<kDppQuadXor1>((uint32_t)v);
-    v += (int)dpp_u32<kDppQuadXor2>((uint32_t)v);
-    v += (int)dpp_u32<kDppRowHalfMirror>((uint32_t)v);
-    v += (int)dpp_u32<kDppRowMirror>((uint32_t)v);
-    return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
-           (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
-  };
   if (fast) {
     const uint32_t nposf = (uint32_t)W * (uint32_t)(__popcll(__ballot(ec[0] >= 0)) +
                                                     __popcll(__ballot(ec[1] >= 0)));
@@ -117,11 +109,11 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
     int lo_l = max(1, emin - 2 * W), hi_l = emax - 2;
     while (lo_l < hi_l) {
       const int mid = (lo_l + hi_l + 1) >> 1;
-      if ((uint32_t)wave_isum(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
+      if ((uint32_t)wave_sum_i32(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
       else hi_l = mid - 1;
     }
     const int Ls = lo_l;
-    const uint32_t above = (uint32_t)wave_isum(cnt_ge(0, Ls + 1) + cnt_ge(1, Ls + 1));
+    const uint32_t above = (uint32_t)wave_sum_i32(cnt_ge(0, Ls + 1) + cnt_ge(1, Ls + 1));
     const uint32_t rem = Bk - above;  // >= 1
     bool at[2];
 #pragma unroll
@@ -442,7 +434,7 @@ __device__ __forceinline__ double half_sum(double v) {
 template <int GQA, int DT>
 __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const void* q, uint8_t* tk,
                                                   int H, int G, int W, float RK, int64_t capmax,
-                                                  int ntile_ws, double* ebuf, _Float16* e16,
+                                                  int ntile_ws, float* ebuf, _Float16* e16,
                                                   double* tilepart) {
   constexpr int esize = DT == 0 ? 2 : 4;
   constexpr int NG = kTile / kGroup;  // 16 groups; wave w owns groups 4w .. 4w + 3
@@ -845,14 +837,14 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       const int hc = min(hh, GQA - 1);
       const double mt = fmax(fmax(redm[0][hc], redm[1][hc]), fmax(redm[2][hc], redm[3][hc]));
       const int64_t lane0 = ((int64_t)b * H + (int64_t)g * GQA + hc) * capmax + t0 + 128 * wv + (lane & 15);
-      double* const ep = ebuf + lane0;
+      float* const ep = ebuf + lane0;
       _Float16* const hp = e16 + lane0;
       double z = 0.0;
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb) {
         const double e = exp_nonpos(sv[tb][hq] - mt);
         if (sv[tb][hq] > -INFINITY) {
-          ep[16 * tb] = e;
+          ep[16 * tb] = (float)e;
           hp[16 * tb] = to_half(e);
           z += e;
         }
@@ -873,43 +865,42 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
 }
 
 // ---------------------------------------------------------------------------
-// Value allocation: one block of 1024 threads per (request, KV head); token
-// j is owned by thread j mod 1024 (coalesced reads).
+// Value allocation: one block of 1024 threads per (request, KV head).
 //   m_h = max_tile m_tile, Z_h = sum_tile z_tile exp(m_tile - m_h)
 //   f_{h,tile} = exp(m_tile - m_h) / Z_h         (alpha_hat = e * f)
 //   a_j = (sum_h alpha_hat_hj^2) * s_gamma(j)     (Eq. (3))
 // then ChooseDepths with B_V = floor(R_V * T_packed) over the (token, level)
-// gains a_j 4^-t, ties to the lowest token.  A token with a normal a_j
-// whose exponent field E exceeds 2W has its W gains at exponents E-2t with
-// a_j's mantissa; smaller ("tiny") ones are multiplied out.  Threshold
-// search: the exponent class E* of the B_V-th largest gain from an exponent
-// histogram (E* and the count above it), then 11/11/10/10/10-bit radix
-// passes over the mantissas of the candidates in class E*.
+// gains a_j 4^-t (t = 1..W), ties to the lowest token.
+// Token j = 2048 k + 128 w + 2 l + s belongs to lane l of wave w in round k
+// (s = 0, 1): the 128 tokens of a wave in one round lie in one tile, so the
+// per-tile factors are LDS broadcasts.
+// Threshold.  A token whose a_j is a normal double with exponent field
+// E > 2W ("regular") has its W gains at fields E - 2t, all with a_j's
+// mantissa, so it holds min(W, max(0, floor((E - L) / 2))) gains at field L
+// or above.  The field L* of the B_V-th largest gain comes from a bisection
+// over L with block-wide counts; other positive a_j (subnormal products,
+// infinities) have their products formed one by one.  Within field L* the
+// gains are ranked by mantissa with 11/11/10/10/10-bit radix passes, which
+// stop once the gains sharing the chosen digits are exactly the ones still
+// to be taken.
 // ---------------------------------------------------------------------------
 constexpr int kVNT = 1024;
-constexpr int kVPMAX = 16;  // tokens per thread held in registers
+constexpr int kVRound = 2 * kVNT;  // tokens per round
+constexpr int kVRMAX = 8;          // most rounds whose weights stay in registers
 
-// hist[bin] += 1 for every active lane, one LDS atomic per distinct bin of
-// the wave: a lane's peers with the same 11-bit bin are found by matching
-// the ballots of each bin bit; the lowest peer adds the peer count.
-__device__ __forceinline__ void agg_add(uint32_t* hist, uint32_t bin, bool act) {
-  uint64_t same = __ballot(act);
-#pragma unroll
-  for (int bit = 0; bit < 11; ++bit) {
-    const uint64_t ones = __ballot(act && ((bin >> bit) & 1u));
-    same &= ((bin >> bit) & 1u) ? ones : ~ones;
-  }
-  if (act && (same & ((1ull << __lane_id()) - 1ull)) == 0ull)
-    atomicAdd(&hist[bin & 2047u], (uint32_t)__popcll(same));
-}
-
-template <int GQA, bool REG>
+// RMAX > 0: the weights of RMAX rounds stay in registers (a capacity of at
+// most RMAX * kVRound tokens); RMAX == 0: they go through aval
+template <int GQA, int RMAX>
 __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int H, int G, int W,
                                                       int esize, float RV, int vscale,
                                                       int64_t capmax, int ntile_ws,
-                                                      const double* ebuf, const double* tilepart,
+                                                      const float* ebuf, const double* tilepart,
                                                       double* ftile, double* aval, uint8_t* tv) {
   constexpr int NT = kVNT;
+  constexpr int NW = NT / 64;
+  constexpr bool REG = RMAX > 0;
+  constexpr int kVTileMax = RMAX * kVRound / kTile;
+  static_assert(kTile % 128 == 0 && kVRound % kTile == 0, "a wave's tokens of one round lie in one tile");
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
@@ -918,107 +909,226 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
-  __shared__ uint32_t hA[2048];
-  __shared__ uint32_t hB[2048];
-  __shared__ uint32_t wsum[NT / 64 + 1];
-  __shared__ uint32_t sh[2];
+  __shared__ __align__(16) uint32_t hA[2048];
+  __shared__ __align__(16) uint32_t hB[2048];
+  __shared__ double fs[REG ? GQA * kVTileMax : 1];
+  __shared__ double evs[REG ? RMAX * kVRound / kGroup : 1];
+  __shared__ uint32_t wsum[NW + 1];
+  __shared__ uint32_t sh[3];
+
+  const int nr = (int)((Tp + kVRound - 1) / kVRound);
+  const float* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
+  double* fg = ftile + ((int64_t)b * H + (int64_t)g * GQA) * ntile_ws;
+  double* ab = aval + ((int64_t)b * G + g) * capmax;
+  uint8_t* tvb = tv + ((int64_t)b * G + g) * capmax;
+  const int jl = 128 * wv + 2 * lane;  // first token of the lane in round 0
+  auto tok0 = [&](int k) -> int64_t { return (int64_t)kVRound * k + jl; };
+  auto load_e = [&](int k, float2* e) __attribute__((always_inline)) {
+    const int64_t j0 = tok0(k);
+    const int64_t jc = j0 < Tp ? j0 : 0;  // Tp > 0 whenever a round exists
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh)
+      e[hh] = *reinterpret_cast<const float2*>(eb + (int64_t)hh * capmax + jc);
+  };
+  // register path: RB rounds of exponentials in flight at a time, the first
+  // batch already during the softmax statistics; rounds past the tokens
+  // load clamped addresses (no branches, so nothing waits on a merge of
+  // paths) and come out as zero weights
+  constexpr int RB0 = GQA >= 8 ? 2 : (GQA >= 4 ? 4 : 8);
+  constexpr int RB = REG ? (RB0 < RMAX ? RB0 : RMAX) : 1;
+  // loads first, in the order they are used, all unconditional (clamped
+  // addresses): this wave's tile partials (waves past GQA read the last
+  // head's and drop them), one group scale per thread, the exponentials
+  const double* tp = tilepart + ((int64_t)b * H + (int64_t)g * GQA + min(wv, GQA - 1)) * ntile_ws * 2;
+  const double2 p0 = *reinterpret_cast<const double2*>(tp + 2 * min(lane, max(ntile_b - 1, 0)));
+  const int ngrp = (int)(Tp / kGroup);
+  const double evr = REG ? u.ev[min(tid, max(ngrp - 1, 0))] : 0.0;
+  float2 e0[RB][GQA];
+  if constexpr (REG) {
+    if (nr > 0) {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) load_e(i, e0[i]);
+    }
+  }
 
   // ---- softmax statistics -> per-tile factors (wave h handles head h) ----
   if (wv < GQA) {
-    const int h = g * GQA + wv;
-    const double* tp = tilepart + ((int64_t)b * H + h) * ntile_ws * 2;
-    double m = -INFINITY;
-    for (int t = lane; t < ntile_b; t += 64) m = fmax(m, tp[2 * t]);
+    // the lane's first tile is in registers (all of them up to 64 tiles)
+    const double m0 = lane < ntile_b ? p0.x : -INFINITY, z0 = lane < ntile_b ? p0.y : 0.0;
+    double m = m0;
+    for (int t = lane + 64; t < ntile_b; t += 64) m = fmax(m, tp[2 * t]);
     m = wave_max(m);
-    double Z = 0.0;
-    for (int t = lane; t < ntile_b; t += 64) Z += tp[2 * t + 1] * exp(tp[2 * t] - m);
+    const double x0 = lane < ntile_b ? exp(m0 - m) : 0.0;
+    double Z = z0 * x0;
+    for (int t = lane + 64; t < ntile_b; t += 64) Z += tp[2 * t + 1] * exp(tp[2 * t] - m);
     Z = wave_sum(Z);
-    double* f = ftile + ((int64_t)b * H + h) * ntile_ws;
-    for (int t = lane; t < ntile_b; t += 64) f[t] = exp(tp[2 * t] - m) / Z;
+    auto put_f = [&](int t, double f) {
+      fg[(int64_t)wv * ntile_ws + t] = f;
+      if constexpr (REG) fs[wv * kVTileMax + t] = f;
+    };
+    if (lane < ntile_b) put_f(lane, x0 / Z);
+    for (int t = lane + 64; t < ntile_b; t += 64) put_f(t, exp(tp[2 * t] - m) / Z);
   }
+  static_assert(!REG || RMAX * kVRound / kGroup <= NT, "one group scale per thread");
+  if constexpr (REG) {
+    if (tid < ngrp) evs[tid] = evr;
+  }
+  if (tid == 0) { sh[0] = 0u; sh[1] = 0u; sh[2] = 0u; }
   for (int i = tid; i < 2048; i += NT) { hA[i] = 0u; hB[i] = 0u; }
   __threadfence_block();
   __syncthreads();
 
   // ---- value weights ----
-  const int per = (int)((Tp + NT - 1) / NT);
-  // loop bound over owned-token rounds: a compile-time constant when the
-  // weights live in registers (so that the loops unroll and index them
-  // statically), the actual count otherwise
-  const int kmax = REG ? kVPMAX : per;
-  const double* fb = ftile + ((int64_t)b * H + (int64_t)g * GQA) * ntile_ws;
-  const double* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
-  double* ab = aval + ((int64_t)b * G + g) * capmax;
-  uint8_t* tvb = tv + ((int64_t)b * G + g) * capmax;
-  double areg[REG ? kVPMAX : 1];
+  // the lane's two weights of round k from its exponentials e[hh]
+  auto weights = [&](int k, const float2* e, double& a0, double& a1) __attribute__((always_inline)) {
+    const int64_t j0 = tok0(k);
+    const bool in = j0 < Tp;  // Tp is even: both tokens or neither
+    const int tl = in ? (kVRound / kTile) * k + (128 * wv) / kTile : 0;
+    double s0 = 0.0, s1 = 0.0;
 #pragma unroll
-  for (int k = 0; k < kmax; ++k) {
-    if (k >= per) break;
-    const int64_t j = tid + (int64_t)NT * k;
-    double a = 0.0;
-    if (j < Tp) {
-      const int tl = (int)(j / kTile);
-      double asq = 0.0;
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) {
-        const double al = __dmul_rn(eb[(int64_t)hh * capmax + j], fb[(int64_t)hh * ntile_ws + tl]);
-        asq = __dadd_rn(asq, __dmul_rn(al, al));
-      }
-      a = (vscale == 0) ? __dmul_rn(asq, u.ev[j / kGroup]) : asq;
+    for (int hh = 0; hh < GQA; ++hh) {
+      const double f = REG ? fs[hh * kVTileMax + tl] : fg[(int64_t)hh * ntile_ws + tl];
+      const double x0 = __dmul_rn((double)e[hh].x, f), x1 = __dmul_rn((double)e[hh].y, f);
+      s0 = __dadd_rn(s0, __dmul_rn(x0, x0));
+      s1 = __dadd_rn(s1, __dmul_rn(x1, x1));
     }
-    if constexpr (REG) areg[k] = a;
-    else if (j < Tp) ab[j] = a;
-  }
-  auto aof = [&](int k) -> double {
-    const int64_t j = tid + (int64_t)NT * k;
-    if (j >= Tp) return 0.0;
-    if constexpr (REG) return areg[k];
-    else return ab[j];
+    if (vscale == 0) {
+      const int64_t gi = in ? j0 / kGroup : 0;
+      const double sg = REG ? evs[gi] : u.ev[gi];
+      s0 = __dmul_rn(s0, sg);
+      s1 = __dmul_rn(s1, sg);
+    }
+    a0 = in ? s0 : 0.0;
+    a1 = in ? s1 : 0.0;
   };
 
-  const uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
+  // per token: exponent field when regular, else kNoField; tokens that are
+  // positive but not regular are "odd" (products formed one by one)
+  constexpr int kNoField = -8192;
   const int twoW = 2 * W;
-
-  // ---- exponent histogram: hA[E] regular tokens, hB[E] tiny tokens' gains ----
-  uint32_t npos_l = 0;
-#pragma unroll
-  for (int k = 0; k < kmax; ++k) {
-    if (k >= per) break;
-    const double a = aof(k);
-    const bool posv = a > 0.0;
+  double areg[REG ? RMAX : 1][2];
+  int freg[REG ? RMAX : 1][2];  // field_of(areg)
+  bool any_odd = false;
+  auto field_of = [&](double a) __attribute__((always_inline)) -> int {
     const int E = (int)(dbits(a) >> 52);
-    const bool reg = posv && E > twoW;
-    agg_add(hA, (uint32_t)E, reg);
-    if (reg) npos_l += W;
-    if (posv && !reg) {
-      for (int t = 1; t <= W; ++t) {
-        const uint64_t kk = dbits(__dmul_rn(a, ldexp_pow2(-2 * t)));
-        if (kk) { atomicAdd(&hB[(uint32_t)(kk >> 52)], 1u); ++npos_l; }
+    return (a > 0.0 && E > twoW && E < 2047) ? E : kNoField;
+  };
+  // field, odd flag and the exponent histogram hA[E] of regular tokens
+  auto classify = [&](double a) __attribute__((always_inline)) -> int {
+    const int ef = field_of(a);
+    any_odd |= a > 0.0 && ef == kNoField;
+    if (ef != kNoField) atomicAdd(&hA[ef], 1u);
+    return ef;
+  };
+  if constexpr (REG) {
+    if (nr > 0) {
+#pragma unroll
+      for (int k0 = 0; k0 < RMAX; k0 += RB) {
+        if (k0 >= nr) {  // uniform; a whole batch is skipped or run
+#pragma unroll
+          for (int i = 0; i < RB; ++i)
+            if (k0 + i < RMAX) {
+              areg[k0 + i][0] = areg[k0 + i][1] = 0.0;
+              freg[k0 + i][0] = freg[k0 + i][1] = kNoField;
+            }
+          continue;
+        }
+        float2 e[RB][GQA];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          if (k0 + i >= RMAX) break;
+          if (k0 == 0) {
+#pragma unroll
+            for (int hh = 0; hh < GQA; ++hh) e[i][hh] = e0[i][hh];
+          } else {
+            load_e(k0 + i, e[i]);
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+          const int k = k0 + i;
+          if (k >= RMAX) break;
+          weights(k, e[i], areg[k][0], areg[k][1]);
+          freg[k][0] = classify(areg[k][0]);
+          freg[k][1] = classify(areg[k][1]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < RMAX; ++k) {
+        areg[k][0] = areg[k][1] = 0.0;
+        freg[k][0] = freg[k][1] = kNoField;
       }
     }
+  } else {
+    for (int k = 0; k < nr; ++k) {
+      float2 e[GQA];
+      load_e(k, e);
+      double a0, a1;
+      weights(k, e, a0, a1);
+      classify(a0);
+      classify(a1);
+      const int64_t j0 = tok0(k);
+      if (j0 < Tp) { ab[j0] = a0; ab[j0 + 1] = a1; }
+    }
   }
-  block_excl_scan<NT>(npos_l, wsum);
-  const uint32_t npos = wsum[NT / 64];
+  // visit every owned token: fn(a, field, round, s)
+  auto for_tokens = [&](auto&& fn) __attribute__((always_inline)) {
+    if constexpr (REG) {
+#pragma unroll
+      for (int k = 0; k < RMAX; ++k) {
+        if (k >= nr) break;
+        fn(areg[k][0], freg[k][0], k, 0);
+        fn(areg[k][1], freg[k][1], k, 1);
+      }
+    } else {
+      for (int k = 0; k < nr; ++k) {
+        const int64_t j0 = tok0(k);
+        const double a0 = j0 < Tp ? ab[j0] : 0.0, a1 = j0 < Tp ? ab[j0 + 1] : 0.0;
+        fn(a0, field_of(a0), k, 0);
+        fn(a1, field_of(a1), k, 1);
+      }
+    }
+  };
+  auto is_odd = [&](double a, int ef) { return a > 0.0 && ef == kNoField; };
+  auto gain_bits = [&](double a, int t) { return dbits(__dmul_rn(a, ldexp_pow2(-2 * t))); };
+
+  // ---- gain-field histogram: hA[E] regular tokens (filled with the
+  // weights), hB[f] odd products ----
+  if (any_odd) {
+    for_tokens([&](double a, int ef, int, int) {
+      if (is_odd(a, ef))
+        for (int t = 1; t <= W; ++t) {
+          const uint64_t kk = gain_bits(a, t);
+          if (kk) atomicAdd(&hB[(uint32_t)(kk >> 52)], 1u);
+        }
+    });
+  }
   __syncthreads();
-  // hB[E] += sum_t hA[E + 2t]: the gain-exponent histogram of all candidates
-  for (int E = tid; E < 2048; E += NT) {
-    uint32_t s = hB[E];
-    for (int t = 1; t <= W; ++t)
-      if (E + 2 * t < 2048) s += hA[E + 2 * t];
-    hB[E] = s;
+  // hB[f] += sum_t hA[f + 2t]: the number of gains at field f (W <= 8)
+  for (int f = tid; f < 2048; f += NT) {
+    uint32_t c = hB[f];
+#pragma unroll
+    for (int t = 1; t <= 8; ++t) {
+      const uint32_t v = hA[min(f + 2 * t, 2047)];
+      c += (t <= W && f + 2 * t < 2048) ? v : 0u;
+    }
+    hB[f] = c;
   }
   __syncthreads();
 
+  const uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
+  if (tid < 64) wave_find_digit<2048>(hB, Bv > 0u ? Bv : 1u, &sh[0], &sh[1], &sh[2]);
+  __syncthreads();
+  const uint32_t npos = sh[2];
   const bool all_pos = npos <= Bv;
   int Es = -1;
   uint64_t prefix = 0, mask = 0;  // over the 52 mantissa bits
   uint32_t rem = 0, n_eq = 0;
   if (!all_pos && Bv > 0) {
-    if (tid < 64) wave_find_digit<2048>(hB, Bv, &sh[0], &sh[1]);
-    __syncthreads();
     Es = (int)sh[0];
-    rem = Bv - sh[1];
-    n_eq = hB[Es];
+    rem = Bv - sh[1];  // >= 1
+    n_eq = hB[Es];     // >= rem
     __syncthreads();
     // digits of the 52 mantissa bits: 11, 11, 10, 10, 10 (MSB first)
     for (int pass = 0; pass < 5 && n_eq != rem; ++pass) {
@@ -1027,27 +1137,24 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
       const uint32_t dmask = (1u << width) - 1u;
       for (int i = tid; i < 2048; i += NT) hA[i] = 0u;
       __syncthreads();
-#pragma unroll
-      for (int k = 0; k < kmax; ++k) {
-        if (k >= per) break;
-        const double a = aof(k);
-        if (!(a > 0.0)) continue;
-        const uint64_t ab_ = dbits(a);
-        const int E = (int)(ab_ >> 52);
-        if (E > twoW) {
-          const int d = E - Es;
-          if (d >= 2 && d <= twoW && !(d & 1)) {
-            const uint64_t mnt = ab_ & 0x000FFFFFFFFFFFFFull;
-            if ((mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
-          }
-        } else {
-          for (int t = 1; t <= W; ++t) {
-            const uint64_t kk = dbits(__dmul_rn(a, ldexp_pow2(-2 * t)));
-            if (kk && (int)(kk >> 52) == Es) {
-              const uint64_t mnt = kk & 0x000FFFFFFFFFFFFFull;
-              if ((mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
-            }
-          }
+      {
+        for_tokens([&](double a, int ef, int, int) __attribute__((always_inline)) {
+          const int d = ef - Es;
+          const bool c = d >= 2 && d <= twoW && !(d & 1);
+          const uint64_t mnt = dbits(a) & 0x000FFFFFFFFFFFFFull;
+          if (c && (mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
+        });
+        if (any_odd) {
+          for_tokens([&](double a, int ef, int, int) {
+            if (is_odd(a, ef))
+              for (int t = 1; t <= W; ++t) {
+                const uint64_t kk = gain_bits(a, t);
+                if (kk && (int)(kk >> 52) == Es) {
+                  const uint64_t mnt = kk & 0x000FFFFFFFFFFFFFull;
+                  if ((mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
+                }
+              }
+          });
         }
       }
       __syncthreads();
@@ -1067,32 +1174,26 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
 
   // ---- depths: levels above the threshold, plus ties in token order ----
   // returns (levels above the threshold) | (levels equal to it) << 16
-  auto count_levels = [&](double a) -> uint32_t {
-    uint32_t above = 0, tie = 0;
-    if (!(a > 0.0)) return 0u;
-    const uint64_t ab_ = dbits(a);
-    const int E = (int)(ab_ >> 52);
+  auto count_levels = [&](double a, int ef) __attribute__((always_inline)) -> uint32_t {
+    if (!(a > 0.0) || Bv == 0) return 0u;
     if (all_pos) {
-      if (E > twoW) above = (uint32_t)W;
-      else
-        for (int t = 1; t <= W; ++t) above += dbits(__dmul_rn(a, ldexp_pow2(-2 * t))) != 0ull;
-      return above;
+      if (ef != kNoField) return (uint32_t)W;
+      uint32_t n = 0;
+      for (int t = 1; t <= W; ++t) n += gain_bits(a, t) != 0ull;
+      return n;
     }
-    if (Bv == 0) return 0u;
-    if (E > twoW) {
-      const int d = E - Es;
-      if (d > 0) {
-        int n = (d - 1) >> 1;
-        above = (uint32_t)(n > W ? W : n);
-      }
+    uint32_t above = 0, tie = 0;
+    if (ef != kNoField) {
+      const int d = ef - Es;
+      above = (uint32_t)min(max((d - 1) >> 1, 0), W);
       if (d >= 2 && d <= twoW && !(d & 1)) {
-        const uint64_t mnt = (ab_ & 0x000FFFFFFFFFFFFFull) & mask;
+        const uint64_t mnt = (dbits(a) & 0x000FFFFFFFFFFFFFull) & mask;
         if (mnt > prefix) ++above;
         else if (mnt == prefix) ++tie;
       }
     } else {
       for (int t = 1; t <= W; ++t) {
-        const uint64_t kk = dbits(__dmul_rn(a, ldexp_pow2(-2 * t)));
+        const uint64_t kk = gain_bits(a, t);
         if (!kk) continue;
         const int e = (int)(kk >> 52);
         if (e > Es) ++above;
@@ -1106,24 +1207,28 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
     return above | (tie << 16);
   };
   const bool rank_ties = !all_pos && Bv > 0 && rem < n_eq;
-  uint32_t running = 0;  // ties in earlier rounds (token order = round, thread)
-#pragma unroll
-  for (int k = 0; k < kmax; ++k) {
-    if (k >= per) break;
-    const int64_t j = tid + (int64_t)NT * k;
-    const uint32_t lv = count_levels(aof(k));
-    uint32_t above = lv & 0xFFFFu;
-    const uint32_t tie = lv >> 16;
+  uint32_t running = 0;  // ties in earlier rounds (token order = round, thread, s)
+  uint32_t lv0 = 0;
+  for_tokens([&](double a, int ef, int k, int s) __attribute__((always_inline)) {
+    const uint32_t lv = count_levels(a, ef);
+    if (s == 0) { lv0 = lv; return; }
+    uint32_t above0 = lv0 & 0xFFFFu, above1 = lv & 0xFFFFu;
+    const uint32_t tie0 = lv0 >> 16, tie1 = lv >> 16;
     if (rank_ties) {
-      const uint32_t before = block_excl_scan<NT>(tie, wsum) + running;
-      running += wsum[NT / 64];
-      __syncthreads();
-      if (tie && before < rem) ++above;
+      const uint32_t before = block_excl_scan<NT>(tie0 + tie1, wsum) + running;
+      running += wsum[NW];
+      if (tie0 && before < rem) ++above0;
+      if (tie1 && before + tie0 < rem) ++above1;
     } else {
-      above += tie;
+      above0 += tie0;
+      above1 += tie1;
     }
-    if (j < Tp) tvb[j] = (uint8_t)above;
-  }
+    const int64_t j0 = tok0(k);
+    if (j0 < Tp) {
+      tvb[j0] = (uint8_t)above0;
+      tvb[j0 + 1] = (uint8_t)above1;
+    }
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -1450,19 +1555,19 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   const int nrun = (L.ntile + run - 1) / run;
   hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), dyn, st,
                      (const uint8_t*)a.store, a.q, tk, a.H, a.G, a.W, a.RK, a.capmax,
-                     L.ntile, (double*)(ws + L.ebuf), (_Float16*)(ws + L.e16),
+                     L.ntile, (float*)(ws + L.ebuf), (_Float16*)(ws + L.e16),
                      (double*)(ws + L.tilepart));
   mark(a, 2, st);
-  if (a.capmax <= (int64_t)kVNT * kVPMAX)
-    hipLaunchKernelGGL((k_value_alloc<GQA, true>), dim3(a.B * a.G), dim3(kVNT), 0, st,
-                       (const uint8_t*)a.store, a.H, a.G, a.W, esize, a.RV, a.vscale, a.capmax,
-                       L.ntile, (const double*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
+  {
+    auto va = &k_value_alloc<GQA, 0>;
+    if (a.capmax <= (int64_t)kVRound * 4) va = &k_value_alloc<GQA, 4>;
+    else if (a.capmax <= (int64_t)kVRound * 5) va = &k_value_alloc<GQA, 5>;
+    else if (a.capmax <= (int64_t)kVRound * kVRMAX) va = &k_value_alloc<GQA, kVRMAX>;
+    hipLaunchKernelGGL(va, dim3(a.B * a.G), dim3(kVNT), 0, st, (const uint8_t*)a.store, a.H, a.G,
+                       a.W, esize, a.RV, a.vscale, a.capmax, L.ntile,
+                       (const float*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
                        (double*)(ws + L.ftile), (double*)(ws + L.aval), tv);
-  else
-    hipLaunchKernelGGL((k_value_alloc<GQA, false>), dim3(a.B * a.G), dim3(kVNT), 0, st,
-                       (const uint8_t*)a.store, a.H, a.G, a.W, esize, a.RV, a.vscale, a.capmax,
-                       L.ntile, (const double*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
-                       (double*)(ws + L.ftile), (double*)(ws + L.aval), tv);
+  }
   mark(a, 3, st);
   {
     // runs of consecutive chunks per block: about four blocks per compute

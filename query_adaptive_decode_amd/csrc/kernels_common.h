@@ -128,6 +128,16 @@ __device__ __forceinline__ int wave_max_i32(int v) {
              max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 
+// integer sum over the wave, every lane gets it
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += (int)dpp_u32<kDppQuadXor1>((uint32_t)v);
+  v += (int)dpp_u32<kDppQuadXor2>((uint32_t)v);
+  v += (int)dpp_u32<kDppRowHalfMirror>((uint32_t)v);
+  v += (int)dpp_u32<kDppRowMirror>((uint32_t)v);
+  return (__builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16)) +
+         (__builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48));
+}
+
 // sum / max over the wave (rows combined in fixed order 0,1,2,3)
 __device__ __forceinline__ double wave_sum(double v) {
   v = row_reduce(v, [](double a, double b) { return a + b; });

@@ -118,7 +118,7 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 // Decode workspace (one call).  capmax = largest request capacity.
 //   tk     u8  [B][G][d]          key depths
 //   tv     u8  [B][G][capmax]     value depths
-//   ebuf   f64 [B][H][capmax]     exp(s - m_tile) per token (tile = kTile)
+//   ebuf   f32 [B][H][capmax]     exp(s - m_tile) per token (tile = kTile)
 //   e16    f16 [B][H][capmax]     the same rounded to fp16 (value gather)
 //   tilepart f64 [B][H][ntile][2] (m_tile, sum of exp) per tile
 //   ftile  f64 [B][H][ntile]      exp(m_tile - m) / Z
@@ -138,7 +138,7 @@ RKV_HD WsLayout ws_layout(int B, int H, int G, int d, int64_t capmax) {
   int64_t off = 0;
   L.tk = off; off = align_up(off + (int64_t)B * G * d, 256);
   L.tv = off; off = align_up(off + (int64_t)B * G * capmax, 256);
-  L.ebuf = off; off = align_up(off + (int64_t)B * H * capmax * 8, 256);
+  L.ebuf = off; off = align_up(off + (int64_t)B * H * capmax * 4, 256);
   L.e16 = off; off = align_up(off + (int64_t)B * H * capmax * 2, 256);
   L.tilepart = off; off = align_up(off + (int64_t)B * H * L.ntile * 16, 256);
   L.ftile = off; off = align_up(off + (int64_t)B * H * L.ntile * 8, 256);

@@ -39,31 +39,40 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
   return v;
 }
 
-// Wave 0 of the block scans NB bins (LDS) from the highest digit down and
-// finds the digit where the cumulative count reaches `rem`.  Requires the
-// total count >= rem >= 1.  Writes digit and count strictly above it.
+// One wave scans NB bins (LDS) from the highest digit down and finds the
+// digit where the cumulative count reaches `rem` (>= 1): writes the digit
+// and the count strictly above it.  If the bins hold fewer than `rem` in
+// all, nothing is written.  `out_total` (may be null) gets the sum of all
+// bins.  Each lane reads PER consecutive bins with 16-byte LDS reads.
 template <int NB>
 __device__ __forceinline__ void wave_find_digit(const uint32_t* hist, uint32_t rem, uint32_t* out_digit,
-                                                uint32_t* out_above) {
+                                                uint32_t* out_above, uint32_t* out_total = nullptr) {
   constexpr int PER = NB / 64;
+  static_assert(PER % 4 == 0, "whole 16-byte reads per lane");
   const int l = __lane_id();
-  uint32_t h[PER];
+  const int base = NB - (l + 1) * PER;  // lane l holds bins base .. base + PER - 1
+  uint32_t h[PER];                      // h[i] = bin base + PER - 1 - i (descending)
   uint32_t tot = 0;
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    h[i] = hist[NB - 1 - (l * PER + i)];
-    tot += h[i];
+  for (int i = 0; i < PER / 4; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + base + 4 * i);
+    h[PER - 1 - 4 * i] = v.x;
+    h[PER - 2 - 4 * i] = v.y;
+    h[PER - 3 - 4 * i] = v.z;
+    h[PER - 4 - 4 * i] = v.w;
+    tot += (v.x + v.y) + (v.z + v.w);
   }
   const uint32_t incl = wave_incl_scan_u32(tot);
   const uint32_t excl = incl - tot;
+  if (out_total && l == 63) *out_total = incl;
   const uint64_t bal = __ballot(incl >= rem);
-  const int L = __ffsll((unsigned long long)bal) - 1;
+  const int L = bal ? __ffsll((unsigned long long)bal) - 1 : -1;
   if (l == L) {
     uint32_t c = excl;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (c + h[i] >= rem) {
-        *out_digit = (uint32_t)(NB - 1 - (l * PER + i));
+        *out_digit = (uint32_t)(base + PER - 1 - i);
         *out_above = c;
         break;
       }
