@@ -890,6 +890,59 @@ constexpr int kVRMAX = 8;          // most rounds whose weights stay in register
 
 // RMAX > 0: the weights of RMAX rounds stay in registers (a capacity of at
 // most RMAX * kVRound tokens); RMAX == 0: they go through aval
+// One wave: the gain-field histogram G[f] = hB[f] + sum_{t=1..W} hA[f + 2t]
+// (hA counts regular tokens by exponent field, hB odd products by field;
+// W <= 8) is formed in registers and scanned from the top field down for
+// the field where the count reaches rem (>= 1).  out[0] = field, out[1] =
+// count above it, out[2] = G[field] (all three only if the total reaches
+// rem), out[3] = total count.
+__device__ __forceinline__ void wave_find_gain_field(const uint32_t* hA, const uint32_t* hB, int W,
+                                                     uint32_t rem, uint32_t* out) {
+  constexpr int PER = 32;
+  const int l = __lane_id();
+  const int base = 2048 - (l + 1) * PER;  // lane l: fields base .. base + 31
+  uint32_t w[PER + 16];                   // hA[base .. base + 47], 0 past the end
+#pragma unroll
+  for (int i = 0; i < (PER + 16) / 4; ++i) {
+    const int idx = base + 4 * i;
+    uint4 v = *reinterpret_cast<const uint4*>(hA + min(idx, 2044));
+    if (idx >= 2048) v = make_uint4(0u, 0u, 0u, 0u);
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  uint32_t G[PER];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hB + base + 4 * i);
+    G[4 * i] = v.x; G[4 * i + 1] = v.y; G[4 * i + 2] = v.z; G[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int t = 1; t <= 8; ++t) {
+    if (t > W) break;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) G[i] += w[i + 2 * t];
+  }
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) tot += G[i];
+  const uint32_t incl = wave_incl_scan_u32(tot);
+  if (l == 63) out[3] = incl;
+  const uint64_t bal = __ballot(incl >= rem);
+  const int L = bal ? __ffsll((unsigned long long)bal) - 1 : -1;
+  if (l == L) {
+    uint32_t c = incl - tot;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (c + G[i] >= rem) {
+        out[0] = (uint32_t)(base + i);
+        out[1] = c;
+        out[2] = G[i];
+        break;
+      }
+      c += G[i];
+    }
+  }
+}
+
 template <int GQA, int RMAX>
 __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int H, int G, int W,
                                                       int esize, float RV, int vscale,
@@ -911,10 +964,11 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
 
   __shared__ __align__(16) uint32_t hA[2048];
   __shared__ __align__(16) uint32_t hB[2048];
+  __shared__ __align__(16) uint32_t hC[2048];
   __shared__ double fs[REG ? GQA * kVTileMax : 1];
   __shared__ double evs[REG ? RMAX * kVRound / kGroup : 1];
   __shared__ uint32_t wsum[NW + 1];
-  __shared__ uint32_t sh[3];
+  __shared__ uint32_t sh[4];
 
   const int nr = (int)((Tp + kVRound - 1) / kVRound);
   const float* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
@@ -934,7 +988,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   // batch already during the softmax statistics; rounds past the tokens
   // load clamped addresses (no branches, so nothing waits on a merge of
   // paths) and come out as zero weights
-  constexpr int RB0 = GQA >= 8 ? 2 : (GQA >= 4 ? 4 : 8);
+  constexpr int RB0 = RMAX * GQA <= 20 ? RMAX : (GQA >= 8 ? 2 : (GQA >= 4 ? 4 : 8));
   constexpr int RB = REG ? (RB0 < RMAX ? RB0 : RMAX) : 1;
   // loads first, in the order they are used, all unconditional (clamped
   // addresses): this wave's tile partials (waves past GQA read the last
@@ -973,10 +1027,14 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   if constexpr (REG) {
     if (tid < ngrp) evs[tid] = evr;
   }
-  if (tid == 0) { sh[0] = 0u; sh[1] = 0u; sh[2] = 0u; }
-  for (int i = tid; i < 2048; i += NT) { hA[i] = 0u; hB[i] = 0u; }
-  __threadfence_block();
-  __syncthreads();
+  if (tid == 0) { sh[0] = 0u; sh[1] = 0u; sh[2] = 0u; sh[3] = 0u; }
+  for (int i = tid; i < 2048; i += NT) { hA[i] = 0u; hB[i] = 0u; hC[i] = 0u; }
+  if constexpr (REG) {
+    lds_barrier();  // the exponentials stay in flight
+  } else {
+    __threadfence_block();  // ftile is read back through memory
+    __syncthreads();
+  }
 
   // ---- value weights ----
   // the lane's two weights of round k from its exponentials e[hh]
@@ -1105,22 +1163,11 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
     });
   }
   __syncthreads();
-  // hB[f] += sum_t hA[f + 2t]: the number of gains at field f (W <= 8)
-  for (int f = tid; f < 2048; f += NT) {
-    uint32_t c = hB[f];
-#pragma unroll
-    for (int t = 1; t <= 8; ++t) {
-      const uint32_t v = hA[min(f + 2 * t, 2047)];
-      c += (t <= W && f + 2 * t < 2048) ? v : 0u;
-    }
-    hB[f] = c;
-  }
-  __syncthreads();
 
   const uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
-  if (tid < 64) wave_find_digit<2048>(hB, Bv > 0u ? Bv : 1u, &sh[0], &sh[1], &sh[2]);
+  if (tid < 64) wave_find_gain_field(hA, hB, W, Bv > 0u ? Bv : 1u, sh);
   __syncthreads();
-  const uint32_t npos = sh[2];
+  const uint32_t npos = sh[3];
   const bool all_pos = npos <= Bv;
   int Es = -1;
   uint64_t prefix = 0, mask = 0;  // over the 52 mantissa bits
@@ -1128,21 +1175,25 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   if (!all_pos && Bv > 0) {
     Es = (int)sh[0];
     rem = Bv - sh[1];  // >= 1
-    n_eq = hB[Es];     // >= rem
-    __syncthreads();
+    n_eq = sh[2];      // >= rem
     // digits of the 52 mantissa bits: 11, 11, 10, 10, 10 (MSB first)
     for (int pass = 0; pass < 5 && n_eq != rem; ++pass) {
       const int width = pass < 2 ? 11 : 10;
       const int shift = pass < 2 ? 41 - 11 * pass : 40 - 10 * pass;
       const uint32_t dmask = (1u << width) - 1u;
-      for (int i = tid; i < 2048; i += NT) hA[i] = 0u;
-      __syncthreads();
+      // the first pass counts into hC (cleared at the start), later ones
+      // into hA, cleared here
+      uint32_t* const hist = pass == 0 ? hC : hA;
+      if (pass > 0) {
+        for (int i = tid; i < 2048; i += NT) hA[i] = 0u;
+        __syncthreads();
+      }
       {
         for_tokens([&](double a, int ef, int, int) __attribute__((always_inline)) {
           const int d = ef - Es;
           const bool c = d >= 2 && d <= twoW && !(d & 1);
           const uint64_t mnt = dbits(a) & 0x000FFFFFFFFFFFFFull;
-          if (c && (mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
+          if (c && (mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
         });
         if (any_odd) {
           for_tokens([&](double a, int ef, int, int) {
@@ -1151,7 +1202,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
                 const uint64_t kk = gain_bits(a, t);
                 if (kk && (int)(kk >> 52) == Es) {
                   const uint64_t mnt = kk & 0x000FFFFFFFFFFFFFull;
-                  if ((mnt & mask) == prefix) atomicAdd(&hA[(uint32_t)(mnt >> shift) & dmask], 1u);
+                  if ((mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
                 }
               }
           });
@@ -1159,12 +1210,12 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
       }
       __syncthreads();
       if (tid < 64) {
-        if (width == 11) wave_find_digit<2048>(hA, rem, &sh[0], &sh[1]);
-        else wave_find_digit<1024>(hA, rem, &sh[0], &sh[1]);
+        if (width == 11) wave_find_digit<2048>(hist, rem, &sh[0], &sh[1]);
+        else wave_find_digit<1024>(hist, rem, &sh[0], &sh[1]);
       }
       __syncthreads();
       const uint32_t dg = sh[0];
-      n_eq = hA[dg];
+      n_eq = hist[dg];
       rem -= sh[1];
       prefix |= (uint64_t)dg << shift;
       mask |= (uint64_t)dmask << shift;
