@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
-KERNELS = ["key_alloc", "score", "value_alloc", "value_gather"]
+KERNELS = ["score", "value_alloc", "value_gather"]
 METRIC = "decode attn query-heads\u00b7ctx-tokens/s + achieved HBM GB/s vs peak, (W,R)=(8,4),(8,2)"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_step_llama3-8b-B16-T8192.txt")
 
@@ -117,7 +117,7 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, evict=True):
     # ---- per-kernel timing with HIP events on the launch stream ----
     h = _hip()
     stream = torch.cuda.current_stream().cuda_stream
-    ev = [_events(h, 5) for _ in range(steps)]
+    ev = [_events(h, len(KERNELS) + 1) for _ in range(steps)]
     eenc = [_events(h, 2) for _ in range(steps)]
     ksum = torch.zeros((), dtype=torch.int64, device="cuda")
     vsum = torch.zeros((), dtype=torch.int64, device="cuda")
@@ -166,8 +166,9 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, evict=True):
     kpay = float(ksum.item()) / steps * tpm / 8            # bytes per launch, all (b,g)
     vpay = float(vsum.item()) / steps * d / 8
     meta = B * G * ng * d * 4                              # one of K or V metadata
-    alg = {"score": kpay + meta, "value_gather": vpay + meta,
-           "key_alloc": B * G * d * 8 + B * H * d * 2, "value_alloc": B * G * ng * 8}
+    # the score launch also reads q and E^K for the key allocation in its prologue
+    alg = {"score": kpay + meta + B * G * d * 8 + B * H * d * 2, "value_gather": vpay + meta,
+           "value_alloc": B * G * ng * 8}
     step_bytes = kpay + vpay + 2 * meta
     return dict(R=R, ms_per_step=wall / steps * 1e3, qh_tok_per_s=qh_tok / wall,
                 evicted_ms_per_step=evict_ms,

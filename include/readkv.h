@@ -139,13 +139,14 @@ int readkv_decode_attn(const readkv_config* cfg, const void* store,
                        uint8_t* key_depths_out, uint8_t* value_depths_out,
                        void* stream);
 
-/* readkv_decode_attn with timing hooks: `events` points to 5 hipEvent_t
+/* readkv_decode_attn with timing hooks: `events` points to 4 hipEvent_t
  * handles created by the caller (as void*); events[0] is recorded on
- * `stream` before the first kernel and events[i] after kernel i of the
- * step, in the order key allocation, score (with the split-context softmax
- * partials), value allocation (with the softmax statistics), value gather
- * (with the output reduction).  Arguments and results are otherwise those
- * of readkv_decode_attn (EINVAL if events is NULL). */
+ * `stream` before the first kernel and events[i] after stage i of the
+ * step, in the order score (with the key allocation in its prologue and
+ * the split-context softmax partials), value allocation (with the softmax
+ * statistics), value gather (with the output reduction).  Arguments and
+ * results are otherwise those of readkv_decode_attn (EINVAL if events or
+ * any of the 4 handles is NULL). */
 int readkv_decode_attn_timed(const readkv_config* cfg, const void* store,
                              const void* q, float R_K, float R_V,
                              int32_t vscale, float* out, void* workspace,

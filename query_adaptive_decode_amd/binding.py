@@ -158,13 +158,14 @@ def decode_attn(cfg: Config, store, q, R_K, R_V, workspace, out=None,
 
 def decode_attn_timed(cfg: Config, store, q, R_K, R_V, workspace, events, out=None,
                       vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None):
-    """decode_attn that records five caller-created hipEvent_t handles
-    (``events``: sequence of ints) around its four kernels."""
+    """decode_attn that records four caller-created hipEvent_t handles
+    (``events``: sequence of ints) around its three stages (score, value
+    allocation, value gather)."""
     if out is None:
         out = torch.empty((cfg.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32,
                           device=q.device)
     _need_cuda(store, q, out, workspace, key_depths, value_depths)
-    ev = (ctypes.c_void_p * 5)(*[int(e) for e in events])
+    ev = (ctypes.c_void_p * 4)(*[int(e) for e in events])
     _check("readkv_decode_attn_timed", lib().readkv_decode_attn_timed(
         ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(vscale),
         _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),

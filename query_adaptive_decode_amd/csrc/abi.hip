@@ -197,7 +197,7 @@ int readkv_decode_attn_timed(const readkv_config* cfg, const void* store, const 
                              size_t workspace_bytes, uint8_t* key_depths_out,
                              uint8_t* value_depths_out, void* const* events, void* stream) {
   if (!events) return READKV_EINVAL;
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 4; ++i)
     if (!events[i]) return READKV_EINVAL;
   return decode_impl(cfg, store, q, R_K, R_V, vscale, out, workspace, workspace_bytes,
                      key_depths_out, value_depths_out, events, stream);

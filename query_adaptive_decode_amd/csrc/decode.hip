@@ -1,19 +1,20 @@
 // One ReadKV decode step ("Read What Matters: Query-Adaptive Quantization
-// for KV Caches", Sec. 3.2-3.3, Algorithm 1) as five launches on one stream:
+// for KV Caches", Sec. 3.2-3.3, Algorithm 1) as four launches on one stream:
 //
-//   k_key_alloc   (B*G waves)         key weights (Eq. (2)) and ChooseDepths
-//                                     over the d_h channels -> t^K
-//   k_score       (B*G x tiles)       prefix-gather of the chosen key planes
-//                                     through LDS, reconstructed logits in
-//                                     fp64, per-tile max and sum of exp
-//                                     (split-context softmax)
+//   k_score       (B*G x runs)        key weights (Eq. (2)) and ChooseDepths
+//                                     over the d_h channels -> t^K (block
+//                                     prologue), then the prefix-gather of
+//                                     the chosen key planes through LDS,
+//                                     reconstructed logits in fp64, per-tile
+//                                     max and sum of exp (split-context
+//                                     softmax)
 //   k_value_alloc (B*G blocks)        softmax statistics, value weights
 //                                     (Eq. (3)) and ChooseDepths over the
 //                                     packed tokens -> t^V
-//   k_gather      (B*G x chunks)      prefix-gather of the chosen value
+//   k_gather      (B*G x runs)        prefix-gather of the chosen value
 //                                     planes, attention-weighted sums per
-//                                     chunk
-//   k_out_reduce  (B*H*d threads)     chunk partials summed in chunk order
+//                                     run of chunks
+//   k_out_reduce  (B*H*d threads)     run partials summed in run order
 //
 // The k_value_alloc -> k_gather boundary is the staged(2) reader's second
 // batch: value reads depend on attention computed from the first batch.
@@ -258,37 +259,6 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
       }
     }
   }
-}
-
-template <int GQA, int DT>
-__global__ __launch_bounds__(64) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
-                                                  int W, float RK, uint8_t* tk) {
-  constexpr int esize = DT == 0 ? 2 : 4;
-  const int unit = blockIdx.x;
-  const int b = unit / G, g = unit - b * G;
-  const ReqRecord r = req_of(store, b);
-  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const int lane = threadIdx.x;
-  __shared__ uint64_t ck[2 * 64 * 8];
-  __shared__ uint32_t cc[2 * 64 * 8];
-  double wv[2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int c = lane + 64 * k;
-    double qv[GQA];
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh)
-      qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + c);
-    const double ekc = u.ek[c];
-    double qsq = 0.0;
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
-    wv[k] = __dmul_rn(qsq, ekc);
-  }
-  uint32_t sel[2];
-  key_depths_wave(wv, W, (uint32_t)floor((double)RK * (double)kDim), ck, cc, sel);
-  tk[(int64_t)unit * kDim + lane] = (uint8_t)sel[0];
-  tk[(int64_t)unit * kDim + lane + 64] = (uint8_t)sel[1];
 }
 
 // ---------------------------------------------------------------------------
@@ -1580,8 +1550,6 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   const int esize = DT == 0 ? 2 : 4;
 
   mark(a, 0, st);
-  // (the key allocation runs inside the score kernel)
-  mark(a, 1, st);
   // slots staged per score tile: at most min(B_K, 128 W) chosen key lines,
   // 64 B each
   double bk = floor((double)a.RK * (double)kDim);
@@ -1608,7 +1576,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
                      (const uint8_t*)a.store, a.q, tk, a.H, a.G, a.W, a.RK, a.capmax,
                      L.ntile, (float*)(ws + L.ebuf), (_Float16*)(ws + L.e16),
                      (double*)(ws + L.tilepart));
-  mark(a, 2, st);
+  mark(a, 1, st);
   {
     auto va = &k_value_alloc<GQA, 0>;
     if (a.capmax <= (int64_t)kVRound * 4) va = &k_value_alloc<GQA, 4>;
@@ -1619,7 +1587,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
                        (const float*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
                        (double*)(ws + L.ftile), (double*)(ws + L.aval), tv);
   }
-  mark(a, 3, st);
+  mark(a, 2, st);
   {
     // runs of consecutive chunks per block: about four blocks per compute
     // unit (37 KB of LDS each)
@@ -1636,7 +1604,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
     hipLaunchKernelGGL(k_out_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st, nrun,
                        L.nchunk, nout, (const float*)(ws + L.opart), a.out);
   }
-  mark(a, 4, st);
+  mark(a, 3, st);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
