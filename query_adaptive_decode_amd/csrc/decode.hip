@@ -1348,14 +1348,23 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
     if (tid < GQA) pfs = (float)ftile[(hrow0 + tid) * ntile_ws + (int)(c0 / kTile)];
   };
   auto load_rows = [&](int chunk, uint32_t t) __attribute__((always_inline)) {
-    const uint4* vp = reinterpret_cast<const uint4*>(u.vplanes) + ((int64_t)chunk * kChunk + jl) * W;
-    // planes past the depth re-read plane 0 of the same row (same line, no
-    // extra traffic); they are masked in the un-plane
+    // buffer loads over the chunk's plane rows: planes past the depth take
+    // an offset beyond the buffer's size, which reads zeros without a
+    // memory access, so a token costs only the lines its prefix touches
+    // (nothing at depth 0)
+    const uint8_t* cbase = reinterpret_cast<const uint8_t*>(u.vplanes) + (int64_t)chunk * kChunk * W * 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cbase), (short)0, kChunk * W * 16, kBufWord3);
+    const int tok = jl * W * 16;
     const uint32_t p0 = (uint32_t)rh;
-    prow0 = vp[p0 < t ? p0 : 0u];
-    prow1 = vp[p0 + 2 < t ? p0 + 2 : 0u];
-    prow2 = vp[p0 + 4 < t ? p0 + 4 : 0u];
-    prow3 = vp[p0 + 6 < t ? p0 + 6 : 0u];
+    auto ld = [&](uint32_t p) __attribute__((always_inline)) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, p < t ? tok + (int)p * 16 : kBufOff, 0, 0);
+      return make_uint4(v[0], v[1], v[2], v[3]);
+    };
+    prow0 = ld(p0);
+    prow1 = ld(p0 + 2);
+    prow2 = ld(p0 + 4);
+    prow3 = ld(p0 + 6);
   };
   auto store_chunk = [&](uint32_t t) __attribute__((always_inline)) {
     if (tid < kChunk) {
@@ -1369,7 +1378,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
       vmeta_s[i / kDim][i % kDim] = pmeta[k];
     }
     if (tid < GQA) fs[tid] = pfs;
-    (void)t;  // rows past the depth hold plane 0 again: masked in the un-plane
+    (void)t;  // rows past the depth hold zeros (also masked in the un-plane)
     rows[rh][jl] = prow0;
     rows[rh + 2][jl] = prow1;
     rows[rh + 4][jl] = prow2;

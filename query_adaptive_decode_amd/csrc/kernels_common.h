@@ -46,6 +46,12 @@ __device__ __forceinline__ float ldexp_pow2f(int e) {
   return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
+// Raw buffer resources (stride 0): the fourth descriptor word of the GFX9
+// family for untyped 32-bit data, and an offset past any buffer this code
+// builds (a load there returns zeros and makes no memory access).
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufOff = (int)0x80000000u;
+
 // wave64 helpers built on DPP lane moves (no LDS round trips).
 // DPP control codes of the GFX9 family.
 constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
