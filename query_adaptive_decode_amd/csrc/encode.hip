@@ -251,8 +251,12 @@ __global__ __launch_bounds__(256) void k_append_small(uint8_t* store, const void
   }
   __syncthreads();
   if (tid == 0) {
+    // the ticket only orders this block's reads of the record (all done:
+    // their values are in use) before the length changes; the data written
+    // here reaches the next launch through the kernel boundary, so no
+    // device-scope fence (which would write back the L2) is needed
     unsigned long long* ticket = reinterpret_cast<unsigned long long*>(&rp->reserved);
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     last_s = atomicAdd(ticket, 1ull) == (unsigned long long)(G - 1);
   }
   __syncthreads();
