@@ -12,9 +12,10 @@ header (align_up(256 + 32*B, 4096) bytes)
   i64 capacity, i64 total_bytes;  at 256 + 32*b: i64 len, i64 cap,
   i64 offset, i64 reserved  for request b.
 request region b (cap = cap_b, a multiple of 32; ng = cap/32):
-  Kplanes u32 [G][d][W][ngk]  bit i of word (g,c,p,gamma) = plane p (bit
-                              W-1-p of the code) of token 32*gamma+i, chan c;
-                              ngk = ng rounded up to a multiple of 32
+  Kplanes u32 [G][ntk][d][W][16]  bit i of word (g,tau,c,p,k) = plane p
+                              (bit W-1-p of the code) of token
+                              32*(16*tau+k)+i, channel c; ntk = ng/16
+                              rounded up (tiles of 16 groups)
   Vplanes u32 [G][cap][W][d/32]  bit (c%32) of word (g,j,p,c/32) = plane p
                               of token j, channel c
   Kmeta   u32 [G][ng][d]      lo bf16 bits | rng bf16 bits << 16
@@ -43,9 +44,9 @@ def region_layout(G: int, d: int, W: int, cap: int, esize: int) -> dict:
     """Byte offsets (relative to the region start) and sizes of each
     sub-array of one request region."""
     ng = cap // 32
-    ngk = _al(ng, 32)
+    ntk = (ng + 15) // 16
     parts = [
-        ("Kplanes", G * d * W * ngk * 4),
+        ("Kplanes", G * ntk * d * W * 16 * 4),
         ("Vplanes", G * cap * W * (d // 32) * 4),
         ("Kmeta", G * ng * d * 4),
         ("Vmeta", G * ng * d * 4),
@@ -76,12 +77,14 @@ def pack_unit(enc_k, enc_v, cap: int, dtype: str) -> dict:
     tp, d = enc_k.codes.shape
     ng = cap // 32
     ngc = enc_k.n_groups
-    kpl = np.zeros((d, W, _al(ng, 32)), dtype=np.uint32)
+    ntk = (ng + 15) // 16
+    kpl = np.zeros((ntk, d, W, 16), dtype=np.uint32)
     ck = enc_k.codes.reshape(ngc, 32, d)
     for p in range(W):
         bits = ((ck >> (W - 1 - p)) & 1).astype(np.uint64)       # [ngc][32][d]
-        word = (bits << np.arange(32, dtype=np.uint64)[None, :, None]).sum(axis=1)
-        kpl[:, p, :ngc] = word.T.astype(np.uint32)
+        word = (bits << np.arange(32, dtype=np.uint64)[None, :, None]).sum(axis=1)  # [ngc][d]
+        for gam in range(ngc):
+            kpl[gam // 16, :, p, gam % 16] = word[gam].astype(np.uint32)
     vpl = np.zeros((cap, W, d // 32), dtype=np.uint32)
     for p in range(W):
         bits = ((enc_v.codes >> (W - 1 - p)) & 1).astype(np.uint64)  # [tp][d]
@@ -151,7 +154,7 @@ def unpack_unit(buf: np.ndarray, hdr: dict, b: int, g: int) -> dict:
 
     edt = np.uint16 if esize == 2 else np.float32
     return dict(
-        Kplanes=sub("Kplanes", np.uint32, (d, W, _al(ng, 32))),
+        Kplanes=sub("Kplanes", np.uint32, ((ng + 15) // 16, d, W, 16)),
         Vplanes=sub("Vplanes", np.uint32, (cap, W, d // 32)),
         Kmeta=sub("Kmeta", np.uint32, (ng, d)),
         Vmeta=sub("Vmeta", np.uint32, (ng, d)),

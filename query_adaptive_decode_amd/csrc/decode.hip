@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     const int c = s2c[s];
     const int p = s - offs[c];
     if (4 * q4 < ngp)
-      v = *reinterpret_cast<const uint4*>(u.kplanes + ((int64_t)c * W + p) * u.ngk + gam0 + 4 * q4);
+      v = *reinterpret_cast<const uint4*>(u.kplanes + (((gam0 >> 4) * kDim + c) * W + p) * 16 + 4 * q4);
     return v;
   };
   uint4 pre[PRE];

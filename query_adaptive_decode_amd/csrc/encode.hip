@@ -97,7 +97,7 @@ __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, co
       uint32_t word = 0;
 #pragma unroll
       for (int s = 0; s < kGroup; ++s) word |= ((code[s] >> (W - 1 - p)) & 1u) << s;
-      u.kplanes[((int64_t)c * W + p) * u.ngk + gam] = word;
+      u.kplanes[(((gam >> 4) * kDim + c) * W + p) * 16 + (gam & 15)] = word;
     }
   } else {
     u.vmeta[gam * kDim + c] = meta;

@@ -6,12 +6,13 @@
 // rounded up to 4096 bytes.  A request region with capacity `cap` tokens
 // (multiple of 32, ng = cap/32 groups) holds, each sub-array 256-byte
 // aligned:
-//   Kplanes u32 [G][d][W][ngk]     token-packed: bit i of word (g,c,p,gamma)
-//                                  is plane p of token 32*gamma+i, channel c;
-//                                  ngk = ng rounded up to a multiple of 32:
-//                                  every line is whole 128 B cache lines, so
-//                                  a 16-group (512-token) segment is one
-//                                  aligned 64 B half line
+//   Kplanes u32 [G][ntk][d][W][16] token-packed, tile-major: bit i of word
+//                                  (g,tau,c,p,k) is plane p of token
+//                                  32*(16 tau + k) + i, channel c; ntk =
+//                                  ceil(ng/16) tiles of 512 tokens.  A
+//                                  channel's depth-t prefix over one tile is
+//                                  t*64 contiguous bytes (planes 2k, 2k+1
+//                                  share a 128 B line)
 //   Vplanes u32 [G][cap][W][d/32]  channel-packed: a token's t-plane prefix
 //                                  is t*d/8 contiguous bytes
 //   Kmeta   u32 [G][ng][d]         lo bf16 | rng bf16 << 16
@@ -59,8 +60,8 @@ RKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 RKV_HD int64_t header_bytes(int B) { return align_up(256 + 32 * (int64_t)B, 4096); }
 
-// words per key-plane line (one (channel, plane) over all groups)
-RKV_HD int64_t key_line_words(int64_t cap) { return align_up(cap / kGroup, 32); }
+// 512-token tiles of the key planes (16 groups each)
+RKV_HD int64_t key_tiles(int64_t cap) { return (cap / kGroup + 15) / 16; }
 
 struct RegionLayout {
   int64_t kplanes, vplanes, kmeta, vmeta, ek, ev, ktail, vtail, size;
@@ -70,7 +71,7 @@ RKV_HD RegionLayout region_layout(int G, int d, int W, int64_t cap, int esize) {
   const int64_t ng = cap / kGroup;
   RegionLayout L;
   int64_t off = 0;
-  L.kplanes = off; off += (int64_t)G * d * W * key_line_words(cap) * 4; off = align_up(off, 256);
+  L.kplanes = off; off += (int64_t)G * key_tiles(cap) * d * W * 16 * 4; off = align_up(off, 256);
   L.vplanes = off; off += (int64_t)G * cap * W * (d / 32) * 4; off = align_up(off, 256);
   L.kmeta = off; off += (int64_t)G * ng * d * 4; off = align_up(off, 256);
   L.vmeta = off; off += (int64_t)G * ng * d * 4; off = align_up(off, 256);
@@ -84,7 +85,7 @@ RKV_HD RegionLayout region_layout(int G, int d, int W, int64_t cap, int esize) {
 
 // Pointers to one (request, KV head) unit's arrays.
 struct Unit {
-  uint32_t* kplanes;   // [d][W][ngk]
+  uint32_t* kplanes;   // [ntk][d][W][16]
   uint32_t* vplanes;   // [cap][W][d/32]
   uint32_t* kmeta;     // [ng][d]
   uint32_t* vmeta;     // [ng][d]
@@ -92,7 +93,7 @@ struct Unit {
   double* ev;          // [ng]
   uint8_t* ktail;      // [32][d] elements
   uint8_t* vtail;
-  int64_t cap, ng, ngk;
+  int64_t cap, ng, ntk;
 };
 
 RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int W,
@@ -103,8 +104,8 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
   Unit u;
   u.cap = r.cap;
   u.ng = ng;
-  u.ngk = key_line_words(r.cap);
-  u.kplanes = (uint32_t*)(base + L.kplanes) + (int64_t)g * d * W * u.ngk;
+  u.ntk = key_tiles(r.cap);
+  u.kplanes = (uint32_t*)(base + L.kplanes) + (int64_t)g * u.ntk * d * W * 16;
   u.vplanes = (uint32_t*)(base + L.vplanes) + (int64_t)g * r.cap * W * (d / 32);
   u.kmeta = (uint32_t*)(base + L.kmeta) + (int64_t)g * ng * d;
   u.vmeta = (uint32_t*)(base + L.vmeta) + (int64_t)g * ng * d;

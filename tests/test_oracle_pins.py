@@ -121,7 +121,7 @@ def test_plane_packing_round_trip():
     for c in range(64):
         for pl in range(8):
             for gam in range(2):
-                w = int(p["Kplanes"][c, pl, gam])
+                w = int(p["Kplanes"][gam // 16, c, pl, gam % 16])
                 for i in range(32):
                     kc[gam * 32 + i, c] |= ((w >> i) & 1) << (7 - pl)
     assert np.array_equal(kc, ek.codes)
@@ -133,12 +133,30 @@ def test_plane_packing_round_trip():
                 for i in range(32):
                     vc[j, wd * 32 + i] |= ((w >> i) & 1) << (7 - pl)
     assert np.array_equal(vc, ev.codes)
-    assert p["Kplanes"][:, :, 2:].sum() == 0 and p["Vplanes"][64:].sum() == 0
+    assert p["Kplanes"][0, :, :, 2:].sum() == 0 and p["Vplanes"][64:].sum() == 0
     lo = torch.tensor((p["Kmeta"][:2] & 0xFFFF).astype(np.int16)).view(torch.bfloat16).double().numpy()
     assert np.array_equal(lo, ek.lo)
 
 
 # -------------------------------------------------------- P2/P3 brute force
+
+def test_key_planes_span_tiles():
+    # 34 closed groups: three 16-group tiles, the last one partly filled
+    rng = np.random.default_rng(5)
+    cap = 1120
+    K = _rand_bf16(rng, (1090, 32))
+    ek = O.encode_stream(K)
+    p = O.pack_unit(ek, O.encode_stream(K), cap, "bf16")
+    kp = p["Kplanes"]
+    assert kp.shape == (3, 32, 8, 16)
+    kc = np.zeros((34 * 32, 32), dtype=np.int64)
+    for gam in range(34):
+        w = kp[gam // 16, :, :, gam % 16].astype(np.int64)        # [c][plane]
+        bits = (w[None, :, :] >> np.arange(32)[:, None, None]) & 1  # [i][c][plane]
+        kc[gam * 32:(gam + 1) * 32] = (bits << (7 - np.arange(8))[None, None, :]).sum(axis=2)
+    assert np.array_equal(kc, ek.codes)
+    assert kp[2, :, :, 2:].sum() == 0
+
 def _brute_best(a, W, B):
     """Exact minimum of sum_i a_i 4^-t_i over t in {0..W}^N, sum t <= B.
     Canonical optimum: fewest increments, then lexicographically largest."""
