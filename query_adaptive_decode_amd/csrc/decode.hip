@@ -582,11 +582,19 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     load_pieces(tile);
     load_meta(tile);
   };
+  // 8-byte chunk k of staged slot s sits at chunk k ^ (s & 7): the 8 slots
+  // one transposing read touches (the planes of a channel) then fall on
+  // distinct LDS banks
+  auto stage_put = [&](int idx, uint4 v) __attribute__((always_inline)) {
+    const int sl = idx >> 2, x = sl & 7;
+    if (x & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+    *reinterpret_cast<uint4*>(planes + (sl * 4 + ((idx & 3) ^ (x >> 1))) * 4) = v;
+  };
   auto store_ahead = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
       const int idx = k * 256 + tid;
-      if (idx < nq) *reinterpret_cast<uint4*>(planes + idx * 4) = pre[k];
+      if (idx < nq) stage_put(idx, pre[k]);
     }
 #pragma unroll
     for (int k = 0; k < MPT; ++k) {
@@ -597,7 +605,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     const int64_t gam0 = (int64_t)tile * NG;
     const int ngp = tile_ngp(tile);
     for (int idx = PRE * 256 + tid; idx < nq; idx += 256)
-      *reinterpret_cast<uint4*>(planes + idx * 4) = piece(idx, gam0, ngp);
+      stage_put(idx, piece(idx, gam0, ngp));
   };
   load_pieces(tile_begin);  // the first tile's metadata is already in flight
   store_ahead(tile_begin);
@@ -609,9 +617,9 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
 
   const int kq = lane >> 4, jj = (lane & 15) >> 1, ss = lane & 1;
   // transposing plane read: lane 2j + s of quarter q addresses plane 7 - j,
-  // groups 4q + 2s and 4q + 2s + 1 (8 bytes); lane o then holds the plane
-  // bytes of octet o
-  const int troff = (7 - jj) * 64 + (4 * kq + 2 * ss) * 4;
+  // groups 4q + 2s and 4q + 2s + 1 (8-byte chunk 2q + s, swizzled as
+  // staged); lane o then holds the plane bytes of octet o
+  const int c8 = 2 * kq + ss;
   // digit chunk (channel octet co, channel j, set s) of block (hq, half m)
   auto achunk = [&](int hq, int m, int co, int j, int s) -> int {
     return (2 * hq + m) * AMS + co * AOS + (2 * j + s) * 8;
@@ -688,7 +696,8 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
           const uint32_t inf = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 4 * bt + k);
           tk4[k] = (int)(inf & 0xFFu);
           tmax = max(tmax, tk4[k]);
-          const long v = tr8_read(reinterpret_cast<const uint8_t*>(planes) + (inf >> 8) * 64 + troff);
+          const int sl = (int)(inf >> 8) + 7 - jj;
+          const long v = tr8_read(reinterpret_cast<const uint8_t*>(planes) + sl * 64 + ((c8 ^ (sl & 7)) << 3));
           pb[k] = __builtin_bit_cast(uint2, v);
         }
         if (tmax == 0) continue;
@@ -1293,12 +1302,20 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
   constexpr int NG = kChunk / kGroup;                  // 4 groups per chunk
   constexpr int GS = (16 / GQA < NG) ? 16 / GQA : NG;  // groups per MFMA column set
   constexpr int NSET = (NG + GS - 1) / GS;
-  constexpr int XS = kDim + 8;  // code-tile row stride: rows 2 apart fall in different banks
+  // code-tile row stride 144 B (36 words): the 8 rows an MFMA operand read
+  // touches start 4 banks apart
+  constexpr int XS = kDim + 16;
+  // plane-row stride kChunk + 1 chunks: the 8 planes a transposing read
+  // touches start 4 banks apart (an unpadded 2 KB stride puts them all on
+  // the same banks)
+  constexpr int RS = kChunk + 1;
   constexpr int MPT = NG * kDim / 256;  // metadata words per thread
-  __shared__ __attribute__((aligned(16))) uint4 rows[8][kChunk];     // [plane][token]; reused at the end
+  __shared__ __attribute__((aligned(16))) uint4 rows[8 * RS];        // [plane][token]; reused at the end
   __shared__ __attribute__((aligned(16))) uint8_t xl[kChunk * XS];   // codes [token][channel]
-  __shared__ __attribute__((aligned(16))) _Float16 es[GQA][kChunk];
-  __shared__ uint32_t vmeta_s[NG][kDim];
+  // rows padded so that the heads' weight rows (es) and the groups'
+  // metadata rows (vmeta_s) read by one MFMA fold start on different banks
+  __shared__ __attribute__((aligned(16))) _Float16 es[GQA][kChunk + 8];
+  __shared__ uint32_t vmeta_s[NG][kDim + 1];
   __shared__ float Ag[NG][GQA], Bg[NG][GQA];
   __shared__ __attribute__((aligned(4))) uint8_t tvs[kChunk];
   __shared__ float fs[GQA];
@@ -1379,10 +1396,10 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
     }
     if (tid < GQA) fs[tid] = pfs;
     (void)t;  // rows past the depth hold zeros (also masked in the un-plane)
-    rows[rh][jl] = prow0;
-    rows[rh + 2][jl] = prow1;
-    rows[rh + 4][jl] = prow2;
-    rows[rh + 6][jl] = prow3;
+    rows[rh * RS + jl] = prow0;
+    rows[(rh + 2) * RS + jl] = prow1;
+    rows[(rh + 4) * RS + jl] = prow2;
+    rows[(rh + 6) * RS + jl] = prow3;
   };
 
   uint32_t t_rows = tv_of(cb);  // depth of token jl in the chunk whose rows are in flight
@@ -1402,7 +1419,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
   // transposing plane read: lane 2e + s of a quarter addresses plane 7 - e,
   // bytes 8s .. 8s + 7 of the quarter's token row; lane L then holds the
   // plane bytes of channel octet L
-  const int troff = (7 - (L >> 1)) * (kChunk * 16) + 8 * (L & 1);
+  const int troff = (7 - (L >> 1)) * (RS * 16) + 8 * (L & 1);
 
   for (int chunk = cb; chunk < ce; ++chunk) {
     const int64_t c0 = (int64_t)chunk * kChunk;
