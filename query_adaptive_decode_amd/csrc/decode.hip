@@ -1168,12 +1168,22 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
         __syncthreads();
       }
       {
-        for_tokens([&](double a, int ef, int, int) __attribute__((always_inline)) {
-          const int d = ef - Es;
-          const bool c = d >= 2 && d <= twoW && !(d & 1);
-          const uint64_t mnt = dbits(a) & 0x000FFFFFFFFFFFFFull;
-          if (c && (mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
-        });
+        // a regular token's candidate: d = E - Es even in [2, 2W]
+        const uint32_t dspan = (uint32_t)(twoW - 2);
+        if (pass == 0) {  // no prefix yet: the top 11 mantissa bits
+          for_tokens([&](double a, int ef, int, int) __attribute__((always_inline)) {
+            const uint32_t d2 = (uint32_t)(ef - Es - 2);
+            const uint32_t hi = (uint32_t)(dbits(a) >> 32);
+            if (d2 <= dspan && !(d2 & 1u)) atomicAdd(&hist[(hi >> 9) & 2047u], 1u);
+          });
+        } else {
+          for_tokens([&](double a, int ef, int, int) __attribute__((always_inline)) {
+            const uint32_t d2 = (uint32_t)(ef - Es - 2);
+            const uint64_t mnt = dbits(a) & 0x000FFFFFFFFFFFFFull;
+            if (d2 <= dspan && !(d2 & 1u) && (mnt & mask) == prefix)
+              atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
+          });
+        }
         if (any_odd) {
           for_tokens([&](double a, int ef, int, int) {
             if (is_odd(a, ef))
