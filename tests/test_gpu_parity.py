@@ -37,6 +37,12 @@ def _gpu():
     binding.lib()   # raises if the library was not built
 
 
+def _kp_groups(kp):
+    """Key planes [tile][c][p][16] as [c][p][group]."""
+    nt, d, W, k = kp.shape
+    return kp.transpose(1, 2, 0, 3).reshape(d, W, nt * k)
+
+
 class Run:
     """Prefill + `steps` (append, decode) rounds on the GPU, keeping every
     decode's outputs and depth schedules on the host."""
@@ -127,7 +133,8 @@ class Run:
             got = F.unpack_unit(self.store, hdr, b, g)
             ngc, tp, r = ek.n_groups, ek.t_packed, n - ek.t_packed
             tag = f"unit=({b},{g}) n={n}"
-            assert np.array_equal(got["Kplanes"][:, :, :ngc], want["Kplanes"][:, :, :ngc]), tag
+            assert np.array_equal(_kp_groups(got["Kplanes"])[:, :, :ngc],
+                                  _kp_groups(want["Kplanes"])[:, :, :ngc]), tag
             assert np.array_equal(got["Vplanes"][:tp], want["Vplanes"][:tp]), tag
             assert np.array_equal(got["Kmeta"][:ngc], want["Kmeta"][:ngc]), tag
             assert np.array_equal(got["Vmeta"][:ngc], want["Vmeta"][:ngc]), tag
@@ -171,6 +178,26 @@ def test_ragged_tails_and_tiles(T0):
     run = Run(cfg, steps=2, rates=[(4.0, 4.0), (0.0, 0.0), (8.0, 8.0), (100.0, 0.5), (0.25, 100.0)])
     run.check_store()
     run.check()
+
+
+def test_long_context_eight_register_rounds():
+    # capacity between 10,240 and 16,384 tokens: the value allocator keeps
+    # eight rounds of weights in registers
+    cfg = synth.workload(2, B=1, H=8, G=2, T0=12000)
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 2.0)])
+    run.check_store()
+    run.check()
+
+
+def test_long_context_131k_weights_through_memory():
+    # the long-context configuration at its full length (one request, two
+    # KV heads): above 16,384 tokens the value weights go through memory
+    # (the oracle takes about 25 s per unit and step at this length: one
+    # unit is checked)
+    cfg = synth.workload(3, B=1, H=8, G=2)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0)])
+    run.check_store([(0, 1)])
+    run.check([(0, 1)])
 
 
 def test_full_size_llama_layer_sampled_units():
