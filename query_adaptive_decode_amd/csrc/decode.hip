@@ -80,7 +80,6 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
   // (M_c descending, c ascending).
   int ec[2];
   uint64_t mc[2];
-  uint32_t rk[2] = {0u, 0u};
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const uint64_t wb = dbits(wv[k]);
@@ -123,26 +122,46 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
       const int d = ec[k] - 2 - Ls;
       at[k] = ec[k] >= 0 && d >= 0 && (d & 1) == 0 && d / 2 < W;
     }
-    // rank within the level: walk the lanes holding a candidate there
-#pragma unroll
-    for (int k2 = 0; k2 < 2; ++k2) {
-      uint64_t lanes = __ballot(at[k2]);
-      while (lanes) {
-        const int src = __builtin_ctzll(lanes);
-        lanes &= lanes - 1;
-        const uint64_t m2 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mc[k2] >> 32), src) << 32) |
-                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)mc[k2], src);
-        const int c2 = src + 64 * k2;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int c = lane + 64 * k;
-          if (at[k] && (m2 > mc[k] || (m2 == mc[k] && c2 < c))) ++rk[k];
-        }
+    // the rem largest at the level by (M_c descending, c ascending): an
+    // MSB-first search over the 52 mantissa bits (wave ballots) that stops
+    // as soon as the candidates still equal to the threshold on the decided
+    // bits are exactly the ones left to take
+    uint64_t pre = 0ull, hm = 0ull;  // threshold bits decided so far, their mask
+    uint32_t rm = rem;
+    bool early = false;
+    for (int bit = 51; bit >= 0; --bit) {
+      const bool a0 = at[0] && ((mc[0] ^ pre) & hm) == 0ull;
+      const bool a1 = at[1] && ((mc[1] ^ pre) & hm) == 0ull;
+      if ((uint32_t)(__popcll(__ballot(a0)) + __popcll(__ballot(a1))) == rm) {
+        early = true;
+        break;
       }
+      const uint64_t bm = 1ull << bit;
+      const uint32_t c1 = (uint32_t)(__popcll(__ballot(a0 && (mc[0] & bm))) +
+                                     __popcll(__ballot(a1 && (mc[1] & bm))));
+      if (c1 >= rm) pre |= bm;
+      else rm -= c1;
+      hm |= bm;
     }
+    // above the threshold on the decided bits: taken; equal to it: all of
+    // them after an early stop, else (equal mantissas) the first rm in
+    // channel order
+    bool eq[2];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (at[k] && rk[k] < rem) ++sel[k];
+    for (int k = 0; k < 2; ++k) {
+      const uint64_t hv = mc[k] & hm;
+      eq[k] = at[k] && hv == pre;
+      if (at[k] && hv > pre) ++sel[k];
+    }
+    if (early) {
+      sel[0] += eq[0];
+      sel[1] += eq[1];
+    } else {
+      const uint64_t b0 = __ballot(eq[0]), b1 = __ballot(eq[1]);
+      const uint64_t below = (1ull << lane) - 1ull;
+      if (eq[0] && (uint32_t)__popcll(b0 & below) < rm) ++sel[0];
+      if (eq[1] && (uint32_t)(__popcll(b0) + __popcll(b1 & below)) < rm) ++sel[1];
+    }
     return;
   }
   // Exact path (some gain is subnormal or not finite): the 64-bit patterns
