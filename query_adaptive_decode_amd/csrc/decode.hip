@@ -471,15 +471,15 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     const int64_t n = Tp / kGroup - (int64_t)tile * NG;
     return (int)(n < 0 ? 0 : (n > NG ? NG : n));
   };
+  // metadata word k of this thread: group k * 256 / kDim + tid / kDim of
+  // the tile, channel tid % kDim; buffer loads, zero past the closed groups
   uint32_t pmeta[MPT];
+  const __amdgpu_buffer_rsrc_t rs_meta = __builtin_amdgcn_make_buffer_rsrc(
+      u.kmeta, (short)0, (int)(Tp / kGroup) * kDim * 4, kBufWord3);
   auto load_meta = [&](int tile) {
-    const int64_t gam0 = (int64_t)tile * NG;
-    const int ngp = tile_ngp(tile);
 #pragma unroll
-    for (int k = 0; k < MPT; ++k) {
-      const int i = k * 256 + tid, gl = i / kDim, c = i % kDim;
-      pmeta[k] = gl < ngp ? u.kmeta[(gam0 + gl) * kDim + c] : 0u;
-    }
+    for (int k = 0; k < MPT; ++k)
+      pmeta[k] = __builtin_amdgcn_raw_buffer_load_b32(rs_meta, (tile * NG * kDim + k * 256 + tid) * 4, 0, 0);
   };
   load_meta(tile_begin);  // independent of the depths: in flight during the setup
 
@@ -587,14 +587,30 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       v = *reinterpret_cast<const uint4*>(u.kplanes + (((gam0 >> 4) * kDim + c) * W + p) * 16 + 4 * q4);
     return v;
   };
+  // Piece k of this thread is idx = k * 256 + tid.  Its byte offset in a
+  // tile's plane block and its place in LDS do not depend on the tile, so
+  // both are set up once; the tile is the scalar base of a buffer (pieces
+  // past the chosen lines take an offset outside it and read as zeros, and
+  // the groups of a partial tile past the closed ones are read but unused).
+  uint32_t poff[PRE];
+#pragma unroll
+  for (int k = 0; k < PRE; ++k) {
+    const int idx = k * 256 + tid;
+    int o = kBufOff;
+    if (idx < nq) {
+      const int s = idx >> 2, c = s2c[s], p = s - offs[c];
+      o = ((c * W + p) * 16 + 4 * (idx & 3)) * 4;
+    }
+    poff[k] = (uint32_t)o;
+  }
   uint4 pre[PRE];
   auto load_pieces = [&](int tile) {
-    const int64_t gam0 = (int64_t)tile * NG;
-    const int ngp = tile_ngp(tile);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        u.kplanes + (int64_t)tile * kDim * W * 16, (short)0, kDim * W * 64, kBufWord3);
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
-      const int idx = k * 256 + tid;
-      pre[k] = idx < nq ? piece(idx, gam0, ngp) : make_uint4(0u, 0u, 0u, 0u);
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)poff[k], 0, 0);
+      pre[k] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
   auto load_ahead = [&](int tile) {
@@ -609,11 +625,18 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     if (x & 1) v = make_uint4(v.z, v.w, v.x, v.y);
     *reinterpret_cast<uint4*>(planes + (sl * 4 + ((idx & 3) ^ (x >> 1))) * 4) = v;
   };
+  // piece k sits in slot 64 k + tid / 4, so the slot's chunk swizzle is
+  // the same for every k: two 8-byte writes at fixed offsets
+  const int sl0 = tid >> 2, x0 = sl0 & 7, q40 = tid & 3;
+  uint8_t* const pl_lo = reinterpret_cast<uint8_t*>(planes) + sl0 * 64 + (((2 * q40) ^ x0) << 3);
+  uint8_t* const pl_hi = reinterpret_cast<uint8_t*>(planes) + sl0 * 64 + (((2 * q40 + 1) ^ x0) << 3);
   auto store_ahead = [&](int tile) {
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
-      const int idx = k * 256 + tid;
-      if (idx < nq) stage_put(idx, pre[k]);
+      if (k * 256 + tid < nq) {
+        *reinterpret_cast<uint2*>(pl_lo + k * 4096) = make_uint2(pre[k].x, pre[k].y);
+        *reinterpret_cast<uint2*>(pl_hi + k * 4096) = make_uint2(pre[k].z, pre[k].w);
+      }
     }
 #pragma unroll
     for (int k = 0; k < MPT; ++k) {
