@@ -1510,18 +1510,20 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
         Bg[pr / GQA][pr % GQA] = bh;
       }
     }
-    // ---- un-plane: wave w, step i -> tokens 32 w + 4 i + quarter ----
+    // ---- un-plane: wave w, step i -> tokens 32 w + 4 i + quarter.  The
+    // rows of planes past a token's depth were loaded as zeros, so the
+    // codes need no mask; the deepest of the 4 tokens (a scalar) picks the
+    // transpose (at most 4 planes: the upper half only) ----
 #pragma unroll 2
     for (int it = 0; it < 8; ++it) {
       const int j0 = 32 * wv + 4 * it;
-      const uint32_t t4 = *reinterpret_cast<const uint32_t*>(&tvs[j0]);  // the 4 tokens' depths
+      const uint32_t t4 = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)*reinterpret_cast<const uint32_t*>(&tvs[j0]));  // the 4 tokens' depths
       const uint32_t tmax = max(max(t4 & 0xFFu, (t4 >> 8) & 0xFFu), max((t4 >> 16) & 0xFFu, t4 >> 24));
       const int j = j0 + q4;
-      const uint32_t t = (t4 >> (8 * q4)) & 0xFFu;
       const long v = tr8_read(reinterpret_cast<const uint8_t*>(rows) + j * 16 + troff);
       const uint2 pb = __builtin_bit_cast(uint2, v);
-      const uint64_t keep = t >= 8u ? ~0ull : (t == 0u ? 0ull : ~0ull << (64 - 8 * t));
-      uint32_t lo = pb.x & (uint32_t)keep, hi = pb.y & (uint32_t)(keep >> 32);
+      uint32_t lo = pb.x, hi = pb.y;
       if (tmax <= 4u) transpose8_hi4(lo, hi);
       else transpose8_halves(lo, hi);
       *reinterpret_cast<uint2*>(xl + j * XS + 8 * L) = make_uint2(lo, hi);
