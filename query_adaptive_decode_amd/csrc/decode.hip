@@ -1392,29 +1392,36 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
 
   // ---- register prefetch of one chunk ----
   uint32_t ptv = 0;                 // depth of token jl (for the row loads)
-  _Float16 pes[GQA];
+  uint32_t pes[GQA];  // e of tokens 2 tid, 2 tid + 1 (tid < 64) per head, as fp16 pairs
   uint32_t pmeta[MPT];
-  float pfs = 0.f;
+  double pfs = 0.0;  // converted when stored: no wait right after its load
   uint4 prow0, prow1, prow2, prow3;  // planes rh, rh + 2, rh + 4, rh + 6 of token jl
+  // Buffer loads whose range check supplies the zeros past the data (offset
+  // kBufOff lies outside every buffer): no branches around the loads.
+  const __amdgpu_buffer_rsrc_t rs_tv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tvu), (short)0, (int)Tp, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rs_meta = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(u.vmeta), (short)0, (int)(Tp / kGroup) * kDim * 4, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rs_ft = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<double*>(ftile + hrow0 * ntile_ws), (short)0, GQA * ntile_ws * 8, kBufWord3);
   auto tv_of = [&](int chunk) __attribute__((always_inline)) -> uint32_t {
-    const int64_t j = (int64_t)chunk * kChunk + jl;
-    return j < Tp ? (uint32_t)tvu[j] : 0u;
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_tv, chunk * kChunk + jl, 0, 0);
   };
   auto load_small = [&](int chunk) __attribute__((always_inline)) {
-    const int64_t c0 = (int64_t)chunk * kChunk;
-    if (tid < kChunk) {
-      const int64_t j = c0 + tid;
+    const int c0 = chunk * kChunk;
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh)
-        pes[hh] = (j < len) ? e16[(hrow0 + hh) * capmax + j] : (_Float16)0.0f;
+    for (int hh = 0; hh < GQA; ++hh) {
+      // (an odd length reads one stale half past it; tokens past the
+      // length are never used)
+      const __amdgpu_buffer_rsrc_t rs_e = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<_Float16*>(e16 + (hrow0 + hh) * capmax), (short)0, ((int)len * 2 + 3) & ~3, kBufWord3);
+      pes[hh] = __builtin_amdgcn_raw_buffer_load_b32(rs_e, tid < kChunk / 2 ? (c0 + 2 * tid) * 2 : kBufOff, 0, 0);
     }
 #pragma unroll
-    for (int k = 0; k < MPT; ++k) {
-      const int i = k * 256 + tid, gl = i / kDim, c = i % kDim;
-      const int64_t gam = c0 / kGroup + gl;
-      pmeta[k] = ((gam + 1) * kGroup <= Tp) ? u.vmeta[gam * kDim + c] : 0u;
-    }
-    if (tid < GQA) pfs = (float)ftile[(hrow0 + tid) * ntile_ws + (int)(c0 / kTile)];
+    for (int k = 0; k < MPT; ++k)
+      pmeta[k] = __builtin_amdgcn_raw_buffer_load_b32(rs_meta, ((c0 / kGroup) * kDim + k * 256 + tid) * 4, 0, 0);
+    pfs = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(
+                                         rs_ft, tid < GQA ? (tid * ntile_ws + c0 / kTile) * 8 : kBufOff, 0, 0));
   };
   auto load_rows = [&](int chunk, uint32_t t) __attribute__((always_inline)) {
     // buffer loads over the chunk's plane rows: planes past the depth take
@@ -1436,17 +1443,17 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
     prow3 = ld(p0 + 6);
   };
   auto store_chunk = [&](uint32_t t) __attribute__((always_inline)) {
-    if (tid < kChunk) {
-      tvs[tid] = (uint8_t)t;
+    if (tid < kChunk) tvs[tid] = (uint8_t)t;
+    if (tid < kChunk / 2) {
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) es[hh][tid] = pes[hh];
+      for (int hh = 0; hh < GQA; ++hh) *reinterpret_cast<uint32_t*>(&es[hh][2 * tid]) = pes[hh];
     }
 #pragma unroll
     for (int k = 0; k < MPT; ++k) {
       const int i = k * 256 + tid;
       vmeta_s[i / kDim][i % kDim] = pmeta[k];
     }
-    if (tid < GQA) fs[tid] = pfs;
+    if (tid < GQA) fs[tid] = (float)pfs;
     (void)t;  // rows past the depth hold zeros (also masked in the un-plane)
     rows[rh * RS + jl] = prow0;
     rows[(rh + 2) * RS + jl] = prow1;
@@ -1454,10 +1461,12 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
     rows[(rh + 6) * RS + jl] = prow3;
   };
 
-  uint32_t t_rows = tv_of(cb);  // depth of token jl in the chunk whose rows are in flight
+  // depths of token jl: tA of the chunk whose rows are in flight, tB of the
+  // next one (loaded a chunk ahead); the loop runs two chunks per turn with
+  // the roles swapped, so a depth load never has to land in another register
+  uint32_t tA = tv_of(cb), tB = tv_of(cb + 1);  // past the run: unused
   load_small(cb);
-  load_rows(cb, t_rows);
-  uint32_t t_next = cb + 1 < ce ? tv_of(cb + 1) : 0u;
+  load_rows(cb, tA);
 
   const int m = lane & 15, kb = lane >> 4;
   const int gp = m / GQA, hn = m % GQA;
@@ -1473,17 +1482,16 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
   // plane bytes of channel octet L
   const int troff = (7 - (L >> 1)) * (RS * 16) + 8 * (L & 1);
 
-  for (int chunk = cb; chunk < ce; ++chunk) {
+  auto chunk_step = [&](int chunk, uint32_t& tcur, uint32_t& tnext) __attribute__((always_inline)) {
     const int64_t c0 = (int64_t)chunk * kChunk;
     const int64_t gam0 = c0 / kGroup;
-    store_chunk(t_rows);
+    store_chunk(tcur);
     lds_barrier();
     // next chunk's loads go out now and land while this one is computed
     if (chunk + 1 < ce) {
-      t_rows = t_next;
       load_small(chunk + 1);
-      load_rows(chunk + 1, t_rows);
-      t_next = chunk + 2 < ce ? tv_of(chunk + 2) : 0u;
+      load_rows(chunk + 1, tnext);
+      tcur = tv_of(chunk + 2);  // tcur is free once stored
     }
     // per-group sums of e (A) and of e 2^-(t+1) (Bh): TPP threads per
     // (group, head), each over 32/TPP tokens, then a shuffle reduction
@@ -1567,6 +1575,11 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
       }
     }
     lds_barrier();
+  };
+  for (int chunk = cb; chunk < ce; chunk += 2) {
+    chunk_step(chunk, tA, tB);
+    if (chunk + 1 >= ce) break;
+    chunk_step(chunk + 1, tB, tA);
   }
 
   // ---- column sums per head, open group, partial output of the run ----
