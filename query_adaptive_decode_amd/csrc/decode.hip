@@ -1018,12 +1018,13 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   const double2 p0 = *reinterpret_cast<const double2*>(tp + 2 * min(lane, max(ntile_b - 1, 0)));
   const int ngrp = (int)(Tp / kGroup);
   const double evr = REG ? u.ev[min(tid, max(ngrp - 1, 0))] : 0.0;
+  asm volatile("" ::: "memory");  // keep these two loads ahead of the exponentials'
   float2 e0[RB][GQA];
   if constexpr (REG) {
-    if (nr > 0) {
+    // unconditional (a branch around them would make the compiler's wait
+    // for the tile partials below also wait for all of these)
 #pragma unroll
-      for (int i = 0; i < RB; ++i) load_e(i, e0[i]);
-    }
+    for (int i = 0; i < RB; ++i) load_e(i, e0[i]);
   }
 
   // ---- softmax statistics -> per-tile factors (wave h handles head h) ----
