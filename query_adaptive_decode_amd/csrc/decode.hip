@@ -1372,6 +1372,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
   __shared__ float Ag[NG][GQA], Bg[NG][GQA];
   __shared__ __attribute__((aligned(4))) uint8_t tvs[kChunk];
   __shared__ float fs[GQA];
+  __shared__ __attribute__((aligned(16))) _Float16 ezero[8];  // a zero weight operand
 
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
@@ -1389,6 +1390,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
   }
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const uint8_t* tvu = tv + ((int64_t)b * G + g) * capmax;
+  if (tid < 4) reinterpret_cast<uint32_t*>(ezero)[tid] = 0u;  // read after the first barrier
   const int jl = tid & (kChunk - 1), rh = tid >> 7;  // row loads: token jl, planes rh, rh + 2, ...
 
   // ---- register prefetch of one chunk ----
@@ -1515,8 +1517,12 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
       a = group_sum<TPP>(a);
       bh = group_sum<TPP>(bh);
       if (pr < NP && part == 0) {
-        Ag[pr / GQA][pr % GQA] = a;
-        Bg[pr / GQA][pr % GQA] = bh;
+        // with the tile factor f folded in: f A and f (Bh - 4 A) (the codes
+        // reach the MFMA as 1024 + X, whose 1024 part is f 4 A after the
+        // 1/256 scale)
+        const float f = fs[pr % GQA], fa = f * a;
+        Ag[pr / GQA][pr % GQA] = fa;
+        Bg[pr / GQA][pr % GQA] = fmaf(f, bh, -4.f * fa);
       }
     }
     // ---- un-plane: wave w, step i -> tokens 32 w + 4 i + quarter.  The
@@ -1528,20 +1534,34 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
       const int j0 = 32 * wv + 4 * it;
       const uint32_t t4 = (uint32_t)__builtin_amdgcn_readfirstlane(
           (int)*reinterpret_cast<const uint32_t*>(&tvs[j0]));  // the 4 tokens' depths
-      const uint32_t tmax = max(max(t4 & 0xFFu, (t4 >> 8) & 0xFFu), max((t4 >> 16) & 0xFFu, t4 >> 24));
+      // all four depths <= 4 (depths are <= 8: adding 123 sets bit 7 of a
+      // byte exactly when it is >= 5, with no carry between bytes)
+      const bool shallow = ((t4 + 0x7B7B7B7Bu) & 0x80808080u) == 0u;
       const int j = j0 + q4;
       const long v = tr8_read(reinterpret_cast<const uint8_t*>(rows) + j * 16 + troff);
       const uint2 pb = __builtin_bit_cast(uint2, v);
       uint32_t lo = pb.x, hi = pb.y;
-      if (tmax <= 4u) transpose8_hi4(lo, hi);
+      if (shallow) transpose8_hi4(lo, hi);
       else transpose8_halves(lo, hi);
       *reinterpret_cast<uint2*>(xl + j * XS + 8 * L) = make_uint2(lo, hi);
     }
     lds_barrier();
 
     // ---- MFMA per (16-channel block, column set); wave w: blocks 2w, 2w+1 ----
+    // closed groups of the chunk (a scalar); the weight operand of group gi
+    // is the same for both channel blocks, so it is read once, from a zero
+    // block for the lanes whose column belongs to another group
+    const int ngc = (int)min(max((Tp - c0) / kGroup, (int64_t)0), (int64_t)NG);
     for (int set = 0; set < NSET; ++set) {
       const int gbase = set * GS;
+      f16x8 bvs[GS];
+#pragma unroll
+      for (int gi = 0; gi < GS; ++gi) {
+        const int gl = gbase + gi;
+        const bool mine = colv && gp == gi && gl < NG;
+        const _Float16* src = mine ? &es[hn][kGroup * gl + 8 * kb] : ezero;
+        bvs[gi] = *reinterpret_cast<const f16x8*>(src);
+      }
 #pragma unroll
       for (int bl = 0; bl < 2; ++bl) {
         const int cbk = 16 * (2 * wv + bl);
@@ -1549,7 +1569,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
 #pragma unroll
         for (int gi = 0; gi < GS; ++gi) {
           const int gl = gbase + gi;
-          if (gl >= NG || (gam0 + gl + 1) * kGroup > Tp) continue;
+          if (gl >= ngc) break;
           const int t0 = kGroup * gl + 8 * kb;
           const uint2 xv = __builtin_bit_cast(uint2, tr8_read(xl + (t0 + (m >> 1)) * XS + cbk + 8 * (m & 1)));
           uint32_t ap[4];
@@ -1558,19 +1578,17 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
           ap[2] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04010400u);
           ap[3] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04030402u);
           const f16x8 av = __builtin_bit_cast(f16x8, ap);
-          f16x8 bv = {0, 0, 0, 0, 0, 0, 0, 0};
-          if (colv && gp == gi) bv = *reinterpret_cast<const f16x8*>(&es[hn][t0]);
-          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, D, 0, 0, 0);
+          D = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bvs[gi], D, 0, 0, 0);
         }
         // fold: D row = channel cbk + 4 kb + rr, column m = (gp, hn)
         const int gl = gbase + gp;
-        if (colv && gl < NG && (gam0 + gl + 1) * kGroup <= Tp) {
-          const float A = Ag[gl][hn], Bh = Bg[gl][hn], f = fs[hn];
+        if (colv && gl < ngc) {
+          const float fA = Ag[gl][hn], fB = Bg[gl][hn], fD = fs[hn] * (1.f / 256.f);
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const uint32_t mt = vmeta_s[gl][cbk + 4 * kb + rr];
             const float lo = bf16_to_float(mt & 0xFFFFu), rng = bf16_to_float(mt >> 16);
-            Oacc[bl][rr] = fmaf(f, fmaf(lo, A, rng * (Bh + (D[rr] - 1024.f * A) * (1.f / 256.f))), Oacc[bl][rr]);
+            Oacc[bl][rr] = fmaf(rng, fmaf(D[rr], fD, fB), fmaf(lo, fA, Oacc[bl][rr]));
           }
         }
       }
