@@ -574,6 +574,18 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     const int e = max(emx[0][hh], emx[1][hh]);
     return e > -100000 ? kSigTop - e : 0;
   };
+  // Per block, for the digit build of each slab: this lane's channel
+  // (sorted position 32 s + lane % 32), whether it has depth, and the live
+  // slabs (deepest first, so the live ones come first)
+  int cAs[4];
+  bool liveAs[4];
+  int nslab = 0;
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    cAs[sb] = cperm[32 * sb + (lane & 31)];
+    liveAs[sb] = tks[cAs[sb]] > 0;
+    nslab += tks[cperm[32 * sb]] != 0 ? 1 : 0;
+  }
 
   // staging: piece idx = (slot s, quad q4) -> planes[s][4 q4 .. 4 q4 + 3]
   auto piece = [&](int idx, int64_t gam0, int ngp) -> uint4 {
@@ -721,8 +733,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
 #pragma unroll
       for (int hq = 0; hq < NHQ; ++hq) acc[i][hq][0] = acc[i][hq][1] = i32x4{0, 0, 0, 0};
 #pragma unroll 1
-    for (int slab = 0; slab < 4; ++slab) {
-      if (tks[cperm[32 * slab]] == 0) break;  // deepest first: the rest is depth 0
+    for (int slab = 0; slab < nslab; ++slab) {  // deepest first: the rest is depth 0
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt) {
         // 4 channels of nearly equal depth (sorted positions w + 4 (4 bt + k)).
@@ -758,8 +769,11 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       // digit words of this lane's channel (sorted position c32), heads
       // 4 hq + 2 sA and 4 hq + 2 sA + 1: the chunk of digit half m holds
       // digits 4m .. 4m + 3 of both heads
-      const int cA = cperm[32 * slab + c32];
-      const bool liveA = tks[cA] > 0;
+      int cA = cAs[0];
+      bool liveA = liveAs[0];
+#pragma unroll
+      for (int sb = 1; sb < 4; ++sb)
+        if (slab == sb) { cA = cAs[sb]; liveA = liveAs[sb]; }
       double qa[NHQ][2];
 #pragma unroll
       for (int hq = 0; hq < NHQ; ++hq)
@@ -768,12 +782,16 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
           const int hh = 4 * hq + 2 * sA + e;
           qa[hq][e] = (hh < GQA && liveA) ? qd[min(hh, GQA - 1)][cA] * ldexp_pow2(head_sig(min(hh, GQA - 1))) : 0.0;
         }
+      // the ranges of the wave's groups for this lane's channel, read together
+      uint32_t rmeta[4];
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) rmeta[gi] = meta[4 * wv + gi][cA];
 #pragma unroll
       for (int gi = 0; gi < 4; ++gi) {
         const int gw = 4 * wv + gi;
         if (gw >= ngp) break;
         {
-          const double rng = (double)bf16_to_float(meta[gw][cA] >> 16);
+          const double rng = (double)bf16_to_float(rmeta[gi] >> 16);
 #pragma unroll
           for (int hq = 0; hq < NHQ; ++hq) {
             const uint64_t d0 = dbits(fma(qa[hq][0], rng, kDigitBias)) ^ 0x8080808080808080ull;
