@@ -1649,7 +1649,16 @@ __global__ __launch_bounds__(256) void k_out_reduce(int nrun, int nrun_ws, int64
   const int c = (int)(o - bh * kDim);
   const float* p = opart + bh * nrun_ws * kDim + c;
   float s = 0.f;
-  for (int k = 0; k < nrun; ++k) s += p[(int64_t)k * kDim];
+  int k = 0;
+  // eight loads in flight at a time, summed in run order
+  for (; k + 8 <= nrun; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(int64_t)(k + i) * kDim];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+  }
+  for (; k < nrun; ++k) s += p[(int64_t)k * kDim];
   out[o] = s;
 }
 
