@@ -351,7 +351,7 @@ typedef __attribute__((address_space(3))) i32x2v lds_i32x2v;
 // 2^52 + sum_{k<6} 128 * 2^(8k)
 constexpr double kDigitBias = 4503599627370496.0 + 141289400074368.0;
 constexpr int kSigTop = 46;  // |q rng 2^sig| < 2^46
-constexpr int kStagePre = 8;  // 16 B pieces per thread loaded ahead of the tile
+constexpr int kStagePre = 4;  // 16 B pieces per thread loaded ahead of the tile
 
 __device__ __forceinline__ long tr8_read(const uint8_t* p) {
   const i32x2v v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2v*)p);
@@ -419,12 +419,13 @@ __device__ __forceinline__ double half_sum(double v) {
 }
 
 template <int GQA, int DT>
-__global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const void* q, uint8_t* tk,
+__global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* store, const void* q, uint8_t* tk,
                                                   int H, int G, int W, float RK, int64_t capmax,
                                                   int ntile_ws, float* ebuf, _Float16* e16,
                                                   double* tilepart) {
   constexpr int esize = DT == 0 ? 2 : 4;
-  constexpr int NG = kTile / kGroup;  // 16 groups; wave w owns groups 4w .. 4w + 3
+  constexpr int NG = kTile / kGroup;  // 8 groups; wave w owns groups 2w, 2w + 1
+  static_assert(NG == 8, "a score tile is half of a 16-group key-plane tile");
   constexpr int NHQ = (GQA + 3) / 4;  // head quads: two MFMA row blocks each
   constexpr int CXS = kTile + 16;     // code-tile row stride (bytes)
   constexpr int AOS = 2 * 8 * 2 * 8 + 16;  // digit chunks of a channel octet: [j][set] x 8 B, padded
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   constexpr int AGS = NHQ * 2 * AMS;  // one group's digit chunks
   constexpr int PRE = kStagePre;
   constexpr int MPT = NG * kDim / 256;
-  extern __shared__ __attribute__((aligned(16))) uint32_t planes[];  // [slot][16]
+  extern __shared__ __attribute__((aligned(16))) uint32_t planes[];  // [slot][8]
   __shared__ double qd[GQA][kDim];
   __shared__ uint32_t meta[NG][kDim + 1];
   __shared__ __attribute__((aligned(16))) uint8_t cx[32 * CXS];
@@ -560,7 +561,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   }
   __syncthreads();
   const int ns = offs[kDim];
-  const int nq = ns * 4;  // 16 B pieces per tile
+  const int nq = ns * 2;  // 16 B pieces per tile
   // scalar table: lane 8 s + i of wave w describes the channel at sorted
   // position 32 s + w + 4 i (depth | first slot << 8; slot 0 when depth 0)
   uint32_t cinf = 0;
@@ -587,36 +588,42 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     nslab += tks[cperm[32 * sb]] != 0 ? 1 : 0;
   }
 
-  // staging: piece idx = (slot s, quad q4) -> planes[s][4 q4 .. 4 q4 + 3]
-  auto piece = [&](int idx, int64_t gam0, int ngp) -> uint4 {
+  // Staging.  A score tile is half (h = tile & 1) of a 16-group key-plane
+  // tile: its segment of a chosen line (channel c, plane p) is words
+  // 8 h .. 8 h + 7 of the line's 16.  Piece idx = (slot s, half q2) is
+  // words 4 q2 .. 4 q2 + 3 of it -> planes[s][4 q2 .. 4 q2 + 3].
+  auto seg_base = [&](int tile) -> const uint32_t* {
+    return u.kplanes + (int64_t)(tile >> 1) * kDim * W * 16 + 8 * (tile & 1);
+  };
+  auto piece = [&](int idx, int tile, int ngp) -> uint4 {
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    const int s = idx >> 2, q4 = idx & 3;
+    const int s = idx >> 1, q2 = idx & 1;
     const int c = s2c[s];
     const int p = s - offs[c];
-    if (4 * q4 < ngp)
-      v = *reinterpret_cast<const uint4*>(u.kplanes + (((gam0 >> 4) * kDim + c) * W + p) * 16 + 4 * q4);
+    if (4 * q2 < ngp) v = *reinterpret_cast<const uint4*>(seg_base(tile) + (c * W + p) * 16 + 4 * q2);
     return v;
   };
-  // Piece k of this thread is idx = k * 256 + tid.  Its byte offset in a
-  // tile's plane block and its place in LDS do not depend on the tile, so
-  // both are set up once; the tile is the scalar base of a buffer (pieces
-  // past the chosen lines take an offset outside it and read as zeros, and
-  // the groups of a partial tile past the closed ones are read but unused).
+  // Piece k of this thread is idx = k * 256 + tid.  Its byte offset from a
+  // tile's segment base and its place in LDS do not depend on the tile, so
+  // both are set up once; the segment base is the scalar base of a buffer
+  // (pieces past the chosen lines take an offset outside it and read as
+  // zeros, and the groups of a partial tile past the closed ones are read
+  // but unused).
   uint32_t poff[PRE];
 #pragma unroll
   for (int k = 0; k < PRE; ++k) {
     const int idx = k * 256 + tid;
     int o = kBufOff;
     if (idx < nq) {
-      const int s = idx >> 2, c = s2c[s], p = s - offs[c];
-      o = ((c * W + p) * 16 + 4 * (idx & 3)) * 4;
+      const int s = idx >> 1, c = s2c[s], p = s - offs[c];
+      o = ((c * W + p) * 16 + 4 * (idx & 1)) * 4;
     }
     poff[k] = (uint32_t)o;
   }
   uint4 pre[PRE];
   auto load_pieces = [&](int tile) {
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        u.kplanes + (int64_t)tile * kDim * W * 16, (short)0, kDim * W * 64, kBufWord3);
+        const_cast<uint32_t*>(seg_base(tile)), (short)0, kDim * W * 64 - 32 * (tile & 1), kBufWord3);
 #pragma unroll
     for (int k = 0; k < PRE; ++k) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)poff[k], 0, 0);
@@ -627,37 +634,24 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     load_pieces(tile);
     load_meta(tile);
   };
-  // 8-byte chunk k of staged slot s sits at chunk k ^ (s & 7): the 8 slots
-  // one transposing read touches (the planes of a channel) then fall on
-  // distinct LDS banks
+  // slot s is 32 B at planes + 32 s; piece k of this thread sits in slot
+  // 128 k + tid / 2
   auto stage_put = [&](int idx, uint4 v) __attribute__((always_inline)) {
-    const int sl = idx >> 2, x = sl & 7;
-    if (x & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-    *reinterpret_cast<uint4*>(planes + (sl * 4 + ((idx & 3) ^ (x >> 1))) * 4) = v;
+    *reinterpret_cast<uint4*>(planes + (idx >> 1) * 8 + (idx & 1) * 4) = v;
   };
-  // piece k sits in slot 64 k + tid / 4, so the slot's chunk swizzle is
-  // the same for every k: two 8-byte writes at fixed offsets
-  const int sl0 = tid >> 2, x0 = sl0 & 7, q40 = tid & 3;
-  uint8_t* const pl_lo = reinterpret_cast<uint8_t*>(planes) + sl0 * 64 + (((2 * q40) ^ x0) << 3);
-  uint8_t* const pl_hi = reinterpret_cast<uint8_t*>(planes) + sl0 * 64 + (((2 * q40 + 1) ^ x0) << 3);
+  uint8_t* const pl0 = reinterpret_cast<uint8_t*>(planes) + (tid >> 1) * 32 + (tid & 1) * 16;
   auto store_ahead = [&](int tile) {
 #pragma unroll
-    for (int k = 0; k < PRE; ++k) {
-      if (k * 256 + tid < nq) {
-        *reinterpret_cast<uint2*>(pl_lo + k * 4096) = make_uint2(pre[k].x, pre[k].y);
-        *reinterpret_cast<uint2*>(pl_hi + k * 4096) = make_uint2(pre[k].z, pre[k].w);
-      }
-    }
+    for (int k = 0; k < PRE; ++k)
+      if (k * 256 + tid < nq) *reinterpret_cast<uint4*>(pl0 + k * 4096) = pre[k];
 #pragma unroll
     for (int k = 0; k < MPT; ++k) {
       const int i = k * 256 + tid;
       meta[i / kDim][i % kDim] = pmeta[k];
     }
     // pieces past the prefetched ones (deep reads only)
-    const int64_t gam0 = (int64_t)tile * NG;
     const int ngp = tile_ngp(tile);
-    for (int idx = PRE * 256 + tid; idx < nq; idx += 256)
-      stage_put(idx, piece(idx, gam0, ngp));
+    for (int idx = PRE * 256 + tid; idx < nq; idx += 256) stage_put(idx, piece(idx, tile, ngp));
   };
   load_pieces(tile_begin);  // the first tile's metadata is already in flight
   store_ahead(tile_begin);
@@ -668,10 +662,13 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
   if (tile_begin + 1 < tile_end) load_ahead(tile_begin + 1);
 
   const int kq = lane >> 4, jj = (lane & 15) >> 1, ss = lane & 1;
-  // transposing plane read: lane 2j + s of quarter q addresses plane 7 - j,
-  // groups 4q + 2s and 4q + 2s + 1 (8-byte chunk 2q + s, swizzled as
-  // staged); lane o then holds the plane bytes of octet o
-  const int c8 = 2 * kq + ss;
+  // transposing plane read of two channels: the half-wave hw = lane / 32
+  // takes one; lane 2j + s of its quarter q2 = (lane / 16) % 2 addresses
+  // plane 7 - j, groups 4 q2 + 2 s and 4 q2 + 2 s + 1 (8-byte chunk
+  // 2 q2 + s of the 32-byte slot); lane o of the half-wave then holds the
+  // plane bytes of octet o (tokens 8 o .. 8 o + 7 of the tile)
+  const int hw = lane >> 5;
+  const int c8 = 2 * (kq & 1) + ss;
   // digit chunk (channel octet co, channel j, set s) of block (hq, half m)
   auto achunk = [&](int hq, int m, int co, int j, int s) -> int {
     return (2 * hq + m) * AMS + co * AOS + (2 * j + s) * 8;
@@ -693,7 +690,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const int c = 32 * wv + 4 * st + kk;
-        const uint32_t m = meta[gA][c];
+        const uint32_t m = gA < NG ? meta[gA][c] : 0u;
         const double lo = (double)bf16_to_float(m & 0xFFFFu);
         const double rng = (double)bf16_to_float(m >> 16);
         const double base = fma(rng, kap[c], lo);
@@ -702,7 +699,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       }
       if (gA < GQA)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Cpart[wv][4 * i + kk][gA] = cd[i];
+        for (int i = 0; i < NG / 4; ++i) Cpart[wv][4 * i + kk][gA] = cd[i];
     }
     const int64_t ntail = len - Tp;
     const bool tail_here = ntail > 0 && Tp >= t0 && Tp < t0 + kTile;
@@ -727,43 +724,42 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     lds_barrier();  // constants and open-group logits (the slab loop may not run)
 
     // ---- un-plane + int8 MFMA, one 32-channel slab at a time ----
-    i32x4 acc[8][NHQ][2];
+    i32x4 acc[4][NHQ][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int hq = 0; hq < NHQ; ++hq) acc[i][hq][0] = acc[i][hq][1] = i32x4{0, 0, 0, 0};
 #pragma unroll 1
     for (int slab = 0; slab < nslab; ++slab) {  // deepest first: the rest is depth 0
+      // The wave's 8 channels of the slab (sorted positions w + 4 k, nearly
+      // equal depth) in pairs (2 r, 2 r + 1): one transposing LDS read per
+      // pair gives lane o of half-wave hw the 8 plane bytes of octet o of
+      // channel 2 r + hw (plane p in byte 7 - p; planes past the depth are
+      // read from the padding and masked).
+      uint2 pb[4];
+      int tpr[4], tmx[4];
 #pragma unroll
-      for (int bt = 0; bt < 2; ++bt) {
-        // 4 channels of nearly equal depth (sorted positions w + 4 (4 bt + k)).
-        // One transposing LDS read per channel gives lane o the 8 plane
-        // bytes of its octet o (plane p in byte 7 - p; planes past the depth
-        // are read from the padding and masked).
-        int tk4[4], tmax = 0;
-        uint2 pb[4];
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t infA = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 2 * r);
+        const uint32_t infB = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 2 * r + 1);
+        tmx[r] = max((int)(infA & 0xFFu), (int)(infB & 0xFFu));
+        const uint32_t inf = hw ? infB : infA;
+        tpr[r] = (int)(inf & 0xFFu);
+        const int sl = (int)(inf >> 8) + 7 - jj;
+        pb[r] = __builtin_bit_cast(uint2, tr8_read(reinterpret_cast<const uint8_t*>(planes) + sl * 32 + (c8 << 3)));
+      }
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const uint32_t inf = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 4 * bt + k);
-          tk4[k] = (int)(inf & 0xFFu);
-          tmax = max(tmax, tk4[k]);
-          const int sl = (int)(inf >> 8) + 7 - jj;
-          const long v = tr8_read(reinterpret_cast<const uint8_t*>(planes) + sl * 64 + ((c8 ^ (sl & 7)) << 3));
-          pb[k] = __builtin_bit_cast(uint2, v);
-        }
-        if (tmax == 0) continue;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int t = tk4[k];
-          // keep bytes 7 .. 8 - t (planes 0 .. t - 1)
-          const uint64_t keep = t >= 8 ? ~0ull : (t <= 0 ? 0ull : ~0ull << (64 - 8 * t));
-          uint32_t lo = pb[k].x & (uint32_t)keep;
-          uint32_t hi = (pb[k].y & (uint32_t)(keep >> 32)) ^ 0xFF000000u;
-          if (tmax <= 4) transpose8_hi4(lo, hi);
-          else transpose8_halves(lo, hi);
-          const int cl = wv + 4 * (4 * bt + k);
-          *reinterpret_cast<uint2*>(cx + cl * CXS + 8 * lane) = make_uint2(lo, hi);
-        }
+      for (int r = 0; r < 4; ++r) {
+        if (tmx[r] == 0) continue;  // both depth 0: their codes meet zero digits
+        const int t = tpr[r];
+        // keep bytes 7 .. 8 - t (planes 0 .. t - 1)
+        const uint64_t keep = t >= 8 ? ~0ull : (t <= 0 ? 0ull : ~0ull << (64 - 8 * t));
+        uint32_t lo = pb[r].x & (uint32_t)keep;
+        uint32_t hi = (pb[r].y & (uint32_t)(keep >> 32)) ^ 0xFF000000u;
+        if (tmx[r] <= 4) transpose8_hi4(lo, hi);
+        else transpose8_halves(lo, hi);
+        const int cl = wv + 4 * (2 * r + hw);
+        *reinterpret_cast<uint2*>(cx + cl * CXS + 8 * (lane & 31)) = make_uint2(lo, hi);
       }
       lds_barrier();
       // digit words of this lane's channel (sorted position c32), heads
@@ -783,12 +779,12 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
           qa[hq][e] = (hh < GQA && liveA) ? qd[min(hh, GQA - 1)][cA] * ldexp_pow2(head_sig(min(hh, GQA - 1))) : 0.0;
         }
       // the ranges of the wave's groups for this lane's channel, read together
-      uint32_t rmeta[4];
+      uint32_t rmeta[2];
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) rmeta[gi] = meta[4 * wv + gi][cA];
+      for (int gi = 0; gi < 2; ++gi) rmeta[gi] = meta[2 * wv + gi][cA];
 #pragma unroll
-      for (int gi = 0; gi < 4; ++gi) {
-        const int gw = 4 * wv + gi;
+      for (int gi = 0; gi < 2; ++gi) {
+        const int gw = 2 * wv + gi;
         if (gw >= ngp) break;
         {
           const double rng = (double)bf16_to_float(rmeta[gi] >> 16);
@@ -811,7 +807,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
 #pragma unroll
         for (int tl = 0; tl < 2; ++tl) {
           const int tb = 2 * gi + tl;         // the wave's token block
-          const int oct = 2 * (8 * wv + tb);  // first octet of the block
+          const int oct = 2 * (4 * wv + tb);  // first octet of the block
           const long Bv = tr8_read(cx + (8 * kq + jj) * CXS + 8 * (oct + ss));
 #pragma unroll
           for (int hq = 0; hq < NHQ; ++hq)
@@ -827,20 +823,20 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     if (more) store_ahead(tile + 1);
     if (tile + 2 < tile_end) load_ahead(tile + 2);
 
-    // ---- logits in registers: lane -> (token 16 (8 w + tb) + lane % 16,
+    // ---- logits in registers: lane -> (token 16 (4 w + tb) + lane % 16,
     // head 4 hq + lane / 16); its digits sit in its own accumulators ----
     const int toff = (int)(Tp - t0);  // tile-local first open-group token (if here)
     const int hl = lane >> 4;
-    double sv[8][NHQ];
+    double sv[4][NHQ];
 #pragma unroll
     for (int hq = 0; hq < NHQ; ++hq) {
       const int hh = 4 * hq + hl;
       const int hc = min(hh, GQA - 1);
       const int sg = head_sig(hc);
 #pragma unroll
-      for (int tb = 0; tb < 8; ++tb) {
-        const int gw = 4 * wv + (tb >> 1);
-        const int tok = 16 * (8 * wv + tb) + (lane & 15);
+      for (int tb = 0; tb < 4; ++tb) {
+        const int gw = 2 * wv + (tb >> 1);
+        const int tok = 16 * (4 * wv + tb) + (lane & 15);
         double s = -INFINITY;
         if (hh < GQA) {
           if (gw < ngp) {
@@ -863,7 +859,7 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
     for (int hq = 0; hq < NHQ; ++hq) {
       double m = sv[0][hq];
 #pragma unroll
-      for (int tb = 1; tb < 8; ++tb) m = fmax(m, sv[tb][hq]);
+      for (int tb = 1; tb < 4; ++tb) m = fmax(m, sv[tb][hq]);
       m = row_reduce(m, [](double a, double c) { return fmax(a, c); });
       const int hh = 4 * hq + hl;
       if ((lane & 15) == 0 && hh < GQA) redm[wv][hh] = m;
@@ -874,12 +870,12 @@ __global__ __launch_bounds__(256, 2) void k_score(const uint8_t* store, const vo
       const int hh = 4 * hq + hl;
       const int hc = min(hh, GQA - 1);
       const double mt = fmax(fmax(redm[0][hc], redm[1][hc]), fmax(redm[2][hc], redm[3][hc]));
-      const int64_t lane0 = ((int64_t)b * H + (int64_t)g * GQA + hc) * capmax + t0 + 128 * wv + (lane & 15);
+      const int64_t lane0 = ((int64_t)b * H + (int64_t)g * GQA + hc) * capmax + t0 + 64 * wv + (lane & 15);
       float* const ep = ebuf + lane0;
       _Float16* const hp = e16 + lane0;
       double z = 0.0;
 #pragma unroll
-      for (int tb = 0; tb < 8; ++tb) {
+      for (int tb = 0; tb < 4; ++tb) {
         const double e = exp_nonpos(sv[tb][hq] - mt);
         if (sv[tb][hq] > -INFINITY) {
           ep[16 * tb] = (float)e;
@@ -1688,25 +1684,25 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   const int esize = DT == 0 ? 2 : 4;
 
   mark(a, 0, st);
-  // slots staged per score tile: at most min(B_K, 128 W) chosen key lines,
-  // 64 B each
+  // slots staged per score tile: at most min(B_K, 128 W) chosen key-line
+  // segments, 32 B each
   double bk = floor((double)a.RK * (double)kDim);
   if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
   if (bk < 0.0) bk = 0.0;
   // (+8 slots: un-plane reads of a batch may run past a shallower channel's
   // last slot; those words are masked)
-  size_t dyn = ((size_t)bk + 8) * 64;
+  size_t dyn = ((size_t)bk + 8) * 32;
   if (dyn < (size_t)(2 * 64 * 8) * 12) dyn = (size_t)(2 * 64 * 8) * 12;  // key-allocation scratch
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GQA, DT>),
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (kDim * 8 + 8) * 64);
+                        hipFuncAttributeMaxDynamicSharedMemorySize, (kDim * 8 + 8) * 32);
     attr_set = true;
   }
-  // each unit's tiles split evenly over nrun blocks: about two blocks per
-  // compute unit in all
+  // each unit's tiles split evenly over nrun blocks: about three blocks per
+  // compute unit in all (two for more than 4 query heads per KV head)
   const int64_t total_tiles = (int64_t)a.B * a.G * L.ntile;
-  const int64_t slots = 2 * (int64_t)device_cu_count();
+  const int64_t slots = (GQA <= 4 ? 3 : 2) * (int64_t)device_cu_count();
   int run = (int)((total_tiles + slots - 1) / slots);
   if (run < 1) run = 1;
   const int nrun = (L.ntile + run - 1) / run;

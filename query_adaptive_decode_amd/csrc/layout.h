@@ -39,8 +39,9 @@ constexpr uint32_t kMagic = 0x52564B31u;
 constexpr uint32_t kVersion = 1u;
 constexpr int kGroup = 32;      // tokens per quantiser group
 constexpr int kDim = 128;       // head_dim supported by the kernels
-constexpr int kTile = 512;      // tokens per score workgroup (16 groups);
-                                // also the softmax split-context unit
+constexpr int kTile = 256;      // tokens per score tile (8 groups, half of a
+                                // key-plane tile); also the softmax
+                                // split-context unit
 constexpr int kChunk = 128;     // tokens per value-gather step (4 groups)
 
 struct StoreHeader {          // first 256 bytes of a store
