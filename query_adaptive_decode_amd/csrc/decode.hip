@@ -729,31 +729,35 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int hq = 0; hq < NHQ; ++hq) acc[i][hq][0] = acc[i][hq][1] = i32x4{0, 0, 0, 0};
-#pragma unroll 1
-    for (int slab = 0; slab < nslab; ++slab) {  // deepest first: the rest is depth 0
+#pragma unroll
+    for (int slab = 0; slab < 4; ++slab) {
+      if (slab >= nslab) break;  // deepest first: the rest is depth 0
       // The wave's 8 channels of the slab (sorted positions w + 4 k, nearly
       // equal depth) in pairs (2 r, 2 r + 1): one transposing LDS read per
       // pair gives lane o of half-wave hw the 8 plane bytes of octet o of
       // channel 2 r + hw (plane p in byte 7 - p; planes past the depth are
       // read from the padding and masked).
+      // keep bytes 7 .. 8 - t (planes 0 .. t - 1), from a scalar depth
+      auto keep_of = [](uint32_t t) -> uint64_t {
+        return t >= 8u ? ~0ull : (t == 0u ? 0ull : ~0ull << (64u - 8u * t));
+      };
       uint2 pb[4];
-      int tpr[4], tmx[4];
+      uint64_t kp[4];
+      int tmx[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const uint32_t infA = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 2 * r);
         const uint32_t infB = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 2 * r + 1);
-        tmx[r] = max((int)(infA & 0xFFu), (int)(infB & 0xFFu));
-        const uint32_t inf = hw ? infB : infA;
-        tpr[r] = (int)(inf & 0xFFu);
-        const int sl = (int)(inf >> 8) + 7 - jj;
+        tmx[r] = (int)max(infA & 0xFFu, infB & 0xFFu);
+        const uint64_t kA = keep_of(infA & 0xFFu), kB = keep_of(infB & 0xFFu);
+        kp[r] = hw ? kB : kA;
+        const int sl = (int)((hw ? infB : infA) >> 8) + 7 - jj;
         pb[r] = __builtin_bit_cast(uint2, tr8_read(reinterpret_cast<const uint8_t*>(planes) + sl * 32 + (c8 << 3)));
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         if (tmx[r] == 0) continue;  // both depth 0: their codes meet zero digits
-        const int t = tpr[r];
-        // keep bytes 7 .. 8 - t (planes 0 .. t - 1)
-        const uint64_t keep = t >= 8 ? ~0ull : (t <= 0 ? 0ull : ~0ull << (64 - 8 * t));
+        const uint64_t keep = kp[r];
         uint32_t lo = pb[r].x & (uint32_t)keep;
         uint32_t hi = (pb[r].y & (uint32_t)(keep >> 32)) ^ 0xFF000000u;
         if (tmx[r] <= 4) transpose8_hi4(lo, hi);
@@ -765,11 +769,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
       // digit words of this lane's channel (sorted position c32), heads
       // 4 hq + 2 sA and 4 hq + 2 sA + 1: the chunk of digit half m holds
       // digits 4m .. 4m + 3 of both heads
-      int cA = cAs[0];
-      bool liveA = liveAs[0];
-#pragma unroll
-      for (int sb = 1; sb < 4; ++sb)
-        if (slab == sb) { cA = cAs[sb]; liveA = liveAs[sb]; }
+      const int cA = cAs[slab];
+      const bool liveA = liveAs[slab];
       double qa[NHQ][2];
 #pragma unroll
       for (int hq = 0; hq < NHQ; ++hq)
