@@ -579,13 +579,20 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // (sorted position 32 s + lane % 32), whether it has depth, and the live
   // slabs (deepest first, so the live ones come first)
   int cAs[4];
-  bool liveAs[4];
   int nslab = 0;
+  double qas[4][NHQ][2];  // q 2^sig of the lane's channel and two heads, per slab
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
     cAs[sb] = cperm[32 * sb + (lane & 31)];
-    liveAs[sb] = tks[cAs[sb]] > 0;
+    const bool live = tks[cAs[sb]] > 0;
     nslab += tks[cperm[32 * sb]] != 0 ? 1 : 0;
+#pragma unroll
+    for (int hq = 0; hq < NHQ; ++hq)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int hh = 4 * hq + 2 * (lane >> 5) + e;
+        qas[sb][hq][e] = (hh < GQA && live) ? qd[min(hh, GQA - 1)][cAs[sb]] * ldexp_pow2(head_sig(min(hh, GQA - 1))) : 0.0;
+      }
   }
 
   // Staging.  A score tile is half (h = tile & 1) of a 16-group key-plane
@@ -770,15 +777,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
       // 4 hq + 2 sA and 4 hq + 2 sA + 1: the chunk of digit half m holds
       // digits 4m .. 4m + 3 of both heads
       const int cA = cAs[slab];
-      const bool liveA = liveAs[slab];
-      double qa[NHQ][2];
-#pragma unroll
-      for (int hq = 0; hq < NHQ; ++hq)
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int hh = 4 * hq + 2 * sA + e;
-          qa[hq][e] = (hh < GQA && liveA) ? qd[min(hh, GQA - 1)][cA] * ldexp_pow2(head_sig(min(hh, GQA - 1))) : 0.0;
-        }
+      const double (&qa)[NHQ][2] = qas[slab];
       // the ranges of the wave's groups for this lane's channel, read together
       uint32_t rmeta[2];
 #pragma unroll
