@@ -580,6 +580,18 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // slabs (deepest first, so the live ones come first)
   int cAs[4];
   int nslab = 0;
+  // the per-group constants' query operand (head lane % 16, channel
+  // 32 w + 4 st + lane / 16) for the 8 steps
+  double qbs[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const int gA = lane & 15, c = 32 * wv + 4 * st + (lane >> 4);
+    qbs[st] = gA < GQA ? qd[min(gA, GQA - 1)][c] : 0.0;
+  }
+  // the logit scale exponent -(sig + 8) of the lane's epilogue head per head quad
+  int lsg[NHQ];
+#pragma unroll
+  for (int hq = 0; hq < NHQ; ++hq) lsg[hq] = -head_sig(min(4 * hq + (lane >> 4), GQA - 1)) - 8;
   double qas[4][NHQ][2];  // q 2^sig of the lane's channel and two heads, per slab
 #pragma unroll
   for (int sb = 0; sb < 4; ++sb) {
@@ -701,8 +713,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
         const double lo = (double)bf16_to_float(m & 0xFFFFu);
         const double rng = (double)bf16_to_float(m >> 16);
         const double base = fma(rng, kap[c], lo);
-        const double qb = gA < GQA ? qd[min(gA, GQA - 1)][c] : 0.0;
-        cd = __builtin_amdgcn_mfma_f64_16x16x4f64(base, qb, cd, 0, 0, 0);
+        cd = __builtin_amdgcn_mfma_f64_16x16x4f64(base, qbs[st], cd, 0, 0, 0);
       }
       if (gA < GQA)
 #pragma unroll
@@ -832,7 +843,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     for (int hq = 0; hq < NHQ; ++hq) {
       const int hh = 4 * hq + hl;
       const int hc = min(hh, GQA - 1);
-      const int sg = head_sig(hc);
+
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const int gw = 2 * wv + (tb >> 1);
@@ -846,7 +857,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
             const int p01 = d0[0] + d0[1] * 256, p23 = d0[2] + d0[3] * 256, p45 = d1[0] + d1[1] * 256;
             const double P = fma((double)p45, 0x1p32, fma((double)p23, 0x1p16, (double)p01));
             const double C = (Cpart[0][gw][hc] + Cpart[1][gw][hc]) + (Cpart[2][gw][hc] + Cpart[3][gw][hc]);
-            s = (C + ldexp(P, -sg - 8)) * kInvSqrtD;
+            s = (C + ldexp(P, lsg[hq])) * kInvSqrtD;
           } else if (tail_here && tok >= toff && tok < toff + ntail) {
             s = tails[tok - toff][hc];
           }
