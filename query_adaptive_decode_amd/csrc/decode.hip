@@ -454,10 +454,12 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
   const int ntl = (int)((len + kTile - 1) / kTile);
-  // this block's share of the unit's tiles: an even split over gridDim.y
-  const int tile_begin = (int)(((int64_t)blockIdx.y * ntl) / gridDim.y);
-  const int tile_end = (int)(((int64_t)(blockIdx.y + 1) * ntl) / gridDim.y);
-  if (tile_begin >= tile_end) {
+  // this block's share of the unit's tiles: every ny-th one from y, so that
+  // the blocks of a unit (all on one XCD) work on neighbouring tiles at the
+  // same time and the two halves of a key-plane tile meet in its L2
+  const int ny = (int)gridDim.y;
+  const int tile_begin = (int)blockIdx.y;
+  if (tile_begin >= ntl) {
     // an empty request has no closed group (E^K = 0): all key depths are 0
     if (ntl == 0 && blockIdx.y == 0 && threadIdx.x < kDim) tk[((int64_t)b * G + g) * kDim + threadIdx.x] = 0;
     return;
@@ -511,7 +513,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
                     reinterpret_cast<uint32_t*>(planes) + 2 * 2 * 64 * 8, sel);
     tks[lane] = (uint8_t)sel[0];
     tks[lane + 64] = (uint8_t)sel[1];
-    if (tile_begin == 0) {  // the unit's first non-empty run writes the depths out
+    if (tile_begin == 0) {  // the unit's first block writes the depths out
       tk[((int64_t)b * G + g) * kDim + lane] = (uint8_t)sel[0];
       tk[((int64_t)b * G + g) * kDim + lane + 64] = (uint8_t)sel[1];
     }
@@ -678,7 +680,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // the register prefetch runs one tile ahead; it is issued right after the
   // previous staging write, before the epilogue's global stores, so that no
   // wait on those stores delays it
-  if (tile_begin + 1 < tile_end) load_ahead(tile_begin + 1);
+  if (tile_begin + ny < ntl) load_ahead(tile_begin + ny);
 
   const int kq = lane >> 4, jj = (lane & 15) >> 1, ss = lane & 1;
   // transposing plane read of two channels: the half-wave hw = lane / 32
@@ -694,10 +696,10 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   };
   const int c32 = lane & 31, sA = lane >> 5;  // A-build: channel, head pair of the quad
 
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
+  for (int tile = tile_begin; tile < ntl; tile += ny) {
     const int64_t t0 = (int64_t)tile * kTile;
     const int ngp = tile_ngp(tile);
-    const bool more = tile + 1 < tile_end;
+    const bool more = tile + ny < ntl;
 
     // ---- per-group constants C[g][h] = sum_c base[g][c] q[h][c] on the fp64
     // matrix cores: wave w contracts its 32 channels in 8 steps of 4 (A:
@@ -831,8 +833,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
       lds_barrier();
     }
     // the staged planes and metadata of this tile are dead: next tile in
-    if (more) store_ahead(tile + 1);
-    if (tile + 2 < tile_end) load_ahead(tile + 2);
+    if (more) store_ahead(tile + ny);
+    if (tile + 2 * ny < ntl) load_ahead(tile + 2 * ny);
 
     // ---- logits in registers: lane -> (token 16 (4 w + tb) + lane % 16,
     // head 4 hq + lane / 16); its digits sit in its own accumulators ----
