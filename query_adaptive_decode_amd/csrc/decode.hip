@@ -564,51 +564,6 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   __syncthreads();
   const int ns = offs[kDim];
   const int nq = ns * 2;  // 16 B pieces per tile
-  // scalar table: lane 8 s + i of wave w describes the channel at sorted
-  // position 32 s + w + 4 i (depth | first slot << 8; slot 0 when depth 0)
-  uint32_t cinf = 0;
-  if (lane < 32) {
-    const int c = cperm[32 * (lane >> 3) + wv + 4 * (lane & 7)];
-    const uint32_t t = tks[c];
-    cinf = t | ((t ? (uint32_t)offs[c] : 0u) << 8);
-  }
-  // digit scale 2^sig of head h: lane quad q of head quad hq is head 4 hq + q
-  auto head_sig = [&](int hh) -> int {
-    const int e = max(emx[0][hh], emx[1][hh]);
-    return e > -100000 ? kSigTop - e : 0;
-  };
-  // Per block, for the digit build of each slab: this lane's channel
-  // (sorted position 32 s + lane % 32), whether it has depth, and the live
-  // slabs (deepest first, so the live ones come first)
-  int cAs[4];
-  int nslab = 0;
-  // the per-group constants' query operand (head lane % 16, channel
-  // 32 w + 4 st + lane / 16) for the 8 steps
-  double qbs[8];
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const int gA = lane & 15, c = 32 * wv + 4 * st + (lane >> 4);
-    qbs[st] = gA < GQA ? qd[min(gA, GQA - 1)][c] : 0.0;
-  }
-  // the logit scale exponent -(sig + 8) of the lane's epilogue head per head quad
-  int lsg[NHQ];
-#pragma unroll
-  for (int hq = 0; hq < NHQ; ++hq) lsg[hq] = -head_sig(min(4 * hq + (lane >> 4), GQA - 1)) - 8;
-  double qas[4][NHQ][2];  // q 2^sig of the lane's channel and two heads, per slab
-#pragma unroll
-  for (int sb = 0; sb < 4; ++sb) {
-    cAs[sb] = cperm[32 * sb + (lane & 31)];
-    const bool live = tks[cAs[sb]] > 0;
-    nslab += tks[cperm[32 * sb]] != 0 ? 1 : 0;
-#pragma unroll
-    for (int hq = 0; hq < NHQ; ++hq)
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int hh = 4 * hq + 2 * (lane >> 5) + e;
-        qas[sb][hq][e] = (hh < GQA && live) ? qd[min(hh, GQA - 1)][cAs[sb]] * ldexp_pow2(head_sig(min(hh, GQA - 1))) : 0.0;
-      }
-  }
-
   // Staging.  A score tile is half (h = tile & 1) of a 16-group key-plane
   // tile: its segment of a chosen line (channel c, plane p) is words
   // 8 h .. 8 h + 7 of the line's 16.  Piece idx = (slot s, half q2) is
@@ -674,7 +629,54 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     const int ngp = tile_ngp(tile);
     for (int idx = PRE * 256 + tid; idx < nq; idx += 256) stage_put(idx, piece(idx, tile, ngp));
   };
-  load_pieces(tile_begin);  // the first tile's metadata is already in flight
+  // the first tile's pieces go out as soon as the slot table is known (its
+  // metadata is already in flight); the per-block set-up below overlaps them
+  load_pieces(tile_begin);
+  // scalar table: lane 8 s + i of wave w describes the channel at sorted
+  // position 32 s + w + 4 i (depth | first slot << 8; slot 0 when depth 0)
+  uint32_t cinf = 0;
+  if (lane < 32) {
+    const int c = cperm[32 * (lane >> 3) + wv + 4 * (lane & 7)];
+    const uint32_t t = tks[c];
+    cinf = t | ((t ? (uint32_t)offs[c] : 0u) << 8);
+  }
+  // digit scale 2^sig of head h: lane quad q of head quad hq is head 4 hq + q
+  auto head_sig = [&](int hh) -> int {
+    const int e = max(emx[0][hh], emx[1][hh]);
+    return e > -100000 ? kSigTop - e : 0;
+  };
+  // Per block, for the digit build of each slab: this lane's channel
+  // (sorted position 32 s + lane % 32), whether it has depth, and the live
+  // slabs (deepest first, so the live ones come first)
+  int cAs[4];
+  int nslab = 0;
+  // the per-group constants' query operand (head lane % 16, channel
+  // 32 w + 4 st + lane / 16) for the 8 steps
+  double qbs[8];
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    const int gA = lane & 15, c = 32 * wv + 4 * st + (lane >> 4);
+    qbs[st] = gA < GQA ? qd[min(gA, GQA - 1)][c] : 0.0;
+  }
+  // the logit scale exponent -(sig + 8) of the lane's epilogue head per head quad
+  int lsg[NHQ];
+#pragma unroll
+  for (int hq = 0; hq < NHQ; ++hq) lsg[hq] = -head_sig(min(4 * hq + (lane >> 4), GQA - 1)) - 8;
+  double qas[4][NHQ][2];  // q 2^sig of the lane's channel and two heads, per slab
+#pragma unroll
+  for (int sb = 0; sb < 4; ++sb) {
+    cAs[sb] = cperm[32 * sb + (lane & 31)];
+    const bool live = tks[cAs[sb]] > 0;
+    nslab += tks[cperm[32 * sb]] != 0 ? 1 : 0;
+#pragma unroll
+    for (int hq = 0; hq < NHQ; ++hq)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int hh = 4 * hq + 2 * (lane >> 5) + e;
+        qas[sb][hq][e] = (hh < GQA && live) ? qd[min(hh, GQA - 1)][cAs[sb]] * ldexp_pow2(head_sig(min(hh, GQA - 1))) : 0.0;
+      }
+  }
+
   store_ahead(tile_begin);
   __syncthreads();
   // the register prefetch runs one tile ahead; it is issued right after the
