@@ -35,20 +35,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr double kInvSqrtD = 0.088388347648318440550;  // 1/sqrt(128)
 
-// byte `ob` of each of 8 plane words (plane p -> byte 7-p of hi:lo), then
-// the 8x8 bit transpose: byte i of hi:lo becomes element 8*ob+i's code
-// prefix, MSB-first (missing planes must be passed as zero words)
-__device__ __forceinline__ void unplane8(const uint32_t (&w)[8], uint32_t sel, uint32_t& lo,
-                                         uint32_t& hi) {
-  const uint32_t r01 = __builtin_amdgcn_perm(w[0], w[1], sel);
-  const uint32_t r23 = __builtin_amdgcn_perm(w[2], w[3], sel);
-  const uint32_t r45 = __builtin_amdgcn_perm(w[4], w[5], sel);
-  const uint32_t r67 = __builtin_amdgcn_perm(w[6], w[7], sel);
-  hi = __builtin_amdgcn_perm(r01, r23, 0x05040100u);
-  lo = __builtin_amdgcn_perm(r45, r67, 0x05040100u);
-  transpose8_halves(lo, hi);
-}
-
 // ---------------------------------------------------------------------------
 // Key allocation: one wave per (request, KV head).  Lane l holds channels l
 // and l+64 and their W candidate gains w_c 4^-t (t = 1..W).  The B_K largest
@@ -281,8 +267,9 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
 }
 
 // ---------------------------------------------------------------------------
-// Score: a block of 256 threads takes a run of consecutive 512-token tiles
-// (16 groups each) of one (request, KV head).  The logit of token j and
+// Score: a block of 256 threads takes every ny-th 256-token tile (8 groups;
+// half of a 512-token key-plane tile) of one (request, KV head), ny = the
+// unit's block count, starting at its own index.  The logit of token j and
 // query head h is
 //   s_hj = (C_gh + sum_c beta_hc X'_jc) / sqrt(d),
 //   beta_hc = q_hc rng_gc / 256,  X' = X - 128 (X = P 2^(8-t), the prefix
@@ -304,20 +291,22 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
 //
 // Once per block: depths, query, per-head scales, the slot table.  Per tile:
 //  1. The tile's segment of every chosen key line (channel c, plane p < t_c;
-//     16 words = 64 B) sits in LDS as planes[slot][group], slot = (sum of t
-//     over channels below c) + p.  The next tile's segments and metadata are
-//     in flight to registers while this tile is computed; they are written
-//     to LDS after its last un-plane, and the loads for the tile after are
-//     issued at once.  Barriers inside the tile loop wait for LDS traffic
-//     only, never for those loads.
+//     8 words = 32 B, one per group) sits in LDS as planes[slot][group],
+//     slot = (sum of t over channels below c) + p.  The next tile's segments
+//     and metadata are in flight to registers while this tile is computed;
+//     they are written to LDS after its last un-plane, and the loads for the
+//     tile after are issued at once (the first tile's go out as soon as the
+//     slot table is known).  Barriers inside the tile loop wait for LDS
+//     traffic only, never for those loads.
 //  2. Per-group constants C_gh: a 16 x 128 x GQA fp64 contraction on the
 //     matrix cores (v_mfma_f64_16x16x4_f64).
 //  3. Four slabs of 32 channels.  Un-plane: wave w takes the slab's channels
-//     w, w+4, ... (uniform depth in the wave, taken from a scalar table),
-//     lane o the tile's tokens 8o..8o+7: byte o%4 of its group's t plane
-//     words, an 8x8 bit transpose gives the 8 codes (the top plane inverted
-//     first, which makes them X'), stored as a code tile [channel][token].
-//     MFMA: wave w takes groups 4w..4w+3; per group it writes the digit
+//     w, w+4, ... in pairs (channels sorted by depth, deepest first; depths
+//     from a scalar table), lane o of a half-wave the tile's tokens
+//     8o..8o+7: one transposing LDS read gives their 8 plane bytes, an 8x8
+//     bit transpose the 8 codes (the top plane inverted first, which makes
+//     them X'), stored as a code tile [channel][token].
+//     MFMA: wave w takes groups 2w and 2w+1; per group it writes the digit
 //     words of its 32 channels x GQA heads, then v_mfma_i32_16x16x32_i8 with
 //     A = digits and B = codes (16 tokens x 32 channels), both read with the
 //     transposing ds_read_b64_tr_b8, accumulating over the slabs.  An A chunk
@@ -325,11 +314,13 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
 //     (4 heads) x (4 digits) and lane l of the result holds all its digits of
 //     head l/16 for token l%16: the digit sums are combined in-lane.
 //  4. Digit sums -> logits (fp64) in registers; open-group tokens use exact
-//     keys; per head the tile max m, e = exp(s - m) (fp64, and rounded to
-//     fp16 for the value gather) and sum e (split-context softmax).
-// Grid (unit, run): consecutive blocks are different units, so all runs of
-// a unit are on one XCD and share its L2.
-// Dynamic LDS: 64 B per staged slot (at most min(B_K, 128 W) slots).
+//     keys; per head the tile max m, e = exp(s - m) (fp64; stored rounded
+//     to fp32 for the value allocation and to fp16 for the value gather)
+//     and sum e (split-context softmax).
+// Grid (unit, ny): consecutive blocks are different units, so all blocks of
+// a unit are on one XCD and share its L2; as they take neighbouring tiles at
+// the same time, the two halves of a key-plane tile are read from HBM once.
+// Dynamic LDS: 32 B per staged slot (at most min(B_K, 128 W) slots).
 // ---------------------------------------------------------------------------
 // transpose8_halves for lo == 0 (at most 4 planes present)
 __device__ __forceinline__ void transpose8_hi4(uint32_t& lo, uint32_t& hi) {
@@ -926,9 +917,10 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
 // Threshold.  A token whose a_j is a normal double with exponent field
 // E > 2W ("regular") has its W gains at fields E - 2t, all with a_j's
 // mantissa, so it holds min(W, max(0, floor((E - L) / 2))) gains at field L
-// or above.  The field L* of the B_V-th largest gain comes from a bisection
-// over L with block-wide counts; other positive a_j (subnormal products,
-// infinities) have their products formed one by one.  Within field L* the
+// or above.  An LDS histogram of the regular tokens' fields (and of the
+// fields of the other positive a_j's products, formed one by one: subnormal
+// products, infinities) gives the count at every field; one wave scans it
+// from the top for the field L* of the B_V-th largest gain.  Within field L* the
 // gains are ranked by mantissa with 11/11/10/10/10-bit radix passes, which
 // stop once the gains sharing the chosen digits are exactly the ones still
 // to be taken.
@@ -1004,12 +996,41 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   constexpr int kVTileMax = RMAX * kVRound / kTile;
   static_assert(kTile % 128 == 0 && kVRound % kTile == 0, "a wave's tokens of one round lie in one tile");
   const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const ReqRecord r = req_of(store, b);
+  const ReqRecord r = req_of(store, b);  // (a scalar load; waited for below)
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const float* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
+  const int jl = 128 * wv + 2 * lane;  // first token of the lane in round 0
+  auto tok0 = [&](int k) -> int64_t { return (int64_t)kVRound * k + jl; };
+  // register path: RB rounds of exponentials in flight at a time, the first
+  // batch already during the softmax statistics
+  constexpr int RB0 = RMAX * GQA <= 20 ? RMAX : (GQA >= 8 ? 2 : (GQA >= 4 ? 4 : 8));
+  constexpr int RB = REG ? (RB0 < RMAX ? RB0 : RMAX) : 1;
+  // The first vector loads do not depend on the request record and go out
+  // while it is in flight, all unconditional (a branch around them would
+  // make the first wait for the tile partials also wait for the
+  // exponentials): this wave's tile partials (waves past GQA read the last
+  // head's and drop them; entries past the request's tiles are dropped too),
+  // then the first batch of exponentials (rounds past the row load its
+  // first token; tokens past the closed groups come out as zero weights).
+  const double* tp = tilepart + ((int64_t)b * H + (int64_t)g * GQA + min(wv, GQA - 1)) * ntile_ws * 2;
+  const double2 p0 = *reinterpret_cast<const double2*>(tp + 2 * min(lane, ntile_ws - 1));
+  asm volatile("" ::: "memory");  // the statistics wait for the partials alone
+  float2 e0[RB][GQA];
+  if constexpr (REG) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int64_t j0 = tok0(i);
+      const int64_t jc = j0 < capmax ? j0 : 0;  // capmax is a multiple of 32
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh)
+        e0[i][hh] = *reinterpret_cast<const float2*>(eb + (int64_t)hh * capmax + jc);
+    }
+  }
+  asm volatile("" ::: "memory");  // issued before the record is waited for
   const int64_t len = r.len;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
   const int ntile_b = (int)((len + kTile - 1) / kTile);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
   __shared__ __align__(16) uint32_t hA[2048];
   __shared__ __align__(16) uint32_t hB[2048];
@@ -1020,12 +1041,9 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   __shared__ uint32_t sh[4];
 
   const int nr = (int)((Tp + kVRound - 1) / kVRound);
-  const float* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
   double* fg = ftile + ((int64_t)b * H + (int64_t)g * GQA) * ntile_ws;
   double* ab = aval + ((int64_t)b * G + g) * capmax;
   uint8_t* tvb = tv + ((int64_t)b * G + g) * capmax;
-  const int jl = 128 * wv + 2 * lane;  // first token of the lane in round 0
-  auto tok0 = [&](int k) -> int64_t { return (int64_t)kVRound * k + jl; };
   auto load_e = [&](int k, float2* e) __attribute__((always_inline)) {
     const int64_t j0 = tok0(k);
     const int64_t jc = j0 < Tp ? j0 : 0;  // Tp > 0 whenever a round exists
@@ -1033,27 +1051,10 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
     for (int hh = 0; hh < GQA; ++hh)
       e[hh] = *reinterpret_cast<const float2*>(eb + (int64_t)hh * capmax + jc);
   };
-  // register path: RB rounds of exponentials in flight at a time, the first
-  // batch already during the softmax statistics; rounds past the tokens
-  // load clamped addresses (no branches, so nothing waits on a merge of
-  // paths) and come out as zero weights
-  constexpr int RB0 = RMAX * GQA <= 20 ? RMAX : (GQA >= 8 ? 2 : (GQA >= 4 ? 4 : 8));
-  constexpr int RB = REG ? (RB0 < RMAX ? RB0 : RMAX) : 1;
-  // loads first, in the order they are used, all unconditional (clamped
-  // addresses): this wave's tile partials (waves past GQA read the last
-  // head's and drop them), one group scale per thread, the exponentials
-  const double* tp = tilepart + ((int64_t)b * H + (int64_t)g * GQA + min(wv, GQA - 1)) * ntile_ws * 2;
-  const double2 p0 = *reinterpret_cast<const double2*>(tp + 2 * min(lane, max(ntile_b - 1, 0)));
+  // one group scale per thread (rounds past the tokens load clamped
+  // addresses: no branches, so nothing waits on a merge of paths)
   const int ngrp = (int)(Tp / kGroup);
   const double evr = REG ? u.ev[min(tid, max(ngrp - 1, 0))] : 0.0;
-  asm volatile("" ::: "memory");  // keep these two loads ahead of the exponentials'
-  float2 e0[RB][GQA];
-  if constexpr (REG) {
-    // unconditional (a branch around them would make the compiler's wait
-    // for the tile partials below also wait for all of these)
-#pragma unroll
-    for (int i = 0; i < RB; ++i) load_e(i, e0[i]);
-  }
 
   // ---- softmax statistics -> per-tile factors (wave h handles head h) ----
   if (wv < GQA) {
