@@ -429,7 +429,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   __shared__ uint32_t meta[NG][kDim + 1];
   __shared__ __attribute__((aligned(16))) uint8_t cx[32 * CXS];
   __shared__ __attribute__((aligned(16))) uint8_t at[4][AGS];
-  __shared__ double Cpart[4][NG][GQA];  // per-wave partial constants
+  __shared__ double Cpart[8][NG][GQA];  // partial constants per (wave, channel set)
   __shared__ double kap[kDim];         // 2^-(t_c+1) + [t_c > 0] / 2
   __shared__ double tails[kGroup][GQA];
   __shared__ double redm[4][GQA], redz[4][GQA], mfin[GQA];
@@ -641,13 +641,15 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // slabs (deepest first, so the live ones come first)
   int cAs[4];
   int nslab = 0;
-  // the per-group constants' query operand (head lane % 16, channel
-  // 32 w + 4 st + lane / 16) for the 8 steps
-  double qbs[8];
+  // the per-group constants' query operand (column lane % 16 = (channel set
+  // z, head h) = (n / 8, n % 8), channel 32 w + 8 st + 4 z + lane / 16) for
+  // the 4 steps
+  static_assert(GQA <= 8, "a channel set's heads fit 8 columns");
+  double qbs[4];
 #pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const int gA = lane & 15, c = 32 * wv + 4 * st + (lane >> 4);
-    qbs[st] = gA < GQA ? qd[min(gA, GQA - 1)][c] : 0.0;
+  for (int st = 0; st < 4; ++st) {
+    const int hB = lane & 7, c = 32 * wv + 8 * st + 4 * ((lane >> 3) & 1) + (lane >> 4);
+    qbs[st] = hB < GQA ? qd[min(hB, GQA - 1)][c] : 0.0;
   }
   // the logit scale exponent -(sig + 8) of the lane's epilogue head per head quad
   int lsg[NHQ];
@@ -695,24 +697,32 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     const bool more = tile + ny < ntl;
 
     // ---- per-group constants C[g][h] = sum_c base[g][c] q[h][c] on the fp64
-    // matrix cores: wave w contracts its 32 channels in 8 steps of 4 (A:
-    // lane l = (group l % 16, channel l / 16), B: (channel l / 16, head
-    // l % 16)); result lane l, register i = (group 4 i + l / 16, head l % 16) ----
+    // matrix cores: wave w contracts its 32 channels in 4 steps of two
+    // channel sets z = 0, 1 of 4 channels each.  Rows m = (z, group) =
+    // (m / 8, m % 8), columns n = (z, head) = (n / 8, n % 8); A: lane l =
+    // (row l % 16, channel l / 16 of the row's set), B: (channel l / 16 of
+    // the column's set, column l % 16).  Result lane l, register i = (row
+    // 4 i + l / 16, column l % 16); only the blocks with equal sets are
+    // wanted: set z's sums are registers 2 z, 2 z + 1 of the lanes with
+    // (l / 8) % 2 = z ----
     {
-      const int gA = lane & 15, kk = lane >> 4;
+      const int mA = lane & 15, kk = lane >> 4;
+      const int gA = mA & 7, zA = mA >> 3;
       f64x4 cd = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int c = 32 * wv + 4 * st + kk;
-        const uint32_t m = gA < NG ? meta[gA][c] : 0u;
+      for (int st = 0; st < 4; ++st) {
+        const int c = 32 * wv + 8 * st + 4 * zA + kk;
+        const uint32_t m = meta[gA][c];
         const double lo = (double)bf16_to_float(m & 0xFFFFu);
         const double rng = (double)bf16_to_float(m >> 16);
         const double base = fma(rng, kap[c], lo);
         cd = __builtin_amdgcn_mfma_f64_16x16x4f64(base, qbs[st], cd, 0, 0, 0);
       }
-      if (gA < GQA)
-#pragma unroll
-        for (int i = 0; i < NG / 4; ++i) Cpart[wv][4 * i + kk][gA] = cd[i];
+      const int hB = lane & 7, zB = (lane >> 3) & 1;
+      if (hB < GQA) {
+        Cpart[2 * wv + zB][kk][hB] = zB ? cd[2] : cd[0];
+        Cpart[2 * wv + zB][4 + kk][hB] = zB ? cd[3] : cd[1];
+      }
     }
     const int64_t ntail = len - Tp;
     const bool tail_here = ntail > 0 && Tp >= t0 && Tp < t0 + kTile;
@@ -851,7 +861,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
             // byte x byte products), so digit pairs combine exactly in int32
             const int p01 = d0[0] + d0[1] * 256, p23 = d0[2] + d0[3] * 256, p45 = d1[0] + d1[1] * 256;
             const double P = fma((double)p45, 0x1p32, fma((double)p23, 0x1p16, (double)p01));
-            const double C = (Cpart[0][gw][hc] + Cpart[1][gw][hc]) + (Cpart[2][gw][hc] + Cpart[3][gw][hc]);
+            const double C = ((Cpart[0][gw][hc] + Cpart[1][gw][hc]) + (Cpart[2][gw][hc] + Cpart[3][gw][hc])) +
+                             ((Cpart[4][gw][hc] + Cpart[5][gw][hc]) + (Cpart[6][gw][hc] + Cpart[7][gw][hc]));
             s = (C + ldexp(P, lsg[hq])) * kInvSqrtD;
           } else if (tail_here && tok >= toff && tok < toff + ntail) {
             s = tails[tok - toff][hc];
