@@ -429,7 +429,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   __shared__ uint32_t meta[NG][kDim + 1];
   __shared__ __attribute__((aligned(16))) uint8_t cx[32 * CXS];
   __shared__ __attribute__((aligned(16))) uint8_t at[4][AGS];
-  __shared__ double Cpart[8][NG][GQA];  // partial constants per (wave, channel set)
+  __shared__ double Cpart[4][NG][GQA];  // per-wave partial constants
   __shared__ double kap[kDim];         // 2^-(t_c+1) + [t_c > 0] / 2
   __shared__ double tails[kGroup][GQA];
   __shared__ double redm[4][GQA], redz[4][GQA], mfin[GQA];
@@ -704,7 +704,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     // the column's set, column l % 16).  Result lane l, register i = (row
     // 4 i + l / 16, column l % 16); only the blocks with equal sets are
     // wanted: set z's sums are registers 2 z, 2 z + 1 of the lanes with
-    // (l / 8) % 2 = z ----
+    // (l / 8) % 2 = z, and the lanes of set 1 add those of set 0, 8 lanes
+    // below in the same row ----
     {
       const int mA = lane & 15, kk = lane >> 4;
       const int gA = mA & 7, zA = mA >> 3;
@@ -718,10 +719,12 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
         const double base = fma(rng, kap[c], lo);
         cd = __builtin_amdgcn_mfma_f64_16x16x4f64(base, qbs[st], cd, 0, 0, 0);
       }
-      const int hB = lane & 7, zB = (lane >> 3) & 1;
-      if (hB < GQA) {
-        Cpart[2 * wv + zB][kk][hB] = zB ? cd[2] : cd[0];
-        Cpart[2 * wv + zB][4 + kk][hB] = zB ? cd[3] : cd[1];
+      const double c0 = cd[2] + dpp_f64<kDppRowShr8>(cd[0]);  // groups kk, 4 + kk
+      const double c1 = cd[3] + dpp_f64<kDppRowShr8>(cd[1]);
+      const int hB = lane & 7;
+      if ((lane & 8) && hB < GQA) {
+        Cpart[wv][kk][hB] = c0;
+        Cpart[wv][4 + kk][hB] = c1;
       }
     }
     const int64_t ntail = len - Tp;
@@ -861,8 +864,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
             // byte x byte products), so digit pairs combine exactly in int32
             const int p01 = d0[0] + d0[1] * 256, p23 = d0[2] + d0[3] * 256, p45 = d1[0] + d1[1] * 256;
             const double P = fma((double)p45, 0x1p32, fma((double)p23, 0x1p16, (double)p01));
-            const double C = ((Cpart[0][gw][hc] + Cpart[1][gw][hc]) + (Cpart[2][gw][hc] + Cpart[3][gw][hc])) +
-                             ((Cpart[4][gw][hc] + Cpart[5][gw][hc]) + (Cpart[6][gw][hc] + Cpart[7][gw][hc]));
+            const double C = (Cpart[0][gw][hc] + Cpart[1][gw][hc]) + (Cpart[2][gw][hc] + Cpart[3][gw][hc]);
             s = (C + ldexp(P, lsg[hq])) * kInvSqrtD;
           } else if (tail_here && tok >= toff && tok < toff + ntail) {
             s = tails[tok - toff][hc];
