@@ -88,18 +88,48 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
       return;
     }
     if (Bk == 0) return;
-    // candidate levels span [min E - 2W, max E - 2]
     const int emax = wave_max_i32(max(ec[0], ec[1]));
-    const int lo0 = min(ec[0] >= 0 ? ec[0] : 4096, ec[1] >= 0 ? ec[1] : 4096);
-    const int emin = -wave_max_i32(-lo0);  // some channel is positive here
-    int lo_l = max(1, emin - 2 * W), hi_l = emax - 2;
-    while (lo_l < hi_l) {
-      const int mid = (lo_l + hi_l + 1) >> 1;
-      if ((uint32_t)wave_sum_i32(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
-      else hi_l = mid - 1;
+    // Lane l evaluates count(L) at level L = emax - 2 - l: with n_i the
+    // number of channels with E_c = emax - i and S_i = n_0 + ... + n_i,
+    //   count(L) = sum_{k=1..W} #{c : E_c >= L + 2k} = sum_k S_{l + 2 - 2k}
+    // (S of a negative index is 0; a channel with E_c < emax - 63 has no
+    // candidate at these levels).  The highest such level with count >= B_K
+    // is the first lane's; when it lies below them all, a bisection over
+    // [min E - 2W, max E - 2] finds it.
+    uint32_t* const hE = cc;       // n_i, i < 64
+    uint32_t* const hS = cc + 64;  // S_i at hS[16 + i], zeros below
+    hE[lane] = 0u;
+    if (lane < 16) hS[lane] = 0u;
+    wave_lds_fence();
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+      if (ec[k] >= 0 && emax - ec[k] < 64) atomicAdd(&hE[emax - ec[k]], 1u);
+    wave_lds_fence();
+    hS[16 + lane] = wave_incl_scan_u32(hE[lane]);
+    wave_lds_fence();
+    uint32_t cntl = 0;
+#pragma unroll
+    for (int k = 1; k <= 8; ++k)
+      if (k <= W) cntl += hS[16 + lane + 2 - 2 * k];
+    const uint64_t okb = __ballot(cntl >= Bk);
+    int Ls;
+    uint32_t above;
+    if (okb) {
+      const int ls = __ffsll((unsigned long long)okb) - 1;
+      Ls = emax - 2 - ls;
+      above = ls > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)cntl, ls - 1) : 0u;
+    } else {
+      const int lo0 = min(ec[0] >= 0 ? ec[0] : 4096, ec[1] >= 0 ? ec[1] : 4096);
+      const int emin = -wave_max_i32(-lo0);  // some channel is positive here
+      int lo_l = max(1, emin - 2 * W), hi_l = emax - 2;
+      while (lo_l < hi_l) {
+        const int mid = (lo_l + hi_l + 1) >> 1;
+        if ((uint32_t)wave_sum_i32(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
+        else hi_l = mid - 1;
+      }
+      Ls = lo_l;
+      above = (uint32_t)wave_sum_i32(cnt_ge(0, Ls + 1) + cnt_ge(1, Ls + 1));
     }
-    const int Ls = lo_l;
-    const uint32_t above = (uint32_t)wave_sum_i32(cnt_ge(0, Ls + 1) + cnt_ge(1, Ls + 1));
     const uint32_t rem = Bk - above;  // >= 1
     bool at[2];
 #pragma unroll
@@ -115,7 +145,24 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
     uint64_t pre = 0ull, hm = 0ull;  // threshold bits decided so far, their mask
     uint32_t rm = rem;
     bool early = false;
-    for (int bit = 51; bit >= 0; --bit) {
+    {
+      // the top 8 mantissa bits in one step: a 256-bin histogram of the
+      // candidates' top digits, scanned from the top (splitting further
+      // never changes which candidates end up taken)
+      uint32_t* const hD = cc;
+      *reinterpret_cast<uint4*>(hD + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+      wave_lds_fence();
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        if (at[k]) atomicAdd(&hD[(uint32_t)(mc[k] >> 44)], 1u);
+      wave_lds_fence();
+      wave_find_digit<256>(hD, rm, cc + 256, cc + 257);
+      wave_lds_fence();
+      pre = (uint64_t)cc[256] << 44;
+      hm = 0xFFull << 44;
+      rm -= cc[257];
+    }
+    for (int bit = 43; bit >= 0; --bit) {
       const bool a0 = at[0] && ((mc[0] ^ pre) & hm) == 0ull;
       const bool a1 = at[1] && ((mc[1] ^ pre) & hm) == 0ull;
       if ((uint32_t)(__popcll(__ballot(a0)) + __popcll(__ballot(a1))) == rm) {
