@@ -172,6 +172,11 @@ def q_step(cfg: dict, b: int, step: int) -> np.ndarray:
         q = _q_base(cfg, b) + 0.1 * r.standard_normal(shape)
     else:
         q = r.standard_t(3.0, size=shape)
+    spread = cfg.get("q_log2_spread", 0)
+    if spread:
+        # channel c scaled by an exact power of two from 2^-spread up to 1:
+        # key weights then span about 2 * spread binary orders of magnitude
+        q = q * np.exp2(np.round(np.linspace(-float(spread), 0.0, shape[1])))
     return cast(cfg, q)
 
 

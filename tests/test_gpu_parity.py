@@ -172,6 +172,15 @@ def test_peaky_needles_unit_scale():
     run.check()
 
 
+def test_query_spanning_many_binary_orders():
+    # key weights spread over ~80 binary orders of magnitude: at R_K = 6 the
+    # threshold level lies more than 64 fields below the top one (the key
+    # allocator's bisection path), at R_K = 4 and 2 within them
+    cfg = synth.workload(2, B=2, T0=700, q_log2_spread=40)
+    run = Run(cfg, steps=2, rates=[(6.0, 4.0), (4.0, 4.0), (2.0, 2.0)])
+    run.check()
+
+
 @pytest.mark.parametrize("T0", [5, 31, 32, 33, 1023, 1025, 2047])
 def test_ragged_tails_and_tiles(T0):
     cfg = synth.workload(2, B=1, H=8, G=2, T0=T0)
