@@ -241,8 +241,9 @@ def main():
                     help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the decode path has no "
-                                   "multi-GPU mode; run with --gpus 1"}))
+        print(json.dumps({"error": "one GPU only: the decode path has no multi-GPU mode "
+                                   "(requests and KV heads are independent; see the sharding "
+                                   "notes); run with --gpus 1"}))
         sys.exit(2)
     import torch
     from query_adaptive_decode_amd import synth, workload
