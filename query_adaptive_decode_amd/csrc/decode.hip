@@ -1618,7 +1618,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
     // rows of planes past a token's depth were loaded as zeros, so the
     // codes need no mask; the deepest of the 4 tokens (a scalar) picks the
     // transpose (at most 4 planes: the upper half only) ----
-#pragma unroll 2
+#pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int j0 = 32 * wv + 4 * it;
       const uint32_t t4 = (uint32_t)__builtin_amdgcn_readfirstlane(
