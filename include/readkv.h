@@ -61,6 +61,29 @@ extern "C" {
 #define READKV_VSCALE_PHYSICAL 0
 #define READKV_VSCALE_UNIT 1
 
+/* Budget scope (Sec. 3.3; Sec. 5.1 and App. F.8 for the per-head policy):
+ * KV_HEAD = one key budget over the d_h channels and one value budget over
+ * the packed tokens of every (request, KV head); LAYER = one key budget over
+ * the G * d_h channels and one value budget over the G * T_packed tokens of
+ * every request (all KV heads of the layer pooled). */
+#define READKV_SCOPE_KV_HEAD 0
+#define READKV_SCOPE_LAYER 1
+
+/* Logical-read counters of one decode call (App. A.1: payload and metadata
+ * bits the reader asks for; workspace and schedules are not counted), summed
+ * over every request and KV head:
+ *   [READKV_CTR_KEY_PAYLOAD]   sum over units of T_packed * sum_c t^K_c
+ *   [READKV_CTR_VALUE_PAYLOAD] sum over units of d_h * sum_j t^V_j
+ *   [READKV_CTR_METADATA]      lo and rng (16 bits each) of every closed group
+ *                              and channel of keys and values, E^K (d_h x 64
+ *                              bits) and E^V (64 bits per closed group)
+ *   [READKV_CTR_OPEN_GROUP]    keys and values of the open group in kv_dtype */
+#define READKV_CTR_KEY_PAYLOAD 0
+#define READKV_CTR_VALUE_PAYLOAD 1
+#define READKV_CTR_METADATA 2
+#define READKV_CTR_OPEN_GROUP 3
+#define READKV_NUM_COUNTERS 4
+
 /* Store flags (readkv_store_status) */
 #define READKV_FLAG_NONFINITE 1u /* a group held a non-finite value; it was
                                     stored with lo = rng = 0 and codes 0     */
@@ -76,7 +99,8 @@ typedef struct readkv_config {
   int32_t group_tokens;    /* quantiser group along tokens; must be 32     */
   int32_t batch;           /* B requests                                   */
   int64_t capacity_tokens; /* largest per-request capacity, tokens (also
-                              the default capacity of every request)       */
+                              the default capacity of every request);
+                              at most 2^26                                 */
   int32_t kv_dtype;        /* READKV_BF16 or READKV_F32: element type of
                               appended K/V, of the open-group buffer and of
                               queries                                      */
@@ -117,26 +141,35 @@ int readkv_encode_append(const readkv_config* cfg, void* store,
                          const void* k_new, const void* v_new,
                          const int32_t* n_new, int32_t n_max, void* stream);
 
-/* One decode step of ReadKV attention for every request and query head.
- * q: device [batch][num_q_heads][head_dim] in kv_dtype.
+/* One decode step of ReadKV attention for every request and query head
+ * (Sec. 3.2-3.3, Algorithm 1).
+ * q: device [batch][num_q_heads][head_dim] in kv_dtype.  A unit (request,
+ *   KV head) any of whose query values is not finite reads nothing: its
+ *   depths are 0 and its outputs NaN.
  * R_K, R_V: read bits per scalar for the key and value stages (finite,
- *   >= 0; the nominal rate is R = (R_K + R_V)/2, Sec. 3.3).  Budgets are
- *   per (request, KV head): B_K = floor(R_K * d_h) key refinements over the
- *   d_h channels, B_V = floor(R_V * T_packed) value refinements over the
- *   tokens of closed groups (R as float32, product in double).
+ *   >= 0; the nominal rate is R = (R_K + R_V)/2, Sec. 3.3).  Budgets (R as
+ *   float32, product in double): B_K = floor(R_K * d_h) key refinements over
+ *   the d_h channels, B_V = floor(R_V * T_packed) value refinements over the
+ *   tokens of closed groups, per (request, KV head) for
+ *   READKV_SCOPE_KV_HEAD.
+ * scope: READKV_SCOPE_KV_HEAD (READKV_SCOPE_LAYER: EUNSUPPORTED).
  * vscale: READKV_VSCALE_PHYSICAL or READKV_VSCALE_UNIT.
  * out: device fp32 [batch][num_q_heads][head_dim].
  * workspace: device, >= readkv_workspace_bytes.
  * key_depths_out: device u8 [batch][num_kv_heads][head_dim] or NULL.
  * value_depths_out: device u8 [batch][num_kv_heads][capacity_max] or NULL
  *   (entries beyond a request's packed length are unspecified).
+ * counters_out: device u64 [READKV_NUM_COUNTERS] or NULL; overwritten with
+ *   this call's logical reads in bits (see READKV_CTR_*).
  * Allocation is ChooseDepths (Sec. 3.3) with gains a_i * 4^-t, exact under
  * diminishing gains (App. E.2.1, Prop. 8); ties go to the lowest channel /
- * token index; only positive gains are taken. */
+ * token index; only positive gains are taken.  Results are bitwise
+ * reproducible from call to call. */
 int readkv_decode_attn(const readkv_config* cfg, const void* store,
-                       const void* q, float R_K, float R_V, int32_t vscale,
-                       float* out, void* workspace, size_t workspace_bytes,
-                       uint8_t* key_depths_out, uint8_t* value_depths_out,
+                       const void* q, float R_K, float R_V, int32_t scope,
+                       int32_t vscale, float* out, void* workspace,
+                       size_t workspace_bytes, uint8_t* key_depths_out,
+                       uint8_t* value_depths_out, uint64_t* counters_out,
                        void* stream);
 
 /* readkv_decode_attn with timing hooks: `events` points to 4 hipEvent_t
@@ -149,9 +182,11 @@ int readkv_decode_attn(const readkv_config* cfg, const void* store,
  * any of the 4 handles is NULL). */
 int readkv_decode_attn_timed(const readkv_config* cfg, const void* store,
                              const void* q, float R_K, float R_V,
-                             int32_t vscale, float* out, void* workspace,
-                             size_t workspace_bytes, uint8_t* key_depths_out,
-                             uint8_t* value_depths_out, void* const* events,
+                             int32_t scope, int32_t vscale, float* out,
+                             void* workspace, size_t workspace_bytes,
+                             uint8_t* key_depths_out,
+                             uint8_t* value_depths_out,
+                             uint64_t* counters_out, void* const* events,
                              void* stream);
 
 /* Read the store's sticky flags and per-request lengths (host arrays;

@@ -30,6 +30,7 @@ reason in the design notes of the repository):
   floor(R d); App. F.1 converts rates to integer increment budgets).
 * Tokens of the not-yet-full group are kept exactly and enter the softmax and
   the output, but not the allocation.
+* A query with a non-finite value reads nothing: depths 0, outputs NaN.
 """
 from __future__ import annotations
 
@@ -44,7 +45,7 @@ __all__ = [
     "bf16_down", "bf16_up", "encode_stream", "EncodedStream", "prefix",
     "reconstruct", "gain_table", "choose_depths", "key_weights",
     "value_weights", "budget", "decode_unit", "softmax",
-    "reuse_overhead", "reuse_reads",
+    "reuse_overhead", "reuse_reads", "logical_reads",
 ]
 
 
@@ -291,6 +292,15 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     gains = gain_table(W)
     gidx = np.arange(tp) // group_tokens
 
+    if not np.isfinite(q_heads).all():
+        # The pages define no read for a query that is not a real vector.
+        # Reading: the unit reads nothing (every key and value depth 0) and
+        # every output of its query heads is NaN.
+        gq = q_heads.shape[0]
+        return dict(out=np.full((gq, d), np.nan), tK=np.zeros(d, dtype=np.int64),
+                    tV=np.zeros(tp, dtype=np.int64), wk=np.zeros(d), wv=np.zeros(tp),
+                    BK=budget(R_K, d), BV=budget(R_V, tp), zhat=None, ahat=None, tp=tp)
+
     # stage 1: key prefix depths
     wk = key_weights(q_heads, enc_k)
     BK = budget(R_K, d)
@@ -318,6 +328,28 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     if diagnostics:
         res.update(Khat=Kfull_hat, Vhat=Vfull_hat, enc_k=enc_k, enc_v=enc_v)
     return res
+
+
+# ----------------------------------------------------------------------------
+# Logical-read accounting of one decode unit ([ReadKV] App. A.1)
+# ----------------------------------------------------------------------------
+def logical_reads(tK, tV, n_tokens, d=128, group_tokens=32, elem_bits=16):
+    """Bits one decode of a (request, KV head) unit asks for ([ReadKV] App.
+    A.1 counts payload and metadata the reader requests, not workspace):
+
+    key payload   = T_packed * sum_c t^K_c   (t bits of every packed token)
+    value payload = d * sum_j t^V_j          (t bits of every channel)
+    metadata      = lo and rng (16 bits each) of every closed group and
+                    channel of keys and of values, plus the channel energies
+                    E^K (d x 64 bits) and the group energies E^V (64 bits each)
+    open group    = keys and values of the not-yet-closed group, exact.
+    """
+    tp = (n_tokens // group_tokens) * group_tokens
+    ng = tp // group_tokens
+    return dict(key_payload=int(tp * int(np.sum(tK))),
+                value_payload=int(d * int(np.sum(tV))),
+                metadata=int(2 * ng * d * 32 + d * 64 + ng * 64),
+                open_group=int(2 * (n_tokens - tp) * d * elem_bits))
 
 
 # ----------------------------------------------------------------------------

@@ -17,6 +17,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libreadkv.so")
 
 BF16, F32 = 0, 1
 VSCALE_PHYSICAL, VSCALE_UNIT = 0, 1
+SCOPE_KV_HEAD, SCOPE_LAYER = 0, 1
+NUM_COUNTERS = 4   # key payload, value payload, metadata, open group (bits)
 FLAG_NONFINITE, FLAG_OVERFLOW = 1, 2
 
 EXPORTED = ["readkv_validate_config", "readkv_store_bytes", "readkv_workspace_bytes",
@@ -57,10 +59,10 @@ def lib():
             "readkv_workspace_bytes": [CP, ctypes.POINTER(SZ)],
             "readkv_store_init": [CP, P, SZ, P, P],
             "readkv_encode_append": [CP, P, P, P, P, I32, P],
-            "readkv_decode_attn": [CP, P, P, ctypes.c_float, ctypes.c_float, I32,
-                                   P, P, SZ, P, P, P],
-            "readkv_decode_attn_timed": [CP, P, P, ctypes.c_float, ctypes.c_float, I32,
-                                         P, P, SZ, P, P, P, P],
+            "readkv_decode_attn": [CP, P, P, ctypes.c_float, ctypes.c_float, I32, I32,
+                                   P, P, SZ, P, P, P, P],
+            "readkv_decode_attn_timed": [CP, P, P, ctypes.c_float, ctypes.c_float, I32, I32,
+                                         P, P, SZ, P, P, P, P, P],
             "readkv_store_status": [CP, P, ctypes.POINTER(ctypes.c_uint32), P],
         }
         for name, args in sig.items():
@@ -141,35 +143,42 @@ def encode_append(cfg: Config, store, k_new, v_new, n_new=None, n_max=None):
         int(n_max), _stream()))
 
 
-def decode_attn(cfg: Config, store, q, R_K, R_V, workspace, out=None,
-                vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None):
-    """q: [B][H][d] device tensor in the config's dtype.  Returns out
-    [B][H][d] fp32."""
+def _out(cfg, q, out):
     if out is None:
         out = torch.empty((cfg.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32,
                           device=q.device)
-    _need_cuda(store, q, out, workspace, key_depths, value_depths)
+    return out
+
+
+def decode_attn(cfg: Config, store, q, R_K, R_V, workspace, out=None,
+                vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None,
+                scope=SCOPE_KV_HEAD, counters=None):
+    """q: [B][H][d] device tensor in the config's dtype.  Returns out
+    [B][H][d] fp32.  counters: optional int64 device tensor of NUM_COUNTERS
+    entries, overwritten with the call's logical reads in bits."""
+    out = _out(cfg, q, out)
+    _need_cuda(store, q, out, workspace, key_depths, value_depths, counters)
     _check("readkv_decode_attn", lib().readkv_decode_attn(
-        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(vscale),
-        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _ptr(key_depths), _ptr(value_depths), _stream()))
+        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(scope),
+        int(vscale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(key_depths), _ptr(value_depths), _ptr(counters), _stream()))
     return out
 
 
 def decode_attn_timed(cfg: Config, store, q, R_K, R_V, workspace, events, out=None,
-                      vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None):
+                      vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None,
+                      scope=SCOPE_KV_HEAD, counters=None):
     """decode_attn that records four caller-created hipEvent_t handles
     (``events``: sequence of ints) around its three stages (score, value
     allocation, value gather)."""
-    if out is None:
-        out = torch.empty((cfg.batch, cfg.num_q_heads, cfg.head_dim), dtype=torch.float32,
-                          device=q.device)
-    _need_cuda(store, q, out, workspace, key_depths, value_depths)
+    out = _out(cfg, q, out)
+    _need_cuda(store, q, out, workspace, key_depths, value_depths, counters)
     ev = (ctypes.c_void_p * 4)(*[int(e) for e in events])
     _check("readkv_decode_attn_timed", lib().readkv_decode_attn_timed(
-        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(vscale),
-        _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _ptr(key_depths), _ptr(value_depths), ctypes.cast(ev, ctypes.c_void_p), _stream()))
+        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(scope),
+        int(vscale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _ptr(key_depths), _ptr(value_depths), _ptr(counters), ctypes.cast(ev, ctypes.c_void_p),
+        _stream()))
     return out
 
 
@@ -194,9 +203,9 @@ class ReadKVCache:
         encode_append(self.cfg, self.store, k_new, v_new, n_new, n_max)
 
     def decode(self, q, R_K, R_V, out=None, vscale=VSCALE_PHYSICAL, key_depths=None,
-               value_depths=None):
+               value_depths=None, scope=SCOPE_KV_HEAD, counters=None):
         return decode_attn(self.cfg, self.store, q, R_K, R_V, self.workspace, out, vscale,
-                           key_depths, value_depths)
+                           key_depths, value_depths, scope, counters)
 
     def status(self):
         return store_status(self.cfg, self.store)

@@ -78,7 +78,7 @@ int readkv_validate_config(const readkv_config* cfg) {
       cfg->batch <= 0 || cfg->group_tokens <= 0 || cfg->capacity_tokens <= 0)
     return READKV_EINVAL;
   if (cfg->num_q_heads % cfg->num_kv_heads != 0) return READKV_EINVAL;
-  if (cfg->capacity_tokens > (int64_t(1) << 31)) return READKV_EINVAL;
+  if (cfg->capacity_tokens > (int64_t(1) << 26)) return READKV_EINVAL;
   if (cfg->reserved != 0) return READKV_EINVAL;
   if (cfg->head_dim != kDim) return READKV_EUNSUPPORTED;
   if (cfg->group_tokens != kGroup) return READKV_EUNSUPPORTED;
@@ -146,14 +146,17 @@ int readkv_encode_append(const readkv_config* cfg, void* store, const void* k_ne
 }
 
 static int decode_impl(const readkv_config* cfg, const void* store, const void* q, float R_K,
-                       float R_V, int32_t vscale, float* out, void* workspace,
+                       float R_V, int32_t scope, int32_t vscale, float* out, void* workspace,
                        size_t workspace_bytes, uint8_t* key_depths_out,
-                       uint8_t* value_depths_out, void* const* events, void* stream) {
+                       uint8_t* value_depths_out, uint64_t* counters_out, void* const* events,
+                       void* stream) {
   int rc = readkv_validate_config(cfg);
   if (rc) return rc;
   if (!store || !q || !out || !workspace) return READKV_EINVAL;
   if (!isfinite(R_K) || !isfinite(R_V) || R_K < 0.f || R_V < 0.f) return READKV_EINVAL;
   if (vscale != READKV_VSCALE_PHYSICAL && vscale != READKV_VSCALE_UNIT) return READKV_EINVAL;
+  if (scope != READKV_SCOPE_KV_HEAD && scope != READKV_SCOPE_LAYER) return READKV_EINVAL;
+  if (scope == READKV_SCOPE_LAYER) return READKV_EUNSUPPORTED;
   // budgets must fit the 32-bit counters: R * T <= 2^31
   if ((double)R_V * (double)align_up(cfg->capacity_tokens, kGroup) > 2147483647.0 ||
       (double)R_K * cfg->head_dim > 2147483647.0)
@@ -172,6 +175,8 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   a.ws = (uint8_t*)workspace;
   a.key_depths_out = key_depths_out;
   a.value_depths_out = value_depths_out;
+  a.counters = counters_out;
+  a.scope = scope;
   a.B = cfg->batch;
   a.H = cfg->num_q_heads;
   a.G = cfg->num_kv_heads;
@@ -185,22 +190,23 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
 }
 
 int readkv_decode_attn(const readkv_config* cfg, const void* store, const void* q, float R_K,
-                       float R_V, int32_t vscale, float* out, void* workspace,
+                       float R_V, int32_t scope, int32_t vscale, float* out, void* workspace,
                        size_t workspace_bytes, uint8_t* key_depths_out,
-                       uint8_t* value_depths_out, void* stream) {
-  return decode_impl(cfg, store, q, R_K, R_V, vscale, out, workspace, workspace_bytes,
-                     key_depths_out, value_depths_out, nullptr, stream);
+                       uint8_t* value_depths_out, uint64_t* counters_out, void* stream) {
+  return decode_impl(cfg, store, q, R_K, R_V, scope, vscale, out, workspace, workspace_bytes,
+                     key_depths_out, value_depths_out, counters_out, nullptr, stream);
 }
 
 int readkv_decode_attn_timed(const readkv_config* cfg, const void* store, const void* q,
-                             float R_K, float R_V, int32_t vscale, float* out, void* workspace,
-                             size_t workspace_bytes, uint8_t* key_depths_out,
-                             uint8_t* value_depths_out, void* const* events, void* stream) {
+                             float R_K, float R_V, int32_t scope, int32_t vscale, float* out,
+                             void* workspace, size_t workspace_bytes, uint8_t* key_depths_out,
+                             uint8_t* value_depths_out, uint64_t* counters_out,
+                             void* const* events, void* stream) {
   if (!events) return READKV_EINVAL;
   for (int i = 0; i < 4; ++i)
     if (!events[i]) return READKV_EINVAL;
-  return decode_impl(cfg, store, q, R_K, R_V, vscale, out, workspace, workspace_bytes,
-                     key_depths_out, value_depths_out, events, stream);
+  return decode_impl(cfg, store, q, R_K, R_V, scope, vscale, out, workspace, workspace_bytes,
+                     key_depths_out, value_depths_out, counters_out, events, stream);
 }
 
 int readkv_store_status(const readkv_config* cfg, const void* store, uint32_t* flags_out,

@@ -36,34 +36,30 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 constexpr double kInvSqrtD = 0.088388347648318440550;  // 1/sqrt(128)
 
 // ---------------------------------------------------------------------------
-// Key allocation: one wave per (request, KV head).  Lane l holds channels l
-// and l+64 and their W candidate gains w_c 4^-t (t = 1..W).  The B_K largest
-// positive gains are chosen, ties to the lowest channel (App. E.2.1: with
-// strictly decreasing per-item gains this is ChooseDepths' result).  The
-// threshold is found in two steps on the 64-bit patterns of the fp64 gains:
-// bisection on the 12-bit sign+exponent field, then an exact rank among the
-// candidates in the threshold's exponent class.
+// Key allocation.  ChooseDepths for one unit's d_h = 128 key channels by one
+// wave: lane l holds channels l and l + 64 with weights wv[0], wv[1]; the W
+// candidate gains of a channel are w_c 4^-t, t = 1..W, and the B_K largest
+// positive ones are chosen, ties to the lowest channel (with strictly
+// decreasing per-item gains this is ChooseDepths' result, [ReadKV] App.
+// E.2.1).  Returns the depths of the lane's two channels.  cc: LDS scratch of
+// 258 words.  Wave-level only (no block barrier).
+//
+// Every positive weight has a normal exponent field E_c in [2W + 1, 2046]:
+// with finite bf16 or fp32 queries (|q| in [2^-149, 2^128)) and ranges (bf16,
+// in [2^-133, 2^128), at most 2^21 groups), w_c = (sum of at most 8 q^2)
+// E^K_c lies in [2^-564, 2^537).  A non-finite query never reaches this
+// function (its unit's weights are zero).  So each gain w_c 4^-(t+1) is exact,
+// with field E_c - 2t - 2 and the mantissa M_c of w_c.  Gains order by that
+// field first; the B_K-th largest lies at the highest field level L with
+//   count(L) = sum_c #{t < W : E_c - 2t - 2 >= L} >= B_K,
+// and at that level each channel has at most one candidate, ranked by (M_c
+// descending, c ascending).
 // ---------------------------------------------------------------------------
-// ChooseDepths for one unit's d_h = 128 key channels by one wave: lane l
-// holds channels l and l + 64 with weights wv[0], wv[1]; the W candidate
-// gains of a channel are w_c 4^-t, t = 1..W, and the B_K largest positive
-// ones are chosen, ties to the lowest channel (with strictly decreasing
-// per-item gains this is ChooseDepths' result, [ReadKV] App. E.2.1).
-// Returns the depths of the lane's two channels.  ck / cc: 1024-entry LDS
-// scratch for the rare exact-rank path.  Wave-level only (no block barrier).
 __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, uint32_t Bk,
-                                                uint64_t* ck, uint32_t* cc, uint32_t (&sel)[2]) {
+                                                uint32_t* cc, uint32_t (&sel)[2]) {
   const int lane = __lane_id();
   sel[0] = 0u;
   sel[1] = 0u;
-  // Fast path: every positive weight w_c has a normal exponent field E_c in
-  // [2W + 1, 2046], so each gain w_c 4^-(t+1) is exact with field
-  // E_c - 2t - 2 and mantissa M_c.  Gains then order by that field first;
-  // the B_K-th largest lies in the highest field level L with
-  //   count(L) = sum_c #{t < W : E_c - 2t - 2 >= L} >= B_K
-  // (bisection on L between the lowest and the highest candidate level),
-  // and at that level each channel has at most one candidate, ranked by
-  // (M_c descending, c ascending).
   int ec[2];
   uint64_t mc[2];
 #pragma unroll
@@ -72,244 +68,125 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
     ec[k] = wv[k] > 0.0 ? (int)(wb >> 52) : -1;  // no candidate unless w_c > 0
     mc[k] = wb & 0x000FFFFFFFFFFFFFull;
   }
-  const bool fast = !__any((ec[0] >= 0 && (ec[0] < 2 * W + 1 || ec[0] > 2046)) ||
-                           (ec[1] >= 0 && (ec[1] < 2 * W + 1 || ec[1] > 2046)));
   auto cnt_ge = [&](int k, int lvl) -> int {  // #{t < W : E - 2t - 2 >= lvl} for slot k
     if (ec[k] < 0) return 0;
     const int d = ec[k] - 2 - lvl;
     return d < 0 ? 0 : min(d / 2 + 1, W);
   };
-  if (fast) {
-    const uint32_t nposf = (uint32_t)W * (uint32_t)(__popcll(__ballot(ec[0] >= 0)) +
-                                                    __popcll(__ballot(ec[1] >= 0)));
-    if (nposf <= Bk) {
-      sel[0] = ec[0] >= 0 ? (uint32_t)W : 0u;
-      sel[1] = ec[1] >= 0 ? (uint32_t)W : 0u;
-      return;
-    }
-    if (Bk == 0) return;
-    const int emax = wave_max_i32(max(ec[0], ec[1]));
-    // Lane l evaluates count(L) at level L = emax - 2 - l: with n_i the
-    // number of channels with E_c = emax - i and S_i = n_0 + ... + n_i,
-    //   count(L) = sum_{k=1..W} #{c : E_c >= L + 2k} = sum_k S_{l + 2 - 2k}
-    // (S of a negative index is 0; a channel with E_c < emax - 63 has no
-    // candidate at these levels).  The highest such level with count >= B_K
-    // is the first lane's; when it lies below them all, a bisection over
-    // [min E - 2W, max E - 2] finds it.
-    uint32_t* const hE = cc;       // n_i, i < 64
-    uint32_t* const hS = cc + 64;  // S_i at hS[16 + i], zeros below
-    hE[lane] = 0u;
-    if (lane < 16) hS[lane] = 0u;
-    wave_lds_fence();
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (ec[k] >= 0 && emax - ec[k] < 64) atomicAdd(&hE[emax - ec[k]], 1u);
-    wave_lds_fence();
-    hS[16 + lane] = wave_incl_scan_u32(hE[lane]);
-    wave_lds_fence();
-    uint32_t cntl = 0;
-#pragma unroll
-    for (int k = 1; k <= 8; ++k)
-      if (k <= W) cntl += hS[16 + lane + 2 - 2 * k];
-    const uint64_t okb = __ballot(cntl >= Bk);
-    int Ls;
-    uint32_t above;
-    if (okb) {
-      const int ls = __ffsll((unsigned long long)okb) - 1;
-      Ls = emax - 2 - ls;
-      above = ls > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)cntl, ls - 1) : 0u;
-    } else {
-      const int lo0 = min(ec[0] >= 0 ? ec[0] : 4096, ec[1] >= 0 ? ec[1] : 4096);
-      const int emin = -wave_max_i32(-lo0);  // some channel is positive here
-      int lo_l = max(1, emin - 2 * W), hi_l = emax - 2;
-      while (lo_l < hi_l) {
-        const int mid = (lo_l + hi_l + 1) >> 1;
-        if ((uint32_t)wave_sum_i32(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
-        else hi_l = mid - 1;
-      }
-      Ls = lo_l;
-      above = (uint32_t)wave_sum_i32(cnt_ge(0, Ls + 1) + cnt_ge(1, Ls + 1));
-    }
-    const uint32_t rem = Bk - above;  // >= 1
-    bool at[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      sel[k] = (uint32_t)cnt_ge(k, Ls + 1);
-      const int d = ec[k] - 2 - Ls;
-      at[k] = ec[k] >= 0 && d >= 0 && (d & 1) == 0 && d / 2 < W;
-    }
-    // the rem largest at the level by (M_c descending, c ascending): an
-    // MSB-first search over the 52 mantissa bits (wave ballots) that stops
-    // as soon as the candidates still equal to the threshold on the decided
-    // bits are exactly the ones left to take
-    uint64_t pre = 0ull, hm = 0ull;  // threshold bits decided so far, their mask
-    uint32_t rm = rem;
-    bool early = false;
-    {
-      // the top 8 mantissa bits in one step: a 256-bin histogram of the
-      // candidates' top digits, scanned from the top (splitting further
-      // never changes which candidates end up taken)
-      uint32_t* const hD = cc;
-      *reinterpret_cast<uint4*>(hD + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
-      wave_lds_fence();
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-        if (at[k]) atomicAdd(&hD[(uint32_t)(mc[k] >> 44)], 1u);
-      wave_lds_fence();
-      wave_find_digit<256>(hD, rm, cc + 256, cc + 257);
-      wave_lds_fence();
-      pre = (uint64_t)cc[256] << 44;
-      hm = 0xFFull << 44;
-      rm -= cc[257];
-    }
-    for (int bit = 43; bit >= 0; --bit) {
-      const bool a0 = at[0] && ((mc[0] ^ pre) & hm) == 0ull;
-      const bool a1 = at[1] && ((mc[1] ^ pre) & hm) == 0ull;
-      if ((uint32_t)(__popcll(__ballot(a0)) + __popcll(__ballot(a1))) == rm) {
-        early = true;
-        break;
-      }
-      const uint64_t bm = 1ull << bit;
-      const uint32_t c1 = (uint32_t)(__popcll(__ballot(a0 && (mc[0] & bm))) +
-                                     __popcll(__ballot(a1 && (mc[1] & bm))));
-      if (c1 >= rm) pre |= bm;
-      else rm -= c1;
-      hm |= bm;
-    }
-    // above the threshold on the decided bits: taken; equal to it: all of
-    // them after an early stop, else (equal mantissas) the first rm in
-    // channel order
-    bool eq[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const uint64_t hv = mc[k] & hm;
-      eq[k] = at[k] && hv == pre;
-      if (at[k] && hv > pre) ++sel[k];
-    }
-    if (early) {
-      sel[0] += eq[0];
-      sel[1] += eq[1];
-    } else {
-      const uint64_t b0 = __ballot(eq[0]), b1 = __ballot(eq[1]);
-      const uint64_t below = (1ull << lane) - 1ull;
-      if (eq[0] && (uint32_t)__popcll(b0 & below) < rm) ++sel[0];
-      if (eq[1] && (uint32_t)(__popcll(b0) + __popcll(b1 & below)) < rm) ++sel[1];
-    }
+  const uint32_t nposf = (uint32_t)W * (uint32_t)(__popcll(__ballot(ec[0] >= 0)) +
+                                                  __popcll(__ballot(ec[1] >= 0)));
+  if (nposf <= Bk) {
+    sel[0] = ec[0] >= 0 ? (uint32_t)W : 0u;
+    sel[1] = ec[1] >= 0 ? (uint32_t)W : 0u;
     return;
   }
-  // Exact path (some gain is subnormal or not finite): the 64-bit patterns
-  // of the fp64 gains themselves
-  uint64_t key[2][8];
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-#pragma unroll
-    for (int t = 1; t <= 8; ++t) {
-      const double gt = __dmul_rn(wv[k], ldexp_pow2(-2 * t));
-      key[k][t - 1] = (t <= W && gt > 0.0) ? dbits(gt) : 0ull;
-    }
-  }
-  // wave-wide counts are sums of ballot popcounts over the 16 candidate slots
-  uint32_t npos = 0;
+  if (Bk == 0) return;
+  const int emax = wave_max_i32(max(ec[0], ec[1]));
+  // Lane l evaluates count(L) at level L = emax - 2 - l: with n_i the
+  // number of channels with E_c = emax - i and S_i = n_0 + ... + n_i,
+  //   count(L) = sum_{k=1..W} #{c : E_c >= L + 2k} = sum_k S_{l + 2 - 2k}
+  // (S of a negative index is 0; a channel with E_c < emax - 63 has no
+  // candidate at these levels).  The highest such level with count >= B_K
+  // is the first lane's; when it lies below them all, a bisection over
+  // [min E - 2W, max E - 2] finds it.
+  uint32_t* const hE = cc;       // n_i, i < 64
+  uint32_t* const hS = cc + 64;  // S_i at hS[16 + i], zeros below
+  hE[lane] = 0u;
+  if (lane < 16) hS[lane] = 0u;
+  wave_lds_fence();
 #pragma unroll
   for (int k = 0; k < 2; ++k)
+    if (ec[k] >= 0 && emax - ec[k] < 64) atomicAdd(&hE[emax - ec[k]], 1u);
+  wave_lds_fence();
+  hS[16 + lane] = wave_incl_scan_u32(hE[lane]);
+  wave_lds_fence();
+  uint32_t cntl = 0;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) npos += (uint32_t)__popcll(__ballot(key[k][t] != 0ull));
-  if (npos <= Bk) {
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) sel[k] += key[k][t] != 0ull;
-  } else if (Bk > 0) {
-    // largest exponent class E with count(key >> 52 >= E) >= Bk
-    int lo = 0, hi = 2047;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      uint32_t c_ = 0;
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          c_ += (uint32_t)__popcll(__ballot(key[k][t] != 0ull && (int)(key[k][t] >> 52) >= mid));
-      if (c_ >= Bk) lo = mid;
-      else hi = mid - 1;
+  for (int k = 1; k <= 8; ++k)
+    if (k <= W) cntl += hS[16 + lane + 2 - 2 * k];
+  const uint64_t okb = __ballot(cntl >= Bk);
+  int Ls;
+  uint32_t above;
+  if (okb) {
+    const int ls = __ffsll((unsigned long long)okb) - 1;
+    Ls = emax - 2 - ls;
+    above = ls > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)cntl, ls - 1) : 0u;
+  } else {
+    const int lo0 = min(ec[0] >= 0 ? ec[0] : 4096, ec[1] >= 0 ? ec[1] : 4096);
+    const int emin = -wave_max_i32(-lo0);  // some channel is positive here
+    int lo_l = max(1, emin - 2 * W), hi_l = emax - 2;
+    while (lo_l < hi_l) {
+      const int mid = (lo_l + hi_l + 1) >> 1;
+      if ((uint32_t)wave_sum_i32(cnt_ge(0, mid) + cnt_ge(1, mid)) >= Bk) lo_l = mid;
+      else hi_l = mid - 1;
     }
-    const int Es = lo;
-    uint32_t above = 0, at = 0;
+    Ls = lo_l;
+    above = (uint32_t)wave_sum_i32(cnt_ge(0, Ls + 1) + cnt_ge(1, Ls + 1));
+  }
+  const uint32_t rem = Bk - above;  // >= 1
+  bool at[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    sel[k] = (uint32_t)cnt_ge(k, Ls + 1);
+    const int d = ec[k] - 2 - Ls;
+    at[k] = ec[k] >= 0 && d >= 0 && (d & 1) == 0 && d / 2 < W;
+  }
+  // the rem largest at the level by (M_c descending, c ascending): an
+  // MSB-first search over the 52 mantissa bits (wave ballots) that stops
+  // as soon as the candidates still equal to the threshold on the decided
+  // bits are exactly the ones left to take
+  uint64_t pre = 0ull, hm = 0ull;  // threshold bits decided so far, their mask
+  uint32_t rm = rem;
+  bool early = false;
+  {
+    // the top 8 mantissa bits in one step: a 256-bin histogram of the
+    // candidates' top digits, scanned from the top (splitting further
+    // never changes which candidates end up taken)
+    uint32_t* const hD = cc;
+    *reinterpret_cast<uint4*>(hD + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+    wave_lds_fence();
 #pragma unroll
     for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int e = (int)(key[k][t] >> 52);
-        above += (uint32_t)__popcll(__ballot(key[k][t] != 0ull && e > Es));
-        at += key[k][t] != 0ull && e == Es;
-      }
-    const uint32_t rem = Bk - above;  // >= 1 by the choice of Es
-    // candidates in class Es: with normal gains at most one level per
-    // channel; lane slot k holds channel lane + 64 k
-    uint32_t atc[2] = {0u, 0u};
-    uint64_t atm[2] = {0ull, 0ull};
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (key[k][t] != 0ull && (int)(key[k][t] >> 52) == Es) {
-          ++atc[k];
-          atm[k] = key[k][t] & 0x000FFFFFFFFFFFFFull;
-        }
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) sel[k] += key[k][t] != 0ull && (int)(key[k][t] >> 52) > Es;
-    if (!__any(atc[0] > 1u || atc[1] > 1u)) {
-      // MSB-first search for the rem-th largest mantissa in the class
-      uint64_t pre = 0ull;
-      uint32_t rm = rem;
-      for (int bit = 51; bit >= 0; --bit) {
-        const uint64_t hi_mask = ~((2ull << bit) - 1ull);  // bits above `bit`
-        const bool f0 = atc[0] && ((atm[0] ^ pre) & hi_mask) == 0ull && ((atm[0] >> bit) & 1ull);
-        const bool f1 = atc[1] && ((atm[1] ^ pre) & hi_mask) == 0ull && ((atm[1] >> bit) & 1ull);
-        const uint32_t c1 = (uint32_t)(__popcll(__ballot(f0)) + __popcll(__ballot(f1)));
-        if (c1 >= rm) pre |= 1ull << bit;
-        else rm -= c1;
-      }
-      // above the threshold mantissa: taken; equal: the first rm in channel order
-      const bool e0 = atc[0] && atm[0] == pre, e1 = atc[1] && atm[1] == pre;
-      const uint64_t b0 = __ballot(e0), b1 = __ballot(e1);
-      const uint64_t below = (1ull << lane) - 1ull;
-      if (atc[0] && atm[0] > pre) ++sel[0];
-      if (atc[1] && atm[1] > pre) ++sel[1];
-      if (e0 && (uint32_t)__popcll(b0 & below) < rm) ++sel[0];
-      if (e1 && (uint32_t)(__popcll(b0) + __popcll(b1 & below)) < rm) ++sel[1];
-    } else {
-      // several levels of one channel in the class (subnormal gains): rank
-      // every class member against the compacted list
-      const uint32_t incl = wave_incl_scan_u32(at);
-      const uint32_t nat = __shfl(incl, 63, 64);
-      uint32_t pos = incl - at;
-#pragma unroll
-      for (int k = 0; k < 2; ++k)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-          if (key[k][t] != 0ull && (int)(key[k][t] >> 52) == Es) {
-            ck[pos] = key[k][t];
-            cc[pos] = (uint32_t)(lane + 64 * k);
-            ++pos;
-          }
-      wave_lds_fence();
-      for (int k = 0; k < 2; ++k) {
-        const uint32_t c = (uint32_t)(lane + 64 * k);
-        for (int t = 0; t < 8; ++t) {
-          const uint64_t kk = key[k][t];
-          if (kk == 0ull || (int)(kk >> 52) != Es) continue;
-          uint32_t beats = 0;
-          for (uint32_t m = 0; m < nat; ++m) {
-            const uint64_t k2 = ck[m];
-            beats += (k2 > kk) || (k2 == kk && cc[m] < c);
-          }
-          if (beats < rem) ++sel[k];
-        }
-      }
+      if (at[k]) atomicAdd(&hD[(uint32_t)(mc[k] >> 44)], 1u);
+    wave_lds_fence();
+    wave_find_digit<256>(hD, rm, cc + 256, cc + 257);
+    wave_lds_fence();
+    pre = (uint64_t)cc[256] << 44;
+    hm = 0xFFull << 44;
+    rm -= cc[257];
+  }
+  for (int bit = 43; bit >= 0; --bit) {
+    const bool a0 = at[0] && ((mc[0] ^ pre) & hm) == 0ull;
+    const bool a1 = at[1] && ((mc[1] ^ pre) & hm) == 0ull;
+    if ((uint32_t)(__popcll(__ballot(a0)) + __popcll(__ballot(a1))) == rm) {
+      early = true;
+      break;
     }
+    const uint64_t bm = 1ull << bit;
+    const uint32_t c1 = (uint32_t)(__popcll(__ballot(a0 && (mc[0] & bm))) +
+                                   __popcll(__ballot(a1 && (mc[1] & bm))));
+    if (c1 >= rm) pre |= bm;
+    else rm -= c1;
+    hm |= bm;
+  }
+  // above the threshold on the decided bits: taken; equal to it: all of
+  // them after an early stop, else (equal mantissas) the first rm in
+  // channel order
+  bool eq[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint64_t hv = mc[k] & hm;
+    eq[k] = at[k] && hv == pre;
+    if (at[k] && hv > pre) ++sel[k];
+  }
+  if (early) {
+    sel[0] += eq[0];
+    sel[1] += eq[1];
+  } else {
+    const uint64_t b0 = __ballot(eq[0]), b1 = __ballot(eq[1]);
+    const uint64_t below = (1ull << lane) - 1ull;
+    if (eq[0] && (uint32_t)__popcll(b0 & below) < rm) ++sel[0];
+    if (eq[1] && (uint32_t)(__popcll(b0) + __popcll(b1 & below)) < rm) ++sel[1];
   }
 }
 
@@ -459,8 +336,8 @@ __device__ __forceinline__ double half_sum(double v) {
 template <int GQA, int DT>
 __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* store, const void* q, uint8_t* tk,
                                                   int H, int G, int W, float RK, int64_t capmax,
-                                                  int ntile_ws, float* ebuf, _Float16* e16,
-                                                  double* tilepart) {
+                                                  int ntile_ws, uint32_t* ebuf,
+                                                  double* tilepart, uint64_t* counters) {
   constexpr int esize = DT == 0 ? 2 : 4;
   constexpr int NG = kTile / kGroup;  // 8 groups; wave w owns groups 2w, 2w + 1
   static_assert(NG == 8, "a score tile is half of a 16-group key-plane tile");
@@ -488,6 +365,9 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   __shared__ uint32_t wtot[2];
   __shared__ uint32_t dcnt[2][9];  // channels per depth value, per wave
 
+  // the call's read counters start from zero (they are added to by the
+  // value allocation, the next launch)
+  if (counters && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0ull;
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
@@ -526,7 +406,11 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // key allocation of the unit (every block of the unit computes it; the
   // first writes it out): w_c = (sum_h q_hc^2) E^K_c in head order, then
   // ChooseDepths over the channels by wave 0
+  // A query with a non-finite value reads nothing: its unit's key weights
+  // are zero (depths 0) and its softmax statistics NaN, so that no value is
+  // refined and every output of the unit is NaN.
   double ek = 0.0;
+  bool qnf = false;
   if (tid < kDim) {
     const int c = tid;
     double qv[GQA];
@@ -538,17 +422,17 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
       qd[hh][c] = qv[hh];
+      qnf |= !isfinite(qv[hh]);
       qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
     }
     kap[c] = __dmul_rn(qsq, ek);  // the key weight, until kap is set below
   }
-  __syncthreads();
+  const bool qbad = __syncthreads_or(qnf);
   if (wv == 0) {
-    const double w2[2] = {kap[lane], kap[lane + 64]};
+    const double w2[2] = {qbad ? 0.0 : kap[lane], qbad ? 0.0 : kap[lane + 64]};
     uint32_t sel[2];
     key_depths_wave(w2, W, (uint32_t)floor((double)RK * (double)kDim),
-                    reinterpret_cast<uint64_t*>(planes),
-                    reinterpret_cast<uint32_t*>(planes) + 2 * 2 * 64 * 8, sel);
+                    reinterpret_cast<uint32_t*>(planes), sel);
     tks[lane] = (uint8_t)sel[0];
     tks[lane + 64] = (uint8_t)sel[1];
     if (tile_begin == 0) {  // the unit's first block writes the depths out
@@ -937,15 +821,13 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
       const int hc = min(hh, GQA - 1);
       const double mt = fmax(fmax(redm[0][hc], redm[1][hc]), fmax(redm[2][hc], redm[3][hc]));
       const int64_t lane0 = ((int64_t)b * H + (int64_t)g * GQA + hc) * capmax + t0 + 64 * wv + (lane & 15);
-      float* const ep = ebuf + lane0;
-      _Float16* const hp = e16 + lane0;
+      uint32_t* const ep = ebuf + lane0;
       double z = 0.0;
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         const double e = exp_nonpos(sv[tb][hq] - mt);
-        if (sv[tb][hq] > -INFINITY) {
-          ep[16 * tb] = (float)e;
-          hp[16 * tb] = to_half(e);
+        if (sv[tb][hq] != -INFINITY) {  // a token of the request (logit NaN if qbad)
+          ep[16 * tb] = qbad ? 0u : enc_e(e);
           z += e;
         }
       }
@@ -958,8 +840,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     lds_barrier();
     if (tid < GQA) {
       double* tp = tilepart + (((int64_t)b * H + (int64_t)g * GQA + tid) * ntile_ws + tile) * 2;
-      tp[0] = mfin[tid];
-      tp[1] = (redz[0][tid] + redz[1][tid]) + (redz[2][tid] + redz[3][tid]);
+      tp[0] = qbad ? __builtin_nan("") : mfin[tid];
+      tp[1] = qbad ? __builtin_nan("") : (redz[0][tid] + redz[1][tid]) + (redz[2][tid] + redz[3][tid]);
     }
   }
 }
@@ -1048,8 +930,9 @@ template <int GQA, int RMAX>
 __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int H, int G, int W,
                                                       int esize, float RV, int vscale,
                                                       int64_t capmax, int ntile_ws,
-                                                      const float* ebuf, const double* tilepart,
-                                                      double* ftile, double* aval, uint8_t* tv) {
+                                                      const uint32_t* ebuf, const double* tilepart,
+                                                      double* ftile, double* aval, uint8_t* tv,
+                                                      const uint8_t* tk, uint64_t* counters) {
   constexpr int NT = kVNT;
   constexpr int NW = NT / 64;
   constexpr bool REG = RMAX > 0;
@@ -1058,7 +941,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);  // (a scalar load; waited for below)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const float* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
+  const uint32_t* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
   const int jl = 128 * wv + 2 * lane;  // first token of the lane in round 0
   auto tok0 = [&](int k) -> int64_t { return (int64_t)kVRound * k + jl; };
   // register path: RB rounds of exponentials in flight at a time, the first
@@ -1075,7 +958,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   const double* tp = tilepart + ((int64_t)b * H + (int64_t)g * GQA + min(wv, GQA - 1)) * ntile_ws * 2;
   const double2 p0 = *reinterpret_cast<const double2*>(tp + 2 * min(lane, ntile_ws - 1));
   asm volatile("" ::: "memory");  // the statistics wait for the partials alone
-  float2 e0[RB][GQA];
+  uint2 e0[RB][GQA];
   if constexpr (REG) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -1083,7 +966,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
       const int64_t jc = j0 < capmax ? j0 : 0;  // capmax is a multiple of 32
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh)
-        e0[i][hh] = *reinterpret_cast<const float2*>(eb + (int64_t)hh * capmax + jc);
+        e0[i][hh] = *reinterpret_cast<const uint2*>(eb + (int64_t)hh * capmax + jc);
     }
   }
   asm volatile("" ::: "memory");  // issued before the record is waited for
@@ -1104,12 +987,12 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   double* fg = ftile + ((int64_t)b * H + (int64_t)g * GQA) * ntile_ws;
   double* ab = aval + ((int64_t)b * G + g) * capmax;
   uint8_t* tvb = tv + ((int64_t)b * G + g) * capmax;
-  auto load_e = [&](int k, float2* e) __attribute__((always_inline)) {
+  auto load_e = [&](int k, uint2* e) __attribute__((always_inline)) {
     const int64_t j0 = tok0(k);
     const int64_t jc = j0 < Tp ? j0 : 0;  // Tp > 0 whenever a round exists
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh)
-      e[hh] = *reinterpret_cast<const float2*>(eb + (int64_t)hh * capmax + jc);
+      e[hh] = *reinterpret_cast<const uint2*>(eb + (int64_t)hh * capmax + jc);
   };
   // one group scale per thread (rounds past the tokens load clamped
   // addresses: no branches, so nothing waits on a merge of paths)
@@ -1149,7 +1032,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
 
   // ---- value weights ----
   // the lane's two weights of round k from its exponentials e[hh]
-  auto weights = [&](int k, const float2* e, double& a0, double& a1) __attribute__((always_inline)) {
+  auto weights = [&](int k, const uint2* e, double& a0, double& a1) __attribute__((always_inline)) {
     const int64_t j0 = tok0(k);
     const bool in = j0 < Tp;  // Tp is even: both tokens or neither
     const int tl = in ? (kVRound / kTile) * k + (128 * wv) / kTile : 0;
@@ -1157,7 +1040,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
       const double f = REG ? fs[hh * kVTileMax + tl] : fg[(int64_t)hh * ntile_ws + tl];
-      const double x0 = __dmul_rn((double)e[hh].x, f), x1 = __dmul_rn((double)e[hh].y, f);
+      const double x0 = __dmul_rn(dec_e(e[hh].x), f), x1 = __dmul_rn(dec_e(e[hh].y), f);
       s0 = __dadd_rn(s0, __dmul_rn(x0, x0));
       s1 = __dadd_rn(s1, __dmul_rn(x1, x1));
     }
@@ -1202,7 +1085,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
             }
           continue;
         }
-        float2 e[RB][GQA];
+        uint2 e[RB][GQA];
 #pragma unroll
         for (int i = 0; i < RB; ++i) {
           if (k0 + i >= RMAX) break;
@@ -1231,7 +1114,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
     }
   } else {
     for (int k = 0; k < nr; ++k) {
-      float2 e[GQA];
+      uint2 e[GQA];
       load_e(k, e);
       double a0, a1;
       weights(k, e, a0, a1);
@@ -1381,6 +1264,7 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
   const bool rank_ties = !all_pos && Bv > 0 && rem < n_eq;
   uint32_t running = 0;  // ties in earlier rounds (token order = round, thread, s)
   uint32_t lv0 = 0;
+  uint32_t vsum = 0;     // this thread's value refinements
   for_tokens([&](double a, int ef, int k, int s) __attribute__((always_inline)) {
     const uint32_t lv = count_levels(a, ef);
     if (s == 0) { lv0 = lv; return; }
@@ -1399,15 +1283,37 @@ __global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int 
     if (j0 < Tp) {
       tvb[j0] = (uint8_t)above0;
       tvb[j0 + 1] = (uint8_t)above1;
+      vsum += above0 + above1;
     }
   });
+  // logical reads of the unit ([ReadKV] App. A.1): key payload T_p * sum_c
+  // t_c bits, value payload d * sum_j t_j bits, metadata (lo and rng of
+  // every closed group and channel of keys and values, E^K, E^V) and the
+  // open group's keys and values in the input type
+  if (counters) {
+    const uint32_t vtot = block_sum_u32<NT>(vsum, wsum);
+    if (wv == 0) {
+      const uint8_t* tkb = tk + ((int64_t)b * G + g) * kDim;
+      const int ks = wave_sum_i32((int)tkb[lane] + (int)tkb[lane + 64]);
+      if (lane == 0) {
+        const unsigned long long ng = (unsigned long long)(Tp / kGroup);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1), (unsigned long long)vtot * kDim);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2),
+                  2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
+                  2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
 // Gather: a block of 256 threads takes a run of consecutive 128-token chunks
 // (4 groups each) of one (request, KV head) and accumulates its share of
 //   O_h = sum_j alpha_hj v_hat_j,  alpha_hj = e_hj f_{h,tile(j)}
-// (e = exp(s - m_tile) rounded to fp16, f_{h,tile} = exp(m_tile - m) / Z).
+// (e = exp(s - m_tile), rounded to fp16 for the matrix cores, f_{h,tile} =
+// exp(m_tile - m) / Z in fp32).
 // Per chunk:
 //  1. The chosen value plane rows (16 B per token and plane) sit in LDS as
 //     rows[plane][token]; depths, weights and metadata of the chunk too.  All
@@ -1438,7 +1344,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int GQA, int DT>
 __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const uint8_t* tv, int H,
                                                    int G, int W, int64_t capmax, int ntile_ws,
-                                                   int nrun_ws, const _Float16* e16,
+                                                   int nrun_ws, const uint32_t* ebuf,
                                                    const double* ftile, float* opart) {
   constexpr int esize = DT == 0 ? 2 : 4;
   constexpr int NG = kChunk / kGroup;                  // 4 groups per chunk
@@ -1484,7 +1390,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
 
   // ---- register prefetch of one chunk ----
   uint32_t ptv = 0;                 // depth of token jl (for the row loads)
-  uint32_t pes[GQA];  // e of tokens 2 tid, 2 tid + 1 (tid < 64) per head, as fp16 pairs
+  uint32_t pes[GQA];  // encoded e of token tid (tid < kChunk) per head
   uint32_t pmeta[MPT];
   double pfs = 0.0;  // converted when stored: no wait right after its load
   uint4 prow0, prow1, prow2, prow3;  // planes rh, rh + 2, rh + 4, rh + 6 of token jl
@@ -1503,11 +1409,9 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
     const int c0 = chunk * kChunk;
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
-      // (an odd length reads one stale half past it; tokens past the
-      // length are never used)
       const __amdgpu_buffer_rsrc_t rs_e = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<_Float16*>(e16 + (hrow0 + hh) * capmax), (short)0, ((int)len * 2 + 3) & ~3, kBufWord3);
-      pes[hh] = __builtin_amdgcn_raw_buffer_load_b32(rs_e, tid < kChunk / 2 ? (c0 + 2 * tid) * 2 : kBufOff, 0, 0);
+          const_cast<uint32_t*>(ebuf + (hrow0 + hh) * capmax), (short)0, (int)len * 4, kBufWord3);
+      pes[hh] = __builtin_amdgcn_raw_buffer_load_b32(rs_e, tid < kChunk ? (c0 + tid) * 4 : kBufOff, 0, 0);
     }
 #pragma unroll
     for (int k = 0; k < MPT; ++k)
@@ -1536,9 +1440,9 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
   };
   auto store_chunk = [&](uint32_t t) __attribute__((always_inline)) {
     if (tid < kChunk) tvs[tid] = (uint8_t)t;
-    if (tid < kChunk / 2) {
+    if (tid < kChunk) {
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) *reinterpret_cast<uint32_t*>(&es[hh][2 * tid]) = pes[hh];
+      for (int hh = 0; hh < GQA; ++hh) es[hh][tid] = to_half(dec_e(pes[hh]));
     }
 #pragma unroll
     for (int k = 0; k < MPT; ++k) {
@@ -1784,8 +1688,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   const int nrun = (L.ntile + run - 1) / run;
   hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), dyn, st,
                      (const uint8_t*)a.store, a.q, tk, a.H, a.G, a.W, a.RK, a.capmax,
-                     L.ntile, (float*)(ws + L.ebuf), (_Float16*)(ws + L.e16),
-                     (double*)(ws + L.tilepart));
+                     L.ntile, (uint32_t*)(ws + L.ebuf), (double*)(ws + L.tilepart), a.counters);
   mark(a, 1, st);
   {
     auto va = &k_value_alloc<GQA, 0>;
@@ -1794,8 +1697,8 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
     else if (a.capmax <= (int64_t)kVRound * kVRMAX) va = &k_value_alloc<GQA, kVRMAX>;
     hipLaunchKernelGGL(va, dim3(a.B * a.G), dim3(kVNT), 0, st, (const uint8_t*)a.store, a.H, a.G,
                        a.W, esize, a.RV, a.vscale, a.capmax, L.ntile,
-                       (const float*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
-                       (double*)(ws + L.ftile), (double*)(ws + L.aval), tv);
+                       (const uint32_t*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
+                       (double*)(ws + L.ftile), (double*)(ws + L.aval), tv, tk, a.counters);
   }
   mark(a, 2, st);
   {
@@ -1808,7 +1711,7 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
     const int nrun = (L.nchunk + run - 1) / run;
     hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), 0, st,
                        (const uint8_t*)a.store, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax,
-                       L.ntile, L.nchunk, (const _Float16*)(ws + L.e16),
+                       L.ntile, L.nchunk, (const uint32_t*)(ws + L.ebuf),
                        (const double*)(ws + L.ftile), (float*)(ws + L.opart));
     const int64_t nout = (int64_t)a.B * a.H * kDim;
     hipLaunchKernelGGL(k_out_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st, nrun,

@@ -46,6 +46,16 @@ __device__ __forceinline__ float ldexp_pow2f(int e) {
   return __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
+// Attention weights e = exp(s - m) in [0, 1] kept in 32 bits: bits 61..30
+// of the fp64 pattern (bits 63 and 62 are zero for every value in [0, 1]),
+// rounded to nearest.  The full fp64 exponent range survives (every e down
+// to 2^-1074 keeps a non-zero code) with 22 mantissa bits, a relative
+// rounding error below 2^-23.
+__device__ __forceinline__ uint32_t enc_e(double e) {
+  return (uint32_t)((dbits(e) + (1ull << 29)) >> 30);
+}
+__device__ __forceinline__ double dec_e(uint32_t b) { return bitsd((uint64_t)b << 30); }
+
 // Raw buffer resources (stride 0): the fourth descriptor word of the GFX9
 // family for untyped 32-bit data, and an offset past any buffer this code
 // builds (a load there returns zeros and makes no memory access).

@@ -120,8 +120,8 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 // Decode workspace (one call).  capmax = largest request capacity.
 //   tk     u8  [B][G][d]          key depths
 //   tv     u8  [B][G][capmax]     value depths
-//   ebuf   f32 [B][H][capmax]     exp(s - m_tile) per token (tile = kTile)
-//   e16    f16 [B][H][capmax]     the same rounded to fp16 (value gather)
+//   ebuf   u32 [B][H][capmax]     exp(s - m_tile) per token (tile = kTile),
+//                                 fp64 bits 61..30 (enc_e)
 //   tilepart f64 [B][H][ntile][2] (m_tile, sum of exp) per tile
 //   ftile  f64 [B][H][ntile]      exp(m_tile - m) / Z
 //   aval   f64 [B][G][capmax]     value weights (only when they do not fit
@@ -129,7 +129,7 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 //   opart  f32 [B][H][nchunk][d]  partial outputs, one per run of chunks
 //                                 (at most nchunk runs)
 struct WsLayout {
-  int64_t tk, tv, ebuf, e16, tilepart, ftile, aval, opart, size;
+  int64_t tk, tv, ebuf, tilepart, ftile, aval, opart, size;
   int ntile, nchunk;
 };
 
@@ -141,7 +141,6 @@ RKV_HD WsLayout ws_layout(int B, int H, int G, int d, int64_t capmax) {
   L.tk = off; off = align_up(off + (int64_t)B * G * d, 256);
   L.tv = off; off = align_up(off + (int64_t)B * G * capmax, 256);
   L.ebuf = off; off = align_up(off + (int64_t)B * H * capmax * 4, 256);
-  L.e16 = off; off = align_up(off + (int64_t)B * H * capmax * 2, 256);
   L.tilepart = off; off = align_up(off + (int64_t)B * H * L.ntile * 16, 256);
   L.ftile = off; off = align_up(off + (int64_t)B * H * L.ntile * 8, 256);
   L.aval = off; off = align_up(off + (int64_t)B * G * capmax * 8, 256);

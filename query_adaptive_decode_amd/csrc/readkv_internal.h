@@ -23,6 +23,8 @@ struct DecodeArgs {
   uint8_t* ws;
   uint8_t* key_depths_out;
   uint8_t* value_depths_out;
+  uint64_t* counters;   // NULL, or 4 device words (readkv_decode_attn)
+  int scope;
   int B, H, G, W, dtype;
   int64_t capmax;
   void* const* events;  // NULL, or 5 hipEvent_t recorded around the 4 kernels

@@ -23,13 +23,25 @@ layer activations, which are replaced here by these synthetic caches):
 4. large batch: 28 q / 4 KV heads (GQA 7), batch 64, per-request T0 drawn
    uniformly from [2048, 32768], 16 steps.
 5. encode+decode mix: 32/8 heads, batch 32, T0=16384, 256 steps, R=3 budgets.
+
+Options a test may add to a workload (``workload(id, **overrides)``):
+
+* ``key_ties``: key channel 2k+1 repeats channel 2k in every token, and so
+  does the query, so key weights come in bitwise-equal pairs;
+* ``gap=(Q, D, period)``: the heads of KV group g share a direction u (per
+  request and KV group); their queries are Q u + N(0, 1) noise, and every
+  ``period``-th token (seeded phase) gets D u added to its key, which puts
+  the other tokens a few hundred nats below those peaks;
+* ``q_scale``: the query is multiplied by this factor (near-uniform
+  attention when small);
+* ``q_log2_spread``: query channel c scaled by an exact power of two.
 """
 from __future__ import annotations
 
 import numpy as np
 
 # stream ids for SeedSequence
-_S_K, _S_V, _S_Q, _S_SIGMA, _S_A, _S_NEEDLE, _S_LEN, _S_QBASE = range(8)
+_S_K, _S_V, _S_Q, _S_SIGMA, _S_A, _S_NEEDLE, _S_LEN, _S_QBASE, _S_GAP = range(9)
 
 WORKLOADS = {
     1: dict(name="tiny-1q1kv-d128-T1024", B=1, H=1, G=1, d=128, T0=1024,
@@ -133,8 +145,21 @@ def kv_unit(cfg: dict, b: int, g: int, n_tokens: int | None = None):
             x = x + u @ A.T
         if cfg["structure"] == "needles" and stream == _S_K:
             x = _plant_needles(cfg, b, g, x)
+        if stream == _S_K and cfg.get("gap"):
+            Q, D, period = cfg["gap"]
+            phase = int(_rng(cfg["id"], _S_GAP, b, g, 1).integers(0, period))
+            x = x.copy()
+            x[phase::period] += D * _gap_dir(cfg, b, g)[None, :]
+        if stream == _S_K and cfg.get("key_ties"):
+            x = x.copy()
+            x[:, 1::2] = x[:, 0::2]
         out.append(cast(cfg, x[:n]))
     return out[0], out[1]
+
+
+def _gap_dir(cfg, b, g):
+    u = _rng(cfg["id"], _S_GAP, b, g, 0).standard_normal(cfg["d"])
+    return u / np.linalg.norm(u)
 
 
 def needle_positions(cfg: dict, b: int, g: int) -> np.ndarray:
@@ -172,6 +197,16 @@ def q_step(cfg: dict, b: int, step: int) -> np.ndarray:
         q = _q_base(cfg, b) + 0.1 * r.standard_normal(shape)
     else:
         q = r.standard_t(3.0, size=shape)
+    if cfg.get("gap"):
+        Q = cfg["gap"][0]
+        gqa = cfg["H"] // cfg["G"]
+        u = np.stack([_gap_dir(cfg, b, h // gqa) for h in range(cfg["H"])])
+        q = Q * u + r.standard_normal(shape)
+    if cfg.get("q_scale"):
+        q = q * float(cfg["q_scale"])
+    if cfg.get("key_ties"):
+        q = q.copy()
+        q[:, 1::2] = q[:, 0::2]
     spread = cfg.get("q_log2_spread", 0)
     if spread:
         # channel c scaled by an exact power of two from 2^-spread up to 1:

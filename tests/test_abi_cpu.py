@@ -49,7 +49,7 @@ def test_config_validation_codes():
     assert b.validate_config(ok) == 0
     cases = {
         -1: [dict(W=0), dict(W=9), dict(num_q_heads=30, num_kv_heads=8), dict(batch=0),
-             dict(capacity_tokens=0), dict(num_kv_heads=0)],
+             dict(capacity_tokens=0), dict(num_kv_heads=0), dict(capacity_tokens=(1 << 26) + 1)],
         -4: [dict(kv_dtype=7)],
         -5: [dict(head_dim=64), dict(group_tokens=16), dict(num_q_heads=80, num_kv_heads=8)],
     }
@@ -93,15 +93,24 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.readkv_encode_append(by, fake, fake, fake, None, 257, None) == -2
     assert L.readkv_encode_append(by, fake, None, fake, None, 4, None) == -1
     ws = b.workspace_bytes(cfg)
+    dec = L.readkv_decode_attn
+
+    def call(cfgp=by, store=fake, rk=1.0, rv=1.0, scope=0, vscale=0, wsb=ws):
+        return dec(cfgp, store, fake, rk, rv, scope, vscale, fake, fake, wsb, None, None, None, None)
+
     for rk, rv in [(float("nan"), 1.0), (1.0, float("inf")), (-0.5, 1.0), (1.0, -1.0)]:
-        assert L.readkv_decode_attn(by, fake, fake, rk, rv, 0, fake, fake, ws, None, None, None) == -1
-    assert L.readkv_decode_attn(by, fake, fake, 1.0, 1.0, 5, fake, fake, ws, None, None, None) == -1
-    assert L.readkv_decode_attn(by, fake, fake, 1.0, 1.0, 0, fake, fake, ws - 1, None, None, None) == -3
-    assert L.readkv_decode_attn(by, None, fake, 1.0, 1.0, 0, fake, fake, ws, None, None, None) == -1
+        assert call(rk=rk, rv=rv) == -1
+    assert call(vscale=5) == -1
+    assert call(scope=2) == -1 and call(scope=-1) == -1
+    assert call(scope=1) == -5   # pooled per-layer budgets: not in this build
+    assert call(wsb=ws - 1) == -3
+    assert call(store=None) == -1
     assert L.readkv_store_init(by, fake, 16, None, None) == -3
     bad = b.make_config(batch=2, capacity_tokens=256, head_dim=64)
-    assert L.readkv_decode_attn(ctypes.byref(bad), fake, fake, 1.0, 1.0, 0, fake, fake, ws, None, None,
-                                None) == -5
+    assert call(cfgp=ctypes.byref(bad)) == -5
+    ev = (ctypes.c_void_p * 4)(fake, fake, None, fake)
+    assert L.readkv_decode_attn_timed(by, fake, fake, 1.0, 1.0, 0, 0, fake, fake, ws, None, None, None,
+                                      ctypes.cast(ev, ctypes.c_void_p), None) == -1
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -390,6 +390,46 @@ def test_budget_accounting_and_write_once():
     assert np.array_equal(e1.lo, e2.lo[:e1.n_groups])
 
 
+def test_logical_reads_at_full_depth_equal_the_stored_record():
+    # reading every plane of every closed group (R = W, the full-read limit of
+    # [ReadKV] App. C.3) asks for exactly the bits the store holds for them:
+    # the plane arrays, the metadata arrays and energies, and the open group
+    # slots in use -- sizes from the store's format description
+    from oracle import store_format as F
+    from query_adaptive_decode_amd.synth import round_to_bf16
+    rng = np.random.default_rng(43)
+    d, W = 128, 8
+    for tp, r, dt in [(1024, 0, 0), (1024, 5, 0), (512, 31, 1)]:
+        n = tp + r
+        K = round_to_bf16(rng.standard_normal((n, d)))
+        V = round_to_bf16(rng.standard_normal((n, d)))
+        q = round_to_bf16(rng.standard_normal((2, d)))
+        res = O.decode_unit(q, K, V, R_K=8.0, R_V=8.0)
+        assert res["tK"].min() == W and res["tV"].min() == W
+        esize = 2 if dt == 0 else 4
+        lr = O.logical_reads(res["tK"], res["tV"], n, d, elem_bits=8 * esize)
+        lay = F.region_layout(1, d, W, tp, esize)   # one KV head, capacity tp
+        size = {k: lay[k][1] for k in ("Kplanes", "Vplanes", "Kmeta", "Vmeta", "EK", "EV",
+                                       "Ktail", "Vtail")}
+        assert lr["key_payload"] == 8 * size["Kplanes"]
+        assert lr["value_payload"] == 8 * size["Vplanes"]
+        assert lr["metadata"] == 8 * (size["Kmeta"] + size["Vmeta"] + size["EK"] + size["EV"])
+        assert lr["open_group"] == 8 * (size["Ktail"] + size["Vtail"]) * r // 32
+
+
+def test_nonfinite_query_reads_nothing():
+    from query_adaptive_decode_amd.synth import round_to_bf16
+    rng = np.random.default_rng(47)
+    K = round_to_bf16(rng.standard_normal((100, 128)))
+    V = round_to_bf16(rng.standard_normal((100, 128)))
+    for bad in (np.nan, np.inf, -np.inf):
+        q = round_to_bf16(rng.standard_normal((4, 128)))
+        q[2, 17] = bad
+        res = O.decode_unit(q, K, V, R_K=4.0, R_V=4.0)
+        assert np.isnan(res["out"]).all() and res["out"].shape == (4, 128)
+        assert res["tK"].sum() == 0 and res["tV"].sum() == 0 and len(res["tV"]) == 96
+
+
 # ---------------------------------------------------- P9 reuse model
 def test_reuse_model_printed_values():
     g = GOLD["reuse_overhead_N8192_L128_W8_W0_4"]
