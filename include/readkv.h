@@ -51,6 +51,8 @@ extern "C" {
 #define READKV_EDTYPE (-4)       /* unknown element type                    */
 #define READKV_EUNSUPPORTED (-5) /* valid but not built (d_h != 128, ...)   */
 #define READKV_ELAUNCH (-6)      /* a HIP launch or copy failed             */
+#define READKV_ESCRATCH (-7)     /* workspace need above the fixed scratch of
+                                    readkv_decode_attn_noalloc              */
 
 #define READKV_BF16 0
 #define READKV_F32 1
@@ -188,6 +190,24 @@ int readkv_decode_attn_timed(const readkv_config* cfg, const void* store,
                              uint8_t* value_depths_out,
                              uint64_t* counters_out, void* const* events,
                              void* stream);
+
+/* readkv_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and arguments, minus the workspace,
+ * which is a fixed array of READKV_NOALLOC_SCRATCH_BYTES per GPU held by the
+ * library until the process ends.  Calls whose readkv_workspace_bytes
+ * exceeds it return READKV_ESCRATCH before enqueuing anything.  The call
+ * allocates nothing; its first call on a device looks the array's address
+ * up (make one call before capturing a graph).  Every call on a GPU uses
+ * that GPU's one array: calls that overlap in time on one GPU (different
+ * streams, or graphs replayed concurrently) race and give wrong results. */
+#define READKV_NOALLOC_SCRATCH_BYTES (64u << 20)
+int readkv_decode_attn_noalloc(const readkv_config* cfg, const void* store,
+                               const void* q, float R_K, float R_V,
+                               int32_t scope, int32_t vscale, float* out,
+                               uint8_t* key_depths_out,
+                               uint8_t* value_depths_out,
+                               uint64_t* counters_out, void* stream);
 
 /* Read the store's sticky flags and per-request lengths (host arrays;
  * lengths_out [batch] may be NULL).  Synchronous device-to-host copy. */

@@ -23,7 +23,8 @@ FLAG_NONFINITE, FLAG_OVERFLOW = 1, 2
 
 EXPORTED = ["readkv_validate_config", "readkv_store_bytes", "readkv_workspace_bytes",
             "readkv_store_init", "readkv_encode_append", "readkv_decode_attn",
-            "readkv_decode_attn_timed", "readkv_store_status", "readkv_strerror"]
+            "readkv_decode_attn_timed", "readkv_decode_attn_noalloc", "readkv_store_status",
+            "readkv_strerror"]
 
 
 class Config(ctypes.Structure):
@@ -63,6 +64,8 @@ def lib():
                                    P, P, SZ, P, P, P, P],
             "readkv_decode_attn_timed": [CP, P, P, ctypes.c_float, ctypes.c_float, I32, I32,
                                          P, P, SZ, P, P, P, P, P],
+            "readkv_decode_attn_noalloc": [CP, P, P, ctypes.c_float, ctypes.c_float, I32, I32,
+                                           P, P, P, P, P],
             "readkv_store_status": [CP, P, ctypes.POINTER(ctypes.c_uint32), P],
         }
         for name, args in sig.items():
@@ -178,6 +181,21 @@ def decode_attn_timed(cfg: Config, store, q, R_K, R_V, workspace, events, out=No
         ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(scope),
         int(vscale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(key_depths), _ptr(value_depths), _ptr(counters), ctypes.cast(ev, ctypes.c_void_p),
+        _stream()))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def decode_attn_noalloc(cfg: Config, store, q, R_K, R_V, out, vscale=VSCALE_PHYSICAL,
+                        key_depths=None, value_depths=None, scope=SCOPE_KV_HEAD, counters=None):
+    """decode_attn without a workspace: the library's fixed per-GPU scratch
+    is used, nothing is allocated (``out`` must be given)."""
+    _need_cuda(store, q, out, key_depths, value_depths, counters)
+    _check("readkv_decode_attn_noalloc", lib().readkv_decode_attn_noalloc(
+        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(scope),
+        int(vscale), _ptr(out), _ptr(key_depths), _ptr(value_depths), _ptr(counters),
         _stream()))
     return out
 

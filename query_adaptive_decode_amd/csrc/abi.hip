@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/readkv.h"
@@ -64,6 +65,31 @@ std::vector<uint8_t> header_image(const readkv_config* cfg, const int64_t* req_c
   memcpy(img.data(), &h, sizeof(h));
   *total = off;
   return img;
+}
+
+// Scratch of readkv_decode_attn_noalloc: one fixed array per GPU, in place
+// of a caller-provided workspace.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device (with that device current), and only
+// that address is handed to kernels.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return READKV_ELAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return READKV_ELAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return READKV_OK;
 }
 
 }  // namespace
@@ -209,6 +235,21 @@ int readkv_decode_attn_timed(const readkv_config* cfg, const void* store, const 
                      key_depths_out, value_depths_out, counters_out, events, stream);
 }
 
+int readkv_decode_attn_noalloc(const readkv_config* cfg, const void* store, const void* q,
+                               float R_K, float R_V, int32_t scope, int32_t vscale, float* out,
+                               uint8_t* key_depths_out, uint8_t* value_depths_out,
+                               uint64_t* counters_out, void* stream) {
+  int rc = readkv_validate_config(cfg);
+  if (rc) return rc;
+  const WsLayout L = ws_layout(cfg->batch, cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim,
+                               capmax_of(cfg));
+  if ((size_t)L.size > kScratchBytes) return READKV_ESCRATCH;
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  return decode_impl(cfg, store, q, R_K, R_V, scope, vscale, out, ws, kScratchBytes,
+                     key_depths_out, value_depths_out, counters_out, nullptr, stream);
+}
+
 int readkv_store_status(const readkv_config* cfg, const void* store, uint32_t* flags_out,
                         int64_t* lengths_out) {
   int rc = readkv_validate_config(cfg);
@@ -239,6 +280,7 @@ const char* readkv_strerror(int code) {
     case READKV_EDTYPE: return "unknown element type";
     case READKV_EUNSUPPORTED: return "configuration not supported by this build";
     case READKV_ELAUNCH: return "HIP launch or copy failed";
+    case READKV_ESCRATCH: return "the call needs more workspace than the fixed scratch holds";
     default: return "unknown error";
   }
 }

@@ -108,6 +108,15 @@ def test_entry_points_reject_bad_arguments_before_launch():
     assert L.readkv_store_init(by, fake, 16, None, None) == -3
     bad = b.make_config(batch=2, capacity_tokens=256, head_dim=64)
     assert call(cfgp=ctypes.byref(bad)) == -5
+    # the allocation-free entry point refuses a workspace need above its
+    # fixed scratch before touching a device
+    big = b.make_config(num_q_heads=32, num_kv_heads=8, batch=64, capacity_tokens=32768)
+    assert b.workspace_bytes(big) > b.NOALLOC_SCRATCH_BYTES
+    assert L.readkv_decode_attn_noalloc(ctypes.byref(big), fake, fake, 1.0, 1.0, 0, 0, fake, None, None,
+                                        None, None) == -7
+    assert L.readkv_decode_attn_noalloc(ctypes.byref(bad), fake, fake, 1.0, 1.0, 0, 0, fake, None, None,
+                                        None, None) == -5
+    assert "fixed scratch" in L.readkv_strerror(-7).decode()
     ev = (ctypes.c_void_p * 4)(fake, fake, None, fake)
     assert L.readkv_decode_attn_timed(by, fake, fake, 1.0, 1.0, 0, 0, fake, fake, ws, None, None, None,
                                       ctypes.cast(ev, ctypes.c_void_p), None) == -1
