@@ -153,8 +153,12 @@ int readkv_encode_append(const readkv_config* cfg, void* store,
  *   float32, product in double): B_K = floor(R_K * d_h) key refinements over
  *   the d_h channels, B_V = floor(R_V * T_packed) value refinements over the
  *   tokens of closed groups, per (request, KV head) for
- *   READKV_SCOPE_KV_HEAD.
- * scope: READKV_SCOPE_KV_HEAD (READKV_SCOPE_LAYER: EUNSUPPORTED).
+ *   READKV_SCOPE_KV_HEAD; for READKV_SCOPE_LAYER one B_K = floor(R_K * G *
+ *   d_h) over the G * d_h channels and one B_V = floor(R_V * G * T_packed)
+ *   over the G * T_packed tokens of each request, items ordered by KV head
+ *   then channel / token (ties to the lowest in that order).
+ * scope: READKV_SCOPE_KV_HEAD or READKV_SCOPE_LAYER (the latter needs
+ *   num_kv_heads <= 32, else EUNSUPPORTED).
  * vscale: READKV_VSCALE_PHYSICAL or READKV_VSCALE_UNIT.
  * out: device fp32 [batch][num_q_heads][head_dim].
  * workspace: device, >= readkv_workspace_bytes.

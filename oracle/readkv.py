@@ -27,7 +27,8 @@ reason in the design notes of the repository):
   the physical-scale choice s_g of App. D.2 read per group, or s = 1).
 * Budgets per (request, KV head): B_K = floor(R_K * d_h),
   B_V = floor(R_V * T_packed), R given as float32 ([ReadKV] Sec. 2 uses
-  floor(R d); App. F.1 converts rates to integer increment budgets).
+  floor(R d); App. F.1 converts rates to integer increment budgets); or per
+  request over all its KV heads (decode_request), items ordered by KV head.
 * Tokens of the not-yet-full group are kept exactly and enter the softmax and
   the output, but not the allocation.
 * A query with a non-finite value reads nothing: depths 0, outputs NaN.
@@ -45,7 +46,7 @@ __all__ = [
     "bf16_down", "bf16_up", "encode_stream", "EncodedStream", "prefix",
     "reconstruct", "gain_table", "choose_depths", "key_weights",
     "value_weights", "budget", "decode_unit", "softmax",
-    "reuse_overhead", "reuse_reads", "logical_reads",
+    "reuse_overhead", "reuse_reads", "logical_reads", "decode_request",
 ]
 
 
@@ -328,6 +329,69 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     if diagnostics:
         res.update(Khat=Kfull_hat, Vhat=Vfull_hat, enc_k=enc_k, enc_v=enc_v)
     return res
+
+
+# ----------------------------------------------------------------------------
+# One decode step for one request with per-layer budgets ([ReadKV] Sec. 3.3)
+# ----------------------------------------------------------------------------
+def decode_request(q_all, Ks, Vs, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
+                   vscale="physical", encs=None):
+    """The flexible reader of [ReadKV] Sec. 3.3: one key budget and one
+    value budget for the whole layer of a request instead of one per KV head
+    (the per-head budgets are the GPU reader's restriction of Sec. 5.1 /
+    App. F.8).  Stage 1 runs ChooseDepths over the G * d_h key channels
+    with B_K = floor(R_K * G * d_h); stage 2 over the G * T_packed packed
+    tokens with B_V = floor(R_V * G * T_packed).  Items are ordered by KV
+    head, then channel / token; ties go to the lowest in that order.
+
+    q_all : [H][d] (query heads of the request, H = G * gqa)
+    Ks, Vs: G arrays [T][d] (the request's KV streams)
+    encs  : optional list of (enc_k, enc_v) per KV head
+    Returns out [G][gqa][d], tK [G][d], tV [G][T_packed], the pooled weight
+    vectors wk [G*d], wv [G*T_packed] and budgets BK, BV.  A KV head with a
+    non-finite query value reads nothing (zero weights, NaN outputs).
+    """
+    q_all = np.asarray(q_all, dtype=np.float64)
+    G = len(Ks)
+    d = q_all.shape[1]
+    gqa = q_all.shape[0] // G
+    if encs is None:
+        encs = [(encode_stream(Ks[g], W, group_tokens), encode_stream(Vs[g], W, group_tokens))
+                for g in range(G)]
+    tp = encs[0][0].t_packed
+    gains = gain_table(W)
+    gidx = np.arange(tp) // group_tokens
+    qs = [q_all[g * gqa:(g + 1) * gqa] for g in range(G)]
+    good = [bool(np.isfinite(qs[g]).all()) for g in range(G)]
+
+    # stage 1: pooled key items
+    wk = np.concatenate([key_weights(qs[g], encs[g][0]) if good[g] else np.zeros(d)
+                         for g in range(G)])
+    BK = budget(R_K, G * d)
+    tK = choose_depths(wk, gains, W, BK).reshape(G, d)
+
+    # intermediate decoder, per KV head
+    ahat = []
+    for g in range(G):
+        ek = encs[g][0]
+        Khat = reconstruct(ek.lo[gidx], ek.rng[gidx], prefix(ek.codes, tK[g][None, :], W),
+                           tK[g][None, :])
+        z = (qs[g] @ np.concatenate([Khat, ek.tail], axis=0).T) / math.sqrt(d)
+        ahat.append(softmax(z) if good[g] else np.full(z.shape, np.nan))
+
+    # stage 2: pooled value items
+    wv = np.concatenate([value_weights(ahat[g][:, :tp], encs[g][1], vscale) if good[g]
+                         else np.zeros(tp) for g in range(G)])
+    BV = budget(R_V, G * tp)
+    tV = choose_depths(wv, gains, W, BV).reshape(G, tp)
+
+    out = np.zeros((G, gqa, d))
+    for g in range(G):
+        ev = encs[g][1]
+        Vhat = reconstruct(ev.lo[gidx], ev.rng[gidx], prefix(ev.codes, tV[g][:, None], W),
+                           tV[g][:, None])
+        out[g] = ahat[g] @ np.concatenate([Vhat, ev.tail], axis=0)
+    return dict(out=out, tK=tK, tV=tV, wk=wk, wv=wv, BK=BK, BV=BV, tp=tp)
 
 
 # ----------------------------------------------------------------------------

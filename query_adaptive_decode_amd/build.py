@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libreadkv.so")
-SOURCES = ["abi.hip", "encode.hip", "decode.hip"]
+SOURCES = ["abi.hip", "encode.hip", "alloc.hip", "decode.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -27,7 +27,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, jobs: int = 3) -> str:
+def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile every source to an object (in parallel) and link the shared
     library.  Always recompiles."""
     os.makedirs(LIBDIR, exist_ok=True)

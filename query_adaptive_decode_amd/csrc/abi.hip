@@ -182,10 +182,11 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   if (!isfinite(R_K) || !isfinite(R_V) || R_K < 0.f || R_V < 0.f) return READKV_EINVAL;
   if (vscale != READKV_VSCALE_PHYSICAL && vscale != READKV_VSCALE_UNIT) return READKV_EINVAL;
   if (scope != READKV_SCOPE_KV_HEAD && scope != READKV_SCOPE_LAYER) return READKV_EINVAL;
-  if (scope == READKV_SCOPE_LAYER) return READKV_EUNSUPPORTED;
-  // budgets must fit the 32-bit counters: R * T <= 2^31
-  if ((double)R_V * (double)align_up(cfg->capacity_tokens, kGroup) > 2147483647.0 ||
-      (double)R_K * cfg->head_dim > 2147483647.0)
+  if (scope == READKV_SCOPE_LAYER && cfg->num_kv_heads > kMaxPooledKV) return READKV_EUNSUPPORTED;
+  // budgets must fit the 32-bit counters: R * (items of a domain) <= 2^31
+  const double nu = scope == READKV_SCOPE_LAYER ? (double)cfg->num_kv_heads : 1.0;
+  if ((double)R_V * (double)align_up(cfg->capacity_tokens, kGroup) * nu > 2147483647.0 ||
+      (double)R_K * cfg->head_dim * nu > 2147483647.0)
     return READKV_EINVAL;
   const int64_t capmax = capmax_of(cfg);
   const WsLayout L = ws_layout(cfg->batch, cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim,

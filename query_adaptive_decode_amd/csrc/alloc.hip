@@ -1,0 +1,418 @@
+// The two allocation stages of a ReadKV decode step ("Read What Matters:
+// Query-Adaptive Quantization for KV Caches", Sec. 3.2-3.3, Algorithm 1):
+//
+//   k_key_alloc     (one block per request; per-layer budgets only)
+//                   key weights (Eq. (2)) and ChooseDepths over the request's
+//                   G * d_h key channels -> t^K (per-KV-head budgets are
+//                   allocated in the score kernel's block prologue)
+//   k_value_weights (B*G x chunks of 1024 tokens, all compute units)
+//                   softmax statistics from the score tiles' partials, the
+//                   per-tile factors exp(m_tile - m)/Z, and the value weights
+//                   (Eq. (3)) of every packed token
+//   k_value_select  (one block per selection domain)
+//                   ChooseDepths over the domain's packed tokens -> t^V, and
+//                   the call's logical-read counters
+//
+// A selection domain is one (request, KV head) under per-KV-head budgets,
+// or one request (its G KV heads pooled, item index = KV head * N + item)
+// under per-layer budgets.
+#include <math.h>
+
+#include "kernels_common.h"
+#include "readkv_internal.h"
+#include "select.h"
+
+namespace readkv {
+
+// ---------------------------------------------------------------------------
+// Key allocation under per-layer budgets (per-KV-head budgets are allocated
+// in the score kernel's prologue).  Item i = (KV head g0 + i / d, channel
+// i % d) of the request; w = (sum_{h in S(g)} q_hc^2) * E^K_gc in head order
+// (Eq. (2) with sigma^2 read as the channel's summed squared group range).
+// A KV head with a non-finite query value gets zero weights (it reads
+// nothing).
+// ---------------------------------------------------------------------------
+template <int GQA, int DT, int NUMAX>
+__global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
+                                                   int W, float RK, int NU, uint8_t* tk) {
+  constexpr int NT = 256;
+  constexpr int esize = DT == 0 ? 2 : 4;
+  __shared__ ChooseShared<NT> S;
+  __shared__ double wl[NUMAX * kDim];
+  __shared__ int bad[NUMAX];
+  const int tid = threadIdx.x;
+  const int u0 = blockIdx.x * NU;
+  const int b = u0 / G, g0 = u0 % G;
+  const ReqRecord r = req_of(store, b);
+  if (tid < NU) bad[tid] = 0;
+  __syncthreads();
+  const int N = NU * kDim;
+  for (int i = tid; i < N; i += NT) {
+    const int k = i / kDim, c = i % kDim;
+    const Unit u = unit_of(const_cast<uint8_t*>(store), r, g0 + k, G, kDim, W, esize);
+    double qsq = 0.0;
+    bool nf = false;
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      const double qv = load_elem<DT>(q, ((int64_t)b * H + (int64_t)(g0 + k) * GQA + hh) * kDim + c);
+      nf |= !isfinite(qv);
+      qsq = __dadd_rn(qsq, __dmul_rn(qv, qv));
+    }
+    wl[i] = __dmul_rn(qsq, u.ek[c]);
+    if (nf) bad[k] = 1;
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += NT)
+    if (bad[i / kDim]) wl[i] = 0.0;
+  __syncthreads();
+  const uint32_t Bk = (uint32_t)floor((double)RK * (double)N);
+  uint8_t* const tkd = tk + (int64_t)u0 * kDim;
+  block_choose_depths<NT, 4>(
+      N, Bk, W, [&](int64_t i) { return wl[i]; },
+      [&](int64_t i, uint32_t t) { tkd[i] = (uint8_t)t; }, S);
+}
+
+// ---------------------------------------------------------------------------
+// Value weights.  Block (unit, y) takes tokens [1024 y, 1024 y + 1024) of the
+// unit (four score tiles); thread t takes tokens 4t .. 4t + 3 of the chunk.
+//   m_h = max_tile m_tile, Z_h = sum_tile z_tile exp(m_tile - m_h)
+//   f_{h,tile} = exp(m_tile - m_h) / Z_h         (alpha_hat = e * f)
+//   a_j = (sum_h alpha_hat_hj^2) * s_gamma(j)     (Eq. (3); s = 1 for UNIT)
+// Every block of a unit computes (m_h, Z_h) from the same partials in the
+// same order, so all get identical factors; each writes the factors of its
+// own tiles (the value gather reads them).  A unit with a non-finite query
+// has NaN partials, so its factors and weights are NaN: no value gains.
+// ---------------------------------------------------------------------------
+constexpr int kVChunk = 1024;
+
+template <int GQA>
+__global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int H, int G, int W,
+                                                       int esize, int vscale, int64_t capmax,
+                                                       int ntile_ws, const uint32_t* ebuf,
+                                                       const double* tilepart, double* ftile,
+                                                       double* aval) {
+  constexpr int TPC = kVChunk / kTile;  // score tiles per chunk
+  static_assert(kVChunk == 4 * 256, "four tokens per thread");
+  __shared__ double fs[GQA][TPC];
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const ReqRecord r = req_of(store, b);
+  const int64_t len = r.len;
+  const int64_t Tp = len & ~(int64_t)(kGroup - 1);
+  const int ntile_b = (int)((len + kTile - 1) / kTile);
+  const int t0 = (int)blockIdx.y * TPC;
+  if (t0 >= ntile_b) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
+  // the thread's exponentials and group scale do not depend on the softmax
+  // statistics: they are in flight while those are formed (a thread past
+  // the packed tokens loads token 0's and drops them)
+  const int64_t j0 = (int64_t)t0 * kTile + 4 * tid;
+  const bool act = j0 < Tp;  // Tp is a multiple of 32: all four tokens or none
+  const int64_t jc = act ? j0 : 0;
+  uint4 ev[GQA];
+#pragma unroll
+  for (int hh = 0; hh < GQA; ++hh)
+    ev[hh] = *reinterpret_cast<const uint4*>(ebuf + (hrow0 + hh) * capmax + jc);
+  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
+  const double sg = vscale == 0 ? u.ev[jc / kGroup] : 1.0;
+  for (int hh = wv; hh < GQA; hh += 4) {
+    const double* tp = tilepart + (hrow0 + hh) * ntile_ws * 2;
+    double m = -INFINITY;
+    for (int t = lane; t < ntile_b; t += 64) m = fmax(m, tp[2 * t]);
+    m = wave_max(m);
+    double Z = 0.0;
+    for (int t = lane; t < ntile_b; t += 64) Z += tp[2 * t + 1] * exp(tp[2 * t] - m);
+    Z = wave_sum(Z);
+    if (lane < TPC && t0 + lane < ntile_b) {
+      const double f = exp(tp[2 * (t0 + lane)] - m) / Z;
+      fs[hh][lane] = f;
+      ftile[(hrow0 + hh) * ntile_ws + t0 + lane] = f;
+    }
+  }
+  __syncthreads();
+  if (!act) return;
+  const int tl = (4 * tid) / kTile;
+  double s[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int hh = 0; hh < GQA; ++hh) {
+    const double f = fs[hh][tl];
+    const uint32_t e4[4] = {ev[hh].x, ev[hh].y, ev[hh].z, ev[hh].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const double x = __dmul_rn(dec_e(e4[k]), f);
+      s[k] = __dadd_rn(s[k], __dmul_rn(x, x));
+    }
+  }
+  if (vscale == 0) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) s[k] = __dmul_rn(s[k], sg);
+  }
+  double2* const ap = reinterpret_cast<double2*>(aval + ((int64_t)b * G + g) * capmax + j0);
+  ap[0] = make_double2(s[0], s[1]);
+  ap[1] = make_double2(s[2], s[3]);
+}
+
+// ---------------------------------------------------------------------------
+// Value selection: ChooseDepths over the domain's packed tokens with
+// B_V = floor(R_V * N), N = NU * T_packed; item i = (KV head g0 + i / T_p,
+// token i % T_p).  Then the call's logical reads of the domain ([ReadKV]
+// App. A.1): key payload T_p * sum_c t^K_c, value payload d * sum_j t^V_j,
+// metadata (lo and rng of every closed group and channel of keys and values,
+// E^K, E^V), the open group's keys and values.
+// ---------------------------------------------------------------------------
+constexpr int kVSelNT = 1024;
+// domains of up to this many tokens are copied to LDS once (8 bytes each)
+constexpr int kVSelLocal = 16384;
+
+template <bool LOCAL>
+__global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, int G, int W,
+                                                          int esize, float RV, int NU,
+                                                          int64_t capmax, const double* aval,
+                                                          uint8_t* tv, const uint8_t* tk,
+                                                          uint64_t* counters) {
+  constexpr int NT = kVSelNT;
+  __shared__ ChooseShared<NT> S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int u0 = blockIdx.x * NU;
+  const int b = u0 / G;
+  const ReqRecord r = req_of(store, b);
+  const int64_t len = r.len;
+  const int64_t Tp = len & ~(int64_t)(kGroup - 1);
+  const int64_t N = (int64_t)NU * Tp;
+  const uint32_t Bv = (uint32_t)floor((double)RV * (double)N);
+  const double* const ab = aval + (int64_t)u0 * capmax;
+  uint8_t* const tvb = tv + (int64_t)u0 * capmax;
+  auto at = [&](int64_t i) -> int64_t {  // item -> offset in the unit-major arrays
+    if (NU == 1) return i;
+    const int64_t k = i / Tp;
+    return k * capmax + (i - k * Tp);
+  };
+  extern __shared__ double acache[];  // [N] when LOCAL
+  uint32_t mine;
+  if constexpr (LOCAL) {
+    // eight loads in flight per thread, then their LDS stores
+    for (int64_t i0 = 0; i0 < N; i0 += 8 * NT) {
+      double v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t i = i0 + k * NT + tid;
+        v[k] = i < N ? ab[at(i)] : 0.0;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int64_t i = i0 + k * NT + tid;
+        if (i < N) acache[i] = v[k];
+      }
+    }
+    __syncthreads();
+    mine = block_choose_depths<NT, 4>(
+        N, Bv, W, [&](int64_t i) { return acache[i]; },
+        [&](int64_t i, uint32_t t) { tvb[at(i)] = (uint8_t)t; }, S);
+  } else {
+    mine = block_choose_depths<NT, 8>(
+        N, Bv, W, [&](int64_t i) { return ab[at(i)]; },
+        [&](int64_t i, uint32_t t) { tvb[at(i)] = (uint8_t)t; }, S);
+  }
+  if (counters) {
+    const uint32_t vtot = block_sum_u32<NT>(mine, S.wsum);
+    if (tid < 64) {
+      int ks = 0;
+      for (int i = lane; i < NU * kDim; i += 64) ks += tk[(int64_t)u0 * kDim + i];
+      ks = wave_sum_i32(ks);
+      if (lane == 0) {
+        const unsigned long long ng = (unsigned long long)(Tp / kGroup), nu = (unsigned long long)NU;
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1), (unsigned long long)vtot * kDim);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2),
+                  nu * (2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull));
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
+                  nu * 2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Value allocation under per-KV-head budgets when the unit's capacity fits
+// LDS (up to kVSelLocal tokens): one block per (request, KV head) forms the
+// softmax statistics and factors, the weights a_j of every packed token
+// straight into LDS (exactly as k_value_weights), then ChooseDepths over
+// them (as k_value_select) and the read counters.  Thread t takes tokens
+// 4t .. 4t + 3 of each round of 4096; the first round's exponentials are in
+// flight while the statistics are formed.
+// ---------------------------------------------------------------------------
+template <int GQA>
+__global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
+    const uint8_t* store, int H, int G, int W, int esize, int vscale, float RV, int64_t capmax,
+    int ntile_ws, const uint32_t* ebuf, const double* tilepart, double* ftile, uint8_t* tv,
+    const uint8_t* tk, uint64_t* counters) {
+  constexpr int NT = kVSelNT;
+  constexpr int RT = 4 * NT;  // tokens per round
+  __shared__ ChooseShared<NT> S;
+  __shared__ double fs[GQA][kVSelLocal / kTile];
+  extern __shared__ double acache[];  // [T_p]
+  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const ReqRecord r = req_of(store, b);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
+  const int64_t len = r.len;
+  const int64_t Tp = len & ~(int64_t)(kGroup - 1);
+  const int ntile_b = (int)((len + kTile - 1) / kTile);
+  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
+  auto load_round = [&](int k, uint4 (&ev)[GQA], double& sg) __attribute__((always_inline)) {
+    const int64_t j0 = (int64_t)k * RT + 4 * tid;
+    const int64_t jc = j0 < Tp ? j0 : 0;  // (a thread past the tokens loads token 0's)
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh)
+      ev[hh] = *reinterpret_cast<const uint4*>(ebuf + (hrow0 + hh) * capmax + jc);
+    sg = vscale == 0 ? u.ev[jc / kGroup] : 1.0;
+  };
+  uint4 ev[GQA];
+  double sg;
+  load_round(0, ev, sg);
+  for (int hh = wv; hh < GQA; hh += NT / 64) {
+    const double* tp = tilepart + (hrow0 + hh) * ntile_ws * 2;
+    // one tile per lane (at most 64 tiles in a unit that fits LDS)
+    const double mt = lane < ntile_b ? tp[2 * lane] : -INFINITY;
+    const double zt = lane < ntile_b ? tp[2 * lane + 1] : 0.0;
+    const double m = wave_max(mt);
+    const double x = lane < ntile_b ? exp(mt - m) : 0.0;
+    const double Z = wave_sum(zt * x);
+    if (lane < ntile_b) {
+      const double f = x / Z;
+      fs[hh][lane] = f;
+      ftile[(hrow0 + hh) * ntile_ws + lane] = f;
+    }
+  }
+  __syncthreads();
+  const int nr = (int)((Tp + RT - 1) / RT);
+  for (int k = 0; k < nr; ++k) {
+    if (k > 0) load_round(k, ev, sg);
+    const int64_t j0 = (int64_t)k * RT + 4 * tid;
+    if (j0 < Tp) {  // Tp is a multiple of 32: all four tokens or none
+      const int tl = (int)(j0 / kTile);
+      double sa[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) {
+        const double f = fs[hh][tl];
+        const uint32_t e4[4] = {ev[hh].x, ev[hh].y, ev[hh].z, ev[hh].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const double xq = __dmul_rn(dec_e(e4[q]), f);
+          sa[q] = __dadd_rn(sa[q], __dmul_rn(xq, xq));
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acache[j0 + q] = vscale == 0 ? __dmul_rn(sa[q], sg) : sa[q];
+    }
+  }
+  __syncthreads();
+  const uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
+  uint8_t* const tvb = tv + ((int64_t)b * G + g) * capmax;
+  const uint32_t mine = block_choose_depths<NT, 4>(
+      Tp, Bv, W, [&](int64_t i) { return acache[i]; },
+      [&](int64_t i, uint32_t t) { tvb[i] = (uint8_t)t; }, S);
+  if (counters) {
+    const uint32_t vtot = block_sum_u32<NT>(mine, S.wsum);
+    if (tid < 64) {
+      const uint8_t* tkb = tk + ((int64_t)b * G + g) * kDim;
+      const int ks = wave_sum_i32((int)tkb[lane] + (int)tkb[lane + 64]);
+      if (lane == 0) {
+        const unsigned long long ng = (unsigned long long)(Tp / kGroup);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1), (unsigned long long)vtot * kDim);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2),
+                  2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
+                  2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int GQA, int DT>
+static void key_alloc_gqa(const DecodeArgs& a, uint8_t* tk, hipStream_t st) {
+  const int NU = a.G;  // per-layer budgets: one selection per request
+  hipLaunchKernelGGL((k_key_alloc<GQA, DT, kMaxPooledKV>), dim3(a.B), dim3(256), 0, st,
+                     (const uint8_t*)a.store, a.q, a.H, a.G, a.W, a.RK, NU, tk);
+}
+
+template <int DT>
+static int key_alloc_dt(const DecodeArgs& a, uint8_t* tk, hipStream_t st) {
+  switch (a.H / a.G) {
+    case 1: key_alloc_gqa<1, DT>(a, tk, st); return 0;
+    case 2: key_alloc_gqa<2, DT>(a, tk, st); return 0;
+    case 3: key_alloc_gqa<3, DT>(a, tk, st); return 0;
+    case 4: key_alloc_gqa<4, DT>(a, tk, st); return 0;
+    case 5: key_alloc_gqa<5, DT>(a, tk, st); return 0;
+    case 6: key_alloc_gqa<6, DT>(a, tk, st); return 0;
+    case 7: key_alloc_gqa<7, DT>(a, tk, st); return 0;
+    case 8: key_alloc_gqa<8, DT>(a, tk, st); return 0;
+    default: return -5;
+  }
+}
+
+int launch_key_alloc(const DecodeArgs& a, uint8_t* tk, hipStream_t st) {
+  return a.dtype == 0 ? key_alloc_dt<0>(a, tk, st) : key_alloc_dt<1>(a, tk, st);
+}
+
+// per-KV-head budgets and a capacity that fits LDS: one fused launch;
+// otherwise value weights (all compute units) then the selection
+template <int GQA>
+static bool value_first_gqa(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk, uint8_t* tv,
+                            hipStream_t st) {
+  if (a.scope == 0 && a.capmax <= kVSelLocal) {
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_value_alloc_unit<GQA>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, kVSelLocal * 8);
+      attr_set = true;
+    }
+    hipLaunchKernelGGL((k_value_alloc_unit<GQA>), dim3(a.B * a.G), dim3(kVSelNT), (size_t)a.capmax * 8,
+                       st, (const uint8_t*)a.store, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.RV,
+                       a.capmax, L.ntile, (const uint32_t*)(a.ws + L.ebuf),
+                       (const double*)(a.ws + L.tilepart), (double*)(a.ws + L.ftile), tv, tk,
+                       a.counters);
+    return true;
+  }
+  const int nch = (int)((a.capmax + kVChunk - 1) / kVChunk);
+  hipLaunchKernelGGL((k_value_weights<GQA>), dim3(a.B * a.G, nch), dim3(256), 0, st,
+                     (const uint8_t*)a.store, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.capmax,
+                     L.ntile, (const uint32_t*)(a.ws + L.ebuf), (const double*)(a.ws + L.tilepart),
+                     (double*)(a.ws + L.ftile), (double*)(a.ws + L.aval));
+  return false;
+}
+
+int launch_value_alloc(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk, uint8_t* tv,
+                       hipStream_t st) {
+  bool done;
+  switch (a.H / a.G) {
+    case 1: done = value_first_gqa<1>(a, L, tk, tv, st); break;
+    case 2: done = value_first_gqa<2>(a, L, tk, tv, st); break;
+    case 3: done = value_first_gqa<3>(a, L, tk, tv, st); break;
+    case 4: done = value_first_gqa<4>(a, L, tk, tv, st); break;
+    case 5: done = value_first_gqa<5>(a, L, tk, tv, st); break;
+    case 6: done = value_first_gqa<6>(a, L, tk, tv, st); break;
+    case 7: done = value_first_gqa<7>(a, L, tk, tv, st); break;
+    case 8: done = value_first_gqa<8>(a, L, tk, tv, st); break;
+    default: return -5;
+  }
+  if (done) return 0;
+  const int NU = a.scope == 1 ? a.G : 1;
+  const int64_t nmax = (int64_t)NU * a.capmax;  // items of a domain, at most
+  const bool local = nmax <= kVSelLocal;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_value_select<true>),
+                        hipFuncAttributeMaxDynamicSharedMemorySize, kVSelLocal * 8);
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(local ? &k_value_select<true> : &k_value_select<false>, dim3(a.B * a.G / NU),
+                     dim3(kVSelNT), local ? (size_t)nmax * 8 : 0, st,
+                     (const uint8_t*)a.store, a.G, a.W, a.dtype == 0 ? 2 : 4, a.RV, NU, a.capmax,
+                     (const double*)(a.ws + L.aval), tv, tk, a.counters);
+  return 0;
+}
+
+}  // namespace readkv

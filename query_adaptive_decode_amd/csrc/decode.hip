@@ -1,22 +1,28 @@
 // One ReadKV decode step ("Read What Matters: Query-Adaptive Quantization
-// for KV Caches", Sec. 3.2-3.3, Algorithm 1) as four launches on one stream:
+// for KV Caches", Sec. 3.2-3.3, Algorithm 1) as five launches on one stream
+// (six under per-layer budgets):
 //
-//   k_score       (B*G x runs)        key weights (Eq. (2)) and ChooseDepths
-//                                     over the d_h channels -> t^K (block
-//                                     prologue), then the prefix-gather of
-//                                     the chosen key planes through LDS,
-//                                     reconstructed logits in fp64, per-tile
-//                                     max and sum of exp (split-context
-//                                     softmax)
-//   k_value_alloc (B*G blocks)        softmax statistics, value weights
-//                                     (Eq. (3)) and ChooseDepths over the
-//                                     packed tokens -> t^V
-//   k_gather      (B*G x runs)        prefix-gather of the chosen value
-//                                     planes, attention-weighted sums per
-//                                     run of chunks
-//   k_out_reduce  (B*H*d threads)     run partials summed in run order
+//   k_key_alloc      (requests)           per-layer budgets only: key
+//                                         weights (Eq. (2)) and ChooseDepths
+//                                         over a request's G*d_h channels
+//                                         -> t^K (alloc.hip)
+//   k_score          (B*G x runs)         per-KV-head budgets: key weights and
+//                                         ChooseDepths over the unit's d_h
+//                                         channels (block prologue); then the
+//                                         prefix-gather of the chosen key
+//                                         planes through LDS, reconstructed
+//                                         logits in fp64, per-tile max and
+//                                         sum of exp (split-context softmax)
+//   k_value_weights  (B*G x chunks)       softmax statistics and value
+//                                         weights (Eq. (3)) (alloc.hip)
+//   k_value_select   (domains)            ChooseDepths over the packed
+//                                         tokens -> t^V (alloc.hip)
+//   k_gather         (B*G x runs)         prefix-gather of the chosen value
+//                                         planes, attention-weighted sums per
+//                                         run of chunks
+//   k_out_reduce     (B*H*d threads)      run partials summed in run order
 //
-// The k_value_alloc -> k_gather boundary is the staged(2) reader's second
+// The value selection -> gather boundary is the staged(2) reader's second
 // batch: value reads depend on attention computed from the first batch.
 //
 // Reconstruction of a depth-t prefix P (t MSB-first planes) of a group with
@@ -335,6 +341,7 @@ __device__ __forceinline__ double half_sum(double v) {
 
 template <int GQA, int DT>
 __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* store, const void* q, uint8_t* tk,
+                                                  int tk_ready,
                                                   int H, int G, int W, float RK, int64_t capmax,
                                                   int ntile_ws, uint32_t* ebuf,
                                                   double* tilepart, uint64_t* counters) {
@@ -365,8 +372,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   __shared__ uint32_t wtot[2];
   __shared__ uint32_t dcnt[2][9];  // channels per depth value, per wave
 
-  // the call's read counters start from zero (they are added to by the
-  // value allocation, the next launch)
+  // the call's read counters start from zero (the value selection, a later
+  // launch, adds to them)
   if (counters && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0ull;
   const int b = blockIdx.x / G, g = blockIdx.x % G;
   const ReqRecord r = req_of(store, b);
@@ -379,7 +386,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   const int tile_begin = (int)blockIdx.y;
   if (tile_begin >= ntl) {
     // an empty request has no closed group (E^K = 0): all key depths are 0
-    if (ntl == 0 && blockIdx.y == 0 && threadIdx.x < kDim) tk[((int64_t)b * G + g) * kDim + threadIdx.x] = 0;
+    if (!tk_ready && ntl == 0 && blockIdx.y == 0 && threadIdx.x < kDim)
+      tk[((int64_t)b * G + g) * kDim + threadIdx.x] = 0;
     return;
   }
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
@@ -403,11 +411,12 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   load_meta(tile_begin);  // independent of the depths: in flight during the setup
 
   // ---- once per block: depths, query, per-head digit scale, slot table ----
-  // key allocation of the unit (every block of the unit computes it; the
-  // first writes it out): w_c = (sum_h q_hc^2) E^K_c in head order, then
-  // ChooseDepths over the channels by wave 0
-  // A query with a non-finite value reads nothing: its unit's key weights
-  // are zero (depths 0) and its softmax statistics NaN, so that no value is
+  // Key allocation of the unit: under per-layer budgets it comes from the
+  // key allocation launch (tk_ready); otherwise every block of the unit
+  // computes it (w_c = (sum_h q_hc^2) E^K_c in head order, then ChooseDepths
+  // over the channels by wave 0) and the unit's first block writes it out.
+  // A query with a non-finite value reads nothing: its unit's key weights are
+  // zero (depths 0) and its softmax statistics NaN, so that no value is
   // refined and every output of the unit is NaN.
   double ek = 0.0;
   bool qnf = false;
@@ -425,22 +434,25 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
       qnf |= !isfinite(qv[hh]);
       qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
     }
-    kap[c] = __dmul_rn(qsq, ek);  // the key weight, until kap is set below
+    if (tk_ready) tks[c] = tk[((int64_t)b * G + g) * kDim + c];
+    else kap[c] = __dmul_rn(qsq, ek);  // the key weight, until kap is set below
   }
   const bool qbad = __syncthreads_or(qnf);
-  if (wv == 0) {
-    const double w2[2] = {qbad ? 0.0 : kap[lane], qbad ? 0.0 : kap[lane + 64]};
-    uint32_t sel[2];
-    key_depths_wave(w2, W, (uint32_t)floor((double)RK * (double)kDim),
-                    reinterpret_cast<uint32_t*>(planes), sel);
-    tks[lane] = (uint8_t)sel[0];
-    tks[lane + 64] = (uint8_t)sel[1];
-    if (tile_begin == 0) {  // the unit's first block writes the depths out
-      tk[((int64_t)b * G + g) * kDim + lane] = (uint8_t)sel[0];
-      tk[((int64_t)b * G + g) * kDim + lane + 64] = (uint8_t)sel[1];
+  if (!tk_ready) {
+    if (wv == 0) {
+      const double w2[2] = {qbad ? 0.0 : kap[lane], qbad ? 0.0 : kap[lane + 64]};
+      uint32_t sel[2];
+      key_depths_wave(w2, W, (uint32_t)floor((double)RK * (double)kDim),
+                      reinterpret_cast<uint32_t*>(planes), sel);
+      tks[lane] = (uint8_t)sel[0];
+      tks[lane + 64] = (uint8_t)sel[1];
+      if (tile_begin == 0) {  // the unit's first block writes the depths out
+        tk[((int64_t)b * G + g) * kDim + lane] = (uint8_t)sel[0];
+        tk[((int64_t)b * G + g) * kDim + lane + 64] = (uint8_t)sel[1];
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
   uint32_t tv_ = 0, inc = 0, below = 0;
   if (tid < kDim) {
     const int c = tid;
@@ -847,468 +859,6 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
 }
 
 // ---------------------------------------------------------------------------
-// Value allocation: one block of 1024 threads per (request, KV head).
-//   m_h = max_tile m_tile, Z_h = sum_tile z_tile exp(m_tile - m_h)
-//   f_{h,tile} = exp(m_tile - m_h) / Z_h         (alpha_hat = e * f)
-//   a_j = (sum_h alpha_hat_hj^2) * s_gamma(j)     (Eq. (3))
-// then ChooseDepths with B_V = floor(R_V * T_packed) over the (token, level)
-// gains a_j 4^-t (t = 1..W), ties to the lowest token.
-// Token j = 2048 k + 128 w + 2 l + s belongs to lane l of wave w in round k
-// (s = 0, 1): the 128 tokens of a wave in one round lie in one tile, so the
-// per-tile factors are LDS broadcasts.
-// Threshold.  A token whose a_j is a normal double with exponent field
-// E > 2W ("regular") has its W gains at fields E - 2t, all with a_j's
-// mantissa, so it holds min(W, max(0, floor((E - L) / 2))) gains at field L
-// or above.  An LDS histogram of the regular tokens' fields (and of the
-// fields of the other positive a_j's products, formed one by one: subnormal
-// products, infinities) gives the count at every field; one wave scans it
-// from the top for the field L* of the B_V-th largest gain.  Within field L* the
-// gains are ranked by mantissa with 11/11/10/10/10-bit radix passes, which
-// stop once the gains sharing the chosen digits are exactly the ones still
-// to be taken.
-// ---------------------------------------------------------------------------
-constexpr int kVNT = 1024;
-constexpr int kVRound = 2 * kVNT;  // tokens per round
-constexpr int kVRMAX = 8;          // most rounds whose weights stay in registers
-
-// RMAX > 0: the weights of RMAX rounds stay in registers (a capacity of at
-// most RMAX * kVRound tokens); RMAX == 0: they go through aval
-// One wave: the gain-field histogram G[f] = hB[f] + sum_{t=1..W} hA[f + 2t]
-// (hA counts regular tokens by exponent field, hB odd products by field;
-// W <= 8) is formed in registers and scanned from the top field down for
-// the field where the count reaches rem (>= 1).  out[0] = field, out[1] =
-// count above it, out[2] = G[field] (all three only if the total reaches
-// rem), out[3] = total count.
-__device__ __forceinline__ void wave_find_gain_field(const uint32_t* hA, const uint32_t* hB, int W,
-                                                     uint32_t rem, uint32_t* out) {
-  constexpr int PER = 32;
-  const int l = __lane_id();
-  const int base = 2048 - (l + 1) * PER;  // lane l: fields base .. base + 31
-  uint32_t w[PER + 16];                   // hA[base .. base + 47], 0 past the end
-#pragma unroll
-  for (int i = 0; i < (PER + 16) / 4; ++i) {
-    const int idx = base + 4 * i;
-    uint4 v = *reinterpret_cast<const uint4*>(hA + min(idx, 2044));
-    if (idx >= 2048) v = make_uint4(0u, 0u, 0u, 0u);
-    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-  }
-  uint32_t G[PER];
-#pragma unroll
-  for (int i = 0; i < PER / 4; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(hB + base + 4 * i);
-    G[4 * i] = v.x; G[4 * i + 1] = v.y; G[4 * i + 2] = v.z; G[4 * i + 3] = v.w;
-  }
-#pragma unroll
-  for (int t = 1; t <= 8; ++t) {
-    if (t > W) break;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) G[i] += w[i + 2 * t];
-  }
-  uint32_t tot = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) tot += G[i];
-  const uint32_t incl = wave_incl_scan_u32(tot);
-  if (l == 63) out[3] = incl;
-  const uint64_t bal = __ballot(incl >= rem);
-  const int L = bal ? __ffsll((unsigned long long)bal) - 1 : -1;
-  if (l == L) {
-    uint32_t c = incl - tot;
-#pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {
-      if (c + G[i] >= rem) {
-        out[0] = (uint32_t)(base + i);
-        out[1] = c;
-        out[2] = G[i];
-        break;
-      }
-      c += G[i];
-    }
-  }
-}
-
-template <int GQA, int RMAX>
-__global__ __launch_bounds__(1024) void k_value_alloc(const uint8_t* store, int H, int G, int W,
-                                                      int esize, float RV, int vscale,
-                                                      int64_t capmax, int ntile_ws,
-                                                      const uint32_t* ebuf, const double* tilepart,
-                                                      double* ftile, double* aval, uint8_t* tv,
-                                                      const uint8_t* tk, uint64_t* counters) {
-  constexpr int NT = kVNT;
-  constexpr int NW = NT / 64;
-  constexpr bool REG = RMAX > 0;
-  constexpr int kVTileMax = RMAX * kVRound / kTile;
-  static_assert(kTile % 128 == 0 && kVRound % kTile == 0, "a wave's tokens of one round lie in one tile");
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
-  const ReqRecord r = req_of(store, b);  // (a scalar load; waited for below)
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const uint32_t* eb = ebuf + ((int64_t)b * H + (int64_t)g * GQA) * capmax;
-  const int jl = 128 * wv + 2 * lane;  // first token of the lane in round 0
-  auto tok0 = [&](int k) -> int64_t { return (int64_t)kVRound * k + jl; };
-  // register path: RB rounds of exponentials in flight at a time, the first
-  // batch already during the softmax statistics
-  constexpr int RB0 = RMAX * GQA <= 20 ? RMAX : (GQA >= 8 ? 2 : (GQA >= 4 ? 4 : 8));
-  constexpr int RB = REG ? (RB0 < RMAX ? RB0 : RMAX) : 1;
-  // The first vector loads do not depend on the request record and go out
-  // while it is in flight, all unconditional (a branch around them would
-  // make the first wait for the tile partials also wait for the
-  // exponentials): this wave's tile partials (waves past GQA read the last
-  // head's and drop them; entries past the request's tiles are dropped too),
-  // then the first batch of exponentials (rounds past the row load its
-  // first token; tokens past the closed groups come out as zero weights).
-  const double* tp = tilepart + ((int64_t)b * H + (int64_t)g * GQA + min(wv, GQA - 1)) * ntile_ws * 2;
-  const double2 p0 = *reinterpret_cast<const double2*>(tp + 2 * min(lane, ntile_ws - 1));
-  asm volatile("" ::: "memory");  // the statistics wait for the partials alone
-  uint2 e0[RB][GQA];
-  if constexpr (REG) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int64_t j0 = tok0(i);
-      const int64_t jc = j0 < capmax ? j0 : 0;  // capmax is a multiple of 32
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh)
-        e0[i][hh] = *reinterpret_cast<const uint2*>(eb + (int64_t)hh * capmax + jc);
-    }
-  }
-  asm volatile("" ::: "memory");  // issued before the record is waited for
-  const int64_t len = r.len;
-  const int64_t Tp = len & ~(int64_t)(kGroup - 1);
-  const int ntile_b = (int)((len + kTile - 1) / kTile);
-  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-
-  __shared__ __align__(16) uint32_t hA[2048];
-  __shared__ __align__(16) uint32_t hB[2048];
-  __shared__ __align__(16) uint32_t hC[2048];
-  __shared__ double fs[REG ? GQA * kVTileMax : 1];
-  __shared__ double evs[REG ? RMAX * kVRound / kGroup : 1];
-  __shared__ uint32_t wsum[NW + 1];
-  __shared__ uint32_t sh[4];
-
-  const int nr = (int)((Tp + kVRound - 1) / kVRound);
-  double* fg = ftile + ((int64_t)b * H + (int64_t)g * GQA) * ntile_ws;
-  double* ab = aval + ((int64_t)b * G + g) * capmax;
-  uint8_t* tvb = tv + ((int64_t)b * G + g) * capmax;
-  auto load_e = [&](int k, uint2* e) __attribute__((always_inline)) {
-    const int64_t j0 = tok0(k);
-    const int64_t jc = j0 < Tp ? j0 : 0;  // Tp > 0 whenever a round exists
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh)
-      e[hh] = *reinterpret_cast<const uint2*>(eb + (int64_t)hh * capmax + jc);
-  };
-  // one group scale per thread (rounds past the tokens load clamped
-  // addresses: no branches, so nothing waits on a merge of paths)
-  const int ngrp = (int)(Tp / kGroup);
-  const double evr = REG ? u.ev[min(tid, max(ngrp - 1, 0))] : 0.0;
-
-  // ---- softmax statistics -> per-tile factors (wave h handles head h) ----
-  if (wv < GQA) {
-    // the lane's first tile is in registers (all of them up to 64 tiles)
-    const double m0 = lane < ntile_b ? p0.x : -INFINITY, z0 = lane < ntile_b ? p0.y : 0.0;
-    double m = m0;
-    for (int t = lane + 64; t < ntile_b; t += 64) m = fmax(m, tp[2 * t]);
-    m = wave_max(m);
-    const double x0 = lane < ntile_b ? exp(m0 - m) : 0.0;
-    double Z = z0 * x0;
-    for (int t = lane + 64; t < ntile_b; t += 64) Z += tp[2 * t + 1] * exp(tp[2 * t] - m);
-    Z = wave_sum(Z);
-    auto put_f = [&](int t, double f) {
-      fg[(int64_t)wv * ntile_ws + t] = f;
-      if constexpr (REG) fs[wv * kVTileMax + t] = f;
-    };
-    if (lane < ntile_b) put_f(lane, x0 / Z);
-    for (int t = lane + 64; t < ntile_b; t += 64) put_f(t, exp(tp[2 * t] - m) / Z);
-  }
-  static_assert(!REG || RMAX * kVRound / kGroup <= NT, "one group scale per thread");
-  if constexpr (REG) {
-    if (tid < ngrp) evs[tid] = evr;
-  }
-  if (tid == 0) { sh[0] = 0u; sh[1] = 0u; sh[2] = 0u; sh[3] = 0u; }
-  for (int i = tid; i < 2048; i += NT) { hA[i] = 0u; hB[i] = 0u; hC[i] = 0u; }
-  if constexpr (REG) {
-    lds_barrier();  // the exponentials stay in flight
-  } else {
-    __threadfence_block();  // ftile is read back through memory
-    __syncthreads();
-  }
-
-  // ---- value weights ----
-  // the lane's two weights of round k from its exponentials e[hh]
-  auto weights = [&](int k, const uint2* e, double& a0, double& a1) __attribute__((always_inline)) {
-    const int64_t j0 = tok0(k);
-    const bool in = j0 < Tp;  // Tp is even: both tokens or neither
-    const int tl = in ? (kVRound / kTile) * k + (128 * wv) / kTile : 0;
-    double s0 = 0.0, s1 = 0.0;
-#pragma unroll
-    for (int hh = 0; hh < GQA; ++hh) {
-      const double f = REG ? fs[hh * kVTileMax + tl] : fg[(int64_t)hh * ntile_ws + tl];
-      const double x0 = __dmul_rn(dec_e(e[hh].x), f), x1 = __dmul_rn(dec_e(e[hh].y), f);
-      s0 = __dadd_rn(s0, __dmul_rn(x0, x0));
-      s1 = __dadd_rn(s1, __dmul_rn(x1, x1));
-    }
-    if (vscale == 0) {
-      const int64_t gi = in ? j0 / kGroup : 0;
-      const double sg = REG ? evs[gi] : u.ev[gi];
-      s0 = __dmul_rn(s0, sg);
-      s1 = __dmul_rn(s1, sg);
-    }
-    a0 = in ? s0 : 0.0;
-    a1 = in ? s1 : 0.0;
-  };
-
-  // per token: exponent field when regular, else kNoField; tokens that are
-  // positive but not regular are "odd" (products formed one by one)
-  constexpr int kNoField = -8192;
-  const int twoW = 2 * W;
-  double areg[REG ? RMAX : 1][2];
-  int freg[REG ? RMAX : 1][2];  // field_of(areg)
-  bool any_odd = false;
-  auto field_of = [&](double a) __attribute__((always_inline)) -> int {
-    const int E = (int)(dbits(a) >> 52);
-    return (a > 0.0 && E > twoW && E < 2047) ? E : kNoField;
-  };
-  // field, odd flag and the exponent histogram hA[E] of regular tokens
-  auto classify = [&](double a) __attribute__((always_inline)) -> int {
-    const int ef = field_of(a);
-    any_odd |= a > 0.0 && ef == kNoField;
-    if (ef != kNoField) atomicAdd(&hA[ef], 1u);
-    return ef;
-  };
-  if constexpr (REG) {
-    if (nr > 0) {
-#pragma unroll
-      for (int k0 = 0; k0 < RMAX; k0 += RB) {
-        if (k0 >= nr) {  // uniform; a whole batch is skipped or run
-#pragma unroll
-          for (int i = 0; i < RB; ++i)
-            if (k0 + i < RMAX) {
-              areg[k0 + i][0] = areg[k0 + i][1] = 0.0;
-              freg[k0 + i][0] = freg[k0 + i][1] = kNoField;
-            }
-          continue;
-        }
-        uint2 e[RB][GQA];
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          if (k0 + i >= RMAX) break;
-          if (k0 == 0) {
-#pragma unroll
-            for (int hh = 0; hh < GQA; ++hh) e[i][hh] = e0[i][hh];
-          } else {
-            load_e(k0 + i, e[i]);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          const int k = k0 + i;
-          if (k >= RMAX) break;
-          weights(k, e[i], areg[k][0], areg[k][1]);
-          freg[k][0] = classify(areg[k][0]);
-          freg[k][1] = classify(areg[k][1]);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < RMAX; ++k) {
-        areg[k][0] = areg[k][1] = 0.0;
-        freg[k][0] = freg[k][1] = kNoField;
-      }
-    }
-  } else {
-    for (int k = 0; k < nr; ++k) {
-      uint2 e[GQA];
-      load_e(k, e);
-      double a0, a1;
-      weights(k, e, a0, a1);
-      classify(a0);
-      classify(a1);
-      const int64_t j0 = tok0(k);
-      if (j0 < Tp) { ab[j0] = a0; ab[j0 + 1] = a1; }
-    }
-  }
-  // visit every owned token: fn(a, field, round, s)
-  auto for_tokens = [&](auto&& fn) __attribute__((always_inline)) {
-    if constexpr (REG) {
-#pragma unroll
-      for (int k = 0; k < RMAX; ++k) {
-        if (k >= nr) break;
-        fn(areg[k][0], freg[k][0], k, 0);
-        fn(areg[k][1], freg[k][1], k, 1);
-      }
-    } else {
-      for (int k = 0; k < nr; ++k) {
-        const int64_t j0 = tok0(k);
-        const double a0 = j0 < Tp ? ab[j0] : 0.0, a1 = j0 < Tp ? ab[j0 + 1] : 0.0;
-        fn(a0, field_of(a0), k, 0);
-        fn(a1, field_of(a1), k, 1);
-      }
-    }
-  };
-  auto is_odd = [&](double a, int ef) { return a > 0.0 && ef == kNoField; };
-  auto gain_bits = [&](double a, int t) { return dbits(__dmul_rn(a, ldexp_pow2(-2 * t))); };
-
-  // ---- gain-field histogram: hA[E] regular tokens (filled with the
-  // weights), hB[f] odd products ----
-  if (any_odd) {
-    for_tokens([&](double a, int ef, int, int) {
-      if (is_odd(a, ef))
-        for (int t = 1; t <= W; ++t) {
-          const uint64_t kk = gain_bits(a, t);
-          if (kk) atomicAdd(&hB[(uint32_t)(kk >> 52)], 1u);
-        }
-    });
-  }
-  __syncthreads();
-
-  const uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
-  if (tid < 64) wave_find_gain_field(hA, hB, W, Bv > 0u ? Bv : 1u, sh);
-  __syncthreads();
-  const uint32_t npos = sh[3];
-  const bool all_pos = npos <= Bv;
-  int Es = -1;
-  uint64_t prefix = 0, mask = 0;  // over the 52 mantissa bits
-  uint32_t rem = 0, n_eq = 0;
-  if (!all_pos && Bv > 0) {
-    Es = (int)sh[0];
-    rem = Bv - sh[1];  // >= 1
-    n_eq = sh[2];      // >= rem
-    // digits of the 52 mantissa bits: 11, 11, 10, 10, 10 (MSB first)
-    for (int pass = 0; pass < 5 && n_eq != rem; ++pass) {
-      const int width = pass < 2 ? 11 : 10;
-      const int shift = pass < 2 ? 41 - 11 * pass : 40 - 10 * pass;
-      const uint32_t dmask = (1u << width) - 1u;
-      // the first pass counts into hC (cleared at the start), later ones
-      // into hA, cleared here
-      uint32_t* const hist = pass == 0 ? hC : hA;
-      if (pass > 0) {
-        for (int i = tid; i < 2048; i += NT) hA[i] = 0u;
-        __syncthreads();
-      }
-      {
-        // a regular token's candidate: d = E - Es even in [2, 2W]
-        const uint32_t dspan = (uint32_t)(twoW - 2);
-        if (pass == 0) {  // no prefix yet: the top 11 mantissa bits
-          for_tokens([&](double a, int ef, int, int) __attribute__((always_inline)) {
-            const uint32_t d2 = (uint32_t)(ef - Es - 2);
-            const uint32_t hi = (uint32_t)(dbits(a) >> 32);
-            if (d2 <= dspan && !(d2 & 1u)) atomicAdd(&hist[(hi >> 9) & 2047u], 1u);
-          });
-        } else {
-          for_tokens([&](double a, int ef, int, int) __attribute__((always_inline)) {
-            const uint32_t d2 = (uint32_t)(ef - Es - 2);
-            const uint64_t mnt = dbits(a) & 0x000FFFFFFFFFFFFFull;
-            if (d2 <= dspan && !(d2 & 1u) && (mnt & mask) == prefix)
-              atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
-          });
-        }
-        if (any_odd) {
-          for_tokens([&](double a, int ef, int, int) {
-            if (is_odd(a, ef))
-              for (int t = 1; t <= W; ++t) {
-                const uint64_t kk = gain_bits(a, t);
-                if (kk && (int)(kk >> 52) == Es) {
-                  const uint64_t mnt = kk & 0x000FFFFFFFFFFFFFull;
-                  if ((mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
-                }
-              }
-          });
-        }
-      }
-      __syncthreads();
-      if (tid < 64) {
-        if (width == 11) wave_find_digit<2048>(hist, rem, &sh[0], &sh[1]);
-        else wave_find_digit<1024>(hist, rem, &sh[0], &sh[1]);
-      }
-      __syncthreads();
-      const uint32_t dg = sh[0];
-      n_eq = hist[dg];
-      rem -= sh[1];
-      prefix |= (uint64_t)dg << shift;
-      mask |= (uint64_t)dmask << shift;
-      __syncthreads();
-    }
-  }
-
-  // ---- depths: levels above the threshold, plus ties in token order ----
-  // returns (levels above the threshold) | (levels equal to it) << 16
-  auto count_levels = [&](double a, int ef) __attribute__((always_inline)) -> uint32_t {
-    if (!(a > 0.0) || Bv == 0) return 0u;
-    if (all_pos) {
-      if (ef != kNoField) return (uint32_t)W;
-      uint32_t n = 0;
-      for (int t = 1; t <= W; ++t) n += gain_bits(a, t) != 0ull;
-      return n;
-    }
-    uint32_t above = 0, tie = 0;
-    if (ef != kNoField) {
-      const int d = ef - Es;
-      above = (uint32_t)min(max((d - 1) >> 1, 0), W);
-      if (d >= 2 && d <= twoW && !(d & 1)) {
-        const uint64_t mnt = (dbits(a) & 0x000FFFFFFFFFFFFFull) & mask;
-        if (mnt > prefix) ++above;
-        else if (mnt == prefix) ++tie;
-      }
-    } else {
-      for (int t = 1; t <= W; ++t) {
-        const uint64_t kk = gain_bits(a, t);
-        if (!kk) continue;
-        const int e = (int)(kk >> 52);
-        if (e > Es) ++above;
-        else if (e == Es) {
-          const uint64_t mnt = (kk & 0x000FFFFFFFFFFFFFull) & mask;
-          if (mnt > prefix) ++above;
-          else if (mnt == prefix) ++tie;
-        }
-      }
-    }
-    return above | (tie << 16);
-  };
-  const bool rank_ties = !all_pos && Bv > 0 && rem < n_eq;
-  uint32_t running = 0;  // ties in earlier rounds (token order = round, thread, s)
-  uint32_t lv0 = 0;
-  uint32_t vsum = 0;     // this thread's value refinements
-  for_tokens([&](double a, int ef, int k, int s) __attribute__((always_inline)) {
-    const uint32_t lv = count_levels(a, ef);
-    if (s == 0) { lv0 = lv; return; }
-    uint32_t above0 = lv0 & 0xFFFFu, above1 = lv & 0xFFFFu;
-    const uint32_t tie0 = lv0 >> 16, tie1 = lv >> 16;
-    if (rank_ties) {
-      const uint32_t before = block_excl_scan<NT>(tie0 + tie1, wsum) + running;
-      running += wsum[NW];
-      if (tie0 && before < rem) ++above0;
-      if (tie1 && before + tie0 < rem) ++above1;
-    } else {
-      above0 += tie0;
-      above1 += tie1;
-    }
-    const int64_t j0 = tok0(k);
-    if (j0 < Tp) {
-      tvb[j0] = (uint8_t)above0;
-      tvb[j0 + 1] = (uint8_t)above1;
-      vsum += above0 + above1;
-    }
-  });
-  // logical reads of the unit ([ReadKV] App. A.1): key payload T_p * sum_c
-  // t_c bits, value payload d * sum_j t_j bits, metadata (lo and rng of
-  // every closed group and channel of keys and values, E^K, E^V) and the
-  // open group's keys and values in the input type
-  if (counters) {
-    const uint32_t vtot = block_sum_u32<NT>(vsum, wsum);
-    if (wv == 0) {
-      const uint8_t* tkb = tk + ((int64_t)b * G + g) * kDim;
-      const int ks = wave_sum_i32((int)tkb[lane] + (int)tkb[lane + 64]);
-      if (lane == 0) {
-        const unsigned long long ng = (unsigned long long)(Tp / kGroup);
-        atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
-        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1), (unsigned long long)vtot * kDim);
-        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2),
-                  2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull);
-        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
-                  2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Gather: a block of 256 threads takes a run of consecutive 128-token chunks
 // (4 groups each) of one (request, KV head) and accumulates its share of
 //   O_h = sum_j alpha_hj v_hat_j,  alpha_hj = e_hj f_{h,tile(j)}
@@ -1661,18 +1211,21 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   uint8_t* ws = a.ws;
   uint8_t* tk = a.key_depths_out ? a.key_depths_out : ws + L.tk;
   uint8_t* tv = a.value_depths_out ? a.value_depths_out : ws + L.tv;
-  const int esize = DT == 0 ? 2 : 4;
+  const int NU = a.scope == 1 ? a.G : 1;  // KV heads per selection domain
 
   mark(a, 0, st);
-  // slots staged per score tile: at most min(B_K, 128 W) chosen key-line
-  // segments, 32 B each
-  double bk = floor((double)a.RK * (double)kDim);
+  // per-layer budgets: one key selection per request in its own launch;
+  // per-KV-head budgets: inside the score kernel's blocks
+  if (NU > 1 && launch_key_alloc(a, tk, st)) return -5;
+  // slots staged per score tile: at most min(B_K of the domain, 128 W) chosen
+  // key-line segments of one unit, 32 B each
+  double bk = floor((double)a.RK * (double)(kDim * NU));
   if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
   if (bk < 0.0) bk = 0.0;
   // (+8 slots: un-plane reads of a batch may run past a shallower channel's
   // last slot; those words are masked)
   size_t dyn = ((size_t)bk + 8) * 32;
-  if (dyn < (size_t)(2 * 64 * 8) * 12) dyn = (size_t)(2 * 64 * 8) * 12;  // key-allocation scratch
+  if (NU == 1 && dyn < 258 * 4) dyn = 258 * 4;  // the key allocation's scratch
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GQA, DT>),
@@ -1687,19 +1240,11 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   if (run < 1) run = 1;
   const int nrun = (L.ntile + run - 1) / run;
   hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), dyn, st,
-                     (const uint8_t*)a.store, a.q, tk, a.H, a.G, a.W, a.RK, a.capmax,
-                     L.ntile, (uint32_t*)(ws + L.ebuf), (double*)(ws + L.tilepart), a.counters);
+                     (const uint8_t*)a.store, a.q, tk, NU > 1 ? 1 : 0, a.H, a.G, a.W, a.RK,
+                     a.capmax, L.ntile, (uint32_t*)(ws + L.ebuf), (double*)(ws + L.tilepart),
+                     a.counters);
   mark(a, 1, st);
-  {
-    auto va = &k_value_alloc<GQA, 0>;
-    if (a.capmax <= (int64_t)kVRound * 4) va = &k_value_alloc<GQA, 4>;
-    else if (a.capmax <= (int64_t)kVRound * 5) va = &k_value_alloc<GQA, 5>;
-    else if (a.capmax <= (int64_t)kVRound * kVRMAX) va = &k_value_alloc<GQA, kVRMAX>;
-    hipLaunchKernelGGL(va, dim3(a.B * a.G), dim3(kVNT), 0, st, (const uint8_t*)a.store, a.H, a.G,
-                       a.W, esize, a.RV, a.vscale, a.capmax, L.ntile,
-                       (const uint32_t*)(ws + L.ebuf), (const double*)(ws + L.tilepart),
-                       (double*)(ws + L.ftile), (double*)(ws + L.aval), tv, tk, a.counters);
-  }
+  if (launch_value_alloc(a, L, tk, tv, st)) return -5;
   mark(a, 2, st);
   {
     // runs of consecutive chunks per block: about four blocks per compute

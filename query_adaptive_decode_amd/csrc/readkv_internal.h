@@ -4,7 +4,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "layout.h"
+
 namespace readkv {
+
+// Per-layer (pooled) budgets: at most this many KV heads per request.
+constexpr int kMaxPooledKV = 32;
 
 struct EncodeArgs {
   void* store;
@@ -27,11 +32,15 @@ struct DecodeArgs {
   int scope;
   int B, H, G, W, dtype;
   int64_t capmax;
-  void* const* events;  // NULL, or 5 hipEvent_t recorded around the 4 kernels
+  void* const* events;  // NULL, or 4 hipEvent_t recorded around the 3 stages
 };
 
 int launch_store_zero(void* store, size_t bytes, hipStream_t st);
 int launch_encode(const EncodeArgs& a, hipStream_t st);
 int launch_decode(const DecodeArgs& a, hipStream_t st);
+// the allocation stages (alloc.hip); tk, tv: the depth arrays of the call
+int launch_key_alloc(const DecodeArgs& a, uint8_t* tk, hipStream_t st);
+int launch_value_alloc(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk, uint8_t* tv,
+                       hipStream_t st);
 
 }  // namespace readkv

@@ -111,4 +111,256 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* wsum) {
   return wsum[NT / 64];  // total is left in wsum[NT/64] until the next scan
 }
 
+// ---------------------------------------------------------------------------
+// ChooseDepths over N items by one block ([ReadKV] Sec. 3.3; exactness App.
+// E.2.1, Prop. 8).  Item i has a weight a_i >= 0 (NaN or 0: no gains) and W
+// candidate gains a_i 4^-t, t = 1..W; the Bud largest positive gains are
+// chosen, ties to the lowest item index.
+//
+// Gain fields.  When a_i is a normal double with exponent field E in
+// (2W, 2047) ("regular"), every gain is exact, with field E - 2t and a_i's
+// mantissa, so a regular item holds min(W, max(0, floor((E - L) / 2))) gains
+// at field L or above.  Other positive weights ("odd": some gains are
+// subnormal) have their gains formed one by one.  An LDS histogram of the
+// regular items' fields (hA) and of the odd gains' fields (hB) gives the
+// count at every field; one wave finds the field L* of the Bud-th largest
+// gain; within L* the gains are ranked by mantissa with 11/11/10/10/10-bit
+// radix passes that stop once the gains sharing the chosen digits are
+// exactly the ones still to be taken; the remaining equal gains are ranked
+// by item index.
+// ---------------------------------------------------------------------------
+constexpr int kNoField = -8192;
+constexpr uint64_t kMant = 0x000FFFFFFFFFFFFFull;
+
+__device__ __forceinline__ int regular_field(double a, int twoW) {
+  const int E = (int)(dbits(a) >> 52);
+  return (a > 0.0 && E > twoW && E < 2047) ? E : kNoField;
+}
+__device__ __forceinline__ uint64_t gain_bits(double a, int t) {
+  return dbits(__dmul_rn(a, bitsd((uint64_t)(1023 - 2 * t) << 52)));
+}
+
+// One wave: the gain-field histogram G[f] = hB[f] + sum_{t=1..W} hA[f + 2t]
+// (W <= 8) is formed in registers and scanned from the top field down for
+// the field where the count reaches rem (>= 1).  out[0] = field, out[1] =
+// count above it, out[2] = G[field] (all three only if the total reaches
+// rem), out[3] = total count.
+__device__ __forceinline__ void wave_find_gain_field(const uint32_t* hA, const uint32_t* hB, int W,
+                                                     uint32_t rem, uint32_t* out) {
+  constexpr int PER = 32;
+  const int l = __lane_id();
+  const int base = 2048 - (l + 1) * PER;  // lane l: fields base .. base + 31
+  uint32_t w[PER + 16];                   // hA[base .. base + 47], 0 past the end
+#pragma unroll
+  for (int i = 0; i < (PER + 16) / 4; ++i) {
+    const int idx = base + 4 * i;
+    uint4 v = *reinterpret_cast<const uint4*>(hA + min(idx, 2044));
+    if (idx >= 2048) v = make_uint4(0u, 0u, 0u, 0u);
+    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  uint32_t G[PER];
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hB + base + 4 * i);
+    G[4 * i] = v.x; G[4 * i + 1] = v.y; G[4 * i + 2] = v.z; G[4 * i + 3] = v.w;
+  }
+#pragma unroll
+  for (int t = 1; t <= 8; ++t) {
+    if (t > W) break;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) G[i] += w[i + 2 * t];
+  }
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) tot += G[i];
+  const uint32_t incl = wave_incl_scan_u32(tot);
+  if (l == 63) out[3] = incl;
+  const uint64_t bal = __ballot(incl >= rem);
+  const int L = bal ? __ffsll((unsigned long long)bal) - 1 : -1;
+  if (l == L) {
+    uint32_t c = incl - tot;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (c + G[i] >= rem) {
+        out[0] = (uint32_t)(base + i);
+        out[1] = c;
+        out[2] = G[i];
+        break;
+      }
+      c += G[i];
+    }
+  }
+}
+
+template <int NT>
+struct ChooseShared {
+  uint32_t hA[2048];  // regular items by field; radix digits of later passes
+  uint32_t hB[2048];  // odd gains by field
+  uint32_t hC[2048];  // radix digits of the first pass
+  uint32_t wsum[NT / 64 + 1];
+  uint32_t sh[4];
+};
+
+// Items are visited in rounds, item i = round * NT + threadIdx.x (so the tie
+// scan in index order is a block scan per round); each pass fetches BATCH
+// rounds of weights together (from LDS or device memory, as geta reads).
+// geta(i) returns a_i (i < N); put(i, t) stores item i's depth.  Returns the
+// sum of this thread's depths.  Every thread of the block must call it
+// (block barriers inside).
+template <int NT, int BATCH, class GetA, class PutT>
+__device__ uint32_t block_choose_depths(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
+                                        ChooseShared<NT>& S) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x;
+  const int twoW = 2 * W;
+  const int64_t nr = (N + NT - 1) / NT;
+  for (int i = tid; i < 2048; i += NT) {
+    S.hA[i] = 0u;
+    S.hB[i] = 0u;
+    S.hC[i] = 0u;
+  }
+  __syncthreads();
+  // fn(i, a, field, in_range) for every round (all threads, uniform count)
+  auto for_items = [&](auto&& fn) __attribute__((always_inline)) {
+    for (int64_t k0 = 0; k0 < nr; k0 += BATCH) {
+      double a[BATCH];
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        const int64_t i = (k0 + q) * NT + tid;
+        a[q] = (k0 + q < nr && i < N) ? geta(i) : 0.0;
+      }
+#pragma unroll
+      for (int q = 0; q < BATCH; ++q) {
+        if (k0 + q >= nr) break;  // uniform
+        const int64_t i = (k0 + q) * NT + tid;
+        fn(i, a[q], regular_field(a[q], twoW), i < N);
+      }
+    }
+  };
+
+  // ---- field histograms ----
+  bool any_odd = false;
+  for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
+    if (ef != kNoField) {
+      atomicAdd(&S.hA[ef], 1u);
+    } else if (a > 0.0) {
+      any_odd = true;
+      for (int t = 1; t <= W; ++t) {
+        const uint64_t kk = gain_bits(a, t);
+        if (kk) atomicAdd(&S.hB[(uint32_t)(kk >> 52)], 1u);
+      }
+    }
+  });
+  __syncthreads();
+  if (tid < 64) wave_find_gain_field(S.hA, S.hB, W, Bud > 0u ? Bud : 1u, S.sh);
+  __syncthreads();
+  const uint32_t npos = S.sh[3];
+  const bool all_pos = npos <= Bud;
+  int Es = -1;
+  uint64_t prefix = 0, mask = 0;  // over the 52 mantissa bits
+  uint32_t rem = 0, n_eq = 0;
+  if (!all_pos && Bud > 0) {
+    Es = (int)S.sh[0];
+    rem = Bud - S.sh[1];  // >= 1
+    n_eq = S.sh[2];       // >= rem
+    // digits of the 52 mantissa bits: 11, 11, 10, 10, 10 (MSB first)
+    for (int pass = 0; pass < 5 && n_eq != rem; ++pass) {
+      const int width = pass < 2 ? 11 : 10;
+      const int shift = pass < 2 ? 41 - 11 * pass : 40 - 10 * pass;
+      const uint32_t dmask = (1u << width) - 1u;
+      uint32_t* const hist = pass == 0 ? S.hC : S.hA;
+      if (pass > 0) {
+        for (int i = tid; i < 2048; i += NT) S.hA[i] = 0u;
+        __syncthreads();
+      }
+      // a regular item's candidate: d = E - Es even in [2, 2W]
+      const uint32_t dspan = (uint32_t)(twoW - 2);
+      for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
+        if (ef != kNoField) {
+          const uint32_t d2 = (uint32_t)(ef - Es - 2);
+          const uint64_t mnt = dbits(a) & kMant;
+          if (d2 <= dspan && !(d2 & 1u) && (mnt & mask) == prefix)
+            atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
+        } else if (any_odd && a > 0.0) {
+          for (int t = 1; t <= W; ++t) {
+            const uint64_t kk = gain_bits(a, t);
+            if (kk && (int)(kk >> 52) == Es) {
+              const uint64_t mnt = kk & kMant;
+              if ((mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
+            }
+          }
+        }
+      });
+      __syncthreads();
+      if (tid < 64) {
+        if (width == 11) wave_find_digit<2048>(hist, rem, &S.sh[0], &S.sh[1]);
+        else wave_find_digit<1024>(hist, rem, &S.sh[0], &S.sh[1]);
+      }
+      __syncthreads();
+      const uint32_t dg = S.sh[0];
+      n_eq = hist[dg];
+      rem -= S.sh[1];
+      prefix |= (uint64_t)dg << shift;
+      mask |= (uint64_t)dmask << shift;
+      __syncthreads();
+    }
+  }
+
+  // ---- depths: levels above the threshold, plus ties in index order ----
+  // (levels above) | (levels equal to the threshold) << 16
+  auto count_levels = [&](double a, int ef) __attribute__((always_inline)) -> uint32_t {
+    if (!(a > 0.0) || Bud == 0) return 0u;
+    if (all_pos) {
+      if (ef != kNoField) return (uint32_t)W;
+      uint32_t n = 0;
+      for (int t = 1; t <= W; ++t) n += gain_bits(a, t) != 0ull;
+      return n;
+    }
+    uint32_t above = 0, tie = 0;
+    if (ef != kNoField) {
+      const int d = ef - Es;
+      above = (uint32_t)min(max((d - 1) >> 1, 0), W);
+      if (d >= 2 && d <= twoW && !(d & 1)) {
+        const uint64_t mnt = (dbits(a) & kMant) & mask;
+        if (mnt > prefix) ++above;
+        else if (mnt == prefix) ++tie;
+      }
+    } else {
+      for (int t = 1; t <= W; ++t) {
+        const uint64_t kk = gain_bits(a, t);
+        if (!kk) continue;
+        const int e = (int)(kk >> 52);
+        if (e > Es) {
+          ++above;
+        } else if (e == Es) {
+          const uint64_t mnt = (kk & kMant) & mask;
+          if (mnt > prefix) ++above;
+          else if (mnt == prefix) ++tie;
+        }
+      }
+    }
+    return above | (tie << 16);
+  };
+  const bool rank_ties = !all_pos && Bud > 0 && rem < n_eq;
+  uint32_t running = 0;  // ties in earlier rounds
+  uint32_t mine = 0;
+  for_items([&](int64_t i, double a, int ef, bool in) __attribute__((always_inline)) {
+    const uint32_t lv = count_levels(a, ef);
+    uint32_t t = lv & 0xFFFFu;
+    const uint32_t tie = lv >> 16;
+    if (rank_ties) {
+      const uint32_t before = block_excl_scan<NT>(tie, S.wsum) + running;
+      running += S.wsum[NW];
+      if (tie && before < rem) ++t;
+    } else {
+      t += tie;
+    }
+    if (in) {
+      put(i, t);
+      mine += t;
+    }
+  });
+  return mine;
+}
+
 }  // namespace readkv

@@ -102,7 +102,8 @@ def test_entry_points_reject_bad_arguments_before_launch():
         assert call(rk=rk, rv=rv) == -1
     assert call(vscale=5) == -1
     assert call(scope=2) == -1 and call(scope=-1) == -1
-    assert call(scope=1) == -5   # pooled per-layer budgets: not in this build
+    many = b.make_config(num_q_heads=66, num_kv_heads=33, batch=2, capacity_tokens=256)
+    assert call(cfgp=ctypes.byref(many), scope=1, wsb=b.workspace_bytes(many)) == -5   # pooling over > 32 KV heads
     assert call(wsb=ws - 1) == -3
     assert call(store=None) == -1
     assert L.readkv_store_init(by, fake, 16, None, None) == -3

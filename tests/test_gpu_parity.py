@@ -20,8 +20,8 @@ import torch
 import oracle as O
 from oracle import store_format as F
 from query_adaptive_decode_amd import synth, workload
-from query_adaptive_decode_amd.binding import (NUM_COUNTERS, ReadKVCache, VSCALE_PHYSICAL,
-                                               VSCALE_UNIT)
+from query_adaptive_decode_amd.binding import (NUM_COUNTERS, SCOPE_KV_HEAD, SCOPE_LAYER,
+                                               ReadKVCache, VSCALE_PHYSICAL, VSCALE_UNIT)
 from tests import parity_util as PU
 from tests.parity_util import OUT_REL_L2, alloc_mismatch, rel_l2
 
@@ -68,12 +68,13 @@ class Run:
     schedules and read counters."""
 
     def __init__(self, cfg, steps, rates, vscale=VSCALE_PHYSICAL, repeat=False, keep_steps=None,
-                 qmod=None):
+                 qmod=None, scope=SCOPE_KV_HEAD):
         self.cfg, self.steps, self.rates, self.vscale = cfg, steps, rates, vscale
+        self.scope = scope
         B, H, G = cfg["B"], cfg["H"], cfg["G"]
         self.T0 = synth.context_lengths(cfg)
         say(f"[case] {cfg['name']} B={B} H={H} G={G} T0={self.T0.tolist()[:4]}"
-            f" steps={steps} rates={rates} vscale={vscale} opts="
+            f" steps={steps} rates={rates} vscale={vscale} scope={scope} opts="
             f"{ {k: cfg[k] for k in ('key_ties', 'gap', 'q_scale', 'q_log2_spread') if k in cfg} }")
         h = workload.host_inputs(cfg, steps)
         # queries as the oracle sees them (float64), after the optional edit
@@ -102,13 +103,13 @@ class Run:
                 tv = torch.zeros(B * G * ((cap + 31) // 32 * 32), dtype=torch.uint8, device="cuda")
                 ctr = torch.full((NUM_COUNTERS,), -1, dtype=torch.int64, device="cuda")
                 out = cache.decode(dv["q"][s], rk, rv, vscale=vscale, key_depths=tk,
-                                   value_depths=tv, counters=ctr)
+                                   value_depths=tv, counters=ctr, scope=scope)
                 item = dict(step=s, rk=rk, rv=rv, out=out.cpu().numpy(),
                             tk=tk.cpu().numpy().reshape(B, G, 128),
                             tv=tv.cpu().numpy().reshape(B, G, -1), ctr=ctr.cpu().numpy())
                 if repeat:
                     out2 = cache.decode(dv["q"][s], rk, rv, vscale=vscale, key_depths=tk,
-                                        value_depths=tv)
+                                        value_depths=tv, scope=scope)
                     item["out2"] = out2.cpu().numpy()
                     item["tv2"] = tv.cpu().numpy().reshape(B, G, -1)
                 self.rec.append(item)
@@ -191,6 +192,57 @@ class Run:
                 assert it["ctr"].tolist() == ora_ctr, f"read counters vs oracle {tag0}"
         say(f"[parity] {cfg['name']}: near ties {st['near']} over {st['checks']} checks, "
             f"worst rel L2 {st['worst']:.3e}")
+        return st
+
+    def check_layer(self, requests=None, steps=None):
+        """Per-layer budgets: every KV head of a request against the oracle's
+        pooled decode (one key and one value selection per request)."""
+        cfg = self.cfg
+        G, H = cfg["G"], cfg["H"]
+        gqa = H // G
+        ebits = 16 if cfg["dtype"] == "bf16" else 32
+        all_req = requests is None
+        requests = list(range(cfg["B"])) if requests is None else requests
+        st = dict(near=0, checks=0, worst=0.0)
+        for it in self.rec:
+            if steps is not None and it["step"] not in steps:
+                continue
+            tag0 = f"step={it['step']} R=({it['rk']},{it['rv']}) layer"
+            assert it["ctr"].tolist() == self.counters_of_schedules(it), f"read counters {tag0}"
+            ora_ctr = [0, 0, 0, 0]
+            for b in requests:
+                n = int(self.T0[b]) + it["step"] + 1
+                units = [self.unit(b, g) for g in range(G)]
+                encs = [self.enc(b, g, n) for g in range(G)]
+                res = O.decode_request(self.qf[it["step"]][b], [K[:n] for K, _ in units],
+                                       [V[:n] for _, V in units], W=cfg["W"], R_K=it["rk"],
+                                       R_V=it["rv"], encs=encs,
+                                       vscale="unit" if self.vscale == VSCALE_UNIT else "physical")
+                tag = f"{tag0} request={b} n={n}"
+                assert np.array_equal(it["tk"][b], res["tK"]), f"key depths differ {tag}"
+                tp = res["tp"]
+                near, bad, det = alloc_mismatch(it["tv"][b, :, :tp].reshape(-1), res["tV"].reshape(-1),
+                                                res["wv"], cfg["W"])
+                assert bad == 0, f"value depths differ {tag}: {det}"
+                st["near"] += near
+                st["checks"] += 1
+                for g in range(G):
+                    got = it["out"][b, g * gqa:(g + 1) * gqa]
+                    if np.isnan(res["out"][g]).all():
+                        assert np.isnan(got).all(), f"outputs of a KV head with a non-finite query {tag}"
+                        continue
+                    err = rel_l2(got, res["out"][g])
+                    st["worst"] = max(st["worst"], float(err.max()))
+                    assert np.all(err <= OUT_REL_L2), f"output rel L2 {err.max():.3e} {tag} g={g}"
+                    lr = O.logical_reads(res["tK"][g], res["tV"][g], n, elem_bits=ebits)
+                    for i, k in enumerate(("key_payload", "value_payload", "metadata", "open_group")):
+                        ora_ctr[i] += lr[k]
+                if np.isnan(res["out"]).any():
+                    all_req = False   # counters of a NaN head are not summed above
+            if all_req:
+                assert it["ctr"].tolist() == ora_ctr, f"read counters vs oracle {tag0}"
+        say(f"[parity] {cfg['name']} (layer budgets): near ties {st['near']} over {st['checks']} "
+            f"checks, worst rel L2 {st['worst']:.3e}")
         return st
 
     def check_store(self, units=None):
@@ -314,6 +366,59 @@ def test_nonfinite_query_reads_nothing(record_property):
         assert np.isfinite(it["out"][0, 0:4]).all() and np.isfinite(it["out"][1, 4:8]).all()
         assert it["tk"][0, 1].sum() == 0 and it["tk"][1, 0].sum() == 0
     report(record_property, "non-finite query", run.check())
+
+
+# ------------------------------------------------------------ per-layer budgets
+def test_layer_budgets_llama_shape(record_property):
+    cfg = synth.workload(2, B=2, T0=2000)
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 2.0), (3.3, 2.7), (6.0, 1.0)],
+              scope=SCOPE_LAYER, repeat=True)
+    report(record_property, "layer budgets llama shape", run.check_layer())
+
+
+def test_layer_budgets_gqa7_ragged(record_property):
+    cfg = synth.workload(4, B=3, T0=(40, 1500))
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 2.0)], scope=SCOPE_LAYER)
+    report(record_property, "layer budgets gqa7 ragged", run.check_layer())
+
+
+@pytest.mark.parametrize("T0", [5, 33, 1025])
+def test_layer_budgets_tails_and_saturation(T0, record_property):
+    cfg = synth.workload(2, B=1, H=8, G=2, T0=T0)
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (0.0, 0.0), (8.0, 8.0), (100.0, 0.5)],
+              scope=SCOPE_LAYER)
+    report(record_property, f"layer budgets tails T0={T0}", run.check_layer())
+
+
+def test_layer_budgets_exact_ties(record_property):
+    # depth-0 keys make the 32 tokens of each group tie, across all KV heads
+    # of the request; duplicated key channels make key weights tie
+    cfg = synth.workload(2, B=2, T0=1000)
+    run = Run(cfg, steps=1, rates=[(0.0, 1.3), (0.0, 2.7)], scope=SCOPE_LAYER)
+    st = run.check_layer()
+    cfg = synth.workload(2, B=2, T0=700, key_ties=True)
+    run = Run(cfg, steps=1, rates=[(2.5009765625, 4.0), (1.0009765625, 1.0)], scope=SCOPE_LAYER)
+    st2 = run.check_layer()
+    report(record_property, "layer budgets ties",
+           dict(near=st["near"] + st2["near"], checks=st["checks"] + st2["checks"],
+                worst=max(st["worst"], st2["worst"])))
+
+
+def test_layer_budgets_nonfinite_query(record_property):
+    def qmod(q, s):
+        q = q.copy()
+        q[0, 5, 17] = np.nan     # request 0, KV head 1
+        return q
+    cfg = synth.workload(2, B=2, H=8, G=2, T0=500)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0)], qmod=qmod, scope=SCOPE_LAYER)
+    report(record_property, "layer budgets non-finite query", run.check_layer())
+
+
+@pytest.mark.timeout(900)
+def test_layer_budgets_full_size_llama_layer(record_property):
+    cfg = synth.workload(2)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 2.0)], scope=SCOPE_LAYER)
+    report(record_property, "layer budgets B=16 T0=8192", run.check_layer([0, 9, 15]))
 
 
 # ------------------------------------------------------------ long context

@@ -191,6 +191,41 @@ def test_greedy_equals_brute_force_optimum(seed):
         assert sum(af[i] * Fraction(1, 4 ** int(t[i])) for i in range(N)) == obj
 
 
+def test_pooled_layer_budgets_equal_brute_force():
+    # per-layer budgets ([ReadKV] Sec. 3.3): the key schedule of a request is
+    # the optimum over all G * d key items under one budget, and the value
+    # schedule the optimum over all G * T_packed value items; checked by
+    # exhaustive search on a tiny layer (G = 2 KV heads, d = 2, 4 packed
+    # tokens each in groups of 2, W = 2), with the second head's keys and
+    # values 8x larger so that per-head budgets would choose differently
+    from query_adaptive_decode_amd.synth import round_to_bf16
+    rng = np.random.default_rng(53)
+    W, G, d, T = 2, 2, 2, 5
+    Ks = [round_to_bf16(rng.standard_normal((T, d)) * (1.0 + 7.0 * g)) for g in range(G)]
+    Vs = [round_to_bf16(rng.standard_normal((T, d)) * (1.0 + 7.0 * g)) for g in range(G)]
+    q = round_to_bf16(rng.standard_normal((G, d)))
+    differs = False
+    for rk, rv in [(0.25, 0.25), (0.5, 0.75), (0.75, 1.0), (1.25, 0.5), (2.0, 1.75)]:
+        res = O.decode_request(q, Ks, Vs, W=W, R_K=rk, R_V=rv, group_tokens=2)
+        assert res["BK"] == math.floor(rk * G * d) and res["BV"] == math.floor(rv * G * 4)
+        tb, _ = _brute_best(res["wk"], W, res["BK"])
+        assert tuple(res["tK"].reshape(-1)) == tuple(tb), (rk, res["tK"], tb)
+        tb, _ = _brute_best(res["wv"], W, res["BV"])
+        assert tuple(res["tV"].reshape(-1)) == tuple(tb), (rv, res["tV"], tb)
+        per_head = [O.decode_unit(q[g:g + 1], Ks[g], Vs[g], W=W, R_K=rk, R_V=rv, group_tokens=2)
+                    for g in range(G)]
+        differs |= not np.array_equal(np.stack([r["tK"] for r in per_head]), res["tK"])
+    assert differs
+    # a KV head with a non-finite query reads nothing; the others keep the
+    # whole layer budget
+    qb = q.copy()
+    qb[0, 1] = np.nan
+    res = O.decode_request(qb, Ks, Vs, W=W, R_K=0.75, R_V=1.0, group_tokens=2)
+    assert res["tK"][0].sum() == 0 and res["tV"][0].sum() == 0 and np.isnan(res["out"][0]).all()
+    assert res["tK"][1].sum() == min(res["BK"], W * int((res["wk"][2:] > 0).sum()))
+    assert np.isfinite(res["out"][1]).all()
+
+
 def test_objective_identity_exact():
     rng = np.random.default_rng(11)
     a = rng.exponential(1.0, 6)
