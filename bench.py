@@ -7,10 +7,19 @@ seeded K/V/q.  One step = append one token per request through the encoder
 + one ReadKV decode (key allocation, score, value allocation, value gather,
 output reduction), for read rates R = 4 and R = 2 (R_K = R_V = R).
 
-Prints one JSON line.  `value` is query-heads x context-tokens per second
-at (W, R) = (8, 4) with inputs resident in HBM; per-rate figures, the
-per-kernel roofline of the dominant kernel (live HIP-event timing) and the
-float64 oracle's CPU throughput on a bounded sample are included.
+Prints one JSON line.  `value` is query-heads x context-tokens per second at
+(W, R) = (8, 4) with the step's inputs resident in HBM and the caches
+flushed before every step (a 512 MiB device write pushes the store out of
+L2 and the Infinity Cache); the warm figure (steps replayed back to back)
+sits beside it.  Both are graph replays timed with HIP events.  Also
+reported: per-kernel HIP-event durations (warm and flushed), the roofline
+of the dominant kernel, bytes moved per step from the committed rocprofv3
+request counters (when they were taken on these sources), a measured
+device-copy bandwidth, and the float64 oracle's CPU throughput on this
+host (all cores, and one core).
+
+`--counters-run` runs the fixed sequence the counter profiles are taken on
+(see query_adaptive_decode_amd/profile_summary.py) and prints nothing else.
 """
 from __future__ import annotations
 
@@ -26,36 +35,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
 KERNELS = ["score", "value_alloc", "value_gather"]
-METRIC = "decode attn query-heads\u00b7ctx-tokens/s + achieved HBM GB/s vs peak, (W,R)=(8,4),(8,2)"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_decode_step_llama3-8b-B16-T8192.txt")
-
-
-def source_hash():
-    """sha256 over the HIP sources and headers the library is built from."""
-    import hashlib
-    h = hashlib.sha256()
-    d = os.path.join(ROOT, "query_adaptive_decode_amd", "csrc")
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(d, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()
-
-
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed counter summary,
-    or None when it was taken on other sources (or is missing)."""
-    try:
-        rows = [l.strip() for l in open(TRAFFIC_FILE) if "=" in l and not l.startswith("#")]
-    except OSError:
-        return None
-    kv = dict(l.split("=", 1) for l in rows)
-    if kv.get("source_sha256") != source_hash():
-        return None
-    try:
-        return float(kv[f"{kernel}.fetch_bytes"]) + float(kv[f"{kernel}.write_bytes"])
-    except (KeyError, ValueError):
-        return None
+METRIC = "decode attn query-heads·ctx-tokens/s + achieved HBM GB/s vs peak, (W,R)=(8,4),(8,2)"
+FLUSH_BYTES = 512 << 20
 
 
 def _hip():
@@ -82,85 +63,120 @@ def _elapsed(h, a, b):
     return ms.value
 
 
-def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, evict=True):
-    from query_adaptive_decode_amd import binding as Bd
+class Stepper:
+    """Device state of one rate: the store (prefilled), fixed input buffers
+    that one step's graph reads, and the decode outputs."""
+
+    def __init__(self, cfg, dev, lcfg, R, torch):
+        from query_adaptive_decode_amd import binding as Bd
+        self.Bd, self.torch, self.cfg, self.dev, self.lcfg, self.R = Bd, torch, cfg, dev, lcfg, R
+        B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
+        self.cache = Bd.ReadKVCache(lcfg)
+        self.cache.append(dev["kpre"], dev["vpre"])
+        self.out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
+        self.kbuf = torch.empty_like(dev["kstep"][0])
+        self.vbuf = torch.empty_like(dev["vstep"][0])
+        self.qbuf = torch.empty_like(dev["q"][0])
+        capmax = (lcfg.capacity_tokens + 31) // 32 * 32
+        self.tk = torch.zeros(B * G * d, dtype=torch.uint8, device="cuda")
+        self.tv = torch.zeros((B, G, capmax), dtype=torch.uint8, device="cuda")
+        self.s = 0          # next decode step (index into the step inputs)
+        self.graph = None
+
+    def load(self):
+        """Copy step s's inputs into the fixed buffers (outside any timing)."""
+        self.kbuf.copy_(self.dev["kstep"][self.s])
+        self.vbuf.copy_(self.dev["vstep"][self.s])
+        self.qbuf.copy_(self.dev["q"][self.s])
+
+    def step_eager(self):
+        self.load()
+        self.cache.append(self.kbuf, self.vbuf)
+        self.cache.decode(self.qbuf, self.R, self.R, out=self.out)
+        self.s += 1
+
+    def capture(self):
+        torch = self.torch
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.cache.append(self.kbuf, self.vbuf)
+            self.cache.decode(self.qbuf, self.R, self.R, out=self.out)
+        torch.cuda.synchronize()
+
+
+def flush(scratch, i):
+    scratch.fill_(i & 0xFF)
+
+
+def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h):
+    """Warm and flushed step times (graph replays) and per-kernel durations
+    (HIP events on the launch stream around each stage)."""
     B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
     T0 = int(cfg["T0"])
-    cache = Bd.ReadKVCache(lcfg)
-    cache.append(dev["kpre"], dev["vpre"])
-    out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
-    capmax = (lcfg.capacity_tokens + 31) // 32 * 32
-    tk = torch.zeros(B * G * d, dtype=torch.uint8, device="cuda")
-    tv = torch.zeros((B, G, capmax), dtype=torch.uint8, device="cuda")
-    s = 0
+    st = Stepper(cfg, dev, lcfg, R, torch)
     for _ in range(warmup):
-        cache.append(dev["kstep"][s], dev["vstep"][s])
-        cache.decode(dev["q"][s], R, R, out=out)
-        s += 1
-    torch.cuda.synchronize()
-    # ---- timed region: whole steps (append + decode), recorded once into a
-    # HIP graph and replayed, so host launch overhead is not timed ----
-    s0 = s
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for i in range(steps):
-            cache.append(dev["kstep"][s0 + i], dev["vstep"][s0 + i])
-            cache.decode(dev["q"][s0 + i], R, R, out=out)
-    torch.cuda.synchronize()
-    t_begin = time.perf_counter()
-    graph.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_begin
-    s = s0 + steps
-    ctx = [T0 + i + 1 for i in range(s0, s0 + steps)]
-    qh_tok = B * H * sum(ctx)
-    # ---- per-kernel timing with HIP events on the launch stream ----
-    h = _hip()
+        st.step_eager()
+    st.capture()
     stream = torch.cuda.current_stream().cuda_stream
-    ev = [_events(h, len(KERNELS) + 1) for _ in range(steps)]
-    eenc = [_events(h, 2) for _ in range(steps)]
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    e0, e1 = _events(h, 2)
+
+    def timed_replay(evict):
+        st.load()
+        if evict:
+            flush(scratch, st.s)
+        h.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
+        st.graph.replay()
+        h.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
+        h.hipEventSynchronize(ctypes.c_void_p(e1))
+        n = T0 + st.s + 1
+        st.s += 1
+        return _elapsed(h, e0, e1), n
+
+    res = {}
+    for mode in ("warm", "evicted"):
+        tot, qh_tok = 0.0, 0
+        for _ in range(steps):
+            ms, n = timed_replay(mode == "evicted")
+            tot += ms
+            qh_tok += B * H * n
+        res[mode] = dict(ms_per_step=tot / steps, qh_tok_per_s=qh_tok / (tot * 1e-3))
+    # per-kernel durations: the timed entry point records events between
+    # its stages; the append is bracketed separately
     ksum = torch.zeros((), dtype=torch.int64, device="cuda")
     vsum = torch.zeros((), dtype=torch.int64, device="cuda")
+    kern = {}
     tp_list = []
-    for i in range(steps):
-        h.hipEventRecord(ctypes.c_void_p(eenc[i][0]), ctypes.c_void_p(stream))
-        cache.append(dev["kstep"][s], dev["vstep"][s])
-        h.hipEventRecord(ctypes.c_void_p(eenc[i][1]), ctypes.c_void_p(stream))
-        Bd.decode_attn_timed(lcfg, cache.store, dev["q"][s], R, R, cache.workspace, ev[i], out=out,
-                             key_depths=tk, value_depths=tv.view(-1))
-        n = T0 + s + 1
-        tp = n // 32 * 32
-        tp_list.append(tp)
-        ksum += tk.sum(dtype=torch.int64)
-        vsum += tv[:, :, :tp].sum(dtype=torch.int64)
-        s += 1
-    torch.cuda.synchronize()
-    # ---- cache-evicted steps: a 512 MiB write before each step pushes the
-    # store out of L2 and the Infinity Cache; the step is timed with events ----
-    evict_ms = None
-    if evict:
-        scratch = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        tot = 0.0
+    for mode in ("warm", "evicted"):
+        evs = [_events(h, len(KERNELS) + 1) for _ in range(steps)]
+        eenc = [_events(h, 2) for _ in range(steps)]
         for i in range(steps):
-            scratch.fill_(i & 0xFF)
-            ev0.record()
-            cache.append(dev["kstep"][s], dev["vstep"][s])
-            cache.decode(dev["q"][s], R, R, out=out)
-            ev1.record()
-            ev1.synchronize()
-            tot += ev0.elapsed_time(ev1)
-            s += 1
-        evict_ms = tot / steps
-        del scratch
-    kern_ms = {k: 0.0 for k in KERNELS}
-    enc_ms = 0.0
-    for i in range(steps):
-        for k in range(len(KERNELS)):
-            kern_ms[KERNELS[k]] += _elapsed(h, ev[i][k], ev[i][k + 1])
-        enc_ms += _elapsed(h, eenc[i][0], eenc[i][1])
-    kern_ms = {k: v / steps for k, v in kern_ms.items()}
-    enc_ms /= steps
+            st.load()
+            if mode == "evicted":
+                flush(scratch, st.s)
+            h.hipEventRecord(ctypes.c_void_p(eenc[i][0]), ctypes.c_void_p(stream))
+            st.cache.append(st.kbuf, st.vbuf)
+            h.hipEventRecord(ctypes.c_void_p(eenc[i][1]), ctypes.c_void_p(stream))
+            st.Bd.decode_attn_timed(lcfg, st.cache.store, st.qbuf, R, R, st.cache.workspace, evs[i],
+                                    out=st.out, key_depths=st.tk, value_depths=st.tv.view(-1))
+            n = T0 + st.s + 1
+            tp = n // 32 * 32
+            if mode == "warm":
+                tp_list.append(tp)
+                ksum += st.tk.sum(dtype=torch.int64)
+                vsum += st.tv[:, :, :tp].sum(dtype=torch.int64)
+            st.s += 1
+        torch.cuda.synchronize()
+        km = {k: 0.0 for k in KERNELS}
+        enc = 0.0
+        for i in range(steps):
+            for k in range(len(KERNELS)):
+                km[KERNELS[k]] += _elapsed(h, evs[i][k], evs[i][k + 1])
+            enc += _elapsed(h, eenc[i][0], eenc[i][1])
+        kern[mode] = {k: v / steps for k, v in km.items()}
+        kern[mode]["append"] = enc / steps
+    del scratch
     tpm = sum(tp_list) / steps
     ng = tpm / 32
     kpay = float(ksum.item()) / steps * tpm / 8            # bytes per launch, all (b,g)
@@ -170,118 +186,197 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, evict=True):
     alg = {"score": kpay + meta + B * G * d * 8 + B * H * d * 2, "value_gather": vpay + meta,
            "value_alloc": B * G * ng * 8}
     step_bytes = kpay + vpay + 2 * meta
-    return dict(R=R, ms_per_step=wall / steps * 1e3, qh_tok_per_s=qh_tok / wall,
-                evicted_ms_per_step=evict_ms,
-                kernel_ms=kern_ms, encode_ms=enc_ms, alg_bytes=alg, step_alg_bytes=step_bytes,
-                logical_GBps_step=step_bytes / (wall / steps) / 1e9,
-                mean_key_bits_per_scalar=float(ksum.item()) / steps / (B * G * d),
-                mean_value_bits_per_scalar=float(vsum.item()) / steps / (B * G * tpm))
+    return dict(R=R, time=res, kernel_ms=kern, alg_bytes=alg, step_alg_bytes=step_bytes,
+                key_bits=float(ksum.item()) / steps / (B * G * d),
+                value_bits=float(vsum.item()) / steps / (B * G * tpm), steps_used=st.s)
 
 
-def cpu_baseline(cfg, budget_s=12.0):
-    """The float64 oracle, untuned, on this host: one decode step of a
-    sample of (request, KV head) units, single-threaded."""
-    import numpy as np
-    try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    import oracle as O
-    from query_adaptive_decode_amd import synth
-    gqa = cfg["H"] // cfg["G"]
-    T0 = int(cfg["T0"])
-    units = [(b, g) for b in range(cfg["B"]) for g in range(cfg["G"])]
-    ctx = None
-    done = 0
-    qh_tok = 0
-    t_all = 0.0
-    import contextlib
-    lim = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
-    with lim:
-        for (b, g) in units:
-            K, V = synth.kv_unit(cfg, b, g, T0 + 1)
-            q = synth.q_step(cfg, b, 0)[g * gqa:(g + 1) * gqa]
-            t = time.perf_counter()
-            O.decode_unit(q, K, V, W=cfg["W"], R_K=4.0, R_V=4.0)
-            t_all += time.perf_counter() - t
-            done += 1
-            qh_tok += gqa * (T0 + 1)
-            ctx = T0 + 1
-            if t_all >= budget_s and done >= 2:
-                break
-    _ = np
-    return dict(value=qh_tok / t_all, unit="query-heads*ctx-tokens/s", cores=1, kind="oracle",
-                sample=f"{done} of {len(units)} (request, KV head) units, one decode step at "
-                       f"T={ctx}, (W,R)=(8,4), float64 numpy single thread, {t_all:.1f} s")
-
-
-def copy_probe(torch, mib=512, reps=3):
-    """A plain device-to-device copy of a known size: its FETCH_SIZE /
-    WRITE_SIZE counter readings give the scale from counter units to bytes."""
+def copy_bandwidth(torch, h, mib=1024, reps=5):
+    """A plain device-to-device copy of `mib` MiB timed with events: bytes
+    moved (read + write) per second."""
     src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
-    for _ in range(reps):
-        dst.copy_(src)
+    dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"# copy probe: {reps} copies of {mib} MiB", file=sys.stderr, flush=True)
+    stream = torch.cuda.current_stream().cuda_stream
+    e0, e1 = _events(h, 2)
+    best = None
+    for _ in range(reps):
+        h.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
+        dst.copy_(src)
+        h.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
+        h.hipEventSynchronize(ctypes.c_void_p(e1))
+        ms = _elapsed(h, e0, e1)
+        best = ms if best is None else min(best, ms)
     del src, dst
+    return 2.0 * (mib << 20) / (best * 1e-3) / 1e9
+
+
+def _oracle_unit(args):
+    """One decode step of one (request, KV head) unit by the oracle, on one
+    thread; returns (query-heads x context-tokens, seconds)."""
+    wid, b, g = args
+    try:
+        from threadpoolctl import threadpool_limits
+        lim = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        lim = None
+    import oracle as O
+    from query_adaptive_decode_amd import synth
+    cfg = synth.workload(wid)
+    gqa = cfg["H"] // cfg["G"]
+    n = int(cfg["T0"]) + 1
+    K, V = synth.kv_unit(cfg, b, g, n)
+    q = synth.q_step(cfg, b, 0)[g * gqa:(g + 1) * gqa]
+    t = time.perf_counter()
+    O.decode_unit(q, K, V, W=cfg["W"], R_K=4.0, R_V=4.0)
+    dt = time.perf_counter() - t
+    del lim
+    return gqa * n, dt
+
+
+def cpu_baseline(cfg, budget_s=20.0):
+    """The float64 oracle, untuned, on this host's cores: a process pool
+    over (request, KV head) units (one thread each) for one decode step,
+    and the same work on one core."""
+    import multiprocessing as mp
+    # worker processes are spawned (fresh interpreters that never open the
+    # GPU), at most 16: the host's CPU share of one GPU
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    units = [(cfg["id"], b, g) for b in range(cfg["B"]) for g in range(cfg["G"])]
+    one = [_oracle_unit(units[0]) for _ in range(2)][-1]
+    per_unit = one[1]
+    # as many units as the pool finishes in about budget_s (all of one step
+    # when that fits)
+    n_units = max(cores, min(len(units), int(budget_s * cores / max(per_unit, 1e-3))))
+    n_units = min(n_units, len(units))
+    ctx = mp.get_context("spawn")
+    t = time.perf_counter()
+    with ctx.Pool(processes=cores) as pool:
+        res = pool.map(_oracle_unit, units[:n_units], chunksize=1)
+    wall = time.perf_counter() - t
+    qh_tok = sum(r[0] for r in res)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return dict(value=qh_tok / wall, unit="query-heads*ctx-tokens/s", cores=cores, kind="oracle",
+                sample=f"{n_units} of {len(units)} (request, KV head) units of one decode step at "
+                       f"T={int(cfg['T0']) + 1}, (W,R)=(8,4): float64 numpy, a pool of {cores} "
+                       f"processes (one thread each; inputs drawn inside the timed tasks), "
+                       f"{wall:.1f} s; CPU {model}",
+                single_core=dict(value=one[0] / one[1], seconds_per_unit=per_unit))
+
+
+def counters_run(cfg, dev, lcfg, rates, warmup, steps, torch):
+    """The fixed launch sequence the rocprofv3 request-counter passes are
+    taken on: a 512 MiB device copy (calibration), then per rate `warmup`
+    steps, `steps` warm steps and `steps` steps each after a 512 MiB flush,
+    all eager."""
+    src = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    for R in rates:
+        st = Stepper(cfg, dev, lcfg, R, torch)
+        for _ in range(warmup + steps):
+            st.step_eager()
+        for _ in range(steps):
+            st.load()
+            flush(scratch, st.s)
+            st.cache.append(st.kbuf, st.vbuf)
+            st.cache.decode(st.qbuf, st.R, st.R, out=st.out)
+            st.s += 1
+        torch.cuda.synchronize()
+        del st
+    print(f"# counters run: rates {rates}, warmup {warmup}, {steps} warm + {steps} flushed steps",
+          file=sys.stderr, flush=True)
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rates", default="4,2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=12.0)
-    ap.add_argument("--no-evict", action="store_true",
-                    help="skip the cache-evicted per-step timing")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--counters-run", action="store_true",
+                    help="run the fixed sequence the counter profiles are taken on, print no line")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "one GPU only: the decode path has no multi-GPU mode "
                                    "(requests and KV heads are independent; see the sharding "
                                    "notes); run with --gpus 1"}))
         sys.exit(2)
-    import torch
     from query_adaptive_decode_amd import synth, workload
-
     cfg = synth.workload(2)
     rates = [float(r) for r in args.rates.split(",")]
-    if args.copy_probe:
-        copy_probe(torch)
-    total_steps = args.warmup + (3 if not args.no_evict else 2) * args.steps
-    if total_steps > int(cfg["steps"]):
-        print(json.dumps({"error": f"warmup + {'3' if not args.no_evict else '2'} x steps = {total_steps} "
+    per_rate = args.warmup + (2 if args.counters_run else 4) * args.steps
+    if per_rate > int(cfg["steps"]):
+        print(json.dumps({"error": f"warmup + {2 if args.counters_run else 4} x steps = {per_rate} "
                                    f"exceeds the workload's {cfg['steps']} decode steps"}))
         sys.exit(2)
+    import torch
     t = time.perf_counter()
-    hin = workload.host_inputs(cfg, total_steps)
+    hin = workload.host_inputs(cfg, per_rate)
     dev = workload.to_device(hin)
     del hin
-    lcfg = workload.config_for(cfg, total_steps)
+    lcfg = workload.config_for(cfg, per_rate)
     print(f"# inputs ready in {time.perf_counter() - t:.1f} s", file=sys.stderr, flush=True)
+    if args.counters_run:
+        counters_run(cfg, dev, lcfg, rates, args.warmup, args.steps, torch)
+        return
+    from query_adaptive_decode_amd import profile_summary as PS
+    h = _hip()
+    copy_gbps = copy_bandwidth(torch, h)
+    print(f"# device copy: {copy_gbps:.0f} GB/s moved", file=sys.stderr, flush=True)
+    moved = PS.committed_bytes()   # per-kernel bytes from the counters, or None
     res = {}
     for R in rates:
-        res[R] = run_rate(cfg, dev, lcfg, R, args.warmup, args.steps, torch, evict=not args.no_evict)
-        r = res[R]
-        print(f"# R={R}: {r['ms_per_step']:.3f} ms/step, {r['qh_tok_per_s'] / 1e9:.2f} G qh*tok/s, "
-              f"kernels {json.dumps({k: round(v * 1e3, 1) for k, v in r['kernel_ms'].items()})} us, "
-              f"encode {r['encode_ms'] * 1e3:.1f} us, evicted "
-              f"{(r['evicted_ms_per_step'] or 0.0):.3f} ms/step", file=sys.stderr, flush=True)
+        r = run_rate(cfg, dev, lcfg, R, args.warmup, args.steps, torch, h)
+        res[R] = r
+        tm, km = r["time"], r["kernel_ms"]
+        print(f"# R={R:g}: evicted {tm['evicted']['ms_per_step']:.3f} ms/step "
+              f"({tm['evicted']['qh_tok_per_s'] / 1e9:.2f} G qh*tok/s), warm "
+              f"{tm['warm']['ms_per_step']:.3f} ms/step ({tm['warm']['qh_tok_per_s'] / 1e9:.2f} G); "
+              f"kernels evicted {json.dumps({k: round(v * 1e3, 1) for k, v in km['evicted'].items()})} us, "
+              f"warm {json.dumps({k: round(v * 1e3, 1) for k, v in km['warm'].items()})} us",
+              file=sys.stderr, flush=True)
     head = res[rates[0]]
-    dom = max(["score", "value_gather"], key=lambda k: head["kernel_ms"][k])
-    ach = head["alg_bytes"][dom] / (head["kernel_ms"][dom] * 1e-3) / 1e9
+    kev = head["kernel_ms"]["evicted"]
+    dom = max(["score", "value_gather"], key=lambda k: kev[k])
+    ach = head["alg_bytes"][dom] / (kev[dom] * 1e-3) / 1e9
+
+    def rate_key(R):
+        return f"8,{R:g}"
+
+    def moved_of(R, mode):
+        if not moved:
+            return None
+        m = moved.get(rate_key(R), {}).get(mode)
+        if not m:
+            return None
+        return m
+
+    traffic = None
+    m_dom = moved_of(rates[0], "evicted")
+    if m_dom and dom in m_dom["kernels"]:
+        traffic = m_dom["kernels"][dom]["read_bytes"] + m_dom["kernels"][dom]["write_bytes"]
     line = {
         "metric": METRIC,
-        "value": head["qh_tok_per_s"],
+        "value": head["time"]["evicted"]["qh_tok_per_s"],
         "unit": "query-heads*ctx-tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step"],
+        "ms_per_step": head["time"]["evicted"]["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -289,25 +384,47 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg["name"], "batch": cfg["B"], "q_heads": cfg["H"],
                    "kv_heads": cfg["G"], "head_dim": cfg["d"], "prompt_tokens": cfg["T0"],
-                   "W": cfg["W"], "R": rates, "step": "append 1 token/request + decode"},
+                   "W": cfg["W"], "R": rates, "budget_scope": "kv_head",
+                   "step": "append 1 token/request + decode, caches flushed before each step"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": ach, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(dom),
-                     "alg_bytes_per_launch": head["alg_bytes"][dom],
-                     "kernel_us": head["kernel_ms"][dom] * 1e3},
-        "rates": {f"8,{R:g}": {
-            "qh_tok_per_s": r["qh_tok_per_s"], "ms_per_step": r["ms_per_step"],
-            "evicted_ms_per_step": r["evicted_ms_per_step"],
-            "kernel_us": {k: v * 1e3 for k, v in r["kernel_ms"].items()},
-            "encode_us": r["encode_ms"] * 1e3,
-            "logical_bytes_per_step": r["step_alg_bytes"],
-            "logical_GBps_step": r["logical_GBps_step"],
-            "key_bits_per_scalar": r["mean_key_bits_per_scalar"],
-            "value_bits_per_scalar": r["mean_value_bits_per_scalar"],
-            "kernel_alg_GBps": {k: r["alg_bytes"][k] / (r["kernel_ms"][k] * 1e-3) / 1e9
-                                for k in ("score", "value_gather")}}
-            for R, r in res.items()},
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": traffic,
+                     "alg_bytes_per_launch": head["alg_bytes"][dom], "kernel_us": kev[dom] * 1e3,
+                     "timing": "HIP events, caches flushed before each step"},
+        "copy_peak_GBps": copy_gbps,
+        "rates": {},
     }
+    for R, r in res.items():
+        tm, km = r["time"], r["kernel_ms"]
+        ent = {
+            "evicted_ms_per_step": tm["evicted"]["ms_per_step"],
+            "evicted_qh_tok_per_s": tm["evicted"]["qh_tok_per_s"],
+            "warm_ms_per_step": tm["warm"]["ms_per_step"],
+            "warm_qh_tok_per_s": tm["warm"]["qh_tok_per_s"],
+            "kernel_us": {mode: {k: v * 1e3 for k, v in km[mode].items()} for mode in km},
+            "logical_bytes_per_step": r["step_alg_bytes"],
+            "logical_GBps": {mode: r["step_alg_bytes"] / (tm[mode]["ms_per_step"] * 1e-3) / 1e9
+                             for mode in tm},
+            "key_bits_per_scalar": r["key_bits"],
+            "value_bits_per_scalar": r["value_bits"],
+            "kernel_alg_GBps_evicted": {k: r["alg_bytes"][k] / (km["evicted"][k] * 1e-3) / 1e9
+                                        for k in ("score", "value_gather")},
+        }
+        ent["logical_frac_of_peak"] = {m: v / HBM_PEAK_GBPS for m, v in ent["logical_GBps"].items()}
+        for mode in ("evicted", "warm"):
+            m = moved_of(R, mode)
+            if m:
+                step_b = m["step_read_bytes"] + m["step_write_bytes"]
+                gbps = step_b / (tm[mode]["ms_per_step"] * 1e-3) / 1e9
+                ent[f"moved_{mode}"] = {
+                    "bytes_per_step": step_b, "read_bytes": m["step_read_bytes"],
+                    "write_bytes": m["step_write_bytes"], "GBps": gbps,
+                    "frac_of_peak": gbps / HBM_PEAK_GBPS, "frac_of_copy": gbps / copy_gbps,
+                    "per_kernel_bytes": {k: v["read_bytes"] + v["write_bytes"]
+                                         for k, v in m["kernels"].items()}}
+        line["rates"][rate_key(R)] = ent
+    if moved is None:
+        line["moved_bytes_note"] = ("no counter summary for these kernel sources "
+                                    "(profiles/ was taken on other sources)")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(line))

@@ -19,10 +19,12 @@
  *
  * Ownership: the caller allocates every buffer (store, workspace, inputs,
  * outputs) in device memory and keeps it alive until the enqueued work
- * completes.  The library allocates nothing, never synchronises the stream
+ * completes.  The library allocates no device memory (apart from the fixed
+ * scratch of readkv_decode_attn_noalloc), never synchronises the stream
  * (except readkv_store_init and readkv_store_status, which say so), and
- * keeps no global state beyond its loaded kernels.  Calls on different
- * streams are independent if they use different stores and workspaces.
+ * keeps no state beyond its loaded kernels and that scratch.  Calls on
+ * different streams are independent if they use different stores and
+ * workspaces.
  *
  * Errors: every entry point returns 0 on success or a negative READKV_E*
  * code.  All argument checks happen on the host before anything is

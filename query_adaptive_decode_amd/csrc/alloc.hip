@@ -33,15 +33,15 @@ namespace readkv {
 // nothing).
 // ---------------------------------------------------------------------------
 template <int GQA, int DT, int NUMAX>
-__global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, const void* q, int H, int G,
-                                                   int W, float RK, int NU, uint8_t* tk) {
+__global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0, const void* q, int H,
+                                                   int G, int W, float RK, int NU, uint8_t* tk) {
   constexpr int NT = 256;
   constexpr int esize = DT == 0 ? 2 : 4;
   __shared__ ChooseShared<NT> S;
   __shared__ double wl[NUMAX * kDim];
   __shared__ int bad[NUMAX];
   const int tid = threadIdx.x;
-  const int u0 = blockIdx.x * NU;
+  const int u0 = ub0 + (int)blockIdx.x * NU;
   const int b = u0 / G, g0 = u0 % G;
   const ReqRecord r = req_of(store, b);
   if (tid < NU) bad[tid] = 0;
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, const v
 constexpr int kVChunk = 1024;
 
 template <int GQA>
-__global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int H, int G, int W,
+__global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int ub0, int H, int G, int W,
                                                        int esize, int vscale, int64_t capmax,
                                                        int ntile_ws, const uint32_t* ebuf,
                                                        const double* tilepart, double* ftile,
@@ -94,7 +94,8 @@ __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int
   constexpr int TPC = kVChunk / kTile;  // score tiles per chunk
   static_assert(kVChunk == 4 * 256, "four tokens per thread");
   __shared__ double fs[GQA][TPC];
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int ux = ub0 + (int)blockIdx.x;
+  const int b = ux / G, g = ux % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
@@ -165,7 +166,7 @@ constexpr int kVSelNT = 1024;
 constexpr int kVSelLocal = 16384;
 
 template <bool LOCAL>
-__global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, int G, int W,
+__global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, int ub0, int G, int W,
                                                           int esize, float RV, int NU,
                                                           int64_t capmax, const double* aval,
                                                           uint8_t* tv, const uint8_t* tk,
@@ -173,7 +174,7 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
   constexpr int NT = kVSelNT;
   __shared__ ChooseShared<NT> S;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int u0 = blockIdx.x * NU;
+  const int u0 = ub0 + (int)blockIdx.x * NU;
   const int b = u0 / G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
 // ---------------------------------------------------------------------------
 template <int GQA>
 __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
-    const uint8_t* store, int H, int G, int W, int esize, int vscale, float RV, int64_t capmax,
+    const uint8_t* store, int ub0, int H, int G, int W, int esize, int vscale, float RV, int64_t capmax,
     int ntile_ws, const uint32_t* ebuf, const double* tilepart, double* ftile, uint8_t* tv,
     const uint8_t* tk, uint64_t* counters) {
   constexpr int NT = kVSelNT;
@@ -251,7 +252,8 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
   __shared__ ChooseShared<NT> S;
   __shared__ double fs[GQA][kVSelLocal / kTile];
   extern __shared__ double acache[];  // [T_p]
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int ux = ub0 + (int)blockIdx.x;
+  const int b = ux / G, g = ux % G;
   const ReqRecord r = req_of(store, b);
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
@@ -332,36 +334,36 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
 
 // ---------------------------------------------------------------------------
 template <int GQA, int DT>
-static void key_alloc_gqa(const DecodeArgs& a, uint8_t* tk, hipStream_t st) {
+static void key_alloc_gqa(const DecodeArgs& a, const Part& P, uint8_t* tk, hipStream_t st) {
   const int NU = a.G;  // per-layer budgets: one selection per request
-  hipLaunchKernelGGL((k_key_alloc<GQA, DT, kMaxPooledKV>), dim3(a.B), dim3(256), 0, st,
-                     (const uint8_t*)a.store, a.q, a.H, a.G, a.W, a.RK, NU, tk);
+  hipLaunchKernelGGL((k_key_alloc<GQA, DT, kMaxPooledKV>), dim3(P.nunits / NU), dim3(256), 0, st,
+                     (const uint8_t*)a.store, P.ub0, a.q, a.H, a.G, a.W, a.RK, NU, tk);
 }
 
 template <int DT>
-static int key_alloc_dt(const DecodeArgs& a, uint8_t* tk, hipStream_t st) {
+static int key_alloc_dt(const DecodeArgs& a, const Part& P, uint8_t* tk, hipStream_t st) {
   switch (a.H / a.G) {
-    case 1: key_alloc_gqa<1, DT>(a, tk, st); return 0;
-    case 2: key_alloc_gqa<2, DT>(a, tk, st); return 0;
-    case 3: key_alloc_gqa<3, DT>(a, tk, st); return 0;
-    case 4: key_alloc_gqa<4, DT>(a, tk, st); return 0;
-    case 5: key_alloc_gqa<5, DT>(a, tk, st); return 0;
-    case 6: key_alloc_gqa<6, DT>(a, tk, st); return 0;
-    case 7: key_alloc_gqa<7, DT>(a, tk, st); return 0;
-    case 8: key_alloc_gqa<8, DT>(a, tk, st); return 0;
+    case 1: key_alloc_gqa<1, DT>(a, P, tk, st); return 0;
+    case 2: key_alloc_gqa<2, DT>(a, P, tk, st); return 0;
+    case 3: key_alloc_gqa<3, DT>(a, P, tk, st); return 0;
+    case 4: key_alloc_gqa<4, DT>(a, P, tk, st); return 0;
+    case 5: key_alloc_gqa<5, DT>(a, P, tk, st); return 0;
+    case 6: key_alloc_gqa<6, DT>(a, P, tk, st); return 0;
+    case 7: key_alloc_gqa<7, DT>(a, P, tk, st); return 0;
+    case 8: key_alloc_gqa<8, DT>(a, P, tk, st); return 0;
     default: return -5;
   }
 }
 
-int launch_key_alloc(const DecodeArgs& a, uint8_t* tk, hipStream_t st) {
-  return a.dtype == 0 ? key_alloc_dt<0>(a, tk, st) : key_alloc_dt<1>(a, tk, st);
+int launch_key_alloc(const DecodeArgs& a, const Part& P, uint8_t* tk, hipStream_t st) {
+  return a.dtype == 0 ? key_alloc_dt<0>(a, P, tk, st) : key_alloc_dt<1>(a, P, tk, st);
 }
 
 // per-KV-head budgets and a capacity that fits LDS: one fused launch;
 // otherwise value weights (all compute units) then the selection
 template <int GQA>
-static bool value_first_gqa(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk, uint8_t* tv,
-                            hipStream_t st) {
+static bool value_first_gqa(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
+                            uint8_t* tv, hipStream_t st) {
   if (a.scope == 0 && a.capmax <= kVSelLocal) {
     static bool attr_set = false;
     if (!attr_set) {
@@ -369,33 +371,33 @@ static bool value_first_gqa(const DecodeArgs& a, const WsLayout& L, const uint8_
                           hipFuncAttributeMaxDynamicSharedMemorySize, kVSelLocal * 8);
       attr_set = true;
     }
-    hipLaunchKernelGGL((k_value_alloc_unit<GQA>), dim3(a.B * a.G), dim3(kVSelNT), (size_t)a.capmax * 8,
-                       st, (const uint8_t*)a.store, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.RV,
+    hipLaunchKernelGGL((k_value_alloc_unit<GQA>), dim3(P.nunits), dim3(kVSelNT), (size_t)a.capmax * 8,
+                       st, (const uint8_t*)a.store, P.ub0, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.RV,
                        a.capmax, L.ntile, (const uint32_t*)(a.ws + L.ebuf),
                        (const double*)(a.ws + L.tilepart), (double*)(a.ws + L.ftile), tv, tk,
                        a.counters);
     return true;
   }
   const int nch = (int)((a.capmax + kVChunk - 1) / kVChunk);
-  hipLaunchKernelGGL((k_value_weights<GQA>), dim3(a.B * a.G, nch), dim3(256), 0, st,
-                     (const uint8_t*)a.store, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.capmax,
+  hipLaunchKernelGGL((k_value_weights<GQA>), dim3(P.nunits, nch), dim3(256), 0, st,
+                     (const uint8_t*)a.store, P.ub0, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.capmax,
                      L.ntile, (const uint32_t*)(a.ws + L.ebuf), (const double*)(a.ws + L.tilepart),
                      (double*)(a.ws + L.ftile), (double*)(a.ws + L.aval));
   return false;
 }
 
-int launch_value_alloc(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk, uint8_t* tv,
-                       hipStream_t st) {
+int launch_value_alloc(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
+                       uint8_t* tv, hipStream_t st) {
   bool done;
   switch (a.H / a.G) {
-    case 1: done = value_first_gqa<1>(a, L, tk, tv, st); break;
-    case 2: done = value_first_gqa<2>(a, L, tk, tv, st); break;
-    case 3: done = value_first_gqa<3>(a, L, tk, tv, st); break;
-    case 4: done = value_first_gqa<4>(a, L, tk, tv, st); break;
-    case 5: done = value_first_gqa<5>(a, L, tk, tv, st); break;
-    case 6: done = value_first_gqa<6>(a, L, tk, tv, st); break;
-    case 7: done = value_first_gqa<7>(a, L, tk, tv, st); break;
-    case 8: done = value_first_gqa<8>(a, L, tk, tv, st); break;
+    case 1: done = value_first_gqa<1>(a, P, L, tk, tv, st); break;
+    case 2: done = value_first_gqa<2>(a, P, L, tk, tv, st); break;
+    case 3: done = value_first_gqa<3>(a, P, L, tk, tv, st); break;
+    case 4: done = value_first_gqa<4>(a, P, L, tk, tv, st); break;
+    case 5: done = value_first_gqa<5>(a, P, L, tk, tv, st); break;
+    case 6: done = value_first_gqa<6>(a, P, L, tk, tv, st); break;
+    case 7: done = value_first_gqa<7>(a, P, L, tk, tv, st); break;
+    case 8: done = value_first_gqa<8>(a, P, L, tk, tv, st); break;
     default: return -5;
   }
   if (done) return 0;
@@ -408,9 +410,9 @@ int launch_value_alloc(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk
                         hipFuncAttributeMaxDynamicSharedMemorySize, kVSelLocal * 8);
     attr_set = true;
   }
-  hipLaunchKernelGGL(local ? &k_value_select<true> : &k_value_select<false>, dim3(a.B * a.G / NU),
+  hipLaunchKernelGGL(local ? &k_value_select<true> : &k_value_select<false>, dim3(P.nunits / NU),
                      dim3(kVSelNT), local ? (size_t)nmax * 8 : 0, st,
-                     (const uint8_t*)a.store, a.G, a.W, a.dtype == 0 ? 2 : 4, a.RV, NU, a.capmax,
+                     (const uint8_t*)a.store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4, a.RV, NU, a.capmax,
                      (const double*)(a.ws + L.aval), tv, tk, a.counters);
   return 0;
 }

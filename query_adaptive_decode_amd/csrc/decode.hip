@@ -340,7 +340,7 @@ __device__ __forceinline__ double half_sum(double v) {
 }
 
 template <int GQA, int DT>
-__global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* store, const void* q, uint8_t* tk,
+__global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* store, int ub0, const void* q, uint8_t* tk,
                                                   int tk_ready,
                                                   int H, int G, int W, float RK, int64_t capmax,
                                                   int ntile_ws, uint32_t* ebuf,
@@ -375,7 +375,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // the call's read counters start from zero (the value selection, a later
   // launch, adds to them)
   if (counters && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0ull;
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int ux = ub0 + (int)blockIdx.x;  // the unit (request, KV head)
+  const int b = ux / G, g = ux % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
   const int ntl = (int)((len + kTile - 1) / kTile);
@@ -892,7 +893,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int GQA, int DT>
-__global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const uint8_t* tv, int H,
+__global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0, const uint8_t* tv, int H,
                                                    int G, int W, int64_t capmax, int ntile_ws,
                                                    int nrun_ws, const uint32_t* ebuf,
                                                    const double* ftile, float* opart) {
@@ -919,7 +920,8 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, const u
   __shared__ float fs[GQA];
   __shared__ __attribute__((aligned(16))) _Float16 ezero[8];  // a zero weight operand
 
-  const int b = blockIdx.x / G, g = blockIdx.x % G;
+  const int ux = ub0 + (int)blockIdx.x;
+  const int b = ux / G, g = ux % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
@@ -1206,17 +1208,18 @@ static inline void mark(const DecodeArgs& a, int i, hipStream_t st) {
   if (a.events) hipEventRecord((hipEvent_t)a.events[i], st);
 }
 
+// The launches for the units P.ub0 .. P.ub0 + P.nunits - 1 (whole
+// requests): key allocation (per-layer budgets), score, value allocation,
+// value gather.  The score of the part that starts at unit 0 zeroes the
+// read counters.
 template <int GQA, int DT>
-static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
+static int launch_part(const DecodeArgs& a, const WsLayout& L, const Part& P, uint8_t* tk, uint8_t* tv,
+                       int nrun_g, hipStream_t st) {
   uint8_t* ws = a.ws;
-  uint8_t* tk = a.key_depths_out ? a.key_depths_out : ws + L.tk;
-  uint8_t* tv = a.value_depths_out ? a.value_depths_out : ws + L.tv;
   const int NU = a.scope == 1 ? a.G : 1;  // KV heads per selection domain
-
-  mark(a, 0, st);
   // per-layer budgets: one key selection per request in its own launch;
   // per-KV-head budgets: inside the score kernel's blocks
-  if (NU > 1 && launch_key_alloc(a, tk, st)) return -5;
+  if (NU > 1 && launch_key_alloc(a, P, tk, st)) return -5;
   // slots staged per score tile: at most min(B_K of the domain, 128 W) chosen
   // key-line segments of one unit, 32 B each
   double bk = floor((double)a.RK * (double)(kDim * NU));
@@ -1234,34 +1237,44 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   }
   // each unit's tiles split evenly over nrun blocks: about three blocks per
   // compute unit in all (two for more than 4 query heads per KV head)
-  const int64_t total_tiles = (int64_t)a.B * a.G * L.ntile;
+  const int64_t total_tiles = (int64_t)P.nunits * L.ntile;
   const int64_t slots = (GQA <= 4 ? 3 : 2) * (int64_t)device_cu_count();
   int run = (int)((total_tiles + slots - 1) / slots);
   if (run < 1) run = 1;
   const int nrun = (L.ntile + run - 1) / run;
-  hipLaunchKernelGGL((k_score<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), dyn, st,
-                     (const uint8_t*)a.store, a.q, tk, NU > 1 ? 1 : 0, a.H, a.G, a.W, a.RK,
+  hipLaunchKernelGGL((k_score<GQA, DT>), dim3(P.nunits, nrun), dim3(256), dyn, st,
+                     (const uint8_t*)a.store, P.ub0, a.q, tk, NU > 1 ? 1 : 0, a.H, a.G, a.W, a.RK,
                      a.capmax, L.ntile, (uint32_t*)(ws + L.ebuf), (double*)(ws + L.tilepart),
-                     a.counters);
-  mark(a, 1, st);
-  if (launch_value_alloc(a, L, tk, tv, st)) return -5;
-  mark(a, 2, st);
-  {
-    // runs of consecutive chunks per block: about four blocks per compute
-    // unit (37 KB of LDS each)
-    const int64_t total = (int64_t)a.B * a.G * L.nchunk;
-    const int64_t slots = 4 * (int64_t)device_cu_count();
-    int run = (int)((total + slots - 1) / slots);
-    if (run < 1) run = 1;
-    const int nrun = (L.nchunk + run - 1) / run;
-    hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(a.B * a.G, nrun), dim3(256), 0, st,
-                       (const uint8_t*)a.store, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax,
-                       L.ntile, L.nchunk, (const uint32_t*)(ws + L.ebuf),
-                       (const double*)(ws + L.ftile), (float*)(ws + L.opart));
-    const int64_t nout = (int64_t)a.B * a.H * kDim;
-    hipLaunchKernelGGL(k_out_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st, nrun,
-                       L.nchunk, nout, (const float*)(ws + L.opart), a.out);
-  }
+                     P.ub0 == 0 ? a.counters : nullptr);
+  if (P.ub0 == 0) mark(a, 1, st);
+  if (launch_value_alloc(a, P, L, tk, tv, st)) return -5;
+  if (P.ub0 == 0) mark(a, 2, st);
+  hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(P.nunits, nrun_g), dim3(256), 0, st,
+                     (const uint8_t*)a.store, P.ub0, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax,
+                     L.ntile, L.nchunk, (const uint32_t*)(ws + L.ebuf), (const double*)(ws + L.ftile),
+                     (float*)(ws + L.opart));
+  return 0;
+}
+
+template <int GQA, int DT>
+static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
+  uint8_t* tk = a.key_depths_out ? a.key_depths_out : a.ws + L.tk;
+  uint8_t* tv = a.value_depths_out ? a.value_depths_out : a.ws + L.tv;
+  // runs of consecutive chunks per gather block: about four blocks per
+  // compute unit over the whole call (37 KB of LDS each)
+  const int64_t total = (int64_t)a.B * a.G * L.nchunk;
+  const int64_t gslots = 4 * (int64_t)device_cu_count();
+  int grun = (int)((total + gslots - 1) / gslots);
+  if (grun < 1) grun = 1;
+  const int nrun_g = (L.nchunk + grun - 1) / grun;
+
+  mark(a, 0, st);
+  const Part P{0, a.B * a.G};
+  const int rc = launch_part<GQA, DT>(a, L, P, tk, tv, nrun_g, st);
+  if (rc) return rc;
+  const int64_t nout = (int64_t)a.B * a.H * kDim;
+  hipLaunchKernelGGL(k_out_reduce, dim3((unsigned)((nout + 255) / 256)), dim3(256), 0, st, nrun_g,
+                     L.nchunk, nout, (const float*)(a.ws + L.opart), a.out);
   mark(a, 3, st);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }

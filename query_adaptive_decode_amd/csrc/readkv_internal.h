@@ -38,9 +38,13 @@ struct DecodeArgs {
 int launch_store_zero(void* store, size_t bytes, hipStream_t st);
 int launch_encode(const EncodeArgs& a, hipStream_t st);
 int launch_decode(const DecodeArgs& a, hipStream_t st);
+// A part of a decode call: the units [ub0, ub0 + nunits) (whole requests).
+struct Part {
+  int ub0, nunits;
+};
 // the allocation stages (alloc.hip); tk, tv: the depth arrays of the call
-int launch_key_alloc(const DecodeArgs& a, uint8_t* tk, hipStream_t st);
-int launch_value_alloc(const DecodeArgs& a, const WsLayout& L, const uint8_t* tk, uint8_t* tv,
-                       hipStream_t st);
+int launch_key_alloc(const DecodeArgs& a, const Part& P, uint8_t* tk, hipStream_t st);
+int launch_value_alloc(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
+                       uint8_t* tv, hipStream_t st);
 
 }  // namespace readkv
