@@ -73,6 +73,17 @@ extern "C" {
 #define READKV_SCOPE_KV_HEAD 0
 #define READKV_SCOPE_LAYER 1
 
+/* Restrictions of the pages' GPU reader (Sec. 5.1, App. F.8), OR'ed into
+ * the policy argument of readkv_decode_attn:
+ * MIN_DEPTH1: every key channel and value token is read to depth >= 1; those
+ *   N levels count against the budget (App. F.6), max(0, B - N) remain, and
+ *   the minimum is kept even when B < N.
+ * VALUE_PAIRS: tokens 2m and 2m + 1 of a KV head share one value depth; a
+ *   pair is one item whose weight is the sum of its tokens' weights, and a
+ *   pair level costs two token levels (floor(B_V / 2) pair levels). */
+#define READKV_RESTRICT_MIN_DEPTH1 0x10
+#define READKV_RESTRICT_VALUE_PAIRS 0x20
+
 /* Logical-read counters of one decode call (App. A.1: payload and metadata
  * bits the reader asks for; workspace and schedules are not counted), summed
  * over every request and KV head:
@@ -159,8 +170,9 @@ int readkv_encode_append(const readkv_config* cfg, void* store,
  *   d_h) over the G * d_h channels and one B_V = floor(R_V * G * T_packed)
  *   over the G * T_packed tokens of each request, items ordered by KV head
  *   then channel / token (ties to the lowest in that order).
- * scope: READKV_SCOPE_KV_HEAD or READKV_SCOPE_LAYER (the latter needs
- *   num_kv_heads <= 32, else EUNSUPPORTED).
+ * policy: READKV_SCOPE_KV_HEAD or READKV_SCOPE_LAYER (the latter needs
+ *   num_kv_heads <= 32, else EUNSUPPORTED), OR'ed with any of the
+ *   READKV_RESTRICT_* flags; other bits give EINVAL.
  * vscale: READKV_VSCALE_PHYSICAL or READKV_VSCALE_UNIT.
  * out: device fp32 [batch][num_q_heads][head_dim].
  * workspace: device, >= readkv_workspace_bytes.
@@ -174,7 +186,7 @@ int readkv_encode_append(const readkv_config* cfg, void* store,
  * token index; only positive gains are taken.  Results are bitwise
  * reproducible from call to call. */
 int readkv_decode_attn(const readkv_config* cfg, const void* store,
-                       const void* q, float R_K, float R_V, int32_t scope,
+                       const void* q, float R_K, float R_V, int32_t policy,
                        int32_t vscale, float* out, void* workspace,
                        size_t workspace_bytes, uint8_t* key_depths_out,
                        uint8_t* value_depths_out, uint64_t* counters_out,
@@ -190,7 +202,7 @@ int readkv_decode_attn(const readkv_config* cfg, const void* store,
  * any of the 4 handles is NULL). */
 int readkv_decode_attn_timed(const readkv_config* cfg, const void* store,
                              const void* q, float R_K, float R_V,
-                             int32_t scope, int32_t vscale, float* out,
+                             int32_t policy, int32_t vscale, float* out,
                              void* workspace, size_t workspace_bytes,
                              uint8_t* key_depths_out,
                              uint8_t* value_depths_out,
@@ -210,7 +222,7 @@ int readkv_decode_attn_timed(const readkv_config* cfg, const void* store,
 #define READKV_NOALLOC_SCRATCH_BYTES (64u << 20)
 int readkv_decode_attn_noalloc(const readkv_config* cfg, const void* store,
                                const void* q, float R_K, float R_V,
-                               int32_t scope, int32_t vscale, float* out,
+                               int32_t policy, int32_t vscale, float* out,
                                uint8_t* key_depths_out,
                                uint8_t* value_depths_out,
                                uint64_t* counters_out, void* stream);

@@ -32,6 +32,9 @@ reason in the design notes of the repository):
 * Tokens of the not-yet-full group are kept exactly and enter the softmax and
   the output, but not the allocation.
 * A query with a non-finite value reads nothing: depths 0, outputs NaN.
+* Restricted reader (min_depth=1, value_pairs): the minimum depth applies to
+  both stages and its levels count against the budget; a value packet's
+  weight is the sum of its two tokens' weights.
 """
 from __future__ import annotations
 
@@ -46,7 +49,7 @@ __all__ = [
     "bf16_down", "bf16_up", "encode_stream", "EncodedStream", "prefix",
     "reconstruct", "gain_table", "choose_depths", "key_weights",
     "value_weights", "budget", "decode_unit", "softmax",
-    "reuse_overhead", "reuse_reads", "logical_reads", "decode_request",
+    "reuse_overhead", "reuse_reads", "logical_reads", "decode_request", "pair_depths",
 ]
 
 
@@ -189,21 +192,29 @@ def gain_table(W: int) -> np.ndarray:
     return np.array([0.0] + [math.ldexp(1.0, -2 * t) for t in range(1, W + 1)])
 
 
-def choose_depths(a: np.ndarray, gains: np.ndarray, W: int, B: int) -> np.ndarray:
+def choose_depths(a: np.ndarray, gains: np.ndarray, W: int, B: int, start: int = 0) -> np.ndarray:
     """ChooseDepths(a, D, W, B): start from depth 0 everywhere and repeatedly
     deepen, by one level, the eligible item (depth < W) whose next refinement
     has the largest positive weighted gain a_i * gain[t_i + 1]; stop after B
     increments or when no positive gain remains.  Ties go to the lowest item
-    index.  Max-heap form, O(N + B log N) ([ReadKV] Sec. 3.3)."""
+    index.  Max-heap form, O(N + B log N) ([ReadKV] Sec. 3.3).
+
+    start = 1: the mandatory minimum depth of the restricted reader ([ReadKV]
+    Sec. 5.1, App. F.8): every item starts at depth 1, and those N levels
+    count against the budget (App. F.6 counts l*N + k(W - l) increments for a
+    lower depth l), so max(0, B - N) increments remain."""
     a = np.asarray(a, dtype=np.float64)
     n = a.shape[0]
-    t = np.zeros(n, dtype=np.int64)
+    t = np.full(n, start, dtype=np.int64)
     heap = []
     for i in range(n):
-        g = float(a[i]) * float(gains[1])
+        if start >= W:
+            break
+        g = float(a[i]) * float(gains[start + 1])
         if g > 0.0:
             heap.append((-g, i))
     heapq.heapify(heap)
+    B = max(0, B - start * n)
     taken = 0
     while taken < B and heap:
         negg, i = heapq.heappop(heap)
@@ -266,8 +277,20 @@ def softmax(z: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # One decode step for one (request, KV head) unit ([ReadKV] Sec. 3, Alg. 1)
 # ----------------------------------------------------------------------------
+def pair_depths(wv, gains, W, BV, start):
+    """Two-token value packets ([ReadKV] Sec. 5.1, App. F.8): tokens 2m and
+    2m + 1 share one depth, so a packet is one item whose weight is the sum
+    of its tokens' weights (the objective sum_j a_j D(t_j) with t shared),
+    and one packet level costs two token levels: floor(B_V / 2) packet
+    levels.  Returns the per-token depths."""
+    wp = wv[0::2] + wv[1::2]
+    tp2 = choose_depths(wp, gains, W, BV // 2, start)
+    return np.repeat(tp2, 2), wp
+
+
 def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
-                vscale="physical", enc_k=None, enc_v=None, diagnostics=False):
+                vscale="physical", enc_k=None, enc_v=None, diagnostics=False,
+                min_depth=0, value_pairs=False):
     """Two-stage (staged(2)) read for the query heads S(g) sharing one KV
     stream.
 
@@ -282,6 +305,10 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     Stage 2: value weights (Eq. (3)) from those probabilities -> ChooseDepths
       with B_V over the packed tokens.
     Final decoder: o_h = sum_j alpha_hat_{h,j} v_hat_j.
+    min_depth = 1 and value_pairs: the restricted GPU reader of [ReadKV]
+    Sec. 5.1 / App. F.8 (mandatory minimum depth one in both stages;
+    adjacent value tokens share a depth); ``wv`` then holds the packet
+    weights.
     """
     q_heads = np.asarray(q_heads, dtype=np.float64)
     d = q_heads.shape[1]
@@ -295,17 +322,18 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
 
     if not np.isfinite(q_heads).all():
         # The pages define no read for a query that is not a real vector.
-        # Reading: the unit reads nothing (every key and value depth 0) and
-        # every output of its query heads is NaN.
+        # Reading: the unit reads nothing beyond the mandatory minimum depth
+        # and every output of its query heads is NaN.
         gq = q_heads.shape[0]
-        return dict(out=np.full((gq, d), np.nan), tK=np.zeros(d, dtype=np.int64),
-                    tV=np.zeros(tp, dtype=np.int64), wk=np.zeros(d), wv=np.zeros(tp),
+        nv = tp // 2 if value_pairs else tp
+        return dict(out=np.full((gq, d), np.nan), tK=np.full(d, min_depth, dtype=np.int64),
+                    tV=np.full(tp, min_depth, dtype=np.int64), wk=np.zeros(d), wv=np.zeros(nv),
                     BK=budget(R_K, d), BV=budget(R_V, tp), zhat=None, ahat=None, tp=tp)
 
     # stage 1: key prefix depths
     wk = key_weights(q_heads, enc_k)
     BK = budget(R_K, d)
-    tK = choose_depths(wk, gains, W, BK)
+    tK = choose_depths(wk, gains, W, BK, min_depth)
 
     # intermediate decoder
     Khat = reconstruct(enc_k.lo[gidx], enc_k.rng[gidx],
@@ -317,7 +345,10 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     # stage 2: value prefix depths
     wv = value_weights(ahat[:, :tp], enc_v, vscale)
     BV = budget(R_V, tp)
-    tV = choose_depths(wv, gains, W, BV)
+    if value_pairs:
+        tV, wv = pair_depths(wv, gains, W, BV, min_depth)
+    else:
+        tV = choose_depths(wv, gains, W, BV, min_depth)
 
     Vhat = reconstruct(enc_v.lo[gidx], enc_v.rng[gidx],
                        prefix(enc_v.codes, tV[:, None], W), tV[:, None])
@@ -335,7 +366,7 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
 # One decode step for one request with per-layer budgets ([ReadKV] Sec. 3.3)
 # ----------------------------------------------------------------------------
 def decode_request(q_all, Ks, Vs, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
-                   vscale="physical", encs=None):
+                   vscale="physical", encs=None, min_depth=0, value_pairs=False):
     """The flexible reader of [ReadKV] Sec. 3.3: one key budget and one
     value budget for the whole layer of a request instead of one per KV head
     (the per-head budgets are the GPU reader's restriction of Sec. 5.1 /
@@ -368,7 +399,7 @@ def decode_request(q_all, Ks, Vs, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     wk = np.concatenate([key_weights(qs[g], encs[g][0]) if good[g] else np.zeros(d)
                          for g in range(G)])
     BK = budget(R_K, G * d)
-    tK = choose_depths(wk, gains, W, BK).reshape(G, d)
+    tK = choose_depths(wk, gains, W, BK, min_depth).reshape(G, d)
 
     # intermediate decoder, per KV head
     ahat = []
@@ -383,7 +414,11 @@ def decode_request(q_all, Ks, Vs, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     wv = np.concatenate([value_weights(ahat[g][:, :tp], encs[g][1], vscale) if good[g]
                          else np.zeros(tp) for g in range(G)])
     BV = budget(R_V, G * tp)
-    tV = choose_depths(wv, gains, W, BV).reshape(G, tp)
+    if value_pairs:
+        tV, wv = pair_depths(wv, gains, W, BV, min_depth)
+        tV = tV.reshape(G, tp)
+    else:
+        tV = choose_depths(wv, gains, W, BV, min_depth).reshape(G, tp)
 
     out = np.zeros((G, gqa, d))
     for g in range(G):

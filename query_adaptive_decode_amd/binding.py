@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libreadkv.so")
 BF16, F32 = 0, 1
 VSCALE_PHYSICAL, VSCALE_UNIT = 0, 1
 SCOPE_KV_HEAD, SCOPE_LAYER = 0, 1
+RESTRICT_MIN_DEPTH1, RESTRICT_VALUE_PAIRS = 0x10, 0x20   # OR'ed into a policy
 NUM_COUNTERS = 4   # key payload, value payload, metadata, open group (bits)
 FLAG_NONFINITE, FLAG_OVERFLOW = 1, 2
 
@@ -155,14 +156,15 @@ def _out(cfg, q, out):
 
 def decode_attn(cfg: Config, store, q, R_K, R_V, workspace, out=None,
                 vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None,
-                scope=SCOPE_KV_HEAD, counters=None):
+                policy=SCOPE_KV_HEAD, counters=None):
     """q: [B][H][d] device tensor in the config's dtype.  Returns out
-    [B][H][d] fp32.  counters: optional int64 device tensor of NUM_COUNTERS
-    entries, overwritten with the call's logical reads in bits."""
+    [B][H][d] fp32.  policy: a budget scope OR'ed with RESTRICT_* flags.
+    counters: optional int64 device tensor of NUM_COUNTERS entries,
+    overwritten with the call's logical reads in bits."""
     out = _out(cfg, q, out)
     _need_cuda(store, q, out, workspace, key_depths, value_depths, counters)
     _check("readkv_decode_attn", lib().readkv_decode_attn(
-        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(scope),
+        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(policy),
         int(vscale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(key_depths), _ptr(value_depths), _ptr(counters), _stream()))
     return out
@@ -170,7 +172,7 @@ def decode_attn(cfg: Config, store, q, R_K, R_V, workspace, out=None,
 
 def decode_attn_timed(cfg: Config, store, q, R_K, R_V, workspace, events, out=None,
                       vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None,
-                      scope=SCOPE_KV_HEAD, counters=None):
+                      policy=SCOPE_KV_HEAD, counters=None):
     """decode_attn that records four caller-created hipEvent_t handles
     (``events``: sequence of ints) around its three stages (score, value
     allocation, value gather)."""
@@ -178,7 +180,7 @@ def decode_attn_timed(cfg: Config, store, q, R_K, R_V, workspace, events, out=No
     _need_cuda(store, q, out, workspace, key_depths, value_depths, counters)
     ev = (ctypes.c_void_p * 4)(*[int(e) for e in events])
     _check("readkv_decode_attn_timed", lib().readkv_decode_attn_timed(
-        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(scope),
+        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(policy),
         int(vscale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _ptr(key_depths), _ptr(value_depths), _ptr(counters), ctypes.cast(ev, ctypes.c_void_p),
         _stream()))
@@ -189,12 +191,12 @@ NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def decode_attn_noalloc(cfg: Config, store, q, R_K, R_V, out, vscale=VSCALE_PHYSICAL,
-                        key_depths=None, value_depths=None, scope=SCOPE_KV_HEAD, counters=None):
+                        key_depths=None, value_depths=None, policy=SCOPE_KV_HEAD, counters=None):
     """decode_attn without a workspace: the library's fixed per-GPU scratch
     is used, nothing is allocated (``out`` must be given)."""
     _need_cuda(store, q, out, key_depths, value_depths, counters)
     _check("readkv_decode_attn_noalloc", lib().readkv_decode_attn_noalloc(
-        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(scope),
+        ctypes.byref(cfg), _ptr(store), _ptr(q), float(R_K), float(R_V), int(policy),
         int(vscale), _ptr(out), _ptr(key_depths), _ptr(value_depths), _ptr(counters),
         _stream()))
     return out
@@ -221,9 +223,9 @@ class ReadKVCache:
         encode_append(self.cfg, self.store, k_new, v_new, n_new, n_max)
 
     def decode(self, q, R_K, R_V, out=None, vscale=VSCALE_PHYSICAL, key_depths=None,
-               value_depths=None, scope=SCOPE_KV_HEAD, counters=None):
+               value_depths=None, policy=SCOPE_KV_HEAD, counters=None):
         return decode_attn(self.cfg, self.store, q, R_K, R_V, self.workspace, out, vscale,
-                           key_depths, value_depths, scope, counters)
+                           key_depths, value_depths, policy, counters)
 
     def status(self):
         return store_status(self.cfg, self.store)

@@ -172,7 +172,7 @@ int readkv_encode_append(const readkv_config* cfg, void* store, const void* k_ne
 }
 
 static int decode_impl(const readkv_config* cfg, const void* store, const void* q, float R_K,
-                       float R_V, int32_t scope, int32_t vscale, float* out, void* workspace,
+                       float R_V, int32_t policy, int32_t vscale, float* out, void* workspace,
                        size_t workspace_bytes, uint8_t* key_depths_out,
                        uint8_t* value_depths_out, uint64_t* counters_out, void* const* events,
                        void* stream) {
@@ -181,7 +181,9 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   if (!store || !q || !out || !workspace) return READKV_EINVAL;
   if (!isfinite(R_K) || !isfinite(R_V) || R_K < 0.f || R_V < 0.f) return READKV_EINVAL;
   if (vscale != READKV_VSCALE_PHYSICAL && vscale != READKV_VSCALE_UNIT) return READKV_EINVAL;
-  if (scope != READKV_SCOPE_KV_HEAD && scope != READKV_SCOPE_LAYER) return READKV_EINVAL;
+  if (policy & ~(READKV_SCOPE_LAYER | READKV_RESTRICT_MIN_DEPTH1 | READKV_RESTRICT_VALUE_PAIRS))
+    return READKV_EINVAL;
+  const int scope = policy & READKV_SCOPE_LAYER;
   if (scope == READKV_SCOPE_LAYER && cfg->num_kv_heads > kMaxPooledKV) return READKV_EUNSUPPORTED;
   // budgets must fit the 32-bit counters: R * (items of a domain) <= 2^31
   const double nu = scope == READKV_SCOPE_LAYER ? (double)cfg->num_kv_heads : 1.0;
@@ -204,6 +206,8 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   a.value_depths_out = value_depths_out;
   a.counters = counters_out;
   a.scope = scope;
+  a.min1 = (policy & READKV_RESTRICT_MIN_DEPTH1) ? 1 : 0;
+  a.pairs = (policy & READKV_RESTRICT_VALUE_PAIRS) ? 1 : 0;
   a.B = cfg->batch;
   a.H = cfg->num_q_heads;
   a.G = cfg->num_kv_heads;
@@ -217,27 +221,27 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
 }
 
 int readkv_decode_attn(const readkv_config* cfg, const void* store, const void* q, float R_K,
-                       float R_V, int32_t scope, int32_t vscale, float* out, void* workspace,
+                       float R_V, int32_t policy, int32_t vscale, float* out, void* workspace,
                        size_t workspace_bytes, uint8_t* key_depths_out,
                        uint8_t* value_depths_out, uint64_t* counters_out, void* stream) {
-  return decode_impl(cfg, store, q, R_K, R_V, scope, vscale, out, workspace, workspace_bytes,
+  return decode_impl(cfg, store, q, R_K, R_V, policy, vscale, out, workspace, workspace_bytes,
                      key_depths_out, value_depths_out, counters_out, nullptr, stream);
 }
 
 int readkv_decode_attn_timed(const readkv_config* cfg, const void* store, const void* q,
-                             float R_K, float R_V, int32_t scope, int32_t vscale, float* out,
+                             float R_K, float R_V, int32_t policy, int32_t vscale, float* out,
                              void* workspace, size_t workspace_bytes, uint8_t* key_depths_out,
                              uint8_t* value_depths_out, uint64_t* counters_out,
                              void* const* events, void* stream) {
   if (!events) return READKV_EINVAL;
   for (int i = 0; i < 4; ++i)
     if (!events[i]) return READKV_EINVAL;
-  return decode_impl(cfg, store, q, R_K, R_V, scope, vscale, out, workspace, workspace_bytes,
+  return decode_impl(cfg, store, q, R_K, R_V, policy, vscale, out, workspace, workspace_bytes,
                      key_depths_out, value_depths_out, counters_out, events, stream);
 }
 
 int readkv_decode_attn_noalloc(const readkv_config* cfg, const void* store, const void* q,
-                               float R_K, float R_V, int32_t scope, int32_t vscale, float* out,
+                               float R_K, float R_V, int32_t policy, int32_t vscale, float* out,
                                uint8_t* key_depths_out, uint8_t* value_depths_out,
                                uint64_t* counters_out, void* stream) {
   int rc = readkv_validate_config(cfg);
@@ -247,7 +251,7 @@ int readkv_decode_attn_noalloc(const readkv_config* cfg, const void* store, cons
   if ((size_t)L.size > kScratchBytes) return READKV_ESCRATCH;
   void* ws = nullptr;
   if ((rc = scratch_of_current_device(&ws))) return rc;
-  return decode_impl(cfg, store, q, R_K, R_V, scope, vscale, out, ws, kScratchBytes,
+  return decode_impl(cfg, store, q, R_K, R_V, policy, vscale, out, ws, kScratchBytes,
                      key_depths_out, value_depths_out, counters_out, nullptr, stream);
 }
 

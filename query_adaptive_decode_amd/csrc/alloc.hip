@@ -34,7 +34,8 @@ namespace readkv {
 // ---------------------------------------------------------------------------
 template <int GQA, int DT, int NUMAX>
 __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0, const void* q, int H,
-                                                   int G, int W, float RK, int NU, uint8_t* tk) {
+                                                   int G, int W, float RK, int NU, int min1,
+                                                   uint8_t* tk) {
   constexpr int NT = 256;
   constexpr int esize = DT == 0 ? 2 : 4;
   __shared__ ChooseShared<NT> S;
@@ -62,14 +63,17 @@ __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0
     if (nf) bad[k] = 1;
   }
   __syncthreads();
-  for (int i = tid; i < N; i += NT)
-    if (bad[i / kDim]) wl[i] = 0.0;
+  // the minimum depth one: levels 2..W of w are levels 1..W-1 of w/4
+  // (exact), over the budget left after the N forced levels
+  const double sc = min1 ? 0.25 : 1.0;
+  for (int i = tid; i < N; i += NT) wl[i] = bad[i / kDim] ? 0.0 : wl[i] * sc;
   __syncthreads();
-  const uint32_t Bk = (uint32_t)floor((double)RK * (double)N);
+  uint32_t Bk = (uint32_t)floor((double)RK * (double)N);
+  if (min1) Bk = Bk > (uint32_t)N ? Bk - (uint32_t)N : 0u;
   uint8_t* const tkd = tk + (int64_t)u0 * kDim;
   block_choose_depths<NT, 4>(
-      N, Bk, W, [&](int64_t i) { return wl[i]; },
-      [&](int64_t i, uint32_t t) { tkd[i] = (uint8_t)t; }, S);
+      N, Bk, W - min1, [&](int64_t i) { return wl[i]; },
+      [&](int64_t i, uint32_t t) { tkd[i] = (uint8_t)(t + (uint32_t)min1); }, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -167,7 +171,8 @@ constexpr int kVSelLocal = 16384;
 
 template <bool LOCAL>
 __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, int ub0, int G, int W,
-                                                          int esize, float RV, int NU,
+                                                          int esize, float RV, int NU, int min1,
+                                                          int pairs,
                                                           int64_t capmax, const double* aval,
                                                           uint8_t* tv, const uint8_t* tk,
                                                           uint64_t* counters) {
@@ -179,40 +184,63 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
-  const int64_t N = (int64_t)NU * Tp;
-  const uint32_t Bv = (uint32_t)floor((double)RV * (double)N);
+  const int64_t NT_ = (int64_t)NU * Tp;  // tokens of the domain
   const double* const ab = aval + (int64_t)u0 * capmax;
   uint8_t* const tvb = tv + (int64_t)u0 * capmax;
-  auto at = [&](int64_t i) -> int64_t {  // item -> offset in the unit-major arrays
+  auto at = [&](int64_t i) -> int64_t {  // token -> offset in the unit-major arrays
     if (NU == 1) return i;
     const int64_t k = i / Tp;
     return k * capmax + (i - k * Tp);
   };
-  extern __shared__ double acache[];  // [N] when LOCAL
-  uint32_t mine;
+  // items: tokens, or pairs of tokens (2m, 2m + 1) with summed weights; the
+  // minimum depth one: weights / 4 over levels 1..W-1, budget less N
+  const int64_t N = pairs ? NT_ / 2 : NT_;
+  uint32_t Bv = (uint32_t)floor((double)RV * (double)NT_);
+  if (pairs) Bv /= 2u;
+  if (min1) Bv = (int64_t)Bv > N ? Bv - (uint32_t)N : 0u;
+  const double sc = min1 ? 0.25 : 1.0;
+  uint32_t mine = 0;  // this thread's token depths
+  auto put = [&](int64_t i, uint32_t t) {
+    t += (uint32_t)min1;
+    if (pairs) {
+      tvb[at(2 * i)] = (uint8_t)t;
+      tvb[at(2 * i + 1)] = (uint8_t)t;
+      mine += 2 * t;
+    } else {
+      tvb[at(i)] = (uint8_t)t;
+      mine += t;
+    }
+  };
+  extern __shared__ double acache[];  // [tokens] when LOCAL
   if constexpr (LOCAL) {
     // eight loads in flight per thread, then their LDS stores
-    for (int64_t i0 = 0; i0 < N; i0 += 8 * NT) {
+    for (int64_t i0 = 0; i0 < NT_; i0 += 8 * NT) {
       double v[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int64_t i = i0 + k * NT + tid;
-        v[k] = i < N ? ab[at(i)] : 0.0;
+        v[k] = i < NT_ ? ab[at(i)] : 0.0;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int64_t i = i0 + k * NT + tid;
-        if (i < N) acache[i] = v[k];
+        if (i < NT_) acache[i] = v[k];
       }
     }
     __syncthreads();
-    mine = block_choose_depths<NT, 4>(
-        N, Bv, W, [&](int64_t i) { return acache[i]; },
-        [&](int64_t i, uint32_t t) { tvb[at(i)] = (uint8_t)t; }, S);
+    block_choose_depths<NT, 4>(
+        N, Bv, W - min1,
+        [&](int64_t i) {
+          return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc;
+        },
+        put, S);
   } else {
-    mine = block_choose_depths<NT, 8>(
-        N, Bv, W, [&](int64_t i) { return ab[at(i)]; },
-        [&](int64_t i, uint32_t t) { tvb[at(i)] = (uint8_t)t; }, S);
+    block_choose_depths<NT, 8>(
+        N, Bv, W - min1,
+        [&](int64_t i) {
+          return (pairs ? __dadd_rn(ab[at(2 * i)], ab[at(2 * i + 1)]) : ab[at(i)]) * sc;
+        },
+        put, S);
   }
   if (counters) {
     const uint32_t vtot = block_sum_u32<NT>(mine, S.wsum);
@@ -244,7 +272,8 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
 // ---------------------------------------------------------------------------
 template <int GQA>
 __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
-    const uint8_t* store, int ub0, int H, int G, int W, int esize, int vscale, float RV, int64_t capmax,
+    const uint8_t* store, int ub0, int H, int G, int W, int esize, int vscale, float RV, int min1,
+    int pairs, int64_t capmax,
     int ntile_ws, const uint32_t* ebuf, const double* tilepart, double* ftile, uint8_t* tv,
     const uint8_t* tk, uint64_t* counters) {
   constexpr int NT = kVSelNT;
@@ -309,11 +338,30 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
     }
   }
   __syncthreads();
-  const uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
+  // items: tokens, or pairs of tokens (2m, 2m + 1) with summed weights; the
+  // minimum depth one: weights / 4 over levels 1..W-1, budget less N
+  const int64_t N = pairs ? Tp / 2 : Tp;
+  uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
+  if (pairs) Bv /= 2u;
+  if (min1) Bv = (int64_t)Bv > N ? Bv - (uint32_t)N : 0u;
+  const double sc = min1 ? 0.25 : 1.0;
   uint8_t* const tvb = tv + ((int64_t)b * G + g) * capmax;
-  const uint32_t mine = block_choose_depths<NT, 4>(
-      Tp, Bv, W, [&](int64_t i) { return acache[i]; },
-      [&](int64_t i, uint32_t t) { tvb[i] = (uint8_t)t; }, S);
+  uint32_t mine = 0;  // this thread's token depths
+  block_choose_depths<NT, 4>(
+      N, Bv, W - min1,
+      [&](int64_t i) { return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc; },
+      [&](int64_t i, uint32_t t) {
+        t += (uint32_t)min1;
+        if (pairs) {
+          tvb[2 * i] = (uint8_t)t;
+          tvb[2 * i + 1] = (uint8_t)t;
+          mine += 2 * t;
+        } else {
+          tvb[i] = (uint8_t)t;
+          mine += t;
+        }
+      },
+      S);
   if (counters) {
     const uint32_t vtot = block_sum_u32<NT>(mine, S.wsum);
     if (tid < 64) {
@@ -337,7 +385,7 @@ template <int GQA, int DT>
 static void key_alloc_gqa(const DecodeArgs& a, const Part& P, uint8_t* tk, hipStream_t st) {
   const int NU = a.G;  // per-layer budgets: one selection per request
   hipLaunchKernelGGL((k_key_alloc<GQA, DT, kMaxPooledKV>), dim3(P.nunits / NU), dim3(256), 0, st,
-                     (const uint8_t*)a.store, P.ub0, a.q, a.H, a.G, a.W, a.RK, NU, tk);
+                     (const uint8_t*)a.store, P.ub0, a.q, a.H, a.G, a.W, a.RK, NU, a.min1, tk);
 }
 
 template <int DT>
@@ -373,7 +421,7 @@ static bool value_first_gqa(const DecodeArgs& a, const Part& P, const WsLayout& 
     }
     hipLaunchKernelGGL((k_value_alloc_unit<GQA>), dim3(P.nunits), dim3(kVSelNT), (size_t)a.capmax * 8,
                        st, (const uint8_t*)a.store, P.ub0, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.RV,
-                       a.capmax, L.ntile, (const uint32_t*)(a.ws + L.ebuf),
+                       a.min1, a.pairs, a.capmax, L.ntile, (const uint32_t*)(a.ws + L.ebuf),
                        (const double*)(a.ws + L.tilepart), (double*)(a.ws + L.ftile), tv, tk,
                        a.counters);
     return true;
@@ -412,7 +460,8 @@ int launch_value_alloc(const DecodeArgs& a, const Part& P, const WsLayout& L, co
   }
   hipLaunchKernelGGL(local ? &k_value_select<true> : &k_value_select<false>, dim3(P.nunits / NU),
                      dim3(kVSelNT), local ? (size_t)nmax * 8 : 0, st,
-                     (const uint8_t*)a.store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4, a.RV, NU, a.capmax,
+                     (const uint8_t*)a.store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4, a.RV, NU, a.min1,
+                     a.pairs, a.capmax,
                      (const double*)(a.ws + L.aval), tv, tk, a.counters);
   return 0;
 }

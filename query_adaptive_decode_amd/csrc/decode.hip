@@ -341,7 +341,7 @@ __device__ __forceinline__ double half_sum(double v) {
 
 template <int GQA, int DT>
 __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* store, int ub0, const void* q, uint8_t* tk,
-                                                  int tk_ready,
+                                                  int tk_ready, int min1,
                                                   int H, int G, int W, float RK, int64_t capmax,
                                                   int ntile_ws, uint32_t* ebuf,
                                                   double* tilepart, uint64_t* counters) {
@@ -387,8 +387,9 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   const int tile_begin = (int)blockIdx.y;
   if (tile_begin >= ntl) {
     // an empty request has no closed group (E^K = 0): all key depths are 0
+    // (or the minimum depth)
     if (!tk_ready && ntl == 0 && blockIdx.y == 0 && threadIdx.x < kDim)
-      tk[((int64_t)b * G + g) * kDim + threadIdx.x] = 0;
+      tk[((int64_t)b * G + g) * kDim + threadIdx.x] = (uint8_t)min1;
     return;
   }
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
@@ -441,10 +442,16 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   const bool qbad = __syncthreads_or(qnf);
   if (!tk_ready) {
     if (wv == 0) {
-      const double w2[2] = {qbad ? 0.0 : kap[lane], qbad ? 0.0 : kap[lane + 64]};
+      // the minimum depth one: levels 2..W of w are levels 1..W-1 of w/4
+      // (exact), over the budget left after the d_h forced levels
+      const double sc = min1 ? 0.25 : 1.0;
+      const double w2[2] = {qbad ? 0.0 : kap[lane] * sc, qbad ? 0.0 : kap[lane + 64] * sc};
+      uint32_t Bk = (uint32_t)floor((double)RK * (double)kDim);
+      if (min1) Bk = Bk > (uint32_t)kDim ? Bk - (uint32_t)kDim : 0u;
       uint32_t sel[2];
-      key_depths_wave(w2, W, (uint32_t)floor((double)RK * (double)kDim),
-                      reinterpret_cast<uint32_t*>(planes), sel);
+      key_depths_wave(w2, W - min1, Bk, reinterpret_cast<uint32_t*>(planes), sel);
+      sel[0] += (uint32_t)min1;
+      sel[1] += (uint32_t)min1;
       tks[lane] = (uint8_t)sel[0];
       tks[lane + 64] = (uint8_t)sel[1];
       if (tile_begin == 0) {  // the unit's first block writes the depths out
@@ -1223,6 +1230,7 @@ static int launch_part(const DecodeArgs& a, const WsLayout& L, const Part& P, ui
   // slots staged per score tile: at most min(B_K of the domain, 128 W) chosen
   // key-line segments of one unit, 32 B each
   double bk = floor((double)a.RK * (double)(kDim * NU));
+  if (a.min1 && bk < (double)kDim) bk = (double)kDim;  // every channel at depth >= 1
   if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
   if (bk < 0.0) bk = 0.0;
   // (+8 slots: un-plane reads of a batch may run past a shallower channel's
@@ -1243,7 +1251,7 @@ static int launch_part(const DecodeArgs& a, const WsLayout& L, const Part& P, ui
   if (run < 1) run = 1;
   const int nrun = (L.ntile + run - 1) / run;
   hipLaunchKernelGGL((k_score<GQA, DT>), dim3(P.nunits, nrun), dim3(256), dyn, st,
-                     (const uint8_t*)a.store, P.ub0, a.q, tk, NU > 1 ? 1 : 0, a.H, a.G, a.W, a.RK,
+                     (const uint8_t*)a.store, P.ub0, a.q, tk, NU > 1 ? 1 : 0, a.min1, a.H, a.G, a.W, a.RK,
                      a.capmax, L.ntile, (uint32_t*)(ws + L.ebuf), (double*)(ws + L.tilepart),
                      P.ub0 == 0 ? a.counters : nullptr);
   if (P.ub0 == 0) mark(a, 1, st);

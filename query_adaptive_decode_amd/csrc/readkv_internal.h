@@ -29,7 +29,9 @@ struct DecodeArgs {
   uint8_t* key_depths_out;
   uint8_t* value_depths_out;
   uint64_t* counters;   // NULL, or 4 device words (readkv_decode_attn)
-  int scope;
+  int scope;            // 0: per (request, KV head) budgets, 1: per request
+  int min1;             // 1: minimum depth one in both stages
+  int pairs;            // 1: two-token value packets
   int B, H, G, W, dtype;
   int64_t capmax;
   void* const* events;  // NULL, or 4 hipEvent_t recorded around the 3 stages

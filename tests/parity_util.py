@@ -38,11 +38,12 @@ def _levels(t_from, t_to, w):
     return out
 
 
-def alloc_mismatch(t_gpu, t_or, w_or, W, rel=NEAR_TIE_REL):
+def alloc_mismatch(t_gpu, t_or, w_or, W, rel=NEAR_TIE_REL, start=0):
     """Returns (n_near_ties, n_bad, detail) for one selection domain.
 
     t_gpu, t_or: depth per item (GPU, oracle); w_or: the oracle's item
-    weights (gain of level t = w * 4^-t)."""
+    weights (gain of level t = w * 4^-t); start: the mandatory minimum depth
+    (levels up to it are not chosen, so they do not define tau_o)."""
     t_gpu = np.asarray(t_gpu, dtype=np.int64)
     t_or = np.asarray(t_or, dtype=np.int64)
     if t_gpu.sum() != t_or.sum():
@@ -50,7 +51,11 @@ def alloc_mismatch(t_gpu, t_or, w_or, W, rel=NEAR_TIE_REL):
     if np.array_equal(t_gpu, t_or):
         return 0, 0, ""
     w = np.asarray(w_or, dtype=np.float64)
-    sel = np.nonzero(t_or > 0)[0]
+    if np.any(t_gpu < start):
+        return 0, 1, f"a depth below the minimum {start}"
+    sel = np.nonzero(t_or > start)[0]
+    if len(sel) == 0:
+        return 0, 1, "the oracle chose no level, the GPU did"
     tau = float(np.min(w[sel] * 4.0 ** (-t_or[sel].astype(np.float64))))
     extra = _levels(t_or, t_gpu, w)     # chosen by the GPU only
     missing = _levels(t_gpu, t_or, w)   # chosen by the oracle only

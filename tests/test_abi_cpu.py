@@ -98,6 +98,8 @@ def test_entry_points_reject_bad_arguments_before_launch():
     def call(cfgp=by, store=fake, rk=1.0, rv=1.0, scope=0, vscale=0, wsb=ws):
         return dec(cfgp, store, fake, rk, rv, scope, vscale, fake, fake, wsb, None, None, None, None)
 
+    assert call(scope=0x2) == -1 and call(scope=0x40) == -1   # unknown policy bits
+
     for rk, rv in [(float("nan"), 1.0), (1.0, float("inf")), (-0.5, 1.0), (1.0, -1.0)]:
         assert call(rk=rk, rv=rv) == -1
     assert call(vscale=5) == -1

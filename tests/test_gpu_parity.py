@@ -20,7 +20,8 @@ import torch
 import oracle as O
 from oracle import store_format as F
 from query_adaptive_decode_amd import synth, workload
-from query_adaptive_decode_amd.binding import (NUM_COUNTERS, SCOPE_KV_HEAD, SCOPE_LAYER,
+from query_adaptive_decode_amd.binding import (NUM_COUNTERS, RESTRICT_MIN_DEPTH1,
+                                               RESTRICT_VALUE_PAIRS, SCOPE_KV_HEAD, SCOPE_LAYER,
                                                ReadKVCache, VSCALE_PHYSICAL, VSCALE_UNIT)
 from tests import parity_util as PU
 from tests.parity_util import OUT_REL_L2, alloc_mismatch, rel_l2
@@ -70,7 +71,9 @@ class Run:
     def __init__(self, cfg, steps, rates, vscale=VSCALE_PHYSICAL, repeat=False, keep_steps=None,
                  qmod=None, scope=SCOPE_KV_HEAD):
         self.cfg, self.steps, self.rates, self.vscale = cfg, steps, rates, vscale
-        self.scope = scope
+        self.scope = scope   # the decode policy: budget scope | RESTRICT_* flags
+        self.min1 = 1 if scope & RESTRICT_MIN_DEPTH1 else 0
+        self.pairs = bool(scope & RESTRICT_VALUE_PAIRS)
         B, H, G = cfg["B"], cfg["H"], cfg["G"]
         self.T0 = synth.context_lengths(cfg)
         say(f"[case] {cfg['name']} B={B} H={H} G={G} T0={self.T0.tolist()[:4]}"
@@ -103,13 +106,13 @@ class Run:
                 tv = torch.zeros(B * G * ((cap + 31) // 32 * 32), dtype=torch.uint8, device="cuda")
                 ctr = torch.full((NUM_COUNTERS,), -1, dtype=torch.int64, device="cuda")
                 out = cache.decode(dv["q"][s], rk, rv, vscale=vscale, key_depths=tk,
-                                   value_depths=tv, counters=ctr, scope=scope)
+                                   value_depths=tv, counters=ctr, policy=scope)
                 item = dict(step=s, rk=rk, rv=rv, out=out.cpu().numpy(),
                             tk=tk.cpu().numpy().reshape(B, G, 128),
                             tv=tv.cpu().numpy().reshape(B, G, -1), ctr=ctr.cpu().numpy())
                 if repeat:
                     out2 = cache.decode(dv["q"][s], rk, rv, vscale=vscale, key_depths=tk,
-                                        value_depths=tv, scope=scope)
+                                        value_depths=tv, policy=scope)
                     item["out2"] = out2.cpu().numpy()
                     item["tv2"] = tv.cpu().numpy().reshape(B, G, -1)
                 self.rec.append(item)
@@ -167,11 +170,19 @@ class Run:
                 q = self.qf[it["step"]][b, g * gqa:(g + 1) * gqa]
                 res = O.decode_unit(q, K[:n], V[:n], W=cfg["W"], R_K=it["rk"], R_V=it["rv"],
                                     vscale="unit" if self.vscale == VSCALE_UNIT else "physical",
-                                    enc_k=ek, enc_v=ev)
+                                    enc_k=ek, enc_v=ev, min_depth=self.min1,
+                                    value_pairs=self.pairs)
                 tag = f"{tag0} unit=({b},{g}) n={n}"
                 assert np.array_equal(it["tk"][b, g], res["tK"]), f"key depths differ {tag}"
                 tp = res["tp"]
-                near, bad, det = alloc_mismatch(it["tv"][b, g, :tp], res["tV"], res["wv"], cfg["W"])
+                tvg = it["tv"][b, g, :tp]
+                if self.pairs:
+                    assert np.array_equal(tvg[0::2], tvg[1::2]), f"packet depths differ {tag}"
+                    near, bad, det = alloc_mismatch(tvg[0::2], res["tV"][0::2], res["wv"], cfg["W"],
+                                                    start=self.min1)
+                else:
+                    near, bad, det = alloc_mismatch(tvg, res["tV"], res["wv"], cfg["W"],
+                                                    start=self.min1)
                 assert bad == 0, f"value depths differ {tag}: {det}"
                 st["near"] += near
                 st["checks"] += 1
@@ -217,12 +228,17 @@ class Run:
                 res = O.decode_request(self.qf[it["step"]][b], [K[:n] for K, _ in units],
                                        [V[:n] for _, V in units], W=cfg["W"], R_K=it["rk"],
                                        R_V=it["rv"], encs=encs,
-                                       vscale="unit" if self.vscale == VSCALE_UNIT else "physical")
+                                       vscale="unit" if self.vscale == VSCALE_UNIT else "physical",
+                                       min_depth=self.min1, value_pairs=self.pairs)
                 tag = f"{tag0} request={b} n={n}"
                 assert np.array_equal(it["tk"][b], res["tK"]), f"key depths differ {tag}"
                 tp = res["tp"]
-                near, bad, det = alloc_mismatch(it["tv"][b, :, :tp].reshape(-1), res["tV"].reshape(-1),
-                                                res["wv"], cfg["W"])
+                tvg = it["tv"][b, :, :tp].reshape(-1)
+                tvo = res["tV"].reshape(-1)
+                if self.pairs:
+                    assert np.array_equal(tvg[0::2], tvg[1::2]), f"packet depths differ {tag}"
+                    tvg, tvo = tvg[0::2], tvo[0::2]
+                near, bad, det = alloc_mismatch(tvg, tvo, res["wv"], cfg["W"], start=self.min1)
                 assert bad == 0, f"value depths differ {tag}: {det}"
                 st["near"] += near
                 st["checks"] += 1
@@ -419,6 +435,46 @@ def test_layer_budgets_full_size_llama_layer(record_property):
     cfg = synth.workload(2)
     run = Run(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 2.0)], scope=SCOPE_LAYER)
     report(record_property, "layer budgets B=16 T0=8192", run.check_layer([0, 9, 15]))
+
+
+# ------------------------------------------------------------ restricted reader
+RESTRICTED = [RESTRICT_MIN_DEPTH1, RESTRICT_VALUE_PAIRS, RESTRICT_MIN_DEPTH1 | RESTRICT_VALUE_PAIRS]
+
+
+@pytest.mark.parametrize("flags", RESTRICTED, ids=["min1", "pairs", "min1+pairs"])
+def test_restricted_reader_llama_shape(flags, record_property):
+    # the pages' GPU-reader restrictions: minimum depth one, two-token value
+    # packets; R = 1 with the minimum forces uniform depth-1 reads
+    cfg = synth.workload(2, B=2, T0=2000)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 2.0), (1.0, 1.0), (0.5, 0.5), (3.3, 2.7)],
+              scope=flags)
+    report(record_property, f"restricted {flags:#x} llama shape", run.check())
+
+
+def test_restricted_reader_gqa7_ragged_and_tails(record_property):
+    flags = RESTRICT_MIN_DEPTH1 | RESTRICT_VALUE_PAIRS
+    cfg = synth.workload(4, B=3, T0=(40, 1500))
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 2.0)], scope=flags)
+    st = run.check()
+    cfg = synth.workload(2, B=1, H=8, G=2, T0=33)
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (0.0, 0.0), (8.0, 8.0)], scope=flags)
+    st2 = run.check()
+    report(record_property, "restricted gqa7 ragged + tails",
+           dict(near=st["near"] + st2["near"], checks=st["checks"] + st2["checks"],
+                worst=max(st["worst"], st2["worst"])))
+
+
+def test_restricted_reader_layer_budgets(record_property):
+    flags = SCOPE_LAYER | RESTRICT_MIN_DEPTH1 | RESTRICT_VALUE_PAIRS
+    cfg = synth.workload(2, B=2, T0=2000)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 2.0), (1.0, 1.0)], scope=flags)
+    st = run.check_layer()
+    cfg = synth.workload(2, B=2, T0=1000)
+    run = Run(cfg, steps=1, rates=[(0.0, 1.3), (0.0, 2.7)], scope=SCOPE_LAYER | RESTRICT_VALUE_PAIRS)
+    st2 = run.check_layer()
+    report(record_property, "restricted layer budgets",
+           dict(near=st["near"] + st2["near"], checks=st["checks"] + st2["checks"],
+                worst=max(st["worst"], st2["worst"])))
 
 
 # ------------------------------------------------------------ long context

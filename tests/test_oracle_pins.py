@@ -226,6 +226,81 @@ def test_pooled_layer_budgets_equal_brute_force():
     assert np.isfinite(res["out"][1]).all()
 
 
+def _brute_best_from(a, W, B, lo):
+    """Exact minimum of sum_i a_i 4^-t_i over t in {lo..W}^N whose increments
+    beyond lo total at most max(0, B - lo N); canonical optimum as in
+    _brute_best."""
+    af = [Fraction(float(x)) for x in a]
+    rem = max(0, B - lo * len(a))
+    best = None
+    for t in itertools.product(range(lo, W + 1), repeat=len(a)):
+        if sum(t) - lo * len(a) > rem:
+            continue
+        obj = sum(ai * Fraction(1, 4 ** ti) for ai, ti in zip(af, t))
+        key = (obj, sum(t), tuple(-x for x in t))
+        if best is None or key < best[0]:
+            best = (key, t)
+    return best[1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_min_depth_one_equals_brute_force(seed):
+    # the restricted reader's mandatory minimum depth ([ReadKV] App. F.8),
+    # with its levels counted against the budget (App. F.6)
+    rng = np.random.default_rng(100 + seed)
+    N, W = 4, 3
+    a = rng.exponential(1.0, N) * 10.0 ** rng.integers(-2, 3, N)
+    if seed % 2 == 0:
+        a[2] = a[1]                     # an exact tie
+    if seed % 3 == 0:
+        a[0] = 0.0                      # zero weight: stays at depth 1
+    for B in range(0, N * W + 2):
+        t = O.choose_depths(a, O.gain_table(W), W, B, start=1)
+        assert tuple(t) == tuple(_brute_best_from(a, W, B, 1)), (a, B, t)
+        assert t.min() >= 1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_value_packets_equal_brute_force(seed):
+    # two-token value packets: tokens 2m and 2m+1 share a depth and a packet
+    # level costs two token levels; the packet schedule minimises
+    # sum_j a_j 4^-t_j over schedules with shared depths
+    rng = np.random.default_rng(200 + seed)
+    W = 3
+    a = rng.exponential(1.0, 6) * 10.0 ** rng.integers(-2, 3, 6)
+    af = [Fraction(float(x)) for x in a]
+    for start in (0, 1):
+        for B in range(0, 6 * W + 2):
+            t, wp = O.pair_depths(a, O.gain_table(W), W, B, start)
+            assert np.array_equal(t[0::2], t[1::2])
+            best = None
+            rem = max(0, B // 2 - start * 3)
+            for tp in itertools.product(range(start, W + 1), repeat=3):
+                if sum(tp) - 3 * start > rem:
+                    continue
+                obj = sum(af[j] * Fraction(1, 4 ** tp[j // 2]) for j in range(6))
+                key = (obj, sum(tp), tuple(-x for x in tp))
+                if best is None or key < best[0]:
+                    best = (key, tp)
+            assert tuple(t[0::2]) == best[1], (a, B, start, t)
+
+
+def test_min_depth_one_forces_uniform_values_at_rate_one():
+    # [ReadKV] App. F.8: a mandatory minimum depth of one forces uniform
+    # value reading when the value budget is R_V = 1 (with and without
+    # packets; keys likewise at R_K = 1)
+    from query_adaptive_decode_amd.synth import round_to_bf16
+    rng = np.random.default_rng(59)
+    K = round_to_bf16(rng.standard_normal((300, 128)) * rng.uniform(0.1, 5, 128))
+    V = round_to_bf16(rng.standard_normal((300, 128)))
+    q = round_to_bf16(rng.standard_t(3, (4, 128)))
+    for pairs in (False, True):
+        res = O.decode_unit(q, K, V, R_K=1.0, R_V=1.0, min_depth=1, value_pairs=pairs)
+        assert np.all(res["tV"] == 1) and np.all(res["tK"] == 1)
+        res0 = O.decode_unit(q, K, V, R_K=1.0, R_V=1.0, value_pairs=pairs)
+        assert not np.all(res0["tV"] == 1)   # without the floor the schedule is not uniform
+
+
 def test_objective_identity_exact():
     rng = np.random.default_rng(11)
     a = rng.exponential(1.0, 6)
