@@ -301,6 +301,7 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
   uint4 ev[GQA];
   double sg;
   load_round(0, ev, sg);
+  choose_clear<NT>(S);  // while the first round's exponentials are in flight
   for (int hh = wv; hh < GQA; hh += NT / 64) {
     const double* tp = tilepart + (hrow0 + hh) * ntile_ws * 2;
     // one tile per lane (at most 64 tiles in a unit that fits LDS)
@@ -315,7 +316,15 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
       ftile[(hrow0 + hh) * ntile_ws + lane] = f;
     }
   }
-  __syncthreads();
+  lds_barrier();
+  // items: tokens, or pairs of tokens (2m, 2m + 1) with summed weights; the
+  // minimum depth one: weights / 4 over levels 1..W-1, budget less N.  The
+  // selection's histograms are built here from the weights in registers, in
+  // exactly the form the selection reads them back from LDS.
+  const int64_t N = pairs ? Tp / 2 : Tp;
+  const double sc = min1 ? 0.25 : 1.0;
+  const int Wc = W - min1;
+  ChooseLocal CL;
   const int nr = (int)((Tp + RT - 1) / RT);
   for (int k = 0; k < nr; ++k) {
     if (k > 0) load_round(k, ev, sg);
@@ -334,21 +343,28 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
         }
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acache[j0 + q] = vscale == 0 ? __dmul_rn(sa[q], sg) : sa[q];
+      for (int q = 0; q < 4; ++q) {
+        sa[q] = vscale == 0 ? __dmul_rn(sa[q], sg) : sa[q];
+        acache[j0 + q] = sa[q];
+      }
+      if (pairs) {
+        choose_add<NT>(__dadd_rn(sa[0], sa[1]) * sc, Wc, S, CL);
+        choose_add<NT>(__dadd_rn(sa[2], sa[3]) * sc, Wc, S, CL);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) choose_add<NT>(sa[q] * sc, Wc, S, CL);
+      }
     }
   }
-  __syncthreads();
-  // items: tokens, or pairs of tokens (2m, 2m + 1) with summed weights; the
-  // minimum depth one: weights / 4 over levels 1..W-1, budget less N
-  const int64_t N = pairs ? Tp / 2 : Tp;
+  choose_flush<NT>(CL, S);
+  lds_barrier();
   uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
   if (pairs) Bv /= 2u;
   if (min1) Bv = (int64_t)Bv > N ? Bv - (uint32_t)N : 0u;
-  const double sc = min1 ? 0.25 : 1.0;
   uint8_t* const tvb = tv + ((int64_t)b * G + g) * capmax;
   uint32_t mine = 0;  // this thread's token depths
-  block_choose_depths<NT, 4>(
-      N, Bv, W - min1,
+  block_choose_depths_hist<NT, 4>(
+      N, Bv, Wc,
       [&](int64_t i) { return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc; },
       [&](int64_t i, uint32_t t) {
         t += (uint32_t)min1;

@@ -290,11 +290,21 @@ __device__ __forceinline__ int ilogb_bits(double v) {  // exponent of |v| (subno
   return (int)((dbits(v) >> 52) & 0x7FFu) - 1023;
 }
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations, not for its outstanding global loads (a full __syncthreads()
-// would also drain the prefetch of the next tile).
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Issue priority of the calling wave from a block's progress: level 3
+// (highest) over the first quarter of its work down to 0 over the last.
+// The SIMD's arbiter prefers older waves among equal priorities, so blocks
+// that share a compute unit would otherwise finish one after another (the
+// youngest up to a third later, with the unit under-occupied meanwhile);
+// dropping the priority of a block that is ahead lets the others catch up,
+// and they end together.
+__device__ __forceinline__ void set_progress_priority(int done, int total) {
+  const int lv = total > 0 ? 3 - (4 * done) / total : 0;
+  switch (lv) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
 }
 
 // e^x for x <= 0 (or -inf), relative error below 1e-9.  Cody-Waite range
@@ -642,7 +652,9 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   };
   const int c32 = lane & 31, sA = lane >> 5;  // A-build: channel, head pair of the quad
 
+  const int my_tiles = (ntl - tile_begin + ny - 1) / ny;
   for (int tile = tile_begin; tile < ntl; tile += ny) {
+    set_progress_priority((tile - tile_begin) / ny, my_tiles);
     const int64_t t0 = (int64_t)tile * kTile;
     const int ngp = tile_ngp(tile);
     const bool more = tile + ny < ntl;
@@ -1038,6 +1050,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   const int troff = (7 - (L >> 1)) * (RS * 16) + 8 * (L & 1);
 
   auto chunk_step = [&](int chunk, uint32_t& tcur, uint32_t& tnext) __attribute__((always_inline)) {
+    set_progress_priority(chunk - cb, ce - cb);
     const int64_t c0 = (int64_t)chunk * kChunk;
     const int64_t gam0 = c0 / kGroup;
     store_chunk(tcur);

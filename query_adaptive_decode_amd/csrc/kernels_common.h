@@ -128,6 +128,14 @@ __device__ __forceinline__ T group_sum(T v) {
   return v;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its outstanding global loads or stores (a full
+// __syncthreads() would also drain loads in flight and stores not yet
+// acknowledged).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // orders this wave's LDS accesses before and after it (no block barrier)
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");

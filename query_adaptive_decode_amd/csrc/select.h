@@ -88,7 +88,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum /
   const int w = tid >> 6;
   const uint32_t incl = wave_incl_scan_u32(v);
   if ((tid & 63) == 63) wsum[w] = incl;
-  __syncthreads();
+  lds_barrier();
   if (tid == 0) {
     uint32_t acc = 0;
     for (int i = 0; i < NT / 64; ++i) {
@@ -98,9 +98,9 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum /
     }
     wsum[NT / 64] = acc;
   }
-  __syncthreads();
+  lds_barrier();
   const uint32_t r = wsum[w] + incl - v;
-  __syncthreads();
+  lds_barrier();
   return r;
 }
 
@@ -122,15 +122,20 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* wsum) {
 // mantissa, so a regular item holds min(W, max(0, floor((E - L) / 2))) gains
 // at field L or above.  Other positive weights ("odd": some gains are
 // subnormal) have their gains formed one by one.  An LDS histogram of the
-// regular items' fields (hA) and of the odd gains' fields (hB) gives the
-// count at every field; one wave finds the field L* of the Bud-th largest
-// gain; within L* the gains are ranked by mantissa with 11/11/10/10/10-bit
-// radix passes that stop once the gains sharing the chosen digits are
-// exactly the ones still to be taken; the remaining equal gains are ranked
-// by item index.
+// regular items' fields (hA) and of the odd gains' fields (hB), with the
+// count of positive gains and the top field, gives the count at every field;
+// one wave scans down from the top field for the field L* of the Bud-th
+// largest gain; within L* the gains are ranked by mantissa with
+// 11/11/10/10/10-bit radix passes that stop once the gains sharing the
+// chosen digits are exactly the ones still to be taken, or, once at most
+// kChooseList of them are left, by one wave that collects them and settles
+// the remaining bits with ballots; the remaining equal gains are ranked by
+// item index.  Barriers here order LDS only (global stores are not waited
+// for).
 // ---------------------------------------------------------------------------
 constexpr int kNoField = -8192;
 constexpr uint64_t kMant = 0x000FFFFFFFFFFFFFull;
+constexpr int kChooseList = 64;
 
 __device__ __forceinline__ int regular_field(double a, int twoW) {
   const int E = (int)(dbits(a) >> 52);
@@ -140,58 +145,6 @@ __device__ __forceinline__ uint64_t gain_bits(double a, int t) {
   return dbits(__dmul_rn(a, bitsd((uint64_t)(1023 - 2 * t) << 52)));
 }
 
-// One wave: the gain-field histogram G[f] = hB[f] + sum_{t=1..W} hA[f + 2t]
-// (W <= 8) is formed in registers and scanned from the top field down for
-// the field where the count reaches rem (>= 1).  out[0] = field, out[1] =
-// count above it, out[2] = G[field] (all three only if the total reaches
-// rem), out[3] = total count.
-__device__ __forceinline__ void wave_find_gain_field(const uint32_t* hA, const uint32_t* hB, int W,
-                                                     uint32_t rem, uint32_t* out) {
-  constexpr int PER = 32;
-  const int l = __lane_id();
-  const int base = 2048 - (l + 1) * PER;  // lane l: fields base .. base + 31
-  uint32_t w[PER + 16];                   // hA[base .. base + 47], 0 past the end
-#pragma unroll
-  for (int i = 0; i < (PER + 16) / 4; ++i) {
-    const int idx = base + 4 * i;
-    uint4 v = *reinterpret_cast<const uint4*>(hA + min(idx, 2044));
-    if (idx >= 2048) v = make_uint4(0u, 0u, 0u, 0u);
-    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-  }
-  uint32_t G[PER];
-#pragma unroll
-  for (int i = 0; i < PER / 4; ++i) {
-    const uint4 v = *reinterpret_cast<const uint4*>(hB + base + 4 * i);
-    G[4 * i] = v.x; G[4 * i + 1] = v.y; G[4 * i + 2] = v.z; G[4 * i + 3] = v.w;
-  }
-#pragma unroll
-  for (int t = 1; t <= 8; ++t) {
-    if (t > W) break;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) G[i] += w[i + 2 * t];
-  }
-  uint32_t tot = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) tot += G[i];
-  const uint32_t incl = wave_incl_scan_u32(tot);
-  if (l == 63) out[3] = incl;
-  const uint64_t bal = __ballot(incl >= rem);
-  const int L = bal ? __ffsll((unsigned long long)bal) - 1 : -1;
-  if (l == L) {
-    uint32_t c = incl - tot;
-#pragma unroll
-    for (int i = PER - 1; i >= 0; --i) {
-      if (c + G[i] >= rem) {
-        out[0] = (uint32_t)(base + i);
-        out[1] = c;
-        out[2] = G[i];
-        break;
-      }
-      c += G[i];
-    }
-  }
-}
-
 template <int NT>
 struct ChooseShared {
   uint32_t hA[2048];  // regular items by field; radix digits of later passes
@@ -199,27 +152,153 @@ struct ChooseShared {
   uint32_t hC[2048];  // radix digits of the first pass
   uint32_t wsum[NT / 64 + 1];
   uint32_t sh[4];
+  uint32_t npos;      // positive gains
+  int etop;           // largest gain field + 2 (-1: no positive gain)
+  uint32_t any_odd;   // some positive weight is not regular
+  uint32_t nlist;     // candidates collected for the last bits
+  uint64_t rprefix, rmask;  // the threshold's mantissa digits, once settled by one wave
+  uint64_t list[kChooseList];
 };
+
+// All threads: zero the histograms and counts (a barrier must follow).
+template <int NT>
+__device__ __forceinline__ void choose_clear(ChooseShared<NT>& S) {
+  for (int i = threadIdx.x; i < 2048; i += NT) {
+    S.hA[i] = 0u;
+    S.hB[i] = 0u;
+    S.hC[i] = 0u;
+  }
+  if (threadIdx.x == 0) {
+    S.npos = 0u;
+    S.etop = -1;
+    S.any_odd = 0u;
+    S.nlist = 0u;
+  }
+}
+
+// One item's weight into the histograms; the thread's count of positive
+// gains and top field are kept in L until choose_flush.
+struct ChooseLocal {
+  uint32_t npos = 0u;
+  int etop = -1;
+  bool odd = false;
+};
+template <int NT>
+__device__ __forceinline__ void choose_add(double a, int W, ChooseShared<NT>& S, ChooseLocal& L) {
+  const int ef = regular_field(a, 2 * W);
+  if (ef != kNoField) {
+    atomicAdd(&S.hA[ef], 1u);
+    L.npos += (uint32_t)W;
+    L.etop = max(L.etop, ef);
+  } else if (a > 0.0) {
+    L.odd = true;
+    for (int t = 1; t <= W; ++t) {
+      const uint64_t kk = gain_bits(a, t);
+      if (kk) {
+        const int f = (int)(kk >> 52);
+        atomicAdd(&S.hB[f], 1u);
+        ++L.npos;
+        L.etop = max(L.etop, f + 2);
+      }
+    }
+  }
+}
+// All threads (every lane active): publish the counts of choose_add.
+template <int NT>
+__device__ __forceinline__ void choose_flush(const ChooseLocal& L, ChooseShared<NT>& S) {
+  const int n = wave_sum_i32((int)L.npos);
+  const int e = wave_max_i32(L.etop);
+  const bool odd = __ballot(L.odd) != 0ull;
+  if ((threadIdx.x & 63) == 0) {
+    atomicAdd(&S.npos, (uint32_t)n);
+    atomicMax(&S.etop, e);
+    if (odd) S.any_odd = 1u;
+  }
+}
+
+// One wave: the field of the rem-th largest gain (1 <= rem <= number of
+// positive gains), scanning down from field `top` 64 fields at a time: lane l
+// forms G[f] = hB[f] + sum_{t=1..W} hA[f + 2t] of field f = f0 - l.  out[0]
+// = field, out[1] = count above it, out[2] = G[field].
+__device__ __forceinline__ void wave_find_gain_field(const uint32_t* hA, const uint32_t* hB, int W,
+                                                     int top, uint32_t rem, uint32_t* out) {
+  const int l = __lane_id();
+  uint32_t above = 0;
+  for (int f0 = top; f0 >= 0; f0 -= 64) {
+    const int f = f0 - l;
+    uint32_t g = 0;
+    if (f >= 0) {
+      g = hB[f];
+      for (int t = 1; t <= W; ++t) {
+        const int fa = f + 2 * t;
+        if (fa < 2048) g += hA[fa];
+      }
+    }
+    const uint32_t incl = wave_incl_scan_u32(g);  // lanes in descending field order
+    const uint64_t bal = __ballot(above + incl >= rem);
+    if (bal) {
+      const int L = __ffsll((unsigned long long)bal) - 1;
+      if (l == L) {
+        out[0] = (uint32_t)f;
+        out[1] = above + incl - g;
+        out[2] = g;
+      }
+      return;
+    }
+    above += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+  }
+}
+
+// One wave: n <= 64 candidate mantissas (list) that agree with prefix under
+// mask, of which the rem largest are to be taken (1 <= rem <= n).  Settles
+// the bits below the mask MSB first with ballots, until the candidates that
+// share the settled bits are exactly the ones still to be taken, or every
+// bit is settled (then the equal ones are ties).  Writes the new prefix and
+// mask, and out[0] = number still to take among the equal ones, out[1] = how
+// many are equal.
+__device__ __forceinline__ void wave_settle_bits(const uint64_t* list, uint32_t n, uint32_t rem,
+                                                 uint64_t prefix, uint64_t mask, uint64_t* pm,
+                                                 uint32_t* out) {
+  const int l = __lane_id();
+  const uint64_t m = l < (int)n ? list[l] : 0ull;
+  uint64_t live = __ballot(l < (int)n);
+  uint32_t r = rem;
+  const int low = mask ? __builtin_ctzll(mask) : 52;  // lowest settled bit
+  for (int b = low - 1; b >= 0; --b) {
+    if ((uint32_t)__popcll(live) == r) break;
+    const uint64_t ones = live & __ballot((m >> b) & 1ull);
+    const uint32_t c1 = (uint32_t)__popcll(ones);
+    if (c1 >= r) {
+      live = ones;
+      prefix |= 1ull << b;
+    } else {
+      r -= c1;
+      live &= ~ones;
+    }
+    mask |= 1ull << b;
+  }
+  if (l == 0) {
+    pm[0] = prefix;
+    pm[1] = mask;
+    out[0] = r;
+    out[1] = (uint32_t)__popcll(live);
+  }
+}
 
 // Items are visited in rounds, item i = round * NT + threadIdx.x (so the tie
 // scan in index order is a block scan per round); each pass fetches BATCH
 // rounds of weights together (from LDS or device memory, as geta reads).
 // geta(i) returns a_i (i < N); put(i, t) stores item i's depth.  Returns the
 // sum of this thread's depths.  Every thread of the block must call it
-// (block barriers inside).
+// (block barriers inside).  The histograms must have been built (choose_clear,
+// choose_add of every item's geta value, choose_flush, a barrier).
 template <int NT, int BATCH, class GetA, class PutT>
-__device__ uint32_t block_choose_depths(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
-                                        ChooseShared<NT>& S) {
+__device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
+                                             ChooseShared<NT>& S) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x;
   const int twoW = 2 * W;
   const int64_t nr = (N + NT - 1) / NT;
-  for (int i = tid; i < 2048; i += NT) {
-    S.hA[i] = 0u;
-    S.hB[i] = 0u;
-    S.hC[i] = 0u;
-  }
-  __syncthreads();
   // fn(i, a, field, in_range) for every round (all threads, uniform count)
   auto for_items = [&](auto&& fn) __attribute__((always_inline)) {
     for (int64_t k0 = 0; k0 < nr; k0 += BATCH) {
@@ -238,71 +317,76 @@ __device__ uint32_t block_choose_depths(int64_t N, uint32_t Bud, int W, GetA&& g
     }
   };
 
-  // ---- field histograms ----
-  bool any_odd = false;
-  for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
-    if (ef != kNoField) {
-      atomicAdd(&S.hA[ef], 1u);
-    } else if (a > 0.0) {
-      any_odd = true;
-      for (int t = 1; t <= W; ++t) {
-        const uint64_t kk = gain_bits(a, t);
-        if (kk) atomicAdd(&S.hB[(uint32_t)(kk >> 52)], 1u);
-      }
-    }
-  });
-  __syncthreads();
-  if (tid < 64) wave_find_gain_field(S.hA, S.hB, W, Bud > 0u ? Bud : 1u, S.sh);
-  __syncthreads();
-  const uint32_t npos = S.sh[3];
+  const uint32_t npos = S.npos;
+  const bool any_odd = S.any_odd != 0u;
   const bool all_pos = npos <= Bud;
   int Es = -1;
   uint64_t prefix = 0, mask = 0;  // over the 52 mantissa bits
   uint32_t rem = 0, n_eq = 0;
   if (!all_pos && Bud > 0) {
+    if (tid < 64) wave_find_gain_field(S.hA, S.hB, W, S.etop - 2, Bud, S.sh);
+    lds_barrier();
     Es = (int)S.sh[0];
     rem = Bud - S.sh[1];  // >= 1
     n_eq = S.sh[2];       // >= rem
+    const uint32_t dspan = (uint32_t)(twoW - 2);
+    // fn(mantissa) for every gain at field Es (a regular item's candidate:
+    // d = E - Es even in [2, 2W])
+    auto for_gains_at_Es = [&](double a, int ef, auto&& fn) __attribute__((always_inline)) {
+      if (ef != kNoField) {
+        const uint32_t d2 = (uint32_t)(ef - Es - 2);
+        if (d2 <= dspan && !(d2 & 1u)) fn(dbits(a) & kMant);
+      } else if (any_odd && a > 0.0) {
+        for (int t = 1; t <= W; ++t) {
+          const uint64_t kk = gain_bits(a, t);
+          if (kk && (int)(kk >> 52) == Es) fn(kk & kMant);
+        }
+      }
+    };
     // digits of the 52 mantissa bits: 11, 11, 10, 10, 10 (MSB first)
     for (int pass = 0; pass < 5 && n_eq != rem; ++pass) {
+      if (n_eq <= (uint32_t)kChooseList) {
+        // collect the n_eq gains that share the digits so far; one wave
+        // settles the remaining bits
+        for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
+          for_gains_at_Es(a, ef, [&](uint64_t mnt) __attribute__((always_inline)) {
+            if ((mnt & mask) == prefix) S.list[atomicAdd(&S.nlist, 1u)] = mnt;
+          });
+        });
+        lds_barrier();
+        if (tid < 64) wave_settle_bits(S.list, n_eq, rem, prefix, mask, &S.rprefix, S.sh);
+        lds_barrier();
+        prefix = S.rprefix;
+        mask = S.rmask;
+        rem = S.sh[0];
+        n_eq = S.sh[1];
+        break;
+      }
       const int width = pass < 2 ? 11 : 10;
       const int shift = pass < 2 ? 41 - 11 * pass : 40 - 10 * pass;
       const uint32_t dmask = (1u << width) - 1u;
       uint32_t* const hist = pass == 0 ? S.hC : S.hA;
       if (pass > 0) {
         for (int i = tid; i < 2048; i += NT) S.hA[i] = 0u;
-        __syncthreads();
+        lds_barrier();
       }
-      // a regular item's candidate: d = E - Es even in [2, 2W]
-      const uint32_t dspan = (uint32_t)(twoW - 2);
       for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
-        if (ef != kNoField) {
-          const uint32_t d2 = (uint32_t)(ef - Es - 2);
-          const uint64_t mnt = dbits(a) & kMant;
-          if (d2 <= dspan && !(d2 & 1u) && (mnt & mask) == prefix)
-            atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
-        } else if (any_odd && a > 0.0) {
-          for (int t = 1; t <= W; ++t) {
-            const uint64_t kk = gain_bits(a, t);
-            if (kk && (int)(kk >> 52) == Es) {
-              const uint64_t mnt = kk & kMant;
-              if ((mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
-            }
-          }
-        }
+        for_gains_at_Es(a, ef, [&](uint64_t mnt) __attribute__((always_inline)) {
+          if ((mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
+        });
       });
-      __syncthreads();
+      lds_barrier();
       if (tid < 64) {
         if (width == 11) wave_find_digit<2048>(hist, rem, &S.sh[0], &S.sh[1]);
         else wave_find_digit<1024>(hist, rem, &S.sh[0], &S.sh[1]);
       }
-      __syncthreads();
+      lds_barrier();
       const uint32_t dg = S.sh[0];
       n_eq = hist[dg];
       rem -= S.sh[1];
       prefix |= (uint64_t)dg << shift;
       mask |= (uint64_t)dmask << shift;
-      __syncthreads();
+      lds_barrier();
     }
   }
 
@@ -361,6 +445,30 @@ __device__ uint32_t block_choose_depths(int64_t N, uint32_t Bud, int W, GetA&& g
     }
   });
   return mine;
+}
+
+// ChooseDepths with the histograms built here from geta.
+template <int NT, int BATCH, class GetA, class PutT>
+__device__ uint32_t block_choose_depths(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
+                                        ChooseShared<NT>& S) {
+  const int tid = threadIdx.x;
+  choose_clear<NT>(S);
+  lds_barrier();
+  ChooseLocal L;
+  const int64_t nr = (N + NT - 1) / NT;
+  for (int64_t k0 = 0; k0 < nr; k0 += BATCH) {
+    double a[BATCH];
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) {
+      const int64_t i = (k0 + q) * NT + tid;
+      a[q] = (k0 + q < nr && i < N) ? geta(i) : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < BATCH; ++q) choose_add<NT>(a[q], W, S, L);
+  }
+  choose_flush<NT>(L, S);
+  lds_barrier();
+  return block_choose_depths_hist<NT, BATCH>(N, Bud, W, geta, put, S);
 }
 
 }  // namespace readkv
