@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0
   uint32_t Bk = (uint32_t)floor((double)RK * (double)N);
   if (min1) Bk = Bk > (uint32_t)N ? Bk - (uint32_t)N : 0u;
   uint8_t* const tkd = tk + (int64_t)u0 * kDim;
-  block_choose_depths<NT, 4>(
+  block_choose_depths<NT>(
       N, Bk, W - min1, [&](int64_t i) { return wl[i]; },
       [&](int64_t i, uint32_t t) { tkd[i] = (uint8_t)(t + (uint32_t)min1); }, S);
 }
@@ -228,14 +228,14 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
       }
     }
     __syncthreads();
-    block_choose_depths<NT, 4>(
+    block_choose_depths<NT>(
         N, Bv, W - min1,
         [&](int64_t i) {
           return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc;
         },
         put, S);
   } else {
-    block_choose_depths<NT, 8>(
+    block_choose_depths<NT>(
         N, Bv, W - min1,
         [&](int64_t i) {
           return (pairs ? __dadd_rn(ab[at(2 * i)], ab[at(2 * i + 1)]) : ab[at(i)]) * sc;
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
   if (min1) Bv = (int64_t)Bv > N ? Bv - (uint32_t)N : 0u;
   uint8_t* const tvb = tv + ((int64_t)b * G + g) * capmax;
   uint32_t mine = 0;  // this thread's token depths
-  block_choose_depths_hist<NT, 4>(
+  block_choose_depths_hist<NT>(
       N, Bv, Wc,
       [&](int64_t i) { return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc; },
       [&](int64_t i, uint32_t t) {

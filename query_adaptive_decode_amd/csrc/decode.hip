@@ -244,9 +244,9 @@ __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, ui
 //     (4 heads) x (4 digits) and lane l of the result holds all its digits of
 //     head l/16 for token l%16: the digit sums are combined in-lane.
 //  4. Digit sums -> logits (fp64) in registers; open-group tokens use exact
-//     keys; per head the tile max m, e = exp(s - m) (fp64; stored rounded
-//     to fp32 for the value allocation and to fp16 for the value gather)
-//     and sum e (split-context softmax).
+//     keys; per head the tile max m, e = exp(s - m) (fp64; stored as bits
+//     61..30 of its fp64 pattern, read by the value allocation and the value
+//     gather) and sum e (split-context softmax).
 // Grid (unit, ny): consecutive blocks are different units, so all blocks of
 // a unit are on one XCD and share its L2; as they take neighbouring tiles at
 // the same time, the two halves of a key-plane tile are read from HBM once.
@@ -381,6 +381,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   __shared__ uint8_t s2c[kDim * 8];
   __shared__ uint32_t wtot[2];
   __shared__ uint32_t dcnt[2][9];  // channels per depth value, per wave
+  __shared__ uint32_t qflag[2];    // a non-finite query value, per wave
 
   // the call's read counters start from zero (the value selection, a later
   // launch, adds to them)
@@ -420,7 +421,6 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     for (int k = 0; k < MPT; ++k)
       pmeta[k] = __builtin_amdgcn_raw_buffer_load_b32(rs_meta, (tile * NG * kDim + k * 256 + tid) * 4, 0, 0);
   };
-  load_meta(tile_begin);  // independent of the depths: in flight during the setup
 
   // ---- once per block: depths, query, per-head digit scale, slot table ----
   // Key allocation of the unit: under per-layer budgets it comes from the
@@ -430,15 +430,22 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // A query with a non-finite value reads nothing: its unit's key weights are
   // zero (depths 0) and its softmax statistics NaN, so that no value is
   // refined and every output of the unit is NaN.
+  // (the query and E^K loads go out before the first tile's metadata, so
+  // that waiting for them does not wait for the metadata)
   double ek = 0.0;
   bool qnf = false;
+  double qv[GQA];
+  uint8_t tkr = 0;
   if (tid < kDim) {
-    const int c = tid;
-    double qv[GQA];
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh)
-      qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + c);
-    ek = u.ek[c];
+      qv[hh] = load_elem<DT>(q, ((int64_t)b * H + (int64_t)g * GQA + hh) * kDim + tid);
+    ek = u.ek[tid];
+    if (tk_ready) tkr = tk[((int64_t)b * G + g) * kDim + tid];
+  }
+  load_meta(tile_begin);  // independent of the depths: in flight during the setup
+  if (tid < kDim) {
+    const int c = tid;
     double qsq = 0.0;
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
@@ -446,10 +453,15 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
       qnf |= !isfinite(qv[hh]);
       qsq = __dadd_rn(qsq, __dmul_rn(qv[hh], qv[hh]));
     }
-    if (tk_ready) tks[c] = tk[((int64_t)b * G + g) * kDim + c];
+    if (tk_ready) tks[c] = tkr;
     else kap[c] = __dmul_rn(qsq, ek);  // the key weight, until kap is set below
+    const bool any = __ballot(qnf) != 0ull;  // (waves 0 and 1: every channel)
+    if (lane == 0) qflag[wv] = any ? 1u : 0u;
   }
-  const bool qbad = __syncthreads_or(qnf);
+  // barriers in the set-up order LDS only: the loads of the first tile in
+  // flight (and the depths written out) are not waited for
+  lds_barrier();
+  const bool qbad = (qflag[0] | qflag[1]) != 0u;
   if (!tk_ready) {
     if (wv == 0) {
       // the minimum depth one: levels 2..W of w are levels 1..W-1 of w/4
@@ -469,7 +481,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
         tk[((int64_t)b * G + g) * kDim + lane + 64] = (uint8_t)sel[1];
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   uint32_t tv_ = 0, inc = 0, below = 0;
   if (tid < kDim) {
@@ -497,7 +509,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     }
     below = (uint32_t)__popcll(mine & ((1ull << lane) - 1ull));
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < kDim) {
     if (wv == 1) inc += wtot[0];
     offs[tid + 1] = (uint16_t)inc;
@@ -513,7 +525,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
     cperm[rank] = (uint8_t)tid;
     kap[tid] = ldexp_pow2(-(int)tv_ - 1) + (tv_ > 0u ? 0.5 : 0.0);
   }
-  __syncthreads();
+  lds_barrier();
   const int ns = offs[kDim];
   const int nq = ns * 2;  // 16 B pieces per tile
   // Staging.  A score tile is half (h = tile & 1) of a 16-group key-plane
@@ -632,7 +644,7 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   }
 
   store_ahead(tile_begin);
-  __syncthreads();
+  lds_barrier();
   // the register prefetch runs one tile ahead; it is issued right after the
   // previous staging write, before the epilogue's global stores, so that no
   // wait on those stores delays it
@@ -1172,7 +1184,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) red2[m * kDim + 16 * (2 * wv + bl) + 4 * kb + rr] = Oacc[bl][rr];
-  __syncthreads();
+  lds_barrier();
   const int64_t cl0 = (int64_t)(ce - 1) * kChunk;  // the last chunk (es, fs still in LDS)
   const int64_t jt0 = Tp > cl0 ? Tp : cl0;
   const int64_t jt1 = len < cl0 + kChunk ? len : cl0 + kChunk;

@@ -127,15 +127,18 @@ __device__ __forceinline__ uint32_t block_sum_u32(uint32_t v, uint32_t* wsum) {
 // one wave scans down from the top field for the field L* of the Bud-th
 // largest gain; within L* the gains are ranked by mantissa with
 // 11/11/10/10/10-bit radix passes that stop once the gains sharing the
-// chosen digits are exactly the ones still to be taken, or, once at most
-// kChooseList of them are left, by one wave that collects them and settles
-// the remaining bits with ballots; the remaining equal gains are ranked by
-// item index.  Barriers here order LDS only (global stores are not waited
-// for).
+// chosen digits are exactly the ones still to be taken; once at most
+// kChooseBig gains share the digits their mantissas are copied to a list in
+// LDS (over the field histograms, no longer needed), so that later passes
+// read the list instead of every item, and once at most kChooseList are left
+// one wave settles the remaining bits with ballots.  The remaining equal
+// gains are ranked by item index.  A thread takes 4 consecutive items per
+// round.  Barriers here order LDS only (global stores are not waited for).
 // ---------------------------------------------------------------------------
 constexpr int kNoField = -8192;
 constexpr uint64_t kMant = 0x000FFFFFFFFFFFFFull;
 constexpr int kChooseList = 64;
+constexpr int kChooseBig = 2048;  // mantissas, 16 KB: hA and hB
 
 __device__ __forceinline__ int regular_field(double a, int twoW) {
   const int E = (int)(dbits(a) >> 52);
@@ -147,15 +150,21 @@ __device__ __forceinline__ uint64_t gain_bits(double a, int t) {
 
 template <int NT>
 struct ChooseShared {
-  uint32_t hA[2048];  // regular items by field; radix digits of later passes
-  uint32_t hB[2048];  // odd gains by field
-  uint32_t hC[2048];  // radix digits of the first pass
+  union {
+    struct {
+      uint32_t hA[2048];  // regular items by field
+      uint32_t hB[2048];  // odd gains by field
+    };
+    uint64_t big[kChooseBig];  // candidate mantissas, once the field is found
+  };
+  uint32_t hC[2048];  // radix digits
   uint32_t wsum[NT / 64 + 1];
   uint32_t sh[4];
   uint32_t npos;      // positive gains
   int etop;           // largest gain field + 2 (-1: no positive gain)
   uint32_t any_odd;   // some positive weight is not regular
   uint32_t nlist;     // candidates collected for the last bits
+  uint32_t nbig;      // candidates in big
   uint64_t rprefix, rmask;  // the threshold's mantissa digits, once settled by one wave
   uint64_t list[kChooseList];
 };
@@ -173,6 +182,7 @@ __device__ __forceinline__ void choose_clear(ChooseShared<NT>& S) {
     S.etop = -1;
     S.any_odd = 0u;
     S.nlist = 0u;
+    S.nbig = 0u;
   }
 }
 
@@ -285,35 +295,31 @@ __device__ __forceinline__ void wave_settle_bits(const uint64_t* list, uint32_t 
   }
 }
 
-// Items are visited in rounds, item i = round * NT + threadIdx.x (so the tie
-// scan in index order is a block scan per round); each pass fetches BATCH
-// rounds of weights together (from LDS or device memory, as geta reads).
+// Items are visited in rounds of 4 NT: thread t takes items 4t .. 4t + 3 of
+// a round (so the tie ranking in index order is a block scan per round).
 // geta(i) returns a_i (i < N); put(i, t) stores item i's depth.  Returns the
 // sum of this thread's depths.  Every thread of the block must call it
 // (block barriers inside).  The histograms must have been built (choose_clear,
 // choose_add of every item's geta value, choose_flush, a barrier).
-template <int NT, int BATCH, class GetA, class PutT>
+template <int NT, class GetA, class PutT>
 __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
                                              ChooseShared<NT>& S) {
   constexpr int NW = NT / 64;
+  constexpr int IPT = 4;
+  constexpr int64_t RT = (int64_t)NT * IPT;
   const int tid = threadIdx.x;
   const int twoW = 2 * W;
-  const int64_t nr = (N + NT - 1) / NT;
-  // fn(i, a, field, in_range) for every round (all threads, uniform count)
+  const int64_t nr = (N + RT - 1) / RT;
+  // fn(i, a, field, in_range) for every item of the thread (all threads,
+  // uniform count)
   auto for_items = [&](auto&& fn) __attribute__((always_inline)) {
-    for (int64_t k0 = 0; k0 < nr; k0 += BATCH) {
-      double a[BATCH];
+    for (int64_t k = 0; k < nr; ++k) {
+      const int64_t i0 = k * RT + (int64_t)IPT * tid;
+      double a[IPT];
 #pragma unroll
-      for (int q = 0; q < BATCH; ++q) {
-        const int64_t i = (k0 + q) * NT + tid;
-        a[q] = (k0 + q < nr && i < N) ? geta(i) : 0.0;
-      }
+      for (int q = 0; q < IPT; ++q) a[q] = i0 + q < N ? geta(i0 + q) : 0.0;
 #pragma unroll
-      for (int q = 0; q < BATCH; ++q) {
-        if (k0 + q >= nr) break;  // uniform
-        const int64_t i = (k0 + q) * NT + tid;
-        fn(i, a[q], regular_field(a[q], twoW), i < N);
-      }
+      for (int q = 0; q < IPT; ++q) fn(i0 + q, a[q], regular_field(a[q], twoW), i0 + q < N);
     }
   };
 
@@ -325,7 +331,7 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
   uint32_t rem = 0, n_eq = 0;
   if (!all_pos && Bud > 0) {
     if (tid < 64) wave_find_gain_field(S.hA, S.hB, W, S.etop - 2, Bud, S.sh);
-    lds_barrier();
+    lds_barrier();  // (hA and hB are free from here on)
     Es = (int)S.sh[0];
     rem = Bud - S.sh[1];  // >= 1
     n_eq = S.sh[2];       // >= rem
@@ -343,16 +349,28 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
         }
       }
     };
+    // fn(mantissa) for every gain that shares the digits so far: from the
+    // list once it exists, else from the items
+    int nbig = -1;
+    auto for_candidates = [&](auto&& fn) __attribute__((always_inline)) {
+      if (nbig >= 0) {
+        for (int i = tid; i < nbig; i += NT) {
+          const uint64_t mnt = S.big[i];
+          if ((mnt & mask) == prefix) fn(mnt);
+        }
+      } else {
+        for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
+          for_gains_at_Es(a, ef, [&](uint64_t mnt) __attribute__((always_inline)) {
+            if ((mnt & mask) == prefix) fn(mnt);
+          });
+        });
+      }
+    };
     // digits of the 52 mantissa bits: 11, 11, 10, 10, 10 (MSB first)
     for (int pass = 0; pass < 5 && n_eq != rem; ++pass) {
       if (n_eq <= (uint32_t)kChooseList) {
-        // collect the n_eq gains that share the digits so far; one wave
-        // settles the remaining bits
-        for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
-          for_gains_at_Es(a, ef, [&](uint64_t mnt) __attribute__((always_inline)) {
-            if ((mnt & mask) == prefix) S.list[atomicAdd(&S.nlist, 1u)] = mnt;
-          });
-        });
+        // the last candidates: one wave settles the remaining bits
+        for_candidates([&](uint64_t mnt) __attribute__((always_inline)) { S.list[atomicAdd(&S.nlist, 1u)] = mnt; });
         lds_barrier();
         if (tid < 64) wave_settle_bits(S.list, n_eq, rem, prefix, mask, &S.rprefix, S.sh);
         lds_barrier();
@@ -362,27 +380,29 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
         n_eq = S.sh[1];
         break;
       }
+      if (nbig < 0 && n_eq <= (uint32_t)kChooseBig) {
+        for_candidates([&](uint64_t mnt) __attribute__((always_inline)) { S.big[atomicAdd(&S.nbig, 1u)] = mnt; });
+        lds_barrier();
+        nbig = (int)n_eq;
+      }
       const int width = pass < 2 ? 11 : 10;
       const int shift = pass < 2 ? 41 - 11 * pass : 40 - 10 * pass;
       const uint32_t dmask = (1u << width) - 1u;
-      uint32_t* const hist = pass == 0 ? S.hC : S.hA;
       if (pass > 0) {
-        for (int i = tid; i < 2048; i += NT) S.hA[i] = 0u;
+        for (int i = tid; i < 2048; i += NT) S.hC[i] = 0u;
         lds_barrier();
       }
-      for_items([&](int64_t, double a, int ef, bool) __attribute__((always_inline)) {
-        for_gains_at_Es(a, ef, [&](uint64_t mnt) __attribute__((always_inline)) {
-          if ((mnt & mask) == prefix) atomicAdd(&hist[(uint32_t)(mnt >> shift) & dmask], 1u);
-        });
+      for_candidates([&](uint64_t mnt) __attribute__((always_inline)) {
+        atomicAdd(&S.hC[(uint32_t)(mnt >> shift) & dmask], 1u);
       });
       lds_barrier();
       if (tid < 64) {
-        if (width == 11) wave_find_digit<2048>(hist, rem, &S.sh[0], &S.sh[1]);
-        else wave_find_digit<1024>(hist, rem, &S.sh[0], &S.sh[1]);
+        if (width == 11) wave_find_digit<2048>(S.hC, rem, &S.sh[0], &S.sh[1]);
+        else wave_find_digit<1024>(S.hC, rem, &S.sh[0], &S.sh[1]);
       }
       lds_barrier();
       const uint32_t dg = S.sh[0];
-      n_eq = hist[dg];
+      n_eq = S.hC[dg];
       rem -= S.sh[1];
       prefix |= (uint64_t)dg << shift;
       mask |= (uint64_t)dmask << shift;
@@ -425,50 +445,57 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
     }
     return above | (tie << 16);
   };
+  // Ties are ranked only when not all equal gains are taken, which needs
+  // all 52 bits settled: then an item has at most one gain equal to the
+  // threshold (its gains differ from each other).
   const bool rank_ties = !all_pos && Bud > 0 && rem < n_eq;
   uint32_t running = 0;  // ties in earlier rounds
   uint32_t mine = 0;
-  for_items([&](int64_t i, double a, int ef, bool in) __attribute__((always_inline)) {
-    const uint32_t lv = count_levels(a, ef);
-    uint32_t t = lv & 0xFFFFu;
-    const uint32_t tie = lv >> 16;
+  for (int64_t k = 0; k < nr; ++k) {
+    const int64_t i0 = k * RT + (int64_t)IPT * tid;
+    uint32_t t[IPT], tie[IPT];
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) {
+      const double a = i0 + q < N ? geta(i0 + q) : 0.0;
+      const uint32_t lv = count_levels(a, regular_field(a, twoW));
+      t[q] = lv & 0xFFFFu;
+      tie[q] = lv >> 16;
+    }
     if (rank_ties) {
-      const uint32_t before = block_excl_scan<NT>(tie, S.wsum) + running;
+      uint32_t before = block_excl_scan<NT>((tie[0] + tie[1]) + (tie[2] + tie[3]), S.wsum) + running;
       running += S.wsum[NW];
-      if (tie && before < rem) ++t;
+#pragma unroll
+      for (int q = 0; q < IPT; ++q) {
+        if (tie[q] && before < rem) ++t[q];
+        before += tie[q];
+      }
     } else {
-      t += tie;
+#pragma unroll
+      for (int q = 0; q < IPT; ++q) t[q] += tie[q];
     }
-    if (in) {
-      put(i, t);
-      mine += t;
+#pragma unroll
+    for (int q = 0; q < IPT; ++q) {
+      if (i0 + q < N) {
+        put(i0 + q, t[q]);
+        mine += t[q];
+      }
     }
-  });
+  }
   return mine;
 }
 
 // ChooseDepths with the histograms built here from geta.
-template <int NT, int BATCH, class GetA, class PutT>
+template <int NT, class GetA, class PutT>
 __device__ uint32_t block_choose_depths(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
                                         ChooseShared<NT>& S) {
   const int tid = threadIdx.x;
   choose_clear<NT>(S);
   lds_barrier();
   ChooseLocal L;
-  const int64_t nr = (N + NT - 1) / NT;
-  for (int64_t k0 = 0; k0 < nr; k0 += BATCH) {
-    double a[BATCH];
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) {
-      const int64_t i = (k0 + q) * NT + tid;
-      a[q] = (k0 + q < nr && i < N) ? geta(i) : 0.0;
-    }
-#pragma unroll
-    for (int q = 0; q < BATCH; ++q) choose_add<NT>(a[q], W, S, L);
-  }
+  for (int64_t i = tid; i < N; i += NT) choose_add<NT>(geta(i), W, S, L);
   choose_flush<NT>(L, S);
   lds_barrier();
-  return block_choose_depths_hist<NT, BATCH>(N, Bud, W, geta, put, S);
+  return block_choose_depths_hist<NT>(N, Bud, W, geta, put, S);
 }
 
 }  // namespace readkv
