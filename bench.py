@@ -9,8 +9,9 @@ output reduction), for read rates R = 4 and R = 2 (R_K = R_V = R).
 
 Prints one JSON line.  `value` is query-heads x context-tokens per second at
 (W, R) = (8, 4) with the step's inputs resident in HBM and the caches
-flushed before every step (a 512 MiB device write pushes the store out of
-L2 and the Infinity Cache); the warm figure (steps replayed back to back)
+flushed before every step (reading a 512 MiB buffer pushes the store out of
+L2 and the Infinity Cache and leaves only clean lines behind); the warm
+figure (steps replayed back to back)
 sits beside it.  Both are graph replays timed with HIP events.  Also
 reported: per-kernel HIP-event durations (warm and flushed), the roofline
 of the dominant kernel, bytes moved per step from the committed rocprofv3
@@ -105,8 +106,17 @@ class Stepper:
         torch.cuda.synchronize()
 
 
-def flush(scratch, i):
-    scratch.fill_(i & 0xFF)
+def flush_buffer(torch):
+    """A 512 MiB device buffer, written once (its lines are clean by the
+    time it is read again)."""
+    return torch.empty(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda").fill_(1)
+
+
+def flush(scratch):
+    """Evict the store from the L2s and the 256 MB Infinity Cache by reading
+    512 MiB.  A read leaves clean lines behind; a write would leave about
+    256 MB of dirty lines whose write-back to HBM lands in the timed step."""
+    scratch.sum()
 
 
 def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h):
@@ -119,13 +129,13 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h):
         st.step_eager()
     st.capture()
     stream = torch.cuda.current_stream().cuda_stream
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    scratch = flush_buffer(torch)
     e0, e1 = _events(h, 2)
 
     def timed_replay(evict):
         st.load()
         if evict:
-            flush(scratch, st.s)
+            flush(scratch)
         h.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream))
         st.graph.replay()
         h.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream))
@@ -154,7 +164,7 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h):
         for i in range(steps):
             st.load()
             if mode == "evicted":
-                flush(scratch, st.s)
+                flush(scratch)
             h.hipEventRecord(ctypes.c_void_p(eenc[i][0]), ctypes.c_void_p(stream))
             st.cache.append(st.kbuf, st.vbuf)
             h.hipEventRecord(ctypes.c_void_p(eenc[i][1]), ctypes.c_void_p(stream))
@@ -282,14 +292,14 @@ def counters_run(cfg, dev, lcfg, rates, warmup, steps, torch):
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    scratch = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    scratch = flush_buffer(torch)
     for R in rates:
         st = Stepper(cfg, dev, lcfg, R, torch)
         for _ in range(warmup + steps):
             st.step_eager()
         for _ in range(steps):
             st.load()
-            flush(scratch, st.s)
+            flush(scratch)
             st.cache.append(st.kbuf, st.vbuf)
             st.cache.decode(st.qbuf, st.R, st.R, out=st.out)
             st.s += 1

@@ -969,14 +969,16 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const uint8_t* tvu = tv + ((int64_t)b * G + g) * capmax;
   if (tid < 4) reinterpret_cast<uint32_t*>(ezero)[tid] = 0u;  // read after the first barrier
-  const int jl = tid & (kChunk - 1), rh = tid >> 7;  // row loads: token jl, planes rh, rh + 2, ...
+  // row loads: plane pl of tokens tq .. tq + 3, so that the 8 lanes of a
+  // token read its 128-byte row (all planes) together and one load
+  // instruction covers 8 whole rows
+  const int tq = 4 * (tid >> 3), pl = tid & 7;
 
   // ---- register prefetch of one chunk ----
-  uint32_t ptv = 0;                 // depth of token jl (for the row loads)
   uint32_t pes[GQA];  // encoded e of token tid (tid < kChunk) per head
   uint32_t pmeta[MPT];
   double pfs = 0.0;  // converted when stored: no wait right after its load
-  uint4 prow0, prow1, prow2, prow3;  // planes rh, rh + 2, rh + 4, rh + 6 of token jl
+  uint4 prow[4];     // plane pl of tokens tq .. tq + 3
   // Buffer loads whose range check supplies the zeros past the data (offset
   // kBufOff lies outside every buffer): no branches around the loads.
   const __amdgpu_buffer_rsrc_t rs_tv =
@@ -985,8 +987,10 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
       const_cast<uint32_t*>(u.vmeta), (short)0, (int)(Tp / kGroup) * kDim * 4, kBufWord3);
   const __amdgpu_buffer_rsrc_t rs_ft = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<double*>(ftile + hrow0 * ntile_ws), (short)0, GQA * ntile_ws * 8, kBufWord3);
+  // the depths of tokens tq .. tq + 3 (one byte each; Tp is a multiple of
+  // 32, so the four are all inside the buffer or all past it)
   auto tv_of = [&](int chunk) __attribute__((always_inline)) -> uint32_t {
-    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rs_tv, chunk * kChunk + jl, 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(rs_tv, chunk * kChunk + tq, 0, 0);
   };
   auto load_small = [&](int chunk) __attribute__((always_inline)) {
     const int c0 = chunk * kChunk;
@@ -1002,7 +1006,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
     pfs = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(
                                          rs_ft, tid < GQA ? (tid * ntile_ws + c0 / kTile) * 8 : kBufOff, 0, 0));
   };
-  auto load_rows = [&](int chunk, uint32_t t) __attribute__((always_inline)) {
+  auto load_rows = [&](int chunk, uint32_t t4) __attribute__((always_inline)) {
     // buffer loads over the chunk's plane rows: planes past the depth take
     // an offset beyond the buffer's size, which reads zeros without a
     // memory access, so a token costs only the lines its prefix touches
@@ -1010,19 +1014,16 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
     const uint8_t* cbase = reinterpret_cast<const uint8_t*>(u.vplanes) + (int64_t)chunk * kChunk * W * 16;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cbase), (short)0, kChunk * W * 16, kBufWord3);
-    const int tok = jl * W * 16;
-    const uint32_t p0 = (uint32_t)rh;
-    auto ld = [&](uint32_t p) __attribute__((always_inline)) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, p < t ? tok + (int)p * 16 : kBufOff, 0, 0);
-      return make_uint4(v[0], v[1], v[2], v[3]);
-    };
-    prow0 = ld(p0);
-    prow1 = ld(p0 + 2);
-    prow2 = ld(p0 + 4);
-    prow3 = ld(p0 + 6);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t t = (t4 >> (8 * r)) & 0xFFu;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(
+          rs, (uint32_t)pl < t ? ((tq + r) * W + pl) * 16 : kBufOff, 0, 0);
+      prow[r] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
   };
-  auto store_chunk = [&](uint32_t t) __attribute__((always_inline)) {
-    if (tid < kChunk) tvs[tid] = (uint8_t)t;
+  auto store_chunk = [&](uint32_t t4) __attribute__((always_inline)) {
+    if (pl == 0) *reinterpret_cast<uint32_t*>(&tvs[tq]) = t4;
     if (tid < kChunk) {
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) es[hh][tid] = to_half(dec_e(pes[hh]));
@@ -1033,16 +1034,15 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
       vmeta_s[i / kDim][i % kDim] = pmeta[k];
     }
     if (tid < GQA) fs[tid] = (float)pfs;
-    (void)t;  // rows past the depth hold zeros (also masked in the un-plane)
-    rows[rh * RS + jl] = prow0;
-    rows[(rh + 2) * RS + jl] = prow1;
-    rows[(rh + 4) * RS + jl] = prow2;
-    rows[(rh + 6) * RS + jl] = prow3;
+    // (rows past a token's depth hold zeros)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) rows[pl * RS + tq + r] = prow[r];
   };
 
-  // depths of token jl: tA of the chunk whose rows are in flight, tB of the
-  // next one (loaded a chunk ahead); the loop runs two chunks per turn with
-  // the roles swapped, so a depth load never has to land in another register
+  // depths of tokens tq .. tq + 3: tA of the chunk whose rows are in
+  // flight, tB of the next one (loaded a chunk ahead); the loop runs two
+  // chunks per turn with the roles swapped, so a depth load never has to
+  // land in another register
   uint32_t tA = tv_of(cb), tB = tv_of(cb + 1);  // past the run: unused
   load_small(cb);
   load_rows(cb, tA);
