@@ -431,6 +431,18 @@ def main():
                     "frac_of_peak": gbps / HBM_PEAK_GBPS, "frac_of_copy": gbps / copy_gbps,
                     "per_kernel_bytes": {k: v["read_bytes"] + v["write_bytes"]
                                          for k, v in m["kernels"].items()}}
+        m_pre, m_ev = moved_of(R, "prefill"), moved_of(R, "evicted")
+        if m_pre and m_ev and "append" in m_ev["kernels"]:
+            # encoder writes (the prompt's encoding, then one append per step)
+            # against the decode steps' reads, over the prompt plus L steps
+            L = 128
+            enc_w = m_pre["step_write_bytes"] + L * m_ev["kernels"]["append"]["write_bytes"]
+            dec_r = L * m_ev["step_read_bytes"]
+            ent["encode_traffic"] = {
+                "steps": L, "prompt_tokens": int(cfg["T0"]), "prefill_write_bytes": m_pre["step_write_bytes"],
+                "append_write_bytes_per_step": m_ev["kernels"]["append"]["write_bytes"],
+                "decode_read_bytes_per_step": m_ev["step_read_bytes"],
+                "encode_write_over_decode_read": enc_w / dec_r}
         line["rates"][rate_key(R)] = ent
     if moved is None:
         line["moved_bytes_note"] = ("no counter summary for these kernel sources "

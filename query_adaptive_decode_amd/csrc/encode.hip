@@ -32,10 +32,16 @@ __device__ __forceinline__ int64_t clamp_n(const ReqRecord& r, const int32_t* n_
 // tokens (row0 = the unit's first new-token row).  Returns rng^2 of the
 // thread's channel (0 for a non-finite group).  Contains block barriers:
 // every thread of the block must call it.
+// The group's value planes (32 rows of W x 16 contiguous bytes) are staged
+// in vst (LDS, 32 W 4 words) and written with one 16-byte store per thread.
+// Its key-plane words (one word of each (channel, plane) line of its
+// 512-token tile) go to kst (LDS, the tile's d W 16 words) when the caller
+// writes the whole tile out afterwards, else straight to the store.
 template <int DT>
 __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, const void* knew,
                                                const void* vnew, int64_t row0, int64_t len0,
-                                               int64_t gam, int W, int* bad_s, double* rv2) {
+                                               int64_t gam, int W, int* bad_s, double* rv2,
+                                               uint32_t* vst, uint32_t* kst) {
   const int tid = threadIdx.x;
   const bool isv = tid >= 128;
   const int c = tid & 127;
@@ -97,25 +103,27 @@ __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, co
       uint32_t word = 0;
 #pragma unroll
       for (int s = 0; s < kGroup; ++s) word |= ((code[s] >> (W - 1 - p)) & 1u) << s;
-      u.kplanes[(((gam >> 4) * kDim + c) * W + p) * 16 + (gam & 15)] = word;
+      if (kst) kst[(c * W + p) * 16 + (gam & 15)] = word;
+      else u.kplanes[(((gam >> 4) * kDim + c) * W + p) * 16 + (gam & 15)] = word;
     }
   } else {
     u.vmeta[gam * kDim + c] = meta;
     rv2[c] = r2;
     const int half = c >> 6;  // which 64-channel half this wave holds
     for (int s = 0; s < kGroup; ++s) {
-      const int64_t j = gam * kGroup + s;
       for (int p = 0; p < W; ++p) {
         const uint64_t m = __ballot((code[s] >> (W - 1 - p)) & 1u);
         if ((c & 63) == 0) {
-          uint32_t* dst = u.vplanes + ((j * W + p) * (kDim / 32)) + 2 * half;
-          dst[0] = (uint32_t)m;
-          dst[1] = (uint32_t)(m >> 32);
+          vst[(s * W + p) * 4 + 2 * half] = (uint32_t)m;
+          vst[(s * W + p) * 4 + 2 * half + 1] = (uint32_t)(m >> 32);
         }
       }
     }
   }
   __syncthreads();
+  if (tid < kGroup * W)  // the group's value rows: 16 bytes per thread
+    reinterpret_cast<uint4*>(u.vplanes + gam * kGroup * W * (kDim / 32))[tid] =
+        reinterpret_cast<const uint4*>(vst)[tid];
   if (tid == 128) {
     double e = 0.0;
     for (int cc = 0; cc < kDim; ++cc) e = e + rv2[cc];
@@ -124,24 +132,40 @@ __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, co
   return r2;
 }
 
-// grid (max groups closing, G, B), 256 threads: one closing group per block.
+// grid (tiles touched, G, B), 256 threads: block i encodes the closing
+// groups of the unit's i-th 512-token key tile touched by this append, in
+// group order.  When it encodes all 16 groups of the tile, the key planes
+// are staged in LDS and written as whole 64-byte lines (else word by word:
+// the tile's other groups are already stored).
 template <int DT>
-__global__ __launch_bounds__(256) void k_encode_groups(uint8_t* store, const void* knew,
-                                                       const void* vnew, const int32_t* n_new,
-                                                       int n_max, int G, int W) {
+__global__ __launch_bounds__(256) void k_encode_tiles(uint8_t* store, const void* knew,
+                                                      const void* vnew, const int32_t* n_new,
+                                                      int n_max, int G, int W) {
   constexpr int esize = DT == 0 ? 2 : 4;
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const ReqRecord r = req_of(store, b);
   const int64_t len0 = r.len;
   const int64_t n = clamp_n(r, n_new, b, n_max);
-  const int64_t first = len0 / kGroup;
-  const int64_t count = (len0 + n) / kGroup - first;
-  if (i >= count) return;
+  const int64_t first = len0 / kGroup, last = (len0 + n) / kGroup;
+  if (last == first) return;
+  const int64_t tile = (first >> 4) + i;
+  if (tile > ((last - 1) >> 4)) return;
+  const int64_t g0 = first > 16 * tile ? first : 16 * tile;
+  const int64_t g1 = last < 16 * tile + 16 ? last : 16 * tile + 16;
+  const bool whole = g0 == 16 * tile && g1 == 16 * tile + 16;
   __shared__ int bad_s[2];
   __shared__ double rv2[128];
+  __shared__ __attribute__((aligned(16))) uint32_t vst[kGroup * 8 * 4];
+  __shared__ __attribute__((aligned(16))) uint32_t kst[kDim * 8 * 16];
   const Unit u = unit_of(store, r, g, G, kDim, W, esize);
-  encode_group<DT>(store, u, knew, vnew, ((int64_t)b * G + g) * n_max, len0, first + i, W, bad_s,
-                   rv2);
+  for (int64_t gam = g0; gam < g1; ++gam)
+    encode_group<DT>(store, u, knew, vnew, ((int64_t)b * G + g) * n_max, len0, gam, W, bad_s, rv2,
+                     vst, whole ? kst : nullptr);
+  if (whole) {
+    __syncthreads();
+    uint4* dst = reinterpret_cast<uint4*>(u.kplanes + tile * kDim * W * 16);
+    for (int k = threadIdx.x; k < kDim * W * 4; k += 256) dst[k] = reinterpret_cast<const uint4*>(kst)[k];
+  }
 }
 
 // grid (G, B), 128 threads: E^K[c] += rng^2 of every newly closed group,
@@ -220,6 +244,7 @@ __global__ __launch_bounds__(256) void k_append_small(uint8_t* store, const void
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   __shared__ int bad_s[2];
   __shared__ double rv2[128];
+  __shared__ __attribute__((aligned(16))) uint32_t vst[kGroup * 8 * 4];
   __shared__ int last_s;
   ReqRecord* rp = reinterpret_cast<ReqRecord*>(store + 256 + 32 * (int64_t)b);
   const ReqRecord r = *rp;
@@ -232,7 +257,7 @@ __global__ __launch_bounds__(256) void k_append_small(uint8_t* store, const void
   const Unit u = unit_of(store, r, g, G, kDim, W, esize);
   const int64_t row0 = ((int64_t)b * G + g) * n_max;
   for (int64_t gam = first; gam < last; ++gam) {
-    const double r2 = encode_group<DT>(store, u, knew, vnew, row0, len0, gam, W, bad_s, rv2);
+    const double r2 = encode_group<DT>(store, u, knew, vnew, row0, len0, gam, W, bad_s, rv2, vst, nullptr);
     if (tid < kDim) u.ek[tid] = u.ek[tid] + r2;
     __syncthreads();  // the group's tail rows are read before they are replaced
   }
@@ -293,16 +318,18 @@ int launch_encode(const EncodeArgs& a, hipStream_t st) {
                          a.vnew, a.n_new, a.n_max, a.G, a.W);
     return hipGetLastError() == hipSuccess ? 0 : -6;
   }
-  const int max_groups = (int)((a.n_max + kGroup - 1) / kGroup);
+  // key tiles an append of n_max tokens can touch: its groups, plus one
+  // for a start inside a tile
+  const int max_tiles = (int)((a.n_max + kGroup - 1) / kGroup + 15) / 16 + 1;
   if (a.dtype == 0) {
-    hipLaunchKernelGGL((k_encode_groups<0>), dim3(max_groups, a.G, a.B), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_encode_tiles<0>), dim3(max_tiles, a.G, a.B), dim3(256), 0, st,
                        (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
     hipLaunchKernelGGL((k_ek_update<0>), dim3(a.G, a.B), dim3(128), 0, st, (uint8_t*)a.store,
                        a.n_new, a.n_max, a.G, a.W);
     hipLaunchKernelGGL((k_tail_update<0>), dim3(a.B), dim3(256), 0, st, (uint8_t*)a.store,
                        a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
   } else {
-    hipLaunchKernelGGL((k_encode_groups<1>), dim3(max_groups, a.G, a.B), dim3(256), 0, st,
+    hipLaunchKernelGGL((k_encode_tiles<1>), dim3(max_tiles, a.G, a.B), dim3(256), 0, st,
                        (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
     hipLaunchKernelGGL((k_ek_update<1>), dim3(a.G, a.B), dim3(128), 0, st, (uint8_t*)a.store,
                        a.n_new, a.n_max, a.G, a.W);

@@ -37,6 +37,10 @@ NAMES = [("k_append_small", "append"), ("k_key_alloc", "key_alloc"), ("k_score",
          ("k_value_select", "value_select"), ("k_gather", "value_gather"),
          ("k_out_reduce", "out_reduce")]
 STEP_KERNELS = [n for _, n in NAMES]
+# the prompt's encoding (one launch each per rate, when its store is filled)
+PREFILL = [("k_encode_tiles", "encode_tiles"), ("k_ek_update", "encode_ek"),
+           ("k_tail_update", "encode_tail")]
+PREFILL_KERNELS = [n for _, n in PREFILL]
 
 
 def source_hash() -> str:
@@ -52,7 +56,7 @@ def source_hash() -> str:
 
 def _short(kname: str):
     base = kname.split("(")[0].replace("void ", "").replace("readkv::", "").split("<")[0].strip()
-    for pre, short in NAMES:
+    for pre, short in NAMES + PREFILL:
         if base == pre:
             return short
     if "copyBuffer" in kname:
@@ -115,6 +119,18 @@ def summarize(p1: str, p2: str, warmup: int, steps: int, rates):
                 ks[n] = dict(read_bytes=rd, write_bytes=wr, dram_read_bytes=dr, launches=len(sel))
             ent[mode] = dict(kernels=ks, step_read_bytes=sum(k["read_bytes"] for k in ks.values()),
                              step_write_bytes=sum(k["write_bytes"] for k in ks.values()))
+        # the prompt's encoding: launch ri of each prefill kernel
+        pk = {}
+        for n in PREFILL_KERNELS:
+            launches = merged(n) if n in d1 else []
+            if len(launches) > ri:
+                c = launches[ri]
+                rd, wr, dr = raw_bytes(c)
+                pk[n] = dict(read_bytes=rd * scale["read"], write_bytes=wr * scale["write"],
+                             dram_read_bytes=dr * scale["dram"], launches=1)
+        if pk:
+            ent["prefill"] = dict(kernels=pk, step_read_bytes=sum(k["read_bytes"] for k in pk.values()),
+                                  step_write_bytes=sum(k["write_bytes"] for k in pk.values()))
         out["rates"][f"8,{R:g}"] = ent
     return out
 
@@ -127,8 +143,9 @@ def write_summary(s, path, command, warmup, steps, rates):
         f"# command (two passes, counters below): {command}",
         "#   pass 1: TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum",
         "#   pass 2: TCC_BUBBLE_sum TCC_EA0_RDREQ_DRAM_32B_sum TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum",
-        f"# launch sequence: 512 MiB copy; per rate {rates}: {warmup} warm-up, {steps} warm, "
-        f"{steps} flushed steps; medians over the {steps} launches of each mode",
+        f"# launch sequence: 512 MiB copy; per rate {rates}: the prompt's encoding (prefill), "
+        f"{warmup} warm-up, {steps} warm, {steps} flushed steps; medians over the {steps} launches "
+        f"of each mode",
         f"source_sha256={source_hash()}",
         f"copy.raw_read_bytes={s['copy']['raw_read']:.0f}",
         f"copy.raw_write_bytes={s['copy']['raw_write']:.0f}",

@@ -548,6 +548,52 @@ def test_encode_decode_mix_full_shape(record_property):
 
 
 # ------------------------------------------------------------ store flags
+def test_large_appends_starting_inside_a_key_tile():
+    """Appends of more than 64 tokens take the tile encoder: a 700-token
+    prompt leaves a partial key tile and a 28-token tail, then 900 tokens
+    close groups 21..49 (tile 1 from its sixth group, tile 2 whole, tile 3
+    in part), then 333 more; every store byte matches the oracle's
+    encoding of the 1933 tokens."""
+    chunks = [700, 900, 333]
+    total = sum(chunks)
+    cfg = synth.workload(2, B=2, H=8, G=2, T0=total)
+    B, G, d = cfg["B"], cfg["G"], cfg["d"]
+    lcfg = workload.config_for(cfg, 0)
+    say(f"[case] large appends {chunks} B={B} G={G}")
+    units = {(b, g): synth.kv_unit(cfg, b, g, total) for b in range(B) for g in range(G)}
+    cache = ReadKVCache(lcfg)
+    done = 0
+    for n in chunks:
+        kk = np.zeros((B, G, n, d), dtype=np.uint16)
+        vv = np.zeros((B, G, n, d), dtype=np.uint16)
+        for (b, g), (Ku, Vu) in units.items():
+            kk[b, g] = synth.to_device_bits(cfg, Ku[done:done + n])
+            vv[b, g] = synth.to_device_bits(cfg, Vu[done:done + n])
+        dv = workload.to_device(dict(k=kk, v=vv))
+        cache.append(dv["k"], dv["v"])
+        done += n
+    torch.cuda.synchronize()
+    flags, lens = cache.status()
+    assert flags == 0 and lens == [total] * B
+    store = cache.store.cpu().numpy()
+    hdr = F.read_header(store)
+    for (b, g), (Ku, Vu) in units.items():
+        ek, ev = O.encode_stream(Ku), O.encode_stream(Vu)
+        want = F.pack_unit(ek, ev, hdr["requests"][b]["cap"], cfg["dtype"])
+        got = F.unpack_unit(store, hdr, b, g)
+        ngc, tp, r = ek.n_groups, ek.t_packed, total - ek.t_packed
+        tag = f"unit=({b},{g})"
+        assert np.array_equal(_kp_groups(got["Kplanes"])[:, :, :ngc],
+                              _kp_groups(want["Kplanes"])[:, :, :ngc]), tag
+        assert np.array_equal(got["Vplanes"][:tp], want["Vplanes"][:tp]), tag
+        for f in ("Kmeta", "Vmeta", "EV"):
+            assert np.array_equal(got[f][:ngc], want[f][:ngc]), (tag, f)
+        assert np.array_equal(got["EK"], want["EK"]), tag
+        assert np.array_equal(got["Ktail"][:r], want["Ktail"][:r]), tag
+        assert np.array_equal(got["Vtail"][:r], want["Vtail"][:r]), tag
+    say(f"[store] large appends: {len(units)} units bit-exact")
+
+
 def test_nonfinite_input_sets_flag():
     cfg = synth.workload(2, B=1, H=4, G=1, T0=64)
     lcfg = workload.config_for(cfg, 0)
