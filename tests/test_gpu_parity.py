@@ -548,6 +548,55 @@ def test_encode_decode_mix_full_shape(record_property):
 
 
 # ------------------------------------------------------------ store flags
+def test_graph_replay_matches_eager_steps():
+    """The benchmark's step (append one token per request, then decode) captured
+    once in a HIP graph and replayed step after step, with eager work and
+    synchronisations between the replays, gives bitwise the outputs, depths
+    and read counters of the same steps run eagerly on a second cache."""
+    cfg = synth.workload(2, B=2, H=8, G=2, T0=1000)
+    steps, R = 6, 3.0
+    B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
+    say(f"[case] graph replay B={B} G={G} T0=1000 steps={steps} R={R}")
+    h = workload.host_inputs(cfg, steps)
+    dv = workload.to_device(h)
+    lcfg = workload.config_for(cfg, steps)
+    cap = (lcfg.capacity_tokens + 31) // 32 * 32
+    caches = [ReadKVCache(lcfg), ReadKVCache(lcfg)]
+    for c in caches:
+        c.append(dv["kpre"], dv["vpre"])
+    bufs = dict(k=torch.empty_like(dv["kstep"][0]), v=torch.empty_like(dv["vstep"][0]),
+                q=torch.empty_like(dv["q"][0]))
+    outs = [torch.empty((B, H, d), dtype=torch.float32, device="cuda") for _ in range(2)]
+    tks = [torch.zeros(B * G * d, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    tvs = [torch.zeros(B * G * cap, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    ctrs = [torch.zeros(NUM_COUNTERS, dtype=torch.int64, device="cuda") for _ in range(2)]
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        caches[1].append(bufs["k"], bufs["v"])
+        caches[1].decode(bufs["q"], R, R, out=outs[1], key_depths=tks[1], value_depths=tvs[1],
+                         counters=ctrs[1])
+    torch.cuda.synchronize()
+    junk = torch.ones(1 << 20, device="cuda")
+    for s in range(steps):
+        bufs["k"].copy_(dv["kstep"][s])
+        bufs["v"].copy_(dv["vstep"][s])
+        bufs["q"].copy_(dv["q"][s])
+        graph.replay()
+        # eager work between replays, then the same step eagerly on cache 0
+        junk.mul_(1.0001).sum()
+        torch.cuda.synchronize()
+        caches[0].append(dv["kstep"][s], dv["vstep"][s])
+        caches[0].decode(dv["q"][s], R, R, out=outs[0], key_depths=tks[0], value_depths=tvs[0],
+                         counters=ctrs[0])
+        torch.cuda.synchronize()
+        for name, (a, b) in dict(out=outs, tk=tks, tv=tvs, ctr=ctrs).items():
+            assert torch.equal(a, b), f"step {s}: {name} differs between replay and eager"
+    assert caches[0].status() == caches[1].status()
+    assert torch.equal(caches[0].store, caches[1].store)
+    say(f"[graph] {steps} replays equal to the eager steps")
+
+
 def test_large_appends_starting_inside_a_key_tile():
     """Appends of more than 64 tokens take the tile encoder: a 700-token
     prompt leaves a partial key tile and a 28-token tail, then 900 tokens
