@@ -35,13 +35,19 @@ Options a test may add to a workload (``workload(id, **overrides)``):
 * ``q_scale``: the query is multiplied by this factor (near-uniform
   attention when small);
 * ``q_log2_spread``: query channel c scaled by an exact power of two.
+
+For the pages' own codec (Gaussian Lloyd tree with Hadamard-sign transforms)
+two more draws: ``codec_signs`` (the two sign vectors, drawn once per layer)
+and ``calibration_split`` (held-out tokens of every KV head, from the same
+distribution as the cache but from draws of their own).
 """
 from __future__ import annotations
 
 import numpy as np
 
 # stream ids for SeedSequence
-_S_K, _S_V, _S_Q, _S_SIGMA, _S_A, _S_NEEDLE, _S_LEN, _S_QBASE, _S_GAP = range(9)
+(_S_K, _S_V, _S_Q, _S_SIGMA, _S_A, _S_NEEDLE, _S_LEN, _S_QBASE, _S_GAP, _S_CAL,
+ _S_SIGN) = range(11)
 
 WORKLOADS = {
     1: dict(name="tiny-1q1kv-d128-T1024", B=1, H=1, G=1, d=128, T0=1024,
@@ -114,6 +120,15 @@ def total_tokens(cfg: dict) -> np.ndarray:
     return context_lengths(cfg) + int(cfg["steps"])
 
 
+def codec_signs(cfg: dict):
+    """The sign vectors of the key and the value Hadamard-sign transforms:
+    two int8 arrays [d] of +-1."""
+    r = _rng(cfg["id"], _S_SIGN, 0, 0, 0)
+    s = r.integers(0, 2, size=(2, cfg["d"]))
+    s = (1 - 2 * s).astype(np.int8)
+    return s[0].copy(), s[1].copy()
+
+
 def _sigma(cfg, stream, g):
     r = _rng(cfg["id"], _S_SIGMA, stream, g, 0)
     return np.exp(r.uniform(np.log(0.1), np.log(10.0), size=cfg["d"]))
@@ -154,6 +169,24 @@ def kv_unit(cfg: dict, b: int, g: int, n_tokens: int | None = None):
             x = x.copy()
             x[:, 1::2] = x[:, 0::2]
         out.append(cast(cfg, x[:n]))
+    return out[0], out[1]
+
+
+def calibration_split(cfg: dict, g: int, n: int):
+    """n held-out keys and values of KV head g ([n][d] float64, exact in the
+    workload's dtype): the cache's per-channel scales and shared low-rank
+    part, with token draws of their own (no needles, ties or gaps)."""
+    d = cfg["d"]
+    out = []
+    for stream in (_S_K, _S_V):
+        sig = _sigma(cfg, stream, g)
+        r = _rng(cfg["id"], _S_CAL, stream, g, 0)
+        x = r.standard_normal((n, d)) * sig[None, :]
+        if cfg["structure"] in ("lowrank", "needles"):
+            ra = _rng(cfg["id"], _S_A, stream, g, 0)
+            A = ra.normal(0.0, np.sqrt(1.0 / 8.0), size=(d, 8))
+            x = x + r.standard_normal((n, 8)) @ A.T
+        out.append(cast(cfg, x))
     return out[0], out[1]
 
 
