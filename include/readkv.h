@@ -11,11 +11,22 @@
  * every value token to read (Sec. 3.2-3.3, Algorithm 1; a staged(2) reader
  * in the sense of Sec. 2).  Stored records are never rewritten.
  *
- * Code used here: per (request, KV head, channel, 32-token group) uniform
- * min/max quantiser; lo = bf16 group minimum rounded down, rng = bf16 range
- * rounded up; code = min(floor((x - lo) * 2^W / rng), 2^W - 1); stored as W
- * MSB-first bit-planes.  A depth-t prefix P reconstructs to
- * lo + rng * (2P + 1) / 2^(t+1).  Refinement gains follow D(t) ~ 4^-t.
+ * Two codes (readkv_config.codec):
+ * READKV_CODEC_UNIFORM: per (request, KV head, channel, 32-token group)
+ *   uniform min/max quantiser; lo = bf16 group minimum rounded down, rng =
+ *   bf16 range rounded up; code = min(floor((x - lo) * 2^W / rng), 2^W - 1);
+ *   stored as W MSB-first bit-planes.  A depth-t prefix P reconstructs to
+ *   lo + rng * (2P + 1) / 2^(t+1).  Refinement gains follow D(t) ~ 4^-t.
+ * READKV_CODEC_LLOYD: the pages' own code (Sec. 3.1, App. D.1).  Keys and
+ *   queries pass through a Hadamard-sign transform U_K x = H (s_K . x) /
+ *   sqrt(d_h), values through U_V (the output is mapped back by U_V^T);
+ *   every transformed scalar is standardised with its KV head's calibrated
+ *   channel mean and scale, z = (x' - mu) / sigma, and stored as its path
+ *   in the depth-8 Gaussian Lloyd tree (first W levels), as W MSB-first
+ *   bit-planes.  A depth-t prefix reconstructs to mu + sigma * (float32
+ *   centroid of its depth-t cell); gains are the tree's float32 Delta_t
+ *   (Lemma 7).  The store carries the tree, the signs and the calibration
+ *   (readkv_codec_init) in a codec block after its header.
  *
  * Ownership: the caller allocates every buffer (store, workspace, inputs,
  * outputs) in device memory and keeps it alive until the enqueued work
@@ -59,8 +70,12 @@ extern "C" {
 #define READKV_BF16 0
 #define READKV_F32 1
 
+#define READKV_CODEC_UNIFORM 0
+#define READKV_CODEC_LLOYD 1
+
 /* Value-item scale s in the value weight (Sec. 3.2, Eq. (3); App. D.2):
- * PHYSICAL = sum over channels of the token group's squared range,
+ * PHYSICAL = sum over channels of the token group's squared range (uniform
+ * code) or of the KV head's squared calibrated scales sigma^V (Lloyd code),
  * UNIT = 1 (standardised units). */
 #define READKV_VSCALE_PHYSICAL 0
 #define READKV_VSCALE_UNIT 1
@@ -89,9 +104,14 @@ extern "C" {
  * over every request and KV head:
  *   [READKV_CTR_KEY_PAYLOAD]   sum over units of T_packed * sum_c t^K_c
  *   [READKV_CTR_VALUE_PAYLOAD] sum over units of d_h * sum_j t^V_j
- *   [READKV_CTR_METADATA]      lo and rng (16 bits each) of every closed group
- *                              and channel of keys and values, E^K (d_h x 64
- *                              bits) and E^V (64 bits per closed group)
+ *   [READKV_CTR_METADATA]      uniform code: lo and rng (16 bits each) of
+ *                              every closed group and channel of keys and
+ *                              values, E^K (d_h x 64 bits) and E^V (64 bits
+ *                              per closed group); Lloyd code: one load per
+ *                              call of the layer's calibration arrays (mu,
+ *                              sigma of keys and values, 32 bits per KV head
+ *                              and channel) and of the decoder table (510
+ *                              centroids and 8 gains, 32 bits each)
  *   [READKV_CTR_OPEN_GROUP]    keys and values of the open group in kv_dtype */
 #define READKV_CTR_KEY_PAYLOAD 0
 #define READKV_CTR_VALUE_PAYLOAD 1
@@ -101,7 +121,7 @@ extern "C" {
 
 /* Store flags (readkv_store_status) */
 #define READKV_FLAG_NONFINITE 1u /* a group held a non-finite value; it was
-                                    stored with lo = rng = 0 and codes 0     */
+                                    stored with codes 0 (and lo = rng = 0)   */
 #define READKV_FLAG_OVERFLOW 2u  /* an append ran past a request's capacity;
                                     the tokens beyond it were dropped        */
 
@@ -119,7 +139,7 @@ typedef struct readkv_config {
   int32_t kv_dtype;        /* READKV_BF16 or READKV_F32: element type of
                               appended K/V, of the open-group buffer and of
                               queries                                      */
-  int32_t reserved;        /* must be 0                                    */
+  int32_t codec;           /* READKV_CODEC_UNIFORM or READKV_CODEC_LLOYD   */
 } readkv_config;
 
 /* Check a config.  Returns 0, EINVAL, EDTYPE or EUNSUPPORTED. */
@@ -144,13 +164,39 @@ int readkv_store_init(const readkv_config* cfg, void* store,
                       size_t store_bytes, const int64_t* req_capacity,
                       void* stream);
 
+/* Lloyd code only: set the store's transform signs and calibrate it
+ * (Sec. 3.1; App. D.1: means and scales per KV head and transformed
+ * channel from held-out data).  Call after readkv_store_init and before the
+ * first append (until then the signs are +1, means 0 and scales 1).
+ * signs_k, signs_v: host int8 [head_dim] of +1 / -1 (the signs s_K, s_V of
+ *   U_K and U_V, drawn once by the caller), or NULL for all +1.
+ * k_cal, v_cal: device [n_cal][num_kv_heads][head_dim] calibration keys and
+ *   values in kv_dtype, 1 <= n_cal <= 2^24.
+ * Per KV head g and channel c: x' = U x of every calibration token;
+ * mu = (sum x') / n_cal and sigma = sqrt(sum (x' - mu)^2 / n_cal), sums in
+ * token order in float64, then rounded to float32; a zero or non-finite
+ * sigma becomes 1.  Also stores s_g = sum_c sigma^V_{g,c}^2.  EINVAL for a
+ * uniform-code store or a bad argument.  Synchronises `stream`. */
+int readkv_codec_init(const readkv_config* cfg, void* store,
+                      const int8_t* signs_k, const int8_t* signs_v,
+                      const void* k_cal, const void* v_cal, int64_t n_cal,
+                      void* stream);
+
+/* The library's Lloyd-tree table (App. D.1), host arrays: cent_out [511]
+ * float32 centroids, depth-t cell P at (2^t - 1) + P (t = 0..8, depth 0 is
+ * 0); bounds_out [255] the encoder's boundary of depth-t cell P at
+ * (2^t - 1) + P (t = 0..7, the midpoint of the two float32 child
+ * centroids); gains_out [9] the float32 gains Delta_t = D(t-1) - D(t),
+ * t = 1..8 (gains_out[0] = 0).  Host only, no device access. */
+int readkv_codec_tables(float* cent_out, double* bounds_out, double* gains_out);
+
 /* Append new tokens (the encoder of Sec. 3.1 / Algorithm 1).
  * k_new, v_new: device [batch][num_kv_heads][n_max][head_dim] in kv_dtype;
  *   request b contributes its first n_new[b] rows (ragged prefill).
  * n_new: device int32 [batch], or NULL for n_max rows in every request.
  * When a request's open group reaches 32 tokens the group is quantised and
- * its bit-planes, metadata and energy sums are written once; tokens of a
- * still-open group are kept exactly.  Returns ENOSPC if n_max exceeds the
+ * its bit-planes (uniform code: also its metadata and energy sums) are
+ * written once; tokens of a still-open group are kept exactly.  Returns ENOSPC if n_max exceeds the
  * store's default capacity. */
 int readkv_encode_append(const readkv_config* cfg, void* store,
                          const void* k_new, const void* v_new,
@@ -181,9 +227,13 @@ int readkv_encode_append(const readkv_config* cfg, void* store,
  *   (entries beyond a request's packed length are unspecified).
  * counters_out: device u64 [READKV_NUM_COUNTERS] or NULL; overwritten with
  *   this call's logical reads in bits (see READKV_CTR_*).
- * Allocation is ChooseDepths (Sec. 3.3) with gains a_i * 4^-t, exact under
- * diminishing gains (App. E.2.1, Prop. 8); ties go to the lowest channel /
- * token index; only positive gains are taken.  Results are bitwise
+ * Allocation is ChooseDepths (Sec. 3.3) with gains a_i * 4^-t (uniform
+ * code) or a_i * Delta_t (Lloyd code), exact under diminishing gains (App.
+ * E.2.1, Prop. 8); ties go to the lowest channel / token index; only
+ * positive gains are taken.  Lloyd code: key weights (q'_c sigma^K_c)^2
+ * summed over the KV head's query heads with q' = U_K q, logits
+ * q' . k_hat' / sqrt(d_h), output U_V^T (sum alpha v_hat'); tokens of the
+ * open group use q . k / sqrt(d_h) and their exact values.  Results are bitwise
  * reproducible from call to call. */
 int readkv_decode_attn(const readkv_config* cfg, const void* store,
                        const void* q, float R_K, float R_V, int32_t policy,

@@ -287,6 +287,19 @@ class LloydStream:
     def t_packed(self) -> int:
         return self.codes.shape[0]
 
+    @property
+    def n_groups(self) -> int:
+        return self.codes.shape[0] // self.group_tokens
+
+    # the store keeps no group metadata for this code: zero lo / rng
+    @property
+    def lo(self) -> np.ndarray:
+        return np.zeros((self.n_groups, self.codes.shape[1]))
+
+    @property
+    def rng(self) -> np.ndarray:
+        return np.zeros((self.n_groups, self.codes.shape[1]))
+
 
 def lloyd_encode_stream(X: np.ndarray, tree: LloydTree, signs, mu, sigma, W: int = 8,
                         group_tokens: int = 32) -> LloydStream:

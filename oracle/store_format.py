@@ -9,8 +9,17 @@ Layout (all little-endian; every sub-array starts on a 256-byte boundary):
 header (align_up(256 + 32*B, 4096) bytes)
   u32 magic 0x52564B31, u32 version 1, i32 W, i32 d, i32 H, i32 G,
   i32 group_tokens, i32 B, i32 kv_dtype (0 bf16, 1 f32), u32 flags,
-  i64 capacity, i64 total_bytes;  at 256 + 32*b: i64 len, i64 cap,
-  i64 offset, i64 reserved  for request b.
+  i64 capacity, i64 total_bytes, i32 codec (0 uniform, 1 Lloyd tree);
+  at 256 + 32*b: i64 len, i64 cap, i64 offset, i64 reserved  for request b.
+codec block (Lloyd tree only, right after the header; 256-byte aligned
+  parts, total rounded up to 4096):
+  cent   f32 [512]   centroid of depth-t cell P at 2^t - 1 + P (t = 0..8)
+  bounds f64 [256]   boundary of depth-t cell P at 2^t - 1 + P (t = 0..7)
+  gains  f64 [16]    Delta_t at t = 1..8
+  sk, sv f64 [d]     transform signs
+  vtab   f16 [9][256]  entry (t, X): centroid of depth-t cell X >> (8 - t)
+  muk, sigk, muv, sigv f32 [G][d];  sphys f64 [G]
+  (the first five parts are packed back to back, vtab then padded to 256)
 request region b (cap = cap_b, a multiple of 32; ng = cap/32):
   Kplanes u32 [G][ntk][d][W][16]  bit i of word (g,tau,c,p,k) = plane p
                               (bit W-1-p of the code) of token
@@ -63,6 +72,64 @@ def region_layout(G: int, d: int, W: int, cap: int, esize: int) -> dict:
         off += size
     lay["_size"] = _al(off, 4096)
     return lay
+
+
+def codec_block_bytes(G: int, d: int) -> int:
+    return _codec_parts(G, d)["_size"]
+
+
+def _codec_parts(G: int, d: int) -> dict:
+    off = 0
+    lay = {}
+    for name, size in [("cent", 512 * 4), ("bounds", 256 * 8), ("gains", 16 * 8),
+                       ("sk", d * 8), ("sv", d * 8), ("vtab", 9 * 256 * 2)]:
+        lay[name] = (off, size)
+        off += size
+    for name, size in [("muk", G * d * 4), ("sigk", G * d * 4), ("muv", G * d * 4),
+                       ("sigv", G * d * 4), ("sphys", G * 8)]:
+        off = _al(off, 256) if name == "muk" else off
+        lay[name] = (off, size)
+        off += size
+    lay["_size"] = _al(off, 4096)
+    return lay
+
+
+def codec_block(codec, G: int, d: int) -> np.ndarray:
+    """The bytes of a Lloyd-tree store's codec block for the oracle's codec
+    state (oracle.lloyd.Codec with calibration arrays of G KV heads)."""
+    lay = _codec_parts(G, d)
+    out = np.zeros(lay["_size"], dtype=np.uint8)
+
+    def put(name, arr):
+        o, n = lay[name]
+        raw = np.ascontiguousarray(arr).view(np.uint8).reshape(-1)
+        assert raw.size <= n
+        out[o:o + raw.size] = raw
+
+    T = codec.tree
+    cent = np.zeros(512, dtype=np.float32)
+    cent[:511] = T.flat_centroids32().astype(np.float32)
+    put("cent", cent)
+    bnd = np.zeros(256)
+    bnd[:255] = np.concatenate([T.bounds[t] for t in range(8)])
+    put("bounds", bnd)
+    gains = np.zeros(16)
+    gains[:9] = T.gains32
+    put("gains", gains)
+    ones = np.ones(d)
+    put("sk", ones if codec.sK is None else np.asarray(codec.sK, dtype=np.float64))
+    put("sv", ones if codec.sV is None else np.asarray(codec.sV, dtype=np.float64))
+    vt = np.zeros((9, 256), dtype=np.float16)
+    flat = T.flat_centroids32()
+    for t in range(9):
+        vt[t] = flat[(1 << t) - 1 + (np.arange(256) >> (8 - t))].astype(np.float32).astype(np.float16)
+    put("vtab", vt)
+    put("muk", np.asarray(codec.muK, dtype=np.float32))
+    put("sigk", np.asarray(codec.sigK, dtype=np.float32))
+    put("muv", np.asarray(codec.muV, dtype=np.float32))
+    put("sigv", np.asarray(codec.sigV, dtype=np.float32))
+    put("sphys", np.array([codec.s_phys(g) for g in range(G)]))
+    return out
 
 
 def _bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -121,13 +188,13 @@ def pack_unit(enc_k, enc_v, cap: int, dtype: str) -> dict:
 def read_header(buf: np.ndarray) -> dict:
     """Parse the store header from raw bytes (uint8 array)."""
     b = np.asarray(buf, dtype=np.uint8)
-    u32 = b[:48].view(np.uint32)
-    i32 = b[:48].view(np.int32)
-    i64 = b[:48].view(np.int64)
+    u32 = b[:64].view(np.uint32)
+    i32 = b[:64].view(np.int32)
+    i64 = b[:64].view(np.int64)
     hdr = dict(magic=int(u32[0]), version=int(u32[1]), W=int(i32[2]), d=int(i32[3]),
                H=int(i32[4]), G=int(i32[5]), group_tokens=int(i32[6]),
                B=int(i32[7]), kv_dtype=int(i32[8]), flags=int(u32[9]),
-               capacity=int(i64[5]))
+               capacity=int(i64[5]), codec=int(i32[14]))
     reqs = []
     for r in range(hdr["B"]):
         rec = b[256 + 32 * r: 256 + 32 * r + 32].view(np.int64)

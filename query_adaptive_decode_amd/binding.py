@@ -20,12 +20,13 @@ VSCALE_PHYSICAL, VSCALE_UNIT = 0, 1
 SCOPE_KV_HEAD, SCOPE_LAYER = 0, 1
 RESTRICT_MIN_DEPTH1, RESTRICT_VALUE_PAIRS = 0x10, 0x20   # OR'ed into a policy
 NUM_COUNTERS = 4   # key payload, value payload, metadata, open group (bits)
+CODEC_UNIFORM, CODEC_LLOYD = 0, 1
 FLAG_NONFINITE, FLAG_OVERFLOW = 1, 2
 
 EXPORTED = ["readkv_validate_config", "readkv_store_bytes", "readkv_workspace_bytes",
             "readkv_store_init", "readkv_encode_append", "readkv_decode_attn",
             "readkv_decode_attn_timed", "readkv_decode_attn_noalloc", "readkv_store_status",
-            "readkv_strerror"]
+            "readkv_strerror", "readkv_codec_init", "readkv_codec_tables"]
 
 
 class Config(ctypes.Structure):
@@ -33,7 +34,7 @@ class Config(ctypes.Structure):
                 ("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("group_tokens", ctypes.c_int32), ("batch", ctypes.c_int32),
                 ("capacity_tokens", ctypes.c_int64), ("kv_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("codec", ctypes.c_int32)]
 
 
 class ReadKVError(RuntimeError):
@@ -68,6 +69,8 @@ def lib():
             "readkv_decode_attn_noalloc": [CP, P, P, ctypes.c_float, ctypes.c_float, I32, I32,
                                            P, P, P, P, P],
             "readkv_store_status": [CP, P, ctypes.POINTER(ctypes.c_uint32), P],
+            "readkv_codec_init": [CP, P, P, P, P, P, I64, P],
+            "readkv_codec_tables": [P, P, P],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -86,9 +89,9 @@ def _check(fn, rc):
 
 
 def make_config(W=8, head_dim=128, num_q_heads=32, num_kv_heads=8, batch=1,
-                capacity_tokens=1024, kv_dtype=BF16, group_tokens=32) -> Config:
+                capacity_tokens=1024, kv_dtype=BF16, group_tokens=32, codec=CODEC_UNIFORM) -> Config:
     return Config(W, head_dim, num_q_heads, num_kv_heads, group_tokens, batch,
-                  capacity_tokens, kv_dtype, 0)
+                  capacity_tokens, kv_dtype, codec)
 
 
 def _ptr(t):
@@ -134,6 +137,36 @@ def store_init(cfg: Config, store: torch.Tensor, req_capacity=None):
     keep, p = _caps(cfg, req_capacity)
     _check("readkv_store_init", lib().readkv_store_init(
         ctypes.byref(cfg), _ptr(store), store.numel() * store.element_size(), p, _stream()))
+
+
+def codec_init(cfg: Config, store, signs_k, signs_v, k_cal, v_cal):
+    """Lloyd code: set the transform signs (host int8 sequences of +-1, or
+    None) and calibrate from device tensors k_cal, v_cal [n][G][d] in the
+    config's dtype.  Synchronises the stream."""
+    _need_cuda(store, k_cal, v_cal)
+
+    def signs(s):
+        if s is None:
+            return None, None
+        arr = (ctypes.c_int8 * cfg.head_dim)(*[int(x) for x in s])
+        return arr, ctypes.cast(arr, ctypes.c_void_p)
+    ka, kp = signs(signs_k)
+    va, vp = signs(signs_v)
+    _check("readkv_codec_init", lib().readkv_codec_init(
+        ctypes.byref(cfg), _ptr(store), kp, vp, _ptr(k_cal), _ptr(v_cal), int(k_cal.shape[0]),
+        _stream()))
+
+
+def codec_tables():
+    """The library's Lloyd-tree table: (centroids float32 [511], boundaries
+    float64 [255], gains float64 [9]) as Python lists.  Host only."""
+    cent = (ctypes.c_float * 511)()
+    bnd = (ctypes.c_double * 255)()
+    gains = (ctypes.c_double * 9)()
+    _check("readkv_codec_tables", lib().readkv_codec_tables(
+        ctypes.cast(cent, ctypes.c_void_p), ctypes.cast(bnd, ctypes.c_void_p),
+        ctypes.cast(gains, ctypes.c_void_p)))
+    return list(cent), list(bnd), list(gains)
 
 
 def encode_append(cfg: Config, store, k_new, v_new, n_new=None, n_max=None):

@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIBDIR, "libreadkv.so")
-SOURCES = ["abi.hip", "encode.hip", "alloc.hip", "decode.hip"]
+SOURCES = ["abi.hip", "codec.hip", "encode.hip", "alloc.hip", "decode.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -50,7 +50,8 @@ std::vector<uint8_t> header_image(const readkv_config* cfg, const int64_t* req_c
   h.kv_dtype = cfg->kv_dtype;
   h.flags = 0;
   h.capacity = capmax_of(cfg);
-  int64_t off = hb;
+  h.codec = cfg->codec;
+  int64_t off = hb + codec_bytes(cfg->codec, cfg->num_kv_heads, cfg->head_dim);
   for (int b = 0; b < cfg->batch; ++b) {
     ReqRecord r;
     r.len = 0;
@@ -105,7 +106,7 @@ int readkv_validate_config(const readkv_config* cfg) {
     return READKV_EINVAL;
   if (cfg->num_q_heads % cfg->num_kv_heads != 0) return READKV_EINVAL;
   if (cfg->capacity_tokens > (int64_t(1) << 26)) return READKV_EINVAL;
-  if (cfg->reserved != 0) return READKV_EINVAL;
+  if (cfg->codec != READKV_CODEC_UNIFORM && cfg->codec != READKV_CODEC_LLOYD) return READKV_EINVAL;
   if (cfg->head_dim != kDim) return READKV_EUNSUPPORTED;
   if (cfg->group_tokens != kGroup) return READKV_EUNSUPPORTED;
   if (cfg->num_q_heads / cfg->num_kv_heads > 8) return READKV_EUNSUPPORTED;
@@ -146,7 +147,57 @@ int readkv_store_init(const readkv_config* cfg, void* store, size_t store_bytes,
   if (launch_store_zero(store, (size_t)total, st)) return READKV_ELAUNCH;
   if (hipMemcpyAsync(store, img.data(), img.size(), hipMemcpyHostToDevice, st) != hipSuccess)
     return READKV_ELAUNCH;
+  std::vector<uint8_t> cimg;
+  if (cfg->codec == READKV_CODEC_LLOYD) {
+    cimg.resize((size_t)codec_bytes(1, cfg->num_kv_heads, cfg->head_dim));
+    codec_block_image(cfg->num_kv_heads, cimg.data());
+    if (hipMemcpyAsync((uint8_t*)store + img.size(), cimg.data(), cimg.size(),
+                       hipMemcpyHostToDevice, st) != hipSuccess)
+      return READKV_ELAUNCH;
+  }
   if (hipStreamSynchronize(st) != hipSuccess) return READKV_ELAUNCH;
+  return READKV_OK;
+}
+
+int readkv_codec_init(const readkv_config* cfg, void* store, const int8_t* signs_k,
+                      const int8_t* signs_v, const void* k_cal, const void* v_cal, int64_t n_cal,
+                      void* stream) {
+  int rc = readkv_validate_config(cfg);
+  if (rc) return rc;
+  if (cfg->codec != READKV_CODEC_LLOYD || !store || !k_cal || !v_cal || n_cal < 1 ||
+      n_cal > (int64_t(1) << 24))
+    return READKV_EINVAL;
+  std::vector<double> sg(2 * (size_t)kDim, 1.0);
+  for (int c = 0; c < kDim; ++c) {
+    if (signs_k) {
+      if (signs_k[c] != 1 && signs_k[c] != -1) return READKV_EINVAL;
+      sg[c] = (double)signs_k[c];
+    }
+    if (signs_v) {
+      if (signs_v[c] != 1 && signs_v[c] != -1) return READKV_EINVAL;
+      sg[kDim + c] = (double)signs_v[c];
+    }
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const CodecLayout C = codec_layout(cfg->num_kv_heads, kDim);
+  uint8_t* cb = (uint8_t*)store + header_bytes(cfg->batch);
+  static_assert(sizeof(double) * kDim * 2 == 2048, "sk and sv are adjacent");
+  if (C.sv != C.sk + kDim * 8) return READKV_ELAUNCH;
+  if (hipMemcpyAsync(cb + C.sk, sg.data(), sg.size() * sizeof(double), hipMemcpyHostToDevice, st) !=
+      hipSuccess)
+    return READKV_ELAUNCH;
+  if (launch_calibrate(cb, cfg->num_kv_heads, cfg->kv_dtype, k_cal, v_cal, n_cal, st))
+    return READKV_ELAUNCH;
+  if (hipStreamSynchronize(st) != hipSuccess) return READKV_ELAUNCH;
+  return READKV_OK;
+}
+
+int readkv_codec_tables(float* cent_out, double* bounds_out, double* gains_out) {
+  if (!cent_out || !bounds_out || !gains_out) return READKV_EINVAL;
+  const TreeTables& T = lloyd_tables();
+  for (int i = 0; i < 511; ++i) cent_out[i] = T.cent[i];
+  for (int i = 0; i < 255; ++i) bounds_out[i] = T.bounds[i];
+  for (int t = 0; t <= kTreeDepth; ++t) gains_out[t] = T.gains[t];
   return READKV_OK;
 }
 
@@ -168,6 +219,8 @@ int readkv_encode_append(const readkv_config* cfg, void* store, const void* k_ne
   a.G = cfg->num_kv_heads;
   a.W = cfg->W;
   a.dtype = cfg->kv_dtype;
+  a.codec = cfg->codec;
+  a.cblock = (const uint8_t*)store + header_bytes(cfg->batch);
   return launch_encode(a, (hipStream_t)stream) ? READKV_ELAUNCH : READKV_OK;
 }
 
@@ -183,6 +236,7 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   if (vscale != READKV_VSCALE_PHYSICAL && vscale != READKV_VSCALE_UNIT) return READKV_EINVAL;
   if (policy & ~(READKV_SCOPE_LAYER | READKV_RESTRICT_MIN_DEPTH1 | READKV_RESTRICT_VALUE_PAIRS))
     return READKV_EINVAL;
+  if (cfg->codec == READKV_CODEC_LLOYD) return READKV_EUNSUPPORTED;
   const int scope = policy & READKV_SCOPE_LAYER;
   if (scope == READKV_SCOPE_LAYER && cfg->num_kv_heads > kMaxPooledKV) return READKV_EUNSUPPORTED;
   // budgets must fit the 32-bit counters: R * (items of a domain) <= 2^31
@@ -215,6 +269,8 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   a.dtype = cfg->kv_dtype;
   a.capmax = capmax;
   a.events = events;
+  a.codec = cfg->codec;
+  a.cblock = (const uint8_t*)store + header_bytes(cfg->batch);
   rc = launch_decode(a, (hipStream_t)stream);
   if (rc == -5) return READKV_EUNSUPPORTED;
   return rc ? READKV_ELAUNCH : READKV_OK;

@@ -39,7 +39,7 @@ namespace readkv {
 
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr double kInvSqrtD = 0.088388347648318440550;  // 1/sqrt(128)
+constexpr double kInvSqrtD = kInvSqrt128;
 
 // ---------------------------------------------------------------------------
 // Key allocation.  ChooseDepths for one unit's d_h = 128 key channels by one

@@ -10,6 +10,14 @@
 // The floor is exact: the fp64 quotient is corrected by comparing q*rng
 // with the numerator, both of which are exact in fp64 (q <= 2^W has at
 // most 9 bits and rng 8 significant bits).
+//
+// Under the pages' own codec (Sec. 3.1, App. D.1; the store's codec block
+// holds the tree and calibration) each token of a closing group is mapped
+// through the Hadamard-sign transform x' = H (s . x) / sqrt(d) (in-place
+// Walsh-Hadamard butterflies over the block, float64: the sums of +-x are
+// exact for bf16 inputs), standardised z = (x' - mu_c) / sigma_c, and coded
+// as its path down the Lloyd tree: at each node the upper child when
+// z >= the node's boundary, the first W levels of the depth-8 walk.
 #include "kernels_common.h"
 #include "readkv_internal.h"
 
@@ -37,11 +45,15 @@ __device__ __forceinline__ int64_t clamp_n(const ReqRecord& r, const int32_t* n_
 // Its key-plane words (one word of each (channel, plane) line of its
 // 512-token tile) go to kst (LDS, the tile's d W 16 words) when the caller
 // writes the whole tile out afterwards, else straight to the store.
-template <int DT>
+// Lloyd-tree code (LL): cb = the codec block, g / G the KV head, xs = LDS
+// [2][32][d] doubles (the group's tokens while they are transformed), bnd =
+// the tree's boundaries in LDS; no metadata, E^K or E^V.
+template <int DT, bool LL>
 __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, const void* knew,
                                                const void* vnew, int64_t row0, int64_t len0,
                                                int64_t gam, int W, int* bad_s, double* rv2,
-                                               uint32_t* vst, uint32_t* kst) {
+                                               uint32_t* vst, uint32_t* kst, const uint8_t* cb,
+                                               int g, int G, double* xs, const double* bnd) {
   const int tid = threadIdx.x;
   const bool isv = tid >= 128;
   const int c = tid & 127;
@@ -70,35 +82,68 @@ __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, co
       mx = fmax(mx, x[s]);
     }
   }
-  const uint32_t lo_b = bf16_round_dir(mn, false);
-  const double lo = (double)bf16_to_float(lo_b);
-  const uint32_t rng_b = bf16_round_dir(mx - lo, true);
-  const double rng = (double)bf16_to_float(rng_b);
-  if (!(isfinite(lo) && isfinite(rng))) atomicOr(&bad_s[isv], 1);
-  __syncthreads();
-  const bool bad = bad_s[isv] != 0;
-
   uint32_t code[kGroup];
-  const double scale = (double)(1u << W);
-  const double cmax = (double)((1u << W) - 1u);
+  uint32_t meta = 0u;
+  double r2 = 0.0;
+  if constexpr (LL) {
+    const CodecLayout C = codec_layout(G, kDim);
+    const double sgn = reinterpret_cast<const double*>(cb + (isv ? C.sv : C.sk))[c];
+    const double mu = (double)reinterpret_cast<const float*>(cb + (isv ? C.muv : C.muk))[g * kDim + c];
+    const double sd = (double)reinterpret_cast<const float*>(cb + (isv ? C.sigv : C.sigk))[g * kDim + c];
+    __syncthreads();
+    const bool bad = bad_s[isv] != 0;
+    double* xb = xs + (isv ? kGroup * kDim : 0);
 #pragma unroll
-  for (int s = 0; s < kGroup; ++s) {
-    double q = 0.0;
-    if (!bad && rng > 0.0) {
-      const double num = (x[s] - lo) * scale;  // fl64(x - lo) * 2^W, exact scaling
-      q = floor(num / rng);
-      if (q * rng > num) q -= 1.0;             // q*rng exact: <= 9 x 8 significant bits
-      else if ((q + 1.0) * rng <= num) q += 1.0;
-      q = fmin(q, cmax);
+    for (int s = 0; s < kGroup; ++s) xb[s * kDim + c] = bad ? 0.0 : x[s] * sgn;
+    for (int h = 1; h < kDim; h <<= 1) {
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < kGroup; ++s) {
+        const double a = xb[s * kDim + c], o = xb[s * kDim + (c ^ h)];
+        x[s] = (c & h) ? o - a : a + o;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int s = 0; s < kGroup; ++s) xb[s * kDim + c] = x[s];
     }
-    code[s] = (uint32_t)q;
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) {
+      const double z = __ddiv_rn(__dsub_rn(__dmul_rn(x[s], kInvSqrt128), mu), sd);
+      uint32_t P = 0;
+      for (int t = 0; t < kTreeDepth; ++t) P = 2 * P + (z >= bnd[(1 << t) - 1 + P] ? 1u : 0u);
+      code[s] = bad ? 0u : P >> (kTreeDepth - W);
+    }
+    if (bad && c == 0) atomicOr(&header_of(store)->flags, 1u);
+  } else {
+    const uint32_t lo_b = bf16_round_dir(mn, false);
+    const double lo = (double)bf16_to_float(lo_b);
+    const uint32_t rng_b = bf16_round_dir(mx - lo, true);
+    const double rng = (double)bf16_to_float(rng_b);
+    if (!(isfinite(lo) && isfinite(rng))) atomicOr(&bad_s[isv], 1);
+    __syncthreads();
+    const bool bad = bad_s[isv] != 0;
+
+    const double scale = (double)(1u << W);
+    const double cmax = (double)((1u << W) - 1u);
+#pragma unroll
+    for (int s = 0; s < kGroup; ++s) {
+      double q = 0.0;
+      if (!bad && rng > 0.0) {
+        const double num = (x[s] - lo) * scale;  // fl64(x - lo) * 2^W, exact scaling
+        q = floor(num / rng);
+        if (q * rng > num) q -= 1.0;             // q*rng exact: <= 9 x 8 significant bits
+        else if ((q + 1.0) * rng <= num) q += 1.0;
+        q = fmin(q, cmax);
+      }
+      code[s] = (uint32_t)q;
+    }
+    meta = bad ? 0u : (lo_b | (rng_b << 16));
+    r2 = bad ? 0.0 : rng * rng;
+    if (bad && c == 0) atomicOr(&header_of(store)->flags, 1u);
   }
-  const uint32_t meta = bad ? 0u : (lo_b | (rng_b << 16));
-  const double r2 = bad ? 0.0 : rng * rng;
-  if (bad && c == 0) atomicOr(&header_of(store)->flags, 1u);
 
   if (!isv) {
-    u.kmeta[gam * kDim + c] = meta;
+    if constexpr (!LL) u.kmeta[gam * kDim + c] = meta;
     for (int p = 0; p < W; ++p) {
       uint32_t word = 0;
 #pragma unroll
@@ -107,8 +152,10 @@ __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, co
       else u.kplanes[(((gam >> 4) * kDim + c) * W + p) * 16 + (gam & 15)] = word;
     }
   } else {
-    u.vmeta[gam * kDim + c] = meta;
-    rv2[c] = r2;
+    if constexpr (!LL) {
+      u.vmeta[gam * kDim + c] = meta;
+      rv2[c] = r2;
+    }
     const int half = c >> 6;  // which 64-channel half this wave holds
     for (int s = 0; s < kGroup; ++s) {
       for (int p = 0; p < W; ++p) {
@@ -124,7 +171,7 @@ __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, co
   if (tid < kGroup * W)  // the group's value rows: 16 bytes per thread
     reinterpret_cast<uint4*>(u.vplanes + gam * kGroup * W * (kDim / 32))[tid] =
         reinterpret_cast<const uint4*>(vst)[tid];
-  if (tid == 128) {
+  if (!LL && tid == 128) {
     double e = 0.0;
     for (int cc = 0; cc < kDim; ++cc) e = e + rv2[cc];
     u.ev[gam] = e;
@@ -137,10 +184,10 @@ __device__ __forceinline__ double encode_group(uint8_t* store, const Unit& u, co
 // group order.  When it encodes all 16 groups of the tile, the key planes
 // are staged in LDS and written as whole 64-byte lines (else word by word:
 // the tile's other groups are already stored).
-template <int DT>
+template <int DT, bool LL>
 __global__ __launch_bounds__(256) void k_encode_tiles(uint8_t* store, const void* knew,
                                                       const void* vnew, const int32_t* n_new,
-                                                      int n_max, int G, int W) {
+                                                      int n_max, int G, int W, const uint8_t* cb) {
   constexpr int esize = DT == 0 ? 2 : 4;
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const ReqRecord r = req_of(store, b);
@@ -157,10 +204,16 @@ __global__ __launch_bounds__(256) void k_encode_tiles(uint8_t* store, const void
   __shared__ double rv2[128];
   __shared__ __attribute__((aligned(16))) uint32_t vst[kGroup * 8 * 4];
   __shared__ __attribute__((aligned(16))) uint32_t kst[kDim * 8 * 16];
+  __shared__ double xs[LL ? 2 * kGroup * kDim : 1];
+  __shared__ double bnd[LL ? 256 : 1];
+  if constexpr (LL) {
+    const double* bsrc = reinterpret_cast<const double*>(cb + codec_layout(G, kDim).bounds);
+    bnd[threadIdx.x] = bsrc[threadIdx.x];  // read after encode_group's first barrier
+  }
   const Unit u = unit_of(store, r, g, G, kDim, W, esize);
   for (int64_t gam = g0; gam < g1; ++gam)
-    encode_group<DT>(store, u, knew, vnew, ((int64_t)b * G + g) * n_max, len0, gam, W, bad_s, rv2,
-                     vst, whole ? kst : nullptr);
+    encode_group<DT, LL>(store, u, knew, vnew, ((int64_t)b * G + g) * n_max, len0, gam, W, bad_s,
+                         rv2, vst, whole ? kst : nullptr, cb, g, G, xs, bnd);
   if (whole) {
     __syncthreads();
     uint4* dst = reinterpret_cast<uint4*>(u.kplanes + tile * kDim * W * 16);
@@ -236,16 +289,22 @@ __global__ __launch_bounds__(256) void k_tail_update(uint8_t* store, const void*
 // tokens into the tail.  The request's last block to finish (a ticket
 // counter in the request record's spare field, reset by that block)
 // publishes the new length, after every block has read the old one.
-template <int DT>
+template <int DT, bool LL>
 __global__ __launch_bounds__(256) void k_append_small(uint8_t* store, const void* knew,
                                                       const void* vnew, const int32_t* n_new,
-                                                      int n_max, int G, int W) {
+                                                      int n_max, int G, int W, const uint8_t* cb) {
   constexpr int esize = DT == 0 ? 2 : 4;
   const int g = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   __shared__ int bad_s[2];
   __shared__ double rv2[128];
   __shared__ __attribute__((aligned(16))) uint32_t vst[kGroup * 8 * 4];
   __shared__ int last_s;
+  __shared__ double xs[LL ? 2 * kGroup * kDim : 1];
+  __shared__ double bnd[LL ? 256 : 1];
+  if constexpr (LL) {
+    const double* bsrc = reinterpret_cast<const double*>(cb + codec_layout(G, kDim).bounds);
+    bnd[tid] = bsrc[tid];  // read after encode_group's first barrier
+  }
   ReqRecord* rp = reinterpret_cast<ReqRecord*>(store + 256 + 32 * (int64_t)b);
   const ReqRecord r = *rp;
   const int64_t want = n_new ? (int64_t)n_new[b] : (int64_t)n_max;
@@ -257,8 +316,9 @@ __global__ __launch_bounds__(256) void k_append_small(uint8_t* store, const void
   const Unit u = unit_of(store, r, g, G, kDim, W, esize);
   const int64_t row0 = ((int64_t)b * G + g) * n_max;
   for (int64_t gam = first; gam < last; ++gam) {
-    const double r2 = encode_group<DT>(store, u, knew, vnew, row0, len0, gam, W, bad_s, rv2, vst, nullptr);
-    if (tid < kDim) u.ek[tid] = u.ek[tid] + r2;
+    const double r2 = encode_group<DT, LL>(store, u, knew, vnew, row0, len0, gam, W, bad_s, rv2, vst,
+                                           nullptr, cb, g, G, xs, bnd);
+    if (!LL && tid < kDim) u.ek[tid] = u.ek[tid] + r2;
     __syncthreads();  // the group's tail rows are read before they are replaced
   }
   const int64_t per = (len1 - from) * kDim;
@@ -307,34 +367,33 @@ int launch_store_zero(void* store, size_t bytes, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-int launch_encode(const EncodeArgs& a, hipStream_t st) {
-  if (a.n_max <= 0) return 0;
+template <int DT, bool LL>
+static void launch_encode_t(const EncodeArgs& a, hipStream_t st) {
   if (a.n_max <= kSmallAppend) {
-    if (a.dtype == 0)
-      hipLaunchKernelGGL((k_append_small<0>), dim3(a.G, a.B), dim3(256), 0, st, (uint8_t*)a.store, a.knew,
-                         a.vnew, a.n_new, a.n_max, a.G, a.W);
-    else
-      hipLaunchKernelGGL((k_append_small<1>), dim3(a.G, a.B), dim3(256), 0, st, (uint8_t*)a.store, a.knew,
-                         a.vnew, a.n_new, a.n_max, a.G, a.W);
-    return hipGetLastError() == hipSuccess ? 0 : -6;
+    hipLaunchKernelGGL((k_append_small<DT, LL>), dim3(a.G, a.B), dim3(256), 0, st, (uint8_t*)a.store,
+                       a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W, a.cblock);
+    return;
   }
   // key tiles an append of n_max tokens can touch: its groups, plus one
   // for a start inside a tile
   const int max_tiles = (int)((a.n_max + kGroup - 1) / kGroup + 15) / 16 + 1;
-  if (a.dtype == 0) {
-    hipLaunchKernelGGL((k_encode_tiles<0>), dim3(max_tiles, a.G, a.B), dim3(256), 0, st,
-                       (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
-    hipLaunchKernelGGL((k_ek_update<0>), dim3(a.G, a.B), dim3(128), 0, st, (uint8_t*)a.store,
+  hipLaunchKernelGGL((k_encode_tiles<DT, LL>), dim3(max_tiles, a.G, a.B), dim3(256), 0, st,
+                     (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W, a.cblock);
+  if (!LL)
+    hipLaunchKernelGGL((k_ek_update<DT>), dim3(a.G, a.B), dim3(128), 0, st, (uint8_t*)a.store,
                        a.n_new, a.n_max, a.G, a.W);
-    hipLaunchKernelGGL((k_tail_update<0>), dim3(a.B), dim3(256), 0, st, (uint8_t*)a.store,
-                       a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
+  hipLaunchKernelGGL((k_tail_update<DT>), dim3(a.B), dim3(256), 0, st, (uint8_t*)a.store, a.knew,
+                     a.vnew, a.n_new, a.n_max, a.G, a.W);
+}
+
+int launch_encode(const EncodeArgs& a, hipStream_t st) {
+  if (a.n_max <= 0) return 0;
+  if (a.codec) {
+    if (a.dtype == 0) launch_encode_t<0, true>(a, st);
+    else launch_encode_t<1, true>(a, st);
   } else {
-    hipLaunchKernelGGL((k_encode_tiles<1>), dim3(max_tiles, a.G, a.B), dim3(256), 0, st,
-                       (uint8_t*)a.store, a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
-    hipLaunchKernelGGL((k_ek_update<1>), dim3(a.G, a.B), dim3(128), 0, st, (uint8_t*)a.store,
-                       a.n_new, a.n_max, a.G, a.W);
-    hipLaunchKernelGGL((k_tail_update<1>), dim3(a.B), dim3(256), 0, st, (uint8_t*)a.store,
-                       a.knew, a.vnew, a.n_new, a.n_max, a.G, a.W);
+    if (a.dtype == 0) launch_encode_t<0, false>(a, st);
+    else launch_encode_t<1, false>(a, st);
   }
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }

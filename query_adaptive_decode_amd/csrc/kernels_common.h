@@ -10,6 +10,10 @@
 
 namespace readkv {
 
+// 1/sqrt(128), the double nearest to it (the attention scale 1/sqrt(d_h) and
+// the Hadamard-sign transforms' normalisation)
+constexpr double kInvSqrt128 = 0.088388347648318440550;
+
 __device__ __forceinline__ const ReqRecord& req_of(const uint8_t* store, int b) {
   return *reinterpret_cast<const ReqRecord*>(store + 256 + 32 * (int64_t)b);
 }

@@ -1,9 +1,10 @@
 // Store and workspace layout shared by the host entry points and the kernels.
 //
-// Store = header + one region per request.  Header: 256 bytes of fields,
-// then one 32-byte record {len, cap, offset, ticket} per request (ticket:
-// the append's completion counter, zero between calls),
-// rounded up to 4096 bytes.  A request region with capacity `cap` tokens
+// Store = header + (Lloyd-tree code only) codec block + one region per
+// request.  Header: 256 bytes of fields, then one 32-byte record {len, cap,
+// offset, ticket} per request (ticket: the append's completion counter, zero
+// between calls), rounded up to 4096 bytes.  The codec block (see
+// codec_layout) follows the header.  A request region with capacity `cap` tokens
 // (multiple of 32, ng = cap/32 groups) holds, each sub-array 256-byte
 // aligned:
 //   Kplanes u32 [G][ntk][d][W][16] token-packed, tile-major: bit i of word
@@ -23,7 +24,8 @@
 //   Vtail   elem [G][32][d]
 // Plane p holds bit (W-1-p) of the code (most significant first), so a
 // depth-t read of a key channel is t whole lines and a depth-t read of a
-// value token is one contiguous run.
+// value token is one contiguous run.  Under the Lloyd-tree code the code is
+// the scalar's tree path and Kmeta, Vmeta, EK and EV are not used.
 #pragma once
 #include <stdint.h>
 
@@ -49,7 +51,8 @@ struct StoreHeader {          // first 256 bytes of a store
   int32_t W, d, H, G, group_tokens, B, kv_dtype;
   uint32_t flags;
   int64_t capacity, total_bytes;
-  int64_t reserved[25];
+  int32_t codec, reserved0;   // 0: uniform min/max code, 1: Lloyd tree
+  int64_t reserved[24];
 };
 static_assert(sizeof(StoreHeader) == 256, "header size");
 
@@ -60,6 +63,39 @@ struct ReqRecord {            // at byte 256 + 32*b
 RKV_HD int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
 RKV_HD int64_t header_bytes(int B) { return align_up(256 + 32 * (int64_t)B, 4096); }
+
+// Codec block of a Lloyd-tree store, at byte header_bytes(B):
+//   cent   f32 [512]     centroid of depth-t cell P at (2^t - 1) + P, t = 0..8
+//   bounds f64 [256]     boundary splitting depth-t cell P at (2^t - 1) + P,
+//                        t = 0..7 (midpoint of the float32 child centroids)
+//   gains  f64 [16]      gains[t] = Delta_t (float32 values), t = 1..8
+//   sk, sv f64 [d]       signs of the key and value Hadamard-sign transforms
+//   vtab   f16 [9][256]  vtab[t][X] = cent of depth-t cell X >> (8 - t)
+//                        (X = an 8-bit code with its bits past depth t zero)
+//   muk, sigk, muv, sigv f32 [G][d]   calibration means and scales
+//   sphys  f64 [G]       sum over channels of sigv^2, left to right
+constexpr int kTreeDepth = 8;
+struct CodecLayout {
+  int64_t cent, bounds, gains, sk, sv, vtab, muk, sigk, muv, sigv, sphys, size;
+};
+RKV_HD CodecLayout codec_layout(int G, int d) {
+  CodecLayout L;
+  int64_t off = 0;
+  L.cent = off; off += 512 * 4;
+  L.bounds = off; off += 256 * 8;
+  L.gains = off; off += 16 * 8;
+  L.sk = off; off += (int64_t)d * 8;
+  L.sv = off; off += (int64_t)d * 8;
+  L.vtab = off; off += 9 * 256 * 2; off = align_up(off, 256);
+  L.muk = off; off += (int64_t)G * d * 4;
+  L.sigk = off; off += (int64_t)G * d * 4;
+  L.muv = off; off += (int64_t)G * d * 4;
+  L.sigv = off; off += (int64_t)G * d * 4;
+  L.sphys = off; off += (int64_t)G * 8;
+  L.size = align_up(off, 4096);
+  return L;
+}
+RKV_HD int64_t codec_bytes(int codec, int G, int d) { return codec ? codec_layout(G, d).size : 0; }
 
 // 512-token tiles of the key planes (16 groups each)
 RKV_HD int64_t key_tiles(int64_t cap) { return (cap / kGroup + 15) / 16; }
@@ -128,8 +164,12 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 //                                 in the allocator's registers)
 //   opart  f32 [B][H][nchunk][d]  partial outputs, one per run of chunks
 //                                 (at most nchunk runs)
+//   Lloyd-tree code only:
+//   qp     f64 [B][H][d]          transformed query U_K q
+//   qb     f64 [B][H]             sum_c q'_c mu^K_c
+//   otail  f32 [B][H][d]          the open group's share of the output
 struct WsLayout {
-  int64_t tk, tv, ebuf, tilepart, ftile, aval, opart, size;
+  int64_t tk, tv, ebuf, tilepart, ftile, aval, opart, qp, qb, otail, size;
   int ntile, nchunk;
 };
 
@@ -145,6 +185,9 @@ RKV_HD WsLayout ws_layout(int B, int H, int G, int d, int64_t capmax) {
   L.ftile = off; off = align_up(off + (int64_t)B * H * L.ntile * 8, 256);
   L.aval = off; off = align_up(off + (int64_t)B * G * capmax * 8, 256);
   L.opart = off; off = align_up(off + (int64_t)B * H * L.nchunk * d * 4, 256);
+  L.qp = off; off = align_up(off + (int64_t)B * H * d * 8, 256);
+  L.qb = off; off = align_up(off + (int64_t)B * H * 8, 256);
+  L.otail = off; off = align_up(off + (int64_t)B * H * d * 4, 256);
   L.size = off;
   return L;
 }

@@ -17,6 +17,8 @@ struct EncodeArgs {
   const void* vnew;
   const int32_t* n_new;
   int n_max, B, G, W, dtype;
+  int codec;                 // 0: uniform min/max, 1: Lloyd tree
+  const uint8_t* cblock;     // the Lloyd-tree store's codec block (device)
 };
 
 struct DecodeArgs {
@@ -35,7 +37,24 @@ struct DecodeArgs {
   int B, H, G, W, dtype;
   int64_t capmax;
   void* const* events;  // NULL, or 4 hipEvent_t recorded around the 3 stages
+  int codec;            // 0: uniform min/max, 1: Lloyd tree
+  const uint8_t* cblock;  // the Lloyd-tree store's codec block (device)
 };
+
+// The Lloyd tree's float32 table ("Read What Matters", App. D.1), built on
+// the host once: cent[(2^t - 1) + P] (t = 0..8), bounds[(2^t - 1) + P]
+// (t = 0..7), gains[t] (t = 1..8).
+struct TreeTables {
+  float cent[512];
+  double bounds[256];
+  double gains[16];
+};
+const TreeTables& lloyd_tables();
+// codec.hip: the codec block of a new Lloyd-tree store (host image: tables,
+// signs +1, mean 0, scale 1), and the calibration launch.
+void codec_block_image(int G, uint8_t* img);
+int launch_calibrate(uint8_t* cblock, int G, int dtype, const void* kcal, const void* vcal,
+                     int64_t ncal, hipStream_t st);
 
 int launch_store_zero(void* store, size_t bytes, hipStream_t st);
 int launch_encode(const EncodeArgs& a, hipStream_t st);
@@ -48,5 +67,6 @@ struct Part {
 int launch_key_alloc(const DecodeArgs& a, const Part& P, uint8_t* tk, hipStream_t st);
 int launch_value_alloc(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
                        uint8_t* tv, hipStream_t st);
+int launch_key_alloc_lloyd(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, hipStream_t st);
 
 }  // namespace readkv

@@ -7,16 +7,32 @@ import numpy as np
 import torch
 
 from . import synth
-from .binding import BF16, F32, make_config
+from .binding import BF16, CODEC_LLOYD, CODEC_UNIFORM, F32, make_config
 
 
 def config_for(cfg: dict, steps: int | None = None):
-    """Library config for a workload: capacity = longest prefill + steps."""
+    """Library config for a workload: capacity = longest prefill + steps.
+    ``cfg["codec"] == "lloyd"`` selects the Lloyd-tree code."""
     steps = cfg["steps"] if steps is None else steps
     cap = int(synth.context_lengths(cfg).max()) + int(steps)
     return make_config(W=cfg["W"], head_dim=cfg["d"], num_q_heads=cfg["H"],
                        num_kv_heads=cfg["G"], batch=cfg["B"], capacity_tokens=cap,
-                       kv_dtype=BF16 if cfg["dtype"] == "bf16" else F32)
+                       kv_dtype=BF16 if cfg["dtype"] == "bf16" else F32,
+                       codec=CODEC_LLOYD if cfg.get("codec") == "lloyd" else CODEC_UNIFORM)
+
+
+def calibration_inputs(cfg: dict, n: int):
+    """The Lloyd code's inputs in upload form: (signs_k, signs_v) int8 [d]
+    and the calibration split kcal, vcal [n][G][d]."""
+    sk, sv = synth.codec_signs(cfg)
+    edt = np.uint16 if cfg["dtype"] == "bf16" else np.float32
+    kc = np.zeros((n, cfg["G"], cfg["d"]), dtype=edt)
+    vc = np.zeros((n, cfg["G"], cfg["d"]), dtype=edt)
+    for g in range(cfg["G"]):
+        K, V = synth.calibration_split(cfg, g, n)
+        kc[:, g] = synth.to_device_bits(cfg, K)
+        vc[:, g] = synth.to_device_bits(cfg, V)
+    return dict(sk=sk, sv=sv, kcal=kc, vcal=vc)
 
 
 def host_inputs(cfg: dict, steps: int | None = None) -> dict:
