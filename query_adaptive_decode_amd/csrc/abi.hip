@@ -129,7 +129,7 @@ int readkv_workspace_bytes(const readkv_config* cfg, size_t* bytes) {
   if (rc) return rc;
   if (!bytes) return READKV_EINVAL;
   const WsLayout L = ws_layout(cfg->batch, cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim,
-                               capmax_of(cfg));
+                               capmax_of(cfg), cfg->codec);
   *bytes = (size_t)L.size;
   return READKV_OK;
 }
@@ -236,7 +236,6 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   if (vscale != READKV_VSCALE_PHYSICAL && vscale != READKV_VSCALE_UNIT) return READKV_EINVAL;
   if (policy & ~(READKV_SCOPE_LAYER | READKV_RESTRICT_MIN_DEPTH1 | READKV_RESTRICT_VALUE_PAIRS))
     return READKV_EINVAL;
-  if (cfg->codec == READKV_CODEC_LLOYD) return READKV_EUNSUPPORTED;
   const int scope = policy & READKV_SCOPE_LAYER;
   if (scope == READKV_SCOPE_LAYER && cfg->num_kv_heads > kMaxPooledKV) return READKV_EUNSUPPORTED;
   // budgets must fit the 32-bit counters: R * (items of a domain) <= 2^31
@@ -246,7 +245,7 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
     return READKV_EINVAL;
   const int64_t capmax = capmax_of(cfg);
   const WsLayout L = ws_layout(cfg->batch, cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim,
-                               capmax);
+                               capmax, cfg->codec);
   if ((int64_t)workspace_bytes < L.size) return READKV_EWORKSPACE;
   DecodeArgs a;
   a.store = store;
@@ -303,7 +302,7 @@ int readkv_decode_attn_noalloc(const readkv_config* cfg, const void* store, cons
   int rc = readkv_validate_config(cfg);
   if (rc) return rc;
   const WsLayout L = ws_layout(cfg->batch, cfg->num_q_heads, cfg->num_kv_heads, cfg->head_dim,
-                               capmax_of(cfg));
+                               capmax_of(cfg), cfg->codec);
   if ((size_t)L.size > kScratchBytes) return READKV_ESCRATCH;
   void* ws = nullptr;
   if ((rc = scratch_of_current_device(&ws))) return rc;

@@ -77,6 +77,99 @@ __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0
 }
 
 // ---------------------------------------------------------------------------
+// Key allocation under the Lloyd-tree code ([ReadKV] Sec. 3.1-3.2), one
+// block per selection domain (a unit, or a request's NU = G KV heads under
+// per-layer budgets).  Per KV head: the query heads' rows q' = U_K q
+// (Walsh-Hadamard butterflies over the block in fp64, times 1/sqrt(d)),
+// written to the workspace with qb_h = sum_c q'_hc mu^K_c (channel order);
+// weights w_c = sum_h (q'_hc sigma^K_c)^2 in head order (Eq. (2)); then
+// ChooseDepths with the tree's gains Delta_t.  A KV head with a non-finite
+// query value gets zero weights and qb = NaN (the score reads nothing for
+// it).  Block 0 zeroes the call's read counters.
+// ---------------------------------------------------------------------------
+template <int GQA, int DT, int NUMAX>
+__global__ __launch_bounds__(256) void k_key_alloc_lloyd(const uint8_t* cb, const void* q, int H,
+                                                         int G, int W, float RK, int NU, int min1,
+                                                         uint8_t* tk, double* qp, double* qb,
+                                                         uint64_t* counters) {
+  constexpr int NT = 256;
+  constexpr int PER = (GQA * kDim + NT - 1) / NT;
+  __shared__ ChooseShared<NT> S;
+  __shared__ double wl[NUMAX * kDim];
+  __shared__ double xb[GQA * kDim];
+  __shared__ double gt[16];
+  const CodecLayout C = codec_layout(G, kDim);
+  const int tid = threadIdx.x;
+  if (counters && blockIdx.x == 0 && tid < 4) counters[tid] = 0ull;
+  const int u0 = (int)blockIdx.x * NU;
+  const int b = u0 / G, g0 = u0 % G;
+  if (tid < 16) gt[tid] = reinterpret_cast<const double*>(cb + C.gains)[tid];
+  const double* sk = reinterpret_cast<const double*>(cb + C.sk);
+  for (int k = 0; k < NU; ++k) {
+    const int g = g0 + k;
+    const int64_t hrow = (int64_t)b * H + (int64_t)g * GQA;
+    int nf = 0;
+    for (int i = tid; i < GQA * kDim; i += NT) {
+      const double v = load_elem<DT>(q, hrow * kDim + i);
+      nf |= !isfinite(v);
+      xb[i] = v * sk[i % kDim];
+    }
+    nf = __syncthreads_or(nf);
+    for (int h = 1; h < kDim; h <<= 1) {
+      double y[PER];
+#pragma unroll
+      for (int n = 0; n < PER; ++n) {
+        const int i = tid + n * NT;
+        if (i < GQA * kDim) {
+          const double a = xb[i], o = xb[i ^ h];  // (h < d: the partner is in the same row)
+          y[n] = (i & h) ? o - a : a + o;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int n = 0; n < PER; ++n) {
+        const int i = tid + n * NT;
+        if (i < GQA * kDim) xb[i] = y[n];
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < GQA * kDim; i += NT) {
+      const double v = __dmul_rn(xb[i], kInvSqrt128);
+      xb[i] = v;
+      qp[hrow * kDim + i] = v;
+    }
+    __syncthreads();
+    if (tid < kDim) {
+      const int c = tid;
+      const double sg = (double)reinterpret_cast<const float*>(cb + C.sigk)[g * kDim + c];
+      double a = 0.0;
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) {
+        const double x = __dmul_rn(xb[hh * kDim + c], sg);
+        a = __dadd_rn(a, __dmul_rn(x, x));
+      }
+      wl[k * kDim + c] = nf ? 0.0 : a;
+    } else if (tid < kDim + GQA) {
+      const int hh = tid - kDim;
+      const float* mu = reinterpret_cast<const float*>(cb + C.muk) + g * kDim;
+      double sacc = 0.0;
+      for (int c = 0; c < kDim; ++c) sacc = __dadd_rn(sacc, __dmul_rn(xb[hh * kDim + c], (double)mu[c]));
+      qb[hrow + hh] = nf ? __builtin_nan("") : sacc;
+    }
+    __syncthreads();
+  }
+  const int N = NU * kDim;
+  uint32_t Bk = (uint32_t)floor((double)RK * (double)N);
+  if (min1) Bk = Bk > (uint32_t)N ? Bk - (uint32_t)N : 0u;
+  uint8_t* const tkd = tk + (int64_t)u0 * kDim;
+  // the minimum depth one: levels 2..W, i.e. the table from Delta_2 on
+  block_choose_depths<NT>(
+      N, Bk, W - min1, [&](int64_t i) { return wl[i]; },
+      [&](int64_t i, uint32_t t) { tkd[i] = (uint8_t)(t + (uint32_t)min1); }, S,
+      TableGains{gt + min1});
+}
+
+// ---------------------------------------------------------------------------
 // Value weights.  Block (unit, y) takes tokens [1024 y, 1024 y + 1024) of the
 // unit (four score tiles); thread t takes tokens 4t .. 4t + 3 of the chunk.
 //   m_h = max_tile m_tile, Z_h = sum_tile z_tile exp(m_tile - m_h)
@@ -89,12 +182,12 @@ __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0
 // ---------------------------------------------------------------------------
 constexpr int kVChunk = 1024;
 
-template <int GQA>
+template <int GQA, bool LL>
 __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int ub0, int H, int G, int W,
                                                        int esize, int vscale, int64_t capmax,
                                                        int ntile_ws, const uint32_t* ebuf,
                                                        const double* tilepart, double* ftile,
-                                                       double* aval) {
+                                                       double* aval, const uint8_t* cb) {
   constexpr int TPC = kVChunk / kTile;  // score tiles per chunk
   static_assert(kVChunk == 4 * 256, "four tokens per thread");
   __shared__ double fs[GQA][TPC];
@@ -115,11 +208,23 @@ __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int
   const bool act = j0 < Tp;  // Tp is a multiple of 32: all four tokens or none
   const int64_t jc = act ? j0 : 0;
   uint4 ev[GQA];
+  double2 ld[GQA][2];  // Lloyd code: the logits of the four tokens
 #pragma unroll
-  for (int hh = 0; hh < GQA; ++hh)
-    ev[hh] = *reinterpret_cast<const uint4*>(ebuf + (hrow0 + hh) * capmax + jc);
+  for (int hh = 0; hh < GQA; ++hh) {
+    if constexpr (LL) {
+      const double2* lp = reinterpret_cast<const double2*>(
+          reinterpret_cast<const double*>(ebuf) + (hrow0 + hh) * capmax + jc);
+      ld[hh][0] = lp[0];
+      ld[hh][1] = lp[1];
+    } else {
+      ev[hh] = *reinterpret_cast<const uint4*>(ebuf + (hrow0 + hh) * capmax + jc);
+    }
+  }
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  const double sg = vscale == 0 ? u.ev[jc / kGroup] : 1.0;
+  const double sg = vscale != 0 ? 1.0
+                    : LL ? reinterpret_cast<const double*>(cb + codec_layout(G, kDim).sphys)[g]
+                         : u.ev[jc / kGroup];
+  __shared__ double mh[GQA], zh[GQA];
   for (int hh = wv; hh < GQA; hh += 4) {
     const double* tp = tilepart + (hrow0 + hh) * ntile_ws * 2;
     double m = -INFINITY;
@@ -128,6 +233,10 @@ __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int
     double Z = 0.0;
     for (int t = lane; t < ntile_b; t += 64) Z += tp[2 * t + 1] * exp(tp[2 * t] - m);
     Z = wave_sum(Z);
+    if (lane == 0) {
+      mh[hh] = m;
+      zh[hh] = Z;
+    }
     if (lane < TPC && t0 + lane < ntile_b) {
       const double f = exp(tp[2 * (t0 + lane)] - m) / Z;
       fs[hh][lane] = f;
@@ -140,12 +249,22 @@ __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int
   double s[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int hh = 0; hh < GQA; ++hh) {
-    const double f = fs[hh][tl];
-    const uint32_t e4[4] = {ev[hh].x, ev[hh].y, ev[hh].z, ev[hh].w};
+    if constexpr (LL) {
+      // alpha = exp(s - m) / Z from the logit: equal logits, equal weights
+      const double lg[4] = {ld[hh][0].x, ld[hh][0].y, ld[hh][1].x, ld[hh][1].y};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const double x = __dmul_rn(dec_e(e4[k]), f);
-      s[k] = __dadd_rn(s[k], __dmul_rn(x, x));
+      for (int k = 0; k < 4; ++k) {
+        const double x = __ddiv_rn(exp_nonpos(lg[k] - mh[hh]), zh[hh]);
+        s[k] = __dadd_rn(s[k], __dmul_rn(x, x));
+      }
+    } else {
+      const double f = fs[hh][tl];
+      const uint32_t e4[4] = {ev[hh].x, ev[hh].y, ev[hh].z, ev[hh].w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const double x = __dmul_rn(dec_e(e4[k]), f);
+        s[k] = __dadd_rn(s[k], __dmul_rn(x, x));
+      }
     }
   }
   if (vscale == 0) {
@@ -166,18 +285,30 @@ __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int
 // E^K, E^V), the open group's keys and values.
 // ---------------------------------------------------------------------------
 constexpr int kVSelNT = 1024;
+
+// Lloyd code: one load per call of the layer's calibration arrays (mu and
+// sigma of keys and values, 32 bits per KV head and channel), charged to the
+// first request's domains, and of the decoder table (510 centroids and 8
+// gains, 32 bits each), charged to the first domain ([ReadKV] App. A.1).
+__device__ __forceinline__ unsigned long long lloyd_meta_bits(bool first_request, bool first_domain,
+                                                              unsigned long long nu) {
+  return (first_request ? nu * 4ull * kDim * 32ull : 0ull) + (first_domain ? 518ull * 32ull : 0ull);
+}
 // domains of up to this many tokens are copied to LDS once (8 bytes each)
 constexpr int kVSelLocal = 16384;
 
-template <bool LOCAL>
+template <bool LOCAL, bool LL>
 __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, int ub0, int G, int W,
                                                           int esize, float RV, int NU, int min1,
                                                           int pairs,
                                                           int64_t capmax, const double* aval,
                                                           uint8_t* tv, const uint8_t* tk,
-                                                          uint64_t* counters) {
+                                                          uint64_t* counters, const uint8_t* cb) {
   constexpr int NT = kVSelNT;
   __shared__ ChooseShared<NT> S;
+  __shared__ double gt[16];
+  if (LL && threadIdx.x < 16)
+    gt[threadIdx.x] = reinterpret_cast<const double*>(cb + codec_layout(G, kDim).gains)[threadIdx.x];
   const int tid = threadIdx.x, lane = tid & 63;
   const int u0 = ub0 + (int)blockIdx.x * NU;
   const int b = u0 / G;
@@ -198,7 +329,7 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
   uint32_t Bv = (uint32_t)floor((double)RV * (double)NT_);
   if (pairs) Bv /= 2u;
   if (min1) Bv = (int64_t)Bv > N ? Bv - (uint32_t)N : 0u;
-  const double sc = min1 ? 0.25 : 1.0;
+  const double sc = (min1 && !LL) ? 0.25 : 1.0;
   uint32_t mine = 0;  // this thread's token depths
   auto put = [&](int64_t i, uint32_t t) {
     t += (uint32_t)min1;
@@ -212,6 +343,14 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
     }
   };
   extern __shared__ double acache[];  // [tokens] when LOCAL
+  auto select = [&](auto&& geta) {
+    if constexpr (LL) {
+      __syncthreads();  // gt
+      block_choose_depths<NT>(N, Bv, W - min1, geta, put, S, TableGains{gt + min1});
+    } else {
+      block_choose_depths<NT>(N, Bv, W - min1, geta, put, S);
+    }
+  };
   if constexpr (LOCAL) {
     // eight loads in flight per thread, then their LDS stores
     for (int64_t i0 = 0; i0 < NT_; i0 += 8 * NT) {
@@ -228,19 +367,13 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
       }
     }
     __syncthreads();
-    block_choose_depths<NT>(
-        N, Bv, W - min1,
-        [&](int64_t i) {
-          return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc;
-        },
-        put, S);
+    select([&](int64_t i) {
+      return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc;
+    });
   } else {
-    block_choose_depths<NT>(
-        N, Bv, W - min1,
-        [&](int64_t i) {
-          return (pairs ? __dadd_rn(ab[at(2 * i)], ab[at(2 * i + 1)]) : ab[at(i)]) * sc;
-        },
-        put, S);
+    select([&](int64_t i) {
+      return (pairs ? __dadd_rn(ab[at(2 * i)], ab[at(2 * i + 1)]) : ab[at(i)]) * sc;
+    });
   }
   if (counters) {
     const uint32_t vtot = block_sum_u32<NT>(mine, S.wsum);
@@ -252,8 +385,10 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
         const unsigned long long ng = (unsigned long long)(Tp / kGroup), nu = (unsigned long long)NU;
         atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
         atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1), (unsigned long long)vtot * kDim);
-        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2),
-                  nu * (2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull));
+        const unsigned long long meta =
+            LL ? lloyd_meta_bits(b == 0, u0 == 0, nu)
+               : nu * (2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2), meta);
         atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
                   nu * 2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
       }
@@ -270,15 +405,16 @@ __global__ __launch_bounds__(kVSelNT) void k_value_select(const uint8_t* store, 
 // 4t .. 4t + 3 of each round of 4096; the first round's exponentials are in
 // flight while the statistics are formed.
 // ---------------------------------------------------------------------------
-template <int GQA>
+template <int GQA, bool LL>
 __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
     const uint8_t* store, int ub0, int H, int G, int W, int esize, int vscale, float RV, int min1,
     int pairs, int64_t capmax,
     int ntile_ws, const uint32_t* ebuf, const double* tilepart, double* ftile, uint8_t* tv,
-    const uint8_t* tk, uint64_t* counters) {
+    const uint8_t* tk, uint64_t* counters, const uint8_t* cb) {
   constexpr int NT = kVSelNT;
   constexpr int RT = 4 * NT;  // tokens per round
   __shared__ ChooseShared<NT> S;
+  __shared__ double gt[16];
   __shared__ double fs[GQA][kVSelLocal / kTile];
   extern __shared__ double acache[];  // [T_p]
   const int ux = ub0 + (int)blockIdx.x;
@@ -290,17 +426,34 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
   const int64_t Tp = len & ~(int64_t)(kGroup - 1);
   const int ntile_b = (int)((len + kTile - 1) / kTile);
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
-  auto load_round = [&](int k, uint4 (&ev)[GQA], double& sg) __attribute__((always_inline)) {
+  // Lloyd code: one scale per KV head, the tree's gains
+  const double sg_ll = LL && vscale == 0
+                           ? reinterpret_cast<const double*>(cb + codec_layout(G, kDim).sphys)[g]
+                           : 1.0;
+  if (LL && tid < 16) gt[tid] = reinterpret_cast<const double*>(cb + codec_layout(G, kDim).gains)[tid];
+  // the four tokens' exponentials (uniform code) or logits (Lloyd code)
+  auto load_round = [&](int k, uint4 (&ev)[GQA], double2 (&ld)[GQA][2], double& sg)
+                        __attribute__((always_inline)) {
     const int64_t j0 = (int64_t)k * RT + 4 * tid;
     const int64_t jc = j0 < Tp ? j0 : 0;  // (a thread past the tokens loads token 0's)
 #pragma unroll
-    for (int hh = 0; hh < GQA; ++hh)
-      ev[hh] = *reinterpret_cast<const uint4*>(ebuf + (hrow0 + hh) * capmax + jc);
-    sg = vscale == 0 ? u.ev[jc / kGroup] : 1.0;
+    for (int hh = 0; hh < GQA; ++hh) {
+      if constexpr (LL) {
+        const double2* lp = reinterpret_cast<const double2*>(
+            reinterpret_cast<const double*>(ebuf) + (hrow0 + hh) * capmax + jc);
+        ld[hh][0] = lp[0];
+        ld[hh][1] = lp[1];
+      } else {
+        ev[hh] = *reinterpret_cast<const uint4*>(ebuf + (hrow0 + hh) * capmax + jc);
+      }
+    }
+    sg = LL ? sg_ll : vscale == 0 ? u.ev[jc / kGroup] : 1.0;
   };
   uint4 ev[GQA];
+  double2 ld[GQA][2];
   double sg;
-  load_round(0, ev, sg);
+  __shared__ double mh[GQA], zh[GQA];
+  load_round(0, ev, ld, sg);
   choose_clear<NT>(S);  // while the first round's exponentials are in flight
   for (int hh = wv; hh < GQA; hh += NT / 64) {
     const double* tp = tilepart + (hrow0 + hh) * ntile_ws * 2;
@@ -310,6 +463,10 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
     const double m = wave_max(mt);
     const double x = lane < ntile_b ? exp(mt - m) : 0.0;
     const double Z = wave_sum(zt * x);
+    if (lane == 0) {
+      mh[hh] = m;
+      zh[hh] = Z;
+    }
     if (lane < ntile_b) {
       const double f = x / Z;
       fs[hh][lane] = f;
@@ -322,24 +479,39 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
   // selection's histograms are built here from the weights in registers, in
   // exactly the form the selection reads them back from LDS.
   const int64_t N = pairs ? Tp / 2 : Tp;
-  const double sc = min1 ? 0.25 : 1.0;
+  const double sc = (min1 && !LL) ? 0.25 : 1.0;
   const int Wc = W - min1;
   ChooseLocal CL;
+  const TableGains tg{gt + min1};
+  auto add = [&](double a) __attribute__((always_inline)) {
+    if constexpr (LL) choose_add<NT>(a, Wc, S, CL, tg);
+    else choose_add<NT>(a, Wc, S, CL);
+  };
   const int nr = (int)((Tp + RT - 1) / RT);
   for (int k = 0; k < nr; ++k) {
-    if (k > 0) load_round(k, ev, sg);
+    if (k > 0) load_round(k, ev, ld, sg);
     const int64_t j0 = (int64_t)k * RT + 4 * tid;
     if (j0 < Tp) {  // Tp is a multiple of 32: all four tokens or none
       const int tl = (int)(j0 / kTile);
       double sa[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) {
-        const double f = fs[hh][tl];
-        const uint32_t e4[4] = {ev[hh].x, ev[hh].y, ev[hh].z, ev[hh].w};
+        if constexpr (LL) {
+          // alpha = exp(s - m) / Z from the logit: equal logits, equal weights
+          const double lg[4] = {ld[hh][0].x, ld[hh][0].y, ld[hh][1].x, ld[hh][1].y};
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const double xq = __dmul_rn(dec_e(e4[q]), f);
-          sa[q] = __dadd_rn(sa[q], __dmul_rn(xq, xq));
+          for (int q = 0; q < 4; ++q) {
+            const double xq = __ddiv_rn(exp_nonpos(lg[q] - mh[hh]), zh[hh]);
+            sa[q] = __dadd_rn(sa[q], __dmul_rn(xq, xq));
+          }
+        } else {
+          const double f = fs[hh][tl];
+          const uint32_t e4[4] = {ev[hh].x, ev[hh].y, ev[hh].z, ev[hh].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const double xq = __dmul_rn(dec_e(e4[q]), f);
+            sa[q] = __dadd_rn(sa[q], __dmul_rn(xq, xq));
+          }
         }
       }
 #pragma unroll
@@ -348,11 +520,11 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
         acache[j0 + q] = sa[q];
       }
       if (pairs) {
-        choose_add<NT>(__dadd_rn(sa[0], sa[1]) * sc, Wc, S, CL);
-        choose_add<NT>(__dadd_rn(sa[2], sa[3]) * sc, Wc, S, CL);
+        add(__dadd_rn(sa[0], sa[1]) * sc);
+        add(__dadd_rn(sa[2], sa[3]) * sc);
       } else {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) choose_add<NT>(sa[q] * sc, Wc, S, CL);
+        for (int q = 0; q < 4; ++q) add(sa[q] * sc);
       }
     }
   }
@@ -363,21 +535,22 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
   if (min1) Bv = (int64_t)Bv > N ? Bv - (uint32_t)N : 0u;
   uint8_t* const tvb = tv + ((int64_t)b * G + g) * capmax;
   uint32_t mine = 0;  // this thread's token depths
-  block_choose_depths_hist<NT>(
-      N, Bv, Wc,
-      [&](int64_t i) { return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc; },
-      [&](int64_t i, uint32_t t) {
-        t += (uint32_t)min1;
-        if (pairs) {
-          tvb[2 * i] = (uint8_t)t;
-          tvb[2 * i + 1] = (uint8_t)t;
-          mine += 2 * t;
-        } else {
-          tvb[i] = (uint8_t)t;
-          mine += t;
-        }
-      },
-      S);
+  auto geta = [&](int64_t i) {
+    return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc;
+  };
+  auto put = [&](int64_t i, uint32_t t) {
+    t += (uint32_t)min1;
+    if (pairs) {
+      tvb[2 * i] = (uint8_t)t;
+      tvb[2 * i + 1] = (uint8_t)t;
+      mine += 2 * t;
+    } else {
+      tvb[i] = (uint8_t)t;
+      mine += t;
+    }
+  };
+  if constexpr (LL) block_choose_depths_hist<NT>(N, Bv, Wc, geta, put, S, tg);
+  else block_choose_depths_hist<NT>(N, Bv, Wc, geta, put, S);
   if (counters) {
     const uint32_t vtot = block_sum_u32<NT>(mine, S.wsum);
     if (tid < 64) {
@@ -387,8 +560,9 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
         const unsigned long long ng = (unsigned long long)(Tp / kGroup);
         atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
         atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1), (unsigned long long)vtot * kDim);
-        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2),
-                  2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull);
+        const unsigned long long meta = LL ? lloyd_meta_bits(b == 0, ux == 0, 1ull)
+                                           : 2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull;
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2), meta);
         atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
                   2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
       }
@@ -423,45 +597,79 @@ int launch_key_alloc(const DecodeArgs& a, const Part& P, uint8_t* tk, hipStream_
   return a.dtype == 0 ? key_alloc_dt<0>(a, P, tk, st) : key_alloc_dt<1>(a, P, tk, st);
 }
 
+template <int GQA, int DT>
+static void key_alloc_lloyd_gqa(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, hipStream_t st) {
+  const int NU = a.scope == 1 ? a.G : 1;
+  const int nd = a.B * a.G / NU;
+  if (NU > 1)
+    hipLaunchKernelGGL((k_key_alloc_lloyd<GQA, DT, kMaxPooledKV>), dim3(nd), dim3(256), 0, st, a.cblock,
+                       a.q, a.H, a.G, a.W, a.RK, NU, a.min1, tk, (double*)(a.ws + L.qp),
+                       (double*)(a.ws + L.qb), a.counters);
+  else
+    hipLaunchKernelGGL((k_key_alloc_lloyd<GQA, DT, 1>), dim3(nd), dim3(256), 0, st, a.cblock, a.q,
+                       a.H, a.G, a.W, a.RK, NU, a.min1, tk, (double*)(a.ws + L.qp),
+                       (double*)(a.ws + L.qb), a.counters);
+}
+
+template <int DT>
+static int key_alloc_lloyd_dt(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, hipStream_t st) {
+  switch (a.H / a.G) {
+    case 1: key_alloc_lloyd_gqa<1, DT>(a, L, tk, st); return 0;
+    case 2: key_alloc_lloyd_gqa<2, DT>(a, L, tk, st); return 0;
+    case 3: key_alloc_lloyd_gqa<3, DT>(a, L, tk, st); return 0;
+    case 4: key_alloc_lloyd_gqa<4, DT>(a, L, tk, st); return 0;
+    case 5: key_alloc_lloyd_gqa<5, DT>(a, L, tk, st); return 0;
+    case 6: key_alloc_lloyd_gqa<6, DT>(a, L, tk, st); return 0;
+    case 7: key_alloc_lloyd_gqa<7, DT>(a, L, tk, st); return 0;
+    case 8: key_alloc_lloyd_gqa<8, DT>(a, L, tk, st); return 0;
+    default: return -5;
+  }
+}
+
+int launch_key_alloc_lloyd(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, hipStream_t st) {
+  return a.dtype == 0 ? key_alloc_lloyd_dt<0>(a, L, tk, st) : key_alloc_lloyd_dt<1>(a, L, tk, st);
+}
+
 // per-KV-head budgets and a capacity that fits LDS: one fused launch;
 // otherwise value weights (all compute units) then the selection
-template <int GQA>
+template <int GQA, bool LL>
 static bool value_first_gqa(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
                             uint8_t* tv, hipStream_t st) {
   if (a.scope == 0 && a.capmax <= kVSelLocal) {
     static bool attr_set = false;
     if (!attr_set) {
-      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_value_alloc_unit<GQA>),
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&k_value_alloc_unit<GQA, LL>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, kVSelLocal * 8);
       attr_set = true;
     }
-    hipLaunchKernelGGL((k_value_alloc_unit<GQA>), dim3(P.nunits), dim3(kVSelNT), (size_t)a.capmax * 8,
+    hipLaunchKernelGGL((k_value_alloc_unit<GQA, LL>), dim3(P.nunits), dim3(kVSelNT), (size_t)a.capmax * 8,
                        st, (const uint8_t*)a.store, P.ub0, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.RV,
                        a.min1, a.pairs, a.capmax, L.ntile, (const uint32_t*)(a.ws + L.ebuf),
                        (const double*)(a.ws + L.tilepart), (double*)(a.ws + L.ftile), tv, tk,
-                       a.counters);
+                       a.counters, a.cblock);
     return true;
   }
   const int nch = (int)((a.capmax + kVChunk - 1) / kVChunk);
-  hipLaunchKernelGGL((k_value_weights<GQA>), dim3(P.nunits, nch), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_value_weights<GQA, LL>), dim3(P.nunits, nch), dim3(256), 0, st,
                      (const uint8_t*)a.store, P.ub0, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.capmax,
                      L.ntile, (const uint32_t*)(a.ws + L.ebuf), (const double*)(a.ws + L.tilepart),
-                     (double*)(a.ws + L.ftile), (double*)(a.ws + L.aval));
+                     (double*)(a.ws + L.ftile), (double*)(a.ws + L.aval), a.cblock);
   return false;
 }
 
-int launch_value_alloc(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
-                       uint8_t* tv, hipStream_t st) {
+template <bool LL>
+static int launch_value_alloc_t(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
+                                uint8_t* tv, hipStream_t st) {
   bool done;
   switch (a.H / a.G) {
-    case 1: done = value_first_gqa<1>(a, P, L, tk, tv, st); break;
-    case 2: done = value_first_gqa<2>(a, P, L, tk, tv, st); break;
-    case 3: done = value_first_gqa<3>(a, P, L, tk, tv, st); break;
-    case 4: done = value_first_gqa<4>(a, P, L, tk, tv, st); break;
-    case 5: done = value_first_gqa<5>(a, P, L, tk, tv, st); break;
-    case 6: done = value_first_gqa<6>(a, P, L, tk, tv, st); break;
-    case 7: done = value_first_gqa<7>(a, P, L, tk, tv, st); break;
-    case 8: done = value_first_gqa<8>(a, P, L, tk, tv, st); break;
+    case 1: done = value_first_gqa<1, LL>(a, P, L, tk, tv, st); break;
+    case 2: done = value_first_gqa<2, LL>(a, P, L, tk, tv, st); break;
+    case 3: done = value_first_gqa<3, LL>(a, P, L, tk, tv, st); break;
+    case 4: done = value_first_gqa<4, LL>(a, P, L, tk, tv, st); break;
+    case 5: done = value_first_gqa<5, LL>(a, P, L, tk, tv, st); break;
+    case 6: done = value_first_gqa<6, LL>(a, P, L, tk, tv, st); break;
+    case 7: done = value_first_gqa<7, LL>(a, P, L, tk, tv, st); break;
+    case 8: done = value_first_gqa<8, LL>(a, P, L, tk, tv, st); break;
     default: return -5;
   }
   if (done) return 0;
@@ -470,16 +678,23 @@ int launch_value_alloc(const DecodeArgs& a, const Part& P, const WsLayout& L, co
   const bool local = nmax <= kVSelLocal;
   static bool attr_set = false;
   if (!attr_set) {
-    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_value_select<true>),
+    hipFuncSetAttribute(reinterpret_cast<const void*>(&k_value_select<true, LL>),
                         hipFuncAttributeMaxDynamicSharedMemorySize, kVSelLocal * 8);
     attr_set = true;
   }
-  hipLaunchKernelGGL(local ? &k_value_select<true> : &k_value_select<false>, dim3(P.nunits / NU),
+  auto* const ksel = local ? &k_value_select<true, LL> : &k_value_select<false, LL>;
+  hipLaunchKernelGGL(ksel, dim3(P.nunits / NU),
                      dim3(kVSelNT), local ? (size_t)nmax * 8 : 0, st,
                      (const uint8_t*)a.store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4, a.RV, NU, a.min1,
                      a.pairs, a.capmax,
-                     (const double*)(a.ws + L.aval), tv, tk, a.counters);
+                     (const double*)(a.ws + L.aval), tv, tk, a.counters, a.cblock);
   return 0;
+}
+
+int launch_value_alloc(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
+                       uint8_t* tv, hipStream_t st) {
+  return a.codec ? launch_value_alloc_t<true>(a, P, L, tk, tv, st)
+                 : launch_value_alloc_t<false>(a, P, L, tk, tv, st);
 }
 
 }  // namespace readkv

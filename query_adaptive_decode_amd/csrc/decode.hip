@@ -307,29 +307,6 @@ __device__ __forceinline__ void set_progress_priority(int done, int total) {
   }
 }
 
-// e^x for x <= 0 (or -inf), relative error below 1e-9.  Cody-Waite range
-// reduction x = k ln2 + r (k = rint(x / ln2), ln2 in two parts, so r is
-// exact to ~1e-17 and |r| <= ln2 / 2), then
-//   e^r = 1 + r + r^2 (1/2 + r P(r)),  P(r) = sum_{i>=0} r^i / (i + 3)!
-// with P's Taylor polynomial (degree 5: truncation r^9 / 9! below 3e-10) evaluated
-// in fp32: its rounding error, weighted by |r|^3 <= 0.042, stays below
-// 1e-9 of the result.  Then the exact scaling 2^k.
-__device__ __forceinline__ double exp_nonpos(double x) {
-  const double xc = fmax(x, -745.0);
-  const double k = rint(xc * 1.4426950408889634074);
-  const double r = fma(k, -1.9082149292705877000e-10, fma(k, -6.9314718036912381649e-01, xc));
-  const float rf = (float)r;
-  float pp = 2.4801587e-05f;                 // 1/8!
-  pp = fmaf(pp, rf, 1.9841270e-04f);         // 1/7!
-  pp = fmaf(pp, rf, 1.3888889e-03f);         // 1/6!
-  pp = fmaf(pp, rf, 8.3333333e-03f);         // 1/5!
-  pp = fmaf(pp, rf, 4.1666668e-02f);         // 1/4!
-  pp = fmaf(pp, rf, 1.6666667e-01f);         // 1/3!
-  const double e = fma(r * r, fma(r, (double)pp, 0.5), 1.0 + r);
-  const double v = ldexp(e, (int)k);
-  return x > -745.0 ? v : 0.0;
-}
-
 // fp64 -> fp16 through an fp32 value the optimiser cannot fold away (a
 // direct f64 -> f16 truncation is a long software sequence on this target)
 __device__ __forceinline__ _Float16 to_half(double v) {
@@ -891,6 +868,172 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
 }
 
 // ---------------------------------------------------------------------------
+// Score under the Lloyd-tree code ([ReadKV] Sec. 3.1-3.2).  Block (unit, y)
+// takes every ny-th 256-token tile from y; thread j takes token j of the
+// tile and forms, for every query head h of the unit,
+//   s_hj = (qb_h + sum_c w_hc C(t_c, P_jc)) / sqrt(d)   packed tokens
+//   s_hj = (sum_c q_hc k_jc) / sqrt(d)                  open group (exact)
+// in fp64, with w_hc = q'_hc sigma^K_c, qb_h = sum_c q'_hc mu^K_c (from the
+// key allocation), and C(t, P) the float32 centroid of depth-t cell P (P =
+// the token's first t planes of channel c); a channel at depth 0
+// reconstructs to its mean and appears only in qb.  Per tile: the chosen
+// planes' words of the tile (32 bytes per channel and plane) are staged in
+// LDS as [word][channel slot][plane], so a thread reads every plane of its
+// word of a channel with two 16-byte reads; then the split-context softmax
+// partials as the uniform code's score (per-tile max and sum of exp(s - m)),
+// but every token's fp64 logit is kept in place of its exponential: the
+// value allocation forms alpha = exp(s - m) / Z from it, so that equal
+// logits anywhere in the context give bitwise-equal weights (every token
+// shares the calibrated mean at depth 0, so ties across tiles are common
+// here).  A unit whose query is not finite (qb NaN) writes NaN partials and
+// NaN logits.
+// ---------------------------------------------------------------------------
+template <int GQA, int DT>
+__global__ __launch_bounds__(256, 2) void k_score_lloyd(const uint8_t* store, const uint8_t* cb,
+                                                        const void* q, const uint8_t* tk,
+                                                        const double* qp, const double* qb, int H,
+                                                        int G, int W, int64_t capmax, int ntile_ws,
+                                                        uint32_t* ebuf, double* tilepart) {
+  __shared__ __attribute__((aligned(16))) uint32_t stg[8][kDim][8];
+  __shared__ double ctab[512];
+  __shared__ double wq[kDim][GQA];
+  __shared__ double qraw[GQA][kDim];
+  __shared__ uint8_t cch[kDim], cdp[kDim];
+  __shared__ uint16_t pairs[kDim * 8];  // staged (slot, plane) pairs: slot << 3 | plane
+  __shared__ int npair_s, nslot_s;
+  __shared__ double redm[4][GQA], redz[4][GQA];
+  const CodecLayout C = codec_layout(G, kDim);
+  const int ux = (int)blockIdx.x;
+  const int b = ux / G, g = ux % G;
+  const ReqRecord r = req_of(store, b);
+  const int64_t len = r.len;
+  const int ntl = (int)((len + kTile - 1) / kTile);
+  const int ny = (int)gridDim.y;
+  if ((int)blockIdx.y >= ntl) return;
+  const int64_t Tp = len & ~(int64_t)(kGroup - 1);
+  const int esize = DT == 0 ? 2 : 4;
+  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
+
+  // ---- once per block: slots of the channels read, tables, weights ----
+  if (tid == 0) {
+    int n = 0, np = 0;
+    for (int c = 0; c < kDim; ++c) {
+      const int t = tk[(int64_t)ux * kDim + c];
+      if (t > 0) {
+        cch[n] = (uint8_t)c;
+        cdp[n] = (uint8_t)t;
+        for (int p = 0; p < t; ++p) pairs[np++] = (uint16_t)(n << 3 | p);
+        ++n;
+      }
+    }
+    nslot_s = n;
+    npair_s = np;
+  }
+  const float* cent = reinterpret_cast<const float*>(cb + C.cent);
+  for (int i = tid; i < 511; i += 256) ctab[i] = (double)cent[i];
+  for (int i = tid; i < GQA * kDim; i += 256)
+    qraw[i / kDim][i % kDim] = load_elem<DT>(q, hrow0 * kDim + i);
+  double qbv[GQA];
+  bool qbad = false;
+#pragma unroll
+  for (int hh = 0; hh < GQA; ++hh) {
+    qbv[hh] = qb[hrow0 + hh];
+    qbad |= !isfinite(qbv[hh]);
+  }
+  __syncthreads();
+  const int nslot = nslot_s, npair = npair_s;
+  const float* sgk = reinterpret_cast<const float*>(cb + C.sigk) + g * kDim;
+  for (int i = tid; i < nslot * GQA; i += 256) {
+    const int n = i / GQA, hh = i % GQA;
+    const int c = cch[n];
+    wq[n][hh] = __dmul_rn(qp[(hrow0 + hh) * kDim + c], (double)sgk[c]);
+  }
+
+  const int kw = tid >> 5, bit = tid & 31;  // the thread's word of a 256-token line, its bit
+  for (int tile = (int)blockIdx.y; tile < ntl; tile += ny) {
+    const int64_t t0 = (int64_t)tile * kTile;
+    // stage the chosen planes of this half of key tile tile / 2
+    const uint32_t* kt = u.kplanes + (int64_t)(tile >> 1) * kDim * W * 16 + 8 * (tile & 1);
+    __syncthreads();  // the previous tile's words (and the set-up) are done with
+    for (int i = tid; i < 2 * npair; i += 256) {
+      const int pr = pairs[i >> 1], piece = i & 1;
+      const int n = pr >> 3, pl = pr & 7;
+      const uint4 v = *reinterpret_cast<const uint4*>(kt + ((int)cch[n] * W + pl) * 16 + 4 * piece);
+      stg[4 * piece + 0][n][pl] = v.x;
+      stg[4 * piece + 1][n][pl] = v.y;
+      stg[4 * piece + 2][n][pl] = v.z;
+      stg[4 * piece + 3][n][pl] = v.w;
+    }
+    __syncthreads();
+    const int64_t tok = t0 + tid;
+    double sv[GQA];
+    if (tok < Tp) {
+      double acc[GQA];
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
+      for (int n = 0; n < nslot; ++n) {
+        const int t = cdp[n];
+        const uint4 w0 = *reinterpret_cast<const uint4*>(&stg[kw][n][0]);
+        uint4 w1 = make_uint4(0u, 0u, 0u, 0u);
+        if (t > 4) w1 = *reinterpret_cast<const uint4*>(&stg[kw][n][4]);
+        const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+        uint32_t P = 0;
+#pragma unroll
+        for (int pl = 0; pl < 8; ++pl)
+          if (pl < t) P = (P << 1) | ((ws[pl] >> bit) & 1u);
+        const double cv = ctab[(1 << t) - 1 + P];
+#pragma unroll
+        for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(wq[n][hh], cv, acc[hh]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) sv[hh] = __dmul_rn(__dadd_rn(qbv[hh], acc[hh]), kInvSqrt128);
+    } else if (tok < len) {
+      // the open group, exact keys
+      double acc[GQA];
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
+      for (int c = 0; c < kDim; ++c) {
+        const double kv = load_elem<DT>(u.ktail, (tok - Tp) * kDim + c);
+#pragma unroll
+        for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(qraw[hh][c], kv, acc[hh]);
+      }
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) sv[hh] = __dmul_rn(acc[hh], kInvSqrt128);
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) sv[hh] = -INFINITY;
+    }
+    // tile max and sum of exp per head
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      const double m = wave_max(sv[hh]);
+      if (lane == 0) redm[wv][hh] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      const double mt = fmax(fmax(redm[0][hh], redm[1][hh]), fmax(redm[2][hh], redm[3][hh]));
+      double e = 0.0;
+      if (tok < len) {
+        e = exp_nonpos(sv[hh] - mt);
+        reinterpret_cast<double*>(ebuf)[(hrow0 + hh) * capmax + tok] = qbad ? __builtin_nan("") : sv[hh];
+      }
+      const double z = wave_sum(e);
+      if (lane == 0) redz[wv][hh] = z;
+    }
+    __syncthreads();
+    if (tid < GQA) {
+      const double mt = fmax(fmax(redm[0][tid], redm[1][tid]), fmax(redm[2][tid], redm[3][tid]));
+      double* tp = tilepart + ((hrow0 + tid) * ntile_ws + tile) * 2;
+      tp[0] = qbad ? __builtin_nan("") : mt;
+      tp[1] = qbad ? __builtin_nan("") : (redz[0][tid] + redz[1][tid]) + (redz[2][tid] + redz[3][tid]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Gather: a block of 256 threads takes a run of consecutive 128-token chunks
 // (4 groups each) of one (request, KV head) and accumulates its share of
 //   O_h = sum_j alpha_hj v_hat_j,  alpha_hj = e_hj f_{h,tile(j)}
@@ -923,11 +1066,22 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int GQA, int DT>
+// Lloyd-tree code (LL): the un-planed codes X of a token at depth t become
+// the fp16 centroids vtab[t][X] in a channel-major tile (xh), which is the
+// MFMA's A operand directly; per group and head
+//   sum_j e_j v_hat'_jc = mu_c A + sigma_c U_c,  U_c = sum_j e_j C(t_j, P_jc),
+// so the fold uses the channel's calibration (mu, sigma) in place of the
+// group's (lo, rng).  The score kept logits s (fp64) in place of the
+// exponentials: e = exp(s - m_tile) is formed here (fp32).  The partial
+// outputs are in the transformed space; the open group's exact values go to
+// otail instead (written by the last run).
+template <int GQA, int DT, bool LL>
 __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0, const uint8_t* tv, int H,
                                                    int G, int W, int64_t capmax, int ntile_ws,
                                                    int nrun_ws, const uint32_t* ebuf,
-                                                   const double* ftile, float* opart) {
+                                                   const double* ftile, float* opart,
+                                                   const uint8_t* cblk, float* otail,
+                                                   const double* tilepart) {
   constexpr int esize = DT == 0 ? 2 : 4;
   constexpr int NG = kChunk / kGroup;                  // 4 groups per chunk
   constexpr int GS = (16 / GQA < NG) ? 16 / GQA : NG;  // groups per MFMA column set
@@ -941,7 +1095,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   constexpr int RS = kChunk + 1;
   constexpr int MPT = NG * kDim / 256;  // metadata words per thread
   __shared__ __attribute__((aligned(16))) uint4 rows[8 * RS];        // [plane][token]; reused at the end
-  __shared__ __attribute__((aligned(16))) uint8_t xl[kChunk * XS];   // codes [token][channel]
+  __shared__ __attribute__((aligned(16))) uint8_t xl[LL ? 16 : kChunk * XS];  // codes [token][channel]
   // rows padded so that the heads' weight rows (es) and the groups'
   // metadata rows (vmeta_s) read by one MFMA fold start on different banks
   __shared__ __attribute__((aligned(16))) _Float16 es[GQA][kChunk + 8];
@@ -950,6 +1104,11 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   __shared__ __attribute__((aligned(4))) uint8_t tvs[kChunk];
   __shared__ float fs[GQA];
   __shared__ __attribute__((aligned(16))) _Float16 ezero[8];  // a zero weight operand
+  // Lloyd code: centroid tile [channel][token], the fp16 table, mu and sigma
+  constexpr int XHS = kChunk + 8;
+  __shared__ __attribute__((aligned(16))) _Float16 xh[LL ? kDim * XHS : 8];
+  __shared__ _Float16 vts[LL ? 9 * 256 : 1];
+  __shared__ float mus[LL ? kDim : 1], sgs[LL ? kDim : 1];
 
   const int ux = ub0 + (int)blockIdx.x;
   const int b = ux / G, g = ux % G;
@@ -962,13 +1121,24 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   const int cb = (int)(((int64_t)blockIdx.y * nch) / gridDim.y);
   const int ce = (int)(((int64_t)(blockIdx.y + 1) * nch) / gridDim.y);
   if (cb >= ce) {  // empty run: its partial output is zero
-    for (int o = tid; o < GQA * kDim; o += 256)
+    for (int o = tid; o < GQA * kDim; o += 256) {
       opart[((hrow0 + o / kDim) * nrun_ws + blockIdx.y) * kDim + o % kDim] = 0.f;
+      if (LL && blockIdx.y == gridDim.y - 1) otail[hrow0 * kDim + o] = 0.f;
+    }
     return;
   }
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const uint8_t* tvu = tv + ((int64_t)b * G + g) * capmax;
   if (tid < 4) reinterpret_cast<uint32_t*>(ezero)[tid] = 0u;  // read after the first barrier
+  if constexpr (LL) {  // (read after the first barrier)
+    const CodecLayout CL = codec_layout(G, kDim);
+    const _Float16* vt = reinterpret_cast<const _Float16*>(cblk + CL.vtab);
+    for (int i = tid; i < 9 * 256; i += 256) vts[i] = vt[i];
+    if (tid < kDim) {
+      mus[tid] = reinterpret_cast<const float*>(cblk + CL.muv)[g * kDim + tid];
+      sgs[tid] = reinterpret_cast<const float*>(cblk + CL.sigv)[g * kDim + tid];
+    }
+  }
   // row loads: plane pl of tokens tq .. tq + 3, so that the 8 lanes of a
   // token read its 128-byte row (all planes) together and one load
   // instruction covers 8 whole rows
@@ -976,6 +1146,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
 
   // ---- register prefetch of one chunk ----
   uint32_t pes[GQA];  // encoded e of token tid (tid < kChunk) per head
+  double pls[GQA], pmt[GQA];  // Lloyd code: its logit and its tile's maximum
   uint32_t pmeta[MPT];
   double pfs = 0.0;  // converted when stored: no wait right after its load
   uint4 prow[4];     // plane pl of tokens tq .. tq + 3
@@ -996,13 +1167,23 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
     const int c0 = chunk * kChunk;
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
-      const __amdgpu_buffer_rsrc_t rs_e = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint32_t*>(ebuf + (hrow0 + hh) * capmax), (short)0, (int)len * 4, kBufWord3);
-      pes[hh] = __builtin_amdgcn_raw_buffer_load_b32(rs_e, tid < kChunk ? (c0 + tid) * 4 : kBufOff, 0, 0);
+      if constexpr (LL) {
+        const __amdgpu_buffer_rsrc_t rs_e = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t*>(ebuf) + (hrow0 + hh) * capmax * 2, (short)0, (int)len * 8, kBufWord3);
+        pls[hh] = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(
+                                                 rs_e, tid < kChunk ? (c0 + tid) * 8 : kBufOff, 0, 0));
+        pmt[hh] = tilepart[((hrow0 + hh) * ntile_ws + c0 / kTile) * 2];
+      } else {
+        const __amdgpu_buffer_rsrc_t rs_e = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint32_t*>(ebuf + (hrow0 + hh) * capmax), (short)0, (int)len * 4, kBufWord3);
+        pes[hh] = __builtin_amdgcn_raw_buffer_load_b32(rs_e, tid < kChunk ? (c0 + tid) * 4 : kBufOff, 0, 0);
+      }
     }
+    if constexpr (!LL) {
 #pragma unroll
-    for (int k = 0; k < MPT; ++k)
-      pmeta[k] = __builtin_amdgcn_raw_buffer_load_b32(rs_meta, ((c0 / kGroup) * kDim + k * 256 + tid) * 4, 0, 0);
+      for (int k = 0; k < MPT; ++k)
+        pmeta[k] = __builtin_amdgcn_raw_buffer_load_b32(rs_meta, ((c0 / kGroup) * kDim + k * 256 + tid) * 4, 0, 0);
+    }
     pfs = __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(
                                          rs_ft, tid < GQA ? (tid * ntile_ws + c0 / kTile) * 8 : kBufOff, 0, 0));
   };
@@ -1026,12 +1207,17 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
     if (pl == 0) *reinterpret_cast<uint32_t*>(&tvs[tq]) = t4;
     if (tid < kChunk) {
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) es[hh][tid] = to_half(dec_e(pes[hh]));
+      for (int hh = 0; hh < GQA; ++hh) {
+        if constexpr (LL) es[hh][tid] = (_Float16)__expf((float)(pls[hh] - pmt[hh]));
+        else es[hh][tid] = to_half(dec_e(pes[hh]));
+      }
     }
+    if constexpr (!LL) {
 #pragma unroll
-    for (int k = 0; k < MPT; ++k) {
-      const int i = k * 256 + tid;
-      vmeta_s[i / kDim][i % kDim] = pmeta[k];
+      for (int k = 0; k < MPT; ++k) {
+        const int i = k * 256 + tid;
+        vmeta_s[i / kDim][i % kDim] = pmeta[k];
+      }
     }
     if (tid < GQA) fs[tid] = (float)pfs;
     // (rows past a token's depth hold zeros)
@@ -1120,7 +1306,16 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
       uint32_t lo = pb.x, hi = pb.y;
       if (shallow) transpose8_hi4(lo, hi);
       else transpose8_halves(lo, hi);
-      *reinterpret_cast<uint2*>(xl + j * XS + 8 * L) = make_uint2(lo, hi);
+      if constexpr (LL) {
+        const int tb = 256 * (int)tvs[j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t X = ((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFFu;
+          xh[(8 * L + i) * XHS + j] = vts[tb + (int)X];
+        }
+      } else {
+        *reinterpret_cast<uint2*>(xl + j * XS + 8 * L) = make_uint2(lo, hi);
+      }
     }
     lds_barrier();
 
@@ -1148,24 +1343,38 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
           const int gl = gbase + gi;
           if (gl >= ngc) break;
           const int t0 = kGroup * gl + 8 * kb;
-          const uint2 xv = __builtin_bit_cast(uint2, tr8_read(xl + (t0 + (m >> 1)) * XS + cbk + 8 * (m & 1)));
-          uint32_t ap[4];
-          ap[0] = __builtin_amdgcn_perm(0x64646464u, xv.x, 0x04010400u);
-          ap[1] = __builtin_amdgcn_perm(0x64646464u, xv.x, 0x04030402u);
-          ap[2] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04010400u);
-          ap[3] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04030402u);
-          const f16x8 av = __builtin_bit_cast(f16x8, ap);
+          f16x8 av;
+          if constexpr (LL) {
+            av = *reinterpret_cast<const f16x8*>(&xh[(cbk + m) * XHS + t0]);
+          } else {
+            const uint2 xv = __builtin_bit_cast(uint2, tr8_read(xl + (t0 + (m >> 1)) * XS + cbk + 8 * (m & 1)));
+            uint32_t ap[4];
+            ap[0] = __builtin_amdgcn_perm(0x64646464u, xv.x, 0x04010400u);
+            ap[1] = __builtin_amdgcn_perm(0x64646464u, xv.x, 0x04030402u);
+            ap[2] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04010400u);
+            ap[3] = __builtin_amdgcn_perm(0x64646464u, xv.y, 0x04030402u);
+            av = __builtin_bit_cast(f16x8, ap);
+          }
           D = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bvs[gi], D, 0, 0, 0);
         }
         // fold: D row = channel cbk + 4 kb + rr, column m = (gp, hn)
         const int gl = gbase + gp;
         if (colv && gl < ngc) {
-          const float fA = Ag[gl][hn], fB = Bg[gl][hn], fD = fs[hn] * (1.f / 256.f);
+          if constexpr (LL) {
+            const float fA = Ag[gl][hn], fD = fs[hn];
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const uint32_t mt = vmeta_s[gl][cbk + 4 * kb + rr];
-            const float lo = bf16_to_float(mt & 0xFFFFu), rng = bf16_to_float(mt >> 16);
-            Oacc[bl][rr] = fmaf(rng, fmaf(D[rr], fD, fB), fmaf(lo, fA, Oacc[bl][rr]));
+            for (int rr = 0; rr < 4; ++rr) {
+              const int c = cbk + 4 * kb + rr;
+              Oacc[bl][rr] = fmaf(sgs[c], D[rr] * fD, fmaf(mus[c], fA, Oacc[bl][rr]));
+            }
+          } else {
+            const float fA = Ag[gl][hn], fB = Bg[gl][hn], fD = fs[hn] * (1.f / 256.f);
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const uint32_t mt = vmeta_s[gl][cbk + 4 * kb + rr];
+              const float lo = bf16_to_float(mt & 0xFFFFu), rng = bf16_to_float(mt >> 16);
+              Oacc[bl][rr] = fmaf(rng, fmaf(D[rr], fD, fB), fmaf(lo, fA, Oacc[bl][rr]));
+            }
           }
         }
       }
@@ -1195,7 +1404,12 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
     float st = 0.f;
     for (int64_t j = jt0; j < jt1; ++j)
       st = fmaf((float)es[hh][j - cl0], load_elem_f<DT>(u.vtail, (j - Tp) * kDim + c), st);
-    opart[((hrow0 + hh) * nrun_ws + blockIdx.y) * kDim + c] = fmaf(st, fs[hh], s);
+    if constexpr (LL) {
+      opart[((hrow0 + hh) * nrun_ws + blockIdx.y) * kDim + c] = s;
+      if (blockIdx.y == gridDim.y - 1) otail[(hrow0 + hh) * kDim + c] = st * fs[hh];
+    } else {
+      opart[((hrow0 + hh) * nrun_ws + blockIdx.y) * kDim + c] = fmaf(st, fs[hh], s);
+    }
   }
 }
 
@@ -1220,6 +1434,39 @@ __global__ __launch_bounds__(256) void k_out_reduce(int nrun, int nrun_ws, int64
   }
   for (; k < nrun; ++k) s += p[(int64_t)k * kDim];
   out[o] = s;
+}
+
+// Lloyd code: one block of d_h threads per (request, query head): the run
+// partials summed in run order (transformed space), then
+//   o = U_V^T o' + o_open = s_V . (H o') / sqrt(d) + o_open
+// with in-place Walsh-Hadamard butterflies over the block (fp32).
+__global__ __launch_bounds__(kDim) void k_out_reduce_lloyd(int nrun, int nrun_ws, const float* opart,
+                                                           const float* otail, const uint8_t* cb,
+                                                           int G, float* out) {
+  __shared__ float y[kDim];
+  const int64_t bh = blockIdx.x;
+  const int c = threadIdx.x;
+  const float* p = opart + bh * nrun_ws * kDim + c;
+  float s = 0.f;
+  int k = 0;
+  for (; k + 8 <= nrun; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(int64_t)(k + i) * kDim];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += v[i];
+  }
+  for (; k < nrun; ++k) s += p[(int64_t)k * kDim];
+  y[c] = s;
+  __syncthreads();
+  for (int h = 1; h < kDim; h <<= 1) {
+    const float a = y[c], o = y[c ^ h];
+    __syncthreads();
+    y[c] = (c & h) ? o - a : a + o;
+    __syncthreads();
+  }
+  const double sv = reinterpret_cast<const double*>(cb + codec_layout(G, kDim).sv)[c];
+  out[bh * kDim + c] = y[c] * ((float)kInvSqrt128 * (float)sv) + otail[bh * kDim + c];
 }
 
 // ---------------------------------------------------------------------------
@@ -1282,10 +1529,10 @@ static int launch_part(const DecodeArgs& a, const WsLayout& L, const Part& P, ui
   if (P.ub0 == 0) mark(a, 1, st);
   if (launch_value_alloc(a, P, L, tk, tv, st)) return -5;
   if (P.ub0 == 0) mark(a, 2, st);
-  hipLaunchKernelGGL((k_gather<GQA, DT>), dim3(P.nunits, nrun_g), dim3(256), 0, st,
+  hipLaunchKernelGGL((k_gather<GQA, DT, false>), dim3(P.nunits, nrun_g), dim3(256), 0, st,
                      (const uint8_t*)a.store, P.ub0, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax,
                      L.ntile, L.nchunk, (const uint32_t*)(ws + L.ebuf), (const double*)(ws + L.ftile),
-                     (float*)(ws + L.opart));
+                     (float*)(ws + L.opart), nullptr, nullptr, nullptr);
   return 0;
 }
 
@@ -1312,8 +1559,60 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
+// Lloyd code: key allocation (own launch, per domain), score, value
+// allocation, gather, output reduction with the inverse value transform.
+template <int GQA, int DT>
+static int launch_all_lloyd(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
+  uint8_t* ws = a.ws;
+  uint8_t* tk = a.key_depths_out ? a.key_depths_out : ws + L.tk;
+  uint8_t* tv = a.value_depths_out ? a.value_depths_out : ws + L.tv;
+  const int nunits = a.B * a.G;
+  mark(a, 0, st);
+  if (launch_key_alloc_lloyd(a, L, tk, st)) return -5;
+  const int64_t total_tiles = (int64_t)nunits * L.ntile;
+  const int64_t slots = 3 * (int64_t)device_cu_count();
+  int run = (int)((total_tiles + slots - 1) / slots);
+  if (run < 1) run = 1;
+  const int nrun = (L.ntile + run - 1) / run;
+  hipLaunchKernelGGL((k_score_lloyd<GQA, DT>), dim3(nunits, nrun), dim3(256), 0, st,
+                     (const uint8_t*)a.store, a.cblock, a.q, (const uint8_t*)tk,
+                     (const double*)(ws + L.qp), (const double*)(ws + L.qb), a.H, a.G, a.W, a.capmax,
+                     L.ntile, (uint32_t*)(ws + L.ebuf), (double*)(ws + L.tilepart));
+  mark(a, 1, st);
+  const Part P{0, nunits};
+  if (launch_value_alloc(a, P, L, tk, tv, st)) return -5;
+  mark(a, 2, st);
+  const int64_t total = (int64_t)nunits * L.nchunk;
+  const int64_t gslots = 4 * (int64_t)device_cu_count();
+  int grun = (int)((total + gslots - 1) / gslots);
+  if (grun < 1) grun = 1;
+  const int nrun_g = (L.nchunk + grun - 1) / grun;
+  hipLaunchKernelGGL((k_gather<GQA, DT, true>), dim3(nunits, nrun_g), dim3(256), 0, st,
+                     (const uint8_t*)a.store, 0, (const uint8_t*)tv, a.H, a.G, a.W, a.capmax,
+                     L.ntile, L.nchunk, (const uint32_t*)(ws + L.ebuf), (const double*)(ws + L.ftile),
+                     (float*)(ws + L.opart), a.cblock, (float*)(ws + L.otail),
+                     (const double*)(ws + L.tilepart));
+  hipLaunchKernelGGL(k_out_reduce_lloyd, dim3(a.B * a.H), dim3(kDim), 0, st, nrun_g, L.nchunk,
+                     (const float*)(ws + L.opart), (const float*)(ws + L.otail), a.cblock, a.G, a.out);
+  mark(a, 3, st);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
 template <int DT>
 static int dispatch_gqa(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
+  if (a.codec) {
+    switch (a.H / a.G) {
+      case 1: return launch_all_lloyd<1, DT>(a, L, st);
+      case 2: return launch_all_lloyd<2, DT>(a, L, st);
+      case 3: return launch_all_lloyd<3, DT>(a, L, st);
+      case 4: return launch_all_lloyd<4, DT>(a, L, st);
+      case 5: return launch_all_lloyd<5, DT>(a, L, st);
+      case 6: return launch_all_lloyd<6, DT>(a, L, st);
+      case 7: return launch_all_lloyd<7, DT>(a, L, st);
+      case 8: return launch_all_lloyd<8, DT>(a, L, st);
+      default: return -5;
+    }
+  }
   switch (a.H / a.G) {
     case 1: return launch_all<1, DT>(a, L, st);
     case 2: return launch_all<2, DT>(a, L, st);
@@ -1328,7 +1627,7 @@ static int dispatch_gqa(const DecodeArgs& a, const WsLayout& L, hipStream_t st) 
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const WsLayout L = ws_layout(a.B, a.H, a.G, kDim, a.capmax);
+  const WsLayout L = ws_layout(a.B, a.H, a.G, kDim, a.capmax, a.codec);
   return a.dtype == 0 ? dispatch_gqa<0>(a, L, st) : dispatch_gqa<1>(a, L, st);
 }
 

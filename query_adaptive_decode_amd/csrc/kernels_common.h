@@ -60,6 +60,30 @@ __device__ __forceinline__ uint32_t enc_e(double e) {
 }
 __device__ __forceinline__ double dec_e(uint32_t b) { return bitsd((uint64_t)b << 30); }
 
+// e^x for x <= 0 (or -inf), relative error below 1e-9.  Cody-Waite range
+// reduction x = k ln2 + r (k = rint(x / ln2), ln2 in two parts, so r is
+// exact to ~1e-17 and |r| <= ln2 / 2), then
+//   e^r = 1 + r + r^2 (1/2 + r P(r)),  P(r) = sum_{i>=0} r^i / (i + 3)!
+// with P's Taylor polynomial (degree 5: truncation r^9 / 9! below 3e-10) evaluated
+// in fp32: its rounding error, weighted by |r|^3 <= 0.042, stays below
+// 1e-9 of the result.  Then the exact scaling 2^k.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  const double xc = fmax(x, -745.0);
+  const double k = rint(xc * 1.4426950408889634074);
+  const double r = fma(k, -1.9082149292705877000e-10, fma(k, -6.9314718036912381649e-01, xc));
+  const float rf = (float)r;
+  float pp = 2.4801587e-05f;                 // 1/8!
+  pp = fmaf(pp, rf, 1.9841270e-04f);         // 1/7!
+  pp = fmaf(pp, rf, 1.3888889e-03f);         // 1/6!
+  pp = fmaf(pp, rf, 8.3333333e-03f);         // 1/5!
+  pp = fmaf(pp, rf, 4.1666668e-02f);         // 1/4!
+  pp = fmaf(pp, rf, 1.6666667e-01f);         // 1/3!
+  const double e = fma(r * r, fma(r, (double)pp, 0.5), 1.0 + r);
+  const double v = ldexp(e, (int)k);
+  return x > -745.0 ? v : 0.0;
+}
+
+
 // Raw buffer resources (stride 0): the fourth descriptor word of the GFX9
 // family for untyped 32-bit data, and an offset past any buffer this code
 // builds (a load there returns zeros and makes no memory access).

@@ -157,7 +157,8 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 //   tk     u8  [B][G][d]          key depths
 //   tv     u8  [B][G][capmax]     value depths
 //   ebuf   u32 [B][H][capmax]     exp(s - m_tile) per token (tile = kTile),
-//                                 fp64 bits 61..30 (enc_e)
+//                                 fp64 bits 61..30 (enc_e); Lloyd-tree code:
+//                                 f64, the logit s itself
 //   tilepart f64 [B][H][ntile][2] (m_tile, sum of exp) per tile
 //   ftile  f64 [B][H][ntile]      exp(m_tile - m) / Z
 //   aval   f64 [B][G][capmax]     value weights (only when they do not fit
@@ -173,14 +174,14 @@ struct WsLayout {
   int ntile, nchunk;
 };
 
-RKV_HD WsLayout ws_layout(int B, int H, int G, int d, int64_t capmax) {
+RKV_HD WsLayout ws_layout(int B, int H, int G, int d, int64_t capmax, int codec) {
   WsLayout L;
   L.ntile = (int)((capmax + kTile - 1) / kTile);
   L.nchunk = (int)((capmax + kChunk - 1) / kChunk);
   int64_t off = 0;
   L.tk = off; off = align_up(off + (int64_t)B * G * d, 256);
   L.tv = off; off = align_up(off + (int64_t)B * G * capmax, 256);
-  L.ebuf = off; off = align_up(off + (int64_t)B * H * capmax * 4, 256);
+  L.ebuf = off; off = align_up(off + (int64_t)B * H * capmax * (codec ? 8 : 4), 256);
   L.tilepart = off; off = align_up(off + (int64_t)B * H * L.ntile * 16, 256);
   L.ftile = off; off = align_up(off + (int64_t)B * H * L.ntile * 8, 256);
   L.aval = off; off = align_up(off + (int64_t)B * G * capmax * 8, 256);

@@ -148,6 +148,21 @@ __device__ __forceinline__ uint64_t gain_bits(double a, int t) {
   return dbits(__dmul_rn(a, bitsd((uint64_t)(1023 - 2 * t) << 52)));
 }
 
+// Gain tables.  Pow4Gains: gain of level t = a 4^-t (uniform code; regular
+// items use the shared-mantissa fields above).  TableGains: gain = a g[t]
+// with a caller's table of decreasing positive g[1..W] (the Lloyd tree's
+// Delta_t): every positive item forms its W gains one by one (the "odd"
+// path), each an fp64 product rounded to nearest.
+struct Pow4Gains {
+  __device__ __forceinline__ int regular(double a, int twoW) const { return regular_field(a, twoW); }
+  __device__ __forceinline__ uint64_t gain(double a, int t) const { return gain_bits(a, t); }
+};
+struct TableGains {
+  const double* g;  // g[t], t = 1..W
+  __device__ __forceinline__ int regular(double, int) const { return kNoField; }
+  __device__ __forceinline__ uint64_t gain(double a, int t) const { return dbits(__dmul_rn(a, g[t])); }
+};
+
 template <int NT>
 struct ChooseShared {
   union {
@@ -193,9 +208,10 @@ struct ChooseLocal {
   int etop = -1;
   bool odd = false;
 };
-template <int NT>
-__device__ __forceinline__ void choose_add(double a, int W, ChooseShared<NT>& S, ChooseLocal& L) {
-  const int ef = regular_field(a, 2 * W);
+template <int NT, class GP = Pow4Gains>
+__device__ __forceinline__ void choose_add(double a, int W, ChooseShared<NT>& S, ChooseLocal& L,
+                                           const GP& gp = GP()) {
+  const int ef = gp.regular(a, 2 * W);
   if (ef != kNoField) {
     atomicAdd(&S.hA[ef], 1u);
     L.npos += (uint32_t)W;
@@ -203,7 +219,7 @@ __device__ __forceinline__ void choose_add(double a, int W, ChooseShared<NT>& S,
   } else if (a > 0.0) {
     L.odd = true;
     for (int t = 1; t <= W; ++t) {
-      const uint64_t kk = gain_bits(a, t);
+      const uint64_t kk = gp.gain(a, t);
       if (kk) {
         const int f = (int)(kk >> 52);
         atomicAdd(&S.hB[f], 1u);
@@ -301,9 +317,9 @@ __device__ __forceinline__ void wave_settle_bits(const uint64_t* list, uint32_t 
 // sum of this thread's depths.  Every thread of the block must call it
 // (block barriers inside).  The histograms must have been built (choose_clear,
 // choose_add of every item's geta value, choose_flush, a barrier).
-template <int NT, class GetA, class PutT>
+template <int NT, class GetA, class PutT, class GP = Pow4Gains>
 __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
-                                             ChooseShared<NT>& S) {
+                                             ChooseShared<NT>& S, const GP& gp = GP()) {
   constexpr int NW = NT / 64;
   constexpr int IPT = 4;
   constexpr int64_t RT = (int64_t)NT * IPT;
@@ -319,7 +335,7 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
 #pragma unroll
       for (int q = 0; q < IPT; ++q) a[q] = i0 + q < N ? geta(i0 + q) : 0.0;
 #pragma unroll
-      for (int q = 0; q < IPT; ++q) fn(i0 + q, a[q], regular_field(a[q], twoW), i0 + q < N);
+      for (int q = 0; q < IPT; ++q) fn(i0 + q, a[q], gp.regular(a[q], twoW), i0 + q < N);
     }
   };
 
@@ -344,7 +360,7 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
         if (d2 <= dspan && !(d2 & 1u)) fn(dbits(a) & kMant);
       } else if (any_odd && a > 0.0) {
         for (int t = 1; t <= W; ++t) {
-          const uint64_t kk = gain_bits(a, t);
+          const uint64_t kk = gp.gain(a, t);
           if (kk && (int)(kk >> 52) == Es) fn(kk & kMant);
         }
       }
@@ -417,7 +433,7 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
     if (all_pos) {
       if (ef != kNoField) return (uint32_t)W;
       uint32_t n = 0;
-      for (int t = 1; t <= W; ++t) n += gain_bits(a, t) != 0ull;
+      for (int t = 1; t <= W; ++t) n += gp.gain(a, t) != 0ull;
       return n;
     }
     uint32_t above = 0, tie = 0;
@@ -431,7 +447,7 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
       }
     } else {
       for (int t = 1; t <= W; ++t) {
-        const uint64_t kk = gain_bits(a, t);
+        const uint64_t kk = gp.gain(a, t);
         if (!kk) continue;
         const int e = (int)(kk >> 52);
         if (e > Es) {
@@ -457,7 +473,7 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
 #pragma unroll
     for (int q = 0; q < IPT; ++q) {
       const double a = i0 + q < N ? geta(i0 + q) : 0.0;
-      const uint32_t lv = count_levels(a, regular_field(a, twoW));
+      const uint32_t lv = count_levels(a, gp.regular(a, twoW));
       t[q] = lv & 0xFFFFu;
       tie[q] = lv >> 16;
     }
@@ -485,17 +501,17 @@ __device__ uint32_t block_choose_depths_hist(int64_t N, uint32_t Bud, int W, Get
 }
 
 // ChooseDepths with the histograms built here from geta.
-template <int NT, class GetA, class PutT>
+template <int NT, class GetA, class PutT, class GP = Pow4Gains>
 __device__ uint32_t block_choose_depths(int64_t N, uint32_t Bud, int W, GetA&& geta, PutT&& put,
-                                        ChooseShared<NT>& S) {
+                                        ChooseShared<NT>& S, const GP& gp = GP()) {
   const int tid = threadIdx.x;
   choose_clear<NT>(S);
   lds_barrier();
   ChooseLocal L;
-  for (int64_t i = tid; i < N; i += NT) choose_add<NT>(geta(i), W, S, L);
+  for (int64_t i = tid; i < N; i += NT) choose_add<NT>(geta(i), W, S, L, gp);
   choose_flush<NT>(L, S);
   lds_barrier();
-  return block_choose_depths_hist<NT>(N, Bud, W, geta, put, S);
+  return block_choose_depths_hist<NT>(N, Bud, W, geta, put, S, gp);
 }
 
 }  // namespace readkv

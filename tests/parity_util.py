@@ -28,22 +28,27 @@ OUT_REL_L2 = 2e-3
 REPORT = []
 
 
-def _levels(t_from, t_to, w):
+def _gain(w, lvl, gains):
+    return float(w) * (4.0 ** (-lvl) if gains is None else float(gains[lvl]))
+
+
+def _levels(t_from, t_to, w, gains=None):
     """(item, level, gain) of the levels item i holds in t_to but not in
     t_from."""
     out = []
     for i in np.nonzero(t_to > t_from)[0]:
         for lvl in range(int(t_from[i]) + 1, int(t_to[i]) + 1):
-            out.append((int(i), lvl, float(w[i]) * 4.0 ** (-lvl)))
+            out.append((int(i), lvl, _gain(w[i], lvl, gains)))
     return out
 
 
-def alloc_mismatch(t_gpu, t_or, w_or, W, rel=NEAR_TIE_REL, start=0):
+def alloc_mismatch(t_gpu, t_or, w_or, W, rel=NEAR_TIE_REL, start=0, gains=None):
     """Returns (n_near_ties, n_bad, detail) for one selection domain.
 
     t_gpu, t_or: depth per item (GPU, oracle); w_or: the oracle's item
-    weights (gain of level t = w * 4^-t); start: the mandatory minimum depth
-    (levels up to it are not chosen, so they do not define tau_o)."""
+    weights (gain of level t = w * 4^-t, or w * gains[t] with a gain table);
+    start: the mandatory minimum depth (levels up to it are not chosen, so
+    they do not define tau_o)."""
     t_gpu = np.asarray(t_gpu, dtype=np.int64)
     t_or = np.asarray(t_or, dtype=np.int64)
     if t_gpu.sum() != t_or.sum():
@@ -56,9 +61,9 @@ def alloc_mismatch(t_gpu, t_or, w_or, W, rel=NEAR_TIE_REL, start=0):
     sel = np.nonzero(t_or > start)[0]
     if len(sel) == 0:
         return 0, 1, "the oracle chose no level, the GPU did"
-    tau = float(np.min(w[sel] * 4.0 ** (-t_or[sel].astype(np.float64))))
-    extra = _levels(t_or, t_gpu, w)     # chosen by the GPU only
-    missing = _levels(t_gpu, t_or, w)   # chosen by the oracle only
+    tau = min(_gain(w[i], int(t_or[i]), gains) for i in sel)
+    extra = _levels(t_or, t_gpu, w, gains)     # chosen by the GPU only
+    missing = _levels(t_gpu, t_or, w, gains)   # chosen by the oracle only
     near = bad = 0
     worst = 0.0
     for (_, _, g) in extra + missing:
