@@ -19,8 +19,13 @@ request counters (when they were taken on these sources), a measured
 device-copy bandwidth, and the float64 oracle's CPU throughput on this
 host (all cores, and one core).
 
+The same step over the pages' own code (Gaussian Lloyd tree with
+Hadamard-sign transforms, calibrated on a held-out synthetic split) is
+timed the same way at `--lloyd-rates` and reported under "lloyd_codec".
+
 `--counters-run` runs the fixed sequence the counter profiles are taken on
-(see query_adaptive_decode_amd/profile_summary.py) and prints nothing else.
+(see query_adaptive_decode_amd/profile_summary.py) and prints nothing else
+(`--lloyd` there: the same sequence over the Lloyd code).
 """
 from __future__ import annotations
 
@@ -68,11 +73,14 @@ class Stepper:
     """Device state of one rate: the store (prefilled), fixed input buffers
     that one step's graph reads, and the decode outputs."""
 
-    def __init__(self, cfg, dev, lcfg, R, torch):
+    def __init__(self, cfg, dev, lcfg, R, torch, codec=None):
         from query_adaptive_decode_amd import binding as Bd
         self.Bd, self.torch, self.cfg, self.dev, self.lcfg, self.R = Bd, torch, cfg, dev, lcfg, R
         B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
         self.cache = Bd.ReadKVCache(lcfg)
+        if codec is not None:   # Lloyd code: signs and calibration before the prompt
+            Bd.codec_init(lcfg, self.cache.store, codec["sk"], codec["sv"], codec["kcal"],
+                          codec["vcal"])
         self.cache.append(dev["kpre"], dev["vpre"])
         self.out = torch.empty((B, H, d), dtype=torch.float32, device="cuda")
         self.kbuf = torch.empty_like(dev["kstep"][0])
@@ -119,12 +127,12 @@ def flush(scratch):
     scratch.sum()
 
 
-def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h):
+def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h, codec=None):
     """Warm and flushed step times (graph replays) and per-kernel durations
     (HIP events on the launch stream around each stage)."""
     B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
     T0 = int(cfg["T0"])
-    st = Stepper(cfg, dev, lcfg, R, torch)
+    st = Stepper(cfg, dev, lcfg, R, torch, codec)
     for _ in range(warmup):
         st.step_eager()
     st.capture()
@@ -191,11 +199,20 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h):
     ng = tpm / 32
     kpay = float(ksum.item()) / steps * tpm / 8            # bytes per launch, all (b,g)
     vpay = float(vsum.item()) / steps * d / 8
-    meta = B * G * ng * d * 4                              # one of K or V metadata
-    # the score launch also reads q and E^K for the key allocation in its prologue
-    alg = {"score": kpay + meta + B * G * d * 8 + B * H * d * 2, "value_gather": vpay + meta,
-           "value_alloc": B * G * ng * 8}
-    step_bytes = kpay + vpay + 2 * meta
+    if codec is None:
+        meta = B * G * ng * d * 4                          # one of K or V metadata
+        # the score launch also reads q and E^K for the key allocation in its prologue
+        alg = {"score": kpay + meta + B * G * d * 8 + B * H * d * 2, "value_gather": vpay + meta,
+               "value_alloc": B * G * ng * 8}
+        step_bytes = kpay + vpay + 2 * meta
+    else:
+        # Lloyd code: no per-group metadata; the calibration arrays (4 x G x d
+        # float32) and the decoder table (518 float32) once per call; the
+        # score stage (key allocation + score) reads q
+        shared = G * d * 16 + 518 * 4
+        alg = {"score": kpay + B * H * d * 2 + G * d * 8, "value_gather": vpay + G * d * 8,
+               "value_alloc": 0.0}
+        step_bytes = kpay + vpay + shared
     return dict(R=R, time=res, kernel_ms=kern, alg_bytes=alg, step_alg_bytes=step_bytes,
                 key_bits=float(ksum.item()) / steps / (B * G * d),
                 value_bits=float(vsum.item()) / steps / (B * G * tpm), steps_used=st.s)
@@ -282,7 +299,7 @@ def cpu_baseline(cfg, budget_s=20.0):
                 single_core=dict(value=one[0] / one[1], seconds_per_unit=per_unit))
 
 
-def counters_run(cfg, dev, lcfg, rates, warmup, steps, torch):
+def counters_run(cfg, dev, lcfg, rates, warmup, steps, torch, codec=None):
     """The fixed launch sequence the rocprofv3 request-counter passes are
     taken on: a 512 MiB device copy (calibration), then per rate `warmup`
     steps, `steps` warm steps and `steps` steps each after a 512 MiB flush,
@@ -294,7 +311,7 @@ def counters_run(cfg, dev, lcfg, rates, warmup, steps, torch):
     del src, dst
     scratch = flush_buffer(torch)
     for R in rates:
-        st = Stepper(cfg, dev, lcfg, R, torch)
+        st = Stepper(cfg, dev, lcfg, R, torch, codec)
         for _ in range(warmup + steps):
             st.step_eager()
         for _ in range(steps):
@@ -317,8 +334,12 @@ def main():
     ap.add_argument("--rates", default="4,2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--lloyd-rates", default="4,2",
+                    help="rates timed over the Lloyd-tree code ('' for none)")
     ap.add_argument("--counters-run", action="store_true",
                     help="run the fixed sequence the counter profiles are taken on, print no line")
+    ap.add_argument("--lloyd", action="store_true",
+                    help="with --counters-run: over the Lloyd-tree code")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "one GPU only: the decode path has no multi-GPU mode "
@@ -339,9 +360,19 @@ def main():
     dev = workload.to_device(hin)
     del hin
     lcfg = workload.config_for(cfg, per_rate)
+    lrates = [float(r) for r in args.lloyd_rates.split(",") if r.strip()]
+    codec, lcfg_ll = None, None
+    if lrates or args.lloyd:
+        ci = workload.calibration_inputs(cfg, 512)
+        cd = workload.to_device(dict(kcal=ci["kcal"], vcal=ci["vcal"]))
+        codec = dict(sk=ci["sk"].tolist(), sv=ci["sv"].tolist(), kcal=cd["kcal"], vcal=cd["vcal"])
+        lcfg_ll = workload.config_for(dict(cfg, codec="lloyd"), per_rate)
     print(f"# inputs ready in {time.perf_counter() - t:.1f} s", file=sys.stderr, flush=True)
     if args.counters_run:
-        counters_run(cfg, dev, lcfg, rates, args.warmup, args.steps, torch)
+        if args.lloyd:
+            counters_run(cfg, dev, lcfg_ll, rates, args.warmup, args.steps, torch, codec)
+        else:
+            counters_run(cfg, dev, lcfg, rates, args.warmup, args.steps, torch)
         return
     from query_adaptive_decode_amd import profile_summary as PS
     h = _hip()
@@ -447,6 +478,44 @@ def main():
     if moved is None:
         line["moved_bytes_note"] = ("no counter summary for these kernel sources "
                                     "(profiles/ was taken on other sources)")
+    if lrates:
+        ll = {"code": "Gaussian Lloyd tree (depth 8, float32 table) + Hadamard-sign transforms, "
+                      "calibrated on 512 held-out synthetic tokens per KV head",
+              "dtype": "u8 tree paths; f64 logits over centroids; f16 MFMA + f32 values",
+              "rates": {}}
+        moved_ll = PS.committed_bytes(PS.SUMMARY_LLOYD)
+        for R in lrates:
+            r = run_rate(cfg, dev, lcfg_ll, R, args.warmup, args.steps, torch, h, codec)
+            tm, km = r["time"], r["kernel_ms"]
+            print(f"# Lloyd R={R:g}: evicted {tm['evicted']['ms_per_step']:.3f} ms/step "
+                  f"({tm['evicted']['qh_tok_per_s'] / 1e9:.2f} G qh*tok/s), warm "
+                  f"{tm['warm']['ms_per_step']:.3f} ms/step; kernels evicted "
+                  f"{json.dumps({k: round(v * 1e3, 1) for k, v in km['evicted'].items()})} us",
+                  file=sys.stderr, flush=True)
+            ent = {
+                "evicted_ms_per_step": tm["evicted"]["ms_per_step"],
+                "evicted_qh_tok_per_s": tm["evicted"]["qh_tok_per_s"],
+                "warm_ms_per_step": tm["warm"]["ms_per_step"],
+                "warm_qh_tok_per_s": tm["warm"]["qh_tok_per_s"],
+                "kernel_us": {mode: {k: v * 1e3 for k, v in km[mode].items()} for mode in km},
+                "logical_bytes_per_step": r["step_alg_bytes"],
+                "logical_GBps": {mode: r["step_alg_bytes"] / (tm[mode]["ms_per_step"] * 1e-3) / 1e9
+                                 for mode in tm},
+                "key_bits_per_scalar": r["key_bits"],
+                "value_bits_per_scalar": r["value_bits"],
+                "kernel_alg_GBps_evicted": {k: r["alg_bytes"][k] / (km["evicted"][k] * 1e-3) / 1e9
+                                            for k in ("score", "value_gather")},
+            }
+            m = moved_ll.get(rate_key(R), {}).get("evicted") if moved_ll else None
+            if m:
+                step_b = m["step_read_bytes"] + m["step_write_bytes"]
+                gbps = step_b / (tm["evicted"]["ms_per_step"] * 1e-3) / 1e9
+                ent["moved_evicted"] = {"bytes_per_step": step_b, "GBps": gbps,
+                                        "frac_of_peak": gbps / HBM_PEAK_GBPS,
+                                        "per_kernel_bytes": {k: v["read_bytes"] + v["write_bytes"]
+                                                             for k, v in m["kernels"].items()}}
+            ll["rates"][rate_key(R)] = ent
+        line["lloyd_codec"] = ll
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(line))

@@ -29,10 +29,14 @@ import statistics
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SUMMARY = os.path.join(ROOT, "profiles", "hbm_bytes_decode_step_llama3-8b-B16-T8192.txt")
+# the same step over the Lloyd-tree code (bench.py --counters-run --lloyd)
+SUMMARY_LLOYD = os.path.join(ROOT, "profiles", "hbm_bytes_decode_step_lloyd_llama3-8b-B16-T8192.txt")
 COPY_BYTES = 512 << 20
 
 # kernel name prefix -> short name (bench.py's stage names where they exist)
 NAMES = [("k_append_small", "append"), ("k_key_alloc", "key_alloc"), ("k_score", "score"),
+         ("k_key_alloc_lloyd", "key_alloc"), ("k_score_lloyd", "score"),
+         ("k_out_reduce_lloyd", "out_reduce"),
          ("k_value_alloc_unit", "value_alloc"), ("k_value_weights", "value_weights"),
          ("k_value_select", "value_select"), ("k_gather", "value_gather"),
          ("k_out_reduce", "out_reduce")]
