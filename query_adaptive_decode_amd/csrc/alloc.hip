@@ -80,8 +80,9 @@ __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0
 // Key allocation under the Lloyd-tree code ([ReadKV] Sec. 3.1-3.2), one
 // block per selection domain (a unit, or a request's NU = G KV heads under
 // per-layer budgets).  Per KV head: the query heads' rows q' = U_K q
-// (Walsh-Hadamard butterflies over the block in fp64, times 1/sqrt(d)),
-// written to the workspace with qb_h = sum_c q'_hc mu^K_c (channel order);
+// (Walsh-Hadamard butterflies over the block in fp64, times 1/sqrt(d));
+// written to the workspace: the score's channel weights q'_hc sigma^K_c
+// ([unit][channel][head]) and qb_h = sum_c q'_hc mu^K_c (channel order);
 // weights w_c = sum_h (q'_hc sigma^K_c)^2 in head order (Eq. (2)); then
 // ChooseDepths with the tree's gains Delta_t.  A KV head with a non-finite
 // query value gets zero weights and qb = NaN (the score reads nothing for
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(256) void k_key_alloc(const uint8_t* store, int ub0
 template <int GQA, int DT, int NUMAX>
 __global__ __launch_bounds__(256) void k_key_alloc_lloyd(const uint8_t* cb, const void* q, int H,
                                                          int G, int W, float RK, int NU, int min1,
-                                                         uint8_t* tk, double* qp, double* qb,
+                                                         uint8_t* tk, double* qw, double* qb,
                                                          uint64_t* counters) {
   constexpr int NT = 256;
   constexpr int PER = (GQA * kDim + NT - 1) / NT;
@@ -133,19 +134,17 @@ __global__ __launch_bounds__(256) void k_key_alloc_lloyd(const uint8_t* cb, cons
       }
       __syncthreads();
     }
-    for (int i = tid; i < GQA * kDim; i += NT) {
-      const double v = __dmul_rn(xb[i], kInvSqrt128);
-      xb[i] = v;
-      qp[hrow * kDim + i] = v;
-    }
+    for (int i = tid; i < GQA * kDim; i += NT) xb[i] = __dmul_rn(xb[i], kInvSqrt128);
     __syncthreads();
     if (tid < kDim) {
       const int c = tid;
       const double sg = (double)reinterpret_cast<const float*>(cb + C.sigk)[g * kDim + c];
       double a = 0.0;
+      double* const qwc = qw + ((int64_t)(b * G + g) * kDim + c) * GQA;
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) {
         const double x = __dmul_rn(xb[hh * kDim + c], sg);
+        qwc[hh] = x;
         a = __dadd_rn(a, __dmul_rn(x, x));
       }
       wl[k * kDim + c] = nf ? 0.0 : a;

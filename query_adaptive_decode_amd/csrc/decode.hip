@@ -873,34 +873,37 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
 // tile and forms, for every query head h of the unit,
 //   s_hj = (qb_h + sum_c w_hc C(t_c, P_jc)) / sqrt(d)   packed tokens
 //   s_hj = (sum_c q_hc k_jc) / sqrt(d)                  open group (exact)
-// in fp64, with w_hc = q'_hc sigma^K_c, qb_h = sum_c q'_hc mu^K_c (from the
-// key allocation), and C(t, P) the float32 centroid of depth-t cell P (P =
-// the token's first t planes of channel c); a channel at depth 0
-// reconstructs to its mean and appears only in qb.  Per tile: the chosen
-// planes' words of the tile (32 bytes per channel and plane) are staged in
-// LDS as [word][channel slot][plane], so a thread reads every plane of its
-// word of a channel with two 16-byte reads; then the split-context softmax
-// partials as the uniform code's score (per-tile max and sum of exp(s - m)),
-// but every token's fp64 logit is kept in place of its exponential: the
-// value allocation forms alpha = exp(s - m) / Z from it, so that equal
-// logits anywhere in the context give bitwise-equal weights (every token
-// shares the calibrated mean at depth 0, so ties across tiles are common
-// here).  A unit whose query is not finite (qb NaN) writes NaN partials and
-// NaN logits.
+// in fp64, with w_hc = q'_hc sigma^K_c and qb_h = sum_c q'_hc mu^K_c (both
+// from the key allocation), C(t, P) the float32 centroid of depth-t cell P,
+// P = the token's first t planes of channel c; a channel at depth 0
+// reconstructs to its mean and appears only in qb.  Per tile:
+//  1. un-plane: thread (channel quad, 32-token word) loads the chosen plane
+//     words of its four channels, and 8x8 bit transposes turn them into code
+//     bytes X = P 2^(8-t); one 32-bit LDS word per (token, channel quad);
+//  2. thread j reads its code word per channel quad, looks the four centroids
+//     up in an LDS table indexed by (depth, X), and accumulates with the
+//     weights, which the scalar unit loads (the channel loop is uniform).
+// Then the split-context softmax partials as the uniform code's score
+// (per-tile max and sum of exp(s - m)), but every token's fp64 logit is kept
+// in place of its exponential: the value allocation forms alpha = exp(s -
+// m) / Z from it, so that equal logits anywhere in the context give
+// bitwise-equal weights (every token shares the calibrated mean at depth 0,
+// so ties across tiles are common here).  A unit whose query is not finite
+// (qb NaN) writes NaN partials and NaN logits.
 // ---------------------------------------------------------------------------
+typedef const double __attribute__((address_space(4)))* cdptr;
+typedef const uint32_t __attribute__((address_space(4)))* cuptr;
+
 template <int GQA, int DT>
-__global__ __launch_bounds__(256, 2) void k_score_lloyd(const uint8_t* store, const uint8_t* cb,
+__global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, const uint8_t* cb,
                                                         const void* q, const uint8_t* tk,
-                                                        const double* qp, const double* qb, int H,
+                                                        const double* qw, const double* qb, int H,
                                                         int G, int W, int64_t capmax, int ntile_ws,
                                                         uint32_t* ebuf, double* tilepart) {
-  __shared__ __attribute__((aligned(16))) uint32_t stg[8][kDim][8];
-  __shared__ double ctab[512];
-  __shared__ double wq[kDim][GQA];
-  __shared__ double qraw[GQA][kDim];
-  __shared__ uint8_t cch[kDim], cdp[kDim];
-  __shared__ uint16_t pairs[kDim * 8];  // staged (slot, plane) pairs: slot << 3 | plane
-  __shared__ int npair_s, nslot_s;
+  constexpr int CS = kDim / 4 + 1;  // code-word row stride (words): rows 33 banks apart
+  __shared__ uint32_t codes[kTile * CS];
+  __shared__ float ftab[9 * 256];  // centroid of depth t, code byte X at 256 t + X
+  __shared__ uint32_t tk4s[kDim / 4];
   __shared__ double redm[4][GQA], redz[4][GQA];
   const CodecLayout C = codec_layout(G, kDim);
   const int ux = (int)blockIdx.x;
@@ -916,25 +919,13 @@ __global__ __launch_bounds__(256, 2) void k_score_lloyd(const uint8_t* store, co
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
 
-  // ---- once per block: slots of the channels read, tables, weights ----
-  if (tid == 0) {
-    int n = 0, np = 0;
-    for (int c = 0; c < kDim; ++c) {
-      const int t = tk[(int64_t)ux * kDim + c];
-      if (t > 0) {
-        cch[n] = (uint8_t)c;
-        cdp[n] = (uint8_t)t;
-        for (int p = 0; p < t; ++p) pairs[np++] = (uint16_t)(n << 3 | p);
-        ++n;
-      }
-    }
-    nslot_s = n;
-    npair_s = np;
-  }
+  // ---- once per block: depths, the centroid table ----
   const float* cent = reinterpret_cast<const float*>(cb + C.cent);
-  for (int i = tid; i < 511; i += 256) ctab[i] = (double)cent[i];
-  for (int i = tid; i < GQA * kDim; i += 256)
-    qraw[i / kDim][i % kDim] = load_elem<DT>(q, hrow0 * kDim + i);
+  for (int i = tid; i < 9 * 256; i += 256) {
+    const int t = i >> 8, X = i & 255;
+    ftab[i] = cent[(1 << t) - 1 + (X >> (8 - t))];
+  }
+  if (tid < kDim / 4) tk4s[tid] = reinterpret_cast<const uint32_t*>(tk + (int64_t)ux * kDim)[tid];
   double qbv[GQA];
   bool qbad = false;
 #pragma unroll
@@ -942,70 +933,124 @@ __global__ __launch_bounds__(256, 2) void k_score_lloyd(const uint8_t* store, co
     qbv[hh] = qb[hrow0 + hh];
     qbad |= !isfinite(qbv[hh]);
   }
+  // weights and depths through the scalar unit (bases forced uniform: a
+  // per-lane use of the same address elsewhere would otherwise move them to
+  // vector registers and the loads to the vector memory path)
+  auto uniform_ptr = [](const void* p) -> uint64_t {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+  };
+  const cdptr wsc = (cdptr)uniform_ptr(qw + (int64_t)ux * kDim * GQA);
+  const cuptr tsc = (cuptr)uniform_ptr(tk + (int64_t)ux * kDim);
   __syncthreads();
-  const int nslot = nslot_s, npair = npair_s;
-  const float* sgk = reinterpret_cast<const float*>(cb + C.sigk) + g * kDim;
-  for (int i = tid; i < nslot * GQA; i += 256) {
-    const int n = i / GQA, hh = i % GQA;
-    const int c = cch[n];
-    wq[n][hh] = __dmul_rn(qp[(hrow0 + hh) * kDim + c], (double)sgk[c]);
-  }
+  // un-plane role: channels 4 cq .. 4 cq + 3, 32-token word kwd of the tile
+  const int cq = tid >> 3, kwd = tid & 7;
+  const uint32_t t4u = tk4s[cq];
 
-  const int kw = tid >> 5, bit = tid & 31;  // the thread's word of a 256-token line, its bit
   for (int tile = (int)blockIdx.y; tile < ntl; tile += ny) {
     const int64_t t0 = (int64_t)tile * kTile;
-    // stage the chosen planes of this half of key tile tile / 2
-    const uint32_t* kt = u.kplanes + (int64_t)(tile >> 1) * kDim * W * 16 + 8 * (tile & 1);
-    __syncthreads();  // the previous tile's words (and the set-up) are done with
-    for (int i = tid; i < 2 * npair; i += 256) {
-      const int pr = pairs[i >> 1], piece = i & 1;
-      const int n = pr >> 3, pl = pr & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(kt + ((int)cch[n] * W + pl) * 16 + 4 * piece);
-      stg[4 * piece + 0][n][pl] = v.x;
-      stg[4 * piece + 1][n][pl] = v.y;
-      stg[4 * piece + 2][n][pl] = v.z;
-      stg[4 * piece + 3][n][pl] = v.w;
+    // ---- 1. un-plane this half of key tile tile / 2 ----
+    {
+      const uint32_t* kt = u.kplanes + (int64_t)(tile >> 1) * kDim * W * 16 + 8 * (tile & 1) + kwd;
+      uint32_t w[4][8];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int t = (t4u >> (8 * s4)) & 0xFF;
+        const uint32_t* ln = kt + (4 * cq + s4) * W * 16;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) w[s4][p] = (p < t) ? ln[p * 16] : 0u;
+      }
+      __syncthreads();  // the previous tile's codes are done with
+      // per octet o of the word: code bytes of tokens 32 kwd + 8 o + i
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        uint32_t lo[4], hi[4];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          // byte 7 - p = byte o of plane p's word
+          const uint32_t b76 = __builtin_amdgcn_perm(w[s4][6], w[s4][7], (uint32_t)(o | ((o + 4) << 8)) | 0x0C0C0000u);
+          const uint32_t b54 = __builtin_amdgcn_perm(w[s4][4], w[s4][5], (uint32_t)(o | ((o + 4) << 8)) | 0x0C0C0000u);
+          const uint32_t b32 = __builtin_amdgcn_perm(w[s4][2], w[s4][3], (uint32_t)(o | ((o + 4) << 8)) | 0x0C0C0000u);
+          const uint32_t b10 = __builtin_amdgcn_perm(w[s4][0], w[s4][1], (uint32_t)(o | ((o + 4) << 8)) | 0x0C0C0000u);
+          lo[s4] = b76 | (b54 << 16);  // bytes: plane 7, 6, 5, 4
+          hi[s4] = b32 | (b10 << 16);  // bytes: plane 3, 2, 1, 0
+          transpose8_halves(lo[s4], hi[s4]);
+        }
+        // 4 x 4 byte transposes: token i's word holds the four channels' codes
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t* v = half ? hi : lo;
+          const uint32_t a01l = __builtin_amdgcn_perm(v[1], v[0], 0x05010400u);  // x0 y0 x1 y1 (bytes 0,1)
+          const uint32_t a01h = __builtin_amdgcn_perm(v[1], v[0], 0x07030602u);  // bytes 2,3
+          const uint32_t a23l = __builtin_amdgcn_perm(v[3], v[2], 0x05010400u);
+          const uint32_t a23h = __builtin_amdgcn_perm(v[3], v[2], 0x07030602u);
+          const uint32_t tok0 = __builtin_amdgcn_perm(a23l, a01l, 0x05040100u);
+          const uint32_t tok1 = __builtin_amdgcn_perm(a23l, a01l, 0x07060302u);
+          const uint32_t tok2 = __builtin_amdgcn_perm(a23h, a01h, 0x05040100u);
+          const uint32_t tok3 = __builtin_amdgcn_perm(a23h, a01h, 0x07060302u);
+          const int j0 = 32 * kwd + 8 * o + 4 * half;
+          codes[(j0 + 0) * CS + cq] = tok0;
+          codes[(j0 + 1) * CS + cq] = tok1;
+          codes[(j0 + 2) * CS + cq] = tok2;
+          codes[(j0 + 3) * CS + cq] = tok3;
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
+    // ---- 2. logits (uniform control flow: the channel loop's depths and
+    // weights are scalar loads) ----
     const int64_t tok = t0 + tid;
     double sv[GQA];
-    if (tok < Tp) {
+    {
       double acc[GQA];
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
-      for (int n = 0; n < nslot; ++n) {
-        const int t = cdp[n];
-        const uint4 w0 = *reinterpret_cast<const uint4*>(&stg[kw][n][0]);
-        uint4 w1 = make_uint4(0u, 0u, 0u, 0u);
-        if (t > 4) w1 = *reinterpret_cast<const uint4*>(&stg[kw][n][4]);
-        const uint32_t ws[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-        uint32_t P = 0;
+      for (int c4 = 0; c4 < kDim / 4; ++c4) {
+        const uint32_t t4 = tsc[c4];
+        if (t4 == 0u) continue;
+        const uint32_t x4 = codes[tid * CS + c4];
+        float cv[4];
 #pragma unroll
-        for (int pl = 0; pl < 8; ++pl)
-          if (pl < t) P = (P << 1) | ((ws[pl] >> bit) & 1u);
-        const double cv = ctab[(1 << t) - 1 + P];
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const uint32_t t = (t4 >> (8 * s4)) & 0xFFu;
+          cv[s4] = ftab[(t << 8) | ((x4 >> (8 * s4)) & 0xFFu)];
+        }
+        // (a channel at depth 0 looks up table row 0, which is zero: its
+        // fused multiply-adds add an exact zero)
+        double wq[4][GQA];
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(wq[n][hh], cv, acc[hh]);
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+          for (int hh = 0; hh < GQA; ++hh) wq[s4][hh] = wsc[(4 * c4 + s4) * GQA + hh];
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+          for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(wq[s4][hh], (double)cv[s4], acc[hh]);
       }
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) sv[hh] = __dmul_rn(__dadd_rn(qbv[hh], acc[hh]), kInvSqrt128);
-    } else if (tok < len) {
-      // the open group, exact keys
+    }
+    if (t0 + kTile > Tp) {
+      // the open group's tokens are in this tile: exact keys (rows clamped
+      // for the other threads, whose values are not used)
+      const int64_t row = min(max(tok - Tp, (int64_t)0), (int64_t)(kGroup - 1));
       double acc[GQA];
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
       for (int c = 0; c < kDim; ++c) {
-        const double kv = load_elem<DT>(u.ktail, (tok - Tp) * kDim + c);
+        const double kv = load_elem<DT>(u.ktail, row * kDim + c);
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(qraw[hh][c], kv, acc[hh]);
+        for (int hh = 0; hh < GQA; ++hh)
+          acc[hh] = fma(load_elem<DT>(q, (hrow0 + hh) * kDim + c), kv, acc[hh]);
       }
+      if (tok >= Tp) {
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) sv[hh] = __dmul_rn(acc[hh], kInvSqrt128);
-    } else {
-#pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) sv[hh] = -INFINITY;
+        for (int hh = 0; hh < GQA; ++hh) sv[hh] = tok < len ? __dmul_rn(acc[hh], kInvSqrt128) : -INFINITY;
+      }
     }
-    // tile max and sum of exp per head
+    // ---- 3. tile max and sum of exp per head; the logits out ----
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
       const double m = wave_max(sv[hh]);

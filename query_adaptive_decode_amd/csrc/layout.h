@@ -166,7 +166,7 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 //   opart  f32 [B][H][nchunk][d]  partial outputs, one per run of chunks
 //                                 (at most nchunk runs)
 //   Lloyd-tree code only:
-//   qp     f64 [B][H][d]          transformed query U_K q
+//   qp     f64 [B][G][d][H/G]     the score's weights q'_hc sigma^K_c, q' = U_K q
 //   qb     f64 [B][H]             sum_c q'_c mu^K_c
 //   otail  f32 [B][H][d]          the open group's share of the output
 struct WsLayout {
