@@ -889,7 +889,8 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
 // m) / Z from it, so that equal logits anywhere in the context give
 // bitwise-equal weights (every token shares the calibrated mean at depth 0,
 // so ties across tiles are common here).  A unit whose query is not finite
-// (qb NaN) writes NaN partials and NaN logits.
+// (qb NaN) writes NaN partials and NaN logits.  Barriers order LDS only: the
+// next tile's plane words stay in flight across them.
 // ---------------------------------------------------------------------------
 typedef const double __attribute__((address_space(4)))* cdptr;
 typedef const uint32_t __attribute__((address_space(4)))* cuptr;
@@ -944,25 +945,35 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
   };
   const cdptr wsc = (cdptr)uniform_ptr(qw + (int64_t)ux * kDim * GQA);
   const cuptr tsc = (cuptr)uniform_ptr(tk + (int64_t)ux * kDim);
-  __syncthreads();
+  lds_barrier();
   // un-plane role: channels 4 cq .. 4 cq + 3, 32-token word kwd of the tile
   const int cq = tid >> 3, kwd = tid & 7;
   const uint32_t t4u = tk4s[cq];
+
+  // the plane words of this thread's four channels and word of tile `tile`
+  // (buffer loads: planes past a channel's depth take an offset beyond the
+  // buffer and read zero), loaded one tile ahead
+  uint32_t w[4][8];
+  auto load_words = [&](int tile) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        u.kplanes + (int64_t)(tile >> 1) * kDim * W * 16, (short)0, kDim * W * 16 * 4, kBufWord3);
+    const int wo = 8 * (tile & 1) + kwd;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int t = (t4u >> (8 * s4)) & 0xFF;
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        w[s4][p] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, p < t ? (((4 * cq + s4) * W + p) * 16 + wo) * 4 : kBufOff, 0, 0);
+    }
+  };
+  load_words((int)blockIdx.y);
 
   for (int tile = (int)blockIdx.y; tile < ntl; tile += ny) {
     const int64_t t0 = (int64_t)tile * kTile;
     // ---- 1. un-plane this half of key tile tile / 2 ----
     {
-      const uint32_t* kt = u.kplanes + (int64_t)(tile >> 1) * kDim * W * 16 + 8 * (tile & 1) + kwd;
-      uint32_t w[4][8];
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const int t = (t4u >> (8 * s4)) & 0xFF;
-        const uint32_t* ln = kt + (4 * cq + s4) * W * 16;
-#pragma unroll
-        for (int p = 0; p < 8; ++p) w[s4][p] = (p < t) ? ln[p * 16] : 0u;
-      }
-      __syncthreads();  // the previous tile's codes are done with
+      lds_barrier();  // the previous tile's codes are done with
       // per octet o of the word: code bytes of tokens 32 kwd + 8 o + i
 #pragma unroll
       for (int o = 0; o < 4; ++o) {
@@ -997,7 +1008,8 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
           codes[(j0 + 3) * CS + cq] = tok3;
         }
       }
-      __syncthreads();
+      if (tile + ny < ntl) load_words(tile + ny);  // lands during this tile's logits
+      lds_barrier();
     }
     // ---- 2. logits (uniform control flow: the channel loop's depths and
     // weights are scalar loads) ----
@@ -1056,7 +1068,7 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
       const double m = wave_max(sv[hh]);
       if (lane == 0) redm[wv][hh] = m;
     }
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int hh = 0; hh < GQA; ++hh) {
       const double mt = fmax(fmax(redm[0][hh], redm[1][hh]), fmax(redm[2][hh], redm[3][hh]));
@@ -1068,7 +1080,7 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
       const double z = wave_sum(e);
       if (lane == 0) redz[wv][hh] = z;
     }
-    __syncthreads();
+    lds_barrier();
     if (tid < GQA) {
       const double mt = fmax(fmax(redm[0][tid], redm[1][tid]), fmax(redm[2][tid], redm[3][tid]));
       double* tp = tilepart + ((hrow0 + tid) * ntile_ws + tile) * 2;
@@ -1149,8 +1161,9 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   __shared__ __attribute__((aligned(4))) uint8_t tvs[kChunk];
   __shared__ float fs[GQA];
   __shared__ __attribute__((aligned(16))) _Float16 ezero[8];  // a zero weight operand
-  // Lloyd code: centroid tile [channel][token], the fp16 table, mu and sigma
-  constexpr int XHS = kChunk + 8;
+  // Lloyd code: centroid tile [channel][token] (8-token blocks XOR-swizzled
+  // per row, see xh_at), the fp16 table, mu and sigma
+  constexpr int XHS = kChunk;
   __shared__ __attribute__((aligned(16))) _Float16 xh[LL ? kDim * XHS : 8];
   __shared__ _Float16 vts[LL ? 9 * 256 : 1];
   __shared__ float mus[LL ? kDim : 1], sgs[LL ? kDim : 1];
@@ -1175,6 +1188,14 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
   const uint8_t* tvu = tv + ((int64_t)b * G + g) * capmax;
   if (tid < 4) reinterpret_cast<uint32_t*>(ezero)[tid] = 0u;  // read after the first barrier
+  // element (row, token j) of the centroid tile: block j / 8 of the row is
+  // stored at block (j / 8) ^ f(row), f(row) = (row / 8) ^ 2 (row % 8), so
+  // that the un-plane's stores (16 rows 8 apart) and the MFMA operand reads
+  // (16 consecutive rows) each touch 16 different 16-byte blocks
+  auto xh_at = [](int row, int j) __attribute__((always_inline)) -> int {
+    const int f = ((row >> 3) & 15) ^ ((row & 7) << 1);
+    return row * XHS + ((((j >> 3) ^ f) << 3) | (j & 7));
+  };
   if constexpr (LL) {  // (read after the first barrier)
     const CodecLayout CL = codec_layout(G, kDim);
     const _Float16* vt = reinterpret_cast<const _Float16*>(cblk + CL.vtab);
@@ -1356,7 +1377,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t X = ((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFFu;
-          xh[(8 * L + i) * XHS + j] = vts[tb + (int)X];
+          xh[xh_at(8 * L + i, j)] = vts[tb + (int)X];
         }
       } else {
         *reinterpret_cast<uint2*>(xl + j * XS + 8 * L) = make_uint2(lo, hi);
@@ -1390,7 +1411,7 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
           const int t0 = kGroup * gl + 8 * kb;
           f16x8 av;
           if constexpr (LL) {
-            av = *reinterpret_cast<const f16x8*>(&xh[(cbk + m) * XHS + t0]);
+            av = *reinterpret_cast<const f16x8*>(&xh[xh_at(cbk + m, t0)]);
           } else {
             const uint2 xv = __builtin_bit_cast(uint2, tr8_read(xl + (t0 + (m >> 1)) * XS + cbk + 8 * (m & 1)));
             uint32_t ap[4];
