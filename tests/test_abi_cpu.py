@@ -49,7 +49,8 @@ def test_config_validation_codes():
     assert b.validate_config(ok) == 0
     cases = {
         -1: [dict(W=0), dict(W=9), dict(num_q_heads=30, num_kv_heads=8), dict(batch=0),
-             dict(capacity_tokens=0), dict(num_kv_heads=0), dict(capacity_tokens=(1 << 26) + 1)],
+             dict(capacity_tokens=0), dict(num_kv_heads=0), dict(capacity_tokens=(1 << 26) + 1),
+             dict(codec=2), dict(codec=-1)],
         -4: [dict(kv_dtype=7)],
         -5: [dict(head_dim=64), dict(group_tokens=16), dict(num_q_heads=80, num_kv_heads=8)],
     }
@@ -79,6 +80,44 @@ def test_store_size_matches_format_description():
     with pytest.raises(b.ReadKVError):
         b.store_bytes(cfg, [64, 65])           # above capacity_tokens
     assert b.workspace_bytes(cfg) > 0
+    # the Lloyd code: a codec block between the header and the regions
+    for (B, G, cap) in [(1, 1, 1024), (16, 8, 8320)]:
+        c0 = b.make_config(num_q_heads=4 * G, num_kv_heads=G, batch=B, capacity_tokens=cap)
+        c1 = b.make_config(num_q_heads=4 * G, num_kv_heads=G, batch=B, capacity_tokens=cap,
+                           codec=b.CODEC_LLOYD)
+        assert b.store_bytes(c1) == b.store_bytes(c0) + F.codec_block_bytes(G, 128)
+        # logits (8 bytes per token and query head) in place of exponentials (4)
+        assert b.workspace_bytes(c1) >= b.workspace_bytes(c0) + B * 4 * G * cap * 4
+
+
+def test_lloyd_tree_table_equals_the_oracles():
+    """The library builds the tree on the host in its own code; its float32
+    centroids, boundaries and gains equal the oracle's bit for bit."""
+    b = _lib_or_skip()
+    import numpy as np
+    from oracle import lloyd as L
+    cent, bnd, gains = b.codec_tables()
+    T = L.lloyd_tree()
+    assert np.array_equal(np.array(cent, dtype=np.float64), T.flat_centroids32())
+    assert np.array_equal(np.array(bnd), np.concatenate([T.bounds[t] for t in range(8)]))
+    assert np.array_equal(np.array(gains), T.gains32)
+
+
+def test_codec_init_rejects_bad_arguments():
+    b = _lib_or_skip()
+    cfg = b.make_config(num_q_heads=8, num_kv_heads=2, batch=1, capacity_tokens=64)
+    P = ctypes.c_void_p
+    fake = P(0x1000)
+    # a uniform-code store, then a Lloyd store with bad signs / sizes: all
+    # rejected on the host before any device access
+    assert b.lib().readkv_codec_init(ctypes.byref(cfg), fake, None, None, fake, fake, 8, None) == -1
+    cl = b.make_config(num_q_heads=8, num_kv_heads=2, batch=1, capacity_tokens=64,
+                       codec=b.CODEC_LLOYD)
+    bad = (ctypes.c_int8 * 128)(*([1] * 127 + [0]))
+    assert b.lib().readkv_codec_init(ctypes.byref(cl), fake, ctypes.cast(bad, P), None, fake, fake,
+                                     8, None) == -1
+    assert b.lib().readkv_codec_init(ctypes.byref(cl), fake, None, None, fake, fake, 0, None) == -1
+    assert b.lib().readkv_codec_init(ctypes.byref(cl), fake, None, None, None, fake, 8, None) == -1
 
 
 def test_entry_points_reject_bad_arguments_before_launch():
