@@ -313,3 +313,18 @@ def test_lloyd_decode_full_shape_sampled(record_property):
     cfg = synth.workload(2)
     r = LloydRun(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 2.0)])
     _check_decode(r, record_property, "full shape sampled", units=[(0, 0), (5, 3), (11, 6), (15, 7)])
+
+
+@pytest.mark.parametrize("wid,rates,units", [
+    # long context, 131k tokens: the split value path (weights on all compute
+    # units, then one selection block per unit reading them from memory)
+    (3, [(4.0, 4.0), (2.0, 2.0)], [(0, 0), (3, 7)]),
+    # large batch, GQA 7, ragged 2k..32k prompts
+    (4, [(6.0, 6.0), (2.0, 2.0)], [(0, 0), (17, 2), (63, 3)]),
+    # encode + decode mix at its own shape and rates
+    (5, [(3.0, 3.0), (3.5, 2.5)], [(0, 0), (31, 7)]),
+])
+def test_lloyd_decode_other_workloads_sampled(wid, rates, units, record_property):
+    cfg = synth.workload(wid)
+    r = LloydRun(cfg, steps=1, rates=rates)
+    _check_decode(r, record_property, f"workload {wid} sampled", units=units)
