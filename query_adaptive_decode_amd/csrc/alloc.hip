@@ -234,7 +234,7 @@ __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int
     Z = wave_sum(Z);
     if (lane == 0) {
       mh[hh] = m;
-      zh[hh] = Z;
+      zh[hh] = 1.0 / Z;
     }
     if (lane < TPC && t0 + lane < ntile_b) {
       const double f = exp(tp[2 * (t0 + lane)] - m) / Z;
@@ -249,11 +249,11 @@ __global__ __launch_bounds__(256) void k_value_weights(const uint8_t* store, int
 #pragma unroll
   for (int hh = 0; hh < GQA; ++hh) {
     if constexpr (LL) {
-      // alpha = exp(s - m) / Z from the logit: equal logits, equal weights
+      // alpha = exp(s - m) (1/Z) from the logit: equal logits, equal weights
       const double lg[4] = {ld[hh][0].x, ld[hh][0].y, ld[hh][1].x, ld[hh][1].y};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const double x = __ddiv_rn(exp_nonpos(lg[k] - mh[hh]), zh[hh]);
+        const double x = __dmul_rn(exp_nonpos(lg[k] - mh[hh]), zh[hh]);
         s[k] = __dadd_rn(s[k], __dmul_rn(x, x));
       }
     } else {
@@ -464,7 +464,7 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
     const double Z = wave_sum(zt * x);
     if (lane == 0) {
       mh[hh] = m;
-      zh[hh] = Z;
+      zh[hh] = 1.0 / Z;
     }
     if (lane < ntile_b) {
       const double f = x / Z;
@@ -496,11 +496,11 @@ __global__ __launch_bounds__(kVSelNT) void k_value_alloc_unit(
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) {
         if constexpr (LL) {
-          // alpha = exp(s - m) / Z from the logit: equal logits, equal weights
+          // alpha = exp(s - m) (1/Z) from the logit: equal logits, equal weights
           const double lg[4] = {ld[hh][0].x, ld[hh][0].y, ld[hh][1].x, ld[hh][1].y};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const double xq = __ddiv_rn(exp_nonpos(lg[q] - mh[hh]), zh[hh]);
+            const double xq = __dmul_rn(exp_nonpos(lg[q] - mh[hh]), zh[hh]);
             sa[q] = __dadd_rn(sa[q], __dmul_rn(xq, xq));
           }
         } else {

@@ -1019,8 +1019,10 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
       double acc[GQA];
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
+      uint32_t t4n = tsc[0];  // the next quad's depths, loaded a quad ahead
       for (int c4 = 0; c4 < kDim / 4; ++c4) {
-        const uint32_t t4 = tsc[c4];
+        const uint32_t t4 = t4n;
+        if (c4 + 1 < kDim / 4) t4n = tsc[c4 + 1];
         if (t4 == 0u) continue;
         const uint32_t x4 = codes[tid * CS + c4];
         float cv[4];
@@ -1045,21 +1047,32 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
       for (int hh = 0; hh < GQA; ++hh) sv[hh] = __dmul_rn(__dadd_rn(qbv[hh], acc[hh]), kInvSqrt128);
     }
     if (t0 + kTile > Tp) {
-      // the open group's tokens are in this tile: exact keys (rows clamped
-      // for the other threads, whose values are not used)
-      const int64_t row = min(max(tok - Tp, (int64_t)0), (int64_t)(kGroup - 1));
-      double acc[GQA];
+      // the open group's tokens are in this tile: exact keys and query,
+      // staged in the code tile's LDS (dead by now) as fp32 keys [32][d]
+      // (exact for both input types) and fp64 query rows [GQA][d]
+      float* tkey = reinterpret_cast<float*>(codes);
+      double* tq = reinterpret_cast<double*>(codes + kGroup * kDim);
+      static_assert(kGroup * kDim + 2 * GQA * kDim <= kTile * CS, "fits the code tile");
+      const int ntl_tok = (int)(len - Tp);
+      lds_barrier();  // every thread is done with the codes
+      for (int i = tid; i < ntl_tok * kDim; i += 256) tkey[i] = (float)load_elem<DT>(u.ktail, i);
+      for (int i = tid; i < GQA * kDim; i += 256) tq[i] = load_elem<DT>(q, hrow0 * kDim + i);
+      lds_barrier();
+      if (tok >= Tp && tok < len) {
+        const float* kr = tkey + (tok - Tp) * kDim;
+        double acc[GQA];
 #pragma unroll
-      for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
-      for (int c = 0; c < kDim; ++c) {
-        const double kv = load_elem<DT>(u.ktail, row * kDim + c);
+        for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
+        for (int c = 0; c < kDim; ++c) {
+          const double kv = (double)kr[c];
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh)
-          acc[hh] = fma(load_elem<DT>(q, (hrow0 + hh) * kDim + c), kv, acc[hh]);
-      }
-      if (tok >= Tp) {
+          for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(tq[hh * kDim + c], kv, acc[hh]);
+        }
 #pragma unroll
-        for (int hh = 0; hh < GQA; ++hh) sv[hh] = tok < len ? __dmul_rn(acc[hh], kInvSqrt128) : -INFINITY;
+        for (int hh = 0; hh < GQA; ++hh) sv[hh] = __dmul_rn(acc[hh], kInvSqrt128);
+      } else if (tok >= len) {
+#pragma unroll
+        for (int hh = 0; hh < GQA; ++hh) sv[hh] = -INFINITY;
       }
     }
     // ---- 3. tile max and sum of exp per head; the logits out ----
