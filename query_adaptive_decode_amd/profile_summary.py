@@ -40,7 +40,7 @@ NAMES = [("k_append_small", "append"), ("k_key_alloc", "key_alloc"), ("k_score",
          ("k_value_alloc_unit", "value_alloc"), ("k_value_weights", "value_weights"),
          ("k_value_select", "value_select"), ("k_gather", "value_gather"),
          ("k_out_reduce", "out_reduce")]
-STEP_KERNELS = [n for _, n in NAMES]
+STEP_KERNELS = list(dict.fromkeys(n for _, n in NAMES))
 # the prompt's encoding (one launch each per rate, when its store is filled)
 PREFILL = [("k_encode_tiles", "encode_tiles"), ("k_ek_update", "encode_ek"),
            ("k_tail_update", "encode_tail")]
