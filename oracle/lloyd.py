@@ -7,10 +7,10 @@ KV Caches", arXiv 2610.11245) it follows.
 The codec of Sec. 3.1 and App. D.1: every transformed scalar x' of a key or
 value is standardised with a calibrated channel mean and scale,
 z = (x' - mu) / sigma, and stored as its path in a binary tree fitted to
-Z ~ N(0, 1).  Each node splits its interval in two so as to lower the
-probability-weighted squared error, each child reconstructs to its
-conditional mean, and each split sits at Lloyd stationarity (the boundary is
-the midpoint of the two child centroids).  A depth-t prefix of the path
+Z ~ N(0, 1): a node's interval is cut in two where the expected squared
+error under N(0, 1) is lowest, a child reconstructs to E[Z | child], and at
+that cut the boundary equals the average of the two children's
+reconstructions (the Lloyd condition).  A depth-t prefix of the path
 reconstructs to mu + sigma * (centroid of its depth-t cell); depth 0 gives mu.
 
 Readings taken where the pages leave a step open (each is listed in the

@@ -1,8 +1,8 @@
 // The pages' own codec ("Read What Matters: Query-Adaptive Quantization for
-// KV Caches", Sec. 3.1 and App. D.1): a binary tree fitted to Z ~ N(0, 1)
-// whose every node splits its interval at the Lloyd-stationary point (the
-// boundary is the midpoint of the two children's conditional means), and a
-// Hadamard-sign transform with per-channel calibration in front of it.
+// KV Caches", Sec. 3.1 and App. D.1): a binary tree fitted to Z ~ N(0, 1),
+// each node's interval cut where the boundary equals the average of the two
+// children's conditional means (the Lloyd condition), behind a
+// Hadamard-sign transform with per-channel calibration.
 //
 // Host: the depth-8 tree in float64, rounded to the float32 table the
 // decoder reads (centroids, the eight gains Delta_t = D(t-1) - D(t)), and

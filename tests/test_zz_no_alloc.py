@@ -30,17 +30,22 @@ def _prepared(cfg):
     dv = workload.to_device(h)
     lcfg = workload.config_for(cfg, 1)
     cache = Bd.ReadKVCache(lcfg)
+    if cfg.get("codec") == "lloyd":
+        ci = workload.calibration_inputs(cfg, 128)
+        cd = workload.to_device(dict(kcal=ci["kcal"], vcal=ci["vcal"]))
+        Bd.codec_init(lcfg, cache.store, ci["sk"].tolist(), ci["sv"].tolist(), cd["kcal"], cd["vcal"])
     cache.append(dv["kpre"], dv["vpre"], n_new=dv["npre"].to(torch.int32),
                  n_max=dv["kpre"].shape[2])
     cache.append(dv["kstep"][0], dv["vstep"][0])
     return lcfg, cache, dv["q"][0]
 
 
-def test_noalloc_matches_workspace_entry_point_on_two_calls():
+@pytest.mark.parametrize("codec", ["uniform", "lloyd"])
+def test_noalloc_matches_workspace_entry_point_on_two_calls(codec):
     if not torch.cuda.is_available():
         pytest.fail("no GPU visible")
-    cases = [synth.workload(2, B=4, T0=6000),                # larger input first
-             synth.workload(4, B=2, T0=(100, 900))]          # then a smaller one
+    cases = [synth.workload(2, B=4, T0=6000, codec=codec),                # larger input first
+             synth.workload(4, B=2, T0=(100, 900), codec=codec)]          # then a smaller one
     for ci, cfg in enumerate(cases):
         print(f"[case] noalloc {cfg['name']} B={cfg['B']} T0={synth.context_lengths(cfg).tolist()}",
               flush=True)
