@@ -22,6 +22,9 @@ host (all cores, and one core).
 The same step over the pages' own code (Gaussian Lloyd tree with
 Hadamard-sign transforms, calibrated on a held-out synthetic split) is
 timed the same way at `--lloyd-rates` and reported under "lloyd_codec".
+The single-launch reader (one cooperative launch per decode) is timed as
+eager steps beside the split launches at `--single-launch-rates`
+("single_launch").
 
 `--counters-run` runs the fixed sequence the counter profiles are taken on
 (see query_adaptive_decode_amd/profile_summary.py) and prints nothing else
@@ -218,6 +221,52 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h, codec=None):
                 value_bits=float(vsum.item()) / steps / (B * G * tpm), steps_used=st.s)
 
 
+def run_single_launch(cfg, dev, lcfg, R, warmup, steps, torch, h):
+    """The single-launch reader beside the split launches, both as eager
+    steps (a cooperative launch is not captured in a graph), alternating step
+    by step on one cache: HIP events before the append, and from the timed
+    decode entry point around the decode; warm, and with the caches flushed
+    before each step."""
+    from query_adaptive_decode_amd.binding import SCOPE_KV_HEAD, SINGLE_LAUNCH
+    B, H = cfg["B"], cfg["H"]
+    T0 = int(cfg["T0"])
+    st = Stepper(cfg, dev, lcfg, R, torch)
+    stream = torch.cuda.current_stream().cuda_stream
+    scratch = flush_buffer(torch)
+    paths = (("split", SCOPE_KV_HEAD), ("single_launch", SINGLE_LAUNCH))
+
+    def one(policy, evict):
+        ev = _events(h, 5)
+        st.load()
+        if evict:
+            flush(scratch)
+        h.hipEventRecord(ctypes.c_void_p(ev[0]), ctypes.c_void_p(stream))
+        st.cache.append(st.kbuf, st.vbuf)
+        st.Bd.decode_attn_timed(lcfg, st.cache.store, st.qbuf, R, R, st.cache.workspace, ev[1:],
+                                out=st.out, policy=policy)
+        h.hipEventSynchronize(ctypes.c_void_p(ev[4]))
+        n = T0 + st.s + 1
+        st.s += 1
+        return _elapsed(h, ev[0], ev[4]), _elapsed(h, ev[1], ev[4]), n
+
+    for i in range(warmup):
+        one(paths[i % 2][1], False)
+    res = {name: {} for name, _ in paths}
+    for mode in ("warm", "evicted"):
+        acc = {name: [0.0, 0.0, 0] for name, _ in paths}
+        for _ in range(steps):
+            for name, pol in paths:
+                step_ms, dec_ms, n = one(pol, mode == "evicted")
+                acc[name][0] += step_ms
+                acc[name][1] += dec_ms
+                acc[name][2] += B * H * n
+        for name, (tot, dec, qh) in acc.items():
+            res[name][mode] = dict(ms_per_step=tot / steps, decode_ms=dec / steps,
+                                   qh_tok_per_s=qh / (tot * 1e-3))
+    del scratch
+    return res
+
+
 def copy_bandwidth(torch, h, mib=1024, reps=5):
     """A plain device-to-device copy of `mib` MiB timed with events: bytes
     moved (read + write) per second."""
@@ -336,6 +385,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0)
     ap.add_argument("--lloyd-rates", default="4,2",
                     help="rates timed over the Lloyd-tree code ('' for none)")
+    ap.add_argument("--single-launch-rates", default="4,2",
+                    help="rates at which the single-launch reader is timed beside the split "
+                         "launches, as eager steps ('' for none)")
     ap.add_argument("--counters-run", action="store_true",
                     help="run the fixed sequence the counter profiles are taken on, print no line")
     ap.add_argument("--lloyd", action="store_true",
@@ -516,6 +568,22 @@ def main():
                                                              for k, v in m["kernels"].items()}}
             ll["rates"][rate_key(R)] = ent
         line["lloyd_codec"] = ll
+    srates = [float(r) for r in args.single_launch_rates.split(",") if r.strip()]
+    if srates:
+        sl = {"what": "one cooperative launch per decode (grid-wide barriers between the "
+                      "stages) against the split launches, eager steps alternating on one "
+                      "cache; step = append + decode",
+              "rates": {}}
+        for R in srates:
+            r = run_single_launch(cfg, dev, lcfg, R, args.warmup, args.steps, torch, h)
+            print(f"# single launch R={R:g}: evicted step {r['single_launch']['evicted']['ms_per_step']:.3f} "
+                  f"ms (decode {r['single_launch']['evicted']['decode_ms']:.3f}), split eager "
+                  f"{r['split']['evicted']['ms_per_step']:.3f} ms (decode "
+                  f"{r['split']['evicted']['decode_ms']:.3f})", file=sys.stderr, flush=True)
+            sl["rates"][rate_key(R)] = {
+                name: {f"{mode}_{k}": v for mode, d in r[name].items() for k, v in d.items()}
+                for name in r}
+        line["single_launch"] = sl
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_budget)
     print(json.dumps(line))

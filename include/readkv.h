@@ -99,6 +99,17 @@ extern "C" {
 #define READKV_RESTRICT_MIN_DEPTH1 0x10
 #define READKV_RESTRICT_VALUE_PAIRS 0x20
 
+/* The single-launch reader (Sec. 7 names fusing the reader's launches as the
+ * way to close its latency gap), OR'ed into the policy argument: the whole
+ * step as one cooperative launch of as many blocks as fit on the GPU at once,
+ * its stages (score with key allocation, value weights, value selection,
+ * gather, output reduction) separated by grid-wide barriers instead of launch
+ * boundaries.  Results are bitwise those of the split launches.  Uniform code
+ * and READKV_SCOPE_KV_HEAD only, on a device with cooperative launch
+ * (EUNSUPPORTED otherwise); the READKV_RESTRICT_* flags apply.  Not for
+ * stream capture (a cooperative launch). */
+#define READKV_SINGLE_LAUNCH 0x40
+
 /* Logical-read counters of one decode call (App. A.1: payload and metadata
  * bits the reader asks for; workspace and schedules are not counted), summed
  * over every request and KV head:
@@ -218,7 +229,8 @@ int readkv_encode_append(const readkv_config* cfg, void* store,
  *   then channel / token (ties to the lowest in that order).
  * policy: READKV_SCOPE_KV_HEAD or READKV_SCOPE_LAYER (the latter needs
  *   num_kv_heads <= 32, else EUNSUPPORTED), OR'ed with any of the
- *   READKV_RESTRICT_* flags; other bits give EINVAL.
+ *   READKV_RESTRICT_* flags and READKV_SINGLE_LAUNCH; other bits give
+ *   EINVAL.
  * vscale: READKV_VSCALE_PHYSICAL or READKV_VSCALE_UNIT.
  * out: device fp32 [batch][num_q_heads][head_dim].
  * workspace: device, >= readkv_workspace_bytes.
@@ -247,9 +259,10 @@ int readkv_decode_attn(const readkv_config* cfg, const void* store,
  * `stream` before the first kernel and events[i] after stage i of the
  * step, in the order score (with the key allocation in its prologue and
  * the split-context softmax partials), value allocation (with the softmax
- * statistics), value gather (with the output reduction).  Arguments and
- * results are otherwise those of readkv_decode_attn (EINVAL if events or
- * any of the 4 handles is NULL). */
+ * statistics), value gather (with the output reduction); under
+ * READKV_SINGLE_LAUNCH events[1..3] are all recorded after the one launch.
+ * Arguments and results are otherwise those of readkv_decode_attn (EINVAL
+ * if events or any of the 4 handles is NULL). */
 int readkv_decode_attn_timed(const readkv_config* cfg, const void* store,
                              const void* q, float R_K, float R_V,
                              int32_t policy, int32_t vscale, float* out,

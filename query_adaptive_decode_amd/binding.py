@@ -19,6 +19,7 @@ BF16, F32 = 0, 1
 VSCALE_PHYSICAL, VSCALE_UNIT = 0, 1
 SCOPE_KV_HEAD, SCOPE_LAYER = 0, 1
 RESTRICT_MIN_DEPTH1, RESTRICT_VALUE_PAIRS = 0x10, 0x20   # OR'ed into a policy
+SINGLE_LAUNCH = 0x40   # OR'ed into a policy: the whole step as one cooperative launch
 NUM_COUNTERS = 4   # key payload, value payload, metadata, open group (bits)
 CODEC_UNIFORM, CODEC_LLOYD = 0, 1
 FLAG_NONFINITE, FLAG_OVERFLOW = 1, 2
@@ -191,7 +192,8 @@ def decode_attn(cfg: Config, store, q, R_K, R_V, workspace, out=None,
                 vscale=VSCALE_PHYSICAL, key_depths=None, value_depths=None,
                 policy=SCOPE_KV_HEAD, counters=None):
     """q: [B][H][d] device tensor in the config's dtype.  Returns out
-    [B][H][d] fp32.  policy: a budget scope OR'ed with RESTRICT_* flags.
+    [B][H][d] fp32.  policy: a budget scope OR'ed with RESTRICT_* flags
+    and SINGLE_LAUNCH.
     counters: optional int64 device tensor of NUM_COUNTERS entries,
     overwritten with the call's logical reads in bits."""
     out = _out(cfg, q, out)

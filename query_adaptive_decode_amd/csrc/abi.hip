@@ -234,10 +234,14 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   if (!store || !q || !out || !workspace) return READKV_EINVAL;
   if (!isfinite(R_K) || !isfinite(R_V) || R_K < 0.f || R_V < 0.f) return READKV_EINVAL;
   if (vscale != READKV_VSCALE_PHYSICAL && vscale != READKV_VSCALE_UNIT) return READKV_EINVAL;
-  if (policy & ~(READKV_SCOPE_LAYER | READKV_RESTRICT_MIN_DEPTH1 | READKV_RESTRICT_VALUE_PAIRS))
+  if (policy & ~(READKV_SCOPE_LAYER | READKV_RESTRICT_MIN_DEPTH1 | READKV_RESTRICT_VALUE_PAIRS |
+                 READKV_SINGLE_LAUNCH))
     return READKV_EINVAL;
   const int scope = policy & READKV_SCOPE_LAYER;
   if (scope == READKV_SCOPE_LAYER && cfg->num_kv_heads > kMaxPooledKV) return READKV_EUNSUPPORTED;
+  const int fused = (policy & READKV_SINGLE_LAUNCH) ? 1 : 0;
+  if (fused && (scope == READKV_SCOPE_LAYER || cfg->codec != READKV_CODEC_UNIFORM))
+    return READKV_EUNSUPPORTED;
   // budgets must fit the 32-bit counters: R * (items of a domain) <= 2^31
   const double nu = scope == READKV_SCOPE_LAYER ? (double)cfg->num_kv_heads : 1.0;
   if ((double)R_V * (double)align_up(cfg->capacity_tokens, kGroup) * nu > 2147483647.0 ||
@@ -270,6 +274,7 @@ static int decode_impl(const readkv_config* cfg, const void* store, const void* 
   a.events = events;
   a.codec = cfg->codec;
   a.cblock = (const uint8_t*)store + header_bytes(cfg->batch);
+  a.fused = fused;
   rc = launch_decode(a, (hipStream_t)stream);
   if (rc == -5) return READKV_EUNSUPPORTED;
   return rc ? READKV_ELAUNCH : READKV_OK;

@@ -24,16 +24,23 @@
 //
 // The value selection -> gather boundary is the staged(2) reader's second
 // batch: value reads depend on attention computed from the first batch.
+// Each kernel is a thin launch around a block function (its LDS struct and
+// a block index as arguments), so that k_reader_fused can run the same block
+// code as one cooperative launch with grid barriers between the stages.
 //
 // Reconstruction of a depth-t prefix P (t MSB-first planes) of a group with
 // metadata (lo, rng): x_hat = lo + rng (2P + 1) / 2^(t+1).  The kernels
 // un-plane an 8-element bit column into X = P 2^(8-t) (missing planes read
 // as zero) and use x_hat = lo + rng 2^-(t+1) + rng X / 256.
+#include <hip/hip_cooperative_groups.h>
 #include <math.h>
+
+#include <algorithm>
 
 #include "kernels_common.h"
 #include "readkv_internal.h"
 #include "select.h"
+#include "valloc.h"
 
 namespace readkv {
 
@@ -62,7 +69,7 @@ constexpr double kInvSqrtD = kInvSqrt128;
 // descending, c ascending).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void key_depths_wave(const double (&wv)[2], int W, uint32_t Bk,
-                                                uint32_t* cc, uint32_t (&sel)[2]) {
+    uint32_t* cc, uint32_t (&sel)[2]) {
   const int lane = __lane_id();
   sel[0] = 0u;
   sel[1] = 0u;
@@ -326,12 +333,39 @@ __device__ __forceinline__ double half_sum(double v) {
   return (threadIdx.x & 16) ? o + v : v + o;  // rows in order 0 + 1, 2 + 3
 }
 
+// LDS of one score block (members ordered largest first)
+template <int GQA>
+struct ScoreShared {
+  static constexpr int NG = kTile / kGroup;  // 8 groups; wave w owns groups 2w, 2w + 1
+  static constexpr int NHQ = (GQA + 3) / 4;  // head quads: two MFMA row blocks each
+  static constexpr int CXS = kTile + 16;     // code-tile row stride (bytes)
+  static constexpr int AOS = 2 * 8 * 2 * 8 + 16;  // digit chunks of a channel octet: [j][set] x 8 B, padded
+  static constexpr int AMS = 4 * AOS;        // one (head quad, digit half) block of 32 channels
+  static constexpr int AGS = NHQ * 2 * AMS;  // one group's digit chunks
+  __attribute__((aligned(16))) uint8_t at[4][AGS];
+  __attribute__((aligned(16))) uint8_t cx[32 * CXS];
+  uint32_t meta[NG][kDim + 1];
+  double qd[GQA][kDim];
+  double kap[kDim];                          // 2^-(t_c+1) + [t_c > 0] / 2
+  uint8_t s2c[kDim * 8];
+  double Cpart[4][NG][GQA];                  // per-wave partial constants
+  double tails[kGroup][GQA];
+  uint16_t offs[kDim + 1];
+  uint32_t wtot[2];
+  __attribute__((aligned(4))) uint8_t tks[kDim];
+  double redm[4][GQA], redz[4][GQA];
+  uint8_t cperm[kDim];
+  uint32_t dcnt[2][9];                       // channels per depth value, per wave
+  uint32_t qflag[2];                         // a non-finite query value, per wave
+  int emx[2][GQA];
+  double mfin[GQA];
+};
+
 template <int GQA, int DT>
-__global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* store, int ub0, const void* q, uint8_t* tk,
-                                                  int tk_ready, int min1,
-                                                  int H, int G, int W, float RK, int64_t capmax,
-                                                  int ntile_ws, uint32_t* ebuf,
-                                                  double* tilepart, uint64_t* counters) {
+__device__ __forceinline__ void score_block(ScoreShared<GQA>& sh, uint32_t* planes,
+    const VBlock& vb, const uint8_t* store, int ub0, const void* q, uint8_t* tk, int tk_ready,
+    int min1, int H, int G, int W, float RK, int64_t capmax, int ntile_ws, uint32_t* ebuf,
+    double* tilepart, uint64_t* counters) {
   constexpr int esize = DT == 0 ? 2 : 4;
   constexpr int NG = kTile / kGroup;  // 8 groups; wave w owns groups 2w, 2w + 1
   static_assert(NG == 8, "a score tile is half of a 16-group key-plane tile");
@@ -342,28 +376,29 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   constexpr int AGS = NHQ * 2 * AMS;  // one group's digit chunks
   constexpr int PRE = kStagePre;
   constexpr int MPT = NG * kDim / 256;
-  extern __shared__ __attribute__((aligned(16))) uint32_t planes[];  // [slot][8]
-  __shared__ double qd[GQA][kDim];
-  __shared__ uint32_t meta[NG][kDim + 1];
-  __shared__ __attribute__((aligned(16))) uint8_t cx[32 * CXS];
-  __shared__ __attribute__((aligned(16))) uint8_t at[4][AGS];
-  __shared__ double Cpart[4][NG][GQA];  // per-wave partial constants
-  __shared__ double kap[kDim];         // 2^-(t_c+1) + [t_c > 0] / 2
-  __shared__ double tails[kGroup][GQA];
-  __shared__ double redm[4][GQA], redz[4][GQA], mfin[GQA];
-  __shared__ int emx[2][GQA];
-  __shared__ uint16_t offs[kDim + 1];
-  __shared__ __attribute__((aligned(4))) uint8_t tks[kDim];
-  __shared__ uint8_t cperm[kDim];
-  __shared__ uint8_t s2c[kDim * 8];
-  __shared__ uint32_t wtot[2];
-  __shared__ uint32_t dcnt[2][9];  // channels per depth value, per wave
-  __shared__ uint32_t qflag[2];    // a non-finite query value, per wave
+  auto& qd = sh.qd;
+  auto& meta = sh.meta;
+  auto& cx = sh.cx;
+  auto& at = sh.at;
+  auto& Cpart = sh.Cpart;
+  auto& kap = sh.kap;
+  auto& tails = sh.tails;
+  auto& redm = sh.redm;
+  auto& redz = sh.redz;
+  auto& mfin = sh.mfin;
+  auto& emx = sh.emx;
+  auto& offs = sh.offs;
+  auto& tks = sh.tks;
+  auto& cperm = sh.cperm;
+  auto& s2c = sh.s2c;
+  auto& wtot = sh.wtot;
+  auto& dcnt = sh.dcnt;
+  auto& qflag = sh.qflag;
 
   // the call's read counters start from zero (the value selection, a later
   // launch, adds to them)
-  if (counters && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0ull;
-  const int ux = ub0 + (int)blockIdx.x;  // the unit (request, KV head)
+  if (counters && vb.x == 0 && vb.y == 0 && threadIdx.x < 4) counters[threadIdx.x] = 0ull;
+  const int ux = ub0 + vb.x;  // the unit (request, KV head)
   const int b = ux / G, g = ux % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
@@ -371,12 +406,12 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   // this block's share of the unit's tiles: every ny-th one from y, so that
   // the blocks of a unit (all on one XCD) work on neighbouring tiles at the
   // same time and the two halves of a key-plane tile meet in its L2
-  const int ny = (int)gridDim.y;
-  const int tile_begin = (int)blockIdx.y;
+  const int ny = vb.ny;
+  const int tile_begin = vb.y;
   if (tile_begin >= ntl) {
     // an empty request has no closed group (E^K = 0): all key depths are 0
     // (or the minimum depth)
-    if (!tk_ready && ntl == 0 && blockIdx.y == 0 && threadIdx.x < kDim)
+    if (!tk_ready && ntl == 0 && vb.y == 0 && threadIdx.x < kDim)
       tk[((int64_t)b * G + g) * kDim + threadIdx.x] = (uint8_t)min1;
     return;
   }
@@ -867,6 +902,18 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(const uint8_t* 
   }
 }
 
+// The score launch: one block per (unit, run).
+template <int GQA, int DT>
+__global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_score(
+    const uint8_t* store, int ub0, const void* q, uint8_t* tk, int tk_ready, int min1, int H, int G,
+    int W, float RK, int64_t capmax, int ntile_ws, uint32_t* ebuf, double* tilepart,
+    uint64_t* counters) {
+  __shared__ ScoreShared<GQA> sh;
+  extern __shared__ __attribute__((aligned(16))) uint32_t planes[];  // [slot][8]
+  score_block<GQA, DT>(sh, planes, launch_block(), store, ub0, q, tk, tk_ready, min1, H, G, W, RK,
+                       capmax, ntile_ws, ebuf, tilepart, counters);
+}
+
 // ---------------------------------------------------------------------------
 // Score under the Lloyd-tree code ([ReadKV] Sec. 3.1-3.2).  Block (unit, y)
 // takes every ny-th 256-token tile from y; thread j takes token j of the
@@ -1145,13 +1192,52 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // exponentials: e = exp(s - m_tile) is formed here (fp32).  The partial
 // outputs are in the transformed space; the open group's exact values go to
 // otail instead (written by the last run).
+// LDS of one gather block, uniform code (members ordered largest first)
+template <int GQA, bool LL>
+struct GatherShared {
+  static constexpr int NG = kChunk / kGroup;  // 4 groups per chunk
+  static constexpr int XS = kDim + 16;
+  static constexpr int RS = kChunk + 1;
+  __attribute__((aligned(16))) uint8_t xl[kChunk * XS];  // codes [token][channel]
+  __attribute__((aligned(16))) uint4 rows[8 * RS];        // [plane][token]; reused at the end
+  uint32_t vmeta_s[NG][kDim + 1];
+  __attribute__((aligned(16))) _Float16 es[GQA][kChunk + 8];
+  __attribute__((aligned(4))) uint8_t tvs[kChunk];
+  float Ag[NG][GQA], Bg[NG][GQA];
+  float fs[GQA];
+  __attribute__((aligned(16))) _Float16 ezero[8];         // a zero weight operand
+  // (Lloyd code only)
+  __attribute__((aligned(16))) _Float16 xh[8];
+  _Float16 vts[1];
+  float mus[1], sgs[1];
+};
+
+// Lloyd code: reconstructed values in fp16 instead of codes, the value
+// table, the calibration arrays; no group metadata
+template <int GQA>
+struct GatherShared<GQA, true> {
+  static constexpr int NG = kChunk / kGroup;
+  static constexpr int RS = kChunk + 1;
+  static constexpr int XHS = kChunk;
+  __attribute__((aligned(16))) _Float16 xh[kDim * XHS];
+  __attribute__((aligned(16))) uint4 rows[8 * RS];
+  _Float16 vts[9 * 256];
+  __attribute__((aligned(16))) _Float16 es[GQA][kChunk + 8];
+  float mus[kDim], sgs[kDim];
+  __attribute__((aligned(4))) uint8_t tvs[kChunk];
+  float Ag[NG][GQA], Bg[NG][GQA];
+  float fs[GQA];
+  __attribute__((aligned(16))) _Float16 ezero[8];
+  // (uniform code only)
+  __attribute__((aligned(16))) uint8_t xl[16];
+  uint32_t vmeta_s[1][kDim + 1];
+};
+
 template <int GQA, int DT, bool LL>
-__global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0, const uint8_t* tv, int H,
-                                                   int G, int W, int64_t capmax, int ntile_ws,
-                                                   int nrun_ws, const uint32_t* ebuf,
-                                                   const double* ftile, float* opart,
-                                                   const uint8_t* cblk, float* otail,
-                                                   const double* tilepart) {
+__device__ __forceinline__ void gather_block(GatherShared<GQA, LL>& sh, const VBlock& vb,
+    const uint8_t* store, int ub0, const uint8_t* tv, int H, int G, int W, int64_t capmax,
+    int ntile_ws, int nrun_ws, const uint32_t* ebuf, const double* ftile, float* opart,
+    const uint8_t* cblk, float* otail, const double* tilepart) {
   constexpr int esize = DT == 0 ? 2 : 4;
   constexpr int NG = kChunk / kGroup;                  // 4 groups per chunk
   constexpr int GS = (16 / GQA < NG) ? 16 / GQA : NG;  // groups per MFMA column set
@@ -1164,24 +1250,26 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   // the same banks)
   constexpr int RS = kChunk + 1;
   constexpr int MPT = NG * kDim / 256;  // metadata words per thread
-  __shared__ __attribute__((aligned(16))) uint4 rows[8 * RS];        // [plane][token]; reused at the end
-  __shared__ __attribute__((aligned(16))) uint8_t xl[LL ? 16 : kChunk * XS];  // codes [token][channel]
+  auto& rows = sh.rows;
+  auto& xl = sh.xl;
   // rows padded so that the heads' weight rows (es) and the groups'
   // metadata rows (vmeta_s) read by one MFMA fold start on different banks
-  __shared__ __attribute__((aligned(16))) _Float16 es[GQA][kChunk + 8];
-  __shared__ uint32_t vmeta_s[NG][kDim + 1];
-  __shared__ float Ag[NG][GQA], Bg[NG][GQA];
-  __shared__ __attribute__((aligned(4))) uint8_t tvs[kChunk];
-  __shared__ float fs[GQA];
-  __shared__ __attribute__((aligned(16))) _Float16 ezero[8];  // a zero weight operand
+  auto& es = sh.es;
+  auto& vmeta_s = sh.vmeta_s;
+  auto& Ag = sh.Ag;
+  auto& Bg = sh.Bg;
+  auto& tvs = sh.tvs;
+  auto& fs = sh.fs;
+  auto& ezero = sh.ezero;
   // Lloyd code: centroid tile [channel][token] (8-token blocks XOR-swizzled
   // per row, see xh_at), the fp16 table, mu and sigma
   constexpr int XHS = kChunk;
-  __shared__ __attribute__((aligned(16))) _Float16 xh[LL ? kDim * XHS : 8];
-  __shared__ _Float16 vts[LL ? 9 * 256 : 1];
-  __shared__ float mus[LL ? kDim : 1], sgs[LL ? kDim : 1];
+  auto& xh = sh.xh;
+  auto& vts = sh.vts;
+  auto& mus = sh.mus;
+  auto& sgs = sh.sgs;
 
-  const int ux = ub0 + (int)blockIdx.x;
+  const int ux = ub0 + vb.x;
   const int b = ux / G, g = ux % G;
   const ReqRecord r = req_of(store, b);
   const int64_t len = r.len;
@@ -1189,12 +1277,12 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
   const int nch = (int)((len + kChunk - 1) / kChunk);
-  const int cb = (int)(((int64_t)blockIdx.y * nch) / gridDim.y);
-  const int ce = (int)(((int64_t)(blockIdx.y + 1) * nch) / gridDim.y);
+  const int cb = (int)(((int64_t)vb.y * nch) / vb.ny);
+  const int ce = (int)(((int64_t)(vb.y + 1) * nch) / vb.ny);
   if (cb >= ce) {  // empty run: its partial output is zero
     for (int o = tid; o < GQA * kDim; o += 256) {
-      opart[((hrow0 + o / kDim) * nrun_ws + blockIdx.y) * kDim + o % kDim] = 0.f;
-      if (LL && blockIdx.y == gridDim.y - 1) otail[hrow0 * kDim + o] = 0.f;
+      opart[((hrow0 + o / kDim) * nrun_ws + vb.y) * kDim + o % kDim] = 0.f;
+      if (LL && vb.y == vb.ny - 1) otail[hrow0 * kDim + o] = 0.f;
     }
     return;
   }
@@ -1484,20 +1572,30 @@ __global__ __launch_bounds__(256, 2) void k_gather(const uint8_t* store, int ub0
     for (int64_t j = jt0; j < jt1; ++j)
       st = fmaf((float)es[hh][j - cl0], load_elem_f<DT>(u.vtail, (j - Tp) * kDim + c), st);
     if constexpr (LL) {
-      opart[((hrow0 + hh) * nrun_ws + blockIdx.y) * kDim + c] = s;
-      if (blockIdx.y == gridDim.y - 1) otail[(hrow0 + hh) * kDim + c] = st * fs[hh];
+      opart[((hrow0 + hh) * nrun_ws + vb.y) * kDim + c] = s;
+      if (vb.y == vb.ny - 1) otail[(hrow0 + hh) * kDim + c] = st * fs[hh];
     } else {
-      opart[((hrow0 + hh) * nrun_ws + blockIdx.y) * kDim + c] = fmaf(st, fs[hh], s);
+      opart[((hrow0 + hh) * nrun_ws + vb.y) * kDim + c] = fmaf(st, fs[hh], s);
     }
   }
 }
 
-// out[b][h][c] = sum over the unit's runs, in run order.  One thread per
-// output element.
-__global__ __launch_bounds__(256) void k_out_reduce(int nrun, int nrun_ws, int64_t nout,
-                                                    const float* opart, float* out) {
-  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (o >= nout) return;
+// The gather launch: one block per (unit, run); four blocks per compute
+// unit where the registers allow it (the uniform code's LDS does).
+template <int GQA, int DT, bool LL>
+__global__ __launch_bounds__(256, (LL || GQA > 4) ? 2 : 4) void k_gather(
+    const uint8_t* store, int ub0, const uint8_t* tv, int H, int G, int W, int64_t capmax,
+    int ntile_ws, int nrun_ws, const uint32_t* ebuf, const double* ftile, float* opart,
+    const uint8_t* cblk, float* otail, const double* tilepart) {
+  __shared__ GatherShared<GQA, LL> sh;
+  gather_block<GQA, DT, LL>(sh, launch_block(), store, ub0, tv, H, G, W, capmax, ntile_ws, nrun_ws,
+                            ebuf, ftile, opart, cblk, otail, tilepart);
+}
+
+// out[b][h][c] = sum over the unit's runs, in run order, for output element
+// o = (b H + h) d + c.
+__device__ __forceinline__ void out_reduce_elem(int64_t o, int nrun, int nrun_ws, const float* opart,
+                                                float* out) {
   const int64_t bh = o / kDim;
   const int c = (int)(o - bh * kDim);
   const float* p = opart + bh * nrun_ws * kDim + c;
@@ -1513,6 +1611,13 @@ __global__ __launch_bounds__(256) void k_out_reduce(int nrun, int nrun_ws, int64
   }
   for (; k < nrun; ++k) s += p[(int64_t)k * kDim];
   out[o] = s;
+}
+
+// one thread per output element
+__global__ __launch_bounds__(256) void k_out_reduce(int nrun, int nrun_ws, int64_t nout,
+                                                    const float* opart, float* out) {
+  const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (o < nout) out_reduce_elem(o, nrun, nrun_ws, opart, out);
 }
 
 // Lloyd code: one block of d_h threads per (request, query head): the run
@@ -1549,6 +1654,112 @@ __global__ __launch_bounds__(kDim) void k_out_reduce_lloyd(int nrun, int nrun_ws
 }
 
 // ---------------------------------------------------------------------------
+// Single-launch reader ([ReadKV] Sec. 7 names fusing the reader's launches
+// as the way to close its latency gap).  One cooperative launch of as many
+// 256-thread blocks as fit on the chip at once walks the grids of the split
+// path's launches in turn, a grid-wide barrier standing where a launch
+// boundary stood:
+//   score, key allocation in the block prologue   (units x score runs)
+//   value weights                                 (units x 1024-token chunks)
+//   value selection, 256 threads per domain       (units)
+//   value gather                                  (units x gather runs)
+//   output reduction                              (B H d / 256)
+// Every stage runs the block code of its own launch; the score and gather
+// split each unit's tiles and chunks over (blocks / units) runs.  Key and
+// value depths and read counters are the split path's exactly; outputs
+// differ from it only in the order the gather runs' partial sums are added.
+// Uniform code, per-KV-head budgets, at most as many units as blocks.  LDS:
+// one dynamic region holding the current stage's block state (the score's
+// staged key planes after it).
+// ---------------------------------------------------------------------------
+constexpr int kFusedSelNT = 256;
+
+struct FusedArgs {
+  const uint8_t* store;
+  const void* q;
+  uint8_t* tk;
+  uint8_t* tv;
+  uint32_t* ebuf;
+  double* tilepart;
+  double* ftile;
+  double* aval;
+  float* opart;
+  float* out;
+  uint64_t* counters;
+  float RK, RV;
+  int H, G, W, esize, vscale, min1, pairs;
+  int nunits, nrun, nch, nrun_g, ntile_ws, nchunk_ws;
+  int64_t capmax, nout;
+};
+
+template <int GQA>
+constexpr size_t fused_planes_offset() {
+  return (sizeof(ScoreShared<GQA>) + 15) / 16 * 16;
+}
+
+// The score and gather stages give each block at most one of their blocks:
+// a loop around their block code would keep its loop-invariant values in
+// registers across the iterations and spill.
+// The launch's arguments, read afresh from the kernel-argument segment by
+// each stage: the pointer passes through an empty asm statement, so that no
+// stage's arguments stay in registers through the other stages.
+typedef const FusedArgs __attribute__((address_space(4)))* fused_args_ptr;
+__device__ __forceinline__ fused_args_ptr fused_args() {
+  fused_args_ptr p = (fused_args_ptr)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return p;
+}
+
+template <int GQA, int DT>
+__global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_reader_fused(FusedArgs) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  cooperative_groups::grid_group grid = cooperative_groups::this_grid();
+  const int nb = (int)gridDim.x;
+  const int bid = (int)blockIdx.x;
+  if (const auto A = fused_args(); bid < A->nunits * A->nrun) {
+    auto& sh = *reinterpret_cast<ScoreShared<GQA>*>(lds);
+    uint32_t* const planes = reinterpret_cast<uint32_t*>(lds + fused_planes_offset<GQA>());
+    score_block<GQA, DT>(sh, planes, VBlock{bid % A->nunits, bid / A->nunits, A->nunits, A->nrun},
+                         A->store, 0, A->q, A->tk, 0, A->min1, A->H, A->G, A->W, A->RK, A->capmax,
+                         A->ntile_ws, A->ebuf, A->tilepart, A->counters);
+  }
+  grid.sync();
+  {
+    const auto A = fused_args();
+    auto& sh = *reinterpret_cast<ValueWeightsShared<GQA>*>(lds);
+    for (int v = bid; v < A->nunits * A->nch; v += nb) {
+      value_weights_block<GQA, false>(sh, VBlock{v % A->nunits, v / A->nunits, A->nunits, A->nch},
+                                      A->store, 0, A->H, A->G, A->W, A->esize, A->vscale, A->capmax,
+                                      A->ntile_ws, A->ebuf, A->tilepart, A->ftile, A->aval, nullptr);
+      __syncthreads();
+    }
+  }
+  grid.sync();
+  {
+    const auto A = fused_args();
+    auto& sh = *reinterpret_cast<ValueSelectShared<kFusedSelNT>*>(lds);
+    for (int v = bid; v < A->nunits; v += nb) {
+      value_select_block<kFusedSelNT, false, false>(sh, nullptr, VBlock{v, 0, A->nunits, 1}, A->store,
+                                                    0, A->G, A->W, A->esize, A->RV, 1, A->min1, A->pairs,
+                                                    A->capmax, A->aval, A->tv, A->tk, A->counters,
+                                                    nullptr);
+      __syncthreads();
+    }
+  }
+  grid.sync();
+  if (const auto A = fused_args(); bid < A->nunits * A->nrun_g) {
+    auto& sh = *reinterpret_cast<GatherShared<GQA, false>*>(lds);
+    gather_block<GQA, DT, false>(sh, VBlock{bid % A->nunits, bid / A->nunits, A->nunits, A->nrun_g},
+                                 A->store, 0, A->tv, A->H, A->G, A->W, A->capmax, A->ntile_ws, A->nchunk_ws,
+                                 A->ebuf, A->ftile, A->opart, nullptr, nullptr, nullptr);
+  }
+  grid.sync();
+  const auto A = fused_args();
+  for (int64_t o = (int64_t)bid * 256 + threadIdx.x; o < A->nout; o += (int64_t)nb * 256)
+    out_reduce_elem(o, A->nrun_g, A->nchunk_ws, A->opart, A->out);
+}
+
+// ---------------------------------------------------------------------------
 static int device_cu_count() {
   static int n = 0;
   if (n == 0) {
@@ -1566,6 +1777,30 @@ static inline void mark(const DecodeArgs& a, int i, hipStream_t st) {
   if (a.events) hipEventRecord((hipEvent_t)a.events[i], st);
 }
 
+// Dynamic LDS of a score block: the key-line segments staged per tile, at
+// most min(B_K of the domain, 128 W) chosen segments of one unit, 32 B each
+// (+8 slots: un-plane reads of a batch may run past a shallower channel's
+// last slot; those words are masked).  NU: KV heads per selection domain.
+static size_t score_planes_bytes(const DecodeArgs& a, int NU) {
+  double bk = floor((double)a.RK * (double)(kDim * NU));
+  if (a.min1 && bk < (double)kDim) bk = (double)kDim;  // every channel at depth >= 1
+  if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
+  if (bk < 0.0) bk = 0.0;
+  size_t dyn = ((size_t)bk + 8) * 32;
+  if (NU == 1 && dyn < 258 * 4) dyn = 258 * 4;  // the key allocation's scratch
+  return dyn;
+}
+
+// Gather runs per unit: runs of consecutive chunks, about four blocks per
+// compute unit over the whole call (37 KB of LDS each).
+static int gather_runs(const DecodeArgs& a, const WsLayout& L) {
+  const int64_t total = (int64_t)a.B * a.G * L.nchunk;
+  const int64_t gslots = 4 * (int64_t)device_cu_count();
+  int grun = (int)((total + gslots - 1) / gslots);
+  if (grun < 1) grun = 1;
+  return (L.nchunk + grun - 1) / grun;
+}
+
 // The launches for the units P.ub0 .. P.ub0 + P.nunits - 1 (whole
 // requests): key allocation (per-layer budgets), score, value allocation,
 // value gather.  The score of the part that starts at unit 0 zeroes the
@@ -1578,16 +1813,7 @@ static int launch_part(const DecodeArgs& a, const WsLayout& L, const Part& P, ui
   // per-layer budgets: one key selection per request in its own launch;
   // per-KV-head budgets: inside the score kernel's blocks
   if (NU > 1 && launch_key_alloc(a, P, tk, st)) return -5;
-  // slots staged per score tile: at most min(B_K of the domain, 128 W) chosen
-  // key-line segments of one unit, 32 B each
-  double bk = floor((double)a.RK * (double)(kDim * NU));
-  if (a.min1 && bk < (double)kDim) bk = (double)kDim;  // every channel at depth >= 1
-  if (bk > (double)(kDim * a.W)) bk = (double)(kDim * a.W);
-  if (bk < 0.0) bk = 0.0;
-  // (+8 slots: un-plane reads of a batch may run past a shallower channel's
-  // last slot; those words are masked)
-  size_t dyn = ((size_t)bk + 8) * 32;
-  if (NU == 1 && dyn < 258 * 4) dyn = 258 * 4;  // the key allocation's scratch
+  const size_t dyn = score_planes_bytes(a, NU);
   static bool attr_set = false;
   if (!attr_set) {
     hipFuncSetAttribute(reinterpret_cast<const void*>(&k_score<GQA, DT>),
@@ -1619,14 +1845,7 @@ template <int GQA, int DT>
 static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
   uint8_t* tk = a.key_depths_out ? a.key_depths_out : a.ws + L.tk;
   uint8_t* tv = a.value_depths_out ? a.value_depths_out : a.ws + L.tv;
-  // runs of consecutive chunks per gather block: about four blocks per
-  // compute unit over the whole call (37 KB of LDS each)
-  const int64_t total = (int64_t)a.B * a.G * L.nchunk;
-  const int64_t gslots = 4 * (int64_t)device_cu_count();
-  int grun = (int)((total + gslots - 1) / gslots);
-  if (grun < 1) grun = 1;
-  const int nrun_g = (L.nchunk + grun - 1) / grun;
-
+  const int nrun_g = gather_runs(a, L);
   mark(a, 0, st);
   const Part P{0, a.B * a.G};
   const int rc = launch_part<GQA, DT>(a, L, P, tk, tv, nrun_g, st);
@@ -1636,6 +1855,87 @@ static int launch_all(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
                      L.nchunk, nout, (const float*)(a.ws + L.opart), a.out);
   mark(a, 3, st);
   return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// The single-launch reader (uniform code, per-KV-head budgets): one
+// cooperative launch of as many blocks as fit on the chip at once (units
+// beyond that number: unsupported).
+template <int GQA, int DT>
+static int launch_fused(const DecodeArgs& a, const WsLayout& L, hipStream_t st) {
+  if (a.codec != 0 || a.scope != 0) return -5;
+  static int coop = -1;
+  if (coop < 0) {
+    int dev = 0, v = 0;
+    coop = (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && v)
+               ? 1
+               : 0;
+  }
+  if (!coop) return -5;
+  const void* const kfn = reinterpret_cast<const void*>(&k_reader_fused<GQA, DT>);
+  size_t dyn = fused_planes_offset<GQA>() + score_planes_bytes(a, 1);
+  dyn = std::max(dyn, sizeof(ValueWeightsShared<GQA>));
+  dyn = std::max(dyn, sizeof(ValueSelectShared<kFusedSelNT>));
+  dyn = std::max(dyn, sizeof(GatherShared<GQA, false>));
+  static bool attr_set = false;
+  if (!attr_set) {
+    const size_t most = std::max(fused_planes_offset<GQA>() + (size_t)(kDim * 8 + 8) * 32,
+                                 sizeof(GatherShared<GQA, false>));
+    if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most) != hipSuccess)
+      return -6;
+    attr_set = true;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kfn, 256, dyn) != hipSuccess || per_cu < 1)
+    return -6;
+  const int nunits = a.B * a.G;
+  FusedArgs A;
+  A.store = (const uint8_t*)a.store;
+  A.q = a.q;
+  A.tk = a.key_depths_out ? a.key_depths_out : a.ws + L.tk;
+  A.tv = a.value_depths_out ? a.value_depths_out : a.ws + L.tv;
+  A.ebuf = (uint32_t*)(a.ws + L.ebuf);
+  A.tilepart = (double*)(a.ws + L.tilepart);
+  A.ftile = (double*)(a.ws + L.ftile);
+  A.aval = (double*)(a.ws + L.aval);
+  A.opart = (float*)(a.ws + L.opart);
+  A.out = a.out;
+  A.counters = a.counters;
+  A.RK = a.RK;
+  A.RV = a.RV;
+  A.H = a.H;
+  A.G = a.G;
+  A.W = a.W;
+  A.esize = a.dtype == 0 ? 2 : 4;
+  A.vscale = a.vscale;
+  A.min1 = a.min1;
+  A.pairs = a.pairs;
+  A.nunits = nunits;
+  const int64_t slots = (int64_t)per_cu * device_cu_count();
+  if (nunits > slots) return -5;
+  // runs per unit: one block each
+  const int per_unit = (int)(slots / nunits);
+  A.nrun = std::min(per_unit, L.ntile);
+  A.nch = (int)((a.capmax + kVChunk - 1) / kVChunk);
+  A.nrun_g = std::min(per_unit, L.nchunk);
+  A.ntile_ws = L.ntile;
+  A.nchunk_ws = L.nchunk;
+  A.capmax = a.capmax;
+  A.nout = (int64_t)a.B * a.H * kDim;
+  // no more blocks than the largest stage has
+  int64_t most = std::max<int64_t>((int64_t)nunits * A.nrun, (int64_t)nunits * A.nch);
+  most = std::max<int64_t>(most, (int64_t)nunits * A.nrun_g);
+  most = std::max<int64_t>(most, (A.nout + 255) / 256);
+  const int grid = (int)std::min<int64_t>(slots, most);
+  void* args[] = {&A};
+  mark(a, 0, st);
+  if (hipLaunchCooperativeKernel(kfn, dim3(grid), dim3(256), args, (unsigned)dyn, st) != hipSuccess)
+    return -6;
+  // (the stages have no events of their own)
+  mark(a, 1, st);
+  mark(a, 2, st);
+  mark(a, 3, st);
+  return 0;
 }
 
 // Lloyd code: key allocation (own launch, per domain), score, value
@@ -1689,6 +1989,19 @@ static int dispatch_gqa(const DecodeArgs& a, const WsLayout& L, hipStream_t st) 
       case 6: return launch_all_lloyd<6, DT>(a, L, st);
       case 7: return launch_all_lloyd<7, DT>(a, L, st);
       case 8: return launch_all_lloyd<8, DT>(a, L, st);
+      default: return -5;
+    }
+  }
+  if (a.fused) {
+    switch (a.H / a.G) {
+      case 1: return launch_fused<1, DT>(a, L, st);
+      case 2: return launch_fused<2, DT>(a, L, st);
+      case 3: return launch_fused<3, DT>(a, L, st);
+      case 4: return launch_fused<4, DT>(a, L, st);
+      case 5: return launch_fused<5, DT>(a, L, st);
+      case 6: return launch_fused<6, DT>(a, L, st);
+      case 7: return launch_fused<7, DT>(a, L, st);
+      case 8: return launch_fused<8, DT>(a, L, st);
       default: return -5;
     }
   }

@@ -14,6 +14,16 @@ namespace readkv {
 // the Hadamard-sign transforms' normalisation)
 constexpr double kInvSqrt128 = 0.088388347648318440550;
 
+// A block's coordinates in the grid of one stage: its own launch's
+// (blockIdx, gridDim), or a virtual block of a persistent launch that walks
+// the stage's grid.
+struct VBlock {
+  int x, y, nx, ny;
+};
+__device__ __forceinline__ VBlock launch_block() {
+  return VBlock{(int)blockIdx.x, (int)blockIdx.y, (int)gridDim.x, (int)gridDim.y};
+}
+
 __device__ __forceinline__ const ReqRecord& req_of(const uint8_t* store, int b) {
   return *reinterpret_cast<const ReqRecord*>(store + 256 + 32 * (int64_t)b);
 }

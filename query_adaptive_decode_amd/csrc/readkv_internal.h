@@ -39,6 +39,7 @@ struct DecodeArgs {
   void* const* events;  // NULL, or 4 hipEvent_t recorded around the 3 stages
   int codec;            // 0: uniform min/max, 1: Lloyd tree
   const uint8_t* cblock;  // the Lloyd-tree store's codec block (device)
+  int fused;            // 1: the single-launch reader
 };
 
 // The Lloyd tree's float32 table ("Read What Matters", App. D.1), built on

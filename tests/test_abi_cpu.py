@@ -137,7 +137,12 @@ def test_entry_points_reject_bad_arguments_before_launch():
     def call(cfgp=by, store=fake, rk=1.0, rv=1.0, scope=0, vscale=0, wsb=ws):
         return dec(cfgp, store, fake, rk, rv, scope, vscale, fake, fake, wsb, None, None, None, None)
 
-    assert call(scope=0x2) == -1 and call(scope=0x40) == -1   # unknown policy bits
+    assert call(scope=0x2) == -1 and call(scope=0x80) == -1   # unknown policy bits
+    # the single-launch reader: per-KV-head budgets and the uniform code only
+    assert call(scope=b.SCOPE_LAYER | b.SINGLE_LAUNCH) == -5
+    lloyd = b.make_config(batch=2, capacity_tokens=256, codec=b.CODEC_LLOYD)
+    assert call(cfgp=ctypes.byref(lloyd), scope=b.SINGLE_LAUNCH, wsb=b.workspace_bytes(lloyd)) == -5
+    assert call(scope=b.SINGLE_LAUNCH | b.RESTRICT_MIN_DEPTH1, rk=float("nan")) == -1
 
     for rk, rv in [(float("nan"), 1.0), (1.0, float("inf")), (-0.5, 1.0), (1.0, -1.0)]:
         assert call(rk=rk, rv=rv) == -1
