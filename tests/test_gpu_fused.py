@@ -142,6 +142,15 @@ def test_fused_equals_split_gqa7_and_restricted(record_property):
     record_property("worst_rel_l2_vs_split", max(w, w2))
 
 
+@pytest.mark.timeout(900)
+def test_fused_equals_split_large_batch_and_long_prompt_full_shapes(record_property):
+    # B=64, 28 query / 4 KV heads, ragged 2k-32k prompts (256 units, two
+    # blocks per unit at GQA 7); B=32 with 16,384-token prompts (256 units)
+    w = _both_ways(synth.workload(4), steps=1, rates=[(6.0, 6.0), (2.0, 2.0)])
+    w2 = _both_ways(synth.workload(5), steps=1, rates=[(3.3, 2.7)])
+    record_property("worst_rel_l2_vs_split", max(w, w2))
+
+
 def test_fused_rejects_more_units_than_blocks():
     # 260 requests x 8 KV heads: 2080 units, more than the blocks of 256
     # threads that fit on the chip at once (at most 8 per compute unit); the
