@@ -950,7 +950,10 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
                                                         uint32_t* ebuf, double* tilepart) {
   constexpr int CS = kDim / 4 + 1;  // code-word row stride (words): rows 33 banks apart
   __shared__ uint32_t codes[kTile * CS];
-  __shared__ float ftab[9 * 256];  // centroid of depth t, code byte X at 256 t + X
+  // centroid of depth-t cell P at (2^t - 1) + P: a depth's cells are
+  // contiguous, so the up to 2^t distinct entries a lookup at depth t can
+  // touch sit in distinct banks for t <= 5
+  __shared__ float ftab[512];
   __shared__ uint32_t tk4s[kDim / 4];
   __shared__ double redm[4][GQA], redz[4][GQA];
   const CodecLayout C = codec_layout(G, kDim);
@@ -969,10 +972,7 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
 
   // ---- once per block: depths, the centroid table ----
   const float* cent = reinterpret_cast<const float*>(cb + C.cent);
-  for (int i = tid; i < 9 * 256; i += 256) {
-    const int t = i >> 8, X = i & 255;
-    ftab[i] = cent[(1 << t) - 1 + (X >> (8 - t))];
-  }
+  for (int i = tid; i < 512; i += 256) ftab[i] = cent[i];
   if (tid < kDim / 4) tk4s[tid] = reinterpret_cast<const uint32_t*>(tk + (int64_t)ux * kDim)[tid];
   double qbv[GQA];
   bool qbad = false;
@@ -1076,7 +1076,7 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const uint32_t t = (t4 >> (8 * s4)) & 0xFFu;
-          cv[s4] = ftab[(t << 8) | ((x4 >> (8 * s4)) & 0xFFu)];
+          cv[s4] = ftab[((1u << t) - 1u) + (((x4 >> (8 * s4)) & 0xFFu) >> (8u - t))];
         }
         // (a channel at depth 0 looks up table row 0, which is zero: its
         // fused multiply-adds add an exact zero)
@@ -1221,7 +1221,7 @@ struct GatherShared<GQA, true> {
   static constexpr int XHS = kChunk;
   __attribute__((aligned(16))) _Float16 xh[kDim * XHS];
   __attribute__((aligned(16))) uint4 rows[8 * RS];
-  _Float16 vts[9 * 256];
+  _Float16 vts[512];                  // value centroids, compacted per depth
   __attribute__((aligned(16))) _Float16 es[GQA][kChunk + 8];
   float mus[kDim], sgs[kDim];
   __attribute__((aligned(4))) uint8_t tvs[kChunk];
@@ -1300,7 +1300,13 @@ __device__ __forceinline__ void gather_block(GatherShared<GQA, LL>& sh, const VB
   if constexpr (LL) {  // (read after the first barrier)
     const CodecLayout CL = codec_layout(G, kDim);
     const _Float16* vt = reinterpret_cast<const _Float16*>(cblk + CL.vtab);
-    for (int i = tid; i < 9 * 256; i += 256) vts[i] = vt[i];
+    // the table compacted per depth: cell P of depth t at (2^t - 1) + P
+    // (a depth's cells contiguous, so that a lookup's distinct entries
+    // spread over the banks)
+    for (int i = tid; i < 511; i += 256) {
+      const int t = 31 - __builtin_clz(i + 1), P = i + 1 - (1 << t);
+      vts[i] = vt[256 * t + (P << (8 - t))];
+    }
     if (tid < kDim) {
       mus[tid] = reinterpret_cast<const float*>(cblk + CL.muv)[g * kDim + tid];
       sgs[tid] = reinterpret_cast<const float*>(cblk + CL.sigv)[g * kDim + tid];
@@ -1474,11 +1480,12 @@ __device__ __forceinline__ void gather_block(GatherShared<GQA, LL>& sh, const VB
       if (shallow) transpose8_hi4(lo, hi);
       else transpose8_halves(lo, hi);
       if constexpr (LL) {
-        const int tb = 256 * (int)tvs[j];
+        const uint32_t tj = tvs[j];
+        const int tb = (1 << tj) - 1;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const uint32_t X = ((i < 4 ? lo : hi) >> (8 * (i & 3))) & 0xFFu;
-          xh[xh_at(8 * L + i, j)] = vts[tb + (int)X];
+          xh[xh_at(8 * L + i, j)] = vts[tb + (int)(X >> (8u - tj))];
         }
       } else {
         *reinterpret_cast<uint2*>(xl + j * XS + 8 * L) = make_uint2(lo, hi);
