@@ -1066,29 +1066,63 @@ __global__ __launch_bounds__(256, 3) void k_score_lloyd(const uint8_t* store, co
       double acc[GQA];
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) acc[hh] = 0.0;
-      uint32_t t4n = tsc[0];  // the next quad's depths, loaded a quad ahead
-      for (int c4 = 0; c4 < kDim / 4; ++c4) {
-        const uint32_t t4 = t4n;
-        if (c4 + 1 < kDim / 4) t4n = tsc[c4 + 1];
-        if (t4 == 0u) continue;
-        const uint32_t x4 = codes[tid * CS + c4];
-        float cv[4];
+      // software pipeline over the channel quads: quad c's centroid lookups
+      // and weights are in flight during quad c - 1's multiply-adds, its code
+      // word and depths two quads ahead, so that one wait per quad covers
+      // loads issued a quad earlier.  (A channel at depth 0 looks up the
+      // table's entry 0, which is zero; a quad at depth 0 is skipped.)
+      auto lookup = [&](uint32_t t4, uint32_t x4, float (&cv)[4]) __attribute__((always_inline)) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
           const uint32_t t = (t4 >> (8 * s4)) & 0xFFu;
           cv[s4] = ftab[((1u << t) - 1u) + (((x4 >> (8 * s4)) & 0xFFu) >> (8u - t))];
         }
-        // (a channel at depth 0 looks up table row 0, which is zero: its
-        // fused multiply-adds add an exact zero)
-        double wq[4][GQA];
+      };
+      auto weights = [&](int c4, double (&wq)[4][GQA]) __attribute__((always_inline)) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
           for (int hh = 0; hh < GQA; ++hh) wq[s4][hh] = wsc[(4 * c4 + s4) * GQA + hh];
+      };
+      constexpr int NQ = kDim / 4;
+      uint32_t t4c = tsc[0], t4n = tsc[1];
+      uint32_t x4n = codes[tid * CS + 1];
+      float cvc[4];
+      double wqc[4][GQA];
+      lookup(t4c, codes[tid * CS], cvc);
+      weights(0, wqc);
+      // (the prologue's loads complete before the loop: otherwise the loop
+      // head, which merges the first entry with the back edge, waits for them
+      // in every iteration)
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll 2
+      for (int c4 = 0; c4 < NQ; ++c4) {
+        float cvn[4] = {0.f, 0.f, 0.f, 0.f};
+        double wqn[4][GQA];
+        if (c4 + 1 < NQ) {
+          lookup(t4n, x4n, cvn);
+          weights(c4 + 1, wqn);
+        }
+        uint32_t t4nn = 0u, x4nn = 0u;
+        if (c4 + 2 < NQ) {
+          t4nn = tsc[c4 + 2];
+          x4nn = codes[tid * CS + c4 + 2];
+        }
+        if (t4c != 0u) {
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4)
+          for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-          for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(wq[s4][hh], (double)cv[s4], acc[hh]);
+            for (int hh = 0; hh < GQA; ++hh) acc[hh] = fma(wqc[s4][hh], (double)cvc[s4], acc[hh]);
+        }
+        t4c = t4n;
+        t4n = t4nn;
+        x4n = x4nn;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          cvc[s4] = cvn[s4];
+#pragma unroll
+          for (int hh = 0; hh < GQA; ++hh) wqc[s4][hh] = wqn[s4][hh];
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < GQA; ++hh) sv[hh] = __dmul_rn(__dadd_rn(qbv[hh], acc[hh]), kInvSqrt128);
