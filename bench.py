@@ -574,8 +574,16 @@ def main():
                       "stages) against the split launches, eager steps alternating on one "
                       "cache; step = append + decode",
               "rates": {}}
+        from query_adaptive_decode_amd.binding import ReadKVError
         for R in srates:
-            r = run_single_launch(cfg, dev, lcfg, R, args.warmup, args.steps, torch, h)
+            try:
+                r = run_single_launch(cfg, dev, lcfg, R, args.warmup, args.steps, torch, h)
+            except ReadKVError as e:
+                # e.g. a device without cooperative launch: the headline line
+                # still prints, with the reason here
+                sl["rates"][rate_key(R)] = {"error": str(e)}
+                print(f"# single launch R={R:g}: {e}", file=sys.stderr, flush=True)
+                continue
             print(f"# single launch R={R:g}: evicted step {r['single_launch']['evicted']['ms_per_step']:.3f} "
                   f"ms (decode {r['single_launch']['evicted']['decode_ms']:.3f}), split eager "
                   f"{r['split']['evicted']['ms_per_step']:.3f} ms (decode "
