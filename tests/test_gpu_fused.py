@@ -37,6 +37,14 @@ def _gpu():
 
 
 # ------------------------------------------------------------ against the oracle
+def test_fused_tiny_fp32(record_property):
+    # fp32 keys, values and query; one query head on one KV head
+    cfg = synth.workload(1)
+    run = Run(cfg, steps=8, rates=[(4.0, 4.0), (2.0, 2.0), (8.0, 1.0)], scope=SINGLE_LAUNCH,
+              repeat=True)
+    report(record_property, "single launch tiny fp32", run.check())
+
+
 def test_fused_llama_shape_small_context(record_property):
     cfg = synth.workload(2, B=2, T0=2000)
     run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 2.0), (3.3, 2.7)], scope=SINGLE_LAUNCH,
