@@ -1701,8 +1701,9 @@ __global__ __launch_bounds__(kDim) void k_out_reduce_lloyd(int nrun, int nrun_ws
 // path's launches in turn, a grid-wide barrier standing where a launch
 // boundary stood:
 //   score, key allocation in the block prologue   (units x score runs)
-//   value weights                                 (units x 1024-token chunks)
-//   value selection, 256 threads per domain       (units)
+//   value allocation of a unit in one block       (units; capacities up to
+//     16,384 tokens), or value weights            (units x 1024-token chunks)
+//     then value selection                        (units)
 //   value gather                                  (units x gather runs)
 //   output reduction                              (B H d / 256)
 // Every stage runs the block code of its own launch; the score and gather
@@ -1730,6 +1731,8 @@ struct FusedArgs {
   float RK, RV;
   int H, G, W, esize, vscale, min1, pairs;
   int nunits, nrun, nch, nrun_g, ntile_ws, nchunk_ws;
+  int unit_alloc;  // 1: the unit's value allocation in one block (capacity <= kVSelLocal)
+  int reserved;
   int64_t capmax, nout;
 };
 
@@ -1765,26 +1768,41 @@ __global__ __launch_bounds__(256, GQA <= 4 ? 3 : 2) void k_reader_fused(FusedArg
                          A->ntile_ws, A->ebuf, A->tilepart, A->counters);
   }
   grid.sync();
-  {
+  if (fused_args()->unit_alloc) {
+    // capacities up to 16,384 tokens: the value allocation of a unit in one
+    // block, its weights kept in the workspace (read back by the same block)
     const auto A = fused_args();
-    auto& sh = *reinterpret_cast<ValueWeightsShared<GQA>*>(lds);
-    for (int v = bid; v < A->nunits * A->nch; v += nb) {
-      value_weights_block<GQA, false>(sh, VBlock{v % A->nunits, v / A->nunits, A->nunits, A->nch},
-                                      A->store, 0, A->H, A->G, A->W, A->esize, A->vscale, A->capmax,
-                                      A->ntile_ws, A->ebuf, A->tilepart, A->ftile, A->aval, nullptr);
+    auto& sh = *reinterpret_cast<ValueAllocUnitShared<kFusedSelNT, GQA>*>(lds);
+    for (int v = bid; v < A->nunits; v += nb) {
+      value_alloc_unit_block<kFusedSelNT, GQA, false, true>(
+          sh, A->aval + (int64_t)v * A->capmax, VBlock{v, 0, A->nunits, 1}, A->store, 0, A->H, A->G,
+          A->W, A->esize, A->vscale, A->RV, A->min1, A->pairs, A->capmax, A->ntile_ws, A->ebuf,
+          A->tilepart, A->ftile, A->tv, A->tk, A->counters, nullptr);
       __syncthreads();
     }
-  }
-  grid.sync();
-  {
-    const auto A = fused_args();
-    auto& sh = *reinterpret_cast<ValueSelectShared<kFusedSelNT>*>(lds);
-    for (int v = bid; v < A->nunits; v += nb) {
-      value_select_block<kFusedSelNT, false, false>(sh, nullptr, VBlock{v, 0, A->nunits, 1}, A->store,
-                                                    0, A->G, A->W, A->esize, A->RV, 1, A->min1, A->pairs,
-                                                    A->capmax, A->aval, A->tv, A->tk, A->counters,
-                                                    nullptr);
-      __syncthreads();
+  } else {
+    {
+      const auto A = fused_args();
+      auto& sh = *reinterpret_cast<ValueWeightsShared<GQA>*>(lds);
+      for (int v = bid; v < A->nunits * A->nch; v += nb) {
+        value_weights_block<GQA, false>(sh, VBlock{v % A->nunits, v / A->nunits, A->nunits, A->nch},
+                                        A->store, 0, A->H, A->G, A->W, A->esize, A->vscale,
+                                        A->capmax, A->ntile_ws, A->ebuf, A->tilepart, A->ftile,
+                                        A->aval, nullptr);
+        __syncthreads();
+      }
+    }
+    grid.sync();
+    {
+      const auto A = fused_args();
+      auto& sh = *reinterpret_cast<ValueSelectShared<kFusedSelNT>*>(lds);
+      for (int v = bid; v < A->nunits; v += nb) {
+        value_select_block<kFusedSelNT, false, false>(sh, nullptr, VBlock{v, 0, A->nunits, 1},
+                                                      A->store, 0, A->G, A->W, A->esize, A->RV, 1,
+                                                      A->min1, A->pairs, A->capmax, A->aval, A->tv,
+                                                      A->tk, A->counters, nullptr);
+        __syncthreads();
+      }
     }
   }
   grid.sync();
@@ -1917,11 +1935,14 @@ static int launch_fused(const DecodeArgs& a, const WsLayout& L, hipStream_t st) 
   size_t dyn = fused_planes_offset<GQA>() + score_planes_bytes(a, 1);
   dyn = std::max(dyn, sizeof(ValueWeightsShared<GQA>));
   dyn = std::max(dyn, sizeof(ValueSelectShared<kFusedSelNT>));
+  dyn = std::max(dyn, sizeof(ValueAllocUnitShared<kFusedSelNT, GQA>));
   dyn = std::max(dyn, sizeof(GatherShared<GQA, false>));
   static bool attr_set = false;
   if (!attr_set) {
-    const size_t most = std::max(fused_planes_offset<GQA>() + (size_t)(kDim * 8 + 8) * 32,
-                                 sizeof(GatherShared<GQA, false>));
+    const size_t most = std::max({fused_planes_offset<GQA>() + (size_t)(kDim * 8 + 8) * 32,
+                                  sizeof(GatherShared<GQA, false>),
+                                  sizeof(ValueAllocUnitShared<kFusedSelNT, GQA>),
+                                  sizeof(ValueSelectShared<kFusedSelNT>)});
     if (hipFuncSetAttribute(kfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)most) != hipSuccess)
       return -6;
     attr_set = true;
@@ -1958,6 +1979,8 @@ static int launch_fused(const DecodeArgs& a, const WsLayout& L, hipStream_t st) 
   const int per_unit = (int)(slots / nunits);
   A.nrun = std::min(per_unit, L.ntile);
   A.nch = (int)((a.capmax + kVChunk - 1) / kVChunk);
+  A.unit_alloc = a.capmax <= kVSelLocal ? 1 : 0;
+  A.reserved = 0;
   A.nrun_g = std::min(per_unit, L.nchunk);
   A.ntile_ws = L.ntile;
   A.nchunk_ws = L.nchunk;

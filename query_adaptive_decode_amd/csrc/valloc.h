@@ -247,4 +247,179 @@ __device__ __forceinline__ void value_select_block(ValueSelectShared<NT>& sh, do
   }
 }
 
+template <int NT, int GQA>
+struct ValueAllocUnitShared {
+  ChooseShared<NT> S;
+  double gt[16];
+  double fs[GQA][kVSelLocal / kTile];
+  double mh[GQA], zh[GQA];
+};
+
+// NT threads; acache: the unit's weights [T_p], in LDS, or (GCACHE) in
+// device memory that only this block touches
+template <int NT, int GQA, bool LL, bool GCACHE>
+__device__ __forceinline__ void value_alloc_unit_block(ValueAllocUnitShared<NT, GQA>& sh,
+    double* acache, const VBlock& vb, const uint8_t* store, int ub0, int H, int G, int W, int esize,
+    int vscale, float RV, int min1, int pairs, int64_t capmax, int ntile_ws, const uint32_t* ebuf,
+    const double* tilepart, double* ftile, uint8_t* tv, const uint8_t* tk, uint64_t* counters,
+    const uint8_t* cb) {
+  constexpr int RT = 4 * NT;  // tokens per round
+  auto& S = sh.S;
+  auto& gt = sh.gt;
+  auto& fs = sh.fs;
+  const int ux = ub0 + vb.x;
+  const int b = ux / G, g = ux % G;
+  const ReqRecord r = req_of(store, b);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t hrow0 = (int64_t)b * H + (int64_t)g * GQA;
+  const int64_t len = r.len;
+  const int64_t Tp = len & ~(int64_t)(kGroup - 1);
+  const int ntile_b = (int)((len + kTile - 1) / kTile);
+  const Unit u = unit_of(const_cast<uint8_t*>(store), r, g, G, kDim, W, esize);
+  // Lloyd code: one scale per KV head, the tree's gains
+  const double sg_ll = LL && vscale == 0
+                           ? reinterpret_cast<const double*>(cb + codec_layout(G, kDim).sphys)[g]
+                           : 1.0;
+  if (LL && tid < 16) gt[tid] = reinterpret_cast<const double*>(cb + codec_layout(G, kDim).gains)[tid];
+  // the four tokens' exponentials (uniform code) or logits (Lloyd code)
+  auto load_round = [&](int k, uint4 (&ev)[GQA], double2 (&ld)[GQA][2], double& sg)
+                        __attribute__((always_inline)) {
+    const int64_t j0 = (int64_t)k * RT + 4 * tid;
+    const int64_t jc = j0 < Tp ? j0 : 0;  // (a thread past the tokens loads token 0's)
+#pragma unroll
+    for (int hh = 0; hh < GQA; ++hh) {
+      if constexpr (LL) {
+        const double2* lp = reinterpret_cast<const double2*>(
+            reinterpret_cast<const double*>(ebuf) + (hrow0 + hh) * capmax + jc);
+        ld[hh][0] = lp[0];
+        ld[hh][1] = lp[1];
+      } else {
+        ev[hh] = *reinterpret_cast<const uint4*>(ebuf + (hrow0 + hh) * capmax + jc);
+      }
+    }
+    sg = LL ? sg_ll : vscale == 0 ? u.ev[jc / kGroup] : 1.0;
+  };
+  uint4 ev[GQA];
+  double2 ld[GQA][2];
+  double sg;
+  auto& mh = sh.mh;
+  auto& zh = sh.zh;
+  load_round(0, ev, ld, sg);
+  choose_clear<NT>(S);  // while the first round's exponentials are in flight
+  for (int hh = wv; hh < GQA; hh += NT / 64) {
+    const double* tp = tilepart + (hrow0 + hh) * ntile_ws * 2;
+    // one tile per lane (at most 64 tiles in a unit that fits LDS)
+    const double mt = lane < ntile_b ? tp[2 * lane] : -INFINITY;
+    const double zt = lane < ntile_b ? tp[2 * lane + 1] : 0.0;
+    const double m = wave_max(mt);
+    const double x = lane < ntile_b ? exp(mt - m) : 0.0;
+    const double Z = wave_sum(zt * x);
+    if (lane == 0) {
+      mh[hh] = m;
+      zh[hh] = 1.0 / Z;
+    }
+    if (lane < ntile_b) {
+      const double f = x / Z;
+      fs[hh][lane] = f;
+      ftile[(hrow0 + hh) * ntile_ws + lane] = f;
+    }
+  }
+  lds_barrier();
+  // items: tokens, or pairs of tokens (2m, 2m + 1) with summed weights; the
+  // minimum depth one: weights / 4 over levels 1..W-1, budget less N.  The
+  // selection's histograms are built here from the weights in registers, in
+  // exactly the form the selection reads them back from LDS.
+  const int64_t N = pairs ? Tp / 2 : Tp;
+  const double sc = (min1 && !LL) ? 0.25 : 1.0;
+  const int Wc = W - min1;
+  ChooseLocal CL;
+  const TableGains tg{gt + min1};
+  auto add = [&](double a) __attribute__((always_inline)) {
+    if constexpr (LL) choose_add<NT>(a, Wc, S, CL, tg);
+    else choose_add<NT>(a, Wc, S, CL);
+  };
+  const int nr = (int)((Tp + RT - 1) / RT);
+  for (int k = 0; k < nr; ++k) {
+    if (k > 0) load_round(k, ev, ld, sg);
+    const int64_t j0 = (int64_t)k * RT + 4 * tid;
+    if (j0 < Tp) {  // Tp is a multiple of 32: all four tokens or none
+      const int tl = (int)(j0 / kTile);
+      double sa[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int hh = 0; hh < GQA; ++hh) {
+        if constexpr (LL) {
+          // alpha = exp(s - m) (1/Z) from the logit: equal logits, equal weights
+          const double lg[4] = {ld[hh][0].x, ld[hh][0].y, ld[hh][1].x, ld[hh][1].y};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const double xq = __dmul_rn(exp_nonpos(lg[q] - mh[hh]), zh[hh]);
+            sa[q] = __dadd_rn(sa[q], __dmul_rn(xq, xq));
+          }
+        } else {
+          const double f = fs[hh][tl];
+          const uint32_t e4[4] = {ev[hh].x, ev[hh].y, ev[hh].z, ev[hh].w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const double xq = __dmul_rn(dec_e(e4[q]), f);
+            sa[q] = __dadd_rn(sa[q], __dmul_rn(xq, xq));
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sa[q] = vscale == 0 ? __dmul_rn(sa[q], sg) : sa[q];
+        acache[j0 + q] = sa[q];
+      }
+      if (pairs) {
+        add(__dadd_rn(sa[0], sa[1]) * sc);
+        add(__dadd_rn(sa[2], sa[3]) * sc);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) add(sa[q] * sc);
+      }
+    }
+  }
+  choose_flush<NT>(CL, S);
+  if constexpr (GCACHE) __syncthreads();  // the weights in memory, for every thread
+  else lds_barrier();
+  uint32_t Bv = (uint32_t)floor((double)RV * (double)Tp);
+  if (pairs) Bv /= 2u;
+  if (min1) Bv = (int64_t)Bv > N ? Bv - (uint32_t)N : 0u;
+  uint8_t* const tvb = tv + ((int64_t)b * G + g) * capmax;
+  uint32_t mine = 0;  // this thread's token depths
+  auto geta = [&](int64_t i) {
+    return (pairs ? __dadd_rn(acache[2 * i], acache[2 * i + 1]) : acache[i]) * sc;
+  };
+  auto put = [&](int64_t i, uint32_t t) {
+    t += (uint32_t)min1;
+    if (pairs) {
+      tvb[2 * i] = (uint8_t)t;
+      tvb[2 * i + 1] = (uint8_t)t;
+      mine += 2 * t;
+    } else {
+      tvb[i] = (uint8_t)t;
+      mine += t;
+    }
+  };
+  if constexpr (LL) block_choose_depths_hist<NT>(N, Bv, Wc, geta, put, S, tg);
+  else block_choose_depths_hist<NT>(N, Bv, Wc, geta, put, S);
+  if (counters) {
+    const uint32_t vtot = block_sum_u32<NT>(mine, S.wsum);
+    if (tid < 64) {
+      const uint8_t* tkb = tk + ((int64_t)b * G + g) * kDim;
+      const int ks = wave_sum_i32((int)tkb[lane] + (int)tkb[lane + 64]);
+      if (lane == 0) {
+        const unsigned long long ng = (unsigned long long)(Tp / kGroup);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1), (unsigned long long)vtot * kDim);
+        const unsigned long long meta = LL ? lloyd_meta_bits(b == 0, ux == 0, 1ull)
+                                           : 2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull;
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2), meta);
+        atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
+                  2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
+      }
+    }
+  }
+}
+
 }  // namespace readkv
