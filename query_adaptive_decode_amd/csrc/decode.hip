@@ -334,6 +334,12 @@ __device__ __forceinline__ double half_sum(double v) {
 }
 
 // LDS of one score block (members ordered largest first)
+// Mask of the plane bytes of a depth-t channel in a transposing plane read
+// (plane p in byte 7 - p: bytes 7 .. 8 - t kept).
+__device__ __forceinline__ uint64_t plane_keep(uint32_t t) {
+  return t >= 8u ? ~0ull : (t == 0u ? 0ull : ~0ull << (64u - 8u * t));
+}
+
 template <int GQA>
 struct ScoreShared {
   static constexpr int NG = kTile / kGroup;  // 8 groups; wave w owns groups 2w, 2w + 1
@@ -355,6 +361,10 @@ struct ScoreShared {
   __attribute__((aligned(4))) uint8_t tks[kDim];
   double redm[4][GQA], redz[4][GQA];
   uint8_t cperm[kDim];
+  // un-plane descriptors of wave w, channel pair r of slab s, half-wave hw
+  // at [32 w + 2 (4 s + r) + hw]: first slot's byte offset, plane mask
+  // (low word, high word), the pair's larger depth
+  uint4 udesc[128];
   uint32_t dcnt[2][9];                       // channels per depth value, per wave
   uint32_t qflag[2];                         // a non-finite query value, per wave
   int emx[2][GQA];
@@ -394,6 +404,7 @@ __device__ __forceinline__ void score_block(ScoreShared<GQA>& sh, uint32_t* plan
   auto& wtot = sh.wtot;
   auto& dcnt = sh.dcnt;
   auto& qflag = sh.qflag;
+  auto& udesc = sh.udesc;
 
   // the call's read counters start from zero (the value selection, a later
   // launch, adds to them)
@@ -610,11 +621,16 @@ __device__ __forceinline__ void score_block(ScoreShared<GQA>& sh, uint32_t* plan
   load_pieces(tile_begin);
   // scalar table: lane 8 s + i of wave w describes the channel at sorted
   // position 32 s + w + 4 i (depth | first slot << 8; slot 0 when depth 0)
-  uint32_t cinf = 0;
-  if (lane < 32) {
-    const int c = cperm[32 * (lane >> 3) + wv + 4 * (lane & 7)];
+  // the un-plane descriptors (entry e: wave e / 32, slab (e / 8) % 4, pair
+  // (e / 2) % 4, half-wave e % 2; the sorted position 32 slab + wave +
+  // 4 (e % 8)); a depth-0 channel reads slot 0, masked
+  if (tid < 128) {
+    const int pos = 32 * ((tid >> 3) & 3) + (tid >> 5) + 4 * (tid & 7);
+    const int c = cperm[pos], c2 = cperm[pos ^ 4];
     const uint32_t t = tks[c];
-    cinf = t | ((t ? (uint32_t)offs[c] : 0u) << 8);
+    const uint64_t keep = plane_keep(t);
+    udesc[tid] = make_uint4((t ? (uint32_t)offs[c] : 0u) * 32u, (uint32_t)keep, (uint32_t)(keep >> 32),
+                            max(t, (uint32_t)tks[c2]));
   }
   // digit scale 2^sig of head h: lane quad q of head quad hq is head 4 hq + q
   auto head_sig = [&](int hh) -> int {
@@ -670,6 +686,10 @@ __device__ __forceinline__ void score_block(ScoreShared<GQA>& sh, uint32_t* plan
   // plane bytes of octet o (tokens 8 o .. 8 o + 7 of the tile)
   const int hw = lane >> 5;
   const int c8 = 2 * (kq & 1) + ss;
+  // this lane's plane-read address less the channel's first slot, and its
+  // descriptors (channel 2 r + hw of the slab's pair r)
+  const uint8_t* const lane_pl = reinterpret_cast<const uint8_t*>(planes) + (7 - jj) * 32 + (c8 << 3);
+  const uint4* const ldesc = &udesc[32 * wv + hw];
   // digit chunk (channel octet co, channel j, set s) of block (hq, half m)
   auto achunk = [&](int hq, int m, int co, int j, int s) -> int {
     return (2 * hq + m) * AMS + co * AOS + (2 * j + s) * 8;
@@ -750,30 +770,24 @@ __device__ __forceinline__ void score_block(ScoreShared<GQA>& sh, uint32_t* plan
       // pair gives lane o of half-wave hw the 8 plane bytes of octet o of
       // channel 2 r + hw (plane p in byte 7 - p; planes past the depth are
       // read from the padding and masked).
-      // keep bytes 7 .. 8 - t (planes 0 .. t - 1), from a scalar depth
-      auto keep_of = [](uint32_t t) -> uint64_t {
-        return t >= 8u ? ~0ull : (t == 0u ? 0ull : ~0ull << (64u - 8u * t));
-      };
       uint2 pb[4];
-      uint64_t kp[4];
-      int tmx[4];
+      uint32_t kl[4], kh[4];
+      int tmxr[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t infA = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 2 * r);
-        const uint32_t infB = (uint32_t)__builtin_amdgcn_readlane((int)cinf, 8 * slab + 2 * r + 1);
-        tmx[r] = (int)max(infA & 0xFFu, infB & 0xFFu);
-        const uint64_t kA = keep_of(infA & 0xFFu), kB = keep_of(infB & 0xFFu);
-        kp[r] = hw ? kB : kA;
-        const int sl = (int)((hw ? infB : infA) >> 8) + 7 - jj;
-        pb[r] = __builtin_bit_cast(uint2, tr8_read(reinterpret_cast<const uint8_t*>(planes) + sl * 32 + (c8 << 3)));
+        const uint4 d = ldesc[2 * (4 * slab + r)];
+        pb[r] = __builtin_bit_cast(uint2, tr8_read(lane_pl + d.x));
+        kl[r] = d.y;
+        kh[r] = d.z;
+        tmxr[r] = __builtin_amdgcn_readfirstlane((int)d.w);
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        if (tmx[r] == 0) continue;  // both depth 0: their codes meet zero digits
-        const uint64_t keep = kp[r];
-        uint32_t lo = pb[r].x & (uint32_t)keep;
-        uint32_t hi = (pb[r].y & (uint32_t)(keep >> 32)) ^ 0xFF000000u;
-        if (tmx[r] <= 4) transpose8_hi4(lo, hi);
+        const int tmx = tmxr[r];
+        if (tmx == 0) continue;  // both depth 0: their codes meet zero digits
+        uint32_t lo = pb[r].x & kl[r];
+        uint32_t hi = (pb[r].y & kh[r]) ^ 0xFF000000u;
+        if (tmx <= 4) transpose8_hi4(lo, hi);
         else transpose8_halves(lo, hi);
         const int cl = wv + 4 * (2 * r + hw);
         *reinterpret_cast<uint2*>(cx + cl * CXS + 8 * (lane & 31)) = make_uint2(lo, hi);
