@@ -73,6 +73,12 @@ def test_fused_other_head_ratios(H, G, record_property):
     report(record_property, f"single launch gqa{H // G}", run.check())
 
 
+def test_fused_fewer_planes(record_property):
+    cfg = synth.workload(2, B=2, H=8, G=2, T0=900, W=5)
+    run = Run(cfg, steps=1, rates=[(2.5, 2.5), (5.0, 5.0), (6.0, 1.0)], scope=SINGLE_LAUNCH)
+    report(record_property, "single launch W=5", run.check())
+
+
 def test_fused_restricted_reader_unit_scale(record_property):
     cfg = synth.workload(2, B=2, T0=1500)
     flags = SINGLE_LAUNCH | RESTRICT_MIN_DEPTH1 | RESTRICT_VALUE_PAIRS

@@ -132,7 +132,8 @@ class Run:
         if key not in self._enc:
             K, V = self.unit(b, g)
             self._enc = {k: v for k, v in self._enc.items() if k[:2] != (b, g)}
-            self._enc[key] = (O.encode_stream(K[:n]), O.encode_stream(V[:n]))
+            W = self.cfg["W"]
+            self._enc[key] = (O.encode_stream(K[:n], W=W), O.encode_stream(V[:n], W=W))
         return self._enc[key]
 
     def counters_of_schedules(self, it):
@@ -334,6 +335,18 @@ def test_ragged_tails_and_tiles(T0, record_property):
     report(record_property, f"tails T0={T0}", run.check())
 
 
+@pytest.mark.parametrize("W", [1, 3, 5])
+def test_fewer_planes_than_eight(W, record_property):
+    # stores of W < 8 planes: shallower slot tables and plane masks in the
+    # score, shorter value rows in the gather; budgets below, at and past
+    # the full read
+    cfg = synth.workload(2, B=2, H=8, G=2, T0=1100, W=W)
+    run = Run(cfg, steps=2, rates=[(W / 2, W / 2), (float(W), float(W)), (W + 2.0, 0.5),
+                                   (1.0, W - 0.5)])
+    run.check_store()
+    report(record_property, f"W={W}", run.check())
+
+
 # ------------------------------------------------------------ exact ties
 @pytest.mark.parametrize("shape", ["gqa4", "gqa7"])
 def test_exact_value_ties_from_depth0_keys(shape, record_property):
@@ -404,6 +417,12 @@ def test_layer_budgets_tails_and_saturation(T0, record_property):
     run = Run(cfg, steps=2, rates=[(4.0, 4.0), (0.0, 0.0), (8.0, 8.0), (100.0, 0.5)],
               scope=SCOPE_LAYER)
     report(record_property, f"layer budgets tails T0={T0}", run.check_layer())
+
+
+def test_layer_budgets_fewer_planes(record_property):
+    cfg = synth.workload(4, B=2, T0=(300, 1400), W=3)
+    run = Run(cfg, steps=1, rates=[(1.5, 1.5), (3.0, 3.0), (2.2, 0.7)], scope=SCOPE_LAYER)
+    report(record_property, "layer budgets W=3", run.check_layer())
 
 
 def test_layer_budgets_exact_ties(record_property):
