@@ -217,7 +217,11 @@ int readkv_encode_append(const readkv_config* cfg, void* store,
  * (Sec. 3.2-3.3, Algorithm 1).
  * q: device [batch][num_q_heads][head_dim] in kv_dtype.  A unit (request,
  *   KV head) any of whose query values is not finite reads nothing: its
- *   depths are 0 and its outputs NaN.
+ *   depths are 0 and its outputs NaN.  A request that holds no token reads
+ *   nothing and its outputs are 0 (the empty sum), whatever its query; its
+ *   key depths are the minimum under the uniform code (no key energy) and
+ *   are allocated as for any request under the Lloyd code (its key weights
+ *   hold no context term).
  * R_K, R_V: read bits per scalar for the key and value stages (finite,
  *   >= 0; the nominal rate is R = (R_K + R_V)/2, Sec. 3.3).  Budgets (R as
  *   float32, product in double): B_K = floor(R_K * d_h) key refinements over

@@ -39,6 +39,9 @@ design notes of the repository):
   (Eq. (3), App. D.2).  Tokens of the open group are read exactly: their
   logits are q . k / sqrt(d) and their values are added after the inverse
   value transform.
+* A request with no tokens: output zero (the empty sum) whatever the query;
+  its key depths are allocated as for any request (these key weights hold no
+  context term).
 * Logical reads (App. A.1): each decode call is charged one load of the
   layer's calibration arrays (mu, sigma of keys and values, float32) and of
   the decoder table (510 centroids of depths 1..8 and 8 gains, float32).
@@ -398,6 +401,18 @@ def lloyd_decode_request(q_all, streams, codec: Codec, W=8, R_K=4.0, R_V=4.0,
     else:
         BK = budget(R_K, d)
         tK = np.stack([keys(wk[g], BK) for g in range(G)])
+
+    if tp == 0 and all(streams[g][0].tail.shape[0] == 0 for g in range(G)):
+        # No tokens in the request: the output is the empty sum, zero, whatever
+        # the query; the key depths are allocated as for any request (these key
+        # weights do not depend on the context), the minimum for a non-finite
+        # query.
+        for g in range(G):
+            if not good[g]:
+                tK[g] = min_depth
+        return dict(out=np.zeros((G, gqa, d)), tK=tK, tV=np.zeros((G, 0), dtype=np.int64),
+                    wk=np.concatenate(wk) if G else np.zeros(0), wv=np.zeros(0), BK=BK, BV=0,
+                    zhat=[np.zeros((gqa, 0))] * G, ahat=[np.zeros((gqa, 0))] * G, tp=0, nv=0)
 
     zhat, ahat = [], []
     for g in range(G):

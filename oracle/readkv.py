@@ -32,6 +32,9 @@ reason in the design notes of the repository):
 * Tokens of the not-yet-full group are kept exactly and enter the softmax and
   the output, but not the allocation.
 * A query with a non-finite value reads nothing: depths 0, outputs NaN.
+* A unit with no tokens at all (the pages' read is over a non-empty context)
+  reads nothing: its key weights are zero (no key energy), so its key depths
+  are the minimum, and its output is the empty sum, zero, whatever the query.
 * Restricted reader (min_depth=1, value_pairs): the minimum depth applies to
   both stages and its levels count against the budget; a value packet's
   weight is the sum of its two tokens' weights.
@@ -288,6 +291,14 @@ def pair_depths(wv, gains, W, BV, start):
     return np.repeat(tp2, 2), wp
 
 
+def _empty_unit(gq, d, R_K, min_depth):
+    """A unit with no tokens: zero key weights, key depths at the minimum,
+    no value items, output the empty sum (zero)."""
+    return dict(out=np.zeros((gq, d)), tK=np.full(d, min_depth, dtype=np.int64),
+                tV=np.zeros(0, dtype=np.int64), wk=np.zeros(d), wv=np.zeros(0),
+                BK=budget(R_K, d), BV=0, zhat=None, ahat=None, tp=0)
+
+
 def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
                 vscale="physical", enc_k=None, enc_v=None, diagnostics=False,
                 min_depth=0, value_pairs=False):
@@ -312,6 +323,8 @@ def decode_unit(q_heads, K, V, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     """
     q_heads = np.asarray(q_heads, dtype=np.float64)
     d = q_heads.shape[1]
+    if np.asarray(K).shape[0] == 0:
+        return _empty_unit(q_heads.shape[0], d, R_K, min_depth)
     if enc_k is None:
         enc_k = encode_stream(K, W, group_tokens)
     if enc_v is None:
@@ -386,6 +399,11 @@ def decode_request(q_all, Ks, Vs, W=8, R_K=4.0, R_V=4.0, group_tokens=32,
     G = len(Ks)
     d = q_all.shape[1]
     gqa = q_all.shape[0] // G
+    if np.asarray(Ks[0]).shape[0] == 0:
+        # no tokens in the request (every KV head empty): see _empty_unit
+        return dict(out=np.zeros((G, gqa, d)), tK=np.full((G, d), min_depth, dtype=np.int64),
+                    tV=np.zeros((G, 0), dtype=np.int64), wk=np.zeros(G * d), wv=np.zeros(0),
+                    BK=budget(R_K, G * d), BV=0, tp=0)
     if encs is None:
         encs = [(encode_stream(Ks[g], W, group_tokens), encode_stream(Vs[g], W, group_tokens))
                 for g in range(G)]

@@ -79,6 +79,13 @@ def test_fused_fewer_planes(record_property):
     report(record_property, "single launch W=5", run.check())
 
 
+def test_fused_empty_request(record_property):
+    # request 0 holds no token: zero outputs, minimum key depths
+    cfg = synth.workload(2, B=3, H=8, G=2, T0=600)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 3.0)], scope=SINGLE_LAUNCH, empty=[0])
+    report(record_property, "single launch, empty request", run.check())
+
+
 def test_fused_restricted_reader_unit_scale(record_property):
     cfg = synth.workload(2, B=2, T0=1500)
     flags = SINGLE_LAUNCH | RESTRICT_MIN_DEPTH1 | RESTRICT_VALUE_PAIRS

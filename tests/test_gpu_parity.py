@@ -69,13 +69,17 @@ class Run:
     schedules and read counters."""
 
     def __init__(self, cfg, steps, rates, vscale=VSCALE_PHYSICAL, repeat=False, keep_steps=None,
-                 qmod=None, scope=SCOPE_KV_HEAD):
+                 qmod=None, scope=SCOPE_KV_HEAD, empty=()):
+        # empty: requests that are given no token at all (prefill or steps)
         self.cfg, self.steps, self.rates, self.vscale = cfg, steps, rates, vscale
+        self.empty = set(empty)
         self.scope = scope   # the decode policy: budget scope | RESTRICT_* flags
         self.min1 = 1 if scope & RESTRICT_MIN_DEPTH1 else 0
         self.pairs = bool(scope & RESTRICT_VALUE_PAIRS)
         B, H, G = cfg["B"], cfg["H"], cfg["G"]
         self.T0 = synth.context_lengths(cfg)
+        for b in self.empty:
+            self.T0[b] = 0
         say(f"[case] {cfg['name']} B={B} H={H} G={G} T0={self.T0.tolist()[:4]}"
             f" steps={steps} rates={rates} vscale={vscale} scope={scope} opts="
             f"{ {k: cfg[k] for k in ('key_ties', 'gap', 'q_scale', 'q_log2_spread') if k in cfg} }")
@@ -93,12 +97,14 @@ class Run:
         self.lcfg = workload.config_for(cfg, steps)
         cap = self.lcfg.capacity_tokens
         self.cache = cache = ReadKVCache(self.lcfg)
-        cache.append(dv["kpre"], dv["vpre"], n_new=dv["npre"].to(torch.int32),
+        live = torch.tensor([0 if b in self.empty else 1 for b in range(B)], dtype=torch.int32,
+                            device="cuda")
+        cache.append(dv["kpre"], dv["vpre"], n_new=dv["npre"].to(torch.int32) * live,
                      n_max=dv["kpre"].shape[2])
         self.rec = []
         keep = set(range(steps)) if keep_steps is None else set(keep_steps)
         for s in range(steps):
-            cache.append(dv["kstep"][s], dv["vstep"][s])
+            cache.append(dv["kstep"][s], dv["vstep"][s], n_new=live if self.empty else None)
             if s not in keep:
                 continue
             for (rk, rv) in rates:
@@ -122,6 +128,10 @@ class Run:
         self._units = {}
         self._enc = {}
 
+    def n_of(self, b, step):
+        """Tokens of request b at the decode of `step`."""
+        return 0 if b in self.empty else int(self.T0[b]) + step + 1
+
     def unit(self, b, g):
         if (b, g) not in self._units:
             self._units[(b, g)] = synth.kv_unit(self.cfg, b, g, int(self.T0[b]) + self.steps)
@@ -142,7 +152,7 @@ class Run:
         ebits = 16 if cfg["dtype"] == "bf16" else 32
         tot = dict(key_payload=0, value_payload=0, metadata=0, open_group=0)
         for b in range(cfg["B"]):
-            n = int(self.T0[b]) + it["step"] + 1
+            n = self.n_of(b, it["step"])
             tp = n // 32 * 32
             for g in range(cfg["G"]):
                 lr = O.logical_reads(it["tk"][b, g], it["tv"][b, g, :tp], n, elem_bits=ebits)
@@ -165,7 +175,7 @@ class Run:
             assert it["ctr"].tolist() == self.counters_of_schedules(it), f"read counters {tag0}"
             ora_ctr = [0, 0, 0, 0]
             for (b, g) in units:
-                n = int(self.T0[b]) + it["step"] + 1
+                n = self.n_of(b, it["step"])
                 K, V = self.unit(b, g)
                 ek, ev = self.enc(b, g, n)
                 q = self.qf[it["step"]][b, g * gqa:(g + 1) * gqa]
@@ -223,7 +233,7 @@ class Run:
             assert it["ctr"].tolist() == self.counters_of_schedules(it), f"read counters {tag0}"
             ora_ctr = [0, 0, 0, 0]
             for b in requests:
-                n = int(self.T0[b]) + it["step"] + 1
+                n = self.n_of(b, it["step"])
                 units = [self.unit(b, g) for g in range(G)]
                 encs = [self.enc(b, g, n) for g in range(G)]
                 res = O.decode_request(self.qf[it["step"]][b], [K[:n] for K, _ in units],
@@ -345,6 +355,19 @@ def test_fewer_planes_than_eight(W, record_property):
                                    (1.0, W - 0.5)])
     run.check_store()
     report(record_property, f"W={W}", run.check())
+
+
+@pytest.mark.parametrize("scope", [SCOPE_KV_HEAD, SCOPE_LAYER,
+                                   SCOPE_KV_HEAD | RESTRICT_MIN_DEPTH1 | RESTRICT_VALUE_PAIRS],
+                         ids=["kv_head", "layer", "restricted"])
+def test_empty_request_in_batch(scope, record_property):
+    # request 1 holds no token at all (no prefill, no appends): it reads
+    # nothing, its key depths are the minimum and its outputs the empty sum
+    # (zero); the other requests of the batch as usual
+    cfg = synth.workload(4, B=3, T0=(40, 1500))
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (2.0, 1.0)], scope=scope, empty=[1])
+    st = run.check_layer() if scope & SCOPE_LAYER else run.check()
+    report(record_property, f"empty request, policy {scope:#x}", st)
 
 
 # ------------------------------------------------------------ exact ties

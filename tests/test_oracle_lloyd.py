@@ -281,6 +281,31 @@ def test_open_group_only_is_plain_attention(tree):
     assert np.allclose(r["out"], ref, rtol=1e-12, atol=1e-12)
 
 
+def test_empty_request_output_is_zero(tree):
+    """Reading: a request with no tokens outputs the empty sum (zero) and
+    allocates its key depths as any request does (these key weights hold no
+    context term); a non-finite query gets the minimum depths."""
+    rng = np.random.default_rng(29)
+    d = 128
+    s = (1 - 2 * rng.integers(0, 2, d)).astype(np.float64)
+    codec = L.make_codec(tree, s, s, [rng.standard_normal((64, d))], [rng.standard_normal((64, d))])
+    empty = np.zeros((0, d))
+    sk = L.lloyd_encode_stream(empty, tree, s, codec.muK[0], codec.sigK[0], 8)
+    sv = L.lloyd_encode_stream(empty, tree, s, codec.muV[0], codec.sigV[0], 8)
+    q = rng.standard_normal((3, d))
+    r = L.lloyd_decode_unit(q, sk, sv, codec, W=8, R_K=4, R_V=4)
+    assert np.array_equal(r["out"], np.zeros((3, d))) and r["tV"].size == 0
+    # the same key depths as a request with tokens (the weights are equal)
+    K = rng.standard_normal((40, d))
+    sk2 = L.lloyd_encode_stream(K, tree, s, codec.muK[0], codec.sigK[0], 8)
+    sv2 = L.lloyd_encode_stream(K, tree, s, codec.muV[0], codec.sigV[0], 8)
+    r2 = L.lloyd_decode_unit(q, sk2, sv2, codec, W=8, R_K=4, R_V=4)
+    assert np.array_equal(r["tK"], r2["tK"]) and r["tK"].sum() == 4 * d
+    q[1, 3] = np.nan
+    r = L.lloyd_decode_unit(q, sk, sv, codec, W=8, R_K=4, R_V=4, min_depth=1)
+    assert np.array_equal(r["out"], np.zeros((3, d))) and np.all(r["tK"] == 1)
+
+
 def test_full_read_is_attention_over_depth_w_cells(tree):
     """R = W: every key channel and value token is read to depth W, so the
     output is attention over the depth-W reconstructions, built here from

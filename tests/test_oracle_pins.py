@@ -540,6 +540,31 @@ def test_nonfinite_query_reads_nothing():
         assert res["tK"].sum() == 0 and res["tV"].sum() == 0 and len(res["tV"]) == 96
 
 
+def test_empty_context_reads_nothing():
+    # Reading (the pages read a non-empty context): no tokens -> no key
+    # energy, so only the minimum key depth; no value items; the output is
+    # the empty sum, zero, whatever the query.  The counters charge only E^K.
+    rng = np.random.default_rng(53)
+    q = rng.standard_normal((4, 128))
+    empty = np.zeros((0, 128))
+    for md in (0, 1):
+        for qq in (q, np.where(np.arange(128) == 5, np.nan, q)):
+            r = O.decode_unit(qq, empty, empty, R_K=4.0, R_V=4.0, min_depth=md)
+            assert np.array_equal(r["out"], np.zeros((4, 128)))
+            assert np.all(r["tK"] == md) and r["tV"].size == 0
+        r = O.decode_request(np.vstack([q, q]), [empty, empty], [empty, empty], R_K=3.0, R_V=2.0,
+                             min_depth=md)
+        assert np.array_equal(r["out"], np.zeros((2, 4, 128)))
+        assert np.all(r["tK"] == md) and r["tV"].shape == (2, 0)
+    lr = O.logical_reads(np.zeros(128, dtype=np.int64), np.zeros(0, dtype=np.int64), 0)
+    assert lr == dict(key_payload=0, value_payload=0, metadata=128 * 64, open_group=0)
+    # one open token: the softmax over it is 1, so the output is its value
+    # exactly (the open-group path next to the empty case)
+    K1, V1 = rng.standard_normal((1, 128)), rng.standard_normal((1, 128))
+    r = O.decode_unit(q, K1, V1, R_K=4.0, R_V=4.0)
+    assert np.array_equal(r["out"], np.repeat(V1, 4, axis=0))
+
+
 # ---------------------------------------------------- P9 reuse model
 def test_reuse_model_printed_values():
     g = GOLD["reuse_overhead_N8192_L128_W8_W0_4"]
