@@ -54,14 +54,18 @@ class LloydRun:
     at every rate) on the GPU; the decodes are kept on the host."""
 
     def __init__(self, cfg, steps, rates=(), vscale=VSCALE_PHYSICAL, policy=SCOPE_KV_HEAD,
-                 keep_steps=None, qmod=None):
+                 keep_steps=None, qmod=None, empty=()):
+        # empty: requests that are given no token at all (prefill or steps)
         cfg = dict(cfg, codec="lloyd")
+        self.empty = set(empty)
         self.cfg, self.steps, self.rates, self.vscale, self.policy = cfg, steps, rates, vscale, policy
         self.min1 = 1 if policy & RESTRICT_MIN_DEPTH1 else 0
         self.pairs = bool(policy & RESTRICT_VALUE_PAIRS)
         self.scope = "layer" if policy & SCOPE_LAYER else "kv_head"
         B, H, G = cfg["B"], cfg["H"], cfg["G"]
         self.T0 = synth.context_lengths(cfg)
+        for b in self.empty:
+            self.T0[b] = 0
         say(f"[case] lloyd {cfg['name']} B={B} H={H} G={G} W={cfg['W']} T0={self.T0.tolist()[:4]} "
             f"steps={steps} rates={list(rates)} vscale={vscale} policy={policy}")
         h = workload.host_inputs(cfg, steps)
@@ -81,12 +85,14 @@ class LloydRun:
         self.cache = cache = ReadKVCache(self.lcfg)
         binding.codec_init(self.lcfg, cache.store, ci["sk"].tolist(), ci["sv"].tolist(),
                            cd["kcal"], cd["vcal"])
-        cache.append(dv["kpre"], dv["vpre"], n_new=dv["npre"].to(torch.int32),
+        live = torch.tensor([0 if b in self.empty else 1 for b in range(B)], dtype=torch.int32,
+                            device="cuda")
+        cache.append(dv["kpre"], dv["vpre"], n_new=dv["npre"].to(torch.int32) * live,
                      n_max=dv["kpre"].shape[2])
         self.rec = []
         keep = set(range(steps)) if keep_steps is None else set(keep_steps)
         for s in range(steps):
-            cache.append(dv["kstep"][s], dv["vstep"][s])
+            cache.append(dv["kstep"][s], dv["vstep"][s], n_new=live if self.empty else None)
             if s not in keep:
                 continue
             for (rk, rv) in rates:
@@ -104,6 +110,10 @@ class LloydRun:
         say(f"[gpu done] flags={self.flags} lens={self.lens[:4]}")
         self.codec = oracle_codec(cfg)
         self._units, self._enc = {}, {}
+
+    def n_of(self, b, step):
+        """Tokens of request b at the decode of `step`."""
+        return 0 if b in self.empty else int(self.T0[b]) + step + 1
 
     def unit(self, b, g):
         if (b, g) not in self._units:
@@ -189,7 +199,7 @@ def _check_decode(r, record_property, name, units=None, bound=None):
         # metadata one load of the calibration arrays and the table per call
         tot = [0, 0, 0, 0]
         for b in range(cfg["B"]):
-            n = int(r.T0[b]) + it["step"] + 1
+            n = r.n_of(b, it["step"])
             tp = n // 32 * 32
             for g in range(G):
                 tot[0] += tp * int(it["tk"][b, g].sum())
@@ -198,7 +208,7 @@ def _check_decode(r, record_property, name, units=None, bound=None):
         tot[2] = L.lloyd_metadata_bits(G)
         assert it["ctr"].tolist() == tot, f"read counters {tag0}"
         for b in reqs:
-            n = int(r.T0[b]) + it["step"] + 1
+            n = r.n_of(b, it["step"])
             gs = [g for (bb, g) in units if bb == b] if units else list(range(G))
             streams = [r.enc(b, g, n) for g in range(G)]
             res = L.lloyd_decode_request(r.qf[it["step"]][b], streams, r.codec, W=W, R_K=it["rk"],
@@ -304,6 +314,15 @@ def test_lloyd_decode_nonfinite_query(record_property):
     cfg = synth.workload(2, B=2, H=8, G=2, T0=400)
     r = LloydRun(cfg, steps=1, rates=[(4.0, 4.0)], qmod=qmod)
     _check_decode(r, record_property, "non-finite query")
+
+
+@pytest.mark.parametrize("policy", [SCOPE_KV_HEAD, SCOPE_LAYER], ids=["kv_head", "layer"])
+def test_lloyd_decode_empty_request(policy, record_property):
+    # request 2 holds no token: outputs exactly zero, key depths allocated as
+    # for the others
+    cfg = synth.workload(4, B=3, T0=(40, 900))
+    r = LloydRun(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 1.0)], policy=policy, empty=[2])
+    _check_decode(r, record_property, f"empty request {r.scope}")
 
 
 def test_lloyd_decode_full_shape_sampled(record_property):
