@@ -65,7 +65,8 @@ def test_fused_ragged_tails(T0, record_property):
     report(record_property, f"single launch tails T0={T0}", run.check())
 
 
-@pytest.mark.parametrize("H,G", [(4, 2), (6, 2), (10, 2), (16, 2)], ids=["gqa2", "gqa3", "gqa5", "gqa8"])
+@pytest.mark.parametrize("H,G", [(4, 2), (6, 2), (10, 2), (12, 2), (16, 2)],
+                         ids=["gqa2", "gqa3", "gqa5", "gqa6", "gqa8"])
 def test_fused_other_head_ratios(H, G, record_property):
     # the other query-per-KV-head ratios (two blocks per compute unit above 4)
     cfg = synth.workload(2, B=2, H=H, G=G, T0=700)

@@ -316,6 +316,13 @@ def test_lloyd_decode_nonfinite_query(record_property):
     _check_decode(r, record_property, "non-finite query")
 
 
+@pytest.mark.parametrize("H,G", [(4, 2), (10, 2), (16, 2)], ids=["gqa2", "gqa5", "gqa8"])
+def test_lloyd_decode_other_head_ratios(H, G, record_property):
+    cfg = synth.workload(2, B=2, H=H, G=G, T0=700)
+    r = LloydRun(cfg, steps=1, rates=[(4.0, 4.0), (2.5, 1.5)])
+    _check_decode(r, record_property, f"gqa{H // G}")
+
+
 @pytest.mark.parametrize("policy", [SCOPE_KV_HEAD, SCOPE_LAYER], ids=["kv_head", "layer"])
 def test_lloyd_decode_empty_request(policy, record_property):
     # request 2 holds no token: outputs exactly zero, key depths allocated as

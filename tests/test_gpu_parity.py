@@ -345,6 +345,20 @@ def test_ragged_tails_and_tiles(T0, record_property):
     report(record_property, f"tails T0={T0}", run.check())
 
 
+@pytest.mark.parametrize("H,G,scope", [(4, 2, SCOPE_KV_HEAD), (6, 2, SCOPE_KV_HEAD),
+                                       (10, 2, SCOPE_KV_HEAD), (12, 2, SCOPE_KV_HEAD),
+                                       (16, 2, SCOPE_KV_HEAD), (6, 2, SCOPE_LAYER),
+                                       (16, 2, SCOPE_LAYER)],
+                         ids=["gqa2", "gqa3", "gqa5", "gqa6", "gqa8", "gqa3-layer", "gqa8-layer"])
+def test_other_head_ratios(H, G, scope, record_property):
+    # the query-per-KV-head ratios the benchmark shapes leave out (each is its
+    # own kernel instance; two score blocks per compute unit above 4)
+    cfg = synth.workload(2, B=2, H=H, G=G, T0=900)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0), (2.5, 1.5)], scope=scope)
+    st = run.check_layer() if scope & SCOPE_LAYER else run.check()
+    report(record_property, f"gqa{H // G} policy {scope:#x}", st)
+
+
 @pytest.mark.parametrize("W", [1, 3, 5])
 def test_fewer_planes_than_eight(W, record_property):
     # stores of W < 8 planes: shallower slot tables and plane masks in the
