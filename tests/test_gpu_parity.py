@@ -359,6 +359,19 @@ def test_other_head_ratios(H, G, scope, record_property):
     report(record_property, f"gqa{H // G} policy {scope:#x}", st)
 
 
+@pytest.mark.parametrize("H,G,scope", [(32, 8, SCOPE_KV_HEAD), (28, 4, SCOPE_KV_HEAD),
+                                       (32, 8, SCOPE_LAYER)],
+                         ids=["gqa4", "gqa7", "gqa4-layer"])
+def test_fp32_cache_other_shapes(H, G, scope, record_property):
+    # float32 keys, values and queries at the layer's head ratios (their own
+    # kernel instances: 4-byte tail elements, fp32 query loads)
+    cfg = synth.workload(2, B=2, H=H, G=G, T0=(300, 1300), dtype="f32")
+    run = Run(cfg, steps=2, rates=[(4.0, 4.0), (3.3, 2.7)], scope=scope)
+    run.check_store()
+    st = run.check_layer() if scope & SCOPE_LAYER else run.check()
+    report(record_property, f"fp32 gqa{H // G} policy {scope:#x}", st)
+
+
 @pytest.mark.parametrize("W", [1, 3, 5])
 def test_fewer_planes_than_eight(W, record_property):
     # stores of W < 8 planes: shallower slot tables and plane masks in the
