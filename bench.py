@@ -76,9 +76,10 @@ class Stepper:
     """Device state of one rate: the store (prefilled), fixed input buffers
     that one step's graph reads, and the decode outputs."""
 
-    def __init__(self, cfg, dev, lcfg, R, torch, codec=None):
+    def __init__(self, cfg, dev, lcfg, R, torch, codec=None, policy=None):
         from query_adaptive_decode_amd import binding as Bd
         self.Bd, self.torch, self.cfg, self.dev, self.lcfg, self.R = Bd, torch, cfg, dev, lcfg, R
+        self.policy = Bd.SCOPE_KV_HEAD if policy is None else policy
         B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
         self.cache = Bd.ReadKVCache(lcfg)
         if codec is not None:   # Lloyd code: signs and calibration before the prompt
@@ -104,7 +105,7 @@ class Stepper:
     def step_eager(self):
         self.load()
         self.cache.append(self.kbuf, self.vbuf)
-        self.cache.decode(self.qbuf, self.R, self.R, out=self.out)
+        self.cache.decode(self.qbuf, self.R, self.R, out=self.out, policy=self.policy)
         self.s += 1
 
     def capture(self):
@@ -113,7 +114,7 @@ class Stepper:
         self.graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(self.graph):
             self.cache.append(self.kbuf, self.vbuf)
-            self.cache.decode(self.qbuf, self.R, self.R, out=self.out)
+            self.cache.decode(self.qbuf, self.R, self.R, out=self.out, policy=self.policy)
         torch.cuda.synchronize()
 
 
@@ -130,12 +131,13 @@ def flush(scratch):
     scratch.sum()
 
 
-def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h, codec=None):
+def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h, codec=None, policy=None):
     """Warm and flushed step times (graph replays) and per-kernel durations
-    (HIP events on the launch stream around each stage)."""
+    (HIP events on the launch stream around each stage).  policy: the decode
+    policy (default per-KV-head budgets)."""
     B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
     T0 = int(cfg["T0"])
-    st = Stepper(cfg, dev, lcfg, R, torch, codec)
+    st = Stepper(cfg, dev, lcfg, R, torch, codec, policy)
     for _ in range(warmup):
         st.step_eager()
     st.capture()
@@ -180,7 +182,8 @@ def run_rate(cfg, dev, lcfg, R, warmup, steps, torch, h, codec=None):
             st.cache.append(st.kbuf, st.vbuf)
             h.hipEventRecord(ctypes.c_void_p(eenc[i][1]), ctypes.c_void_p(stream))
             st.Bd.decode_attn_timed(lcfg, st.cache.store, st.qbuf, R, R, st.cache.workspace, evs[i],
-                                    out=st.out, key_depths=st.tk, value_depths=st.tv.view(-1))
+                                    out=st.out, key_depths=st.tk, value_depths=st.tv.view(-1),
+                                    policy=st.policy)
             n = T0 + st.s + 1
             tp = n // 32 * 32
             if mode == "warm":
@@ -388,6 +391,9 @@ def main():
     ap.add_argument("--single-launch-rates", default="4,2",
                     help="rates at which the single-launch reader is timed beside the split "
                          "launches, as eager steps ('' for none)")
+    ap.add_argument("--policy-rates", default="4,2",
+                    help="rates at which per-layer budgets and the restricted reader are timed "
+                         "('' for none)")
     ap.add_argument("--counters-run", action="store_true",
                     help="run the fixed sequence the counter profiles are taken on, print no line")
     ap.add_argument("--lloyd", action="store_true",
@@ -568,6 +574,41 @@ def main():
                                                              for k, v in m["kernels"].items()}}
             ll["rates"][rate_key(R)] = ent
         line["lloyd_codec"] = ll
+    prates = [float(r) for r in args.policy_rates.split(",") if r.strip()]
+    if prates:
+        from query_adaptive_decode_amd import binding as Bd
+        pols = {
+            "layer": ("one key and one value budget per request over all its KV heads "
+                      "(READKV_SCOPE_LAYER)", Bd.SCOPE_LAYER),
+            "restricted": ("per-KV-head budgets, minimum depth one and two-token value packets "
+                           "(READKV_RESTRICT_MIN_DEPTH1 | READKV_RESTRICT_VALUE_PAIRS)",
+                           Bd.RESTRICT_MIN_DEPTH1 | Bd.RESTRICT_VALUE_PAIRS),
+        }
+        out_p = {}
+        for name, (what, pol) in pols.items():
+            ent_p = {"what": what, "rates": {}}
+            for R in prates:
+                r = run_rate(cfg, dev, lcfg, R, args.warmup, args.steps, torch, h, policy=pol)
+                tm, km = r["time"], r["kernel_ms"]
+                print(f"# {name} R={R:g}: evicted {tm['evicted']['ms_per_step']:.3f} ms/step "
+                      f"({tm['evicted']['qh_tok_per_s'] / 1e9:.2f} G qh*tok/s), warm "
+                      f"{tm['warm']['ms_per_step']:.3f} ms/step; kernels evicted "
+                      f"{json.dumps({k: round(v * 1e3, 1) for k, v in km['evicted'].items()})} us",
+                      file=sys.stderr, flush=True)
+                ent_p["rates"][rate_key(R)] = {
+                    "evicted_ms_per_step": tm["evicted"]["ms_per_step"],
+                    "evicted_qh_tok_per_s": tm["evicted"]["qh_tok_per_s"],
+                    "warm_ms_per_step": tm["warm"]["ms_per_step"],
+                    "warm_qh_tok_per_s": tm["warm"]["qh_tok_per_s"],
+                    "kernel_us": {mode: {k: v * 1e3 for k, v in km[mode].items()} for mode in km},
+                    "logical_bytes_per_step": r["step_alg_bytes"],
+                    "key_bits_per_scalar": r["key_bits"],
+                    "value_bits_per_scalar": r["value_bits"],
+                    "kernel_alg_GBps_evicted": {k: r["alg_bytes"][k] / (km["evicted"][k] * 1e-3) / 1e9
+                                                for k in ("score", "value_gather")},
+                }
+            out_p[name] = ent_p
+        line["policies"] = out_p
     srates = [float(r) for r in args.single_launch_rates.split(",") if r.strip()]
     if srates:
         sl = {"what": "one cooperative launch per decode (grid-wide barriers between the "

@@ -9,9 +9,11 @@
 //                   softmax statistics from the score tiles' partials, the
 //                   per-tile factors exp(m_tile - m)/Z, and the value weights
 //                   (Eq. (3)) of every packed token
-//   k_value_select  (one block per selection domain)
-//                   ChooseDepths over the domain's packed tokens -> t^V, and
-//                   the call's logical-read counters
+//   k_value_select  (one block per selection domain, when its weights fit
+//                   in LDS) ChooseDepths over the domain's packed tokens ->
+//                   t^V, and the call's logical-read counters
+//   k_sel_*         (otherwise) the same ChooseDepths and counters by many
+//                   blocks per domain, in a chain of launches (msel.h)
 //
 // (The block code of the last two is in valloc.h, which the single-launch
 // reader shares.)  A selection domain is one (request, KV head) under
@@ -21,6 +23,7 @@
 
 #include "kernels_common.h"
 #include "readkv_internal.h"
+#include "msel.h"
 #include "select.h"
 #include "valloc.h"
 
@@ -170,12 +173,27 @@ __global__ __launch_bounds__(256) void k_key_alloc_lloyd(const uint8_t* cb, cons
       TableGains{gt + min1});
 }
 
+// (sel, when not null: the first block of each selection domain of NU units
+// zeroes the domain's histograms and search state for the k_sel_* chain)
 template <int GQA, bool LL>
 __global__ __launch_bounds__(256) void k_value_weights(
     const uint8_t* store, int ub0, int H, int G, int W, int esize, int vscale, int64_t capmax,
     int ntile_ws, const uint32_t* ebuf, const double* tilepart, double* ftile, double* aval,
-    const uint8_t* cb) {
+    const uint8_t* cb, int NU, uint8_t* sel) {
   __shared__ ValueWeightsShared<GQA> sh;
+  const int ux = ub0 + (int)blockIdx.x;
+  if (sel && blockIdx.y == 0 && ux % NU == 0) {
+    const SelDomain D = sel_domain(sel, ux / NU);
+    for (int i = threadIdx.x; i < 4096; i += 256) {
+      D.hA[i] = 0u;  // hA and hB
+      D.hC0[i] = 0u; // hC0 and hC1
+    }
+    if (threadIdx.x == 0) {
+      SelState z = {};
+      z.etop = -1;
+      *D.st = z;
+    }
+  }
   value_weights_block<GQA, LL>(sh, launch_block(), store, ub0, H, G, W, esize, vscale, capmax,
                                ntile_ws, ebuf, tilepart, ftile, aval, cb);
 }
@@ -274,6 +292,310 @@ int launch_key_alloc_lloyd(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, 
 
 // per-KV-head budgets and a capacity that fits LDS: one fused launch;
 // otherwise value weights (all compute units) then the selection
+// ---------------------------------------------------------------------------
+// The multi-block selection (msel.h).  Item-parallel launches: block (unit,
+// chunk of 1024 tokens), 256 threads, 4 tokens each; per-domain launches: one
+// wave (k_sel_field, k_sel_digit) or one block of 1024 (k_sel_ties).
+// ---------------------------------------------------------------------------
+template <bool LL>
+__device__ __forceinline__ void sel_load_gains(double* gt, const uint8_t* cb, int G) {
+  if (LL && threadIdx.x < 16)
+    gt[threadIdx.x] = reinterpret_cast<const double*>(cb + codec_layout(G, kDim).gains)[threadIdx.x];
+}
+
+template <bool LL>
+__global__ __launch_bounds__(256) void k_sel_hist(const uint8_t* store, int ub0, int G, int W, int NU,
+                                                  float RV, int min1, int pairs, int64_t capmax,
+                                                  const double* aval, uint8_t* sel, const uint8_t* cb) {
+  __shared__ uint32_t hA[2048], hB[2048];
+  __shared__ double gt[16];
+  const int tid = threadIdx.x;
+  const int ux = ub0 + (int)blockIdx.x;
+  const ReqRecord r = req_of(store, ux / G);
+  const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
+  if ((int64_t)blockIdx.y * 1024 >= Tp) return;  // (the whole block)
+  for (int i = tid; i < 2048; i += 256) {
+    hA[i] = 0u;
+    hB[i] = 0u;
+  }
+  sel_load_gains<LL>(gt, cb, G);
+  __syncthreads();
+  const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
+  const SelItems it = sel_items(aval, capmax, ux, NU, (int64_t)blockIdx.y * 1024 + 4 * tid, Tp, pairs, P.sc);
+  ChooseLocal L;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q >= it.n) break;
+    if constexpr (LL) sel_add_fields(it.a[q], P.Wc, hA, hB, L, TableGains{gt + min1});
+    else sel_add_fields(it.a[q], P.Wc, hA, hB, L, Pow4Gains{});
+  }
+  const SelDomain D = sel_domain(sel, ux / NU);
+  const int n = wave_sum_i32((int)L.npos);
+  const int e = wave_max_i32(L.etop);
+  const bool odd = __ballot(L.odd) != 0ull;
+  if ((tid & 63) == 0) {
+    if (n) atomicAdd(&D.st->npos, (uint32_t)n);
+    if (e >= 0) atomicMax(&D.st->etop, e);
+    if (odd) atomicOr(&D.st->any_odd, 1u);
+  }
+  __syncthreads();
+  for (int i = tid; i < 2048; i += 256) {
+    if (hA[i]) atomicAdd(&D.hA[i], hA[i]);
+    if (hB[i]) atomicAdd(&D.hB[i], hB[i]);
+  }
+}
+
+template <bool LL>
+__global__ __launch_bounds__(64) void k_sel_field(const uint8_t* store, int ub0, int G, int W, int NU,
+                                                  float RV, int min1, int pairs, uint8_t* sel) {
+  __shared__ uint32_t out[4];
+  const int dom = ub0 / NU + (int)blockIdx.x;
+  const ReqRecord r = req_of(store, dom * NU / G);
+  const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
+  const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
+  const SelDomain D = sel_domain(sel, dom);
+  const uint32_t npos = D.st->npos;
+  const int etop = D.st->etop;
+  uint32_t flags = 0u, rem = 0u, n_eq = 0u;
+  int Es = 0;
+  if (P.bud == 0u || npos <= P.bud) {
+    flags = kSelDone;  // nothing, or every positive gain, is taken
+  } else {
+    if (threadIdx.x == 0) out[0] = out[1] = out[2] = 0u;
+    wave_lds_fence();
+    wave_find_gain_field(D.hA, D.hB, P.Wc, etop - 2, P.bud, out);
+    wave_lds_fence();
+    Es = (int)out[0];
+    rem = P.bud - out[1];
+    n_eq = out[2];
+    if (n_eq == rem) flags = kSelDone;
+  }
+  if (threadIdx.x == 0) {
+    SelState* s = D.st;
+    s->flags = flags;
+    s->Es = Es;
+    s->rem = rem;
+    s->n_eq = n_eq;
+    s->prefix = 0ull;
+    s->mask = 0ull;
+    s->tie_cut = 0;
+  }
+}
+
+template <bool LL, int PASS>
+__global__ __launch_bounds__(256) void k_sel_radix(const uint8_t* store, int ub0, int G, int W, int NU,
+                                                   float RV, int min1, int pairs, int64_t capmax,
+                                                   const double* aval, uint8_t* sel, const uint8_t* cb) {
+  constexpr int width = PASS < 2 ? 11 : 10;
+  constexpr int shift = PASS < 2 ? 41 - 11 * PASS : 40 - 10 * PASS;
+  constexpr uint32_t dmask = (1u << width) - 1u;
+  __shared__ uint32_t hC[2048];
+  __shared__ double gt[16];
+  const int tid = threadIdx.x;
+  const int ux = ub0 + (int)blockIdx.x;
+  const SelDomain D = sel_domain(sel, ux / NU);
+  const SelState S = *D.st;
+  if (S.flags & kSelDone) return;  // (the whole block)
+  const ReqRecord r = req_of(store, ux / G);
+  const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
+  if ((int64_t)blockIdx.y * 1024 >= Tp) return;
+  for (int i = tid; i < 2048; i += 256) hC[i] = 0u;
+  sel_load_gains<LL>(gt, cb, G);
+  __syncthreads();
+  const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
+  const SelItems it = sel_items(aval, capmax, ux, NU, (int64_t)blockIdx.y * 1024 + 4 * tid, Tp, pairs, P.sc);
+  auto bin = [&](uint64_t mnt) __attribute__((always_inline)) {
+    if ((mnt & S.mask) == S.prefix) atomicAdd(&hC[(uint32_t)(mnt >> shift) & dmask], 1u);
+  };
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q >= it.n) break;
+    if constexpr (LL) sel_gains_at(it.a[q], P.Wc, S.Es, S.any_odd != 0u, TableGains{gt + min1}, bin);
+    else sel_gains_at(it.a[q], P.Wc, S.Es, S.any_odd != 0u, Pow4Gains{}, bin);
+  }
+  __syncthreads();
+  uint32_t* const g = (PASS & 1) ? D.hC1 : D.hC0;
+  for (int i = tid; i <= (int)dmask; i += 256)
+    if (hC[i]) atomicAdd(&g[i], hC[i]);
+}
+
+template <int PASS>
+__global__ __launch_bounds__(64) void k_sel_digit(int dom0, uint8_t* sel) {
+  constexpr int width = PASS < 2 ? 11 : 10;
+  constexpr int shift = PASS < 2 ? 41 - 11 * PASS : 40 - 10 * PASS;
+  constexpr uint32_t dmask = (1u << width) - 1u;
+  __shared__ uint32_t out[2];
+  const SelDomain D = sel_domain(sel, dom0 + (int)blockIdx.x);
+  SelState S = *D.st;
+  uint32_t* const g = (PASS & 1) ? D.hC1 : D.hC0;
+  uint32_t* const gnext = (PASS & 1) ? D.hC0 : D.hC1;
+  if (!(S.flags & kSelDone)) {
+    if (threadIdx.x == 0) out[0] = out[1] = 0u;
+    wave_lds_fence();
+    if constexpr (width == 11) wave_find_digit<2048>(g, S.rem, &out[0], &out[1]);
+    else wave_find_digit<1024>(g, S.rem, &out[0], &out[1]);
+    wave_lds_fence();
+    const uint32_t dg = min(out[0], dmask);
+    S.n_eq = g[dg];
+    S.rem -= out[1];
+    S.prefix |= (uint64_t)dg << shift;
+    S.mask |= (uint64_t)dmask << shift;
+    if (S.n_eq == S.rem) S.flags |= kSelDone;
+    else if (PASS == 4) S.flags |= kSelDone | kSelRank;  // every bit settled: rank the ties
+    if (threadIdx.x == 0) {
+      D.st->flags = S.flags;
+      D.st->rem = S.rem;
+      D.st->n_eq = S.n_eq;
+      D.st->prefix = S.prefix;
+      D.st->mask = S.mask;
+    }
+  }
+  // the next pass's histogram starts from zero (this one's is not touched)
+  if (PASS < 4)
+    for (int i = threadIdx.x; i < 2048; i += 64) gnext[i] = 0u;
+}
+
+// Ranked ties: the items whose gain equals the threshold are taken in index
+// order while fewer than rem are; tie_cut = the index after the rem-th.
+template <bool LL>
+__global__ __launch_bounds__(1024) void k_sel_ties(const uint8_t* store, int ub0, int G, int W, int NU,
+                                                   float RV, int min1, int pairs, int64_t capmax,
+                                                   const double* aval, uint8_t* sel, const uint8_t* cb) {
+  constexpr int NT = 1024;
+  __shared__ uint32_t wsum[NT / 64 + 1];
+  __shared__ double gt[16];
+  __shared__ int found;
+  const int tid = threadIdx.x;
+  const int dom = ub0 / NU + (int)blockIdx.x;
+  const SelDomain D = sel_domain(sel, dom);
+  const SelState S = *D.st;
+  if (!(S.flags & kSelRank)) return;  // (the whole block)
+  sel_load_gains<LL>(gt, cb, G);
+  if (tid == 0) found = 0;
+  __syncthreads();
+  const int u0 = dom * NU;
+  const ReqRecord r = req_of(store, u0 / G);
+  const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
+  const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
+  uint32_t running = 0;  // ties in earlier rounds
+  for (int k = 0; k < NU; ++k) {
+    for (int64_t r0 = 0; r0 < Tp; r0 += 4 * NT) {
+      const SelItems it = sel_items(aval, capmax, u0 + k, NU, r0 + 4 * tid, Tp, pairs, P.sc);
+      uint32_t tie[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (q >= it.n) break;
+        const uint32_t lv = LL ? sel_levels(it.a[q], P.Wc, S, P.bud, TableGains{gt + min1})
+                               : sel_levels(it.a[q], P.Wc, S, P.bud, Pow4Gains{});
+        tie[q] = lv >> 16;
+      }
+      uint32_t c = block_excl_scan<NT>((tie[0] + tie[1]) + (tie[2] + tie[3]), wsum) + running;
+      running += wsum[NT / 64];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (tie[q]) {
+          if (c + 1u == S.rem) {
+            D.st->tie_cut = it.idx[q] + 1;
+            found = 1;
+          }
+          ++c;
+        }
+      }
+      __syncthreads();
+      if (found) return;
+    }
+  }
+}
+
+template <bool LL>
+__global__ __launch_bounds__(256) void k_sel_depths(const uint8_t* store, int ub0, int G, int W, int esize,
+                                                    int NU, float RV, int min1, int pairs, int64_t capmax,
+                                                    const double* aval, uint8_t* sel, uint8_t* tv,
+                                                    const uint8_t* tk, uint64_t* counters,
+                                                    const uint8_t* cb) {
+  __shared__ uint32_t wsum[256 / 64 + 1];
+  __shared__ double gt[16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  sel_load_gains<LL>(gt, cb, G);
+  __syncthreads();
+  const int ux = ub0 + (int)blockIdx.x;
+  const int b = ux / G;
+  const ReqRecord r = req_of(store, b);
+  const int64_t len = r.len;
+  const int64_t Tp = len & ~(int64_t)(kGroup - 1);
+  const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
+  const SelDomain D = sel_domain(sel, ux / NU);
+  const SelState S = *D.st;
+  const bool rank = (S.flags & kSelRank) != 0u;
+  const SelItems it = sel_items(aval, capmax, ux, NU, (int64_t)blockIdx.y * 1024 + 4 * tid, Tp, pairs, P.sc);
+  uint8_t* const tvb = tv + (int64_t)ux * capmax;
+  uint32_t mine = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (q >= it.n) break;
+    const uint32_t lv = LL ? sel_levels(it.a[q], P.Wc, S, P.bud, TableGains{gt + min1})
+                           : sel_levels(it.a[q], P.Wc, S, P.bud, Pow4Gains{});
+    const uint32_t tie = lv >> 16;
+    uint32_t t = (lv & 0xFFFFu) + (rank ? (tie && it.idx[q] < S.tie_cut ? 1u : 0u) : tie) + (uint32_t)min1;
+    if (pairs) {
+      tvb[it.j0 + 2 * q] = (uint8_t)t;
+      tvb[it.j0 + 2 * q + 1] = (uint8_t)t;
+      mine += 2 * t;
+    } else {
+      tvb[it.j0 + q] = (uint8_t)t;
+      mine += t;
+    }
+  }
+  if (!counters) return;
+  const uint32_t vtot = block_sum_u32<256>(mine, wsum);
+  if (tid == 0 && vtot) atomicAdd(reinterpret_cast<unsigned long long*>(counters + 1),
+                                  (unsigned long long)vtot * kDim);
+  // the domain's other reads, once (as value_select_block)
+  if (blockIdx.y == 0 && ux % NU == 0 && tid < 64) {
+    int ks = 0;
+    for (int i = lane; i < NU * kDim; i += 64) ks += tk[(int64_t)ux * kDim + i];
+    ks = wave_sum_i32(ks);
+    if (lane == 0) {
+      const unsigned long long ng = (unsigned long long)(Tp / kGroup), nu = (unsigned long long)NU;
+      atomicAdd(reinterpret_cast<unsigned long long*>(counters), (unsigned long long)ks * (unsigned long long)Tp);
+      const unsigned long long meta =
+          LL ? lloyd_meta_bits(b == 0, ux == 0, nu) : nu * (2ull * ng * kDim * 32ull + kDim * 64ull + ng * 64ull);
+      atomicAdd(reinterpret_cast<unsigned long long*>(counters + 2), meta);
+      atomicAdd(reinterpret_cast<unsigned long long*>(counters + 3),
+                nu * 2ull * (unsigned long long)(len - Tp) * kDim * (unsigned long long)esize * 8ull);
+    }
+  }
+}
+
+template <bool LL>
+static void launch_sel_chain(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
+                             uint8_t* tv, int NU, hipStream_t st) {
+  const int nch = (int)((a.capmax + kVChunk - 1) / kVChunk);
+  const int ndom = P.nunits / NU;
+  uint8_t* const sel = a.ws + L.sel;
+  const double* const aval = (const double*)(a.ws + L.aval);
+  const uint8_t* const store = (const uint8_t*)a.store;
+  const dim3 gi(P.nunits, nch);
+  hipLaunchKernelGGL((k_sel_hist<LL>), gi, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1,
+                     a.pairs, a.capmax, aval, sel, a.cblock);
+  hipLaunchKernelGGL((k_sel_field<LL>), dim3(ndom), dim3(64), 0, st, store, P.ub0, a.G, a.W, NU, a.RV,
+                     a.min1, a.pairs, sel);
+#define READKV_SEL_PASS(p)                                                                              \
+  hipLaunchKernelGGL((k_sel_radix<LL, p>), gi, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1, \
+                     a.pairs, a.capmax, aval, sel, a.cblock);                                            \
+  hipLaunchKernelGGL((k_sel_digit<p>), dim3(ndom), dim3(64), 0, st, P.ub0 / NU, sel);
+  READKV_SEL_PASS(0)
+  READKV_SEL_PASS(1)
+  READKV_SEL_PASS(2)
+  READKV_SEL_PASS(3)
+  READKV_SEL_PASS(4)
+#undef READKV_SEL_PASS
+  hipLaunchKernelGGL((k_sel_ties<LL>), dim3(ndom), dim3(1024), 0, st, store, P.ub0, a.G, a.W, NU, a.RV,
+                     a.min1, a.pairs, a.capmax, aval, sel, a.cblock);
+  hipLaunchKernelGGL((k_sel_depths<LL>), gi, dim3(256), 0, st, store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4,
+                     NU, a.RV, a.min1, a.pairs, a.capmax, aval, sel, tv, tk, a.counters, a.cblock);
+}
+
 template <int GQA, bool LL>
 static bool value_first_gqa(const DecodeArgs& a, const Part& P, const WsLayout& L, const uint8_t* tk,
                             uint8_t* tv, hipStream_t st) {
@@ -292,10 +614,13 @@ static bool value_first_gqa(const DecodeArgs& a, const Part& P, const WsLayout& 
     return true;
   }
   const int nch = (int)((a.capmax + kVChunk - 1) / kVChunk);
+  const int NU = a.scope == 1 ? a.G : 1;
+  const bool chain = (int64_t)NU * a.capmax > kVSelLocal;  // the multi-block selection follows
   hipLaunchKernelGGL((k_value_weights<GQA, LL>), dim3(P.nunits, nch), dim3(256), 0, st,
                      (const uint8_t*)a.store, P.ub0, a.H, a.G, a.W, a.dtype == 0 ? 2 : 4, a.vscale, a.capmax,
                      L.ntile, (const uint32_t*)(a.ws + L.ebuf), (const double*)(a.ws + L.tilepart),
-                     (double*)(a.ws + L.ftile), (double*)(a.ws + L.aval), a.cblock);
+                     (double*)(a.ws + L.ftile), (double*)(a.ws + L.aval), a.cblock, NU,
+                     chain ? a.ws + L.sel : nullptr);
   return false;
 }
 
@@ -324,9 +649,13 @@ static int launch_value_alloc_t(const DecodeArgs& a, const Part& P, const WsLayo
                         hipFuncAttributeMaxDynamicSharedMemorySize, kVSelLocal * 8);
     attr_set = true;
   }
-  auto* const ksel = local ? &k_value_select<true, LL> : &k_value_select<false, LL>;
+  if (!local) {
+    launch_sel_chain<LL>(a, P, L, tk, tv, NU, st);
+    return 0;
+  }
+  auto* const ksel = &k_value_select<true, LL>;
   hipLaunchKernelGGL(ksel, dim3(P.nunits / NU),
-                     dim3(kVSelNT), local ? (size_t)nmax * 8 : 0, st,
+                     dim3(kVSelNT), (size_t)nmax * 8, st,
                      (const uint8_t*)a.store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4, a.RV, NU, a.min1,
                      a.pairs, a.capmax,
                      (const double*)(a.ws + L.aval), tv, tk, a.counters, a.cblock);

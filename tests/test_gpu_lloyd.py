@@ -316,6 +316,14 @@ def test_lloyd_decode_nonfinite_query(record_property):
     _check_decode(r, record_property, "non-finite query")
 
 
+def test_lloyd_decode_layer_budgets_many_block_selection(record_property):
+    # 8 KV heads x 2,560 tokens per request: the value selection over many
+    # blocks per request
+    cfg = synth.workload(2, B=2, T0=2500)
+    r = LloydRun(cfg, steps=1, rates=[(4.0, 4.0), (2.0, 1.0)], policy=SCOPE_LAYER)
+    _check_decode(r, record_property, "layer budgets, many-block selection")
+
+
 @pytest.mark.parametrize("H,G", [(4, 2), (10, 2), (16, 2)], ids=["gqa2", "gqa5", "gqa8"])
 def test_lloyd_decode_other_head_ratios(H, G, record_property):
     cfg = synth.workload(2, B=2, H=H, G=G, T0=700)

@@ -475,6 +475,17 @@ def test_layer_budgets_fewer_planes(record_property):
     report(record_property, "layer budgets W=3", run.check_layer())
 
 
+@pytest.mark.parametrize("flags", [0, RESTRICT_MIN_DEPTH1 | RESTRICT_VALUE_PAIRS], ids=["plain", "restricted"])
+def test_layer_budgets_many_block_selection(flags, record_property):
+    # 8 KV heads x 2,560 tokens: more items than one block holds in LDS, so
+    # the value selection runs over many blocks per request; R_K = 0 makes
+    # the 32 tokens of every closed group tie (ranked across blocks)
+    cfg = synth.workload(2, B=2, T0=2500)
+    run = Run(cfg, steps=1, rates=[(4.0, 4.0), (0.0, 1.3), (0.0, 2.7), (3.3, 2.7)],
+              scope=SCOPE_LAYER | flags)
+    report(record_property, f"layer budgets, many-block selection {flags:#x}", run.check_layer())
+
+
 def test_layer_budgets_exact_ties(record_property):
     # depth-0 keys make the 32 tokens of each group tie, across all KV heads
     # of the request; duplicated key channels make key weights tie
