@@ -295,7 +295,7 @@ int launch_key_alloc_lloyd(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, 
 // ---------------------------------------------------------------------------
 // The multi-block selection (msel.h).  Item-parallel launches: block (unit,
 // chunk of 1024 tokens), 256 threads, 4 tokens each; per-domain launches: one
-// wave (k_sel_field, k_sel_digit) or one block of 1024 (k_sel_ties).
+// wave (k_sel_field, k_sel_digit; the last digit with a block of 1024 for the tie cut).
 // ---------------------------------------------------------------------------
 template <bool LL>
 __device__ __forceinline__ void sel_load_gains(double* gt, const uint8_t* cb, int G) {
@@ -313,7 +313,8 @@ __global__ __launch_bounds__(256) void k_sel_hist(const uint8_t* store, int ub0,
   const int ux = ub0 + (int)blockIdx.x;
   const ReqRecord r = req_of(store, ux / G);
   const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
-  if ((int64_t)blockIdx.y * 1024 >= Tp) return;  // (the whole block)
+  const int64_t c0 = (int64_t)blockIdx.y * kSelBlockTokens;
+  if (c0 >= Tp) return;  // (the whole block)
   for (int i = tid; i < 2048; i += 256) {
     hA[i] = 0u;
     hB[i] = 0u;
@@ -321,23 +322,17 @@ __global__ __launch_bounds__(256) void k_sel_hist(const uint8_t* store, int ub0,
   sel_load_gains<LL>(gt, cb, G);
   __syncthreads();
   const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
-  const SelItems it = sel_items(aval, capmax, ux, NU, (int64_t)blockIdx.y * 1024 + 4 * tid, Tp, pairs, P.sc);
-  ChooseLocal L;
+  ChooseLocal L;  // (the counts come from the histograms in k_sel_field)
+  for (int64_t j0 = c0 + 4 * tid; j0 < c0 + kSelBlockTokens; j0 += 1024) {
+    const SelItems it = sel_items(aval, capmax, ux, NU, j0, Tp, pairs, P.sc);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (q >= it.n) break;
-    if constexpr (LL) sel_add_fields(it.a[q], P.Wc, hA, hB, L, TableGains{gt + min1});
-    else sel_add_fields(it.a[q], P.Wc, hA, hB, L, Pow4Gains{});
+    for (int q = 0; q < 4; ++q) {
+      if (q >= it.n) break;
+      if constexpr (LL) sel_add_fields(it.a[q], P.Wc, hA, hB, L, TableGains{gt + min1});
+      else sel_add_fields(it.a[q], P.Wc, hA, hB, L, Pow4Gains{});
+    }
   }
   const SelDomain D = sel_domain(sel, ux / NU);
-  const int n = wave_sum_i32((int)L.npos);
-  const int e = wave_max_i32(L.etop);
-  const bool odd = __ballot(L.odd) != 0ull;
-  if ((tid & 63) == 0) {
-    if (n) atomicAdd(&D.st->npos, (uint32_t)n);
-    if (e >= 0) atomicMax(&D.st->etop, e);
-    if (odd) atomicOr(&D.st->any_odd, 1u);
-  }
   __syncthreads();
   for (int i = tid; i < 2048; i += 256) {
     if (hA[i]) atomicAdd(&D.hA[i], hA[i]);
@@ -354,8 +349,20 @@ __global__ __launch_bounds__(64) void k_sel_field(const uint8_t* store, int ub0,
   const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
   const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
   const SelDomain D = sel_domain(sel, dom);
-  const uint32_t npos = D.st->npos;
-  const int etop = D.st->etop;
+  // positive gains, top field (+2) and odd gains, from the histograms: a
+  // regular item at field f holds Wc gains, the top one at f - 2
+  uint32_t np = 0u, odd = 0u;
+  int et = -1;
+  for (int f = (int)threadIdx.x; f < 2048; f += 64) {
+    const uint32_t a = D.hA[f], o = D.hB[f];
+    np += a * (uint32_t)P.Wc + o;
+    odd |= o;
+    if (a) et = max(et, f);
+    if (o) et = max(et, f + 2);
+  }
+  const uint32_t npos = (uint32_t)wave_sum_i32((int)np);
+  const int etop = wave_max_i32(et);
+  const uint32_t any_odd = __ballot(odd != 0u) != 0ull ? 1u : 0u;
   uint32_t flags = 0u, rem = 0u, n_eq = 0u;
   int Es = 0;
   if (P.bud == 0u || npos <= P.bud) {
@@ -372,6 +379,9 @@ __global__ __launch_bounds__(64) void k_sel_field(const uint8_t* store, int ub0,
   }
   if (threadIdx.x == 0) {
     SelState* s = D.st;
+    s->npos = npos;
+    s->etop = etop;
+    s->any_odd = any_odd;
     s->flags = flags;
     s->Es = Es;
     s->rem = rem;
@@ -398,20 +408,23 @@ __global__ __launch_bounds__(256) void k_sel_radix(const uint8_t* store, int ub0
   if (S.flags & kSelDone) return;  // (the whole block)
   const ReqRecord r = req_of(store, ux / G);
   const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
-  if ((int64_t)blockIdx.y * 1024 >= Tp) return;
+  const int64_t c0 = (int64_t)blockIdx.y * kSelBlockTokens;
+  if (c0 >= Tp) return;
   for (int i = tid; i < 2048; i += 256) hC[i] = 0u;
   sel_load_gains<LL>(gt, cb, G);
   __syncthreads();
   const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
-  const SelItems it = sel_items(aval, capmax, ux, NU, (int64_t)blockIdx.y * 1024 + 4 * tid, Tp, pairs, P.sc);
   auto bin = [&](uint64_t mnt) __attribute__((always_inline)) {
     if ((mnt & S.mask) == S.prefix) atomicAdd(&hC[(uint32_t)(mnt >> shift) & dmask], 1u);
   };
+  for (int64_t j0 = c0 + 4 * tid; j0 < c0 + kSelBlockTokens; j0 += 1024) {
+    const SelItems it = sel_items(aval, capmax, ux, NU, j0, Tp, pairs, P.sc);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    if (q >= it.n) break;
-    if constexpr (LL) sel_gains_at(it.a[q], P.Wc, S.Es, S.any_odd != 0u, TableGains{gt + min1}, bin);
-    else sel_gains_at(it.a[q], P.Wc, S.Es, S.any_odd != 0u, Pow4Gains{}, bin);
+    for (int q = 0; q < 4; ++q) {
+      if (q >= it.n) break;
+      if constexpr (LL) sel_gains_at(it.a[q], P.Wc, S.Es, S.any_odd != 0u, TableGains{gt + min1}, bin);
+      else sel_gains_at(it.a[q], P.Wc, S.Es, S.any_odd != 0u, Pow4Gains{}, bin);
+    }
   }
   __syncthreads();
   uint32_t* const g = (PASS & 1) ? D.hC1 : D.hC0;
@@ -419,60 +432,15 @@ __global__ __launch_bounds__(256) void k_sel_radix(const uint8_t* store, int ub0
     if (hC[i]) atomicAdd(&g[i], hC[i]);
 }
 
-template <int PASS>
-__global__ __launch_bounds__(64) void k_sel_digit(int dom0, uint8_t* sel) {
-  constexpr int width = PASS < 2 ? 11 : 10;
-  constexpr int shift = PASS < 2 ? 41 - 11 * PASS : 40 - 10 * PASS;
-  constexpr uint32_t dmask = (1u << width) - 1u;
-  __shared__ uint32_t out[2];
-  const SelDomain D = sel_domain(sel, dom0 + (int)blockIdx.x);
-  SelState S = *D.st;
-  uint32_t* const g = (PASS & 1) ? D.hC1 : D.hC0;
-  uint32_t* const gnext = (PASS & 1) ? D.hC0 : D.hC1;
-  if (!(S.flags & kSelDone)) {
-    if (threadIdx.x == 0) out[0] = out[1] = 0u;
-    wave_lds_fence();
-    if constexpr (width == 11) wave_find_digit<2048>(g, S.rem, &out[0], &out[1]);
-    else wave_find_digit<1024>(g, S.rem, &out[0], &out[1]);
-    wave_lds_fence();
-    const uint32_t dg = min(out[0], dmask);
-    S.n_eq = g[dg];
-    S.rem -= out[1];
-    S.prefix |= (uint64_t)dg << shift;
-    S.mask |= (uint64_t)dmask << shift;
-    if (S.n_eq == S.rem) S.flags |= kSelDone;
-    else if (PASS == 4) S.flags |= kSelDone | kSelRank;  // every bit settled: rank the ties
-    if (threadIdx.x == 0) {
-      D.st->flags = S.flags;
-      D.st->rem = S.rem;
-      D.st->n_eq = S.n_eq;
-      D.st->prefix = S.prefix;
-      D.st->mask = S.mask;
-    }
-  }
-  // the next pass's histogram starts from zero (this one's is not touched)
-  if (PASS < 4)
-    for (int i = threadIdx.x; i < 2048; i += 64) gnext[i] = 0u;
-}
-
-// Ranked ties: the items whose gain equals the threshold are taken in index
-// order while fewer than rem are; tie_cut = the index after the rem-th.
+// Ranked ties (block of 1024): the items whose gain equals the threshold
+// are taken in index order while fewer than rem are; tie_cut = the index
+// after the rem-th.
 template <bool LL>
-__global__ __launch_bounds__(1024) void k_sel_ties(const uint8_t* store, int ub0, int G, int W, int NU,
-                                                   float RV, int min1, int pairs, int64_t capmax,
-                                                   const double* aval, uint8_t* sel, const uint8_t* cb) {
+__device__ void sel_tie_cut(const uint8_t* store, int G, int W, int NU, float RV, int min1, int pairs,
+                            int64_t capmax, const double* aval, const SelDomain& D, const SelState& S,
+                            int dom, const double* gt, uint32_t* wsum, int* found) {
   constexpr int NT = 1024;
-  __shared__ uint32_t wsum[NT / 64 + 1];
-  __shared__ double gt[16];
-  __shared__ int found;
   const int tid = threadIdx.x;
-  const int dom = ub0 / NU + (int)blockIdx.x;
-  const SelDomain D = sel_domain(sel, dom);
-  const SelState S = *D.st;
-  if (!(S.flags & kSelRank)) return;  // (the whole block)
-  sel_load_gains<LL>(gt, cb, G);
-  if (tid == 0) found = 0;
-  __syncthreads();
   const int u0 = dom * NU;
   const ReqRecord r = req_of(store, u0 / G);
   const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
@@ -496,15 +464,70 @@ __global__ __launch_bounds__(1024) void k_sel_ties(const uint8_t* store, int ub0
         if (tie[q]) {
           if (c + 1u == S.rem) {
             D.st->tie_cut = it.idx[q] + 1;
-            found = 1;
+            *found = 1;
           }
           ++c;
         }
       }
       __syncthreads();
-      if (found) return;
+      if (*found) return;
     }
   }
+}
+
+// Digit PASS of every domain by one wave; the last pass's launch (1024
+// threads) then cuts the ties when they are ranked.
+template <bool LL, int PASS>
+__global__ __launch_bounds__(PASS == 4 ? 1024 : 64) void k_sel_digit(
+    const uint8_t* store, int ub0, int G, int W, int NU, float RV, int min1, int pairs, int64_t capmax,
+    const double* aval, uint8_t* sel, const uint8_t* cb) {
+  constexpr int width = PASS < 2 ? 11 : 10;
+  constexpr int shift = PASS < 2 ? 41 - 11 * PASS : 40 - 10 * PASS;
+  constexpr uint32_t dmask = (1u << width) - 1u;
+  __shared__ uint32_t out[2];
+  __shared__ uint32_t wsum[1024 / 64 + 1];
+  __shared__ double gt[16];
+  __shared__ int found;
+  const int dom = ub0 / NU + (int)blockIdx.x;
+  const SelDomain D = sel_domain(sel, dom);
+  SelState S = *D.st;
+  uint32_t* const g = (PASS & 1) ? D.hC1 : D.hC0;
+  uint32_t* const gnext = (PASS & 1) ? D.hC0 : D.hC1;
+  if (!(S.flags & kSelDone)) {
+    if (threadIdx.x < 64) {
+      if (threadIdx.x == 0) out[0] = out[1] = 0u;
+      wave_lds_fence();
+      if constexpr (width == 11) wave_find_digit<2048>(g, S.rem, &out[0], &out[1]);
+      else wave_find_digit<1024>(g, S.rem, &out[0], &out[1]);
+    }
+    if constexpr (PASS == 4) __syncthreads();
+    else wave_lds_fence();
+    const uint32_t dg = min(out[0], dmask);
+    S.n_eq = g[dg];
+    S.rem -= out[1];
+    S.prefix |= (uint64_t)dg << shift;
+    S.mask |= (uint64_t)dmask << shift;
+    if (S.n_eq == S.rem) S.flags |= kSelDone;
+    else if (PASS == 4) S.flags |= kSelDone | kSelRank;  // every bit settled: rank the ties
+    if (threadIdx.x == 0) {
+      D.st->flags = S.flags;
+      D.st->rem = S.rem;
+      D.st->n_eq = S.n_eq;
+      D.st->prefix = S.prefix;
+      D.st->mask = S.mask;
+    }
+    if constexpr (PASS == 4) {
+      if (S.flags & kSelRank) {  // (the whole block)
+        sel_load_gains<LL>(gt, cb, G);
+        if (threadIdx.x == 0) found = 0;
+        __syncthreads();
+        sel_tie_cut<LL>(store, G, W, NU, RV, min1, pairs, capmax, aval, D, S, dom, gt, wsum, &found);
+      }
+    }
+  }
+  // the next pass's histogram starts from zero (this one's is not touched)
+  if (PASS < 4)
+    for (int i = threadIdx.x; i < 2048; i += 64) gnext[i] = 0u;
 }
 
 template <bool LL>
@@ -576,22 +599,22 @@ static void launch_sel_chain(const DecodeArgs& a, const Part& P, const WsLayout&
   const double* const aval = (const double*)(a.ws + L.aval);
   const uint8_t* const store = (const uint8_t*)a.store;
   const dim3 gi(P.nunits, nch);
-  hipLaunchKernelGGL((k_sel_hist<LL>), gi, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1,
+  const dim3 gh(P.nunits, (unsigned)((a.capmax + kSelBlockTokens - 1) / kSelBlockTokens));
+  hipLaunchKernelGGL((k_sel_hist<LL>), gh, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1,
                      a.pairs, a.capmax, aval, sel, a.cblock);
   hipLaunchKernelGGL((k_sel_field<LL>), dim3(ndom), dim3(64), 0, st, store, P.ub0, a.G, a.W, NU, a.RV,
                      a.min1, a.pairs, sel);
 #define READKV_SEL_PASS(p)                                                                              \
-  hipLaunchKernelGGL((k_sel_radix<LL, p>), gi, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1, \
+  hipLaunchKernelGGL((k_sel_radix<LL, p>), gh, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1, \
                      a.pairs, a.capmax, aval, sel, a.cblock);                                            \
-  hipLaunchKernelGGL((k_sel_digit<p>), dim3(ndom), dim3(64), 0, st, P.ub0 / NU, sel);
+  hipLaunchKernelGGL((k_sel_digit<LL, p>), dim3(ndom), dim3(p == 4 ? 1024 : 64), 0, st, store, P.ub0, a.G,  \
+                     a.W, NU, a.RV, a.min1, a.pairs, a.capmax, aval, sel, a.cblock);
   READKV_SEL_PASS(0)
   READKV_SEL_PASS(1)
   READKV_SEL_PASS(2)
   READKV_SEL_PASS(3)
   READKV_SEL_PASS(4)
 #undef READKV_SEL_PASS
-  hipLaunchKernelGGL((k_sel_ties<LL>), dim3(ndom), dim3(1024), 0, st, store, P.ub0, a.G, a.W, NU, a.RV,
-                     a.min1, a.pairs, a.capmax, aval, sel, a.cblock);
   hipLaunchKernelGGL((k_sel_depths<LL>), gi, dim3(256), 0, st, store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4,
                      NU, a.RV, a.min1, a.pairs, a.capmax, aval, sel, tv, tk, a.counters, a.cblock);
 }

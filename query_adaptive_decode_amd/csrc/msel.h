@@ -10,13 +10,15 @@
 //   k_value_weights  (also zeroes the domain's histograms and state)
 //   k_sel_hist       field histograms, positive-gain count, top field
 //   k_sel_field      the field of the B-th largest gain
-//   k_sel_radix<p>, k_sel_digit<p>, p = 0..4   one digit per pass
-//   k_sel_ties       the index cut of the exact ties, when they are ranked
+//   k_sel_radix<p>, k_sel_digit<p>, p = 0..4   one digit per pass (the
+//                    last digit's launch also finds the index cut of the
+//                    exact ties, when they are ranked)
 //   k_sel_depths     every item's depth, and the read counters
 // Item i of a domain is token i of the flat (KV head, token) order, or the
 // pair of tokens 2i, 2i + 1 under value packets; item-parallel launches take
-// 1024 tokens of one unit per block, 4 per thread (a pair never straddles
-// threads or units: T_packed is a multiple of 32).
+// 4096 (histograms) or 1024 (depths) tokens of one unit per block, 4 per
+// thread at a time (a pair never straddles threads or units: T_packed is a
+// multiple of 32).
 #pragma once
 #include <math.h>
 
@@ -25,6 +27,10 @@
 #include "select.h"
 
 namespace readkv {
+
+// tokens of one unit per block in the histogram passes (fewer blocks, so
+// fewer flushes of each block's histogram into the domain's)
+constexpr int kSelBlockTokens = 4096;
 
 struct SelState {
   uint32_t npos;     // positive gains of the domain
