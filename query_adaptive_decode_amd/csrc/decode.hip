@@ -1893,10 +1893,22 @@ static int launch_part(const DecodeArgs& a, const WsLayout& L, const Part& P, ui
                         hipFuncAttributeMaxDynamicSharedMemorySize, (kDim * 8 + 8) * 32);
     attr_set = true;
   }
-  // each unit's tiles split evenly over nrun blocks: about three blocks per
-  // compute unit in all (two for more than 4 query heads per KV head)
+  // each unit's tiles split evenly over nrun blocks, as many blocks as fit
+  // on the chip at once (three per compute unit at most: two for more than
+  // 4 query heads per KV head, or when the staged lines of a large key
+  // budget take more LDS)
   const int64_t total_tiles = (int64_t)P.nunits * L.ntile;
-  const int64_t slots = (GQA <= 4 ? 3 : 2) * (int64_t)device_cu_count();
+  static size_t occ_dyn = 0;
+  static int occ_n = 0;
+  if (occ_n == 0 || occ_dyn != dyn) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(&k_score<GQA, DT>), 256,
+                                                     dyn) != hipSuccess || n < 1)
+      n = 1;
+    occ_n = min(n, GQA <= 4 ? 3 : 2);
+    occ_dyn = dyn;
+  }
+  const int64_t slots = (int64_t)occ_n * device_cu_count();
   int run = (int)((total_tiles + slots - 1) / slots);
   if (run < 1) run = 1;
   const int nrun = (L.ntile + run - 1) / run;
