@@ -294,8 +294,10 @@ int launch_key_alloc_lloyd(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, 
 // otherwise value weights (all compute units) then the selection
 // ---------------------------------------------------------------------------
 // The multi-block selection (msel.h).  Item-parallel launches: block (unit,
-// chunk of 1024 tokens), 256 threads, 4 tokens each; per-domain launches: one
-// wave (k_sel_field, k_sel_digit; the last digit with a block of 1024 for the tie cut).
+// 4096 tokens for the histograms, 1024 for the depths), 256 threads, 4 tokens
+// at a time; per-domain launches: one wave decides (k_sel_digit; the field's
+// launch reads the histograms with 256 threads, the last digit's cuts the
+// ties with 1024).
 // ---------------------------------------------------------------------------
 template <bool LL>
 __device__ __forceinline__ void sel_load_gains(double* gt, const uint8_t* cb, int G) {
@@ -341,34 +343,60 @@ __global__ __launch_bounds__(256) void k_sel_hist(const uint8_t* store, int ub0,
 }
 
 template <bool LL>
-__global__ __launch_bounds__(64) void k_sel_field(const uint8_t* store, int ub0, int G, int W, int NU,
-                                                  float RV, int min1, int pairs, uint8_t* sel) {
+__global__ __launch_bounds__(256) void k_sel_field(const uint8_t* store, int ub0, int G, int W, int NU,
+                                                   float RV, int min1, int pairs, uint8_t* sel) {
   __shared__ uint32_t out[4];
+  __shared__ uint32_t wnp[4], wodd[4];
+  __shared__ int wet[4];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int dom = ub0 / NU + (int)blockIdx.x;
   const ReqRecord r = req_of(store, dom * NU / G);
   const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
   const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
   const SelDomain D = sel_domain(sel, dom);
-  // positive gains, top field (+2) and odd gains, from the histograms: a
-  // regular item at field f holds Wc gains, the top one at f - 2
+  // positive gains, top field (+2) and odd gains, from the histograms (a
+  // regular item at field f holds Wc gains, the top one at f - 2); thread t
+  // reads bins 8t .. 8t + 7 of both with 16-byte loads
   uint32_t np = 0u, odd = 0u;
   int et = -1;
-  for (int f = (int)threadIdx.x; f < 2048; f += 64) {
-    const uint32_t a = D.hA[f], o = D.hB[f];
-    np += a * (uint32_t)P.Wc + o;
-    odd |= o;
-    if (a) et = max(et, f);
-    if (o) et = max(et, f + 2);
+  {
+    const uint4* a4 = reinterpret_cast<const uint4*>(D.hA) + 2 * tid;
+    const uint4* b4 = reinterpret_cast<const uint4*>(D.hB) + 2 * tid;
+    const uint4 av[2] = {a4[0], a4[1]}, ov[2] = {b4[0], b4[1]};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint4& x = av[k >> 2];
+      const uint4& y = ov[k >> 2];
+      const uint32_t a = (k & 3) == 0 ? x.x : (k & 3) == 1 ? x.y : (k & 3) == 2 ? x.z : x.w;
+      const uint32_t o = (k & 3) == 0 ? y.x : (k & 3) == 1 ? y.y : (k & 3) == 2 ? y.z : y.w;
+      const int f = 8 * tid + k;
+      np += a * (uint32_t)P.Wc + o;
+      odd |= o;
+      if (a) et = max(et, f);
+      if (o) et = max(et, f + 2);
+    }
   }
-  const uint32_t npos = (uint32_t)wave_sum_i32((int)np);
-  const int etop = wave_max_i32(et);
-  const uint32_t any_odd = __ballot(odd != 0u) != 0ull ? 1u : 0u;
+  {
+    const uint32_t n = (uint32_t)wave_sum_i32((int)np);
+    const int e = wave_max_i32(et);
+    const bool o = __ballot(odd != 0u) != 0ull;
+    if (lane == 0) {
+      wnp[wv] = n;
+      wet[wv] = e;
+      wodd[wv] = o ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  if (wv != 0) return;
+  const uint32_t npos = (wnp[0] + wnp[1]) + (wnp[2] + wnp[3]);
+  const int etop = max(max(wet[0], wet[1]), max(wet[2], wet[3]));
+  const uint32_t any_odd = (wodd[0] | wodd[1] | wodd[2] | wodd[3]) ? 1u : 0u;
   uint32_t flags = 0u, rem = 0u, n_eq = 0u;
   int Es = 0;
   if (P.bud == 0u || npos <= P.bud) {
     flags = kSelDone;  // nothing, or every positive gain, is taken
   } else {
-    if (threadIdx.x == 0) out[0] = out[1] = out[2] = 0u;
+    if (lane == 0) out[0] = out[1] = out[2] = 0u;
     wave_lds_fence();
     wave_find_gain_field(D.hA, D.hB, P.Wc, etop - 2, P.bud, out);
     wave_lds_fence();
@@ -377,7 +405,7 @@ __global__ __launch_bounds__(64) void k_sel_field(const uint8_t* store, int ub0,
     n_eq = out[2];
     if (n_eq == rem) flags = kSelDone;
   }
-  if (threadIdx.x == 0) {
+  if (lane == 0) {
     SelState* s = D.st;
     s->npos = npos;
     s->etop = etop;
@@ -602,7 +630,7 @@ static void launch_sel_chain(const DecodeArgs& a, const Part& P, const WsLayout&
   const dim3 gh(P.nunits, (unsigned)((a.capmax + kSelBlockTokens - 1) / kSelBlockTokens));
   hipLaunchKernelGGL((k_sel_hist<LL>), gh, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1,
                      a.pairs, a.capmax, aval, sel, a.cblock);
-  hipLaunchKernelGGL((k_sel_field<LL>), dim3(ndom), dim3(64), 0, st, store, P.ub0, a.G, a.W, NU, a.RV,
+  hipLaunchKernelGGL((k_sel_field<LL>), dim3(ndom), dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV,
                      a.min1, a.pairs, sel);
 #define READKV_SEL_PASS(p)                                                                              \
   hipLaunchKernelGGL((k_sel_radix<LL, p>), gh, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1, \
