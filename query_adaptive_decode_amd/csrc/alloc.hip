@@ -184,10 +184,8 @@ __global__ __launch_bounds__(256) void k_value_weights(
   const int ux = ub0 + (int)blockIdx.x;
   if (sel && blockIdx.y == 0 && ux % NU == 0) {
     const SelDomain D = sel_domain(sel, ux / NU);
-    for (int i = threadIdx.x; i < 4096; i += 256) {
-      D.hA[i] = 0u;  // hA and hB
-      D.hC0[i] = 0u; // hC0 and hC1
-    }
+    for (int i = threadIdx.x; i < 4096; i += 256) D.hA[i] = 0u;               // hA and hB
+    for (int i = threadIdx.x; i < 2 * kSelDigitBins; i += 256) D.hC0[i] = 0u;  // hC0 and hC1
     if (threadIdx.x == 0) {
       SelState z = {};
       z.etop = -1;
@@ -295,9 +293,8 @@ int launch_key_alloc_lloyd(const DecodeArgs& a, const WsLayout& L, uint8_t* tk, 
 // ---------------------------------------------------------------------------
 // The multi-block selection (msel.h).  Item-parallel launches: block (unit,
 // 4096 tokens for the histograms, 1024 for the depths), 256 threads, 4 tokens
-// at a time; per-domain launches: one wave decides (k_sel_digit; the field's
-// launch reads the histograms with 256 threads, the last digit's cuts the
-// ties with 1024).
+// at a time; per-domain launches: one block of 256 decides (k_sel_field,
+// k_sel_digit; the last digit's block of 1024 also cuts the ties).
 // ---------------------------------------------------------------------------
 template <bool LL>
 __device__ __forceinline__ void sel_load_gains(double* gt, const uint8_t* cb, int G) {
@@ -424,10 +421,9 @@ template <bool LL, int PASS>
 __global__ __launch_bounds__(256) void k_sel_radix(const uint8_t* store, int ub0, int G, int W, int NU,
                                                    float RV, int min1, int pairs, int64_t capmax,
                                                    const double* aval, uint8_t* sel, const uint8_t* cb) {
-  constexpr int width = PASS < 2 ? 11 : 10;
-  constexpr int shift = PASS < 2 ? 41 - 11 * PASS : 40 - 10 * PASS;
-  constexpr uint32_t dmask = (1u << width) - 1u;
-  __shared__ uint32_t hC[2048];
+  constexpr int shift = 52 - kSelDigitBits * (PASS + 1);
+  constexpr uint32_t dmask = (uint32_t)kSelDigitBins - 1u;
+  __shared__ uint32_t hC[kSelDigitBins];
   __shared__ double gt[16];
   const int tid = threadIdx.x;
   const int ux = ub0 + (int)blockIdx.x;
@@ -438,7 +434,7 @@ __global__ __launch_bounds__(256) void k_sel_radix(const uint8_t* store, int ub0
   const int64_t Tp = r.len & ~(int64_t)(kGroup - 1);
   const int64_t c0 = (int64_t)blockIdx.y * kSelBlockTokens;
   if (c0 >= Tp) return;
-  for (int i = tid; i < 2048; i += 256) hC[i] = 0u;
+  for (int i = tid; i < kSelDigitBins; i += 256) hC[i] = 0u;
   sel_load_gains<LL>(gt, cb, G);
   __syncthreads();
   const SelParams P = sel_params(Tp, NU, RV, W, min1, pairs, LL);
@@ -503,17 +499,18 @@ __device__ void sel_tie_cut(const uint8_t* store, int G, int W, int NU, float RV
   }
 }
 
-// Digit PASS of every domain by one wave; the last pass's launch (1024
+// Digit PASS of every domain by one block; the last pass's launch (1024
 // threads) then cuts the ties when they are ranked.
 template <bool LL, int PASS>
-__global__ __launch_bounds__(PASS == 4 ? 1024 : 64) void k_sel_digit(
+__global__ __launch_bounds__(PASS == kSelPasses - 1 ? 1024 : 256) void k_sel_digit(
     const uint8_t* store, int ub0, int G, int W, int NU, float RV, int min1, int pairs, int64_t capmax,
     const double* aval, uint8_t* sel, const uint8_t* cb) {
-  constexpr int width = PASS < 2 ? 11 : 10;
-  constexpr int shift = PASS < 2 ? 41 - 11 * PASS : 40 - 10 * PASS;
-  constexpr uint32_t dmask = (1u << width) - 1u;
+  constexpr bool LAST = PASS == kSelPasses - 1;
+  constexpr int NT = LAST ? 1024 : 256;
+  constexpr int shift = 52 - kSelDigitBits * (PASS + 1);
+  constexpr uint32_t dmask = (uint32_t)kSelDigitBins - 1u;
   __shared__ uint32_t out[2];
-  __shared__ uint32_t wsum[1024 / 64 + 1];
+  __shared__ uint32_t wsum[NT / 64 + 1];
   __shared__ double gt[16];
   __shared__ int found;
   const int dom = ub0 / NU + (int)blockIdx.x;
@@ -521,22 +518,17 @@ __global__ __launch_bounds__(PASS == 4 ? 1024 : 64) void k_sel_digit(
   SelState S = *D.st;
   uint32_t* const g = (PASS & 1) ? D.hC1 : D.hC0;
   uint32_t* const gnext = (PASS & 1) ? D.hC0 : D.hC1;
-  if (!(S.flags & kSelDone)) {
-    if (threadIdx.x < 64) {
-      if (threadIdx.x == 0) out[0] = out[1] = 0u;
-      wave_lds_fence();
-      if constexpr (width == 11) wave_find_digit<2048>(g, S.rem, &out[0], &out[1]);
-      else wave_find_digit<1024>(g, S.rem, &out[0], &out[1]);
-    }
-    if constexpr (PASS == 4) __syncthreads();
-    else wave_lds_fence();
+  if (!(S.flags & kSelDone)) {  // (the whole block)
+    if (threadIdx.x == 0) out[0] = out[1] = 0u;
+    __syncthreads();
+    block_find_digit<NT>(g, S.rem, wsum, out);
     const uint32_t dg = min(out[0], dmask);
     S.n_eq = g[dg];
     S.rem -= out[1];
     S.prefix |= (uint64_t)dg << shift;
     S.mask |= (uint64_t)dmask << shift;
     if (S.n_eq == S.rem) S.flags |= kSelDone;
-    else if (PASS == 4) S.flags |= kSelDone | kSelRank;  // every bit settled: rank the ties
+    else if (LAST) S.flags |= kSelDone | kSelRank;  // every bit settled: rank the ties
     if (threadIdx.x == 0) {
       D.st->flags = S.flags;
       D.st->rem = S.rem;
@@ -544,7 +536,7 @@ __global__ __launch_bounds__(PASS == 4 ? 1024 : 64) void k_sel_digit(
       D.st->prefix = S.prefix;
       D.st->mask = S.mask;
     }
-    if constexpr (PASS == 4) {
+    if constexpr (LAST) {
       if (S.flags & kSelRank) {  // (the whole block)
         sel_load_gains<LL>(gt, cb, G);
         if (threadIdx.x == 0) found = 0;
@@ -554,8 +546,8 @@ __global__ __launch_bounds__(PASS == 4 ? 1024 : 64) void k_sel_digit(
     }
   }
   // the next pass's histogram starts from zero (this one's is not touched)
-  if (PASS < 4)
-    for (int i = threadIdx.x; i < 2048; i += 64) gnext[i] = 0u;
+  if (!LAST)
+    for (int i = threadIdx.x; i < kSelDigitBins; i += NT) gnext[i] = 0u;
 }
 
 template <bool LL>
@@ -635,13 +627,13 @@ static void launch_sel_chain(const DecodeArgs& a, const Part& P, const WsLayout&
 #define READKV_SEL_PASS(p)                                                                              \
   hipLaunchKernelGGL((k_sel_radix<LL, p>), gh, dim3(256), 0, st, store, P.ub0, a.G, a.W, NU, a.RV, a.min1, \
                      a.pairs, a.capmax, aval, sel, a.cblock);                                            \
-  hipLaunchKernelGGL((k_sel_digit<LL, p>), dim3(ndom), dim3(p == 4 ? 1024 : 64), 0, st, store, P.ub0, a.G,  \
-                     a.W, NU, a.RV, a.min1, a.pairs, a.capmax, aval, sel, a.cblock);
+  hipLaunchKernelGGL((k_sel_digit<LL, p>), dim3(ndom), dim3(p == kSelPasses - 1 ? 1024 : 256), 0, st, store, \
+                     P.ub0, a.G, a.W, NU, a.RV, a.min1, a.pairs, a.capmax, aval, sel, a.cblock);
+  static_assert(kSelPasses == 4, "one launch pair per digit below");
   READKV_SEL_PASS(0)
   READKV_SEL_PASS(1)
   READKV_SEL_PASS(2)
   READKV_SEL_PASS(3)
-  READKV_SEL_PASS(4)
 #undef READKV_SEL_PASS
   hipLaunchKernelGGL((k_sel_depths<LL>), gi, dim3(256), 0, st, store, P.ub0, a.G, a.W, a.dtype == 0 ? 2 : 4,
                      NU, a.RV, a.min1, a.pairs, a.capmax, aval, sel, tv, tk, a.counters, a.cblock);

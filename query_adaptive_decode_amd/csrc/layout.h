@@ -169,10 +169,10 @@ RKV_HD Unit unit_of(uint8_t* store, const ReqRecord& r, int g, int G, int d, int
 //   qp     f64 [B][G][d][H/G]     the score's weights q'_hc sigma^K_c, q' = U_K q
 //   qb     f64 [B][H]             sum_c q'_c mu^K_c
 //   otail  f32 [B][H][d]          the open group's share of the output
-// Per selection domain of the multi-block value selection: four 2048-bin
-// histograms (exponent fields of regular items and of odd gains, and two
-// alternating radix-digit histograms) and the search state.
-constexpr int64_t kSelDomainBytes = 4 * 2048 * 4 + 256;
+// Per selection domain of the multi-block value selection: two 2048-bin
+// histograms (exponent fields of regular items and of odd gains), two
+// alternating 8192-bin radix-digit histograms and the search state.
+constexpr int64_t kSelDomainBytes = (2 * 2048 + 2 * 8192) * 4 + 256;
 
 struct WsLayout {
   int64_t tk, tv, ebuf, tilepart, ftile, aval, opart, qp, qb, otail, sel, size;

@@ -5,12 +5,15 @@
 // of block_choose_depths_hist (select.h) -- exponent-field histograms, then
 // 11/11/10/10/10-bit radix digits of the mantissas in the threshold field,
 // ties ranked by item index -- with each histogram summed in memory by all
-// blocks that hold the domain's items and each decision taken by one wave
-// per domain.  A chain of launches on one stream, so it can be captured:
+// blocks that hold the domain's items and each decision taken by one block
+// per domain; the mantissas are ranked in four 13-bit digits (fewer passes
+// than the single block's 11/11/10/10/10, each a launch here).  A chain of
+// launches on one stream, so it can be captured:
 //   k_value_weights  (also zeroes the domain's histograms and state)
-//   k_sel_hist       field histograms, positive-gain count, top field
-//   k_sel_field      the field of the B-th largest gain
-//   k_sel_radix<p>, k_sel_digit<p>, p = 0..4   one digit per pass (the
+//   k_sel_hist       field histograms
+//   k_sel_field      positive-gain count, top field, the field of the B-th
+//                    largest gain
+//   k_sel_radix<p>, k_sel_digit<p>, p = 0..3   one digit per pass (the
 //                    last digit's launch also finds the index cut of the
 //                    exact ties, when they are ranked)
 //   k_sel_depths     every item's depth, and the read counters
@@ -49,13 +52,55 @@ constexpr uint32_t kSelRank = 2u;  // every bit settled, fewer to take than equa
 struct SelDomain {
   uint32_t* hA;   // regular items by field
   uint32_t* hB;   // odd gains by field
-  uint32_t* hC0;  // radix digits, even passes
+  uint32_t* hC0;  // radix digits, even passes (8192 bins)
   uint32_t* hC1;  // radix digits, odd passes
   SelState* st;
 };
+constexpr int kSelDigitBits = 13;
+constexpr int kSelDigitBins = 1 << kSelDigitBits;
+constexpr int kSelPasses = 4;  // 4 x 13 = the 52 mantissa bits
 __device__ __forceinline__ SelDomain sel_domain(uint8_t* sel, int64_t dom) {
   uint32_t* h = reinterpret_cast<uint32_t*>(sel + dom * kSelDomainBytes);
-  return SelDomain{h, h + 2048, h + 4096, h + 6144, reinterpret_cast<SelState*>(h + 8192)};
+  return SelDomain{h, h + 2048, h + 4096, h + 4096 + kSelDigitBins,
+                   reinterpret_cast<SelState*>(h + 4096 + 2 * kSelDigitBins)};
+}
+
+// One block (NT threads): the digit (of kSelDigitBins bins, in memory) where
+// the count from the top reaches rem (>= 1, at most the bins' total); out[0]
+// = digit, out[1] = count above it.  Thread t holds the t-th group of
+// bins from the top; a block scan in thread order ranks the groups.
+template <int NT>
+__device__ __forceinline__ void block_find_digit(const uint32_t* hist, uint32_t rem, uint32_t* wsum,
+                                                 uint32_t* out) {
+  constexpr int PER = kSelDigitBins / NT;
+  static_assert(PER % 4 == 0, "whole 16-byte reads per thread");
+  const int tid = threadIdx.x;
+  const int base = kSelDigitBins - (tid + 1) * PER;  // bins base .. base + PER - 1
+  uint32_t h[PER];
+  uint32_t tot = 0;
+#pragma unroll
+  for (int i = 0; i < PER / 4; ++i) {
+    const uint4 v = *reinterpret_cast<const uint4*>(hist + base + 4 * i);
+    h[4 * i] = v.x;
+    h[4 * i + 1] = v.y;
+    h[4 * i + 2] = v.z;
+    h[4 * i + 3] = v.w;
+    tot += (v.x + v.y) + (v.z + v.w);
+  }
+  const uint32_t excl = block_excl_scan<NT>(tot, wsum);
+  if (excl < rem && excl + tot >= rem) {
+    uint32_t c = excl;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (c + h[i] >= rem) {
+        out[0] = (uint32_t)(base + i);
+        out[1] = c;
+        break;
+      }
+      c += h[i];
+    }
+  }
+  __syncthreads();
 }
 
 // A domain's budget and item form (as value_select_block): B_V =
