@@ -628,15 +628,20 @@ def test_encode_decode_mix_full_shape(record_property):
 
 
 # ------------------------------------------------------------ store flags
-def test_graph_replay_matches_eager_steps():
+@pytest.mark.parametrize("policy,T0", [(SCOPE_KV_HEAD, 1000), (SCOPE_LAYER, 2500)],
+                         ids=["kv_head", "layer-many-block-selection"])
+def test_graph_replay_matches_eager_steps(policy, T0):
     """The benchmark's step (append one token per request, then decode) captured
     once in a HIP graph and replayed step after step, with eager work and
     synchronisations between the replays, gives bitwise the outputs, depths
-    and read counters of the same steps run eagerly on a second cache."""
-    cfg = synth.workload(2, B=2, H=8, G=2, T0=1000)
+    and read counters of the same steps run eagerly on a second cache (under
+    per-layer budgets with 8 KV heads x 2,500 tokens: the many-block value
+    selection's chain of launches in the graph)."""
+    cfg = synth.workload(2, B=2, H=8 if policy == SCOPE_KV_HEAD else 32,
+                         G=2 if policy == SCOPE_KV_HEAD else 8, T0=T0)
     steps, R = 6, 3.0
     B, H, G, d = cfg["B"], cfg["H"], cfg["G"], cfg["d"]
-    say(f"[case] graph replay B={B} G={G} T0=1000 steps={steps} R={R}")
+    say(f"[case] graph replay B={B} G={G} T0={T0} steps={steps} R={R} policy={policy:#x}")
     h = workload.host_inputs(cfg, steps)
     dv = workload.to_device(h)
     lcfg = workload.config_for(cfg, steps)
@@ -655,7 +660,7 @@ def test_graph_replay_matches_eager_steps():
     with torch.cuda.graph(graph):
         caches[1].append(bufs["k"], bufs["v"])
         caches[1].decode(bufs["q"], R, R, out=outs[1], key_depths=tks[1], value_depths=tvs[1],
-                         counters=ctrs[1])
+                         counters=ctrs[1], policy=policy)
     torch.cuda.synchronize()
     junk = torch.ones(1 << 20, device="cuda")
     for s in range(steps):
@@ -668,7 +673,7 @@ def test_graph_replay_matches_eager_steps():
         torch.cuda.synchronize()
         caches[0].append(dv["kstep"][s], dv["vstep"][s])
         caches[0].decode(dv["q"][s], R, R, out=outs[0], key_depths=tks[0], value_depths=tvs[0],
-                         counters=ctrs[0])
+                         counters=ctrs[0], policy=policy)
         torch.cuda.synchronize()
         for name, (a, b) in dict(out=outs, tk=tks, tv=tvs, ctr=ctrs).items():
             assert torch.equal(a, b), f"step {s}: {name} differs between replay and eager"
