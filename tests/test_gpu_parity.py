@@ -580,6 +580,15 @@ def test_long_context_131k_weights_through_memory(record_property):
 
 
 @pytest.mark.timeout(900)
+def test_long_context_131k_layer_budgets(record_property):
+    # per-layer budgets over two KV heads of 131,072 tokens: 262,144 items in
+    # one selection, over many blocks (the oracle takes about a minute)
+    cfg = synth.workload(3, B=1, H=8, G=2)
+    run = Run(cfg, steps=1, rates=[(3.3, 2.7)], scope=SCOPE_LAYER)
+    report(record_property, "T0=131072 per-layer budgets", run.check_layer())
+
+
+@pytest.mark.timeout(900)
 def test_long_context_131k_near_uniform_weights(record_property):
     # a query scaled by 2^-10: every logit is within a fraction of a nat of
     # the others, so 131k near-equal weights enter the fp16 operand of the
